@@ -1,0 +1,222 @@
+"""Pins of the float64 attention oracle against closed forms, special cases,
+a library routine (torch SDPA in float64) and the pages' merge rule."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+
+rng = np.random.default_rng(2024)
+
+
+def rand(*shape):
+    return rng.standard_normal(shape)
+
+
+def sdpa_causal(q, k, v):
+    """torch float64 causal SDPA for one document, GQA by enable_gqa. q [n,H,d]."""
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def lse_causal_torch(q, k):
+    """torch.logsumexp of masked scaled scores, per head: [H,n]."""
+    n, H, d = q.shape
+    G = H // k.shape[1]
+    out = np.zeros((H, n))
+    for h in range(H):
+        s = torch.from_numpy(q[:, h]) @ torch.from_numpy(k[:, h // G]).T / math.sqrt(d)
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+        out[h] = torch.logsumexp(s, dim=1).numpy()
+    return out
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(4, 2, 16), (2, 2, 64), (8, 2, 32)])
+def test_varlen_matches_torch_sdpa(H, Hkv, d):
+    lengths = [1, 7, 33, 2, 50]
+    T = sum(lengths)
+    q, k, v = rand(T, H, d), rand(T, Hkv, d), rand(T, Hkv, d)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    out, lse = A.varlen_attention(q, k, v, cu, H, Hkv)
+    for s in range(len(lengths)):
+        sl = slice(cu[s], cu[s + 1])
+        np.testing.assert_allclose(out[sl], sdpa_causal(q[sl], k[sl], v[sl]), atol=1e-10, rtol=0)
+        np.testing.assert_allclose(lse[:, sl], lse_causal_torch(q[sl], k[sl]), atol=1e-10, rtol=0)
+
+
+def test_rows_subset_equals_full():
+    lengths = [10, 40, 14]
+    T = sum(lengths)
+    q, k, v = rand(T, 4, 8), rand(T, 2, 8), rand(T, 2, 8)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    out, lse = A.varlen_attention(q, k, v, cu, 4, 2)
+    rows = np.array([63, 0, 11, 10, 50])
+    o2, l2 = A.varlen_attention(q, k, v, cu, 4, 2, rows=rows)
+    # same arithmetic; only BLAS blocking of the row groups differs
+    np.testing.assert_allclose(o2, out[rows], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l2, lse[:, rows], atol=1e-13, rtol=0)
+
+
+def test_single_token_document_returns_its_value():
+    lengths = [4, 1, 6, 1]
+    T = sum(lengths)
+    q, k, v = rand(T, 2, 16), rand(T, 2, 16), rand(T, 2, 16)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    out, lse = A.varlen_attention(q, k, v, cu, 2, 2)
+    for t in (4, 11):
+        np.testing.assert_array_equal(out[t], v[t])
+        for h in range(2):
+            assert lse[h, t] == pytest.approx(q[t, h] @ k[t, h] / 4.0, abs=1e-13)
+
+
+def test_constant_value_is_returned():
+    lengths = [3, 30, 9]
+    T = sum(lengths)
+    q, k = rand(T, 4, 8) * 3, rand(T, 2, 8) * 3
+    v = np.full((T, 2, 8), -1.75)
+    out, _ = A.varlen_attention(q, k, v, [0, 3, 33, 42], 4, 2)
+    assert np.max(np.abs(out + 1.75)) <= 1e-12
+
+
+def test_zero_query_counts_visible_keys():
+    """q = 0 makes every visible logit 0, so lse_i = ln(number of visible keys)."""
+    lengths = [5, 17, 42]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v = np.zeros((T, 2, 8)), rand(T, 2, 8), rand(T, 2, 8)
+    _, lse = A.varlen_attention(q, k, v, cu, 2, 2)
+    n = np.concatenate([np.arange(1, l + 1) for l in lengths])
+    np.testing.assert_array_equal(np.rint(np.exp(lse[0])).astype(int), n)
+    np.testing.assert_allclose(lse[1], np.log(n), atol=1e-15)
+
+
+def test_two_key_closed_form():
+    """Row 1 of a 2-token document sees k0 (logit a*scale) and k1 (logit 0)."""
+    d = 16
+    a = 2.5
+    q = np.zeros((2, 1, d)); q[1, 0, 0] = a
+    k = np.zeros((2, 1, d)); k[0, 0, 0] = 1.0
+    v = rand(2, 1, d)
+    out, lse = A.varlen_attention(q, k, v, [0, 2], 1, 1)
+    s0 = a / math.sqrt(d)
+    w0 = math.exp(s0) / (math.exp(s0) + 1.0)
+    np.testing.assert_allclose(out[1, 0], w0 * v[0, 0] + (1 - w0) * v[1, 0], atol=1e-14)
+    assert lse[0, 1] == pytest.approx(math.log(math.exp(s0) + 1.0), abs=1e-14)
+    np.testing.assert_allclose(out[0, 0], v[0, 0], atol=0)
+    assert lse[0, 0] == 0.0
+
+
+def test_shared_question_equals_causal_on_question_plus_answer():
+    Q, Alen, m = 12, 7, 3
+    lengths = [Q] + [Alen] * m
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v = rand(T, 4, 8), rand(T, 2, 8), rand(T, 2, 8)
+    out, lse = A.varlen_attention(q, k, v, cu, 4, 2, mask="shared_question")
+    np.testing.assert_allclose(out[:Q], sdpa_causal(q[:Q], k[:Q], v[:Q]), atol=1e-10)
+    for a in range(m):
+        sl = np.r_[0:Q, cu[a + 1]:cu[a + 2]]
+        ref = sdpa_causal(q[sl], k[sl], v[sl])[Q:]
+        np.testing.assert_allclose(out[cu[a + 1]:cu[a + 2]], ref, atol=1e-10)
+        np.testing.assert_allclose(lse[:, cu[a + 1]:cu[a + 2]], lse_causal_torch(q[sl], k[sl])[:, Q:], atol=1e-10)
+
+
+def test_shared_question_zero_query_counts():
+    Q, Alen, m = 9, 5, 2
+    lengths = [Q] + [Alen] * m
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    _, lse = A.varlen_attention(np.zeros((T, 1, 4)), rand(T, 1, 4), rand(T, 1, 4), cu, 1, 1,
+                                mask="shared_question")
+    n = list(range(1, Q + 1)) + [Q + i for _ in range(m) for i in range(1, Alen + 1)]
+    np.testing.assert_array_equal(np.rint(np.exp(lse[0])).astype(int), n)
+
+
+def test_merge_identities():
+    o = rand(6, 3, 8)
+    l = rand(3, 6)
+    inf = np.full((3, 6), -np.inf)
+    m_o, m_l = A.lse_merge(o, l, rand(6, 3, 8), inf)
+    np.testing.assert_array_equal(m_o, o)
+    np.testing.assert_array_equal(m_l, l)
+    m_o, m_l = A.lse_merge(rand(6, 3, 8), inf, o, l)
+    np.testing.assert_array_equal(m_o, o)
+    np.testing.assert_array_equal(m_l, l)
+    m_o, m_l = A.lse_merge(o, l, o, l)
+    np.testing.assert_allclose(m_o, o, atol=1e-15)
+    np.testing.assert_allclose(m_l, l + math.log(2.0), atol=1e-14)
+
+
+@pytest.mark.parametrize("n_chunks", [2, 3, 8])
+def test_kv_split_and_merge_equals_unsharded(n_chunks):
+    lengths = [20, 3, 61, 1, 35]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v = rand(T, 4, 16), rand(T, 2, 16), rand(T, 2, 16)
+    full_o, full_l = A.varlen_attention(q, k, v, cu, 4, 2)
+    pos, doc = A.pack_positions(lengths)
+    cuts = np.sort(rng.choice(np.arange(1, T), n_chunks - 1, replace=False))
+    bounds = np.concatenate([[0], cuts, [T]])
+    order = rng.permutation(n_chunks)  # merge order must not matter
+    acc = None
+    for c in order:
+        sl = slice(bounds[c], bounds[c + 1])
+        o, l = A.block_attention(q, k[sl], v[sl], pos, pos[sl], doc, doc[sl], 4, 2)
+        acc = (o, l) if acc is None else A.lse_merge(acc[0], acc[1], o, l)
+    np.testing.assert_allclose(acc[0], full_o, atol=1e-12)
+    np.testing.assert_allclose(acc[1], full_l, atol=1e-12)
+
+
+def test_block_equals_varlen_on_whole_pack():
+    lengths = [30, 2, 40]
+    T = sum(lengths)
+    q, k, v = rand(T, 2, 8), rand(T, 1, 8), rand(T, 1, 8)
+    pos, doc = A.pack_positions(lengths)
+    o1, l1 = A.varlen_attention(q, k, v, np.concatenate([[0], np.cumsum(lengths)]), 2, 1)
+    o2, l2 = A.block_attention(q, k, v, pos, pos, doc, doc, 2, 1)
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+def test_block_empty_rows():
+    q, k, v = rand(4, 1, 8), rand(3, 1, 8), rand(3, 1, 8)
+    o, l = A.block_attention(q, k, v, [0, 1, 5, 6], [2, 3, 4], [0, 0, 1, 1], [0, 0, 0], 1, 1)
+    assert np.all(l[0] == -np.inf) and np.all(o == 0)
+
+
+@pytest.mark.parametrize("cp,chunk", [(2, 24), (4, 16), (8, 8)])
+def test_zigzag_reassembly_equals_unsharded(cp, chunk):
+    T = 2 * cp * chunk
+    lengths = []
+    r = np.random.default_rng(cp)
+    while sum(lengths) < T:
+        lengths.append(int(min(T - sum(lengths), r.integers(1, 3 * chunk))))
+    q, k, v = rand(T, 4, 8), rand(T, 2, 8), rand(T, 2, 8)
+    full_o, full_l = A.varlen_attention(q, k, v, np.concatenate([[0], np.cumsum(lengths)]), 4, 2)
+
+    def get_chunk(c):
+        sl = slice(c * chunk, (c + 1) * chunk)
+        return q[sl], k[sl], v[sl]
+
+    for rank in range(cp):
+        o, l, steps = A.zigzag_rank_attention(get_chunk, lengths, chunk, rank, cp, 4, 2)
+        assert len(steps) == cp
+        rows = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+        np.testing.assert_allclose(o, full_o[rows], atol=1e-12)
+        np.testing.assert_allclose(l, full_l[:, rows], atol=1e-12)
+
+
+def test_large_row_lse_statistics():
+    """For N(0,1) keys, E[exp(scale<q,k>)] = exp(scale^2 |q|^2 / 2): lse ~ ln n + scale^2|q|^2/2."""
+    n, d = 8192, 128
+    q = rand(1, 1, d)
+    k = rand(n, 1, d)
+    v = rand(n, 1, d)
+    _, lse = A.block_attention(q, k, v, [n], np.arange(n), [0], np.zeros(n), 1, 1)
+    expect = math.log(n) + (q[0, 0] @ q[0, 0]) / d / 2
+    assert abs(lse[0, 0] - expect) < 0.1

@@ -1,0 +1,214 @@
+"""Pins of the reference tile enumerator: brute force on tiny packs, closed
+forms, and the worked examples the pages print."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as A
+from oracle import plan as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+with open(os.path.join(GOLDEN, "page_examples.json")) as f:
+    PAGES = json.load(f)
+
+
+def brute_check(tiles, visible, n_q):
+    """Every tile's cost equals the explicit mask count of its rows, and its spans
+    cover exactly the visible keys of each row (each key once)."""
+    covered = np.zeros(n_q, dtype=bool)
+    for t in tiles:
+        rows = np.arange(t["q_start"], t["q_start"] + t["q_len"])
+        assert not covered[rows].any()
+        covered[rows] = True
+        assert t["cost"] == int(visible[rows].sum())
+        for i, r in enumerate(rows):
+            got = np.zeros(visible.shape[1], dtype=int)
+            for (ks, kl, kp0) in t["spans"]:
+                n = P.visible_in_span(t["q_pos0"] + i, kl, kp0)
+                got[ks:ks + n] += 1
+            assert np.array_equal(got, visible[r].astype(int)), (t, r)
+    assert covered.all()
+
+
+def random_lengths(r, total):
+    out = []
+    while sum(out) < total:
+        out.append(int(min(total - sum(out), r.integers(1, 60))))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_causal_doc_brute_force(seed, bm):
+    r = np.random.default_rng(seed)
+    lengths = random_lengths(r, int(r.integers(1, 300)))
+    cu = workloads.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    seg = A.doc_of_tokens(cu)
+    vis = A.visible_causal_doc(seg, np.arange(T), np.arange(T))
+    tl = P.tiles(P.fragments_varlen(cu), bm)
+    brute_check(tl, vis, T)
+    assert P.total_pairs(tl) == sum(l * (l + 1) // 2 for l in lengths)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("bm", [16, 64])
+def test_shared_question_brute_force(seed, bm):
+    r = np.random.default_rng(100 + seed)
+    Q = int(r.integers(1, 90))
+    ans = [int(r.integers(1, 70)) for _ in range(int(r.integers(0, 5)))]
+    cu = workloads.cu_from_lengths([Q] + ans)
+    T = int(cu[-1])
+    seg = A.doc_of_tokens(cu)
+    vis = A.visible_shared_question(seg, np.arange(T), np.arange(T))
+    tl = P.tiles(P.fragments_varlen(cu, "shared_question"), bm)
+    brute_check(tl, vis, T)
+    closed = Q * (Q + 1) // 2 + sum(a * Q + a * (a + 1) // 2 for a in ans)
+    assert P.total_pairs(tl) == closed
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("bm", [16, 32])
+def test_block_brute_force(seed, bm):
+    """Random zigzag-like shards: runs of positions cut from a packed sequence."""
+    r = np.random.default_rng(200 + seed)
+    cp = int(r.choice([2, 3, 4]))
+    chunk = int(r.integers(4, 40))
+    T = 2 * cp * chunk
+    lengths = random_lengths(r, T)
+    pos, doc = A.pack_positions(lengths)
+    rank = int(r.integers(0, cp))
+    src = int(r.integers(0, cp))
+    qi = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+    ki = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(src, cp)])
+    q_pos, q_doc, kv_pos, kv_doc = pos[qi], doc[qi], pos[ki], doc[ki]
+    vis = A.visible_block(q_pos, q_doc, kv_pos, kv_doc, np.arange(len(qi)), np.arange(len(ki)))
+    tl = P.tiles(P.fragments_block(q_pos, q_doc, kv_pos, kv_doc), bm)
+    brute_check(tl, vis, len(qi))
+
+
+def test_runs():
+    assert P.runs([0, 1, 2, 7, 8, 9], [0, 0, 1, 1, 1, 2]) == [(0, 2, 0, 0), (2, 1, 2, 1), (3, 2, 7, 1), (5, 1, 9, 2)]
+
+
+def test_lpt_order():
+    cu = workloads.cu_from_lengths([100, 5, 300, 64, 64])
+    tl = P.tiles(P.fragments_varlen(cu), 32)
+    order = P.lpt_order(tl)
+    costs = [tl[i]["cost"] for i in order]
+    assert costs == sorted(costs, reverse=True)
+    for a, b in zip(order, order[1:]):
+        if tl[a]["cost"] == tl[b]["cost"]:
+            assert a < b
+    assert sorted(order) == list(range(len(tl)))
+    # two 64-token docs give equal tile costs; the earlier document comes first
+    p = P.plan(P.fragments_varlen(cu), 32)
+    eq = [t["q_start"] for t in p if t["cost"] == 32 * 33 // 2 and t["q_len"] == 32]
+    assert eq == sorted(eq)
+
+
+def test_libra_ten_times_example():
+    ex = PAGES["libra_pair_example"]
+    a = P.total_pairs(P.tiles(P.fragments_varlen([0, ex["long_doc"]]), 64))
+    b = P.total_pairs(P.tiles(P.fragments_varlen(workloads.cu_from_lengths(ex["short_docs"])), 64))
+    assert sum(ex["short_docs"]) == ex["long_doc"]
+    assert a == 838_881_280 and b == 83_906_560
+    assert abs(a / b - ex["flop_ratio_approx"]) <= ex["ratio_tolerance"]
+    # sum of squares proxy gives exactly 10
+    assert ex["long_doc"] ** 2 / sum(l * l for l in ex["short_docs"]) == 10.0
+
+
+def test_fixture_pair_counts():
+    with open(os.path.join(GOLDEN, "oracle_pairs.json")) as f:
+        fx = json.load(f)
+    with open(os.path.join(GOLDEN, "workload_lengths.json")) as f:
+        lens = json.load(f)
+    for s in range(5):
+        ls = lens[f"longtail_seed{s}"]
+        assert fx[f"longtail_seed{s}"] == sum(l * (l + 1) // 2 for l in ls)
+    Q, Al, m = 8192, 4096, 8
+    assert fx["shared_question_pack"] == Q * (Q + 1) // 2 + m * (Al * Q + Al * (Al + 1) // 2)
+
+
+# --------------------------------------------------------------------------
+# zigzag / ring worked examples ("03 · 长文负载均衡", sections 4.2 and 4.4)
+# --------------------------------------------------------------------------
+def step_pairs(lengths, chunk, rank, cp, src, seq_chunks=None):
+    pos, doc = A.pack_positions(lengths)
+    qc = A.zigzag_chunks_of_rank(rank, cp) if seq_chunks is None else seq_chunks[0]
+    kc = A.zigzag_chunks_of_rank(src, cp) if seq_chunks is None else seq_chunks[1]
+    out = []
+    for c in kc:
+        qi = np.concatenate([np.arange(x * chunk, (x + 1) * chunk) for x in qc])
+        ki = np.arange(c * chunk, (c + 1) * chunk)
+        tl = P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 16)
+        out.append(P.total_pairs(tl))
+    return out
+
+
+def test_zigzag_rule_from_page():
+    ex = PAGES["zigzag_rule"]
+    assert list(A.zigzag_chunks_of_rank(ex["rank"], ex["cp"])) == ex["chunks"]
+
+
+@pytest.mark.parametrize("cp", [2, 4, 8])
+def test_zigzag_balances_a_single_document(cp):
+    C = 8
+    lengths = [2 * cp * C]
+    per_rank = [sum(sum(step_pairs(lengths, C, r, cp, s)) for s in range(cp)) for r in range(cp)]
+    assert per_rank == [(2 * cp - 1) * C * C + C * (C + 1)] * cp
+
+
+@pytest.mark.parametrize("cp", [2, 4, 8])
+def test_zigzag_causal_redundancy_is_a_quarter(cp):
+    C = 4
+    lengths = [2 * cp * C]
+    useless = received = 0
+    for r in range(cp):
+        for t in range(1, cp):
+            for pairs in step_pairs(lengths, C, r, cp, A.ring_source(r, t, cp)):
+                received += 1
+                useless += pairs == 0
+    assert received == 2 * cp * (cp - 1)
+    assert useless == cp * (cp - 1) // 2
+    assert useless / received == PAGES["causal_ring_redundancy"]["fraction_approx"]
+
+
+def test_sequential_ring_block_counts():
+    ex = PAGES["sequential_ring_blocks"]
+    cp, C = ex["cp"], 8
+    lengths = [cp * C]
+    counts = []
+    for r in range(cp):
+        n = 0
+        for t in range(cp):
+            src = A.ring_source(r, t, cp)
+            n += step_pairs(lengths, C, r, cp, src, seq_chunks=([r], [src]))[0] > 0
+        counts.append(n)
+    assert counts == ex["blocks_per_rank"]
+
+
+@pytest.mark.slow
+def test_zigzag_rank3_step_pairs_match_explicit_mask():
+    """Per-step visible pairs of rank 3 (cp=8, 8192-token chunks) by the span count
+    and by an explicit mask count, on the 131072-token lognormal pack, seed 0."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    pos, doc = A.pack_positions(lengths)
+    C, cp, rank = 8192, 8, 3
+    qi = np.concatenate([np.arange(c * C, (c + 1) * C) for c in A.zigzag_chunks_of_rank(rank, cp)])
+    got = []
+    for t in range(cp):
+        src = A.ring_source(rank, t, cp)
+        ki = np.concatenate([np.arange(c * C, (c + 1) * C) for c in A.zigzag_chunks_of_rank(src, cp)])
+        tl = P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 64)
+        span_count = P.total_pairs(tl)
+        explicit = 0
+        for b in range(0, len(qi), 2048):
+            rows = np.arange(b, b + 2048)
+            explicit += int(A.visible_block(pos[qi], doc[qi], pos[ki], doc[ki], rows, np.arange(len(ki))).sum())
+        assert span_count == explicit
+        got.append(span_count)
+    assert got == [20_319_978, 7_981_112, 0, 0, 0, 0, 0, 3_473_470]
