@@ -1,0 +1,198 @@
+/*
+ * lbattn.h -- document-masked varlen attention for MI355X (gfx950), C ABI.
+ *
+ * What the library computes
+ * -------------------------
+ * Packed documents attend only inside themselves, so a pack's attention work
+ * grows with the sum of squared document lengths rather than the square of
+ * the pack length ("03 · 长文负载均衡" (llm-infra-atlas), section 1.1, the
+ * W_attn formula; "数据并行负载均衡" (LoongForge), section 1).  The library
+ * runs three operations on one GPU:
+ *
+ *   lb_varlen_attn_fwd  full forward over a packed sequence (cu_seqlens), with
+ *                       a per-document causal mask or a shared-question mask
+ *                       ("03 · 长文负载均衡", section 1.2);
+ *   lb_block_attn_fwd   one ring step of a context-parallel rank: its query
+ *                       shard against one key/value chunk, with global
+ *                       positions and document ids carried per token, returning
+ *                       out and log-sum-exp ("03 · 长文负载均衡", sections 3.2
+ *                       and 4.2; "长序列训练与上下文并行", Ring Attention);
+ *   lb_lse_merge        the online-softmax rescale-and-sum that folds two such
+ *                       partial results ("03 · 长文负载均衡", section 3.2, DCP).
+ *
+ * Inside each forward call, a planning kernel cuts the queries into tiles,
+ * keeps only the key spans that hold visible pairs (DCP's computation blocks,
+ * section 3.2; MagiAttention's full/causal slices, section 4.4), bills each
+ * tile its exact visible-pair count (Libra TAP, section 3.2), and orders tiles
+ * longest first (VRSP, section 2.1; "数据并行负载均衡", section 4.4).  A
+ * persistent attention kernel then pulls (tile, key/value head) items from
+ * that queue, so the next free compute unit always takes the largest
+ * remaining item.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers, owned by the caller.  The
+ *    library never allocates or frees memory.
+ *  - Layout is THD (token-major): q [T][H][d], k and v [T][H_kv][d]; rows are
+ *    contiguous, no padding between heads or tokens.  bf16 means IEEE
+ *    bfloat16 stored in 16 bits.
+ *  - Softmax scale is 1/sqrt(d).  lse is the natural log of the sum of
+ *    exp(scaled logits) over the visible keys.  Query head h uses key/value
+ *    head h / (H / H_kv).
+ *  - Every compute call is asynchronous on `stream` (0 = the null stream) and
+ *    returns before the GPU work finishes.  Host-checkable errors return
+ *    before anything is enqueued.  Problems only the device can see (e.g. a
+ *    decreasing cu_seqlens) set an error word in the workspace, make the
+ *    attention kernel do nothing, and are read back with lb_read_device_error.
+ *  - Supported shapes: d in {64, 128}; H % H_kv == 0 with H / H_kv in
+ *    {1, 2, 4, 8}.  Other shapes return LB_EUNSUPPORTED.
+ *  - Alignment: q, k, v, kv_chunk, out and out_* must be 16-byte aligned;
+ *    the workspace must be 256-byte aligned.
+ *  - No exception crosses this boundary; nothing here keeps state between
+ *    calls except a per-device cache of the compute-unit count.
+ */
+#ifndef LBATTN_H
+#define LBATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LB_OK = 0,
+  LB_EINVAL = 1,        /* null pointer, negative size, bad mask kind, H % H_kv != 0 */
+  LB_EUNSUPPORTED = 2,  /* shape outside what the kernels implement */
+  LB_EWORKSPACE = 3,    /* workspace too small or misaligned */
+  LB_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} lb_status;
+
+typedef enum {
+  LB_MASK_CAUSAL_DOC = 0,       /* key j visible to query i iff same segment and j <= i */
+  LB_MASK_SHARED_QUESTION = 1   /* segment 0 is a question, the rest are answers: an answer
+                                   sees the whole question and itself causally, never another
+                                   answer; the question sees itself causally */
+} lb_mask_kind;
+
+/* Device error word values (lb_read_device_error). */
+enum {
+  LB_DEVERR_NONE = 0,
+  LB_DEVERR_CU_SEQLENS = 1,   /* cu_seqlens[0] != 0, decreasing, or cu_seqlens[n_seg] != total_tokens */
+  LB_DEVERR_CAPACITY = 2,     /* more fragments or tiles than the workspace holds */
+  LB_DEVERR_SPANS = 4         /* a query run meets more than LB_MAX_SPANS key runs of its document */
+};
+
+#define LB_MAX_SPANS 4
+
+/* One tile of the plan, as lb_read_plan returns it (longest-first order). */
+typedef struct {
+  int32_t q_start;               /* first query row (index into the call's query rows) */
+  int32_t q_len;                 /* rows in the tile (<= lb_tile_rows) */
+  int32_t q_pos0;                /* mask position of the first row; row r has q_pos0 + r */
+  int32_t n_spans;               /* key spans that hold visible pairs, 0..LB_MAX_SPANS */
+  int64_t cost;                  /* exact visible (query, key) pairs of the tile, one head */
+  int32_t k_start[LB_MAX_SPANS]; /* first key row of each span */
+  int32_t k_len[LB_MAX_SPANS];   /* keys kept: those the tile's last row can see */
+  int32_t k_pos0[LB_MAX_SPANS];  /* mask position of the span's first key */
+  int32_t reserved[2];
+} lb_plan_tile;
+
+/* One persistent workgroup's record (lb_read_worker_timing). */
+typedef struct {
+  uint32_t hw_id;        /* raw HW_ID register of the workgroup's first wave */
+  uint32_t xcc_id;       /* raw XCC_ID register (accelerator complex die) */
+  uint64_t t_start;      /* 100 MHz device clock when the workgroup started */
+  uint64_t t_end;        /* ... and when it found the queue empty */
+  int64_t pairs;         /* visible pairs x heads of the items it ran */
+  int32_t items;         /* items it ran */
+  int32_t reserved;
+} lb_worker_record;
+
+/* Query rows per tile for this head configuration (256 / (H / H_kv)); -1 if unsupported. */
+int32_t lb_tile_rows(int32_t heads, int32_t kv_heads, int32_t d);
+
+/*
+ * Workspace bytes for calls of up to `max_tokens` query tokens (and, on the
+ * block path, key/value tokens) and up to `max_segments` segments (varlen) or
+ * runs of equal document id and consecutive position on either side (block).
+ * Returns 0 for invalid or unsupported arguments.  The workspace holds the
+ * plan and the per-workgroup records of the last call; it needs no clearing.
+ */
+size_t lb_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads);
+
+/*
+ * Varlen forward.
+ *   q          bf16 [total_tokens][heads][d]
+ *   k, v       bf16 [total_tokens][kv_heads][d]
+ *   cu_seqlens int32 [n_seg + 1], device; cu_seqlens[0] = 0, non-decreasing,
+ *              cu_seqlens[n_seg] = total_tokens (checked on the device)
+ *   mask_kind  lb_mask_kind
+ *   out        bf16 [total_tokens][heads][d] (written for every row)
+ *   lse        fp32 [heads][total_tokens]
+ *   workspace  >= lb_workspace_bytes(total_tokens, n_seg, heads, kv_heads)
+ * Every query sees at least itself, so every row gets a finite lse.
+ */
+lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
+                             int32_t d, int32_t mask_kind, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block attention of one context-parallel step.
+ *   q_shard    bf16 [n_q][heads][d]
+ *   kv_chunk   bf16 [2][n_kv][kv_heads][d]: all of K, then all of V
+ *   q_pos, kv_pos  int32 global positions of each token
+ *   q_doc, kv_doc  int32 document ids of each token
+ *   out        fp32 [n_q][heads][d]; rows with no visible key are not written
+ *   lse        fp32 [heads][n_q]; -inf for rows with no visible key
+ *   workspace  >= lb_workspace_bytes(max(n_q, n_kv), max_runs, heads, kv_heads),
+ *              max_runs bounding the runs of equal doc id and consecutive
+ *              position on either side (exceeding it: LB_DEVERR_CAPACITY)
+ * Key j is visible to query i iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i].
+ */
+lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,
+                            const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
+                            const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * In-place merge a <- merge(a, b) of two partials over disjoint key sets:
+ *   M = max(lse_a, lse_b), w_x = exp(lse_x - M),
+ *   lse_a = M + ln(w_a + w_b),  out_a = (w_a out_a + w_b out_b) / (w_a + w_b).
+ * Where lse_b = -inf, row a is left untouched and out_b is not read; where
+ * lse_a = -inf, out_a and lse_a are replaced by b's.
+ *   out_a, out_b  fp32 [n_rows][heads][d];  lse_a, lse_b  fp32 [heads][n_rows]
+ */
+lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const float* lse_b,
+                       int32_t n_rows, int32_t heads, int32_t d, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* lb_status_string(lb_status s);
+
+/* Synchronises `stream`, then copies the device error word of the last call that used
+   `workspace` into *host_err (LB_DEVERR_* bits). */
+lb_status lb_read_device_error(const void* workspace, size_t workspace_bytes, int32_t* host_err,
+                               hipStream_t stream);
+
+/* Synchronises `stream`, then copies the last call's plan: *n_tiles tiles in the order the
+   persistent kernel hands them out (longest first; ties in natural order).  At most
+   max_tiles are copied; *n_tiles is the full count. */
+lb_status lb_read_plan(const void* workspace, size_t workspace_bytes, lb_plan_tile* host_tiles,
+                       int32_t max_tiles, int32_t* n_tiles, hipStream_t stream);
+
+/* Synchronises `stream`, then copies one record per persistent workgroup of the last
+   attention launch (at most max_records; *n_records is the launch's count). */
+lb_status lb_read_worker_timing(const void* workspace, size_t workspace_bytes,
+                                lb_worker_record* host_records, int32_t max_records,
+                                int32_t* n_records, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBATTN_H */

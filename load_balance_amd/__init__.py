@@ -1,0 +1,208 @@
+"""MI355X-native document-masked varlen attention.
+
+Thin ctypes binding over ``liblbattn.so`` (C ABI in ``include/lbattn.h``):
+argument marshalling only -- every step of the computation runs in the HIP
+kernels.  torch supplies device memory and the current stream.  There is no
+CPU fallback: if the library is missing, every call raises.
+
+Python names match the C entry points without their ``lb_`` prefix:
+``varlen_attn_fwd``, ``block_attn_fwd``, ``lse_merge``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import zigzag  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblbattn.so")
+
+MASK_CAUSAL_DOC = 0
+MASK_SHARED_QUESTION = 1
+MAX_SPANS = 4
+
+DEVERR_CU_SEQLENS = 1
+DEVERR_CAPACITY = 2
+DEVERR_SPANS = 4
+
+
+class LBError(RuntimeError):
+    pass
+
+
+class PlanTile(ctypes.Structure):
+    _fields_ = [("q_start", ctypes.c_int32), ("q_len", ctypes.c_int32), ("q_pos0", ctypes.c_int32),
+                ("n_spans", ctypes.c_int32), ("cost", ctypes.c_int64),
+                ("k_start", ctypes.c_int32 * MAX_SPANS), ("k_len", ctypes.c_int32 * MAX_SPANS),
+                ("k_pos0", ctypes.c_int32 * MAX_SPANS), ("reserved", ctypes.c_int32 * 2)]
+
+
+class WorkerRecord(ctypes.Structure):
+    _fields_ = [("hw_id", ctypes.c_uint32), ("xcc_id", ctypes.c_uint32), ("t_start", ctypes.c_uint64),
+                ("t_end", ctypes.c_uint64), ("pairs", ctypes.c_int64), ("items", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LBError(f"{LIB_PATH} is missing: build it with `python -m load_balance_amd.build` "
+                      "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.lb_tile_rows.argtypes = [I32, I32, I32]
+    L.lb_tile_rows.restype = I32
+    L.lb_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    L.lb_workspace_bytes.restype = SZ
+    L.lb_varlen_attn_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_varlen_attn_fwd.restype = ctypes.c_int
+    L.lb_block_attn_fwd.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_block_attn_fwd.restype = ctypes.c_int
+    L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
+    L.lb_lse_merge.restype = ctypes.c_int
+    L.lb_status_string.argtypes = [ctypes.c_int]
+    L.lb_status_string.restype = ctypes.c_char_p
+    L.lb_read_device_error.argtypes = [P, SZ, ctypes.POINTER(I32), P]
+    L.lb_read_device_error.restype = ctypes.c_int
+    L.lb_read_plan.argtypes = [P, SZ, ctypes.POINTER(PlanTile), I32, ctypes.POINTER(I32), P]
+    L.lb_read_plan.restype = ctypes.c_int
+    L.lb_read_worker_timing.argtypes = [P, SZ, ctypes.POINTER(WorkerRecord), I32, ctypes.POINTER(I32), P]
+    L.lb_read_worker_timing.restype = ctypes.c_int
+    del I64
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().lb_status_string(status).decode()
+        raise LBError(f"{what}: {msg} (status {status})")
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def tile_rows(heads: int, kv_heads: int, d: int) -> int:
+    return int(lib().lb_tile_rows(heads, kv_heads, d))
+
+
+def workspace_bytes(max_tokens: int, max_segments: int, heads: int, kv_heads: int) -> int:
+    n = int(lib().lb_workspace_bytes(max_tokens, max_segments, heads, kv_heads))
+    if n == 0:
+        raise LBError("lb_workspace_bytes: invalid or unsupported arguments")
+    return n
+
+
+def new_workspace(max_tokens: int, max_segments: int, heads: int, kv_heads: int, device="cuda"):
+    """A uint8 device tensor sized for the given bounds (torch's allocator aligns to 256 B or more)."""
+    return torch.empty(workspace_bytes(max_tokens, max_segments, heads, kv_heads), dtype=torch.uint8,
+                       device=device)
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, out=None, lse=None, workspace=None,
+                    stream=None):
+    """out [T,H,d] bf16, lse [H,T] fp32 for q [T,H,d], k/v [T,H_kv,d] bf16 and int32 cu_seqlens."""
+    T, H, d = q.shape
+    Hkv = k.shape[1]
+    n_seg = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(T, max(1, n_seg), H, Hkv, q.device)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+    if cu_seqlens.dtype != torch.int32 or lse.dtype != torch.float32:
+        raise LBError("cu_seqlens must be int32 and lse float32")
+    st = lib().lb_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), n_seg, T, H, Hkv, d,
+                                  int(mask_kind), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(_stream(stream)))
+    _check(st, "lb_varlen_attn_fwd")
+    return out, lse
+
+
+def block_attn_fwd(q_shard, kv_chunk, q_pos, kv_pos, q_doc, kv_doc, out=None, lse=None, workspace=None,
+                   max_runs=None, stream=None):
+    """One ring step: q_shard [n_q,H,d] bf16 against kv_chunk [2,n_kv,H_kv,d] bf16 (K then V).
+
+    Returns out [n_q,H,d] fp32 (rows with no visible key left unwritten) and lse [H,n_q] fp32.
+    """
+    n_q, H, d = q_shard.shape
+    _, n_kv, Hkv, _ = kv_chunk.shape
+    if out is None:
+        out = torch.empty((n_q, H, d), dtype=torch.float32, device=q_shard.device)
+    if lse is None:
+        lse = torch.empty((H, n_q), dtype=torch.float32, device=q_shard.device)
+    if workspace is None:
+        runs = max_runs if max_runs is not None else max(n_q, n_kv, 1)
+        workspace = new_workspace(max(n_q, n_kv), runs, H, Hkv, q_shard.device)
+    for t, name in ((q_shard, "q_shard"), (kv_chunk, "kv_chunk")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+    for t, name in ((q_pos, "q_pos"), (kv_pos, "kv_pos"), (q_doc, "q_doc"), (kv_doc, "kv_doc")):
+        if t.dtype != torch.int32:
+            raise LBError(f"{name} must be int32")
+    st = lib().lb_block_attn_fwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(q_pos), _ptr(kv_pos),
+                                 _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel(), ctypes.c_void_p(_stream(stream)))
+    _check(st, "lb_block_attn_fwd")
+    return out, lse
+
+
+def lse_merge(out_a, lse_a, out_b, lse_b, stream=None):
+    """In place: (out_a, lse_a) <- merge((out_a, lse_a), (out_b, lse_b)).  fp32 [R,H,d] and [H,R]."""
+    R, H, d = out_a.shape
+    for t in (out_a, lse_a, out_b, lse_b):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise LBError("lse_merge takes contiguous float32 tensors")
+    st = lib().lb_lse_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), R, H, d,
+                            ctypes.c_void_p(_stream(stream)))
+    _check(st, "lb_lse_merge")
+    return out_a, lse_a
+
+
+def read_device_error(workspace, stream=None) -> int:
+    err = ctypes.c_int32(0)
+    _check(lib().lb_read_device_error(_ptr(workspace), workspace.numel(), ctypes.byref(err),
+                                      ctypes.c_void_p(_stream(stream))), "lb_read_device_error")
+    return err.value
+
+
+def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
+    """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost)."""
+    buf = (PlanTile * max_tiles)()
+    n = ctypes.c_int32(0)
+    _check(lib().lb_read_plan(_ptr(workspace), workspace.numel(), buf, max_tiles, ctypes.byref(n),
+                              ctypes.c_void_p(_stream(stream))), "lb_read_plan")
+    out = []
+    for i in range(min(n.value, max_tiles)):
+        t = buf[i]
+        spans = [(t.k_start[s], t.k_len[s], t.k_pos0[s]) for s in range(t.n_spans)]
+        out.append(dict(q_start=t.q_start, q_len=t.q_len, q_pos0=t.q_pos0, spans=spans, cost=t.cost))
+    return out
+
+
+def read_worker_timing(workspace, max_records: int = 4096, stream=None):
+    buf = (WorkerRecord * max_records)()
+    n = ctypes.c_int32(0)
+    _check(lib().lb_read_worker_timing(_ptr(workspace), workspace.numel(), buf, max_records, ctypes.byref(n),
+                                       ctypes.c_void_p(_stream(stream))), "lb_read_worker_timing")
+    return [dict(hw_id=r.hw_id, xcc_id=r.xcc_id, t_start=r.t_start, t_end=r.t_end, pairs=r.pairs,
+                 items=r.items) for r in buf[:min(n.value, max_records)]]

@@ -1,0 +1,262 @@
+// Host side of the C ABI declared in include/lbattn.h: argument checks,
+// workspace carving, launch configuration and read-back helpers.  Every
+// check that the host can make happens before anything is enqueued.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <vector>
+
+#include "lbattn_internal.h"
+
+using namespace lb;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_workers[kMaxDevices];  // persistent workgroups per device (0 = unknown)
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool group_supported(int32_t heads, int32_t kv_heads) {
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return false;
+  const int g = heads / kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Persistent grid size: resident workgroups of the attention kernel on the current device.
+lb_status persistent_workers(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LB_EHIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_workers[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return LB_OK;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return LB_EHIP;
+  // one 512-thread workgroup per compute unit: 71.7 KB of LDS and ~2 waves per SIMD of registers
+  const int n = std::min(cus, kMaxWorkers);
+  if (dev >= 0 && dev < kMaxDevices) g_workers[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return LB_OK;
+}
+
+lb_status launch_forward(const PlanArgs& p, AttnArgs at, int d, bool out_f32, hipStream_t stream) {
+  int workers = 0;
+  lb_status st = persistent_workers(&workers);
+  if (st != LB_OK) return st;
+  if (launch_plan(p, stream) != hipSuccess) return LB_EHIP;
+  if (launch_attention(at, d, out_f32, workers, stream) != hipSuccess) return LB_EHIP;
+  return LB_OK;
+}
+
+bool read_header(const void* ws, size_t bytes, WsHeader* h, hipStream_t s) {
+  if (!ws || bytes < sizeof(WsHeader)) return false;
+  if (hipStreamSynchronize(s) != hipSuccess) return false;
+  return hipMemcpy(h, ws, sizeof(WsHeader), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lb_tile_rows(int32_t heads, int32_t kv_heads, int32_t d) {
+  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return -1;
+  return tile_rows_for_group(heads / kv_heads);
+}
+
+size_t lb_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads) {
+  if (max_tokens < 0 || max_segments < 1 || !group_supported(heads, kv_heads)) return 0;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  const int64_t tiles = std::min<int64_t>(kSortCap, ceil_div(max_tokens, bm) + max_segments);
+  return (size_t)ws_layout(max_segments, tiles).total;
+}
+
+lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
+                             int32_t d, int32_t mask_kind, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !cu_seqlens || !out || !lse || !workspace) return LB_EINVAL;
+  if (n_seg < 1 || total_tokens < 0) return LB_EINVAL;
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return LB_EINVAL;
+  if (mask_kind != LB_MASK_CAUSAL_DOC && mask_kind != LB_MASK_SHARED_QUESTION) return LB_EINVAL;
+  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return LB_EUNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens, 4))
+    return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  const int64_t tiles = ceil_div(total_tokens, bm) + n_seg;
+  if (tiles > kSortCap) return LB_EUNSUPPORTED;
+  const WsLayout L = ws_layout(n_seg, tiles);
+  if ((int64_t)workspace_bytes < L.total) return LB_EWORKSPACE;
+  if (total_tokens == 0) return LB_OK;
+
+  PlanArgs p{};
+  p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
+  p.cu_seqlens = cu_seqlens;
+  p.n_seg = n_seg;
+  p.total_tokens = total_tokens;
+  p.tile_rows = bm;
+  p.kv_heads = kv_heads;
+  p.ws = static_cast<char*>(workspace);
+  p.L = L;
+
+  AttnArgs at{};
+  at.q = q; at.k = k; at.v = v;
+  at.out = out;
+  at.lse = lse;
+  at.n_q = total_tokens;
+  at.n_kv = total_tokens;
+  at.heads = heads;
+  at.kv_heads = kv_heads;
+  at.group = heads / kv_heads;
+  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  at.ws = static_cast<char*>(workspace);
+  at.off_tiles = L.off_tiles;
+  at.off_order = L.off_order;
+  at.off_workers = L.off_workers;
+  return launch_forward(p, at, d, /*out_f32=*/false, stream);
+}
+
+lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,
+                            const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
+                            const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
+  if (!q_shard || !q_pos || !q_doc || !out || !lse || !workspace) return LB_EINVAL;
+  if (n_kv > 0 && (!kv_chunk || !kv_pos || !kv_doc)) return LB_EINVAL;
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return LB_EINVAL;
+  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return LB_EUNSUPPORTED;
+  if (!aligned(q_shard, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(q_pos, 4) || !aligned(q_doc, 4))
+    return LB_EINVAL;
+  if (n_kv > 0 && (!aligned(kv_chunk, 16) || !aligned(kv_pos, 4) || !aligned(kv_doc, 4))) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  // Runs are unknown to the host: take the largest fragment capacity the workspace holds.
+  const int64_t max_runs = std::max<int64_t>(1, std::max(n_q, n_kv));
+  auto layout_for = [&](int64_t f) {
+    return ws_layout(f, std::min<int64_t>(kSortCap, ceil_div(n_q, bm) + f));
+  };
+  if ((int64_t)workspace_bytes < layout_for(1).total) return LB_EWORKSPACE;
+  int64_t lo = 1, hi = max_runs;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (layout_for(mid).total <= (int64_t)workspace_bytes) lo = mid; else hi = mid - 1;
+  }
+  const WsLayout L = layout_for(lo);
+  if (n_q == 0) return LB_OK;
+
+  PlanArgs p{};
+  p.mode = kPlanBlock;
+  p.q_pos = q_pos; p.q_doc = q_doc; p.kv_pos = kv_pos; p.kv_doc = kv_doc;
+  p.n_q = n_q;
+  p.n_kv = n_kv;
+  p.tile_rows = bm;
+  p.kv_heads = kv_heads;
+  p.ws = static_cast<char*>(workspace);
+  p.L = L;
+
+  const __bf16* kbase = static_cast<const __bf16*>(n_kv > 0 ? kv_chunk : q_shard);
+  AttnArgs at{};
+  at.q = q_shard;
+  at.k = kbase;
+  at.v = n_kv > 0 ? kbase + (int64_t)n_kv * kv_heads * d : kbase;
+  at.out = out;
+  at.lse = lse;
+  at.n_q = n_q;
+  at.n_kv = n_kv;
+  at.heads = heads;
+  at.kv_heads = kv_heads;
+  at.group = heads / kv_heads;
+  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  at.ws = static_cast<char*>(workspace);
+  at.off_tiles = L.off_tiles;
+  at.off_order = L.off_order;
+  at.off_workers = L.off_workers;
+  return launch_forward(p, at, d, /*out_f32=*/true, stream);
+}
+
+lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const float* lse_b, int32_t n_rows,
+                       int32_t heads, int32_t d, hipStream_t stream) {
+  if (!out_a || !lse_a || !out_b || !lse_b) return LB_EINVAL;
+  if (n_rows < 0 || heads <= 0 || d <= 0) return LB_EINVAL;
+  if (d % 4 != 0 || d > 1024) return LB_EUNSUPPORTED;
+  if (!aligned(out_a, 16) || !aligned(out_b, 16) || !aligned(lse_a, 4) || !aligned(lse_b, 4)) return LB_EINVAL;
+  if (n_rows == 0) return LB_OK;
+  MergeArgs m{out_a, lse_a, out_b, lse_b, n_rows, heads, d};
+  return launch_lse_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+const char* lb_status_string(lb_status s) {
+  switch (s) {
+    case LB_OK: return "ok";
+    case LB_EINVAL: return "invalid argument";
+    case LB_EUNSUPPORTED: return "unsupported shape";
+    case LB_EWORKSPACE: return "workspace too small or misaligned";
+    case LB_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+lb_status lb_read_device_error(const void* workspace, size_t workspace_bytes, int32_t* host_err,
+                               hipStream_t stream) {
+  if (!host_err) return LB_EINVAL;
+  WsHeader h;
+  if (!workspace || workspace_bytes < sizeof(WsHeader)) return LB_EWORKSPACE;
+  if (!read_header(workspace, workspace_bytes, &h, stream)) return LB_EHIP;
+  *host_err = h.err;
+  return LB_OK;
+}
+
+lb_status lb_read_plan(const void* workspace, size_t workspace_bytes, lb_plan_tile* host_tiles,
+                       int32_t max_tiles, int32_t* n_tiles, hipStream_t stream) {
+  if (!n_tiles || (max_tiles > 0 && !host_tiles) || max_tiles < 0) return LB_EINVAL;
+  WsHeader h;
+  if (!workspace || workspace_bytes < sizeof(WsHeader)) return LB_EWORKSPACE;
+  if (!read_header(workspace, workspace_bytes, &h, stream)) return LB_EHIP;
+  *n_tiles = h.n_tiles;
+  const int n = std::min(h.n_tiles, max_tiles);
+  if (n <= 0) return LB_OK;
+  if (h.off_order + (int64_t)h.n_tiles * 4 > (int64_t)workspace_bytes ||
+      h.off_tiles + (int64_t)h.n_tiles * (int64_t)sizeof(lb_plan_tile) > (int64_t)workspace_bytes)
+    return LB_EWORKSPACE;
+  std::vector<int32_t> order(h.n_tiles);
+  std::vector<lb_plan_tile> nat(h.n_tiles);
+  const char* base = static_cast<const char*>(workspace);
+  if (hipMemcpy(order.data(), base + h.off_order, order.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(nat.data(), base + h.off_tiles, nat.size() * sizeof(lb_plan_tile), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return LB_EHIP;
+  for (int i = 0; i < n; ++i) {
+    const int32_t j = order[i];
+    if (j < 0 || j >= h.n_tiles) return LB_EHIP;
+    host_tiles[i] = nat[j];
+  }
+  return LB_OK;
+}
+
+lb_status lb_read_worker_timing(const void* workspace, size_t workspace_bytes, lb_worker_record* host_records,
+                                int32_t max_records, int32_t* n_records, hipStream_t stream) {
+  if (!n_records || (max_records > 0 && !host_records) || max_records < 0) return LB_EINVAL;
+  WsHeader h;
+  if (!workspace || workspace_bytes < sizeof(WsHeader)) return LB_EWORKSPACE;
+  if (!read_header(workspace, workspace_bytes, &h, stream)) return LB_EHIP;
+  *n_records = h.n_workers;
+  const int n = std::min(h.n_workers, max_records);
+  if (n <= 0) return LB_OK;
+  if (h.off_workers + (int64_t)n * (int64_t)sizeof(lb_worker_record) > (int64_t)workspace_bytes)
+    return LB_EWORKSPACE;
+  if (hipMemcpy(host_records, static_cast<const char*>(workspace) + h.off_workers,
+                n * sizeof(lb_worker_record), hipMemcpyDeviceToHost) != hipSuccess)
+    return LB_EHIP;
+  return LB_OK;
+}
+
+}  // extern "C"

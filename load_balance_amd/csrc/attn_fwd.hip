@@ -1,0 +1,352 @@
+// Persistent masked attention forward for gfx950 (MI355X).
+//
+// Work items are (tile, key/value head) pairs taken from the longest-first
+// queue the planning kernel wrote: every workgroup loops "pop the next item,
+// run it", so an idle compute unit always takes the largest remaining item --
+// LPT list scheduling ("03 · 长文负载均衡", section 2.1, VRSP's LPT placement;
+// "数据并行负载均衡", section 4.4, the greedy first phase), done at run time
+// rather than from a static assignment because equal FLOPs do not take equal
+// time on every device (same page, section 2.1: 256 identical GPUs differ by
+// about 7%).
+//
+// Per item the workgroup runs blocked attention with online softmax (the
+// FlashAttention prerequisite of "长序列训练与上下文并行"): key/value blocks of
+// 64 tokens go through LDS; each of the 8 waves owns 32 query rows of one of
+// the G = H/H_kv query heads that share the key/value head, so one K/V load
+// serves G heads.  Both products run on bf16 MFMA (v_mfma_f32_32x32x16_bf16)
+// with fp32 accumulation, in transposed form so that no register transpose is
+// needed:
+//   S^T[key][q] = K . Q^T    A = K rows from LDS, B = Q held in registers
+//   O^T[d][q]  += V^T . P^T  A = V^T rows from LDS, B = P^T straight from S^T
+// A lane of the 32x32 accumulator owns one query column (q = lane % 32), so
+// row max / row sum are per-lane loops plus one exchange with lane ^ 32, and
+// the rescale of O is a per-lane scalar.  Exponentials use exp2 with the
+// softmax scale folded into one FMA.  The running maximum is only moved when
+// it grows by more than 2^8 in the exp2 domain, which keeps every exp2 <= 256
+// (safe in fp32/bf16) and skips almost all rescales of O.
+//
+// Masking is decided per (wave, key block): blocks entirely above the wave's
+// diagonal are skipped, blocks entirely visible take the mask-free path, only
+// diagonal and ragged blocks evaluate "key position <= query position" per
+// element.
+#include "lbattn_internal.h"
+
+namespace lb {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = kBlockN;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int D>
+struct Lds {
+  static constexpr int kStride = D * 2 + 16;   // bytes per key row of K (16 B pad: conflict-free b128 reads)
+  static constexpr int vStride = BN * 2 + 16;  // bytes per d row of V^T
+  static constexpr int kBytes = BN * kStride;
+  static constexpr int vBytes = D * vStride;
+  static constexpr int stage = kBytes + vBytes;
+  static constexpr int kChunks = BN * D / 8;          // 16-byte pieces of a K block
+  static constexpr int kPerThread = kChunks / kThreads;
+  static constexpr int vUnits = (BN / 2) * (D / 8);  // (key pair, 8-wide d chunk) units of a V block
+};
+
+// V^T keeps keys permuted inside each group of 16 so that the 8 keys one lane feeds to
+// the PV product are contiguous: swap bits 2 and 3 of the key index.
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+__device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+// s_getreg immediates: (size - 1) << 11 | offset << 6 | register id.
+__device__ __forceinline__ uint32_t hw_id_reg() { return __builtin_amdgcn_s_getreg((31 << 11) | 4); }
+__device__ __forceinline__ uint32_t xcc_id_reg() { return __builtin_amdgcn_s_getreg((15 << 11) | 20); }
+
+template <int D>
+struct KvLoader {
+  u32x4 kreg[Lds<D>::kPerThread];
+  u32x4 vreg[2];
+
+  // Loads key block [k0, k0 + BN) of a span into registers; rows at or past `valid` read as zero.
+  __device__ __forceinline__ void load(const __bf16* __restrict__ K, const __bf16* __restrict__ V, int k0,
+                                       int valid, int kv_heads, int g, int tid) {
+#pragma unroll
+    for (int e = 0; e < Lds<D>::kPerThread; ++e) {
+      const int c = tid + e * kThreads;
+      const int row = c / (D / 8), ch = c % (D / 8);
+      kreg[e] = u32x4{0, 0, 0, 0};
+      if (row < valid)
+        kreg[e] = *reinterpret_cast<const u32x4*>(K + ((int64_t)(k0 + row) * kv_heads + g) * D + ch * 8);
+    }
+    if (tid < Lds<D>::vUnits) {
+      const int p = tid % (BN / 2), ch = tid / (BN / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 2 * p + e;
+        vreg[e] = u32x4{0, 0, 0, 0};
+        if (row < valid)
+          vreg[e] = *reinterpret_cast<const u32x4*>(V + ((int64_t)(k0 + row) * kv_heads + g) * D + ch * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* stage, int tid) {
+    char* ks = stage;
+    char* vs = stage + Lds<D>::kBytes;
+#pragma unroll
+    for (int e = 0; e < Lds<D>::kPerThread; ++e) {
+      const int c = tid + e * kThreads;
+      const int row = c / (D / 8), ch = c % (D / 8);
+      *reinterpret_cast<u32x4*>(ks + row * Lds<D>::kStride + ch * 16) = kreg[e];
+    }
+    if (tid < Lds<D>::vUnits) {
+      const int p = tid % (BN / 2), ch = tid / (BN / 2);
+      const int col = vt_pos(2 * p) * 2;  // byte offset of the key pair inside a V^T row
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t x0 = vreg[0][m], x1 = vreg[1][m];
+        const uint32_t lo = (x0 & 0xFFFFu) | (x1 << 16);          // d = ch*8 + 2m
+        const uint32_t hi = (x0 >> 16) | (x1 & 0xFFFF0000u);      // d = ch*8 + 2m + 1
+        *reinterpret_cast<uint32_t*>(vs + (ch * 8 + 2 * m) * Lds<D>::vStride + col) = lo;
+        *reinterpret_cast<uint32_t*>(vs + (ch * 8 + 2 * m + 1) * Lds<D>::vStride + col) = hi;
+      }
+    }
+  }
+};
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * Lds<D>::stage];
+  __shared__ int s_item;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
+  const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + a.off_tiles);
+  const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.off_order);
+  const int n_items = hdr->n_items;
+
+  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
+
+  const int G = a.group;
+  const int head_in_group = wave % G;
+  const int wr0 = (wave / G) * kRowsPerWave;  // first tile row of this wave
+  const float c = a.scale_log2;
+
+  uint64_t t_start = 0;
+  if (tid == 0) t_start = device_clock();
+  int my_items = 0;
+  int64_t my_pairs = 0;
+
+  KvLoader<D> ld;
+
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(&hdr->queue_head, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (item >= n_items) break;
+
+    const int g = item % a.kv_heads;
+    const lb_plan_tile* T = &tiles[order[item / a.kv_heads]];
+    const int q_start = T->q_start, q_len = T->q_len, q_pos0 = T->q_pos0;
+    const int n_spans = T->n_spans;
+    int n_kv_tiles = 0;
+    for (int s = 0; s < n_spans; ++s) n_kv_tiles += (T->k_len[s] + BN - 1) / BN;
+    if (tid == 0) {
+      ++my_items;
+      my_pairs += T->cost * G;
+    }
+
+    const int head = g * G + head_in_group;
+    const int my_row = wr0 + l32;                 // tile row owned by this lane
+    const bool wave_rows = wr0 < q_len;           // this wave has at least one real row
+    const int wave_last = min(wr0 + kRowsPerWave, q_len) - 1;
+    const int64_t grow = (int64_t)q_start + my_row;
+
+    // Q fragment: B operand of S^T = K Q^T; lane holds Q[q = l32][d = kk*16 + hh*8 .. +8].
+    bf16x8 qreg[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (wave_rows && my_row < q_len)
+        x = *reinterpret_cast<const u32x4*>(Q + (grow * a.heads + head) * D + kk * 16 + hh * 8);
+      qreg[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    f32x16 acc_o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
+    float m_used = -__builtin_inff();
+    float l_part = 0.f;
+
+    // prologue: first key block into stage 0 (spans with zero keys never reach the plan)
+    int cur_s = 0, cur_t = 0;
+    if (n_kv_tiles > 0) {
+      ld.load(K, V, T->k_start[0], T->k_len[0], a.kv_heads, g, tid);
+      ld.store(smem, tid);
+    }
+
+    for (int it = 0; it < n_kv_tiles; ++it) {
+      __syncthreads();
+      // the block computed now (span cur_s, block cur_t) and the one loaded next
+      const int s_len = T->k_len[cur_s], s_pos0 = T->k_pos0[cur_s];
+      const int kt = cur_t;
+      int nx_s = cur_s, nx_t = cur_t + 1;
+      if (nx_t * BN >= s_len) { ++nx_s; nx_t = 0; }
+      const bool has_next = it + 1 < n_kv_tiles;
+      if (has_next) {
+        const int k0 = T->k_start[nx_s] + nx_t * BN;
+        ld.load(K, V, k0, T->k_len[nx_s] - nx_t * BN, a.kv_heads, g, tid);
+      }
+      const char* ks = smem + (it & 1) * Lds<D>::stage;
+      const char* vs = ks + Lds<D>::kBytes;
+
+      const int key0 = kt * BN;                     // first key of the block, relative to the span
+      const int kpos_first = s_pos0 + key0;
+      const int kpos_last = kpos_first + BN - 1;
+      const bool skip = !wave_rows || kpos_first > q_pos0 + wave_last;
+      if (!skip) {
+        const bool full = key0 + BN <= s_len && kpos_last <= q_pos0 + wr0;
+        // ---- S^T = K Q^T ----
+        f32x16 acc_s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          acc_s[kb] = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 kf =
+                *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds<D>::kStride + (kk * 16 + hh * 8) * 2);
+            acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], acc_s[kb], 0, 0, 0);
+          }
+        }
+        // ---- mask (diagonal / ragged blocks only) ----
+        if (!full) {
+          const int qpos = q_pos0 + my_row;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + kb * 32 + (i / 4) * 8 + hh * 4 + (i % 4);
+              const bool vis = key < s_len && s_pos0 + key <= qpos;
+              if (!vis) acc_s[kb][i] = -__builtin_inff();
+            }
+        }
+        // ---- online softmax ----
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_tile = mx * c;
+        const bool need = m_tile > m_used + kRescaleThreshold;  // false when the row saw nothing
+        if (__any(need)) {
+          const float m_new = need ? m_tile : m_used;
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.0f;
+          m_used = m_new;
+          l_part *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+        }
+        const float m_sub = m_used == -__builtin_inff() ? 0.0f : m_used;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j], c, -m_sub));
+              l_part += p;
+              pf[kb * 2 + cc][j] = (__bf16)p;
+            }
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int ks16 = 0; ks16 < 4; ++ks16) {
+            const bf16x8 vf =
+                *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
+            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks16], acc_o[db], 0, 0, 0);
+          }
+      }
+      if (has_next) ld.store(smem + ((it + 1) & 1) * Lds<D>::stage, tid);
+      cur_s = nx_s;
+      cur_t = nx_t;
+    }
+
+    // ---- epilogue: out = O / l, lse = ln(sum exp) ----
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    if (wave_rows && my_row < q_len) {
+      const bool empty = !(l_tot > 0.0f);
+      const float lse = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
+      if (hh == 0) a.lse[(int64_t)head * a.n_q + grow] = lse;
+      if (!empty) {
+        const float inv = 1.0f / l_tot;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d0 = db * 32 + r * 8 + hh * 4;
+            const int64_t off = (grow * a.heads + head) * D + d0;
+            if constexpr (OUT_F32) {
+              f32x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = acc_o[db][r * 4 + e] * inv;
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = o;
+            } else {
+              bf16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc_o[db][r * 4 + e] * inv);
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.out) + off) = o;
+            }
+          }
+      }
+    }
+  }
+
+  if (tid == 0) {
+    lb_worker_record rec;
+    rec.hw_id = hw_id_reg();
+    rec.xcc_id = xcc_id_reg();
+    rec.t_start = t_start;
+    rec.t_end = device_clock();
+    rec.pairs = my_pairs;
+    rec.items = my_items;
+    rec.reserved = 0;
+    lb_worker_record* recs = reinterpret_cast<lb_worker_record*>(a.ws + a.off_workers);
+    recs[blockIdx.x] = rec;
+    if (blockIdx.x == 0) hdr->n_workers = gridDim.x;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
+  dim3 grid(n_workers), block(kThreads);
+  if (d == 128) {
+    if (out_f32) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lb

@@ -1,0 +1,123 @@
+// Internal definitions shared by the host library (api.cpp) and the gfx950
+// kernels: workspace layout, the plan's device records, launcher entry points.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/lbattn.h"
+
+namespace lb {
+
+// Persistent attention kernel geometry: 8 waves of 64 lanes per workgroup, each
+// wave owning 32 query rows of one head; a tile serves G = H / H_kv heads, so it
+// holds 32 * 8 / G query rows.  Keys stream through LDS in blocks of 64.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;
+constexpr int kBlockN = 64;
+
+// Planning kernel: one workgroup sorts the tile keys in LDS.
+constexpr int kPlanThreads = 1024;
+constexpr int kSortCap = 16384;     // tiles per call
+constexpr int kMaxWorkers = 2048;   // persistent workgroups per launch
+
+inline __host__ __device__ int tile_rows_for_group(int group) { return kRowsPerWave * kWaves / group; }
+
+// Workspace header, at offset 0.  Written by the planning kernel, read by the
+// attention kernel and by the host read-back calls.
+struct WsHeader {
+  int32_t err;          // LB_DEVERR_* bits
+  int32_t n_frags;      // query fragments
+  int32_t n_tiles;
+  int32_t n_items;      // n_tiles * kv_heads (0 after an error)
+  int32_t queue_head;   // next item to hand out
+  int32_t n_kvruns;
+  int32_t tile_rows;
+  int32_t n_workers;    // persistent workgroups of the last attention launch
+  int64_t off_frags, off_kvruns, off_tiles, off_order, off_workers;
+  int32_t cap_frags, cap_tiles;
+  int64_t total_pairs;  // sum of tile costs (one head)
+  int32_t pad[10];
+};
+static_assert(sizeof(WsHeader) <= 256, "header must fit its slot");
+
+// A query fragment with its key spans before per-tile clipping.
+struct Frag {
+  int32_t q_start, q_len, q_pos0, n_spans;
+  int32_t k_start[LB_MAX_SPANS], k_len[LB_MAX_SPANS], k_pos0[LB_MAX_SPANS];
+};
+static_assert(sizeof(Frag) == 64, "");
+
+// A key/value run (block path): equal document id, consecutive positions.
+struct KvRun {
+  int32_t start, len, pos0, doc;
+};
+
+static_assert(sizeof(lb_plan_tile) == 80, "lb_plan_tile layout");
+static_assert(sizeof(lb_worker_record) == 40, "lb_worker_record layout");
+
+struct WsLayout {
+  int64_t off_frags, off_ftile, off_kvruns, off_tiles, off_order, off_workers, total;
+  int32_t cap_frags, cap_tiles;
+};
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+inline WsLayout ws_layout(int64_t cap_frags, int64_t cap_tiles) {
+  WsLayout L{};
+  int64_t o = 256;
+  L.off_frags = o;   o = align256(o + cap_frags * (int64_t)sizeof(Frag));
+  L.off_ftile = o;   o = align256(o + (cap_frags + 1) * (int64_t)sizeof(int32_t));
+  L.off_kvruns = o;  o = align256(o + cap_frags * (int64_t)sizeof(KvRun));
+  L.off_tiles = o;   o = align256(o + cap_tiles * (int64_t)sizeof(lb_plan_tile));
+  L.off_order = o;   o = align256(o + cap_tiles * (int64_t)sizeof(int32_t));
+  L.off_workers = o; o = align256(o + kMaxWorkers * (int64_t)sizeof(lb_worker_record));
+  L.total = o;
+  L.cap_frags = (int32_t)cap_frags;
+  L.cap_tiles = (int32_t)cap_tiles;
+  return L;
+}
+
+enum PlanMode { kPlanCausalDoc = 0, kPlanSharedQuestion = 1, kPlanBlock = 2 };
+
+struct PlanArgs {
+  int32_t mode;
+  const int32_t* cu_seqlens;
+  int32_t n_seg, total_tokens;
+  const int32_t *q_pos, *q_doc, *kv_pos, *kv_doc;
+  int32_t n_q, n_kv;
+  int32_t tile_rows, kv_heads;
+  char* ws;
+  WsLayout L;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int32_t n_q, n_kv;
+  int32_t heads, kv_heads, group;
+  float scale_log2;  // softmax scale * log2(e)
+  char* ws;
+  int64_t off_tiles, off_order, off_workers;
+};
+
+struct MergeArgs {
+  float* out_a;
+  float* lse_a;
+  const float* out_b;
+  const float* lse_b;
+  int32_t n_rows, heads, d;
+};
+
+// Launchers, one per translation unit; each returns the launch's hipError_t.
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace lb

@@ -1,0 +1,291 @@
+// Planning kernel: turns cu_seqlens (or per-token positions and document ids)
+// into the longest-first queue of attention tiles.
+//
+// Only (query tile, key span) pairs holding visible pairs become work
+// ("03 · 长文负载均衡", section 3.2: DCP generates computation blocks only for
+// block pairs whose mask is not all zero), masks are described as rectangles
+// of full or causal kind (section 4.4, MagiAttention's AttnSlice), each tile
+// is billed its exact number of visible (query, key) pairs (section 3.2,
+// Libra TAP), and tiles are handed out largest first (section 2.1, VRSP's
+// LPT placement; "数据并行负载均衡", section 4.4).
+//
+// One workgroup of 1024 threads does everything: the metadata is a few
+// thousand integers, far below what a multi-workgroup launch would pay off.
+//   1. fragments: one per segment (varlen) or per run of equal document id and
+//      consecutive position (block path); spans = keys the fragment may see.
+//   2. tiles: each fragment cut into `tile_rows` rows from its start; spans
+//      clipped to what the tile's last row sees; cost in closed form.
+//   3. order: bitonic sort of (cost descending, natural index) keys in LDS.
+// The plan lands in the caller's workspace; the attention kernel reads it.
+#include "lbattn_internal.h"
+
+namespace lb {
+namespace {
+
+constexpr int NT = kPlanThreads;
+constexpr uint64_t kCostMask = (uint64_t(1) << 40) - 1;  // costs < 2^40 (checked on the host)
+
+struct PlanShared {
+  uint64_t keys[kSortCap];
+  int32_t scan[NT];
+  int32_t err;
+  unsigned long long pairs;
+};
+
+// Exclusive prefix sum of one value per thread across the workgroup.
+__device__ int block_excl_scan(int v, int32_t* s, int* total) {
+  const int tid = threadIdx.x;
+  s[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int x = tid >= off ? s[tid - off] : 0;
+    __syncthreads();
+    s[tid] += x;
+    __syncthreads();
+  }
+  const int incl = s[tid];
+  *total = s[NT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Sum over integers y < x of clamp(y, 0, L).
+__device__ int64_t clamp_prefix(int64_t x, int64_t L) {
+  const int64_t m = x - 1;
+  if (m <= 0) return 0;
+  if (m <= L) return m * (m + 1) / 2;
+  return L * (L + 1) / 2 + (m - L) * L;
+}
+
+// Visible pairs between n consecutive query positions p0.. and one span
+// (keys at positions kp0 .. kp0 + L - 1, key visible iff its position <= the query's).
+__device__ int64_t span_pairs(int64_t p0, int64_t n, int64_t kp0, int64_t L) {
+  const int64_t a = p0 - kp0 + 1;  // keys the first row sees, before clamping
+  return clamp_prefix(a + n, L) - clamp_prefix(a, L);
+}
+
+__device__ bool run_start(const int32_t* pos, const int32_t* doc, int i) {
+  return i == 0 || doc[i] != doc[i - 1] || pos[i] != pos[i - 1] + 1;
+}
+
+// Marks run starts of (pos, doc) and writes their indices to starts[]; returns the count.
+__device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap, int32_t* starts,
+                         int stride_ints, PlanShared& sh) {
+  const int tid = threadIdx.x;
+  const int per = (n + NT - 1) / NT;
+  const int b = min(n, tid * per), e = min(n, b + per);
+  int cnt = 0;
+  for (int i = b; i < e; ++i) cnt += run_start(pos, doc, i);
+  int total;
+  int off = block_excl_scan(cnt, sh.scan, &total);
+  if (total > cap) {
+    if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
+    return 0;
+  }
+  for (int i = b; i < e; ++i)
+    if (run_start(pos, doc, i)) starts[(int64_t)(off++) * stride_ints] = i;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
+  __shared__ PlanShared sh;
+  const int tid = threadIdx.x;
+  char* ws = a.ws;
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  Frag* frags = reinterpret_cast<Frag*>(ws + a.L.off_frags);
+  int32_t* ftile = reinterpret_cast<int32_t*>(ws + a.L.off_ftile);
+  KvRun* kvr = reinterpret_cast<KvRun*>(ws + a.L.off_kvruns);
+  lb_plan_tile* tiles = reinterpret_cast<lb_plan_tile*>(ws + a.L.off_tiles);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + a.L.off_order);
+
+  if (tid == 0) {
+    sh.err = 0;
+    sh.pairs = 0;
+  }
+  __syncthreads();
+
+  // ---- 1. fragments and their spans -------------------------------------------------
+  int n_frags = 0, n_kvruns = 0;
+  if (a.mode == kPlanCausalDoc || a.mode == kPlanSharedQuestion) {
+    const int32_t* cu = a.cu_seqlens;
+    for (int i = tid; i <= a.n_seg; i += NT) {
+      const int c = cu[i];
+      bool bad = (i == 0 && c != 0) || (i > 0 && c < cu[i - 1]) || (i == a.n_seg && c != a.total_tokens);
+      if (bad) atomicOr(&sh.err, LB_DEVERR_CU_SEQLENS);
+    }
+    __syncthreads();
+    n_frags = a.n_seg;
+    if (sh.err == 0) {
+      const int Q = cu[1] - cu[0];
+      for (int s = tid; s < n_frags; s += NT) {
+        Frag f{};
+        f.q_start = cu[s];
+        f.q_len = cu[s + 1] - cu[s];
+        if (a.mode == kPlanCausalDoc) {
+          f.q_pos0 = 0;
+          f.n_spans = 1;
+          f.k_start[0] = f.q_start; f.k_len[0] = f.q_len; f.k_pos0[0] = 0;
+        } else if (s == 0) {  // the question: causal on itself
+          f.q_pos0 = 0;
+          f.n_spans = 1;
+          f.k_start[0] = cu[0]; f.k_len[0] = Q; f.k_pos0[0] = 0;
+        } else {  // an answer: positions continue after the question
+          f.q_pos0 = Q;
+          int ns = 0;
+          if (Q > 0) { f.k_start[ns] = cu[0]; f.k_len[ns] = Q; f.k_pos0[ns] = 0; ++ns; }
+          f.k_start[ns] = f.q_start; f.k_len[ns] = f.q_len; f.k_pos0[ns] = Q; ++ns;
+          f.n_spans = ns;
+        }
+        frags[s] = f;
+      }
+    }
+  } else {  // block path: runs of equal doc id and consecutive position
+    n_frags = find_runs(a.q_pos, a.q_doc, a.n_q, a.L.cap_frags, &frags[0].q_start, sizeof(Frag) / 4, sh);
+    n_kvruns = find_runs(a.kv_pos, a.kv_doc, a.n_kv, a.L.cap_frags, &kvr[0].start, sizeof(KvRun) / 4, sh);
+    if (sh.err == 0) {
+      for (int r = tid; r < n_kvruns; r += NT) {
+        const int s = kvr[r].start;
+        const int e = r + 1 < n_kvruns ? kvr[r + 1].start : a.n_kv;
+        kvr[r].len = e - s;
+        kvr[r].pos0 = a.kv_pos[s];
+        kvr[r].doc = a.kv_doc[s];
+      }
+      __syncthreads();
+      for (int r = tid; r < n_frags; r += NT) {
+        const int s = frags[r].q_start;
+        const int e = r + 1 < n_frags ? frags[r + 1].q_start : a.n_q;
+        Frag f{};
+        f.q_start = s;
+        f.q_len = e - s;
+        f.q_pos0 = a.q_pos[s];
+        const int doc = a.q_doc[s];
+        const int last_pos = f.q_pos0 + f.q_len - 1;
+        int ns = 0;
+        for (int j = 0; j < n_kvruns; ++j) {
+          const KvRun kr = kvr[j];
+          if (kr.doc != doc || kr.pos0 > last_pos) continue;  // other document, or wholly in the future
+          if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
+          f.k_start[ns] = kr.start; f.k_len[ns] = kr.len; f.k_pos0[ns] = kr.pos0; ++ns;
+        }
+        f.n_spans = ns;
+        frags[r] = f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. tiles in natural order ---------------------------------------------------
+  const int bm = a.tile_rows;
+  int n_tiles = 0;
+  if (sh.err == 0) {
+    int running = 0;
+    for (int base = 0; base < n_frags; base += NT) {
+      const int f = base + tid;
+      const int cnt = f < n_frags ? (frags[f].q_len + bm - 1) / bm : 0;
+      int total;
+      const int off = block_excl_scan(cnt, sh.scan, &total);
+      if (f < n_frags) ftile[f] = running + off;
+      running += total;
+    }
+    n_tiles = running;
+    if (tid == 0) ftile[n_frags] = n_tiles;
+    if (n_tiles > a.L.cap_tiles) {
+      if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
+    }
+  }
+  __syncthreads();
+  if (sh.err == 0) {
+    unsigned long long my_pairs = 0;
+    for (int t = tid; t < n_tiles; t += NT) {
+      int lo = 0, hi = n_frags - 1;  // last fragment whose first tile <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ftile[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const Frag f = frags[lo];
+      const int k = t - ftile[lo];
+      lb_plan_tile T{};
+      T.q_start = f.q_start + k * bm;
+      T.q_len = min(bm, f.q_len - k * bm);
+      T.q_pos0 = f.q_pos0 + k * bm;
+      const int last = T.q_pos0 + T.q_len - 1;
+      int ns = 0;
+      int64_t cost = 0;
+      for (int s = 0; s < f.n_spans; ++s) {
+        const int keep = min(f.k_len[s], last - f.k_pos0[s] + 1);
+        if (keep <= 0) continue;
+        T.k_start[ns] = f.k_start[s];
+        T.k_len[ns] = keep;
+        T.k_pos0[ns] = f.k_pos0[s];
+        cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[s], keep);
+        ++ns;
+      }
+      T.n_spans = ns;
+      T.cost = cost;
+      tiles[t] = T;
+      my_pairs += (unsigned long long)cost;
+    }
+    atomicAdd(&sh.pairs, my_pairs);
+  }
+  __syncthreads();
+
+  // ---- 3. longest-first order: bitonic sort of unique keys in LDS ------------------
+  if (sh.err == 0 && n_tiles > 0) {
+    int n_pad = 1;
+    while (n_pad < n_tiles) n_pad <<= 1;
+    for (int i = tid; i < n_pad; i += NT) {
+      uint64_t key = ~uint64_t(0);
+      if (i < n_tiles) key = ((kCostMask - (uint64_t)tiles[i].cost) << 24) | (uint64_t)i;
+      sh.keys[i] = key;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n_pad; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n_pad; i += NT) {
+          const int p = i ^ j;
+          if (p > i) {
+            const uint64_t x = sh.keys[i], y = sh.keys[p];
+            const bool ascending = (i & k) == 0;
+            if ((x > y) == ascending) {
+              sh.keys[i] = y;
+              sh.keys[p] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < n_tiles; i += NT) order[i] = (int32_t)(sh.keys[i] & 0xFFFFFF);
+  }
+  __syncthreads();
+
+  if (tid == 0) {
+    const bool ok = sh.err == 0;
+    hdr->err = sh.err;
+    hdr->n_frags = ok ? n_frags : 0;
+    hdr->n_tiles = ok ? n_tiles : 0;
+    hdr->n_items = ok ? n_tiles * a.kv_heads : 0;
+    hdr->queue_head = 0;
+    hdr->n_kvruns = n_kvruns;
+    hdr->tile_rows = bm;
+    hdr->n_workers = 0;
+    hdr->off_frags = a.L.off_frags;
+    hdr->off_kvruns = a.L.off_kvruns;
+    hdr->off_tiles = a.L.off_tiles;
+    hdr->off_order = a.L.off_order;
+    hdr->off_workers = a.L.off_workers;
+    hdr->cap_frags = a.L.cap_frags;
+    hdr->cap_tiles = a.L.cap_tiles;
+    hdr->total_pairs = ok ? (int64_t)sh.pairs : 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lb

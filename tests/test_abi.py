@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before anything reaches a GPU (no device needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import load_balance_amd as lb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lbattn.h")
+LB_OK, LB_EINVAL, LB_EUNSUPPORTED, LB_EWORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced by the host checks
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lb.LIB_PATH):
+        from load_balance_amd import build
+        build.build()
+    return lb.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lb_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"lb_varlen_attn_fwd", "lb_block_attn_fwd", "lb_lse_merge"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", lb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (lb_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        getattr(L, n)
+
+
+def test_struct_sizes_match_header(L):
+    assert ctypes.sizeof(lb.PlanTile) == 80
+    assert ctypes.sizeof(lb.WorkerRecord) == 40
+
+
+def test_status_strings(L):
+    assert L.lb_status_string(0) == b"ok"
+    assert b"workspace" in L.lb_status_string(3)
+    assert L.lb_status_string(99) == b"unknown status"
+
+
+def test_tile_rows(L):
+    assert L.lb_tile_rows(32, 8, 128) == 64
+    assert L.lb_tile_rows(2, 2, 64) == 256
+    assert L.lb_tile_rows(16, 8, 128) == 128
+    assert L.lb_tile_rows(64, 8, 128) == 32
+    assert L.lb_tile_rows(24, 8, 128) == -1   # G = 3
+    assert L.lb_tile_rows(32, 8, 96) == -1
+
+
+def test_workspace_bytes(L):
+    a = L.lb_workspace_bytes(32768, 30, 32, 8)
+    b = L.lb_workspace_bytes(65536, 30, 32, 8)
+    c = L.lb_workspace_bytes(32768, 300, 32, 8)
+    assert 0 < a < b and a < c and a % 256 == 0
+    assert L.lb_workspace_bytes(-1, 1, 32, 8) == 0
+    assert L.lb_workspace_bytes(10, 0, 32, 8) == 0
+    assert L.lb_workspace_bytes(10, 1, 30, 8) == 0
+
+
+def varlen(L, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, n_seg=3, T=64, H=2, Hkv=2, d=64, mask=0, out=FAKE, lse=FAKE,
+                ws=FAKE, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return L.lb_varlen_attn_fwd(args["q"], args["k"], args["v"], args["cu"], args["n_seg"], args["T"], args["H"],
+                                args["Hkv"], args["d"], args["mask"], args["out"], args["lse"], args["ws"],
+                                args["ws_bytes"], args["stream"])
+
+
+def test_varlen_host_checks(L):
+    assert varlen(L, q=None) == LB_EINVAL
+    assert varlen(L, cu=None) == LB_EINVAL
+    assert varlen(L, ws=None) == LB_EINVAL
+    assert varlen(L, n_seg=0) == LB_EINVAL
+    assert varlen(L, T=-1) == LB_EINVAL
+    assert varlen(L, H=3, Hkv=2) == LB_EINVAL
+    assert varlen(L, mask=2) == LB_EINVAL
+    assert varlen(L, d=96) == LB_EUNSUPPORTED
+    assert varlen(L, H=6, Hkv=2) == LB_EUNSUPPORTED
+    assert varlen(L, q=ctypes.c_void_p(0x100008)) == LB_EINVAL          # 16-byte alignment
+    assert varlen(L, ws=ctypes.c_void_p(0x100010)) == LB_EWORKSPACE     # 256-byte alignment
+    need = L.lb_workspace_bytes(64, 3, 2, 2)
+    assert varlen(L, ws_bytes=need - 1) == LB_EWORKSPACE
+    assert varlen(L, T=1 << 22, n_seg=1, H=32, Hkv=8, d=128, ws_bytes=1 << 30) == LB_EUNSUPPORTED  # > sort capacity
+    assert varlen(L, T=0, ws_bytes=need) == LB_OK                        # nothing to do, nothing enqueued
+
+
+def test_block_host_checks(L):
+    def call(**kw):
+        a = dict(q=FAKE, n_q=128, kv=FAKE, n_kv=128, qp=FAKE, kp=FAKE, qd=FAKE, kd=FAKE, H=32, Hkv=8, d=128,
+                 out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return L.lb_block_attn_fwd(a["q"], a["n_q"], a["kv"], a["n_kv"], a["qp"], a["kp"], a["qd"], a["kd"], a["H"],
+                                   a["Hkv"], a["d"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+    assert call(q=None) == LB_EINVAL
+    assert call(kv=None) == LB_EINVAL
+    assert call(n_q=-1) == LB_EINVAL
+    assert call(d=80) == LB_EUNSUPPORTED
+    assert call(ws_bytes=100) == LB_EWORKSPACE
+    assert call(n_q=0) == LB_OK
+    assert call(n_q=0, kv=None, n_kv=0) == LB_OK
+
+
+def test_merge_host_checks(L):
+    assert L.lb_lse_merge(None, FAKE, FAKE, FAKE, 4, 2, 8, None) == LB_EINVAL
+    assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, None) == LB_EUNSUPPORTED
+    assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, -1, 2, 8, None) == LB_EINVAL
+    assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 0, 2, 8, None) == LB_OK
+
+
+def test_read_backs_reject_bad_arguments(L):
+    n = ctypes.c_int32()
+    assert L.lb_read_plan(FAKE, 1 << 20, None, 4, ctypes.byref(n), None) == LB_EINVAL
+    assert L.lb_read_plan(None, 1 << 20, None, 0, ctypes.byref(n), None) == LB_EWORKSPACE
+    assert L.lb_read_device_error(FAKE, 1 << 20, None, None) == LB_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(lb, "_lib", None)
+    monkeypatch.setattr(lb, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "liblbattn.so"))
+    with pytest.raises(lb.LBError, match="no CPU fallback"):
+        lb.lib()
+
+
+def test_product_and_oracle_share_no_code():
+    pkg = os.path.join(ROOT, "load_balance_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text and "oracle." not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert not re.search(r"^\s*(from|import)\s+load_balance_amd\b", text, re.M), f
+            assert "liblbattn" not in text, f

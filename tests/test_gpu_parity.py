@@ -1,0 +1,421 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): out max |d| <= 2e-2 and mean
+|d| <= 2e-3, lse max |d| <= 5e-3.  Plans (tiles, spans, exact pair costs and
+longest-first order) must equal the oracle's enumerator bit for bit.
+Large configurations are compared on sampled rows that the oracle computes
+one by one; small ones on every row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import load_balance_amd as lb
+import workloads
+from oracle import attention as OA
+from oracle import plan as OP
+
+pytestmark = pytest.mark.gpu
+
+OUT_MAX, OUT_MEAN, LSE_MAX = 2e-2, 2e-3, 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bits_of(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32(bits):
+    return workloads.bf16_bits_to_f32(bits)
+
+
+def run_varlen(pack, mask_kind=lb.MASK_CAUSAL_DOC):
+    say(f"  varlen_attn_fwd T={pack['tokens']} H={pack['heads']} Hkv={pack['kv_heads']} d={pack['d']} "
+        f"docs={len(pack['lengths'])} mask={mask_kind}")
+    q, k, v = dev_bf16(pack["q"]), dev_bf16(pack["k"]), dev_bf16(pack["v"])
+    cu = torch.from_numpy(np.asarray(pack["cu_seqlens"], dtype=np.int32)).cuda()
+    ws = lb.new_workspace(pack["tokens"], len(pack["lengths"]), pack["heads"], pack["kv_heads"])
+    out, lse = lb.varlen_attn_fwd(q, k, v, cu, mask_kind=mask_kind, workspace=ws)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    return out, lse, ws
+
+
+def check(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
+    og = np.asarray(out_gpu, dtype=np.float64)
+    lg = np.asarray(lse_gpu, dtype=np.float64)
+    assert np.all(np.isfinite(og)), f"{what}: non-finite output"
+    d_out = np.abs(og - out_ref)
+    d_lse = np.abs(lg - lse_ref)
+    say(f"  {what}: out max {d_out.max():.3e} mean {d_out.mean():.3e}  lse max {d_lse.max():.3e}")
+    assert d_out.max() <= OUT_MAX, what
+    assert d_out.mean() <= OUT_MEAN, what
+    assert d_lse.max() <= LSE_MAX, what
+
+
+def sample_rows(lengths, bm, n_random, seed, cap=None):
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    r = np.random.default_rng(seed)
+    rows = set()
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        rows.update([a, b - 1, min(b - 1, a + bm - 1), min(b - 1, a + bm)])
+    rows.update(r.integers(0, int(cu[-1]), n_random).tolist())
+    rows = sorted(rows)
+    if cap is not None and len(rows) > cap:
+        rows = sorted(r.choice(rows, cap, replace=False).tolist())
+    return np.array(rows, dtype=np.int64)
+
+
+def plan_ref_varlen(pack, mask="causal_doc"):
+    bm = lb.tile_rows(pack["heads"], pack["kv_heads"], pack["d"])
+    return OP.plan(OP.fragments_varlen(pack["cu_seqlens"], mask), bm)
+
+
+def assert_same_plan(gpu, ref, what):
+    assert len(gpu) == len(ref), f"{what}: {len(gpu)} tiles vs {len(ref)}"
+    for i, (a, b) in enumerate(zip(gpu, ref)):
+        assert a == b, f"{what}: tile {i}: gpu {a} != oracle {b}"
+
+
+# --------------------------------------------------------------------------
+# fixtures: the five workloads
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny():
+    return workloads.tiny_pack()
+
+
+@pytest.fixture(scope="module")
+def longtail():
+    return workloads.longtail_pack(0)
+
+
+@pytest.fixture(scope="module")
+def pair():
+    return workloads.pair_packs()
+
+
+@pytest.fixture(scope="module")
+def shared_q():
+    return workloads.shared_question_packs()
+
+
+# --------------------------------------------------------------------------
+# config 1: tiny pack, every row
+# --------------------------------------------------------------------------
+def test_tiny_pack_full(tiny):
+    out, lse, ws = run_varlen(tiny)
+    ref_o, ref_l = OA.varlen_attention(tiny["q"], tiny["k"], tiny["v"], tiny["cu_seqlens"], 2, 2)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "tiny pack")
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(tiny), "tiny plan")
+    # reported, not gated: distance to the unrounded fp32 inputs
+    o32, l32 = OA.varlen_attention(tiny["q32"], tiny["k32"], tiny["v32"], tiny["cu_seqlens"], 2, 2)
+    say(f"  vs unrounded fp32 inputs: out max {np.abs(out.float().cpu().numpy() - o32).max():.3e}")
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(2, 2, 64), (4, 2, 64), (8, 2, 128), (16, 2, 128), (32, 8, 128), (8, 8, 128)])
+def test_random_pack_every_row(H, Hkv, d):
+    """Several tiles per document, ragged tails, 1-token documents, all head groupings."""
+    r = np.random.default_rng(H * 1000 + Hkv * 10 + d)
+    lengths = [1, 700, 3, 1, 257, 64, 129, 1000, 2]
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=H, kv_heads=Hkv,
+                d=d, q=q, k=k, v=v)
+    out, lse, ws = run_varlen(pack)
+    ref_o, ref_l = OA.varlen_attention(q, k, v, pack["cu_seqlens"], H, Hkv)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"random pack H={H} Hkv={Hkv} d={d}")
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(pack), "random plan")
+
+
+# --------------------------------------------------------------------------
+# config 2: 32K long-tail pack, sampled rows
+# --------------------------------------------------------------------------
+def test_longtail_pack(longtail):
+    p = longtail
+    out, lse, ws = run_varlen(p)
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(p), "32K long-tail plan")
+    rows = sample_rows(p["lengths"], 64, 96, 1, cap=256)
+    ref_o, ref_l = OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], 32, 8, rows=rows)
+    check(out[rows].float().cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "32K long-tail (sampled)")
+    recs = lb.read_worker_timing(ws)
+    assert len(recs) == torch.cuda.get_device_properties(0).multi_processor_count
+    assert sum(x["items"] for x in recs) == len(lb.read_plan(ws)) * 8
+    assert sum(x["pairs"] for x in recs) == 32 * 49_322_947
+
+
+def test_longtail_is_deterministic(longtail):
+    a, la, _ = run_varlen(longtail)
+    b, lb_, _ = run_varlen(longtail)
+    assert torch.equal(a, b) and torch.equal(la, lb_)
+
+
+@pytest.mark.parametrize("seed", [1, 3])
+def test_longtail_other_seeds_plan(seed):
+    lengths = workloads.lognormal_lengths(32768, seed, 32768)
+    T = 32768
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=32, kv_heads=8,
+                d=128, q=np.zeros((T, 32, 128), np.uint16), k=np.zeros((T, 8, 128), np.uint16),
+                v=np.zeros((T, 8, 128), np.uint16))
+    out, lse, ws = run_varlen(pack)
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(pack), f"seed {seed} plan")
+    # zero inputs: every visible logit is 0, so exp(lse) counts the visible keys exactly
+    n = np.concatenate([np.arange(1, l + 1) for l in lengths])
+    got = np.rint(np.exp(lse[:, :].double().cpu().numpy())).astype(np.int64)
+    assert np.array_equal(got, np.broadcast_to(n, got.shape))
+
+
+# --------------------------------------------------------------------------
+# config 3: equal-token pair
+# --------------------------------------------------------------------------
+def test_pair_A_one_document(pair):
+    p = pair[0]
+    out, lse, ws = run_varlen(p)
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(p), "pair A plan")
+    rows = np.array([0, 1, 63, 64, 65, 4095, 20000, 40894, 40895, 40959] +
+                    np.random.default_rng(3).integers(0, 40960, 22).tolist())
+    ref_o, ref_l = OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], 32, 8, rows=rows)
+    check(out[rows].float().cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "pair A (sampled)")
+
+
+def test_pair_B_ten_documents(pair):
+    p = pair[1]
+    out, lse, ws = run_varlen(p)
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(p), "pair B plan")
+    rows = sample_rows(p["lengths"], 64, 40, 4, cap=96)
+    ref_o, ref_l = OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], 32, 8, rows=rows)
+    check(out[rows].float().cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "pair B (sampled)")
+
+
+# --------------------------------------------------------------------------
+# config 5: shared question, batch of 4 packs (one call per pack)
+# --------------------------------------------------------------------------
+def test_shared_question(shared_q):
+    for i, p in enumerate(shared_q):
+        out, lse, ws = run_varlen(p, lb.MASK_SHARED_QUESTION)
+        assert_same_plan(lb.read_plan(ws), plan_ref_varlen(p, "shared_question"), f"shared question plan {i}")
+        rows = sample_rows(p["lengths"], 64, 16, 10 + i, cap=40)
+        ref_o, ref_l = OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], 32, 8, mask="shared_question",
+                                           rows=rows)
+        check(out[rows].float().cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, f"shared question pack {i}")
+
+
+def test_shared_question_small_every_row():
+    r = np.random.default_rng(77)
+    lengths = [300, 129, 64, 1, 200]
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, 8, 2, 128)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=8, kv_heads=2, d=128,
+                q=q, k=k, v=v)
+    out, lse, ws = run_varlen(pack, lb.MASK_SHARED_QUESTION)
+    ref_o, ref_l = OA.varlen_attention(q, k, v, pack["cu_seqlens"], 8, 2, mask="shared_question")
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "shared question small")
+    assert_same_plan(lb.read_plan(ws), plan_ref_varlen(pack, "shared_question"), "shared question small plan")
+
+
+# --------------------------------------------------------------------------
+# config 4: one zigzag rank's share at cp=8, 8 ring steps + 7 merges
+# --------------------------------------------------------------------------
+def test_zigzag_rank3_cp8():
+    lengths = workloads.zigzag_pack_lengths(0)
+    C, cp, rank = 8192, 8, 3
+    cache = {}
+
+    def get_chunk(c):
+        if c not in cache:
+            cache[c] = workloads.zigzag_chunk_values(c)
+        return cache[c]
+
+    say("  zigzag rank 3 of cp=8: building the share")
+    share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    plans = []
+
+    def per_step(t, o, l):
+        plans.append(lb.read_plan(share.workspace))
+
+    out, lse = share.run(per_step=per_step)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(share.workspace) == 0
+    # plans of every step against the oracle enumerator
+    pos, doc = OA.pack_positions(lengths)
+    qi = np.concatenate([np.arange(c * C, (c + 1) * C) for c in OA.zigzag_chunks_of_rank(rank, cp)])
+    pairs = []
+    for t in range(cp):
+        ki = np.concatenate([np.arange(c * C, (c + 1) * C)
+                             for c in OA.zigzag_chunks_of_rank(OA.ring_source(rank, t, cp), cp)])
+        ref = OP.plan(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 64)
+        assert_same_plan(plans[t], ref, f"zigzag step {t}")
+        pairs.append(OP.total_pairs(ref))
+    assert pairs == [20_319_978, 7_981_112, 0, 0, 0, 0, 0, 3_473_470]
+    # output: oracle fold on sampled rows
+    r = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 8191, 8192, 16383], r.integers(0, 2 * C, 60)]))
+    ref_o, ref_l, _ = OA.zigzag_rank_attention(get_chunk, lengths, C, rank, cp, 32, 8, rows=rows)
+    check(out[rows].cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "zigzag rank 3 (sampled)")
+
+
+def test_zigzag_reassembly_small():
+    """All ranks of a reduced pack (cp=4, 16 chunks of 256... here 8 chunks of 256) against the unsharded oracle."""
+    cp, C, H, Hkv, d = 4, 256, 8, 2, 128
+    T = 2 * cp * C
+    lengths = workloads.lognormal_lengths(T, 9, T)
+    r = np.random.default_rng(12)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+
+    def get_chunk(c):
+        sl = slice(c * C, (c + 1) * C)
+        return q[sl], k[sl], v[sl]
+
+    full_o, full_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv)
+    for rank in range(cp):
+        share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+        out, lse = share.run()
+        rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in OA.zigzag_chunks_of_rank(rank, cp)])
+        check(out.cpu().numpy(), lse.cpu().numpy(), full_o[rows], full_l[:, rows], f"reassembly rank {rank}")
+
+
+# --------------------------------------------------------------------------
+# block path edge cases
+# --------------------------------------------------------------------------
+def run_block(q, k, v, q_pos, kv_pos, q_doc, kv_doc):
+    n_q, H, d = q.shape
+    n_kv, Hkv = k.shape[0], k.shape[1]
+    say(f"  block_attn_fwd n_q={n_q} n_kv={n_kv} H={H} Hkv={Hkv} d={d}")
+    kv = torch.stack([dev_bf16(k), dev_bf16(v)]) if n_kv else torch.zeros((2, 0, Hkv, d), dtype=torch.bfloat16,
+                                                                            device="cuda")
+    i32 = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).cuda()
+    out, lse = lb.block_attn_fwd(dev_bf16(q), kv.contiguous(), i32(q_pos), i32(kv_pos), i32(q_doc), i32(kv_doc))
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_block_random_shards_every_row():
+    r = np.random.default_rng(31)
+    H, Hkv, d = 8, 2, 128
+    T = 2048
+    lengths = workloads.lognormal_lengths(T, 4, T)
+    pos, doc = OA.pack_positions(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    qi = np.r_[256:512, 1536:1792]
+    ki = np.r_[0:384, 1400:2048]
+    out, lse = run_block(q[qi], k[ki], v[ki], pos[qi], pos[ki], doc[qi], doc[ki])
+    ref_o, ref_l = OA.block_attention(q[qi], k[ki], v[ki], pos[qi], pos[ki], doc[qi], doc[ki], H, Hkv)
+    lse_g = lse.cpu().numpy()
+    empty = ref_l == -np.inf
+    assert np.array_equal(lse_g == -np.inf, empty)
+    rows_ok = ~empty[0]
+    check(out.cpu().numpy()[rows_ok], lse_g[:, rows_ok], ref_o[rows_ok], ref_l[:, rows_ok], "block random shards")
+
+
+def test_block_no_keys_gives_minus_inf():
+    r = np.random.default_rng(2)
+    q, _, _ = workloads.values(r, 300, 4, 4, 64)
+    out, lse = run_block(q, np.zeros((0, 4, 64), np.uint16), np.zeros((0, 4, 64), np.uint16), np.arange(300),
+                         [], np.zeros(300), [])
+    assert torch.all(lse == -math.inf)
+    k, v = workloads.values(r, 50, 4, 4, 64)[1:]
+    out, lse = run_block(q, k, v, np.arange(300), np.arange(50), np.zeros(300), np.ones(50))  # other document
+    assert torch.all(lse == -math.inf)
+
+
+# --------------------------------------------------------------------------
+# special cases fixed by the mathematics
+# --------------------------------------------------------------------------
+def test_single_token_documents_return_their_value():
+    r = np.random.default_rng(8)
+    lengths = [1, 90, 1, 1, 130, 1]
+    T = sum(lengths)
+    H, Hkv, d = 8, 2, 128
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=H, kv_heads=Hkv,
+                d=d, q=q, k=k, v=v)
+    out, lse, _ = run_varlen(pack)
+    ob = bits_of(out)
+    scale = 1 / math.sqrt(d)
+    for t in (0, 91, 92, 223):
+        for h in range(H):
+            assert np.array_equal(ob[t, h], v[t, h // 4]), (t, h)
+            expect = scale * float(f32(q[t, h]).astype(np.float64) @ f32(k[t, h // 4]).astype(np.float64))
+            assert abs(float(lse[h, t]) - expect) < 1e-4
+
+
+def test_zero_query_counts_visible_keys_exactly():
+    r = np.random.default_rng(9)
+    lengths = [5, 17, 42, 1000, 3, 2000]
+    T = sum(lengths)
+    _, k, v = workloads.values(r, T, 4, 4, 64)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=4, kv_heads=4, d=64,
+                q=np.zeros((T, 4, 64), np.uint16), k=k, v=v)
+    _, lse, _ = run_varlen(pack)
+    n = np.concatenate([np.arange(1, l + 1) for l in lengths])
+    got = np.rint(np.exp(lse.double().cpu().numpy())).astype(np.int64)
+    assert np.array_equal(got, np.broadcast_to(n, got.shape))
+
+
+def test_constant_value_is_returned():
+    r = np.random.default_rng(10)
+    lengths = [333, 1, 64, 700]
+    T = sum(lengths)
+    q, k, _ = workloads.values(r, T, 8, 2, 128)
+    v = workloads.f32_to_bf16_bits(np.full((T, 2, 128), 0.75, np.float32))
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=8, kv_heads=2,
+                d=128, q=q, k=k, v=v)
+    out, _, _ = run_varlen(pack)
+    assert (out.float() - 0.75).abs().max().item() <= OUT_MAX
+
+
+def test_bad_cu_seqlens_sets_device_error():
+    T = 128
+    q = torch.zeros((T, 4, 64), dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 100, 50, T], dtype=torch.int32, device="cuda")
+    lse = torch.full((4, T), 12345.0, device="cuda")
+    ws = lb.new_workspace(T, 3, 4, 4)
+    lb.varlen_attn_fwd(q, q, q, cu, lse=lse, workspace=ws)
+    assert lb.read_device_error(ws) == lb.DEVERR_CU_SEQLENS
+    assert torch.all(lse == 12345.0)
+    cu = torch.tensor([0, 100, 120, T - 1], dtype=torch.int32, device="cuda")
+    lb.varlen_attn_fwd(q, q, q, cu, lse=lse, workspace=ws)
+    assert lb.read_device_error(ws) == lb.DEVERR_CU_SEQLENS
+
+
+# --------------------------------------------------------------------------
+# lse_merge
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+def test_lse_merge_matches_oracle(d):
+    r = np.random.default_rng(d)
+    R, H = 777, 6
+    oa, ob = r.standard_normal((R, H, d)), r.standard_normal((R, H, d))
+    la, lb_ = r.standard_normal((H, R)) * 3, r.standard_normal((H, R)) * 3
+    la[r.random((H, R)) < 0.2] = -np.inf
+    lb_[r.random((H, R)) < 0.2] = -np.inf
+    ref_o, ref_l = OA.lse_merge(oa, la, ob, lb_)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    ga, gla = t(oa), t(la)
+    gb = t(ob)
+    gb[torch.from_numpy((lb_ == -np.inf).T.copy())] = float("nan")  # never read where lse_b = -inf
+    lb.lse_merge(ga, gla, gb, t(lb_))
+    torch.cuda.synchronize()
+    go, gl = ga.cpu().numpy(), gla.cpu().numpy()
+    both_inf = (la == -np.inf) & (lb_ == -np.inf)
+    assert np.all(gl[both_inf] == -np.inf)
+    fin = ~both_inf
+    assert np.abs(gl[fin] - ref_l[fin]).max() <= 1e-5
+    rows_fin = fin.T
+    assert np.abs(go[rows_fin] - ref_o[rows_fin]).max() <= 1e-5
+    keep = (lb_ == -np.inf).T
+    assert np.array_equal(go[keep], np.float32(oa)[keep])
