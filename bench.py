@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Effective masked-attention TFLOP/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload longtail]
+
+A step is one pass of the hot path over one batch: the planning kernel
+(fragments, key spans, exact pair costs, longest-first order) and the
+persistent attention kernel, i.e. exactly lb_varlen_attn_fwd split into its
+two halves so that HIP events can time each kernel on the stream they run
+on.  Inputs are resident in HBM before timing starts.
+
+Effective FLOPs count only unmasked work: 4 * d * H * (visible query-key
+pairs), with pairs = sum over documents of l(l+1)/2 (diagonal included).
+
+Prints one JSON line.  Extra workloads (--workload pairA|pairB|zigzag|
+shared_question|tiny) print the same fields for their own configuration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective masked-attn TFLOP/s (Σℓ² FLOPs) & % bf16 MFMA peak, 32K varlen pack"
+PEAK_BF16_TFLOPS = 2500.0           # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
+PEAK_BF16_AT_2400MHZ = 256 * 2.4e9 * 4096 / 1e12   # 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU = 2516.6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longtail32k_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "load_balance_amd", "csrc", "attn_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(lengths):
+    return int(sum(int(l) * (int(l) + 1) // 2 for l in lengths))
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+# ----------------------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------------------
+class VarlenStep:
+    """plan + attention over one packed sequence (per-document causal or shared question)."""
+
+    def __init__(self, packs, mask_kind, name, torch, lb):
+        self.torch, self.lb = torch, lb
+        self.name = name
+        self.mask_kind = mask_kind
+        self.items = []
+        for p in packs:
+            T, H, Hkv, d = p["tokens"], p["heads"], p["kv_heads"], p["d"]
+            it = dict(T=T, H=H, Hkv=Hkv, d=d,
+                      q=to_dev(p["q"], torch), k=to_dev(p["k"], torch), v=to_dev(p["v"], torch),
+                      cu=torch.from_numpy(np.asarray(p["cu_seqlens"], np.int32)).cuda())
+            it["out"] = torch.empty_like(it["q"])
+            it["lse"] = torch.empty((H, T), dtype=torch.float32, device="cuda")
+            it["ws"] = lb.new_workspace(T, len(p["lengths"]), H, Hkv)
+            self.items.append(it)
+        self.H, self.d = packs[0]["heads"], packs[0]["d"]
+        if mask_kind == lb.MASK_CAUSAL_DOC:
+            self.pairs = sum(causal_pairs(p["lengths"]) for p in packs)
+        else:
+            self.pairs = 0
+            for p in packs:
+                Q, ans = p["lengths"][0], p["lengths"][1:]
+                self.pairs += Q * (Q + 1) // 2 + sum(a * Q + a * (a + 1) // 2 for a in ans)
+        self.flops = 4 * self.d * self.H * self.pairs
+
+    def n_launches(self):
+        return len(self.items)
+
+    def run(self, evs=None):
+        """evs: optional [launch][3] events recorded before the plan, between plan and attention, after."""
+        lb = self.lb
+        for i, it in enumerate(self.items):
+            ev = None if evs is None else evs[i]
+            if ev is not None:
+                ev[0].record()
+            lb.plan_varlen(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], self.mask_kind, workspace=it["ws"])
+            if ev is not None:
+                ev[1].record()
+            lb.attn_run(it["q"], it["k"], it["v"], it["out"], it["lse"], it["ws"])
+            if ev is not None:
+                ev[2].record()
+
+    def plan_pairs(self):
+        return sum(sum(t["cost"] for t in self.lb.read_plan(it["ws"])) for it in self.items)
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.items[-1]["ws"])
+
+
+class ZigzagStep:
+    """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
+
+    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0):
+        self.torch, self.lb = torch, lb
+        lengths = workloads.zigzag_pack_lengths(seed)
+        cache = {}
+
+        def get_chunk(c):
+            if c not in cache:
+                cache[c] = workloads.zigzag_chunk_values(c, chunk)
+            return cache[c]
+
+        self.share = lb.zigzag.RankShare(lengths, chunk, rank, cp, get_chunk)
+        self.H, self.d = 32, 128
+        # pairs: positions and document ids of the rank's rows against each step's chunks
+        pos, doc = lb.zigzag.token_meta(lengths)
+        total = 0
+        qc = lb.zigzag.chunks_of_rank(rank, cp)
+        for t in range(cp):
+            kc = lb.zigzag.chunks_of_rank(lb.zigzag.ring_source(rank, t, cp), cp)
+            for a in qc:
+                for b in kc:
+                    qs, ks = slice(a * chunk, (a + 1) * chunk), slice(b * chunk, (b + 1) * chunk)
+                    total += int(np.sum((doc[qs][:, None] == doc[ks][None, :]) &
+                                        (pos[ks][None, :] <= pos[qs][:, None])))
+        self.pairs = total
+        self.flops = 4 * self.d * self.H * self.pairs
+        self.name = f"zigzag cp={cp} rank {rank}"
+
+    def n_launches(self):
+        return len(self.share.steps)
+
+    def run(self, evs=None):
+        lb, sh = self.lb, self.share
+        for t, st in enumerate(sh.steps):
+            out = sh.out if t == 0 else sh.step_out
+            lse = sh.lse if t == 0 else sh.step_lse
+            ev = None if evs is None else evs[t]
+            if ev is not None:
+                ev[0].record()
+            lb.plan_block(sh.q_pos, sh.q_doc, st["kv_pos"], st["kv_doc"], self.H, 8, self.d, sh.workspace)
+            if ev is not None:
+                ev[1].record()
+            lb.attn_run(sh.q, st["kv"][0], st["kv"][1], out, lse, sh.workspace)
+            if ev is not None:
+                ev[2].record()
+            if t > 0:
+                lb.lse_merge(sh.out, sh.lse, sh.step_out, sh.step_lse)
+
+    def plan_pairs(self):
+        return None
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.share.workspace)
+
+
+def make_workload(name, seed, torch, lb, workloads):
+    if name == "longtail":
+        p = workloads.longtail_pack(seed)
+        w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
+        w.config = {"workload": f"32K long-tail varlen pack: lognormal lengths (median 644, sigma 1.6), seed {seed}, "
+                                "per-document causal mask",
+                    "tokens": p["tokens"], "documents": len(p["lengths"]), "max_doc": max(p["lengths"]),
+                    "heads": 32, "kv_heads": 8, "head_dim": 128, "seed": seed}
+        w.packs = [p]
+        return w
+    if name in ("pairA", "pairB"):
+        a, b = workloads.pair_packs()
+        p = a if name == "pairA" else b
+        w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
+        w.config = {"workload": "equal-token pair, " + ("A: one 40960-token document" if name == "pairA"
+                                                        else "B: ten 4096-token documents"),
+                    "tokens": 40960, "documents": len(p["lengths"]), "heads": 32, "kv_heads": 8, "head_dim": 128}
+        w.packs = [p]
+        return w
+    if name == "shared_question":
+        packs = workloads.shared_question_packs()
+        w = VarlenStep(packs, lb.MASK_SHARED_QUESTION, name, torch, lb)
+        w.config = {"workload": "shared question: 4 packs of one 8192-token question + 8 answers of 4096",
+                    "tokens": 4 * 40960, "heads": 32, "kv_heads": 8, "head_dim": 128}
+        w.packs = packs
+        return w
+    if name == "tiny":
+        p = workloads.tiny_pack()
+        w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
+        w.config = {"workload": "tiny pack [5,17,42], 2 q heads = 2 kv heads, head_dim 64", "tokens": 64}
+        w.packs = [p]
+        return w
+    if name == "zigzag":
+        w = ZigzagStep(torch, lb, workloads, seed=seed)
+        w.config = {"workload": "one zigzag CP rank's share at cp=8: rank 3 of a 131072-token lognormal pack "
+                                f"(seed {seed}), 16 chunks of 8192, 8 ring steps + 7 merges",
+                    "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128}
+        return w
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ----------------------------------------------------------------------------------------
+# CPU baseline: the oracle, on a bounded sample of the same workload
+# ----------------------------------------------------------------------------------------
+def cpu_baseline(w, seconds, seed=0):
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    p = w.packs[0]
+    lengths = np.asarray(p["lengths"])
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    seg = np.repeat(np.arange(len(lengths)), lengths)
+    pos_in_doc = np.arange(p["tokens"]) - cu[seg]
+    blocks = np.random.default_rng(seed).permutation(p["tokens"] // 256)
+    done_rows = []
+    t0 = time.perf_counter()
+    for b in blocks:
+        rows = np.arange(b * 256, (b + 1) * 256)
+        OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], p["heads"], p["kv_heads"], rows=rows)
+        done_rows.append(rows)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    rows = np.concatenate(done_rows)
+    pairs = int(np.sum(pos_in_doc[rows] + 1))
+    flops = 4 * p["d"] * p["heads"] * pairs
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {p['tokens']} query rows (random 256-row blocks, all {p['heads']} heads), "
+                      f"{pairs} visible pairs per head = {pairs / causal_pairs(lengths):.1%} of the pack, "
+                      f"float64 numpy, {el:.1f} s"}
+
+
+def traffic_entry():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if t.get("source_sha256") != sha:
+            return None
+        return t.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+# ----------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="longtail",
+                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              "(see DESIGN.md for how the attention would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import load_balance_amd as lb
+    import workloads
+
+    lb.lib()
+    log(f"bench: building workload {args.workload}")
+    w = make_workload(args.workload, args.seed, torch, lb, workloads)
+    torch.cuda.synchronize()
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        w.run()
+    torch.cuda.synchronize()
+    if w.plan_pairs() is not None:
+        assert w.plan_pairs() == w.pairs, "plan pair count differs from the closed form"
+
+    n_launch = w.n_launches()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_launch)]
+           for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        w.run(evs[s])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = el / args.steps * 1e3
+    plan_ms = float(np.mean([sum(e[0].elapsed_time(e[1]) for e in step) for step in evs]))
+    attn_ms = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in step) for step in evs]))
+    attn_ms_per_launch = attn_ms / n_launch
+
+    recs = w.workers()
+    busy = np.array([r["t_end"] - r["t_start"] for r in recs], dtype=np.float64)
+    span_ticks = max(r["t_end"] for r in recs) - min(r["t_start"] for r in recs)
+    cu_ratio = float(busy.max() / busy.mean()) if len(busy) and busy.mean() > 0 else None
+
+    value = w.flops / (ms_per_step / 1e3) / 1e12
+    achieved = w.flops / (attn_ms / 1e3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(w.config, pairs_per_head=w.pairs, effective_flops=w.flops),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
+        "cu_busy_max_over_mean": None if cu_ratio is None else round(cu_ratio, 4),
+        "attention_span_device_clock_ms": round(span_ticks / 1e5, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_entry() if args.workload == "longtail" else None,
+            "kernel": "attn_kernel<128,false> (persistent, LPT queue)",
+            "launch_ms": round(attn_ms_per_launch, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and hasattr(w, "packs"):
+        log(f"bench: cpu baseline (~{args.cpu_seconds:.0f} s of the float64 oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,7 +83,8 @@ enum {
   LB_DEVERR_NONE = 0,
   LB_DEVERR_CU_SEQLENS = 1,   /* cu_seqlens[0] != 0, decreasing, or cu_seqlens[n_seg] != total_tokens */
   LB_DEVERR_CAPACITY = 2,     /* more fragments or tiles than the workspace holds */
-  LB_DEVERR_SPANS = 4         /* a query run meets more than LB_MAX_SPANS key runs of its document */
+  LB_DEVERR_SPANS = 4,        /* a query run meets more than LB_MAX_SPANS key runs of its document */
+  LB_DEVERR_PLAN = 8          /* lb_attn_run's shapes differ from those the workspace's plan was made for */
 };
 
 #define LB_MAX_SPANS 4
@@ -159,6 +160,31 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
                             const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * The two halves of the forward calls.  lb_varlen_attn_fwd is lb_plan_varlen followed by
+ * lb_attn_run (bf16 out); lb_block_attn_fwd is lb_plan_block followed by lb_attn_run (fp32
+ * out).  Split, a plan can serve several attention launches -- every layer of a model sees
+ * the same cu_seqlens -- and each half can be timed on its own.  The plan stays valid in
+ * the workspace until the next lb_plan_* call on it; the work queue rewinds itself at the
+ * end of every lb_attn_run, so runs on one stream may repeat without re-planning.  Runs
+ * that overlap in time on one workspace race.
+ *
+ * lb_attn_run's n_q, n_kv, heads and kv_heads must equal those of the plan; otherwise the
+ * device sets LB_DEVERR_PLAN and writes nothing.  k and v are separate [n_kv][kv_heads][d]
+ * bf16 arrays here (for the block path: kv_chunk and kv_chunk + n_kv*kv_heads*d).
+ */
+lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
+                         int32_t kv_heads, int32_t d, int32_t mask_kind, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                        const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                      int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * In-place merge a <- merge(a, b) of two partials over disjoint key sets:

@@ -27,6 +27,7 @@ MAX_SPANS = 4
 DEVERR_CU_SEQLENS = 1
 DEVERR_CAPACITY = 2
 DEVERR_SPANS = 4
+DEVERR_PLAN = 8
 
 
 class LBError(RuntimeError):
@@ -67,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.lb_varlen_attn_fwd.restype = ctypes.c_int
     L.lb_block_attn_fwd.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
     L.lb_block_attn_fwd.restype = ctypes.c_int
+    L.lb_plan_varlen.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_varlen.restype = ctypes.c_int
+    L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_block.restype = ctypes.c_int
+    L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_attn_run.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.lb_lse_merge.restype = ctypes.c_int
     L.lb_status_string.argtypes = [ctypes.c_int]
@@ -163,6 +170,46 @@ def block_attn_fwd(q_shard, kv_chunk, q_pos, kv_pos, q_doc, kv_doc, out=None, ls
                                  _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel(), ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_block_attn_fwd")
+    return out, lse
+
+
+def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAUSAL_DOC, workspace=None,
+                stream=None):
+    """First half of varlen_attn_fwd: writes the tile plan into ``workspace`` (returned)."""
+    n_seg = cu_seqlens.numel() - 1
+    if workspace is None:
+        workspace = new_workspace(total_tokens, max(1, n_seg), heads, kv_heads, cu_seqlens.device)
+    if cu_seqlens.dtype != torch.int32:
+        raise LBError("cu_seqlens must be int32")
+    _check(lib().lb_plan_varlen(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d, int(mask_kind),
+                                _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_plan_varlen")
+    return workspace
+
+
+def plan_block(q_pos, q_doc, kv_pos, kv_doc, heads, kv_heads, d, workspace, stream=None):
+    """First half of block_attn_fwd: writes the tile plan into ``workspace``."""
+    for t, name in ((q_pos, "q_pos"), (kv_pos, "kv_pos"), (q_doc, "q_doc"), (kv_doc, "kv_doc")):
+        if t.dtype != torch.int32:
+            raise LBError(f"{name} must be int32")
+    _check(lib().lb_plan_block(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), _ptr(kv_pos), _ptr(kv_doc), kv_pos.numel(),
+                               heads, kv_heads, d, _ptr(workspace), workspace.numel(),
+                               ctypes.c_void_p(_stream(stream))), "lb_plan_block")
+    return workspace
+
+
+def attn_run(q, k, v, out, lse, workspace, stream=None):
+    """Second half of either forward: runs the plan held in ``workspace``.
+
+    q [n_q,H,d], k/v [n_kv,H_kv,d] bf16; out bf16 or fp32 [n_q,H,d]; lse fp32 [H,n_q].
+    """
+    n_q, H, d = q.shape
+    n_kv, Hkv = k.shape[0], k.shape[1]
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise LBError("out must be bfloat16 or float32")
+    _check(lib().lb_attn_run(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, H, Hkv, d, int(out.dtype == torch.float32),
+                             _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                             ctypes.c_void_p(_stream(stream))), "lb_attn_run")
     return out, lse
 
 

@@ -46,13 +46,124 @@ lb_status persistent_workers(int* out) {
   return LB_OK;
 }
 
-lb_status launch_forward(const PlanArgs& p, AttnArgs at, int d, bool out_f32, hipStream_t stream) {
+lb_status check_heads(int32_t heads, int32_t kv_heads, int32_t d) {
+  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return LB_EINVAL;
+  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return LB_EUNSUPPORTED;
+  return LB_OK;
+}
+
+// Checks of the attention half; nothing is enqueued.
+lb_status check_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                    int32_t kv_heads, int32_t d, void* out, float* lse, void* workspace, size_t workspace_bytes) {
+  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
+  if (!q || !out || !lse || !workspace) return LB_EINVAL;
+  if (n_kv > 0 && (!k || !v)) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return LB_EINVAL;
+  if (n_kv > 0 && (!aligned(k, 16) || !aligned(v, 16))) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  if ((int64_t)workspace_bytes < ws_layout(1, 1).total) return LB_EWORKSPACE;
+  return LB_OK;
+}
+
+lb_status launch_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                     int32_t kv_heads, int32_t d, bool out_f32, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
   int workers = 0;
   lb_status st = persistent_workers(&workers);
   if (st != LB_OK) return st;
-  if (launch_plan(p, stream) != hipSuccess) return LB_EHIP;
-  if (launch_attention(at, d, out_f32, workers, stream) != hipSuccess) return LB_EHIP;
+  AttnArgs at{};
+  at.q = q;
+  at.k = n_kv > 0 ? k : q;
+  at.v = n_kv > 0 ? v : q;
+  at.out = out;
+  at.lse = lse;
+  at.n_q = n_q;
+  at.n_kv = n_kv;
+  at.heads = heads;
+  at.kv_heads = kv_heads;
+  at.group = heads / kv_heads;
+  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  at.ws = static_cast<char*>(workspace);
+  at.ws_bytes = (int64_t)workspace_bytes;
+  return launch_attention(at, d, out_f32, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+// Checks and layout of a varlen plan; *L receives the layout when LB_OK.
+lb_status prepare_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
+                              int32_t kv_heads, int32_t d, int32_t mask_kind, void* workspace,
+                              size_t workspace_bytes, WsLayout* L) {
+  if (!cu_seqlens || !workspace) return LB_EINVAL;
+  if (n_seg < 1 || total_tokens < 0) return LB_EINVAL;
+  if (mask_kind != LB_MASK_CAUSAL_DOC && mask_kind != LB_MASK_SHARED_QUESTION) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(cu_seqlens, 4)) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  const int64_t tiles = ceil_div(total_tokens, bm) + n_seg;
+  if (tiles > kSortCap) return LB_EUNSUPPORTED;
+  *L = ws_layout(n_seg, tiles);
+  if ((int64_t)workspace_bytes < L->total) return LB_EWORKSPACE;
   return LB_OK;
+}
+
+lb_status launch_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
+                             int32_t kv_heads, int32_t mask_kind, void* workspace, const WsLayout& L,
+                             hipStream_t stream) {
+  PlanArgs p{};
+  p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
+  p.cu_seqlens = cu_seqlens;
+  p.n_seg = n_seg;
+  p.total_tokens = total_tokens;
+  p.tile_rows = tile_rows_for_group(heads / kv_heads);
+  p.heads = heads;
+  p.kv_heads = kv_heads;
+  p.ws = static_cast<char*>(workspace);
+  p.L = L;
+  return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status prepare_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                             const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
+                             void* workspace, size_t workspace_bytes, WsLayout* L) {
+  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
+  if (!q_pos || !q_doc || !workspace) return LB_EINVAL;
+  if (n_kv > 0 && (!kv_pos || !kv_doc)) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(q_pos, 4) || !aligned(q_doc, 4)) return LB_EINVAL;
+  if (n_kv > 0 && (!aligned(kv_pos, 4) || !aligned(kv_doc, 4))) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  // Runs are unknown to the host: take the largest run capacity the workspace holds.
+  const int64_t max_runs = std::max<int64_t>(1, std::max(n_q, n_kv));
+  auto layout_for = [&](int64_t f) { return ws_layout(f, std::min<int64_t>(kSortCap, ceil_div(n_q, bm) + f)); };
+  if ((int64_t)workspace_bytes < layout_for(1).total) return LB_EWORKSPACE;
+  int64_t lo = 1, hi = max_runs;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (layout_for(mid).total <= (int64_t)workspace_bytes) lo = mid; else hi = mid - 1;
+  }
+  *L = layout_for(lo);
+  return LB_OK;
+}
+
+lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                            const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
+                            const WsLayout& L, hipStream_t stream) {
+  PlanArgs p{};
+  p.mode = kPlanBlock;
+  p.q_pos = q_pos; p.q_doc = q_doc; p.kv_pos = kv_pos; p.kv_doc = kv_doc;
+  p.n_q = n_q;
+  p.n_kv = n_kv;
+  p.tile_rows = tile_rows_for_group(heads / kv_heads);
+  p.heads = heads;
+  p.kv_heads = kv_heads;
+  p.ws = static_cast<char*>(workspace);
+  p.L = L;
+  return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
 bool read_header(const void* ws, size_t bytes, WsHeader* h, hipStream_t s) {
@@ -77,51 +188,53 @@ size_t lb_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t head
   return (size_t)ws_layout(max_segments, tiles).total;
 }
 
+lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
+                         int32_t kv_heads, int32_t d, int32_t mask_kind, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  WsLayout L;
+  lb_status st = prepare_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, d, mask_kind, workspace,
+                                     workspace_bytes, &L);
+  if (st != LB_OK) return st;
+  return launch_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, mask_kind, workspace, L, stream);
+}
+
+lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                        const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  WsLayout L;
+  lb_status st = prepare_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, d, workspace,
+                                    workspace_bytes, &L);
+  if (st != LB_OK) return st;
+  return launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L, stream);
+}
+
+lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                      int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  lb_status st = check_run(q, k, v, n_q, n_kv, heads, kv_heads, d, out, lse, workspace, workspace_bytes);
+  if (st != LB_OK) return st;
+  if (n_q == 0) return LB_OK;
+  return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, out_f32 != 0, out, lse, workspace, workspace_bytes,
+                    stream);
+}
+
 lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                              int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
                              int32_t d, int32_t mask_kind, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !cu_seqlens || !out || !lse || !workspace) return LB_EINVAL;
-  if (n_seg < 1 || total_tokens < 0) return LB_EINVAL;
-  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return LB_EINVAL;
-  if (mask_kind != LB_MASK_CAUSAL_DOC && mask_kind != LB_MASK_SHARED_QUESTION) return LB_EINVAL;
-  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return LB_EUNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-      !aligned(cu_seqlens, 4))
-    return LB_EINVAL;
-  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
-  const int bm = tile_rows_for_group(heads / kv_heads);
-  const int64_t tiles = ceil_div(total_tokens, bm) + n_seg;
-  if (tiles > kSortCap) return LB_EUNSUPPORTED;
-  const WsLayout L = ws_layout(n_seg, tiles);
-  if ((int64_t)workspace_bytes < L.total) return LB_EWORKSPACE;
+  if (!k || !v) return LB_EINVAL;
+  lb_status st = check_run(q, k, v, total_tokens, total_tokens, heads, kv_heads, d, out, lse, workspace,
+                           workspace_bytes);
+  if (st != LB_OK) return st;
+  WsLayout L;
+  st = prepare_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, d, mask_kind, workspace,
+                           workspace_bytes, &L);
+  if (st != LB_OK) return st;
   if (total_tokens == 0) return LB_OK;
-
-  PlanArgs p{};
-  p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
-  p.cu_seqlens = cu_seqlens;
-  p.n_seg = n_seg;
-  p.total_tokens = total_tokens;
-  p.tile_rows = bm;
-  p.kv_heads = kv_heads;
-  p.ws = static_cast<char*>(workspace);
-  p.L = L;
-
-  AttnArgs at{};
-  at.q = q; at.k = k; at.v = v;
-  at.out = out;
-  at.lse = lse;
-  at.n_q = total_tokens;
-  at.n_kv = total_tokens;
-  at.heads = heads;
-  at.kv_heads = kv_heads;
-  at.group = heads / kv_heads;
-  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
-  at.ws = static_cast<char*>(workspace);
-  at.off_tiles = L.off_tiles;
-  at.off_order = L.off_order;
-  at.off_workers = L.off_workers;
-  return launch_forward(p, at, d, /*out_f32=*/false, stream);
+  st = launch_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, mask_kind, workspace, L, stream);
+  if (st != LB_OK) return st;
+  return launch_run(q, k, v, total_tokens, total_tokens, heads, kv_heads, d, false, out, lse, workspace,
+                    workspace_bytes, stream);
 }
 
 lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,
@@ -129,58 +242,21 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
                             const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
-  if (!q_shard || !q_pos || !q_doc || !out || !lse || !workspace) return LB_EINVAL;
-  if (n_kv > 0 && (!kv_chunk || !kv_pos || !kv_doc)) return LB_EINVAL;
-  if (heads <= 0 || kv_heads <= 0 || heads % kv_heads != 0) return LB_EINVAL;
-  if (!group_supported(heads, kv_heads) || (d != 64 && d != 128)) return LB_EUNSUPPORTED;
-  if (!aligned(q_shard, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(q_pos, 4) || !aligned(q_doc, 4))
-    return LB_EINVAL;
-  if (n_kv > 0 && (!aligned(kv_chunk, 16) || !aligned(kv_pos, 4) || !aligned(kv_doc, 4))) return LB_EINVAL;
-  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
-  const int bm = tile_rows_for_group(heads / kv_heads);
-  // Runs are unknown to the host: take the largest fragment capacity the workspace holds.
-  const int64_t max_runs = std::max<int64_t>(1, std::max(n_q, n_kv));
-  auto layout_for = [&](int64_t f) {
-    return ws_layout(f, std::min<int64_t>(kSortCap, ceil_div(n_q, bm) + f));
-  };
-  if ((int64_t)workspace_bytes < layout_for(1).total) return LB_EWORKSPACE;
-  int64_t lo = 1, hi = max_runs;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) / 2;
-    if (layout_for(mid).total <= (int64_t)workspace_bytes) lo = mid; else hi = mid - 1;
-  }
-  const WsLayout L = layout_for(lo);
+  const __bf16* kbase = static_cast<const __bf16*>(kv_chunk);
+  const __bf16* vbase = kbase ? kbase + (int64_t)n_kv * kv_heads * d : nullptr;
+  if (n_kv < 0 || kv_heads <= 0 || d <= 0) return LB_EINVAL;
+  lb_status st = check_run(q_shard, kbase, vbase, n_q, n_kv, heads, kv_heads, d, out, lse, workspace,
+                           workspace_bytes);
+  if (st != LB_OK) return st;
+  WsLayout L;
+  st = prepare_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, d, workspace, workspace_bytes,
+                          &L);
+  if (st != LB_OK) return st;
   if (n_q == 0) return LB_OK;
-
-  PlanArgs p{};
-  p.mode = kPlanBlock;
-  p.q_pos = q_pos; p.q_doc = q_doc; p.kv_pos = kv_pos; p.kv_doc = kv_doc;
-  p.n_q = n_q;
-  p.n_kv = n_kv;
-  p.tile_rows = bm;
-  p.kv_heads = kv_heads;
-  p.ws = static_cast<char*>(workspace);
-  p.L = L;
-
-  const __bf16* kbase = static_cast<const __bf16*>(n_kv > 0 ? kv_chunk : q_shard);
-  AttnArgs at{};
-  at.q = q_shard;
-  at.k = kbase;
-  at.v = n_kv > 0 ? kbase + (int64_t)n_kv * kv_heads * d : kbase;
-  at.out = out;
-  at.lse = lse;
-  at.n_q = n_q;
-  at.n_kv = n_kv;
-  at.heads = heads;
-  at.kv_heads = kv_heads;
-  at.group = heads / kv_heads;
-  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
-  at.ws = static_cast<char*>(workspace);
-  at.off_tiles = L.off_tiles;
-  at.off_order = L.off_order;
-  at.off_workers = L.off_workers;
-  return launch_forward(p, at, d, /*out_f32=*/true, stream);
+  st = launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L, stream);
+  if (st != LB_OK) return st;
+  return launch_run(q_shard, kbase, vbase, n_q, n_kv, heads, kv_heads, d, true, out, lse, workspace,
+                    workspace_bytes, stream);
 }
 
 lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const float* lse_b, int32_t n_rows,

@@ -132,9 +132,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int hh = lane >> 5;
 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
-  const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + a.off_tiles);
-  const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.off_order);
-  const int n_items = hdr->n_items;
+  // A missing plan, or one made for other shapes or another workspace size, could index
+  // outside this launch's buffers: then run nothing and flag it.
+  const int64_t n_tiles_hdr = hdr->n_tiles;
+  const bool mismatch = hdr->magic != kPlanMagic || hdr->plan_n_q != a.n_q || hdr->plan_n_kv != a.n_kv ||
+                        hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
+                        hdr->n_items != n_tiles_hdr * a.kv_heads || n_tiles_hdr < 0 ||
+                        hdr->off_tiles < kWorkersOffset || hdr->off_order < kWorkersOffset ||
+                        hdr->off_tiles + n_tiles_hdr * (int64_t)sizeof(lb_plan_tile) > a.ws_bytes ||
+                        hdr->off_order + n_tiles_hdr * 4 > a.ws_bytes;
+  const int n_items = mismatch ? 0 : hdr->n_items;
+  const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + (mismatch ? 0 : hdr->off_tiles));
+  const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + (mismatch ? 0 : hdr->off_order));
+  if (mismatch && blockIdx.x == 0 && tid == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
 
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
@@ -329,9 +339,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     rec.pairs = my_pairs;
     rec.items = my_items;
     rec.reserved = 0;
-    lb_worker_record* recs = reinterpret_cast<lb_worker_record*>(a.ws + a.off_workers);
+    lb_worker_record* recs = reinterpret_cast<lb_worker_record*>(a.ws + kWorkersOffset);
     recs[blockIdx.x] = rec;
     if (blockIdx.x == 0) hdr->n_workers = gridDim.x;
+    // The last workgroup out rewinds the queue: every workgroup has made its final pop
+    // before counting itself done, so no pop can follow the reset.
+    __threadfence();
+    if (atomicAdd(&hdr->done, 1) == (int)gridDim.x - 1) {
+      atomicExch(&hdr->queue_head, 0);
+      atomicExch(&hdr->done, 0);
+    }
   }
 }
 

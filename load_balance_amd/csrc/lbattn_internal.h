@@ -40,8 +40,14 @@ struct WsHeader {
   int64_t off_frags, off_kvruns, off_tiles, off_order, off_workers;
   int32_t cap_frags, cap_tiles;
   int64_t total_pairs;  // sum of tile costs (one head)
-  int32_t pad[10];
+  int32_t plan_n_q, plan_n_kv, plan_kv_heads, plan_heads;  // shapes the plan was made for
+  int32_t done;         // attention workgroups that found the queue empty
+  uint32_t magic;       // kPlanMagic once a plan has been written
+  int32_t pad[4];
 };
+
+constexpr uint32_t kPlanMagic = 0x4C424154u;
+constexpr int64_t kWorkersOffset = 256;  // worker records sit right after the header
 static_assert(sizeof(WsHeader) <= 256, "header must fit its slot");
 
 // A query fragment with its key spans before per-tile clipping.
@@ -68,13 +74,13 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 inline WsLayout ws_layout(int64_t cap_frags, int64_t cap_tiles) {
   WsLayout L{};
-  int64_t o = 256;
+  int64_t o = kWorkersOffset;
+  L.off_workers = o; o = align256(o + kMaxWorkers * (int64_t)sizeof(lb_worker_record));
   L.off_frags = o;   o = align256(o + cap_frags * (int64_t)sizeof(Frag));
   L.off_ftile = o;   o = align256(o + (cap_frags + 1) * (int64_t)sizeof(int32_t));
   L.off_kvruns = o;  o = align256(o + cap_frags * (int64_t)sizeof(KvRun));
   L.off_tiles = o;   o = align256(o + cap_tiles * (int64_t)sizeof(lb_plan_tile));
   L.off_order = o;   o = align256(o + cap_tiles * (int64_t)sizeof(int32_t));
-  L.off_workers = o; o = align256(o + kMaxWorkers * (int64_t)sizeof(lb_worker_record));
   L.total = o;
   L.cap_frags = (int32_t)cap_frags;
   L.cap_tiles = (int32_t)cap_tiles;
@@ -89,7 +95,7 @@ struct PlanArgs {
   int32_t n_seg, total_tokens;
   const int32_t *q_pos, *q_doc, *kv_pos, *kv_doc;
   int32_t n_q, n_kv;
-  int32_t tile_rows, kv_heads;
+  int32_t tile_rows, heads, kv_heads;
   char* ws;
   WsLayout L;
 };
@@ -104,7 +110,7 @@ struct AttnArgs {
   int32_t heads, kv_heads, group;
   float scale_log2;  // softmax scale * log2(e)
   char* ws;
-  int64_t off_tiles, off_order, off_workers;
+  int64_t ws_bytes;
 };
 
 struct MergeArgs {

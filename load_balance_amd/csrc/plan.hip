@@ -278,6 +278,12 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
     hdr->cap_frags = a.L.cap_frags;
     hdr->cap_tiles = a.L.cap_tiles;
     hdr->total_pairs = ok ? (int64_t)sh.pairs : 0;
+    hdr->plan_n_q = a.mode == kPlanBlock ? a.n_q : a.total_tokens;
+    hdr->plan_n_kv = a.mode == kPlanBlock ? a.n_kv : a.total_tokens;
+    hdr->plan_kv_heads = a.kv_heads;
+    hdr->plan_heads = a.heads;
+    hdr->done = 0;
+    hdr->magic = kPlanMagic;
   }
 }
 

@@ -112,6 +112,21 @@ def test_block_host_checks(L):
     assert call(n_q=0, kv=None, n_kv=0) == LB_OK
 
 
+def test_split_host_checks(L):
+    n = 64
+    need = L.lb_workspace_bytes(n, 3, 2, 2)
+    assert L.lb_plan_varlen(None, 3, n, 2, 2, 64, 0, FAKE, need, None) == LB_EINVAL
+    assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 5, FAKE, need, None) == LB_EINVAL
+    assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 0, FAKE, need - 1, None) == LB_EWORKSPACE
+    assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 48, 0, FAKE, need, None) == LB_EUNSUPPORTED
+    assert L.lb_plan_block(None, FAKE, n, FAKE, FAKE, n, 2, 2, 64, FAKE, need, None) == LB_EINVAL
+    assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, FAKE, 64, None) == LB_EWORKSPACE
+    assert L.lb_attn_run(FAKE, FAKE, FAKE, n, n, 2, 2, 64, 0, None, FAKE, FAKE, need, None) == LB_EINVAL
+    assert L.lb_attn_run(FAKE, None, FAKE, n, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, need, None) == LB_EINVAL
+    assert L.lb_attn_run(FAKE, FAKE, FAKE, n, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, 100, None) == LB_EWORKSPACE
+    assert L.lb_attn_run(FAKE, FAKE, FAKE, 0, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, need, None) == LB_OK
+
+
 def test_merge_host_checks(L):
     assert L.lb_lse_merge(None, FAKE, FAKE, FAKE, 4, 2, 8, None) == LB_EINVAL
     assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, None) == LB_EUNSUPPORTED

@@ -393,6 +393,45 @@ def test_bad_cu_seqlens_sets_device_error():
 
 
 # --------------------------------------------------------------------------
+# split entry points: one plan, several runs
+# --------------------------------------------------------------------------
+def test_plan_once_run_many_equals_fused():
+    r = np.random.default_rng(21)
+    lengths = [300, 5, 1200, 77]
+    T, H, Hkv, d = sum(lengths), 32, 8, 128
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=H, kv_heads=Hkv,
+                d=d, q=q, k=k, v=v)
+    ref_out, ref_lse, _ = run_varlen(pack)
+    cu = torch.from_numpy(pack["cu_seqlens"]).cuda()
+    ws = lb.plan_varlen(cu, T, H, Hkv, d)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    for _ in range(3):  # the queue rewinds itself after every run
+        out = torch.empty_like(qd)
+        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        lb.attn_run(qd, kd, vd, out, lse, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    assert lb.read_device_error(ws) == 0
+
+
+def test_run_against_wrong_plan_does_nothing():
+    T, H, Hkv, d = 256, 8, 2, 64
+    qd = torch.zeros((T, H, d), dtype=torch.bfloat16, device="cuda")
+    kd = torch.zeros((T, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((T, H, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), 7.0, device="cuda")
+    ws = torch.zeros(lb.workspace_bytes(T, 4, H, Hkv), dtype=torch.uint8, device="cuda")  # never planned
+    lb.attn_run(qd, kd, kd, out, lse, ws)
+    assert lb.read_device_error(ws) & lb.DEVERR_PLAN
+    cu = torch.tensor([0, 100, 200], dtype=torch.int32, device="cuda")
+    lb.plan_varlen(cu, 200, H, Hkv, d, workspace=ws)  # plan for 200 tokens, run with 256
+    lb.attn_run(qd, kd, kd, out, lse, ws)
+    assert lb.read_device_error(ws) & lb.DEVERR_PLAN
+    assert torch.all(out == 3.0) and torch.all(lse == 7.0)
+
+
+# --------------------------------------------------------------------------
 # lse_merge
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [64, 128])
