@@ -39,8 +39,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = kBlockN;
+constexpr int kStages = 3;  // LDS ring: the lagging waves still read block j-1 while block j+1 lands
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -120,9 +122,17 @@ struct KvLoader {
   }
 };
 
+// Uniform description of one key block: which span, which block of it.
+struct KvBlock {
+  int key0;   // first key of the block, relative to its span
+  int len;    // keys of the span (already clipped to the tile's last row)
+  int pos0;   // mask position of the span's first key
+  int start;  // first key row of the span
+};
+
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * Lds<D>::stage];
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
@@ -130,6 +140,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  // Waves 0-3 and 4-7 share the four SIMDs pairwise.  The second group runs half a key
+  // block behind the first (softmax and PV of block j-1, then QK^T of block j), so on every
+  // SIMD one wave feeds the matrix cores while the other runs the exponentials.
+  const bool lagging = wave >= 4;
 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
   // A missing plan, or one made for other shapes or another workspace size, could index
@@ -154,6 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int head_in_group = wave % G;
   const int wr0 = (wave / G) * kRowsPerWave;  // first tile row of this wave
   const float c = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   uint64_t t_start = 0;
   if (tid == 0) t_start = device_clock();
@@ -171,20 +186,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 
     const int g = item % a.kv_heads;
     const lb_plan_tile* T = &tiles[order[item / a.kv_heads]];
-    const int q_start = T->q_start, q_len = T->q_len, q_pos0 = T->q_pos0;
-    const int n_spans = T->n_spans;
+    // tile fields, read once and kept wave-uniform
+    const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
+    const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
+    const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
+    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    int sp_start[LB_MAX_SPANS], sp_len[LB_MAX_SPANS], sp_pos0[LB_MAX_SPANS];
     int n_kv_tiles = 0;
-    for (int s = 0; s < n_spans; ++s) n_kv_tiles += (T->k_len[s] + BN - 1) / BN;
+#pragma unroll
+    for (int s = 0; s < LB_MAX_SPANS; ++s) {
+      sp_start[s] = __builtin_amdgcn_readfirstlane(T->k_start[s]);
+      sp_len[s] = s < n_spans ? __builtin_amdgcn_readfirstlane(T->k_len[s]) : 0;
+      sp_pos0[s] = __builtin_amdgcn_readfirstlane(T->k_pos0[s]);
+      n_kv_tiles += (sp_len[s] + BN - 1) / BN;
+    }
     if (tid == 0) {
       ++my_items;
       my_pairs += T->cost * G;
     }
+    auto pick = [](const int (&v)[LB_MAX_SPANS], int s) {
+      return s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+    };
 
     const int head = g * G + head_in_group;
     const int my_row = wr0 + l32;                 // tile row owned by this lane
     const bool wave_rows = wr0 < q_len;           // this wave has at least one real row
     const int wave_last = min(wr0 + kRowsPerWave, q_len) - 1;
     const int64_t grow = (int64_t)q_start + my_row;
+    const int qpos = q_pos0 + my_row;
 
     // Q fragment: B operand of S^T = K Q^T; lane holds Q[q = l32][d = kk*16 + hh*8 .. +8].
     bf16x8 qreg[D / 16];
@@ -201,104 +230,119 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
     float m_used = -__builtin_inff();
     float l_part = 0.f;
+    f32x16 acc_s[2];
 
-    // prologue: first key block into stage 0 (spans with zero keys never reach the plan)
-    int cur_s = 0, cur_t = 0;
-    if (n_kv_tiles > 0) {
-      ld.load(K, V, T->k_start[0], T->k_len[0], a.kv_heads, g, tid);
-      ld.store(smem, tid);
-    }
+    // does key block b have any visible pair for this wave's real rows?
+    auto live = [&](const KvBlock& b) { return wave_rows && b.pos0 + b.key0 <= q_pos0 + wave_last; };
 
-    for (int it = 0; it < n_kv_tiles; ++it) {
-      __syncthreads();
-      // the block computed now (span cur_s, block cur_t) and the one loaded next
-      const int s_len = T->k_len[cur_s], s_pos0 = T->k_pos0[cur_s];
-      const int kt = cur_t;
-      int nx_s = cur_s, nx_t = cur_t + 1;
-      if (nx_t * BN >= s_len) { ++nx_s; nx_t = 0; }
-      const bool has_next = it + 1 < n_kv_tiles;
-      if (has_next) {
-        const int k0 = T->k_start[nx_s] + nx_t * BN;
-        ld.load(K, V, k0, T->k_len[nx_s] - nx_t * BN, a.kv_heads, g, tid);
+    auto qk = [&](const char* ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        acc_s[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds<D>::kStride + (kk * 16 + hh * 8) * 2);
+          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], acc_s[kb], 0, 0, 0);
+        }
       }
-      const char* ks = smem + (it & 1) * Lds<D>::stage;
-      const char* vs = ks + Lds<D>::kBytes;
+    };
 
-      const int key0 = kt * BN;                     // first key of the block, relative to the span
-      const int kpos_first = s_pos0 + key0;
-      const int kpos_last = kpos_first + BN - 1;
-      const bool skip = !wave_rows || kpos_first > q_pos0 + wave_last;
-      if (!skip) {
-        const bool full = key0 + BN <= s_len && kpos_last <= q_pos0 + wr0;
-        // ---- S^T = K Q^T ----
-        f32x16 acc_s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          acc_s[kb] = f32x16{};
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            const bf16x8 kf =
-                *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds<D>::kStride + (kk * 16 + hh * 8) * 2);
-            acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], acc_s[kb], 0, 0, 0);
-          }
-        }
-        // ---- mask (diagonal / ragged blocks only) ----
-        if (!full) {
-          const int qpos = q_pos0 + my_row;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + kb * 32 + (i / 4) * 8 + hh * 4 + (i % 4);
-              const bool vis = key < s_len && s_pos0 + key <= qpos;
-              if (!vis) acc_s[kb][i] = -__builtin_inff();
-            }
-        }
-        // ---- online softmax ----
-        float mx = -__builtin_inff();
+    // mask (diagonal / ragged blocks only), online softmax, O^T += V^T P^T
+    auto softmax_pv = [&](const KvBlock& b, const char* vs) {
+      const bool full = b.key0 + BN <= b.len && b.pos0 + b.key0 + BN - 1 <= q_pos0 + wr0;
+      if (!full) {
+        // key k of the block is visible iff k < lim (span end, and position <= this row's)
+        const int lim = min(b.len, qpos - b.pos0 + 1) - b.key0 - hh * 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_tile = mx * c;
-        const bool need = m_tile > m_used + kRescaleThreshold;  // false when the row saw nothing
-        if (__any(need)) {
-          const float m_new = need ? m_tile : m_used;
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.0f;
-          m_used = m_new;
-          l_part *= alpha;
+          for (int i = 0; i < 16; ++i)
+            if (!(kb * 32 + (i / 4) * 8 + (i % 4) < lim)) acc_s[kb][i] = -__builtin_inff();
+      }
+      float mx = -__builtin_inff();
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-        }
-        const float m_sub = m_used == -__builtin_inff() ? 0.0f : m_used;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j], c, -m_sub));
-              l_part += p;
-              pf[kb * 2 + cc][j] = (__bf16)p;
-            }
-        // ---- O^T += V^T P^T ----
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = mx * c;
+      const bool need = m_tile > m_used + kRescaleThreshold;  // false when the row saw nothing
+      if (__any(need)) {
+        const float m_new = need ? m_tile : m_used;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.0f;
+        m_used = m_new;
+        l_part *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int ks16 = 0; ks16 < 4; ++ks16) {
-            const bf16x8 vf =
-                *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
-            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks16], acc_o[db], 0, 0, 0);
-          }
+          for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
       }
-      if (has_next) ld.store(smem + ((it + 1) & 1) * Lds<D>::stage, tid);
+      const float m_sub = m_used == -__builtin_inff() ? 0.0f : m_used;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j], c, -m_sub));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j + 1], c, -m_sub));
+            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            // the row sum takes exactly the bf16 weights that enter the PV product
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
+            pf[kb * 2 + cc][j] = pp[0];
+            pf[kb * 2 + cc][j + 1] = pp[1];
+          }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ks16 = 0; ks16 < 4; ++ks16) {
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks16], acc_o[db], 0, 0, 0);
+        }
+    };
+
+    // prologue: first key block into stage 0 (spans in the plan are never empty)
+    int cur_s = 0, cur_t = 0;
+    if (n_kv_tiles > 0) {
+      ld.load(K, V, sp_start[0], sp_len[0], a.kv_heads, g, tid);
+      ld.store(smem, tid);
+    }
+    KvBlock prev{0, 0, 0, 0};
+    bool prev_live = false;
+
+    for (int it = 0; it < n_kv_tiles; ++it) {
+      __syncthreads();
+      const KvBlock cur{cur_t * BN, pick(sp_len, cur_s), pick(sp_pos0, cur_s), pick(sp_start, cur_s)};
+      int nx_s = cur_s, nx_t = cur_t + 1;
+      if (nx_t * BN >= cur.len) { ++nx_s; nx_t = 0; }
+      const bool has_next = it + 1 < n_kv_tiles;
+      if (has_next) {
+        const int nlen = pick(sp_len, nx_s);
+        ld.load(K, V, pick(sp_start, nx_s) + nx_t * BN, nlen - nx_t * BN, a.kv_heads, g, tid);
+      }
+      const char* stage = smem + (it % kStages) * Lds<D>::stage;
+      const char* prev_stage = smem + ((it + kStages - 1) % kStages) * Lds<D>::stage;
+      const bool cur_live = live(cur);
+      if (!lagging) {
+        if (cur_live) {
+          qk(stage);
+          softmax_pv(cur, stage + Lds<D>::kBytes);
+        }
+      } else {
+        if (prev_live) softmax_pv(prev, prev_stage + Lds<D>::kBytes);
+        if (cur_live) qk(stage);
+      }
+      if (has_next) ld.store(smem + ((it + 1) % kStages) * Lds<D>::stage, tid);
+      prev = cur;
+      prev_live = cur_live;
       cur_s = nx_s;
       cur_t = nx_t;
     }
+    if (lagging && prev_live)
+      softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
 
     // ---- epilogue: out = O / l, lse = ln(sum exp) ----
     const float l_tot = l_part + __shfl_xor(l_part, 32);
