@@ -255,7 +255,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longtail",
-                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny"])
+                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,6 +267,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.workload == "copy":
+        # calibration for rocprofv3's FETCH_SIZE / WRITE_SIZE: a plain 1 GiB device copy
+        a = torch.ones(1 << 28, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "copy", "bytes_per_copy": a.numel() * 4, "copies": 3}), flush=True)
+        return
     import load_balance_amd as lb
     import workloads
 
