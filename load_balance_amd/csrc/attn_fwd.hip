@@ -70,31 +70,42 @@ __device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_m
 __device__ __forceinline__ uint32_t hw_id_reg() { return __builtin_amdgcn_s_getreg((31 << 11) | 4); }
 __device__ __forceinline__ uint32_t xcc_id_reg() { return __builtin_amdgcn_s_getreg((15 << 11) | 20); }
 
+// Raw buffer resource word 3 for gfx9-family dword loads (no format conversion).
+constexpr int kBufferFlags = 0x00020000;
+
 template <int D>
 struct KvLoader {
   u32x4 kreg[Lds<D>::kPerThread];
   u32x4 vreg[2];
+  int k_off[Lds<D>::kPerThread];  // byte offset of this thread's 16-byte piece inside a block
+  int v_off[2];
 
-  // Loads key block [k0, k0 + BN) of a span into registers; rows at or past `valid` read as zero.
-  __device__ __forceinline__ void load(const __bf16* __restrict__ K, const __bf16* __restrict__ V, int k0,
-                                       int valid, int kv_heads, int g, int tid) {
+  __device__ __forceinline__ void init(int row_bytes, int tid) {
 #pragma unroll
     for (int e = 0; e < Lds<D>::kPerThread; ++e) {
       const int c = tid + e * kThreads;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      kreg[e] = u32x4{0, 0, 0, 0};
-      if (row < valid)
-        kreg[e] = *reinterpret_cast<const u32x4*>(K + ((int64_t)(k0 + row) * kv_heads + g) * D + ch * 8);
+      k_off[e] = (c / (D / 8)) * row_bytes + (c % (D / 8)) * 16;
     }
-    if (tid < Lds<D>::vUnits) {
-      const int p = tid % (BN / 2), ch = tid / (BN / 2);
+    const int p = tid % (BN / 2), ch = tid / (BN / 2);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = 2 * p + e;
-        vreg[e] = u32x4{0, 0, 0, 0};
-        if (row < valid)
-          vreg[e] = *reinterpret_cast<const u32x4*>(V + ((int64_t)(k0 + row) * kv_heads + g) * D + ch * 8);
-      }
+    for (int e = 0; e < 2; ++e) v_off[e] = (2 * p + e) * row_bytes + ch * 16;
+  }
+
+  // Loads key rows [k0, k0 + BN) of kv head g into registers.  The buffer range ends after
+  // `valid` rows, and the hardware returns zeros beyond it: no bounds code, no zero fill.
+  __device__ __forceinline__ void load(const char* K, const char* V, int k0, int valid, int row_bytes, int g,
+                                       int tid) {
+    const int64_t base = (int64_t)k0 * row_bytes + (int64_t)g * D * 2;
+    const int nbytes = min(valid, BN) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, nbytes,
+                                                                        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, nbytes,
+                                                                        kBufferFlags);
+#pragma unroll
+    for (int e = 0; e < Lds<D>::kPerThread; ++e) kreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[e], 0, 0);
+    if (tid < Lds<D>::vUnits) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[e], 0, 0);
     }
   }
 
@@ -161,8 +172,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   if (mismatch && blockIdx.x == 0 && tid == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
 
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
-  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
+  const char* Kb = reinterpret_cast<const char*>(a.k);
+  const char* Vb = reinterpret_cast<const char*>(a.v);
+  const int row_bytes = a.kv_heads * D * 2;  // one token's K (or V) across all kv heads
 
   const int G = a.group;
   const int head_in_group = wave % G;
@@ -176,6 +188,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   int64_t my_pairs = 0;
 
   KvLoader<D> ld;
+  ld.init(row_bytes, tid);
 
   for (;;) {
     if (tid == 0) s_item = atomicAdd(&hdr->queue_head, 1);
@@ -191,21 +204,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
     const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
-    int sp_start[LB_MAX_SPANS], sp_len[LB_MAX_SPANS], sp_pos0[LB_MAX_SPANS];
+    // Span fields ride in the lanes of one register: lanes 0-3 k_start, 4-7 k_len, 8-11 k_pos0;
+    // a wave reads them back with v_readlane only when it steps into a new span.
+    const int span_v = lane < 3 * LB_MAX_SPANS ? (&T->k_start[0])[lane] : 0;
     int n_kv_tiles = 0;
 #pragma unroll
-    for (int s = 0; s < LB_MAX_SPANS; ++s) {
-      sp_start[s] = __builtin_amdgcn_readfirstlane(T->k_start[s]);
-      sp_len[s] = s < n_spans ? __builtin_amdgcn_readfirstlane(T->k_len[s]) : 0;
-      sp_pos0[s] = __builtin_amdgcn_readfirstlane(T->k_pos0[s]);
-      n_kv_tiles += (sp_len[s] + BN - 1) / BN;
-    }
+    for (int s = 0; s < LB_MAX_SPANS; ++s)
+      if (s < n_spans) n_kv_tiles += (__builtin_amdgcn_readlane(span_v, LB_MAX_SPANS + s) + BN - 1) / BN;
     if (tid == 0) {
       ++my_items;
       my_pairs += T->cost * G;
     }
-    auto pick = [](const int (&v)[LB_MAX_SPANS], int s) {
-      return s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+    auto span_of = [&](int s) {
+      KvBlock b;
+      b.key0 = 0;
+      b.start = __builtin_amdgcn_readlane(span_v, s);
+      b.len = __builtin_amdgcn_readlane(span_v, LB_MAX_SPANS + s);
+      b.pos0 = __builtin_amdgcn_readlane(span_v, 2 * LB_MAX_SPANS + s);
+      return b;
     };
 
     const int head = g * G + head_in_group;
@@ -305,9 +321,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     };
 
     // prologue: first key block into stage 0 (spans in the plan are never empty)
-    int cur_s = 0, cur_t = 0;
+    int cur_s = 0;
+    KvBlock cur = span_of(0);
     if (n_kv_tiles > 0) {
-      ld.load(K, V, sp_start[0], sp_len[0], a.kv_heads, g, tid);
+      ld.load(Kb, Vb, cur.start, cur.len, row_bytes, g, tid);
       ld.store(smem, tid);
     }
     KvBlock prev{0, 0, 0, 0};
@@ -315,14 +332,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 
     for (int it = 0; it < n_kv_tiles; ++it) {
       __syncthreads();
-      const KvBlock cur{cur_t * BN, pick(sp_len, cur_s), pick(sp_pos0, cur_s), pick(sp_start, cur_s)};
-      int nx_s = cur_s, nx_t = cur_t + 1;
-      if (nx_t * BN >= cur.len) { ++nx_s; nx_t = 0; }
-      const bool has_next = it + 1 < n_kv_tiles;
-      if (has_next) {
-        const int nlen = pick(sp_len, nx_s);
-        ld.load(K, V, pick(sp_start, nx_s) + nx_t * BN, nlen - nx_t * BN, a.kv_heads, g, tid);
+      // the block after this one: next 64 keys of this span, or the first of the next span
+      KvBlock nxt = cur;
+      nxt.key0 += BN;
+      int nx_s = cur_s;
+      if (nxt.key0 >= cur.len) {
+        ++nx_s;
+        if (nx_s < n_spans) nxt = span_of(nx_s);
       }
+      const bool has_next = it + 1 < n_kv_tiles;
+      if (has_next) ld.load(Kb, Vb, nxt.start + nxt.key0, nxt.len - nxt.key0, row_bytes, g, tid);
       const char* stage = smem + (it % kStages) * Lds<D>::stage;
       const char* prev_stage = smem + ((it + kStages - 1) % kStages) * Lds<D>::stage;
       const bool cur_live = live(cur);
@@ -338,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       if (has_next) ld.store(smem + ((it + 1) % kStages) * Lds<D>::stage, tid);
       prev = cur;
       prev_live = cur_live;
+      cur = nxt;
       cur_s = nx_s;
-      cur_t = nx_t;
     }
     if (lagging && prev_live)
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
