@@ -163,6 +163,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const bool mismatch = hdr->magic != kPlanMagic || hdr->plan_n_q != a.n_q || hdr->plan_n_kv != a.n_kv ||
                         hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
                         hdr->n_items != n_tiles_hdr * a.kv_heads || n_tiles_hdr < 0 ||
+                        (hdr->n_queues != 1 && hdr->n_queues != kXcds) || a.kv_heads % hdr->n_queues != 0 ||
+                        (int64_t)hdr->per_queue * hdr->n_queues != hdr->n_items ||
                         hdr->off_tiles < kWorkersOffset || hdr->off_order < kWorkersOffset ||
                         hdr->off_tiles + n_tiles_hdr * (int64_t)sizeof(lb_plan_tile) > a.ws_bytes ||
                         hdr->off_order + n_tiles_hdr * 4 > a.ws_bytes;
@@ -190,15 +192,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   KvLoader<D> ld;
   ld.init(row_bytes, tid);
 
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(&hdr->queue_head, 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (item >= n_items) break;
+  // Work queues: with one queue per XCD, a workgroup serves its own XCD's queue (kv heads
+  // q, q + 8, ...) so the XCD's L2 keeps those heads' keys and values, and steals from the
+  // other queues, in turn, once its own is empty.
+  const int n_queues = mismatch ? 1 : hdr->n_queues;
+  const int per_queue = mismatch ? 0 : hdr->per_queue;
+  const int heads_per_queue = a.kv_heads / n_queues;
+  int queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
+  int queues_left = n_queues;
 
-    const int g = item % a.kv_heads;
-    const lb_plan_tile* T = &tiles[order[item / a.kv_heads]];
+  for (;;) {
+    if (tid == 0) {
+      int k = per_queue;
+      while (queues_left > 0) {
+        k = atomicAdd(&hdr->queue_head[queue], 1);
+        if (k < per_queue) break;
+        queue = queue + 1 == n_queues ? 0 : queue + 1;
+        --queues_left;
+      }
+      s_item = queues_left > 0 ? queue * per_queue + k : -1;
+    }
+    __syncthreads();
+    const int qitem = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (qitem < 0 || n_items == 0) break;
+
+    // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
+    const int q_of = qitem / max(per_queue, 1), k_in = qitem - q_of * per_queue;
+    const int g = q_of + n_queues * (k_in % heads_per_queue);
+    const lb_plan_tile* T = &tiles[order[k_in / heads_per_queue]];
     // tile fields, read once and kept wave-uniform
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
@@ -236,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 x = u32x4{0, 0, 0, 0};
-      if (wave_rows && my_row < q_len)
+      if (n_kv_tiles > 0 && wave_rows && my_row < q_len)  // an item with no keys only writes lse
         x = *reinterpret_cast<const u32x4*>(Q + (grow * a.heads + head) * D + kk * 16 + hh * 8);
       qreg[kk] = __builtin_bit_cast(bf16x8, x);
     }
@@ -409,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     // before counting itself done, so no pop can follow the reset.
     __threadfence();
     if (atomicAdd(&hdr->done, 1) == (int)gridDim.x - 1) {
-      atomicExch(&hdr->queue_head, 0);
+      for (int q = 0; q < kXcds; ++q) atomicExch(&hdr->queue_head[q], 0);
       atomicExch(&hdr->done, 0);
     }
   }

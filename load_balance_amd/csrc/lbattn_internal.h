@@ -23,6 +23,7 @@ constexpr int kBlockN = 64;
 constexpr int kPlanThreads = 1024;
 constexpr int kSortCap = 16384;     // tiles per call
 constexpr int kMaxWorkers = 2048;   // persistent workgroups per launch
+constexpr int kXcds = 8;            // accelerator complex dies (XCDs) of an MI355X, one L2 each
 
 inline __host__ __device__ int tile_rows_for_group(int group) { return kRowsPerWave * kWaves / group; }
 
@@ -33,7 +34,7 @@ struct WsHeader {
   int32_t n_frags;      // query fragments
   int32_t n_tiles;
   int32_t n_items;      // n_tiles * kv_heads (0 after an error)
-  int32_t queue_head;   // next item to hand out
+  int32_t n_queues;     // work queues: one per XCD when kv_heads is a multiple of kXcds, else 1
   int32_t n_kvruns;
   int32_t tile_rows;
   int32_t n_workers;    // persistent workgroups of the last attention launch
@@ -41,9 +42,11 @@ struct WsHeader {
   int32_t cap_frags, cap_tiles;
   int64_t total_pairs;  // sum of tile costs (one head)
   int32_t plan_n_q, plan_n_kv, plan_kv_heads, plan_heads;  // shapes the plan was made for
-  int32_t done;         // attention workgroups that found the queue empty
+  int32_t done;         // attention workgroups that found every queue empty
   uint32_t magic;       // kPlanMagic once a plan has been written
-  int32_t pad[4];
+  int32_t per_queue;    // items per queue
+  int32_t pad[3];
+  int32_t queue_head[8];  // next item of each queue
 };
 
 constexpr uint32_t kPlanMagic = 0x4C424154u;

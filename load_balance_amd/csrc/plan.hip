@@ -25,28 +25,38 @@ namespace {
 constexpr int NT = kPlanThreads;
 constexpr uint64_t kCostMask = (uint64_t(1) << 40) - 1;  // costs < 2^40 (checked on the host)
 
+constexpr int kPlanWaves = NT / 64;
+
 struct PlanShared {
   uint64_t keys[kSortCap];
-  int32_t scan[NT];
+  int32_t wave_sum[kPlanWaves];
   int32_t err;
   unsigned long long pairs;
 };
 
-// Exclusive prefix sum of one value per thread across the workgroup.
-__device__ int block_excl_scan(int v, int32_t* s, int* total) {
-  const int tid = threadIdx.x;
-  s[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int x = tid >= off ? s[tid - off] : 0;
-    __syncthreads();
-    s[tid] += x;
-    __syncthreads();
+// Exclusive prefix sum of one value per thread across the workgroup (thread order),
+// with the workgroup total in *total: a shuffle scan inside each wave, then the wave
+// totals through LDS.  Two barriers.
+__device__ int block_excl_scan(int v, PlanShared& sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(incl, off);
+    if (lane >= off) incl += x;
   }
-  const int incl = s[tid];
-  *total = s[NT - 1];
+  if (lane == 63) sh.wave_sum[w] = incl;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) {
+    const int c = sh.wave_sum[i];
+    base += i < w ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
 }
 
 // Sum over integers y < x of clamp(y, 0, L).
@@ -68,25 +78,44 @@ __device__ bool run_start(const int32_t* pos, const int32_t* doc, int i) {
   return i == 0 || doc[i] != doc[i - 1] || pos[i] != pos[i - 1] + 1;
 }
 
-// Marks run starts of (pos, doc) and writes their indices to starts[]; returns the count.
+// Marks run starts of (pos, doc) and writes their indices, in order, to starts[]; returns
+// the count.  Tokens are visited in coalesced rounds of NT; a run start is a ballot bit.
 __device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap, int32_t* starts,
                          int stride_ints, PlanShared& sh) {
   const int tid = threadIdx.x;
-  const int per = (n + NT - 1) / NT;
-  const int b = min(n, tid * per), e = min(n, b + per);
-  int cnt = 0;
-  for (int i = b; i < e; ++i) cnt += run_start(pos, doc, i);
-  int total;
-  int off = block_excl_scan(cnt, sh.scan, &total);
+  const int lane = tid & 63, w = tid >> 6;
+  int total = 0;
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
+    const bool f = i < n && run_start(pos, doc, i);
+    const unsigned long long m = __ballot(f);
+    if (lane == 0) sh.wave_sum[w] = __popcll(m);
+    __syncthreads();
+    int before = 0, round = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanWaves; ++k) {
+      const int c = sh.wave_sum[k];
+      before += k < w ? c : 0;
+      round += c;
+    }
+    __syncthreads();
+    const int idx = total + before + __popcll(m & ((1ull << lane) - 1));
+    if (f && idx < cap) starts[(int64_t)idx * stride_ints] = i;
+    total += round;
+  }
   if (total > cap) {
     if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
-    return 0;
+    total = 0;
   }
-  for (int i = b; i < e; ++i)
-    if (run_start(pos, doc, i)) starts[(int64_t)(off++) * stride_ints] = i;
   __syncthreads();
   return total;
 }
+
+// LDS staging inside the sort buffer, used before the sort needs it: key/value runs in the
+// first half, each fragment's first tile index in the second half.
+constexpr int kLdsRuns = kSortCap * 8 / 2 / (int)sizeof(KvRun);
+constexpr int kLdsFtile = kSortCap * 8 / 2 / (int)sizeof(int32_t);
+constexpr int kMaxTilesPerThread = kSortCap / NT;
 
 __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
   __shared__ PlanShared sh;
@@ -94,10 +123,11 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
   char* ws = a.ws;
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   Frag* frags = reinterpret_cast<Frag*>(ws + a.L.off_frags);
-  int32_t* ftile = reinterpret_cast<int32_t*>(ws + a.L.off_ftile);
   KvRun* kvr = reinterpret_cast<KvRun*>(ws + a.L.off_kvruns);
   lb_plan_tile* tiles = reinterpret_cast<lb_plan_tile*>(ws + a.L.off_tiles);
   int32_t* order = reinterpret_cast<int32_t*>(ws + a.L.off_order);
+  KvRun* lds_runs = reinterpret_cast<KvRun*>(&sh.keys[0]);
+  int32_t* lds_ftile = reinterpret_cast<int32_t*>(&sh.keys[kSortCap / 2]);
 
   if (tid == 0) {
     sh.err = 0;
@@ -142,14 +172,14 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
     }
   } else {  // block path: runs of equal doc id and consecutive position
     n_frags = find_runs(a.q_pos, a.q_doc, a.n_q, a.L.cap_frags, &frags[0].q_start, sizeof(Frag) / 4, sh);
-    n_kvruns = find_runs(a.kv_pos, a.kv_doc, a.n_kv, a.L.cap_frags, &kvr[0].start, sizeof(KvRun) / 4, sh);
+    n_kvruns = find_runs(a.kv_pos, a.kv_doc, a.n_kv, min(a.L.cap_frags, kLdsRuns), &kvr[0].start,
+                         sizeof(KvRun) / 4, sh);
     if (sh.err == 0) {
+      // complete the key/value runs, in LDS for the span search below
       for (int r = tid; r < n_kvruns; r += NT) {
         const int s = kvr[r].start;
         const int e = r + 1 < n_kvruns ? kvr[r + 1].start : a.n_kv;
-        kvr[r].len = e - s;
-        kvr[r].pos0 = a.kv_pos[s];
-        kvr[r].doc = a.kv_doc[s];
+        lds_runs[r] = KvRun{s, e - s, a.kv_pos[s], a.kv_doc[s]};
       }
       __syncthreads();
       for (int r = tid; r < n_frags; r += NT) {
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
         const int last_pos = f.q_pos0 + f.q_len - 1;
         int ns = 0;
         for (int j = 0; j < n_kvruns; ++j) {
-          const KvRun kr = kvr[j];
+          const KvRun kr = lds_runs[j];
           if (kr.doc != doc || kr.pos0 > last_pos) continue;  // other document, or wholly in the future
           if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
           f.k_start[ns] = kr.start; f.k_len[ns] = kr.len; f.k_pos0[ns] = kr.pos0; ++ns;
@@ -173,6 +203,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
       }
     }
   }
+  if (n_frags + 1 > kLdsFtile && tid == 0) sh.err |= LB_DEVERR_CAPACITY;
   __syncthreads();
 
   // ---- 2. tiles in natural order ---------------------------------------------------
@@ -184,60 +215,67 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
       const int f = base + tid;
       const int cnt = f < n_frags ? (frags[f].q_len + bm - 1) / bm : 0;
       int total;
-      const int off = block_excl_scan(cnt, sh.scan, &total);
-      if (f < n_frags) ftile[f] = running + off;
+      const int off = block_excl_scan(cnt, sh, &total);
+      if (f < n_frags) lds_ftile[f] = running + off;
       running += total;
     }
     n_tiles = running;
-    if (tid == 0) ftile[n_frags] = n_tiles;
+    if (tid == 0) lds_ftile[n_frags] = n_tiles;
     if (n_tiles > a.L.cap_tiles) {
       if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
     }
   }
   __syncthreads();
+  // sort keys of this thread's tiles, (2^40 - 1 - cost) << 24 | natural index: ascending
+  // order is cost descending with ties in natural order, and every key is unique
+  uint64_t my_keys[kMaxTilesPerThread];
   if (sh.err == 0) {
     unsigned long long my_pairs = 0;
-    for (int t = tid; t < n_tiles; t += NT) {
+#pragma unroll
+    for (int k = 0; k < kMaxTilesPerThread; ++k) {
+      const int t = tid + k * NT;
+      if (t >= n_tiles) break;
       int lo = 0, hi = n_frags - 1;  // last fragment whose first tile <= t
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (ftile[mid] <= t) lo = mid; else hi = mid - 1;
+        if (lds_ftile[mid] <= t) lo = mid; else hi = mid - 1;
       }
       const Frag f = frags[lo];
-      const int k = t - ftile[lo];
+      const int kt = t - lds_ftile[lo];
       lb_plan_tile T{};
-      T.q_start = f.q_start + k * bm;
-      T.q_len = min(bm, f.q_len - k * bm);
-      T.q_pos0 = f.q_pos0 + k * bm;
+      T.q_start = f.q_start + kt * bm;
+      T.q_len = min(bm, f.q_len - kt * bm);
+      T.q_pos0 = f.q_pos0 + kt * bm;
       const int last = T.q_pos0 + T.q_len - 1;
       int ns = 0;
       int64_t cost = 0;
-      for (int s = 0; s < f.n_spans; ++s) {
-        const int keep = min(f.k_len[s], last - f.k_pos0[s] + 1);
+      for (int sp = 0; sp < f.n_spans; ++sp) {
+        const int keep = min(f.k_len[sp], last - f.k_pos0[sp] + 1);
         if (keep <= 0) continue;
-        T.k_start[ns] = f.k_start[s];
+        T.k_start[ns] = f.k_start[sp];
         T.k_len[ns] = keep;
-        T.k_pos0[ns] = f.k_pos0[s];
-        cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[s], keep);
+        T.k_pos0[ns] = f.k_pos0[sp];
+        cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[sp], keep);
         ++ns;
       }
       T.n_spans = ns;
       T.cost = cost;
       tiles[t] = T;
       my_pairs += (unsigned long long)cost;
+      my_keys[k] = ((kCostMask - (uint64_t)cost) << 24) | (uint64_t)t;
     }
     atomicAdd(&sh.pairs, my_pairs);
   }
-  __syncthreads();
+  __syncthreads();  // the staging areas are dead from here on; the sort buffer takes over
 
-  // ---- 3. longest-first order: bitonic sort of unique keys in LDS ------------------
+  // ---- 3. longest-first order: bitonic sort of the unique keys in LDS --------------
   if (sh.err == 0 && n_tiles > 0) {
     int n_pad = 1;
     while (n_pad < n_tiles) n_pad <<= 1;
-    for (int i = tid; i < n_pad; i += NT) {
-      uint64_t key = ~uint64_t(0);
-      if (i < n_tiles) key = ((kCostMask - (uint64_t)tiles[i].cost) << 24) | (uint64_t)i;
-      sh.keys[i] = key;
+#pragma unroll
+    for (int k = 0; k < kMaxTilesPerThread; ++k) {
+      const int i = tid + k * NT;
+      if (i < n_pad) sh.keys[i] = i < n_tiles ? my_keys[k] : ~uint64_t(0);
     }
     __syncthreads();
     for (int k = 2; k <= n_pad; k <<= 1) {
@@ -262,11 +300,16 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
 
   if (tid == 0) {
     const bool ok = sh.err == 0;
+    // one queue per XCD when the kv heads split evenly over them: queue x serves kv heads
+    // x, x + 8, ... so that an XCD's L2 holds the keys and values of its own heads
+    const int nq = a.kv_heads % kXcds == 0 ? kXcds : 1;
     hdr->err = sh.err;
     hdr->n_frags = ok ? n_frags : 0;
     hdr->n_tiles = ok ? n_tiles : 0;
     hdr->n_items = ok ? n_tiles * a.kv_heads : 0;
-    hdr->queue_head = 0;
+    hdr->n_queues = nq;
+    hdr->per_queue = ok ? n_tiles * a.kv_heads / nq : 0;
+    for (int q = 0; q < kXcds; ++q) hdr->queue_head[q] = 0;
     hdr->n_kvruns = n_kvruns;
     hdr->tile_rows = bm;
     hdr->n_workers = 0;
