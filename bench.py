@@ -304,6 +304,9 @@ def main():
     ms_per_step = el / args.steps * 1e3
     plan_ms = float(np.mean([sum(e[0].elapsed_time(e[1]) for e in step) for step in evs]))
     attn_ms = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in step) for step in evs]))
+    per_launch = [[round(float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])), 4),
+                   round(float(np.mean([evs[s][i][1].elapsed_time(evs[s][i][2]) for s in range(args.steps)])), 4)]
+                  for i in range(n_launch)]
     attn_ms_per_launch = attn_ms / n_launch
 
     recs = w.workers()
@@ -329,6 +332,7 @@ def main():
         "config": dict(w.config, pairs_per_head=w.pairs, effective_flops=w.flops),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
+        "kernels_ms_per_launch": per_launch if n_launch > 1 else None,
         "cu_busy_max_over_mean": None if cu_ratio is None else round(cu_ratio, 4),
         "attention_span_device_clock_ms": round(span_ticks / 1e5, 4),
         "roofline": {

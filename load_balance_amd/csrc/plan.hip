@@ -79,28 +79,28 @@ __device__ bool run_start(const int32_t* pos, const int32_t* doc, int i) {
 }
 
 // Marks run starts of (pos, doc) and writes their indices, in order, to starts[]; returns
-// the count.  Tokens are visited in coalesced rounds of NT; a run start is a ballot bit.
+// the count.  Each round covers 4 * NT consecutive tokens, four per thread.
 __device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap, int32_t* starts,
                          int stride_ints, PlanShared& sh) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
   int total = 0;
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + tid;
-    const bool f = i < n && run_start(pos, doc, i);
-    const unsigned long long m = __ballot(f);
-    if (lane == 0) sh.wave_sum[w] = __popcll(m);
-    __syncthreads();
-    int before = 0, round = 0;
+  for (int base = 0; base < n; base += 4 * NT) {
+    const int i0 = base + 4 * tid;
+    bool f[4];
+    int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < kPlanWaves; ++k) {
-      const int c = sh.wave_sum[k];
-      before += k < w ? c : 0;
-      round += c;
+    for (int e = 0; e < 4; ++e) {
+      f[e] = i0 + e < n && run_start(pos, doc, i0 + e);
+      cnt += f[e];
     }
-    __syncthreads();
-    const int idx = total + before + __popcll(m & ((1ull << lane) - 1));
-    if (f && idx < cap) starts[(int64_t)idx * stride_ints] = i;
+    int round;
+    int idx = total + block_excl_scan(cnt, sh, &round);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (f[e]) {
+        if (idx < cap) starts[(int64_t)idx * stride_ints] = i0 + e;
+        ++idx;
+      }
     total += round;
   }
   if (total > cap) {
@@ -109,6 +109,44 @@ __device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap,
   }
   __syncthreads();
   return total;
+}
+
+// One bitonic phase k over sh.keys[0, n_pad): the stages whose partner distance j is 64
+// or more go through LDS with a workgroup barrier each; the remaining stages (j < 64) pair
+// lanes of one wave and run in registers with lane shuffles.
+__device__ void bitonic_phase(PlanShared& sh, int n_pad, int k, int j_first) {
+  const int tid = threadIdx.x;
+  int j = j_first;
+  for (; j >= 64; j >>= 1) {
+    for (int i = tid; i < n_pad; i += NT) {
+      const int p = i ^ j;
+      if (p > i) {
+        const uint64_t x = sh.keys[i], y = sh.keys[p];
+        const bool ascending = (i & k) == 0;
+        if ((x > y) == ascending) {
+          sh.keys[i] = y;
+          sh.keys[p] = x;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (j == 0) return;
+  // every thread of the workgroup runs the shuffles (padding lanes carry the largest key)
+  for (int base = 0; base < max(n_pad, NT); base += NT) {
+    const int i = base + tid;
+    uint64_t x = i < n_pad ? sh.keys[i] : ~uint64_t(0);
+    for (int kk = (j_first >= 64 ? k : 2); kk <= k; kk <<= 1) {
+      for (int jj = (kk == k ? j : kk >> 1); jj > 0; jj >>= 1) {
+        const uint64_t y = __shfl_xor(x, jj);
+        const bool ascending = (i & kk) == 0;
+        const bool lower = (i & jj) == 0;
+        x = (lower == ascending) ? (x < y ? x : y) : (x < y ? y : x);
+      }
+    }
+    if (i < n_pad) sh.keys[i] = x;
+  }
+  __syncthreads();
 }
 
 // LDS staging inside the sort buffer, used before the sort needs it: key/value runs in the
@@ -278,22 +316,9 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
       if (i < n_pad) sh.keys[i] = i < n_tiles ? my_keys[k] : ~uint64_t(0);
     }
     __syncthreads();
-    for (int k = 2; k <= n_pad; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n_pad; i += NT) {
-          const int p = i ^ j;
-          if (p > i) {
-            const uint64_t x = sh.keys[i], y = sh.keys[p];
-            const bool ascending = (i & k) == 0;
-            if ((x > y) == ascending) {
-              sh.keys[i] = y;
-              sh.keys[p] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+    // phases k = 2 .. min(n_pad, 64) pair lanes of one wave only: all in registers at once
+    bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
+    for (int k = 128; k <= n_pad; k <<= 1) bitonic_phase(sh, n_pad, k, k >> 1);
     for (int i = tid; i < n_tiles; i += NT) order[i] = (int32_t)(sh.keys[i] & 0xFFFFFF);
   }
   __syncthreads();
