@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int64_t n_tiles_hdr = hdr->n_tiles;
   const bool mismatch = hdr->magic != kPlanMagic || hdr->plan_n_q != a.n_q || hdr->plan_n_kv != a.n_kv ||
                         hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
-                        hdr->n_items != n_tiles_hdr * a.kv_heads || n_tiles_hdr < 0 ||
+                        hdr->n_empty < 0 || hdr->n_empty > n_tiles_hdr ||
+                        hdr->n_items != (n_tiles_hdr - hdr->n_empty) * a.kv_heads || n_tiles_hdr < 0 ||
                         (hdr->n_queues != 1 && hdr->n_queues != kXcds) || a.kv_heads % hdr->n_queues != 0 ||
                         (int64_t)hdr->per_queue * hdr->n_queues != hdr->n_items ||
                         hdr->off_tiles < kWorkersOffset || hdr->off_order < kWorkersOffset ||
@@ -192,6 +193,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   KvLoader<D> ld;
   ld.init(row_bytes, tid);
 
+  // Tiles with no key span only set lse = -inf on their rows: a grid-stride pass before the
+  // queues, without barriers or LDS.
+  {
+    const int n_empty = mismatch ? 0 : hdr->n_empty;
+    for (int e = blockIdx.x; e < n_empty; e += gridDim.x) {
+      const lb_plan_tile* T = &tiles[order[n_tiles_hdr - n_empty + e]];
+      const int q_start = T->q_start, q_len = T->q_len;
+      for (int idx = tid; idx < q_len * a.heads; idx += kThreads)
+        a.lse[(int64_t)(idx / q_len) * a.n_q + q_start + idx % q_len] = -__builtin_inff();
+    }
+  }
+
   // Work queues: with one queue per XCD, a workgroup serves its own XCD's queue (kv heads
   // q, q + 8, ...) so the XCD's L2 keeps those heads' keys and values, and steals from the
   // other queues, in turn, once its own is empty.
@@ -199,16 +212,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int per_queue = mismatch ? 0 : hdr->per_queue;
   const int heads_per_queue = a.kv_heads / n_queues;
   int queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
-  int queues_left = n_queues;
+  int queues_left = 1;  // 0 once every queue is dry
 
   for (;;) {
+    if (n_items == 0) break;
     if (tid == 0) {
       int k = per_queue;
       while (queues_left > 0) {
         k = atomicAdd(&hdr->queue_head[queue], 1);
         if (k < per_queue) break;
-        queue = queue + 1 == n_queues ? 0 : queue + 1;
-        --queues_left;
+        // this queue is dry: look at every queue head at once and go to the next one in
+        // rotation that still holds items (another workgroup may still empty it first)
+        int heads[kXcds];
+#pragma unroll
+        for (int q = 0; q < kXcds; ++q) heads[q] = q < n_queues ? __atomic_load_n(&hdr->queue_head[q], __ATOMIC_RELAXED) : per_queue;
+        int next = -1;
+        for (int step = 1; step < n_queues; ++step) {
+          const int q = (queue + step) % n_queues;
+          if (heads[q] < per_queue) { next = q; break; }
+        }
+        if (next < 0) { queues_left = 0; break; }
+        queue = next;
       }
       s_item = queues_left > 0 ? queue * per_queue + k : -1;
     }

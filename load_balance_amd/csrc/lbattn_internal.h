@@ -33,7 +33,7 @@ struct WsHeader {
   int32_t err;          // LB_DEVERR_* bits
   int32_t n_frags;      // query fragments
   int32_t n_tiles;
-  int32_t n_items;      // n_tiles * kv_heads (0 after an error)
+  int32_t n_items;      // (n_tiles - n_empty) * kv_heads queued items (0 after an error)
   int32_t n_queues;     // work queues: one per XCD when kv_heads is a multiple of kXcds, else 1
   int32_t n_kvruns;
   int32_t tile_rows;
@@ -45,7 +45,8 @@ struct WsHeader {
   int32_t done;         // attention workgroups that found every queue empty
   uint32_t magic;       // kPlanMagic once a plan has been written
   int32_t per_queue;    // items per queue
-  int32_t pad[3];
+  int32_t n_empty;      // tiles with no key span: the last n_empty of the order, kept out of the queues
+  int32_t pad[2];
   int32_t queue_head[8];  // next item of each queue
 };
 

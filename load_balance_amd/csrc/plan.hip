@@ -27,17 +27,21 @@ constexpr uint64_t kCostMask = (uint64_t(1) << 40) - 1;  // costs < 2^40 (checke
 
 constexpr int kPlanWaves = NT / 64;
 
+constexpr int kRunRounds = 4;
+
 struct PlanShared {
   uint64_t keys[kSortCap];
   int32_t wave_sum[kPlanWaves];
+  int32_t run_sum[kRunRounds][kPlanWaves];
   int32_t err;
+  int32_t n_empty;
   unsigned long long pairs;
 };
 
 // Exclusive prefix sum of one value per thread across the workgroup (thread order),
 // with the workgroup total in *total: a shuffle scan inside each wave, then the wave
 // totals through LDS.  Two barriers.
-__device__ int block_excl_scan(int v, PlanShared& sh, int* total) {
+__device__ __forceinline__ int block_excl_scan(int v, PlanShared& sh, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -60,7 +64,7 @@ __device__ int block_excl_scan(int v, PlanShared& sh, int* total) {
 }
 
 // Sum over integers y < x of clamp(y, 0, L).
-__device__ int64_t clamp_prefix(int64_t x, int64_t L) {
+__device__ __forceinline__ int64_t clamp_prefix(int64_t x, int64_t L) {
   const int64_t m = x - 1;
   if (m <= 0) return 0;
   if (m <= L) return m * (m + 1) / 2;
@@ -69,39 +73,89 @@ __device__ int64_t clamp_prefix(int64_t x, int64_t L) {
 
 // Visible pairs between n consecutive query positions p0.. and one span
 // (keys at positions kp0 .. kp0 + L - 1, key visible iff its position <= the query's).
-__device__ int64_t span_pairs(int64_t p0, int64_t n, int64_t kp0, int64_t L) {
+__device__ __forceinline__ int64_t span_pairs(int64_t p0, int64_t n, int64_t kp0, int64_t L) {
   const int64_t a = p0 - kp0 + 1;  // keys the first row sees, before clamping
   return clamp_prefix(a + n, L) - clamp_prefix(a, L);
 }
 
-__device__ bool run_start(const int32_t* pos, const int32_t* doc, int i) {
-  return i == 0 || doc[i] != doc[i - 1] || pos[i] != pos[i - 1] + 1;
-}
-
 // Marks run starts of (pos, doc) and writes their indices, in order, to starts[]; returns
-// the count.  Each round covers 4 * NT consecutive tokens, four per thread.
-__device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap, int32_t* starts,
+// the count.  A super-round covers kRunRounds rounds of 4 * NT consecutive tokens; thread t
+// takes tokens 4t .. 4t+3 of each round, one 16-byte load per array when aligned (lanes
+// reading 16 bytes apart in separate 4-byte loads run several times slower through the
+// vector cache).  The offsets come from lane ballots (bit counts below the lane) and one
+// exchange of wave totals through LDS.
+__device__ __forceinline__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap, int32_t* starts,
                          int stride_ints, PlanShared& sh) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool vec = ((reinterpret_cast<uintptr_t>(pos) | reinterpret_cast<uintptr_t>(doc)) & 15) == 0;
   int total = 0;
-  for (int base = 0; base < n; base += 4 * NT) {
-    const int i0 = base + 4 * tid;
-    bool f[4];
-    int cnt = 0;
+  for (int sbase = 0; sbase < n; sbase += kRunRounds * 4 * NT) {
+    // tokens i0 - 1 .. i0 + 3 of each round: i0 .. i0 + 3 in one 16-byte load where the
+    // pointers allow it and the round is whole; i0 - 1 from the next lower lane, lane 0
+    // loading its own
+    int pp[kRunRounds][5], dd[kRunRounds][5];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[e] = i0 + e < n && run_start(pos, doc, i0 + e);
-      cnt += f[e];
-    }
-    int round;
-    int idx = total + block_excl_scan(cnt, sh, &round);
+    for (int r = 0; r < kRunRounds; ++r) {
+      const int i0 = sbase + r * 4 * NT + 4 * tid;
+      if (vec && i0 + 3 < n) {
+        const int4 p4 = *reinterpret_cast<const int4*>(pos + i0);
+        const int4 d4 = *reinterpret_cast<const int4*>(doc + i0);
+        pp[r][1] = p4.x; pp[r][2] = p4.y; pp[r][3] = p4.z; pp[r][4] = p4.w;
+        dd[r][1] = d4.x; dd[r][2] = d4.y; dd[r][3] = d4.z; dd[r][4] = d4.w;
+      } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (f[e]) {
-        if (idx < cap) starts[(int64_t)idx * stride_ints] = i0 + e;
-        ++idx;
+        for (int e = 1; e < 5; ++e) {
+          const int i = i0 + e - 1;
+          pp[r][e] = i < n ? pos[i] : 0;
+          dd[r][e] = i < n ? doc[i] : 0;
+        }
       }
-    total += round;
+      const bool own = lane == 0 && i0 > 0 && i0 <= n;
+      const int p_own = own ? pos[i0 - 1] : 0, d_own = own ? doc[i0 - 1] : 0;
+      const int p_up = __shfl_up(pp[r][4], 1), d_up = __shfl_up(dd[r][4], 1);
+      pp[r][0] = lane == 0 ? p_own : p_up;
+      dd[r][0] = lane == 0 ? d_own : d_up;
+    }
+    uint32_t mask[kRunRounds];
+    int below[kRunRounds];  // run starts in lower lanes of this wave, per round
+#pragma unroll
+    for (int r = 0; r < kRunRounds; ++r) {
+      const int i0 = sbase + r * 4 * NT + 4 * tid;
+      mask[r] = 0;
+      below[r] = 0;
+      int wave_total = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const bool st = i < n && (i == 0 || dd[r][e + 1] != dd[r][e] || pp[r][e + 1] != pp[r][e] + 1);
+        mask[r] |= (uint32_t)st << e;
+        const uint64_t b = __ballot(st);
+        below[r] += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        wave_total += __popcll(b);
+      }
+      if (lane == 0) sh.run_sum[r][w] = wave_total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRunRounds; ++r) {
+      const int i0 = sbase + r * 4 * NT + 4 * tid;
+      int before = 0, all = 0;
+#pragma unroll
+      for (int x = 0; x < kPlanWaves; ++x) {
+        const int c = sh.run_sum[r][x];
+        before += x < w ? c : 0;
+        all += c;
+      }
+      int idx = total + before + below[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (mask[r] >> e & 1) {
+          if (idx < cap) starts[(int64_t)idx * stride_ints] = i0 + e;
+          ++idx;
+        }
+      total += all;
+    }
+    __syncthreads();  // run_sum is rewritten by the next super-round or the next call
   }
   if (total > cap) {
     if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
@@ -114,7 +168,7 @@ __device__ int find_runs(const int32_t* pos, const int32_t* doc, int n, int cap,
 // One bitonic phase k over sh.keys[0, n_pad): the stages whose partner distance j is 64
 // or more go through LDS with a workgroup barrier each; the remaining stages (j < 64) pair
 // lanes of one wave and run in registers with lane shuffles.
-__device__ void bitonic_phase(PlanShared& sh, int n_pad, int k, int j_first) {
+__device__ __forceinline__ void bitonic_phase(PlanShared& sh, int n_pad, int k, int j_first) {
   const int tid = threadIdx.x;
   int j = j_first;
   for (; j >= 64; j >>= 1) {
@@ -150,8 +204,10 @@ __device__ void bitonic_phase(PlanShared& sh, int n_pad, int k, int j_first) {
 }
 
 // LDS staging inside the sort buffer, used before the sort needs it: key/value runs in the
-// first half, each fragment's first tile index in the second half.
-constexpr int kLdsRuns = kSortCap * 8 / 2 / (int)sizeof(KvRun);
+// first quarter, a copy of the fragments (when they fit) in the second, each fragment's
+// first tile index in the second half.
+constexpr int kLdsRuns = kSortCap * 8 / 4 / (int)sizeof(KvRun);
+constexpr int kLdsFrags = kSortCap * 8 / 4 / (int)sizeof(Frag);
 constexpr int kLdsFtile = kSortCap * 8 / 2 / (int)sizeof(int32_t);
 constexpr int kMaxTilesPerThread = kSortCap / NT;
 
@@ -165,11 +221,13 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
   lb_plan_tile* tiles = reinterpret_cast<lb_plan_tile*>(ws + a.L.off_tiles);
   int32_t* order = reinterpret_cast<int32_t*>(ws + a.L.off_order);
   KvRun* lds_runs = reinterpret_cast<KvRun*>(&sh.keys[0]);
+  Frag* lds_frags = reinterpret_cast<Frag*>(&sh.keys[kSortCap / 4]);
   int32_t* lds_ftile = reinterpret_cast<int32_t*>(&sh.keys[kSortCap / 2]);
 
   if (tid == 0) {
     sh.err = 0;
     sh.pairs = 0;
+    sh.n_empty = 0;
   }
   __syncthreads();
 
@@ -200,12 +258,13 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
           f.k_start[0] = cu[0]; f.k_len[0] = Q; f.k_pos0[0] = 0;
         } else {  // an answer: positions continue after the question
           f.q_pos0 = Q;
-          int ns = 0;
-          if (Q > 0) { f.k_start[ns] = cu[0]; f.k_len[ns] = Q; f.k_pos0[ns] = 0; ++ns; }
-          f.k_start[ns] = f.q_start; f.k_len[ns] = f.q_len; f.k_pos0[ns] = Q; ++ns;
-          f.n_spans = ns;
+          const int own = Q > 0 ? 1 : 0;  // slot of the answer's own span, after the question's
+          if (Q > 0) { f.k_start[0] = cu[0]; f.k_len[0] = Q; f.k_pos0[0] = 0; }
+          f.k_start[own] = f.q_start; f.k_len[own] = f.q_len; f.k_pos0[own] = Q;
+          f.n_spans = own + 1;
         }
         frags[s] = f;
+        if (n_frags <= kLdsFrags) lds_frags[s] = f;
       }
     }
   } else {  // block path: runs of equal doc id and consecutive position
@@ -234,10 +293,14 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
           const KvRun kr = lds_runs[j];
           if (kr.doc != doc || kr.pos0 > last_pos) continue;  // other document, or wholly in the future
           if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
-          f.k_start[ns] = kr.start; f.k_len[ns] = kr.len; f.k_pos0[ns] = kr.pos0; ++ns;
+#pragma unroll
+          for (int o = 0; o < LB_MAX_SPANS; ++o)  // slot ns, selected so the fields stay in registers
+            if (o == ns) { f.k_start[o] = kr.start; f.k_len[o] = kr.len; f.k_pos0[o] = kr.pos0; }
+          ++ns;
         }
         f.n_spans = ns;
         frags[r] = f;
+        if (n_frags <= kLdsFrags) lds_frags[r] = f;
       }
     }
   }
@@ -251,7 +314,8 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
     int running = 0;
     for (int base = 0; base < n_frags; base += NT) {
       const int f = base + tid;
-      const int cnt = f < n_frags ? (frags[f].q_len + bm - 1) / bm : 0;
+      const int qlen = f < n_frags ? (n_frags <= kLdsFrags ? lds_frags[f].q_len : frags[f].q_len) : 0;
+      const int cnt = (qlen + bm - 1) / bm;
       int total;
       const int off = block_excl_scan(cnt, sh, &total);
       if (f < n_frags) lds_ftile[f] = running + off;
@@ -278,7 +342,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (lds_ftile[mid] <= t) lo = mid; else hi = mid - 1;
       }
-      const Frag f = frags[lo];
+      const Frag f = n_frags <= kLdsFrags ? lds_frags[lo] : frags[lo];
       const int kt = t - lds_ftile[lo];
       lb_plan_tile T{};
       T.q_start = f.q_start + kt * bm;
@@ -287,18 +351,21 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
       const int last = T.q_pos0 + T.q_len - 1;
       int ns = 0;
       int64_t cost = 0;
-      for (int sp = 0; sp < f.n_spans; ++sp) {
+#pragma unroll
+      for (int sp = 0; sp < LB_MAX_SPANS; ++sp) {
+        if (sp >= f.n_spans) break;
         const int keep = min(f.k_len[sp], last - f.k_pos0[sp] + 1);
         if (keep <= 0) continue;
-        T.k_start[ns] = f.k_start[sp];
-        T.k_len[ns] = keep;
-        T.k_pos0[ns] = f.k_pos0[sp];
+#pragma unroll
+        for (int o = 0; o <= sp; ++o)  // slot ns <= sp, selected so T stays in registers
+          if (o == ns) { T.k_start[o] = f.k_start[sp]; T.k_len[o] = keep; T.k_pos0[o] = f.k_pos0[sp]; }
         cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[sp], keep);
         ++ns;
       }
       T.n_spans = ns;
       T.cost = cost;
       tiles[t] = T;
+      if (ns == 0) atomicAdd(&sh.n_empty, 1);  // cost 0: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
       my_keys[k] = ((kCostMask - (uint64_t)cost) << 24) | (uint64_t)t;
     }
@@ -331,9 +398,11 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
     hdr->err = sh.err;
     hdr->n_frags = ok ? n_frags : 0;
     hdr->n_tiles = ok ? n_tiles : 0;
-    hdr->n_items = ok ? n_tiles * a.kv_heads : 0;
+    const int n_work = ok ? n_tiles - sh.n_empty : 0;
+    hdr->n_items = n_work * a.kv_heads;
+    hdr->n_empty = ok ? sh.n_empty : 0;
     hdr->n_queues = nq;
-    hdr->per_queue = ok ? n_tiles * a.kv_heads / nq : 0;
+    hdr->per_queue = n_work * a.kv_heads / nq;
     for (int q = 0; q < kXcds; ++q) hdr->queue_head[q] = 0;
     hdr->n_kvruns = n_kvruns;
     hdr->tile_rows = bm;

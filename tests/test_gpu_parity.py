@@ -332,6 +332,33 @@ def test_block_no_keys_gives_minus_inf():
     assert torch.all(lse == -math.inf)
 
 
+def test_block_plan_many_rounds_ragged_and_unaligned():
+    """Run detection over more than 16384 tokens per side, with a ragged tail and broken
+    runs, from 16-byte aligned and from unaligned metadata pointers: the plan equals the
+    oracle's either way."""
+    H, Hkv, d = 32, 8, 128
+    T = 40_003
+    lengths = workloads.lognormal_lengths(T, 6, 6000)
+    pos, doc = OA.pack_positions(lengths)
+    qi = np.concatenate([np.arange(s, min(s + 700, T)) for s in range(0, T, 1000)])  # gaps break runs
+    ki = np.arange(T)
+    ref = OP.plan(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), lb.tile_rows(H, Hkv, d))
+
+    def dev(x, shift):
+        buf = torch.zeros(len(x) + shift, dtype=torch.int32, device="cuda")
+        buf[shift:] = torch.from_numpy(np.asarray(x, dtype=np.int32)).cuda()
+        return buf[shift:]
+
+    for shift in (0, 1, 3):
+        say(f"  block plan n_q={len(qi)} n_kv={len(ki)} pointer shift {shift} ints")
+        ws = lb.new_workspace(T, 256, H, Hkv)
+        lb.plan_block(dev(pos[qi], shift), dev(doc[qi], shift), dev(pos[ki], shift), dev(doc[ki], shift),
+                      H, Hkv, d, ws)
+        torch.cuda.synchronize()
+        assert lb.read_device_error(ws) == 0
+        assert_same_plan(lb.read_plan(ws), ref, f"block plan, shift {shift}")
+
+
 # --------------------------------------------------------------------------
 # special cases fixed by the mathematics
 # --------------------------------------------------------------------------
