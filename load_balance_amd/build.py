@@ -2,9 +2,10 @@
 
     python -m load_balance_amd.build
 
-Every HIP source is compiled with packed fp32 arithmetic disabled
-(-target-feature -packed-fp32-ops); hipcc's host pass warns that it does not
-know that feature, which is harmless.
+Each source is compiled to its own object under _build/ (in parallel), then the
+objects are linked.  Every HIP source is compiled with packed fp32 arithmetic
+disabled (-target-feature -packed-fp32-ops); hipcc's host pass warns that it
+does not know that feature, which is harmless.
 """
 from __future__ import annotations
 
@@ -12,6 +13,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -28,26 +30,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblbattn.so)")
 
 
-def command(out: str = LIB) -> list[str]:
-    return [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
-            "-I", os.path.join(ROOT, "include"),
-            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument"]
+# The attention kernel is scheduled with the iterative ILP strategy: the default one keeps
+# a single LDS read in flight ahead of the QK^T MFMAs in its key loop.
+EXTRA = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+OBJ_DIR = os.path.join(PKG, "_build")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src: str, obj: str) -> list[str]:
+    return [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-c"] + COMMON + EXTRA.get(src, []) + [
+        "-I", os.path.join(ROOT, "include"), "-o", obj, os.path.join(CSRC, src)]
+
+
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out] + objs
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+        list(pool.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+    tmp = LIB + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

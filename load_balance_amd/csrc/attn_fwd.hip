@@ -58,6 +58,19 @@ struct Lds {
   static constexpr int vUnits = (BN / 2) * (D / 8);  // (key pair, 8-wide d chunk) units of a V block
 };
 
+// Output staging for the epilogue: each wave's rows, row-major, in 1/8 of the LDS ring;
+// two passes of 16 rows where 32 rows do not fit.
+template <int D, bool OUT_F32>
+struct EpilogueLds {
+  static constexpr int kRowBytes = D * (OUT_F32 ? 4 : 2);
+  static constexpr int kStride = kRowBytes + 16;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kWaveBytes = (kStages * Lds<D>::stage / kWaves) & ~15;
+  static constexpr int kPasses = 32 * kStride <= kWaveBytes ? 1 : 2;
+  static constexpr int kRows = 32 / kPasses;
+  static_assert(kRows * kStride <= kWaveBytes, "epilogue staging does not fit in the ring");
+};
+
 // V^T keeps keys permuted inside each group of 16 so that the 8 keys one lane feeds to
 // the PV product are contiguous: swap bits 2 and 3 of the key index.
 __device__ __forceinline__ int vt_pos(int key) {
@@ -65,6 +78,15 @@ __device__ __forceinline__ int vt_pos(int key) {
 }
 
 __device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Workgroup barrier that orders LDS only.  The waves of a workgroup share nothing through
+// global memory here, and __syncthreads() would also wait for every outstanding global
+// store (the previous item's output) to complete.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // s_getreg immediates: (size - 1) << 11 | offset << 6 | register id.
 __device__ __forceinline__ uint32_t hw_id_reg() { return __builtin_amdgcn_s_getreg((31 << 11) | 4); }
@@ -212,34 +234,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int per_queue = mismatch ? 0 : hdr->per_queue;
   const int heads_per_queue = a.kv_heads / n_queues;
   int queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
-  int queues_left = 1;  // 0 once every queue is dry
+  bool queues_dry = n_items == 0;  // kept by thread 0 only
 
-  for (;;) {
-    if (n_items == 0) break;
-    if (tid == 0) {
-      int k = per_queue;
-      while (queues_left > 0) {
-        k = atomicAdd(&hdr->queue_head[queue], 1);
-        if (k < per_queue) break;
-        // this queue is dry: look at every queue head at once and go to the next one in
-        // rotation that still holds items (another workgroup may still empty it first)
-        int heads[kXcds];
+  // Thread 0: completes a pop whose atomicAdd on the current queue returned k.  A dry queue
+  // sends it on to the next queue in rotation that still holds items, judged from one read
+  // of every queue head (another workgroup may still empty that queue first).
+  auto finish_pop = [&](int k) -> int {
+    while (!queues_dry) {
+      if (k < per_queue) return queue * per_queue + k;
+      int heads[kXcds];
 #pragma unroll
-        for (int q = 0; q < kXcds; ++q) heads[q] = q < n_queues ? __atomic_load_n(&hdr->queue_head[q], __ATOMIC_RELAXED) : per_queue;
-        int next = -1;
-        for (int step = 1; step < n_queues; ++step) {
-          const int q = (queue + step) % n_queues;
-          if (heads[q] < per_queue) { next = q; break; }
-        }
-        if (next < 0) { queues_left = 0; break; }
-        queue = next;
+      for (int q = 0; q < kXcds; ++q)
+        heads[q] = q < n_queues ? __atomic_load_n(&hdr->queue_head[q], __ATOMIC_RELAXED) : per_queue;
+      int next = -1;
+      for (int step = 1; step < n_queues; ++step) {
+        const int q = (queue + step) % n_queues;
+        if (heads[q] < per_queue) { next = q; break; }
       }
-      s_item = queues_left > 0 ? queue * per_queue + k : -1;
+      if (next < 0) { queues_dry = true; break; }
+      queue = next;
+      k = atomicAdd(&hdr->queue_head[queue], 1);
     }
-    __syncthreads();
-    const int qitem = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (qitem < 0 || n_items == 0) break;
+    return -1;
+  };
+  if (tid == 0) s_item = queues_dry ? -1 : finish_pop(atomicAdd(&hdr->queue_head[queue], 1));
+  lds_barrier();
+  int qitem = __builtin_amdgcn_readfirstlane(s_item);
+
+  while (qitem >= 0) {
 
     // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
     const int q_of = qitem / max(per_queue, 1), k_in = qitem - q_of * per_queue;
@@ -377,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     bool prev_live = false;
 
     for (int it = 0; it < n_kv_tiles; ++it) {
-      __syncthreads();
+      lds_barrier();
       // the block after this one: next 64 keys of this span, or the first of the next span
       KvBlock nxt = cur;
       nxt.key0 += BN;
@@ -410,33 +432,70 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
 
     // ---- epilogue: out = O / l, lse = ln(sum exp) ----
+    // Every wave is done with the LDS ring after this barrier; thread 0 starts the next pop
+    // here and collects it after the LDS part of the epilogue, before any global store of it.
+    lds_barrier();
+    int k_next = 0;
+    if (tid == 0 && !queues_dry) k_next = atomicAdd(&hdr->queue_head[queue], 1);
     const float l_tot = l_part + __shfl_xor(l_part, 32);
-    if (wave_rows && my_row < q_len) {
-      const bool empty = !(l_tot > 0.0f);
-      const float lse = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
-      if (hh == 0) a.lse[(int64_t)head * a.n_q + grow] = lse;
-      if (!empty) {
-        const float inv = 1.0f / l_tot;
+    const bool row_real = wave_rows && my_row < q_len;
+    const bool empty = !(l_tot > 0.0f);
+    // rows written: bit r for tile row wr0 + r (lanes r and r + 32 hold the same row)
+    const uint32_t wmask = (uint32_t)__ballot(row_real && !empty);
+    const float inv = empty ? 0.0f : 1.0f / l_tot;
+    // Lanes own query rows, so direct stores would put 32 rows, heads * D apart, into every
+    // store instruction.  Each wave stages its rows row-major in its own slice of the ring
+    // and stores them 16 contiguous bytes per lane.
+    using Epi = EpilogueLds<D, OUT_F32>;
+    // lane-only addresses stay here rather than being hoisted out of the item loop, where
+    // they would hold registers through the whole key loop
+    int t_e = tid;
+    asm volatile("" : "+v"(t_e));
+    const int lane_e = t_e & 63, l32_e = t_e & 31;
+    char* ebuf = smem + (t_e >> 6) * Epi::kWaveBytes;
+#pragma unroll
+    for (int pass = 0; pass < Epi::kPasses; ++pass) {
+      const int r_lo = pass * Epi::kRows;
+      if (pass > 0) __builtin_amdgcn_wave_barrier();
+      if (l32_e >= r_lo && l32_e < r_lo + Epi::kRows) {
+        char* rowp = ebuf + (l32_e - r_lo) * Epi::kStride;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int d0 = db * 32 + r * 8 + hh * 4;
-            const int64_t off = (grow * a.heads + head) * D + d0;
             if constexpr (OUT_F32) {
               f32x4 o;
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[e] = acc_o[db][r * 4 + e] * inv;
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = o;
+              *reinterpret_cast<f32x4*>(rowp + d0 * 4) = o;
             } else {
               bf16x4 o;
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc_o[db][r * 4 + e] * inv);
-              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.out) + off) = o;
+              *reinterpret_cast<bf16x4*>(rowp + d0 * 2) = o;
             }
           }
       }
+      if (pass == 0 && tid == 0) s_item = finish_pop(k_next);
+      if (pass == 0 && row_real && hh == 0)
+        a.lse[(int64_t)head * a.n_q + grow] = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
+      // LDS instructions of one wave complete in order: the reads below see the writes above.
+      // One step of 64 lanes covers kRowsPerStep whole rows.
+      constexpr int kRowsPerStep = 64 / Epi::kChunks;
+      const int row0 = lane_e / Epi::kChunks, ch = lane_e % Epi::kChunks;
+      const char* src = ebuf + row0 * Epi::kStride + ch * 16;
+      char* dst = reinterpret_cast<char*>(a.out) +
+                  (((int64_t)q_start + wr0 + r_lo + row0) * a.heads + head) * Epi::kRowBytes + ch * 16;
+      const int64_t dst_step = (int64_t)kRowsPerStep * a.heads * Epi::kRowBytes;
+#pragma unroll
+      for (int j = 0; j < Epi::kRows / kRowsPerStep; ++j) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + j * kRowsPerStep * Epi::kStride);
+        if (wmask >> (r_lo + row0 + j * kRowsPerStep) & 1) *reinterpret_cast<u32x4*>(dst + j * dst_step) = x;
+      }
     }
+    lds_barrier();  // s_item is written; the ring is free again for the next item's first block
+    qitem = __builtin_amdgcn_readfirstlane(s_item);
   }
 
   if (tid == 0) {
