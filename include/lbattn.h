@@ -88,8 +88,16 @@ enum {
 };
 
 #define LB_MAX_SPANS 4
+#define LB_BLOCK_KEYS 64 /* keys per block the attention kernel steps through */
 
-/* One tile of the plan, as lb_read_plan returns it (longest-first order). */
+/*
+ * One tile of the plan, as lb_read_plan returns it, in queue order: `blocks`
+ * descending, ties in natural order (fragment order, then tile order).  A tile's
+ * time is set by the key blocks it sweeps, a short tile costing as much as a full
+ * one ("03 · 长文负载均衡", section 3.3: a query block shorter than one tile is
+ * billed as a whole tile), and items go out longest first ("数据并行负载均衡",
+ * section 4.4, LPT on estimated cost).
+ */
 typedef struct {
   int32_t q_start;               /* first query row (index into the call's query rows) */
   int32_t q_len;                 /* rows in the tile (<= lb_tile_rows) */
@@ -99,7 +107,8 @@ typedef struct {
   int32_t k_start[LB_MAX_SPANS]; /* first key row of each span */
   int32_t k_len[LB_MAX_SPANS];   /* keys kept: those the tile's last row can see */
   int32_t k_pos0[LB_MAX_SPANS];  /* mask position of the span's first key */
-  int32_t reserved[2];
+  int32_t blocks;                /* sum over spans of ceil(k_len / LB_BLOCK_KEYS): the order key */
+  int32_t reserved;
 } lb_plan_tile;
 
 /* One persistent workgroup's record (lb_read_worker_timing). */

@@ -38,7 +38,7 @@ class PlanTile(ctypes.Structure):
     _fields_ = [("q_start", ctypes.c_int32), ("q_len", ctypes.c_int32), ("q_pos0", ctypes.c_int32),
                 ("n_spans", ctypes.c_int32), ("cost", ctypes.c_int64),
                 ("k_start", ctypes.c_int32 * MAX_SPANS), ("k_len", ctypes.c_int32 * MAX_SPANS),
-                ("k_pos0", ctypes.c_int32 * MAX_SPANS), ("reserved", ctypes.c_int32 * 2)]
+                ("k_pos0", ctypes.c_int32 * MAX_SPANS), ("blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class WorkerRecord(ctypes.Structure):
@@ -233,7 +233,7 @@ def read_device_error(workspace, stream=None) -> int:
 
 
 def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
-    """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost)."""
+    """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost, blocks)."""
     buf = (PlanTile * max_tiles)()
     n = ctypes.c_int32(0)
     _check(lib().lb_read_plan(_ptr(workspace), workspace.numel(), buf, max_tiles, ctypes.byref(n),
@@ -242,7 +242,8 @@ def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
     for i in range(min(n.value, max_tiles)):
         t = buf[i]
         spans = [(t.k_start[s], t.k_len[s], t.k_pos0[s]) for s in range(t.n_spans)]
-        out.append(dict(q_start=t.q_start, q_len=t.q_len, q_pos0=t.q_pos0, spans=spans, cost=t.cost))
+        out.append(dict(q_start=t.q_start, q_len=t.q_len, q_pos0=t.q_pos0, spans=spans, cost=t.cost,
+                        blocks=t.blocks))
     return out
 
 

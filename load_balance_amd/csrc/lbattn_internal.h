@@ -17,7 +17,7 @@ namespace lb {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kBlockN = 64;
+constexpr int kBlockN = LB_BLOCK_KEYS;
 
 // Planning kernel: one workgroup sorts the tile keys in LDS.
 constexpr int kPlanThreads = 1024;

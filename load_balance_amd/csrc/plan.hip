@@ -5,17 +5,21 @@
 // ("03 · 长文负载均衡", section 3.2: DCP generates computation blocks only for
 // block pairs whose mask is not all zero), masks are described as rectangles
 // of full or causal kind (section 4.4, MagiAttention's AttnSlice), each tile
-// is billed its exact number of visible (query, key) pairs (section 3.2,
-// Libra TAP), and tiles are handed out largest first (section 2.1, VRSP's
-// LPT placement; "数据并行负载均衡", section 4.4).
+// carries its exact number of visible (query, key) pairs (section 3.2, Libra
+// TAP), and tiles are handed out largest first (section 2.1, VRSP's LPT
+// placement; "数据并行负载均衡", section 4.4, LPT on estimated cost).  The
+// estimate that orders them is the number of 64-key blocks a tile sweeps: the
+// attention kernel spends the same time on a block whatever share of it is
+// visible, and a tile of few rows as long as a full one (section 3.3: a query
+// block shorter than one tile is billed as a whole tile).
 //
 // One workgroup of 1024 threads does everything: the metadata is a few
 // thousand integers, far below what a multi-workgroup launch would pay off.
 //   1. fragments: one per segment (varlen) or per run of equal document id and
 //      consecutive position (block path); spans = keys the fragment may see.
 //   2. tiles: each fragment cut into `tile_rows` rows from its start; spans
-//      clipped to what the tile's last row sees; cost in closed form.
-//   3. order: bitonic sort of (cost descending, natural index) keys in LDS.
+//      clipped to what the tile's last row sees; pairs in closed form, blocks.
+//   3. order: bitonic sort of (blocks descending, natural index) keys in LDS.
 // The plan lands in the caller's workspace; the attention kernel reads it.
 #include "lbattn_internal.h"
 
@@ -23,7 +27,7 @@ namespace lb {
 namespace {
 
 constexpr int NT = kPlanThreads;
-constexpr uint64_t kCostMask = (uint64_t(1) << 40) - 1;  // costs < 2^40 (checked on the host)
+constexpr uint64_t kKeyMask = (uint64_t(1) << 40) - 1;  // block counts < 2^31 fit the key's 40 bits
 
 constexpr int kPlanWaves = NT / 64;
 
@@ -328,8 +332,8 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  // sort keys of this thread's tiles, (2^40 - 1 - cost) << 24 | natural index: ascending
-  // order is cost descending with ties in natural order, and every key is unique
+  // sort keys of this thread's tiles, (2^40 - 1 - blocks) << 24 | natural index: ascending
+  // order is blocks descending with ties in natural order, and every key is unique
   uint64_t my_keys[kMaxTilesPerThread];
   if (sh.err == 0) {
     unsigned long long my_pairs = 0;
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
       T.q_len = min(bm, f.q_len - kt * bm);
       T.q_pos0 = f.q_pos0 + kt * bm;
       const int last = T.q_pos0 + T.q_len - 1;
-      int ns = 0;
+      int ns = 0, blocks = 0;
       int64_t cost = 0;
 #pragma unroll
       for (int sp = 0; sp < LB_MAX_SPANS; ++sp) {
@@ -360,14 +364,16 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
         for (int o = 0; o <= sp; ++o)  // slot ns <= sp, selected so T stays in registers
           if (o == ns) { T.k_start[o] = f.k_start[sp]; T.k_len[o] = keep; T.k_pos0[o] = f.k_pos0[sp]; }
         cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[sp], keep);
+        blocks += (keep + kBlockN - 1) / kBlockN;
         ++ns;
       }
       T.n_spans = ns;
       T.cost = cost;
+      T.blocks = blocks;
       tiles[t] = T;
-      if (ns == 0) atomicAdd(&sh.n_empty, 1);  // cost 0: sorts to the end of the order
+      if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
-      my_keys[k] = ((kCostMask - (uint64_t)cost) << 24) | (uint64_t)t;
+      my_keys[k] = ((kKeyMask - (uint64_t)blocks) << 24) | (uint64_t)t;
     }
     atomicAdd(&sh.pairs, my_pairs);
   }

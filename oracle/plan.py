@@ -5,9 +5,12 @@ key block) pairs with at least one visible pair become work ("03 · 长文负载
 section 3.2, DCP's computation blocks), the work of a block is billed as its
 exact count of visible (query, key) pairs (same section, Libra TAP), a mask is
 described as rectangles of full or causal kind ("03 · 长文负载均衡", section 4.4,
-MagiAttention's AttnSlice), and work is handed out longest first
-("03 · 长文负载均衡", section 2.1, VRSP; "数据并行负载均衡", section 4.4, the
-LPT solver's first phase).
+MagiAttention's AttnSlice), and work is handed out longest first by an
+estimate of its time ("03 · 长文负载均衡", section 2.1, VRSP; "数据并行负载均衡",
+sections 4.3-4.4, LPT over costs from a fitted model).  The estimate here is
+the number of key blocks a tile sweeps: a kernel spends a block's time whatever
+share of the block is visible, and a short query block is billed as a whole
+tile ("03 · 长文负载均衡", section 3.3).
 
 Tiling rule written out here (the plan the library must reproduce exactly):
 
@@ -28,13 +31,16 @@ Tiling rule written out here (the plan the library must reproduce exactly):
    clipped to the keys its last row can see; spans clipped to nothing are
    dropped.  Tiles with no span remain (the kernel writes lse = -inf there).
 4. *Cost* of a tile = its exact number of visible (query, key) pairs for one
-   head, counted row by row.
-5. *Order*: cost descending, ties by natural order (fragment order, then tile
-   order inside the fragment).
+   head, counted row by row.  *Blocks* of a tile = sum over its spans of
+   ceil(keys kept / BLOCK_KEYS), the key blocks of BLOCK_KEYS keys it sweeps.
+5. *Order*: blocks descending, ties by natural order (fragment order, then
+   tile order inside the fragment).
 """
 from __future__ import annotations
 
 import numpy as np
+
+BLOCK_KEYS = 64  # keys per block the attention kernel steps through
 
 
 def fragments_varlen(cu_seqlens, mask="causal_doc"):
@@ -107,13 +113,14 @@ def tiles(frags, bm):
             for r in range(n):
                 for (ks, kl, kp0) in kept:
                     cost += visible_in_span(p0 + r, kl, kp0)
-            out.append(dict(q_start=qs + t0, q_len=n, q_pos0=p0, spans=kept, cost=cost))
+            blocks = sum(-(-kl // BLOCK_KEYS) for (ks, kl, kp0) in kept)
+            out.append(dict(q_start=qs + t0, q_len=n, q_pos0=p0, spans=kept, cost=cost, blocks=blocks))
     return out
 
 
-def lpt_order(tile_list):
-    """Indices of tiles, cost descending, ties in natural order."""
-    return sorted(range(len(tile_list)), key=lambda i: (-tile_list[i]["cost"], i))
+def lpt_order(tile_list, key="blocks"):
+    """Indices of tiles, `key` descending, ties in natural order."""
+    return sorted(range(len(tile_list)), key=lambda i: (-tile_list[i][key], i))
 
 
 def plan(frags, bm):

@@ -30,6 +30,19 @@ def brute_check(tiles, visible, n_q):
                 n = P.visible_in_span(t["q_pos0"] + i, kl, kp0)
                 got[ks:ks + n] += 1
             assert np.array_equal(got, visible[r].astype(int)), (t, r)
+        # blocks: the fewest key blocks of BLOCK_KEYS, laid from each span's start, that hold
+        # every key any row of the tile sees; each of them holds a key the last row sees
+        seen = visible[rows].any(axis=0)
+        swept = np.zeros(visible.shape[1], dtype=bool)
+        n_blocks = 0
+        for (ks, kl, kp0) in t["spans"]:
+            for b0 in range(ks, ks + kl, P.BLOCK_KEYS):
+                b1 = min(b0 + P.BLOCK_KEYS, ks + kl)
+                assert visible[rows[-1], b0:b1].any(), (t, b0)
+                swept[b0:b1] = True
+                n_blocks += 1
+        assert not (seen & ~swept).any(), t
+        assert t["blocks"] == n_blocks, t
     assert covered.all()
 
 
@@ -98,16 +111,33 @@ def test_lpt_order():
     cu = workloads.cu_from_lengths([100, 5, 300, 64, 64])
     tl = P.tiles(P.fragments_varlen(cu), 32)
     order = P.lpt_order(tl)
-    costs = [tl[i]["cost"] for i in order]
-    assert costs == sorted(costs, reverse=True)
+    blocks = [tl[i]["blocks"] for i in order]
+    assert blocks == sorted(blocks, reverse=True)
     for a, b in zip(order, order[1:]):
-        if tl[a]["cost"] == tl[b]["cost"]:
+        if tl[a]["blocks"] == tl[b]["blocks"]:
             assert a < b
     assert sorted(order) == list(range(len(tl)))
-    # two 64-token docs give equal tile costs; the earlier document comes first
+    # the two 64-token docs give equal tiles; the earlier document comes first
     p = P.plan(P.fragments_varlen(cu), 32)
     eq = [t["q_start"] for t in p if t["cost"] == 32 * 33 // 2 and t["q_len"] == 32]
     assert eq == sorted(eq)
+    # ordering by pair count instead is still available to the caller
+    by_cost = [tl[i]["cost"] for i in P.lpt_order(tl, key="cost")]
+    assert by_cost == sorted(by_cost, reverse=True)
+
+
+def test_short_tile_is_billed_as_a_whole_tile():
+    """"03 · 长文负载均衡", section 3.3: a query block shorter than one tile costs a whole
+    tile.  A 4-row ragged tail of a 4100-token document sweeps 65 key blocks, more than
+    any full tile of it, so it leads the queue although the next tile holds 16 times its pairs."""
+    tl = P.tiles(P.fragments_varlen([0, 4100]), 64)
+    p = P.plan(P.fragments_varlen([0, 4100]), 64)
+    assert p[0]["q_len"] == 4 and p[0]["q_start"] == 4096 and p[0]["blocks"] == 65
+    assert p[0]["cost"] == sum(pos + 1 for pos in range(4096, 4100)) == 16_394  # row at position p sees p + 1 keys
+    assert p[1]["cost"] == sum(pos + 1 for pos in range(4032, 4096)) > 15 * p[0]["cost"]
+    assert [t["blocks"] for t in p[1:]] == list(range(64, 0, -1))
+    # tile k of a document covers query positions 64k .. 64k + 63: it sweeps k + 1 blocks
+    assert all(t["blocks"] == t["q_start"] // 64 + 1 for t in tl[:-1])
 
 
 def test_libra_ten_times_example():
