@@ -88,6 +88,7 @@ enum {
 };
 
 #define LB_MAX_SPANS 4
+#define LB_MAX_PLAN_STEPS 16 /* block steps one lb_plan_block_steps call can plan */
 #define LB_BLOCK_KEYS 64 /* keys per block the attention kernel steps through */
 
 /*
@@ -190,6 +191,25 @@ lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Plans n_steps block steps of one query shard in one launch, one workgroup per step:
+ * step s plans the shard (q_pos, q_doc, n_q) against kv_pos[s], kv_doc[s] (n_kv[s]
+ * tokens) into workspaces[s] (workspace_bytes[s]), exactly as lb_plan_block would.  A
+ * ring step's key/value positions and document ids follow from the packing alone, so a
+ * rank can plan every step before the chunks arrive ("长序列训练与上下文并行", Ring
+ * Attention: each step attends the chunk received from the previous rank; "03 ·
+ * 长文负载均衡", section 4.2: the zigzag chunk assignment).
+ *   kv_pos, kv_doc, n_kv, workspaces, workspace_bytes: host arrays of n_steps entries
+ *   (the pointers in them are device pointers);  1 <= n_steps <= LB_MAX_PLAN_STEPS.
+ * Every step is checked as lb_plan_block checks it before anything is launched; the
+ * first failing step's status is returned and nothing runs.  Workspaces must be
+ * distinct.
+ */
+lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
+                              const int32_t* const* kv_pos, const int32_t* const* kv_doc, const int32_t* n_kv,
+                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d,
+                              void* const* workspaces, const size_t* workspace_bytes, hipStream_t stream);
 
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "liblbattn.so")
 MASK_CAUSAL_DOC = 0
 MASK_SHARED_QUESTION = 1
 MAX_SPANS = 4
+MAX_PLAN_STEPS = 16
 
 DEVERR_CU_SEQLENS = 1
 DEVERR_CAPACITY = 2
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.lb_plan_varlen.restype = ctypes.c_int
     L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_block.restype = ctypes.c_int
+    L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, P, P, P]
+    L.lb_plan_block_steps.restype = ctypes.c_int
     L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
@@ -196,6 +199,25 @@ def plan_block(q_pos, q_doc, kv_pos, kv_doc, heads, kv_heads, d, workspace, stre
                                heads, kv_heads, d, _ptr(workspace), workspace.numel(),
                                ctypes.c_void_p(_stream(stream))), "lb_plan_block")
     return workspace
+
+
+def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d, workspaces, stream=None):
+    """Plans of several block steps of one query shard, one launch: step s plans the shard
+    against kv_pos_list[s], kv_doc_list[s] into workspaces[s] exactly as plan_block would."""
+    n = len(workspaces)
+    if not (len(kv_pos_list) == len(kv_doc_list) == n):
+        raise LBError("kv_pos_list, kv_doc_list and workspaces must have one entry per step")
+    for t, name in [(q_pos, "q_pos"), (q_doc, "q_doc")] + [(x, "kv_pos") for x in kv_pos_list] + \
+            [(x, "kv_doc") for x in kv_doc_list]:
+        if t.dtype != torch.int32:
+            raise LBError(f"{name} must be int32")
+    ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
+    n_kv = (ctypes.c_int32 * max(n, 1))(*[t.numel() for t in kv_pos_list])
+    sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
+    _check(lib().lb_plan_block_steps(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), ptrs(kv_pos_list), ptrs(kv_doc_list),
+                                     n_kv, n, heads, kv_heads, d, ptrs(workspaces), sizes,
+                                     ctypes.c_void_p(_stream(stream))), "lb_plan_block_steps")
+    return workspaces
 
 
 def attn_run(q, k, v, out, lse, workspace, stream=None):

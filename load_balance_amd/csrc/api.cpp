@@ -150,9 +150,9 @@ lb_status prepare_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t
   return LB_OK;
 }
 
-lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
-                            const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
-                            const WsLayout& L, hipStream_t stream) {
+PlanArgs block_plan_args(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
+                         const WsLayout& L) {
   PlanArgs p{};
   p.mode = kPlanBlock;
   p.q_pos = q_pos; p.q_doc = q_doc; p.kv_pos = kv_pos; p.kv_doc = kv_doc;
@@ -163,6 +163,13 @@ lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t 
   p.kv_heads = kv_heads;
   p.ws = static_cast<char*>(workspace);
   p.L = L;
+  return p;
+}
+
+lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
+                            const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
+                            const WsLayout& L, hipStream_t stream) {
+  const PlanArgs p = block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L);
   return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
@@ -206,6 +213,26 @@ lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
                                     workspace_bytes, &L);
   if (st != LB_OK) return st;
   return launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L, stream);
+}
+
+lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
+                              const int32_t* const* kv_pos, const int32_t* const* kv_doc, const int32_t* n_kv,
+                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d,
+                              void* const* workspaces, const size_t* workspace_bytes, hipStream_t stream) {
+  if (n_steps < 1 || n_steps > kMaxPlanSteps) return LB_EINVAL;
+  if (!kv_pos || !kv_doc || !n_kv || !workspaces || !workspace_bytes) return LB_EINVAL;
+  PlanBatch b{};
+  for (int s = 0; s < n_steps; ++s) {
+    for (int r = 0; r < s; ++r)
+      if (workspaces[r] == workspaces[s]) return LB_EINVAL;
+    WsLayout L;
+    lb_status st = prepare_plan_block(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads, d,
+                                      workspaces[s], workspace_bytes[s], &L);
+    if (st != LB_OK) return st;
+    b.step[s] = block_plan_args(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads,
+                                workspaces[s], L);
+  }
+  return launch_plan_steps(b, n_steps, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,

@@ -104,6 +104,12 @@ struct PlanArgs {
   WsLayout L;
 };
 
+// Several block-step plans in one launch, one workgroup per step.
+constexpr int kMaxPlanSteps = LB_MAX_PLAN_STEPS;
+struct PlanBatch {
+  PlanArgs step[kMaxPlanSteps];
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -127,6 +133,7 @@ struct MergeArgs {
 
 // Launchers, one per translation unit; each returns the launch's hipError_t.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 

@@ -3,9 +3,12 @@
 // to one output ("03 · 长文负载均衡", section 3.2, DCP; "长序列训练与上下文并行",
 // Ring Attention: each ring step's local result is merged into the running one).
 //
-// HBM-bound elementwise work: d/4 lanes own one (row, head), each moving 16
-// bytes of out_a and out_b.  Rows whose lse_b is -inf (no visible key in the
-// second partial) read nothing beyond their two lse values.
+// HBM-bound elementwise work.  One wave takes 64 consecutive rows of one head: it
+// reads their 64 lse_b values in one coalesced load, and only the rows with a visible
+// key in the second partial (a ballot, compacted into a per-wave LDS table) move data.
+// A ring step that touches few rows of the shard costs little more than reading lse_b.
+#include <algorithm>
+
 #include "lbattn_internal.h"
 
 namespace lb {
@@ -13,39 +16,70 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int lanes_per_row = a.d / 4;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rh = gid / lanes_per_row;  // row * heads + head
-  const int part = (int)(gid % lanes_per_row);
-  if (rh >= (int64_t)a.n_rows * a.heads) return;
-  const int64_t row = rh / a.heads;
-  const int head = (int)(rh % a.heads);
-  const int64_t li = (int64_t)head * a.n_rows + row;
-  const float lb = a.lse_b[li];
-  if (lb == -__builtin_inff()) return;
-  const float la = a.lse_a[li];
-  f32x4* oa = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + part;
-  const f32x4 ob = reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[part];
-  if (la == -__builtin_inff()) {
-    *oa = ob;
-    if (part == 0) a.lse_a[li] = lb;
-    return;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  // per wave: the taken rows of the current group, compacted, and their two weights
+  __shared__ int s_row[kMergeWaves][64];
+  __shared__ float s_wa[kMergeWaves][64], s_wb[kMergeWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t groups = ((int64_t)a.n_rows + 63) / 64;  // row groups per head
+  const int64_t n_tasks = groups * a.heads;
+  const int chunks = a.d / 4;  // 16-byte pieces of one (row, head) vector
+  for (int64_t task = (int64_t)blockIdx.x * kMergeWaves + w; task < n_tasks; task += (int64_t)gridDim.x * kMergeWaves) {
+    // task-major over heads: neighbouring waves read neighbouring lse entries
+    const int head = (int)(task / groups);
+    const int64_t row0 = (task % groups) * 64;
+    const int64_t row = row0 + lane;
+    const bool in = row < a.n_rows;
+    const int64_t li = (int64_t)head * a.n_rows + row;
+    const float lb = in ? a.lse_b[li] : -__builtin_inff();
+    const bool take = lb != -__builtin_inff();
+    const uint64_t mask = __ballot(take);
+    if (mask == 0) continue;
+    if (take) {
+      // this lane's row: weights of the two partials (wa = 0: out_a is not read) and the merged lse
+      const float la = a.lse_a[li];
+      float wa = 0.0f, wb = 1.0f, lse = lb;
+      if (la != -__builtin_inff()) {
+        const float m = fmaxf(la, lb);
+        const float ea = __expf(la - m), eb = __expf(lb - m);
+        const float inv = 1.0f / (ea + eb);
+        wa = ea * inv;
+        wb = eb * inv;
+        lse = m + __logf(ea + eb);
+      }
+      a.lse_a[li] = lse;
+      const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      s_row[w][slot] = lane;
+      s_wa[w][slot] = wa;
+      s_wb[w][slot] = wb;
+    }
+    // The table is this wave's alone and LDS instructions of one wave complete in order.
+    // Units (taken row, 16-byte piece) are spread over the lanes so that every lane keeps
+    // several independent loads in flight.
+    const int units = __popcll(mask) * chunks;
+#pragma unroll 4
+    for (int u = lane; u < units; u += 64) {
+      const int k = u / chunks, c = u - k * chunks;
+      const int r = s_row[w][k];
+      const float ca = s_wa[w][k], cb = s_wb[w][k];
+      const int64_t rh = (row0 + r) * a.heads + head;
+      f32x4* oa = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + c;
+      const f32x4 y = reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[c];
+      // out_a is not read where lse_a = -inf: the first partial never wrote that row
+      *oa = ca == 0.0f ? y : *oa * ca + y * cb;
+    }
   }
-  const float m = fmaxf(la, lb);
-  const float wa = __expf(la - m), wb = __expf(lb - m);
-  const float inv = 1.0f / (wa + wb);
-  const f32x4 x = *oa;
-  *oa = (x * wa + ob * wb) * inv;
-  if (part == 0) a.lse_a[li] = m + __logf(wa + wb);
 }
 
 }  // namespace
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.n_rows * a.heads * (a.d / 4);
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const int64_t tasks = ((int64_t)a.n_rows + 63) / 64 * a.heads;
+  const int64_t blocks = std::min<int64_t>((tasks + kMergeWaves - 1) / kMergeWaves, 4096);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -215,8 +215,7 @@ constexpr int kLdsFrags = kSortCap * 8 / 4 / (int)sizeof(Frag);
 constexpr int kLdsFtile = kSortCap * 8 / 2 / (int)sizeof(int32_t);
 constexpr int kMaxTilesPerThread = kSortCap / NT;
 
-__global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
-  __shared__ PlanShared sh;
+__device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   const int tid = threadIdx.x;
   char* ws = a.ws;
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
@@ -430,10 +429,29 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
   }
 }
 
+__global__ __launch_bounds__(NT) void plan_kernel(PlanArgs a) {
+  __shared__ PlanShared sh;
+  plan_body(a, sh);
+}
+
+// Independent plans of several block steps: workgroup s plans step s into its own
+// workspace.  The steps differ only in their key/value metadata, which a ring step
+// knows before the chunk's data arrive.
+__global__ __launch_bounds__(NT) void plan_steps_kernel(PlanBatch b) {
+  __shared__ PlanShared sh;
+  const PlanArgs a = b.step[blockIdx.x];
+  plan_body(a, sh);
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s) {
+  hipLaunchKernelGGL(plan_steps_kernel, dim3(n_steps), dim3(NT), 0, s, b);
   return hipGetLastError();
 }
 

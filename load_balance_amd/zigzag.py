@@ -80,6 +80,8 @@ class RankShare:
         # runs per side: at most one per document piece in each of the two chunks
         runs = int(min(max(n_q, n_kv), 2 * len(lengths) + 2))
         self.workspace = new_workspace(max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
+        self._ws_shape = (max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
+        self.step_workspaces = None
 
     def run(self, stream=None, per_step=None):
         """All cp steps plus cp-1 merges; returns (out fp32 [n_q,H,d], lse [H,n_q])."""
@@ -90,6 +92,33 @@ class RankShare:
             lse = self.lse if first else self.step_lse
             block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
                            workspace=self.workspace, stream=stream)
+            if per_step is not None:
+                per_step(t, out, lse)
+            if not first:
+                lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
+        return self.out, self.lse
+
+    def plan_all(self, stream=None):
+        """Plans every ring step in one launch, one workspace per step: a step's key/value
+        positions and document ids follow from the packing, before its chunk arrives."""
+        from . import new_workspace, plan_block_steps
+        if self.step_workspaces is None:
+            self.step_workspaces = [new_workspace(*self._ws_shape) for _ in self.steps]
+        n_q, H, d = self.q.shape
+        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in self.steps],
+                         [st["kv_doc"] for st in self.steps], H, self.steps[0]["kv"].shape[2], d,
+                         self.step_workspaces, stream=stream)
+
+    def run_planned(self, stream=None, per_step=None):
+        """run() with the plans of all steps made up front by plan_all(): one planning launch,
+        then per step the attention launch and (from step 1 on) the merge."""
+        from . import attn_run, lse_merge
+        self.plan_all(stream)
+        for t, st in enumerate(self.steps):
+            first = t == 0
+            out = self.out if first else self.step_out
+            lse = self.lse if first else self.step_lse
+            attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=stream)
             if per_step is not None:
                 per_step(t, out, lse)
             if not first:

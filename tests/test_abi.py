@@ -127,6 +127,26 @@ def test_split_host_checks(L):
     assert L.lb_attn_run(FAKE, FAKE, FAKE, 0, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, need, None) == LB_OK
 
 
+def test_plan_steps_host_checks(L):
+    n = 64
+    need = L.lb_workspace_bytes(n, 3, 2, 2)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    arr = lambda t, xs: (t * len(xs))(*xs)
+    two = [P(0x100000), P(0x200000)]
+
+    def call(n_steps=2, ws=two, sizes=(need, need), kv=(FAKE, FAKE), n_kv=(n, n), d=64, q_pos=FAKE):
+        return L.lb_plan_block_steps(q_pos, FAKE, n, arr(P, kv), arr(P, kv), arr(I32, n_kv), n_steps, 2, 2, d,
+                                     arr(P, ws), arr(SZ, sizes), None)
+    assert call(n_steps=0) == LB_EINVAL
+    assert call(n_steps=17) == LB_EINVAL           # more than LB_MAX_PLAN_STEPS
+    assert call(ws=[FAKE, FAKE]) == LB_EINVAL      # one workspace for two steps
+    assert call(sizes=(need, 64)) == LB_EWORKSPACE  # the second step's workspace is too small
+    assert call(kv=(FAKE, None)) == LB_EINVAL
+    assert call(q_pos=None) == LB_EINVAL
+    assert call(d=48) == LB_EUNSUPPORTED
+    assert L.lb_plan_block_steps(FAKE, FAKE, n, None, None, None, 1, 2, 2, 64, None, None, None) == LB_EINVAL
+
+
 def test_merge_host_checks(L):
     assert L.lb_lse_merge(None, FAKE, FAKE, FAKE, 4, 2, 8, None) == LB_EINVAL
     assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, None) == LB_EUNSUPPORTED

@@ -268,6 +268,32 @@ def test_zigzag_rank3_cp8():
     check(out[rows].cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "zigzag rank 3 (sampled)")
 
 
+def test_zigzag_plans_made_up_front_equal_per_step_plans():
+    """lb_plan_block_steps plans all 8 ring steps of rank 3 in one launch: every step's plan
+    equals lb_plan_block's, and the run over them is bit-identical to the per-step calls."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    C, cp, rank = 8192, 8, 3
+    cache = {}
+
+    def get_chunk(c):
+        if c not in cache:
+            cache[c] = workloads.zigzag_chunk_values(c)
+        return cache[c]
+
+    share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    say("  per-step plans and runs")
+    ref_plans = []
+    out_ref, lse_ref = share.run(per_step=lambda t, o, l: ref_plans.append(lb.read_plan(share.workspace)))
+    out_ref, lse_ref = out_ref.clone(), lse_ref.clone()
+    say("  all plans in one launch, then the runs")
+    out, lse = share.run_planned()
+    torch.cuda.synchronize()
+    for t in range(cp):
+        assert lb.read_device_error(share.step_workspaces[t]) == 0
+        assert_same_plan(lb.read_plan(share.step_workspaces[t]), ref_plans[t], f"step {t}")
+    assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
+
+
 def test_zigzag_reassembly_small():
     """All ranks of a reduced pack (cp=4, 16 chunks of 256... here 8 chunks of 256) against the unsharded oracle."""
     cp, C, H, Hkv, d = 4, 256, 8, 2, 128
@@ -474,6 +500,8 @@ def test_lse_merge_matches_oracle(d):
     ga, gla = t(oa), t(la)
     gb = t(ob)
     gb[torch.from_numpy((lb_ == -np.inf).T.copy())] = float("nan")  # never read where lse_b = -inf
+    # nor out_a where lse_a = -inf and lse_b is finite: the first partial never wrote it
+    ga[torch.from_numpy(((la == -np.inf) & (lb_ != -np.inf)).T.copy())] = float("nan")
     lb.lse_merge(ga, gla, gb, t(lb_))
     torch.cuda.synchronize()
     go, gl = ga.cpu().numpy(), gla.cpu().numpy()
@@ -485,3 +513,4 @@ def test_lse_merge_matches_oracle(d):
     assert np.abs(go[rows_fin] - ref_o[rows_fin]).max() <= 1e-5
     keep = (lb_ == -np.inf).T
     assert np.array_equal(go[keep], np.float32(oa)[keep])
+    assert np.all(np.isfinite(go[rows_fin]))
