@@ -18,6 +18,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kBatch = 8;  // units per lane loaded before any is stored
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   // per wave: the taken rows of the current group, compacted, and their two weights
@@ -57,19 +58,30 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       s_wb[w][slot] = wb;
     }
     // The table is this wave's alone and LDS instructions of one wave complete in order.
-    // Units (taken row, 16-byte piece) are spread over the lanes so that every lane keeps
-    // several independent loads in flight.
+    // Units (taken row, 16-byte piece) are spread over the lanes; each lane loads a batch
+    // of units before it stores any (a store to out_a could alias a later load, so the
+    // compiler would not hoist loads across it), keeping 2 x kBatch loads in flight.
     const int units = __popcll(mask) * chunks;
-#pragma unroll 4
-    for (int u = lane; u < units; u += 64) {
-      const int k = u / chunks, c = u - k * chunks;
-      const int r = s_row[w][k];
-      const float ca = s_wa[w][k], cb = s_wb[w][k];
-      const int64_t rh = (row0 + r) * a.heads + head;
-      f32x4* oa = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + c;
-      const f32x4 y = reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[c];
-      // out_a is not read where lse_a = -inf: the first partial never wrote that row
-      *oa = ca == 0.0f ? y : *oa * ca + y * cb;
+    for (int u0 = 0; u0 < units; u0 += kBatch * 64) {
+      f32x4 x[kBatch], y[kBatch];
+      float ca[kBatch], cb[kBatch];
+      f32x4* dst[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int u = u0 + j * 64 + lane;
+        const bool ok = u < units;
+        const int k = ok ? u / chunks : 0, c = ok ? u - k * chunks : 0;
+        const int64_t rh = (row0 + s_row[w][k]) * a.heads + head;
+        ca[j] = ok ? s_wa[w][k] : -1.0f;  // -1: no unit
+        cb[j] = s_wb[w][k];
+        dst[j] = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + c;
+        y[j] = ok ? reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[c] : f32x4{};
+        // out_a is not read where lse_a = -inf (ca = 0): the first partial never wrote that row
+        x[j] = ca[j] > 0.0f ? *dst[j] : f32x4{};
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (ca[j] >= 0.0f) *dst[j] = ca[j] == 0.0f ? y[j] : x[j] * ca[j] + y[j] * cb[j];
     }
   }
 }
