@@ -105,7 +105,7 @@ class VarlenStep:
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
-    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0):
+    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True):
         self.torch, self.lb = torch, lb
         lengths = workloads.zigzag_pack_lengths(seed)
         cache = {}
@@ -117,6 +117,10 @@ class ZigzagStep:
 
         self.share = lb.zigzag.RankShare(lengths, chunk, rank, cp, get_chunk)
         self.share.plan_all()  # allocates the per-step workspaces outside the timed region
+        # the share's 16 launches are replayed from one HIP graph; per-kernel events need
+        # eager launches (run_eager)
+        self.graph = self.share.capture() if graph else None
+        self.kernel_name = "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)"
         self.H, self.d = 32, 128
         # pairs: positions and document ids of the rank's rows against each step's chunks
         pos, doc = lb.zigzag.token_meta(lengths)
@@ -137,6 +141,12 @@ class ZigzagStep:
         return len(self.share.steps)
 
     def run(self, evs=None):
+        if self.graph is not None and evs is None:
+            self.share.replay()
+            return
+        self.run_eager(evs)
+
+    def run_eager(self, evs=None):
         # one planning launch for all steps (their key/value metadata is known up front),
         # then per step the attention launch and, from step 1 on, the merge
         lb, sh = self.lb, self.share
@@ -165,7 +175,7 @@ class ZigzagStep:
         return self.lb.read_worker_timing(self.share.step_workspaces[0])
 
 
-def make_workload(name, seed, torch, lb, workloads):
+def make_workload(name, seed, torch, lb, workloads, graph=True):
     if name == "longtail":
         p = workloads.longtail_pack(seed)
         w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -198,10 +208,11 @@ def make_workload(name, seed, torch, lb, workloads):
         w.packs = [p]
         return w
     if name == "zigzag":
-        w = ZigzagStep(torch, lb, workloads, seed=seed)
+        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph)
         w.config = {"workload": "one zigzag CP rank's share at cp=8: rank 3 of a 131072-token lognormal pack "
                                 f"(seed {seed}), 16 chunks of 8192, 8 ring steps + 7 merges",
-                    "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128}
+                    "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
+                    "launch": "one HIP graph per step" if graph else "eager"}
         return w
     raise SystemExit(f"unknown workload {name}")
 
@@ -267,6 +278,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -289,7 +301,8 @@ def main():
 
     lb.lib()
     log(f"bench: building workload {args.workload}")
-    w = make_workload(args.workload, args.seed, torch, lb, workloads)
+    w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager)
+    graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup}")
@@ -306,10 +319,19 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        w.run(evs[s])
+        w.run(None if graphed else evs[s])
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
+    eager_ms_per_step = None
+    if graphed:
+        # per-kernel times come from one more pass of eager launches, outside the timed region
+        log(f"bench: {args.steps} eager steps for the per-kernel events")
+        t1 = time.perf_counter()
+        for s in range(args.steps):
+            w.run_eager(evs[s])
+        torch.cuda.synchronize()
+        eager_ms_per_step = (time.perf_counter() - t1) / args.steps * 1e3
     plan_ms = float(np.mean([sum(e[0].elapsed_time(e[1]) for e in step) for step in evs]))
     attn_ms = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in step) for step in evs]))
     per_launch = [[round(float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])), 4),
@@ -341,6 +363,7 @@ def main():
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
         "kernels_ms_per_launch": per_launch if n_launch > 1 else None,
+        "eager_ms_per_step": None if eager_ms_per_step is None else round(eager_ms_per_step, 4),
         "cu_busy_max_over_mean": None if cu_ratio is None else round(cu_ratio, 4),
         "attention_span_device_clock_ms": round(span_ticks / 1e5, 4),
         "roofline": {
@@ -350,7 +373,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_entry() if args.workload == "longtail" else None,
-            "kernel": "attn_kernel<128,false> (persistent, LPT queue)",
+            "kernel": getattr(w, "kernel_name", "attn_kernel<128,false> (persistent, LPT queue)"),
             "launch_ms": round(attn_ms_per_launch, 4),
         },
         "cpu_baseline": None,

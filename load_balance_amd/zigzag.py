@@ -124,3 +124,23 @@ class RankShare:
             if not first:
                 lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
         return self.out, self.lse
+
+    def capture(self, stream=None):
+        """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
+        merges -- into a HIP graph, so that replay() launches the whole share at once.
+        Every kernel of the share is safe to replay: the planner resets the queue heads
+        and the attention kernel rewinds them, and nothing in it clears memory with a
+        memset node."""
+        self.run_planned(stream=stream)  # allocates the step workspaces, caches the CU count
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_planned()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        """One launch of the captured share; returns (out, lse), written in place."""
+        self.graph.replay()
+        return self.out, self.lse
