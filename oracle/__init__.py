@@ -12,12 +12,14 @@ Modules
 ``attention``  explicit-mask attention per document / pack / block, the
                log-sum-exp merge and the zigzag ring fold.
 ``plan``       the reference tile enumerator: which (query tile, key span)
-               pairs hold visible pairs, their exact pair counts, and the
-               longest-first order.
+               pairs hold visible pairs, their exact pair counts, the key
+               blocks each sweeps, and the longest-first order.
+``sharding``   which tokens each context-parallel rank holds (sequence zigzag,
+               per-document, striped) and one rank's sharded ring fold.
 
 Pins (what each function is checked against, in ``tests/test_oracle_*.py``):
 every function here is pinned by closed forms, special cases, a library
 routine (torch ``scaled_dot_product_attention`` in float64) or brute force on
 tiny inputs; none is marked "parity unpinned".
 """
-from . import attention, plan  # noqa: F401
+from . import attention, plan, sharding  # noqa: F401
