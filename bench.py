@@ -175,7 +175,52 @@ class ZigzagStep:
         return self.lb.read_worker_timing(self.share.step_workspaces[0])
 
 
-def make_workload(name, seed, torch, lb, workloads, graph=True):
+class CpJob:
+    """Every rank's share of a context-parallel job at cp = 8 over the 131072-token pack,
+    one after another on this GPU (each share replayed from its own HIP graph)."""
+
+    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0):
+        from load_balance_amd import sharding as LS
+        self.torch, self.lb = torch, lb
+        lengths = workloads.zigzag_pack_lengths(seed)
+        parts = [workloads.zigzag_chunk_values(c, chunk) for c in range(2 * cp)]
+        q, k, v = (np.concatenate([p[i] for p in parts]) for i in range(3))
+        self.tokens = LS.shard_tokens(rule, lengths, cp)
+        shards = LS.build_shards(lengths, self.tokens, lambda idx: (q[idx], k[idx], v[idx]))
+        self.shares = [LS.ShardedRank(shards, r) for r in range(cp)]
+        for s in self.shares:
+            s.capture()
+        self.H, self.d = 32, 128
+        pos_in_doc = np.concatenate([np.arange(n) for n in lengths])
+        self.rank_pairs = [int(np.sum(pos_in_doc[t] + 1)) for t in self.tokens]
+        self.pairs = sum(self.rank_pairs)
+        self.flops = 4 * self.d * self.H * self.pairs
+        best, cost = LS.choose_sharding(lengths, cp, 64)
+        self.predicted = {"chosen": best,
+                          "rank_us": {r: [round(x, 1) for x in c["us"]] for r, c in cost.items()}}
+        self.kernel_name = "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)"
+        self.graph = None  # events go around each rank's replay
+
+    def n_launches(self):
+        return len(self.shares)
+
+    def run(self, evs=None):
+        for r, s in enumerate(self.shares):
+            if evs is not None:
+                evs[r][0].record()
+                evs[r][1].record()
+            s.replay()
+            if evs is not None:
+                evs[r][2].record()
+
+    def plan_pairs(self):
+        return None
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.shares[0].step_workspaces[0])
+
+
+def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document"):
     if name == "longtail":
         p = workloads.longtail_pack(seed)
         w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -213,6 +258,14 @@ def make_workload(name, seed, torch, lb, workloads, graph=True):
                                 f"(seed {seed}), 16 chunks of 8192, 8 ring steps + 7 merges",
                     "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
                     "launch": "one HIP graph per step" if graph else "eager"}
+        return w
+    if name == "cp_job":
+        w = CpJob(torch, lb, workloads, rule, seed=seed)
+        w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
+                                f"{rule} sharding: all 8 ranks' shares (8 ring steps + 7 merges each) in turn",
+                    "tokens": 131072, "heads": 32, "kv_heads": 8, "head_dim": 128, "sharding": rule,
+                    "rank_pairs_per_head": w.rank_pairs,
+                    "time_model_prediction": w.predicted}
         return w
     raise SystemExit(f"unknown workload {name}")
 
@@ -265,6 +318,18 @@ def traffic_entry():
         return None
 
 
+def cp_job_fields(w, per_launch):
+    """For the context-parallel job: each rank's share time, the makespan if the ranks ran on
+    their own GPUs, and the per-GPU throughput that makespan gives."""
+    if not isinstance(w, CpJob):
+        return {}
+    rank_ms = [pl[1] for pl in per_launch]
+    makespan = max(rank_ms)
+    return {"cp_rank_ms": rank_ms, "cp_makespan_ms": round(makespan, 4),
+            "cp_busiest_over_mean": round(makespan / float(np.mean(rank_ms)), 4),
+            "cp_tflops_per_gpu_if_parallel": round(w.flops / len(rank_ms) / (makespan / 1e3) / 1e12, 3)}
+
+
 # ----------------------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
@@ -274,7 +339,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
-                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy"])
+                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job"])
+    ap.add_argument("--rule", default="per_document", choices=["per_document", "zigzag"],
+                    help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -301,7 +368,7 @@ def main():
 
     lb.lib()
     log(f"bench: building workload {args.workload}")
-    w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager)
+    w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule)
     graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 
@@ -364,6 +431,7 @@ def main():
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
         "kernels_ms_per_launch": per_launch if n_launch > 1 else None,
         "eager_ms_per_step": None if eager_ms_per_step is None else round(eager_ms_per_step, 4),
+        **cp_job_fields(w, per_launch),
         "cu_busy_max_over_mean": None if cu_ratio is None else round(cu_ratio, 4),
         "attention_span_device_clock_ms": round(span_ticks / 1e5, 4),
         "roofline": {

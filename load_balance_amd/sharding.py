@@ -1,0 +1,298 @@
+"""Context-parallel sharding of a packed sequence, and one rank's sharded ring on one GPU.
+
+Which query tokens each of cp ranks holds:
+
+* ``zigzag``: the pack is cut into 2*cp equal chunks and rank i holds chunks i
+  and 2*cp-1-i ("03 · 长文负载均衡", section 4.2).  On a packed sequence this
+  balances the ranks only in expectation (same page, section 1.2; the
+  131072-token pack of seed 0 at cp = 8 leaves the busiest rank 1.63x the mean).
+* ``per_document``: every document is cut into 2*cp chunks and rank i takes
+  chunks i and 2*cp-1-i of each; a length that is not a multiple of 2*cp leaves
+  a tail of len mod 2*cp tokens, dealt round-robin with one pointer over the
+  whole pack (section 4.3, WLB-LLM): every rank gets the same causal area of
+  every document and the same token count to within one.
+* ``striped``: stripes of ``width`` tokens dealt to ranks in turn (section 4.2,
+  Striped Attention).
+
+At ring step t a rank attends its queries to the keys and values of rank
+(r - t) mod cp ("长序列训练与上下文并行", Ring Attention) and folds the step's
+partial result into its running one with ``lse_merge``.  Every step is one
+``block_attn_fwd`` (positions and document ids travel with the tokens, so any
+token set works) -- planned up front with ``plan_block_steps``, since a step's
+metadata is known before its keys and values arrive.
+
+Per-document sharding trades balance for shorter runs, and a short query run
+still costs a whole tile (section 3.3; section 4.3 on WLB-LLM's adaptive choice
+between per-sequence and per-document sharding by predicted latency with
+tile-rounded cost).  ``predicted_work`` counts the key blocks and work items the
+attention kernel would run for a rank; a linear time model over blocks, items
+and ring steps, with coefficients fitted to measured rank times ("数据并行负载均衡",
+section 4.3: costs from a fitted model; "03 · 长文负载均衡", section 2.2:
+coefficients fitted by offline profiling), turns them into a predicted time,
+and ``choose_sharding`` picks the rule whose busiest rank is predicted fastest.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+BLOCK_KEYS = 64  # keys per block of the attention kernel (LB_BLOCK_KEYS)
+
+
+# --------------------------------------------------------------------------
+# sharding rules: per rank, ascending global token indices
+# --------------------------------------------------------------------------
+def zigzag_tokens(total: int, cp: int):
+    if total % (2 * cp):
+        raise ValueError("zigzag sharding needs a pack length divisible by 2*cp")
+    c = total // (2 * cp)
+    return [np.r_[i * c:(i + 1) * c, (2 * cp - 1 - i) * c:(2 * cp - i) * c].astype(np.int64) for i in range(cp)]
+
+
+def per_document_tokens(lengths, cp: int):
+    parts = [[] for _ in range(cp)]
+    start, deal = 0, 0
+    for n in (int(x) for x in lengths):
+        c = n // (2 * cp)
+        for i in range(cp):
+            parts[i].append(np.arange(start + i * c, start + (i + 1) * c))
+            parts[i].append(np.arange(start + (2 * cp - 1 - i) * c, start + (2 * cp - i) * c))
+        tail = np.arange(start + 2 * cp * c, start + n)
+        owner = (deal + np.arange(len(tail))) % cp
+        for i in range(cp):
+            parts[i].append(tail[owner == i])
+        deal = (deal + len(tail)) % cp
+        start += n
+    return [np.sort(np.concatenate(p)).astype(np.int64) for p in parts]
+
+
+def striped_tokens(total: int, cp: int, width: int = 1):
+    t = np.arange(total, dtype=np.int64)
+    return [t[(t // width) % cp == r] for r in range(cp)]
+
+
+def shard_tokens(rule: str, lengths, cp: int, width: int = 1):
+    total = int(np.sum(lengths))
+    if rule == "zigzag":
+        return zigzag_tokens(total, cp)
+    if rule == "per_document":
+        return per_document_tokens(lengths, cp)
+    if rule == "striped":
+        return striped_tokens(total, cp, width)
+    raise ValueError(f"unknown sharding rule {rule!r}")
+
+
+def ring_source(rank: int, step: int, cp: int) -> int:
+    return (rank - step) % cp
+
+
+def token_meta(lengths):
+    """Global position and document id (int32) of every token of a pack."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    pos = np.arange(int(lengths.sum()), dtype=np.int32)
+    doc = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+    return pos, doc
+
+
+# --------------------------------------------------------------------------
+# cost of a sharding: key blocks the attention kernel sweeps (host side)
+# --------------------------------------------------------------------------
+def _runs(pos, doc):
+    """(start, length, first position, doc) of each run of equal doc and consecutive position."""
+    if len(pos) == 0:
+        return np.zeros((0, 4), dtype=np.int64)
+    brk = np.flatnonzero((np.diff(doc) != 0) | (np.diff(pos) != 1)) + 1
+    starts = np.r_[0, brk]
+    lens = np.diff(np.r_[starts, len(pos)])
+    return np.stack([starts, lens, pos[starts], doc[starts]], axis=1).astype(np.int64)
+
+
+def predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int):
+    """(key blocks, work items) of one kv head for a query shard against a key/value shard:
+    each run of the query shard is cut into tiles of ``tile_rows``; a tile sweeps, of every
+    key run of its document, the blocks holding keys its last row can see, and is a work
+    item when it sweeps any."""
+    qr, kr = _runs(np.asarray(q_pos), np.asarray(q_doc)), _runs(np.asarray(kv_pos), np.asarray(kv_doc))
+    blocks = items = 0
+    by_doc = {}
+    for (_, ln, p0, d) in kr:
+        by_doc.setdefault(int(d), []).append((int(ln), int(p0)))
+    for (_, ln, p0, d) in qr:
+        spans = by_doc.get(int(d))
+        if not spans:
+            continue
+        last = p0 + np.minimum(np.arange(tile_rows, int(ln) + tile_rows, tile_rows), ln) - 1  # last row of each tile
+        per_tile = np.zeros(len(last), dtype=np.int64)
+        for (kl, kp0) in spans:
+            keep = np.clip(last - kp0 + 1, 0, kl)
+            per_tile += (keep + BLOCK_KEYS - 1) // BLOCK_KEYS
+        blocks += int(per_tile.sum())
+        items += int(np.count_nonzero(per_tile))
+    return blocks, items
+
+
+def predicted_blocks(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int) -> int:
+    return predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows)[0]
+
+
+def rank_work(lengths, tokens, tile_rows: int):
+    """Per rank: (key blocks, work items, ring steps with any work), one kv head, over all
+    its ring steps."""
+    pos, doc = token_meta(lengths)
+    cp = len(tokens)
+    out = []
+    for r in range(cp):
+        b = i = s = 0
+        for t in range(cp):
+            src = tokens[ring_source(r, t, cp)]
+            bt, it = predicted_work(pos[tokens[r]], doc[tokens[r]], pos[src], doc[src], tile_rows)
+            b, i, s = b + bt, i + it, s + (it > 0)
+        out.append((b, i, s))
+    return out
+
+
+# Rank time model: us = a * blocks * kv_heads / CUs + b * items * kv_heads / CUs + c * steps + d.
+# Fitted (least squares, fit_cost.py) to the 16 rank shares of the 131072-token pack at cp = 8
+# under both rules on one MI355X (256 CUs, 32 q / 8 kv heads, d = 128): within 9% of every one.
+TIME_MODEL_US = dict(per_block=2.128, per_item=16.883, per_step=1.886, fixed=132.0)
+
+
+def predicted_rank_us(work, kv_heads: int, n_cu: int = 256, model=TIME_MODEL_US):
+    return [model["per_block"] * b * kv_heads / n_cu + model["per_item"] * i * kv_heads / n_cu +
+            model["per_step"] * s + model["fixed"] for (b, i, s) in work]
+
+
+def choose_sharding(lengths, cp: int, tile_rows: int, kv_heads: int = 8, n_cu: int = 256,
+                    rules=("zigzag", "per_document")):
+    """The rule whose busiest rank has the smallest predicted time, with, per rule, the
+    per-rank predicted microseconds and work: {rule: {"us": [...], "work": [(blocks, items,
+    steps), ...]}}."""
+    cost = {}
+    for rule in rules:
+        try:
+            work = rank_work(lengths, shard_tokens(rule, lengths, cp), tile_rows)
+        except ValueError:  # the rule does not apply (zigzag needs a multiple of 2*cp tokens)
+            continue
+        cost[rule] = {"us": predicted_rank_us(work, kv_heads, n_cu), "work": work}
+    best = min(cost, key=lambda r: max(cost[r]["us"]))
+    return best, cost
+
+
+# --------------------------------------------------------------------------
+# device-resident shards and one rank's ring
+# --------------------------------------------------------------------------
+def build_shards(lengths, tokens, get_rows, device="cuda"):
+    """Per rank: its tokens' q [n,H,d], stacked k/v [2,n,H_kv,d] (bf16) and positions and
+    document ids (int32), on the device.  get_rows(idx) -> (q, k, v) of the given global
+    token indices, as bf16 bit arrays (uint16) or bf16 tensors."""
+    pos, doc = token_meta(lengths)
+
+    def bf16(x):
+        if isinstance(x, torch.Tensor):
+            return x.to(device=device, dtype=torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+
+    shards = []
+    for idx in tokens:
+        q, k, v = get_rows(idx)
+        shards.append(dict(tokens=idx, q=bf16(q).contiguous(), kv=torch.stack([bf16(k), bf16(v)]).contiguous(),
+                           pos=torch.from_numpy(pos[idx]).to(device), doc=torch.from_numpy(doc[idx]).to(device)))
+    return shards
+
+
+class ShardedRank:
+    """One rank's cp ring steps over device-resident shards (see ``build_shards``).
+
+    run() calls block_attn_fwd per step (planning each); run_planned() plans every step
+    in one launch first; capture()/replay() record run_planned() in a HIP graph.  Results
+    are out (fp32 [n_q,H,d]) and lse ([H,n_q]) of the rank's tokens, in their order.
+    """
+
+    def __init__(self, shards, rank, device="cuda"):
+        from . import new_workspace
+        cp = len(shards)
+        self.cp, self.rank = cp, rank
+        me = shards[rank]
+        self.tokens = me["tokens"]
+        self.q, self.q_pos, self.q_doc = me["q"], me["pos"], me["doc"]
+        self.steps = []
+        for t in range(cp):
+            src = shards[ring_source(rank, t, cp)]
+            self.steps.append(dict(source=ring_source(rank, t, cp), kv=src["kv"], kv_pos=src["pos"],
+                                   kv_doc=src["doc"]))
+        n_q, H, d = self.q.shape
+        Hkv = self.steps[0]["kv"].shape[2]
+        self.out = torch.empty((n_q, H, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((H, n_q), dtype=torch.float32, device=device)
+        self.step_out = torch.empty_like(self.out)
+        self.step_lse = torch.empty_like(self.lse)
+        # workspace sized for the longest side and the most runs of any step
+        n_max = max([n_q] + [s["kv"].shape[1] for s in self.steps])
+        runs = max([len(_runs(self.q_pos.cpu().numpy(), self.q_doc.cpu().numpy()))] +
+                   [len(_runs(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy())) for s in self.steps])
+        self._ws_shape = (n_max, max(1, runs), H, Hkv, device)
+        self.workspace = new_workspace(*self._ws_shape)
+        self.step_workspaces = None
+        self.graph = None
+
+    def run(self, stream=None, per_step=None):
+        """All cp steps, each a block_attn_fwd, plus cp - 1 merges."""
+        from . import block_attn_fwd, lse_merge
+        for t, st in enumerate(self.steps):
+            first = t == 0
+            out = self.out if first else self.step_out
+            lse = self.lse if first else self.step_lse
+            block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
+                           workspace=self.workspace, stream=stream)
+            if per_step is not None:
+                per_step(t, out, lse)
+            if not first:
+                lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
+        return self.out, self.lse
+
+    def plan_all(self, stream=None):
+        """Plans every ring step in one launch, one workspace per step: a step's key/value
+        positions and document ids follow from the sharding, before its data arrive."""
+        from . import new_workspace, plan_block_steps
+        if self.step_workspaces is None:
+            self.step_workspaces = [new_workspace(*self._ws_shape) for _ in self.steps]
+        n_q, H, d = self.q.shape
+        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in self.steps],
+                         [st["kv_doc"] for st in self.steps], H, self.steps[0]["kv"].shape[2], d,
+                         self.step_workspaces, stream=stream)
+
+    def run_planned(self, stream=None, per_step=None):
+        """run() with the plans of all steps made up front by plan_all(): one planning launch,
+        then per step the attention launch and (from step 1 on) the merge."""
+        from . import attn_run, lse_merge
+        self.plan_all(stream)
+        for t, st in enumerate(self.steps):
+            first = t == 0
+            out = self.out if first else self.step_out
+            lse = self.lse if first else self.step_lse
+            attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=stream)
+            if per_step is not None:
+                per_step(t, out, lse)
+            if not first:
+                lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
+        return self.out, self.lse
+
+    def capture(self, stream=None):
+        """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
+        merges -- into a HIP graph, so that replay() launches the whole share at once.
+        Every kernel of the share is safe to replay: the planner resets the queue heads
+        and the attention kernel rewinds them, and nothing in it clears memory with a
+        memset node."""
+        self.run_planned(stream=stream)  # allocates the step workspaces, caches the CU count
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_planned()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        """One launch of the captured share; returns (out, lse), written in place."""
+        self.graph.replay()
+        return self.out, self.lse

@@ -17,6 +17,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from .sharding import ShardedRank
+
 
 def chunks_of_rank(rank: int, cp: int):
     return (rank, 2 * cp - 1 - rank)
@@ -36,8 +38,10 @@ def token_meta(lengths):
     return pos, doc
 
 
-class RankShare:
-    """Device-resident inputs of one rank's cp ring steps.
+class RankShare(ShardedRank):
+    """Device-resident inputs of one rank's cp ring steps under sequence zigzag sharding,
+    built chunk by chunk (only the chunks the rank needs are materialised).  The ring
+    itself (run, plan_all, run_planned, capture, replay) is ShardedRank's.
 
     get_chunk(c) -> (q, k, v) of chunk c as bfloat16 bit arrays (uint16 numpy) or bf16 tensors.
     """
@@ -82,65 +86,4 @@ class RankShare:
         self.workspace = new_workspace(max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
         self._ws_shape = (max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
         self.step_workspaces = None
-
-    def run(self, stream=None, per_step=None):
-        """All cp steps plus cp-1 merges; returns (out fp32 [n_q,H,d], lse [H,n_q])."""
-        from . import block_attn_fwd, lse_merge
-        for t, st in enumerate(self.steps):
-            first = t == 0
-            out = self.out if first else self.step_out
-            lse = self.lse if first else self.step_lse
-            block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
-                           workspace=self.workspace, stream=stream)
-            if per_step is not None:
-                per_step(t, out, lse)
-            if not first:
-                lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
-        return self.out, self.lse
-
-    def plan_all(self, stream=None):
-        """Plans every ring step in one launch, one workspace per step: a step's key/value
-        positions and document ids follow from the packing, before its chunk arrives."""
-        from . import new_workspace, plan_block_steps
-        if self.step_workspaces is None:
-            self.step_workspaces = [new_workspace(*self._ws_shape) for _ in self.steps]
-        n_q, H, d = self.q.shape
-        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in self.steps],
-                         [st["kv_doc"] for st in self.steps], H, self.steps[0]["kv"].shape[2], d,
-                         self.step_workspaces, stream=stream)
-
-    def run_planned(self, stream=None, per_step=None):
-        """run() with the plans of all steps made up front by plan_all(): one planning launch,
-        then per step the attention launch and (from step 1 on) the merge."""
-        from . import attn_run, lse_merge
-        self.plan_all(stream)
-        for t, st in enumerate(self.steps):
-            first = t == 0
-            out = self.out if first else self.step_out
-            lse = self.lse if first else self.step_lse
-            attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=stream)
-            if per_step is not None:
-                per_step(t, out, lse)
-            if not first:
-                lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
-        return self.out, self.lse
-
-    def capture(self, stream=None):
-        """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
-        merges -- into a HIP graph, so that replay() launches the whole share at once.
-        Every kernel of the share is safe to replay: the planner resets the queue heads
-        and the attention kernel rewinds them, and nothing in it clears memory with a
-        memset node."""
-        self.run_planned(stream=stream)  # allocates the step workspaces, caches the CU count
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.run_planned()
-        torch.cuda.synchronize()
-        self.graph = g
-        return g
-
-    def replay(self):
-        """One launch of the captured share; returns (out, lse), written in place."""
-        self.graph.replay()
-        return self.out, self.lse
+        self.graph = None

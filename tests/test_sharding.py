@@ -1,0 +1,83 @@
+"""The library's context-parallel sharding (host side) against the oracle: token sets bit
+for bit, and the key-block cost estimate against the oracle tile enumerator."""
+import numpy as np
+import pytest
+
+import workloads
+from load_balance_amd import sharding as LS
+from oracle import attention as A
+from oracle import plan as OP
+from oracle import sharding as OS
+
+
+@pytest.mark.parametrize("cp", [2, 4, 8])
+@pytest.mark.parametrize("seed", range(5))
+def test_rules_equal_oracle(cp, seed):
+    r = np.random.default_rng(100 + seed)
+    lengths = [int(x) for x in r.integers(1, 400, int(r.integers(1, 25)))]
+    T = sum(lengths)
+    for a, b in zip(LS.per_document_tokens(lengths, cp), OS.per_document_tokens(lengths, cp)):
+        assert np.array_equal(a, b)
+    w = int(r.integers(1, 9))
+    for a, b in zip(LS.striped_tokens(T, cp, w), OS.striped_tokens(T, cp, w)):
+        assert np.array_equal(a, b)
+    T2 = T - T % (2 * cp)
+    if T2:
+        for a, b in zip(LS.zigzag_tokens(T2, cp), OS.zigzag_tokens(T2, cp)):
+            assert np.array_equal(a, b)
+
+
+def test_zigzag_rejects_an_uneven_pack():
+    with pytest.raises(ValueError):
+        LS.zigzag_tokens(30, 4)
+
+
+def oracle_work(pos, doc, qi, ki, bm):
+    tl = [t for t in OP.tiles(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), bm) if t["blocks"] > 0]
+    return sum(t["blocks"] for t in tl), len(tl)
+
+
+@pytest.mark.parametrize("rule", ["zigzag", "per_document", "striped"])
+@pytest.mark.parametrize("bm", [32, 64])
+def test_predicted_work_equals_oracle_enumerator(rule, bm):
+    """Key blocks and work items (tiles with any block) of every rank and ring step equal the
+    oracle enumerator's, bit for bit."""
+    r = np.random.default_rng(bm)
+    cp = 4
+    lengths = [int(x) for x in r.integers(1, 700, 9)]
+    if rule == "zigzag":
+        lengths.append(2 * cp * 600 - sum(lengths))
+    tok = LS.shard_tokens(rule, lengths, cp, width=37)
+    pos, doc = A.pack_positions(lengths)
+    for rank in range(cp):
+        for step in range(cp):
+            qi, ki = tok[rank], tok[LS.ring_source(rank, step, cp)]
+            got = LS.predicted_work(pos[qi].astype(np.int32), doc[qi].astype(np.int32),
+                                    pos[ki].astype(np.int32), doc[ki].astype(np.int32), bm)
+            assert got == oracle_work(pos, doc, qi, ki, bm), (rank, step)
+
+
+def test_choose_sharding_on_the_131072_token_pack():
+    """"03 · 长文负载均衡", section 4.3: per-document sharding balances the ranks but its many
+    short chunks cost whole tiles, so the choice goes by predicted time.  On the 131072-token
+    pack of seed 0 at cp = 8 per-document sharding gives every rank the same area and nearly
+    the same key blocks, but about 7x the work items of sequence zigzag on average; with the fitted time
+    model its busiest rank is the slower one (as measured: 3.0 ms against 1.9 ms), so zigzag
+    is chosen."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    best, cost = LS.choose_sharding(lengths, 8, 64)
+    assert set(cost) == {"zigzag", "per_document"}
+    assert best == min(cost, key=lambda k: max(cost[k]["us"])) == "zigzag"
+    zz, pd = np.array(cost["zigzag"]["work"]), np.array(cost["per_document"]["work"])
+    assert pd[:, 0].max() / pd[:, 0].mean() < 1.03 and zz[:, 0].max() / zz[:, 0].mean() > 1.6  # blocks
+    assert pd[:, 0].max() < zz[:, 0].max()
+    assert pd[:, 1].mean() > 5 * zz[:, 1].mean()  # items
+
+
+def test_choose_sharding_prefers_per_document_for_few_long_documents():
+    # two long documents: sequence zigzag splits the work unevenly, per-document sharding
+    # evens it without short chunks
+    lengths = [98304, 32768]
+    best, cost = LS.choose_sharding(lengths, 8, 64)
+    assert best == "per_document"
+    assert max(cost["per_document"]["us"]) < 0.9 * max(cost["zigzag"]["us"])
