@@ -105,7 +105,7 @@ class VarlenStep:
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
-    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True):
+    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True, overlap=4):
         self.torch, self.lb = torch, lb
         lengths = workloads.zigzag_pack_lengths(seed)
         cache = {}
@@ -117,9 +117,11 @@ class ZigzagStep:
 
         self.share = lb.zigzag.RankShare(lengths, chunk, rank, cp, get_chunk)
         self.share.plan_all()  # allocates the per-step workspaces outside the timed region
-        # the share's 16 launches are replayed from one HIP graph; per-kernel events need
-        # eager launches (run_eager)
-        self.graph = self.share.capture() if graph else None
+        # the share's 16 launches are replayed from one HIP graph, the attention launches
+        # spread over `overlap` streams so that the steps overlap (none: one stream);
+        # per-kernel events need eager launches one at a time (run_eager)
+        self.streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap else None
+        self.graph = self.share.capture(streams=self.streams) if graph else None
         self.kernel_name = "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)"
         self.H, self.d = 32, 128
         # pairs: positions and document ids of the rank's rows against each step's chunks
@@ -179,7 +181,7 @@ class CpJob:
     """Every rank's share of a context-parallel job at cp = 8 over the 131072-token pack,
     one after another on this GPU (each share replayed from its own HIP graph)."""
 
-    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0):
+    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0, overlap=4):
         from load_balance_amd import sharding as LS
         self.torch, self.lb = torch, lb
         lengths = workloads.zigzag_pack_lengths(seed)
@@ -188,8 +190,9 @@ class CpJob:
         self.tokens = LS.shard_tokens(rule, lengths, cp)
         shards = LS.build_shards(lengths, self.tokens, lambda idx: (q[idx], k[idx], v[idx]))
         self.shares = [LS.ShardedRank(shards, r) for r in range(cp)]
+        streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap else None
         for s in self.shares:
-            s.capture()
+            s.capture(streams=streams)
         self.H, self.d = 32, 128
         pos_in_doc = np.concatenate([np.arange(n) for n in lengths])
         self.rank_pairs = [int(np.sum(pos_in_doc[t] + 1)) for t in self.tokens]
@@ -220,7 +223,7 @@ class CpJob:
         return self.lb.read_worker_timing(self.shares[0].step_workspaces[0])
 
 
-def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document"):
+def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4):
     if name == "longtail":
         p = workloads.longtail_pack(seed)
         w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -253,14 +256,15 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
         w.packs = [p]
         return w
     if name == "zigzag":
-        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph)
+        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph, overlap=overlap)
         w.config = {"workload": "one zigzag CP rank's share at cp=8: rank 3 of a 131072-token lognormal pack "
                                 f"(seed {seed}), 16 chunks of 8192, 8 ring steps + 7 merges",
                     "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
-                    "launch": "one HIP graph per step" if graph else "eager"}
+                    "launch": (f"one HIP graph: plan, the 8 attention launches on {overlap} streams, merges in step "
+                               "order" if overlap else "one HIP graph, one stream") if graph else "eager"}
         return w
     if name == "cp_job":
-        w = CpJob(torch, lb, workloads, rule, seed=seed)
+        w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap)
         w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
                                 f"{rule} sharding: all 8 ranks' shares (8 ring steps + 7 merges each) in turn",
                     "tokens": 131072, "heads": 32, "kv_heads": 8, "head_dim": 128, "sharding": rule,
@@ -346,6 +350,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
+    ap.add_argument("--overlap", type=int, default=4,
+                    help="zigzag, cp_job: streams the ring steps' attention launches are spread over (0: one)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -368,7 +374,8 @@ def main():
 
     lb.lib()
     log(f"bench: building workload {args.workload}")
-    w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule)
+    w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule,
+                      overlap=args.overlap)
     graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 

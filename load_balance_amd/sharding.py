@@ -204,8 +204,9 @@ class ShardedRank:
     """One rank's cp ring steps over device-resident shards (see ``build_shards``).
 
     run() calls block_attn_fwd per step (planning each); run_planned() plans every step
-    in one launch first; capture()/replay() record run_planned() in a HIP graph.  Results
-    are out (fp32 [n_q,H,d]) and lse ([H,n_q]) of the rank's tokens, in their order.
+    in one launch first; run_overlapped() also lets the steps' attention launches overlap;
+    capture()/replay() record either in a HIP graph.  Results are out (fp32 [n_q,H,d]) and
+    lse ([H,n_q]) of the rank's tokens, in their order.
     """
 
     def __init__(self, shards, rank, device="cuda"):
@@ -234,6 +235,7 @@ class ShardedRank:
         self.workspace = new_workspace(*self._ws_shape)
         self.step_workspaces = None
         self.graph = None
+        self.overlap_buffers = None
 
     def run(self, stream=None, per_step=None):
         """All cp steps, each a block_attn_fwd, plus cp - 1 merges."""
@@ -277,17 +279,50 @@ class ShardedRank:
                 lse_merge(self.out, self.lse, self.step_out, self.step_lse, stream=stream)
         return self.out, self.lse
 
-    def capture(self, stream=None):
+    def run_overlapped(self, streams, stream=None):
+        """run_planned() with step t's attention launch on streams[t % len(streams)], so
+        that the workgroups of one step take the compute units that the previous step
+        leaves idle while its last items finish (a persistent launch ends with a tail
+        whose length is set by its largest items, not by its total work).  Every step
+        writes its own partial buffers; the merges then run in step order on the
+        calling stream, each once its step is done: the same kernels on the same data
+        as run_planned(), so the same bits."""
+        from . import attn_run, lse_merge
+        main = torch.cuda.current_stream() if stream is None else stream
+        if self.overlap_buffers is None:
+            self.overlap_buffers = [(self.out, self.lse)] + [
+                (torch.empty_like(self.out), torch.empty_like(self.lse)) for _ in self.steps[1:]]
+        self.plan_all(main)
+        planned = torch.cuda.Event()
+        planned.record(main)
+        done = []
+        for t, st in enumerate(self.steps):
+            s = streams[t % len(streams)]
+            s.wait_event(planned)
+            out, lse = self.overlap_buffers[t]
+            attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=s)
+            ev = torch.cuda.Event()
+            ev.record(s)
+            done.append(ev)
+        main.wait_event(done[0])
+        for t in range(1, len(self.steps)):
+            main.wait_event(done[t])
+            lse_merge(self.out, self.lse, *self.overlap_buffers[t], stream=main)
+        return self.out, self.lse
+
+    def capture(self, stream=None, streams=None):
         """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
-        merges -- into a HIP graph, so that replay() launches the whole share at once.
-        Every kernel of the share is safe to replay: the planner resets the queue heads
-        and the attention kernel rewinds them, and nothing in it clears memory with a
-        memset node."""
-        self.run_planned(stream=stream)  # allocates the step workspaces, caches the CU count
+        merges -- or, given side streams, run_overlapped(), into a HIP graph, so that
+        replay() launches the whole share at once.  Every kernel of the share is safe to
+        replay: the planner resets the queue heads and the attention kernel rewinds them,
+        and nothing in it clears memory with a memset node."""
+        body = (lambda st=None: self.run_planned(stream=st)) if streams is None else \
+            (lambda st=None: self.run_overlapped(streams, stream=st))
+        body(stream)  # allocates the step workspaces and buffers, caches the CU count
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.run_planned()
+            body()
         torch.cuda.synchronize()
         self.graph = g
         return g

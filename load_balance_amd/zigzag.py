@@ -87,3 +87,4 @@ class RankShare(ShardedRank):
         self._ws_shape = (max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
         self.step_workspaces = None
         self.graph = None
+        self.overlap_buffers = None

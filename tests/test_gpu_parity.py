@@ -328,6 +328,44 @@ def test_zigzag_graph_replays_equal_eager_runs():
         assert lb.read_device_error(share.step_workspaces[t]) == 0
 
 
+def test_zigzag_overlapped_steps_equal_the_serial_share():
+    """The ring steps' attention launches spread over side streams (eager, then captured in
+    one HIP graph and replayed three times with eager work in between) give the bits of the
+    one-stream share: each step has its own partial buffers and the merges keep step order."""
+    cp, C, H, Hkv, d = 4, 256, 8, 2, 128
+    T = 2 * cp * C
+    lengths = workloads.lognormal_lengths(T, 9, T)
+    r = np.random.default_rng(14)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+
+    def get_chunk(c):
+        sl = slice(c * C, (c + 1) * C)
+        return q[sl], k[sl], v[sl]
+
+    share = lb.zigzag.RankShare(lengths, C, 2, cp, get_chunk)
+    out, lse = share.run_planned()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    out, lse = share.run_overlapped(streams)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), "eager overlapped"
+    say("  capturing the overlapped share")
+    share.capture(streams=streams)
+    for i in range(3):
+        share.out.fill_(7.0)
+        share.lse.fill_(7.0)
+        out, lse = share.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {i}")
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {i}"
+        out, lse = share.run_planned()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager run after replay {i}"
+    for t in range(cp):
+        assert lb.read_device_error(share.step_workspaces[t]) == 0
+
+
 def test_zigzag_reassembly_small():
     """All ranks of a reduced pack (cp=4, 16 chunks of 256... here 8 chunks of 256) against the unsharded oracle."""
     cp, C, H, Hkv, d = 4, 256, 8, 2, 128
