@@ -187,7 +187,8 @@ class CpJob:
         lengths = workloads.zigzag_pack_lengths(seed)
         parts = [workloads.zigzag_chunk_values(c, chunk) for c in range(2 * cp)]
         q, k, v = (np.concatenate([p[i] for p in parts]) for i in range(3))
-        self.tokens = LS.shard_tokens(rule, lengths, cp)
+        base, n_chunks = LS.parse_rule(rule)
+        self.tokens = LS.shard_tokens(base, lengths, cp, n_chunks=n_chunks)
         shards = LS.build_shards(lengths, self.tokens, lambda idx: (q[idx], k[idx], v[idx]))
         self.shares = [LS.ShardedRank(shards, r) for r in range(cp)]
         streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap else None
@@ -198,7 +199,7 @@ class CpJob:
         self.rank_pairs = [int(np.sum(pos_in_doc[t] + 1)) for t in self.tokens]
         self.pairs = sum(self.rank_pairs)
         self.flops = 4 * self.d * self.H * self.pairs
-        best, cost = LS.choose_sharding(lengths, cp, 64)
+        best, cost = LS.choose_sharding(lengths, cp, 64, rules=CP_RULES)
         self.predicted = {"chosen": best,
                           "rank_us": {r: [round(x, 1) for x in c["us"]] for r, c in cost.items()}}
         self.kernel_name = "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)"
@@ -221,6 +222,9 @@ class CpJob:
 
     def workers(self):
         return self.lb.read_worker_timing(self.shares[0].step_workspaces[0])
+
+
+CP_RULES = ("zigzag", "per_document", "dispatch/16", "dispatch/32", "dispatch/64", "dispatch/128")
 
 
 def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4):
@@ -344,7 +348,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
                     choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job"])
-    ap.add_argument("--rule", default="per_document", choices=["per_document", "zigzag"],
+    ap.add_argument("--rule", default="per_document", choices=list(CP_RULES),
                     help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -27,7 +27,8 @@ def fit(lines, n_cu=256, tile_rows=64):
     for d in lines:
         cfg = d["config"]
         lengths = workloads.zigzag_pack_lengths(int(cfg.get("seed", 0)))
-        tokens = sharding.shard_tokens(cfg["sharding"], lengths, len(d["cp_rank_ms"]))
+        rule, n_chunks = sharding.parse_rule(cfg["sharding"])
+        tokens = sharding.shard_tokens(rule, lengths, len(d["cp_rank_ms"]), n_chunks=n_chunks)
         for (b, i, s), ms in zip(sharding.rank_work(lengths, tokens, tile_rows), d["cp_rank_ms"]):
             rows.append([b * cfg["kv_heads"] / n_cu, i * cfg["kv_heads"] / n_cu, s, 1.0])
             times.append(ms * 1e3)

@@ -13,6 +13,13 @@ Which query tokens each of cp ranks holds:
   every document and the same token count to within one.
 * ``striped``: stripes of ``width`` tokens dealt to ranks in turn (section 4.2,
   Striped Attention).
+* ``dispatch``: MagiAttention's dispatch solver (section 4.4): the pack is cut
+  into ``n_chunks`` equal chunks along the query axis; each chunk's mask area
+  (its visible (query, key) pairs) is computed, and the chunks are dealt, largest
+  area first, each to the least-loaded rank that holds fewer than n_chunks / cp
+  chunks (a min-heap).  Token counts stay equal (the linear term of the cost) while
+  the greedy evens the area (the quadratic term).  On one causal document with
+  n_chunks = 2*cp it gives exactly the zigzag pairing.
 
 At ring step t a rank attends its queries to the keys and values of rank
 (r - t) mod cp ("长序列训练与上下文并行", Ring Attention) and folds the step's
@@ -32,6 +39,8 @@ coefficients fitted by offline profiling), turns them into a predicted time,
 and ``choose_sharding`` picks the rule whose busiest rank is predicted fastest.
 """
 from __future__ import annotations
+
+import heapq
 
 import numpy as np
 import torch
@@ -71,7 +80,45 @@ def striped_tokens(total: int, cp: int, width: int = 1):
     return [t[(t // width) % cp == r] for r in range(cp)]
 
 
-def shard_tokens(rule: str, lengths, cp: int, width: int = 1):
+def chunk_areas(lengths, n_chunks: int) -> np.ndarray:
+    """Per-document causal mask area of each of ``n_chunks`` equal query chunks: a token at
+    position p of its document sees p + 1 keys."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    total = int(lengths.sum())
+    if n_chunks <= 0 or total % n_chunks:
+        raise ValueError("dispatch needs a pack length divisible by the chunk count")
+    starts = np.repeat(np.cumsum(lengths) - lengths, lengths)
+    seen = np.arange(total, dtype=np.int64) - starts + 1
+    return seen.reshape(n_chunks, -1).sum(axis=1)
+
+
+def dispatch_chunks(areas, cp: int):
+    """Greedy dispatch of chunks to cp ranks of equal chunk counts: largest area first
+    (ties: lower chunk id), each to the open rank with the least area (ties: lower rank),
+    through a min-heap of (area, rank) that drops a rank once it is full."""
+    n = len(areas)
+    if n % cp:
+        raise ValueError("dispatch needs a chunk count divisible by cp")
+    capacity = n // cp
+    heap = [(0, r) for r in range(cp)]
+    held = [[] for _ in range(cp)]
+    for c in sorted(range(n), key=lambda c: (-int(areas[c]), c)):
+        load, r = heapq.heappop(heap)
+        held[r].append(c)
+        if len(held[r]) < capacity:
+            heapq.heappush(heap, (load + int(areas[c]), r))
+    return [sorted(h) for h in held]
+
+
+def dispatch_tokens(lengths, cp: int, n_chunks: int):
+    total = int(np.sum(lengths))
+    size = total // n_chunks
+    held = dispatch_chunks(chunk_areas(lengths, n_chunks), cp)
+    return [np.concatenate([np.arange(c * size, (c + 1) * size) for c in h]).astype(np.int64) for h in held]
+
+
+def shard_tokens(rule: str, lengths, cp: int, width: int = 1, n_chunks: int = 0):
+    """Token sets of every rank under ``rule``; ``n_chunks`` (dispatch) defaults to 2*cp."""
     total = int(np.sum(lengths))
     if rule == "zigzag":
         return zigzag_tokens(total, cp)
@@ -79,6 +126,8 @@ def shard_tokens(rule: str, lengths, cp: int, width: int = 1):
         return per_document_tokens(lengths, cp)
     if rule == "striped":
         return striped_tokens(total, cp, width)
+    if rule == "dispatch":
+        return dispatch_tokens(lengths, cp, n_chunks or 2 * cp)
     raise ValueError(f"unknown sharding rule {rule!r}")
 
 
@@ -131,6 +180,22 @@ def predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int):
     return blocks, items
 
 
+MAX_SPANS = 4  # key runs of its document one query run may meet (LB_MAX_SPANS)
+
+
+def max_spans(lengths, tokens) -> int:
+    """The most key runs of its own document, not wholly after it, that any query run of any
+    rank meets on any ring step: the planner refuses a step where this exceeds MAX_SPANS."""
+    pos, doc = token_meta(lengths)
+    runs = [_runs(pos[t], doc[t]) for t in tokens]
+    worst = 0
+    for qr in runs:
+        for kr in runs:
+            for (_, ln, p0, d) in qr:
+                worst = max(worst, int(np.count_nonzero((kr[:, 3] == d) & (kr[:, 2] <= p0 + ln - 1))))
+    return worst
+
+
 def predicted_blocks(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int) -> int:
     return predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows)[0]
 
@@ -152,9 +217,11 @@ def rank_work(lengths, tokens, tile_rows: int):
 
 
 # Rank time model: us = a * blocks * kv_heads / CUs + b * items * kv_heads / CUs + c * steps + d.
-# Fitted (least squares, fit_cost.py) to the 16 rank shares of the 131072-token pack at cp = 8
-# under both rules on one MI355X (256 CUs, 32 q / 8 kv heads, d = 128): within 9% of every one.
-TIME_MODEL_US = dict(per_block=2.128, per_item=16.883, per_step=1.886, fixed=132.0)
+# Fitted (least squares, fit_cost.py) to the 32 rank shares of the 131072-token pack at cp = 8
+# under zigzag, per-document and dispatch over 32 and 64 chunks, measured on one MI355X (256
+# CUs, 32 q / 8 kv heads, d = 128, the steps' attention launches on 4 streams): within 8% of
+# every one.  a matches the kernel's per-block time (1.85 us per 64-key block per workgroup).
+TIME_MODEL_US = dict(per_block=1.808, per_item=15.526, per_step=32.888, fixed=132.966)
 
 
 def predicted_rank_us(work, kv_heads: int, n_cu: int = 256, model=TIME_MODEL_US):
@@ -162,18 +229,30 @@ def predicted_rank_us(work, kv_heads: int, n_cu: int = 256, model=TIME_MODEL_US)
             model["per_step"] * s + model["fixed"] for (b, i, s) in work]
 
 
+def parse_rule(name: str):
+    """"dispatch/64" -> ("dispatch", 64); other names -> (name, 0)."""
+    rule, _, n = name.partition("/")
+    return rule, int(n) if n else 0
+
+
 def choose_sharding(lengths, cp: int, tile_rows: int, kv_heads: int = 8, n_cu: int = 256,
                     rules=("zigzag", "per_document")):
     """The rule whose busiest rank has the smallest predicted time, with, per rule, the
     per-rank predicted microseconds and work: {rule: {"us": [...], "work": [(blocks, items,
-    steps), ...]}}."""
+    steps), ...]}}.  A rule is "zigzag", "per_document", or "dispatch/<chunks>"; rules that
+    do not apply (zigzag and dispatch need the pack to divide evenly) or whose runs the
+    planner would refuse (more than MAX_SPANS key runs per query run) are left out."""
     cost = {}
-    for rule in rules:
+    for name in rules:
+        rule, n = parse_rule(name)
         try:
-            work = rank_work(lengths, shard_tokens(rule, lengths, cp), tile_rows)
-        except ValueError:  # the rule does not apply (zigzag needs a multiple of 2*cp tokens)
+            tokens = shard_tokens(rule, lengths, cp, n_chunks=n)
+        except ValueError:
             continue
-        cost[rule] = {"us": predicted_rank_us(work, kv_heads, n_cu), "work": work}
+        if max_spans(lengths, tokens) > MAX_SPANS:
+            continue
+        work = rank_work(lengths, tokens, tile_rows)
+        cost[name] = {"us": predicted_rank_us(work, kv_heads, n_cu), "work": work}
     best = min(cost, key=lambda r: max(cost[r]["us"]))
     return best, cost
 

@@ -13,6 +13,11 @@ Which query tokens each of cp ranks holds:
 * Striped ("03 · 长文负载均衡", section 4.2, Striped Attention; "长序列训练与上下文并行",
   the zigzag / striped remedy): the pack is dealt out in stripes, stripe s to
   rank s mod cp.
+* Mask-area dispatch ("03 · 长文负载均衡", section 4.4, MagiAttention's dispatch
+  solver): the pack is cut along the query axis into n equal chunks, each chunk's
+  mask area (the (query, key) pairs its queries see) is computed, and the chunks go
+  into cp buckets of exactly n/cp chunks each, largest area first, each into the
+  bucket that currently holds the least area and is not yet full.
 
 Readings where the pages leave a step open:
 * per-document chunk length is floor(len / (2*cp)); the remainder is the last
@@ -22,7 +27,10 @@ Readings where the pages leave a step open:
 * the striped rule takes a stripe width (the pages' Striped Attention deals
   single tokens: width 1);
 * inside a rank the tokens are kept in ascending global order (the layout of a
-  shard does not change its result).
+  shard does not change its result);
+* dispatch ties: chunks of equal area go in chunk order, and of equally loaded
+  buckets the lowest-numbered one is taken; the mask is the per-document causal
+  one, so a chunk's area is the sum over its tokens of (position in document + 1).
 
 A rank's attention over the whole ring: at step t it attends its query tokens
 to the key/value tokens of rank (r - t) mod cp ("长序列训练与上下文并行", Ring
@@ -66,6 +74,38 @@ def striped_tokens(total: int, cp: int, width: int = 1):
     t = np.arange(total)
     stripe = t // width
     return [t[stripe % cp == r] for r in range(cp)]
+
+
+def chunk_areas(lengths, n_chunks: int):
+    """Mask area of each of n equal query chunks of the pack under the per-document causal
+    mask: a token at position p of its document sees p + 1 keys."""
+    total = int(sum(int(n) for n in lengths))
+    assert total % n_chunks == 0
+    size = total // n_chunks
+    pos_in_doc = [p for n in lengths for p in range(int(n))]
+    return [sum(pos_in_doc[t] + 1 for t in range(c * size, (c + 1) * size)) for c in range(n_chunks)]
+
+
+def dispatch_chunks(areas, cp: int):
+    """The greedy dispatch: per bucket (rank), the ascending list of chunk ids it gets."""
+    n = len(areas)
+    assert n % cp == 0
+    capacity = n // cp
+    load, held = [0] * cp, [[] for _ in range(cp)]
+    for c in sorted(range(n), key=lambda c: (-areas[c], c)):
+        open_buckets = [b for b in range(cp) if len(held[b]) < capacity]
+        b = min(open_buckets, key=lambda b: (load[b], b))
+        held[b].append(c)
+        load[b] += areas[c]
+    return [sorted(h) for h in held]
+
+
+def dispatch_tokens(lengths, cp: int, n_chunks: int):
+    """Per rank, the global token indices of the chunks the dispatch gives it."""
+    total = int(sum(int(n) for n in lengths))
+    size = total // n_chunks
+    held = dispatch_chunks(chunk_areas(lengths, n_chunks), cp)
+    return [np.concatenate([np.arange(c * size, (c + 1) * size) for c in h]).astype(np.int64) for h in held]
 
 
 def rank_pairs(lengths, tokens):

@@ -386,21 +386,23 @@ def test_zigzag_reassembly_small():
         check(out.cpu().numpy(), lse.cpu().numpy(), full_o[rows], full_l[:, rows], f"reassembly rank {rank}")
 
 
-@pytest.mark.parametrize("rule", ["per_document", "zigzag"])
+@pytest.mark.parametrize("rule", ["per_document", "zigzag", "dispatch"])
 def test_sharded_ranks_reassemble_the_unsharded_result(rule):
-    """Every rank of a cp = 4 sharding (per document: "03 · 长文负载均衡", section 4.3; or
-    sequence zigzag) runs its 4 ring steps through block_attn_fwd + lse_merge; the ranks'
-    rows together equal the unsharded oracle.  The plan-once path is bit-identical to the
-    per-step calls."""
+    """Every rank of a cp = 4 sharding (per document: "03 · 长文负载均衡", section 4.3;
+    sequence zigzag; or the mask-area dispatch of section 4.4 over 16 chunks) runs its 4
+    ring steps through block_attn_fwd + lse_merge; the ranks' rows together equal the
+    unsharded oracle.  The plan-once path is bit-identical to the per-step calls."""
     from load_balance_amd import sharding as LS
     cp, H, Hkv, d = 4, 8, 2, 128
     r = np.random.default_rng(17)
     lengths = [1200, 37, 1, 650, 9, 301, 1900]  # remainders of every size
-    if rule == "zigzag":
+    if rule in ("zigzag", "dispatch"):
         lengths.append(2 * cp * 640 - sum(lengths))
     T = sum(lengths)
     q, k, v = workloads.values(r, T, H, Hkv, d)
-    tok = LS.shard_tokens(rule, lengths, cp)
+    tok = LS.shard_tokens(rule, lengths, cp, n_chunks=4 * cp)
+    if rule == "dispatch":
+        assert LS.max_spans(lengths, tok) <= LS.MAX_SPANS
     shards = LS.build_shards(lengths, tok, lambda idx: (q[idx], k[idx], v[idx]))
     full_o, full_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv)
     for rank in range(cp):

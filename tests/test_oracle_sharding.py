@@ -116,3 +116,88 @@ def test_sharded_ring_reassembles_the_unsharded_result(rule):
         o, l = S.sharded_rank_attention(q, k, v, lengths, tok, rank, H, Hkv)
         assert np.max(np.abs(o - full_o[tok[rank]])) < 1e-12
         assert np.max(np.abs(l - full_l[:, tok[rank]])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# mask-area dispatch ("03 · 长文负载均衡", section 4.4, MagiAttention)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cp", [2, 4, 8])
+def test_dispatch_of_one_causal_document_is_zigzag(cp):
+    """Section 4.4 places zigzag inside the dispatch solver's solution space as a hand-built
+    symmetric point.  For one causal document cut into 2cp chunks of c tokens, chunk i has
+    area c^2 i + c(c+1)/2 (strictly increasing), and the greedy puts chunks 2cp-1 .. cp on
+    ranks 0 .. cp-1 and then chunk j < cp on rank j: exactly rank i <- {i, 2cp-1-i}."""
+    c = 7
+    areas = S.chunk_areas([2 * cp * c], 2 * cp)
+    assert areas == [c * c * i + c * (c + 1) // 2 for i in range(2 * cp)]
+    assert S.dispatch_chunks(areas, cp) == [[i, 2 * cp - 1 - i] for i in range(cp)]
+    for a, b in zip(S.dispatch_tokens([2 * cp * c], cp, 2 * cp), S.zigzag_tokens(2 * cp * c, cp)):
+        assert np.array_equal(a, b)
+
+
+def test_dispatch_worked_example():
+    # areas 5 5 3 3 1 1 into 3 buckets of 2: 0 -> b0, 1 -> b1, 2 -> b2 (loads 5 5 3);
+    # 3 -> b2 (least, now full at 6); 4 -> b0 (tie 5 = 5, lower bucket); 5 -> b1
+    assert S.dispatch_chunks([5, 5, 3, 3, 1, 1], 3) == [[0, 4], [1, 5], [2, 3]]
+    # a chunk never goes to a full bucket even when that bucket is the least loaded
+    assert S.dispatch_chunks([9, 1, 1, 1], 2) == [[0, 3], [1, 2]]
+
+
+def test_chunk_areas_sum_to_the_pack_pairs():
+    r = np.random.default_rng(3)
+    lengths = random_lengths(r, 11, 90)
+    lengths.append(16 * 40 - sum(lengths) % (16 * 40))  # pad to a multiple of 16 chunks
+    areas = S.chunk_areas(lengths, 16)
+    assert sum(areas) == sum(n * (n + 1) // 2 for n in lengths)
+    tok = S.dispatch_tokens(lengths, 4, 16)
+    assert is_partition(tok, sum(lengths))
+    assert len({len(t) for t in tok}) == 1  # equal token counts: n / cp chunks each
+    assert S.rank_pairs(lengths, tok) == [sum(areas[c] for c in h) for h in S.dispatch_chunks(areas, 4)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dispatch_against_brute_force(seed):
+    """Tiny cases against every assignment of 8 chunks to cp buckets of equal size: the
+    greedy's assignment is feasible, and its busiest bucket is at or above the optimum and,
+    on these cases, within one chunk's area of it."""
+    import itertools
+    r = np.random.default_rng(seed)
+    areas = [int(x) for x in r.integers(1, 50, 8)]
+    for cp in (2, 4):
+        cap = 8 // cp
+        best = None
+        for labels in itertools.product(range(cp), repeat=8):
+            if any(labels.count(b) != cap for b in range(cp)):
+                continue
+            mx = max(sum(a for a, l in zip(areas, labels) if l == b) for b in range(cp))
+            best = mx if best is None else min(best, mx)
+        held = S.dispatch_chunks(areas, cp)
+        assert sorted(c for h in held for c in h) == list(range(8)) and all(len(h) == cap for h in held)
+        got = max(sum(areas[c] for c in h) for h in held)
+        assert best <= got <= best + max(areas)
+
+
+def test_dispatch_balances_the_packed_pack():
+    """On the 131072-token pack of seed 0 at cp = 8, where sequence zigzag leaves the busiest
+    rank 1.633x the mean (section 1.2), the dispatch of 64 chunks of 2048 tokens brings it
+    within 1% while every rank keeps 16384 tokens."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    tok = S.dispatch_tokens(lengths, 8, 64)
+    pairs = S.rank_pairs(lengths, tok)
+    assert max(pairs) / np.mean(pairs) < 1.01
+    assert all(len(t) == 16384 for t in tok)
+
+
+@pytest.mark.parametrize("cp", [2, 4])
+def test_dispatch_ring_reassembles_the_unsharded_result(cp):
+    H, Hkv, d = 4, 2, 32
+    r = np.random.default_rng(8)
+    lengths = [37, 5, 90, 1, 59, 48]  # 240 tokens: 8 or 16 chunks
+    T = sum(lengths)
+    q, k, v = (r.standard_normal((T, h, d)) for h in (H, Hkv, Hkv))
+    tok = S.dispatch_tokens(lengths, cp, 4 * cp)
+    full_o, full_l = A.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv)
+    for rank in range(cp):
+        o, l = S.sharded_rank_attention(q, k, v, lengths, tok, rank, H, Hkv)
+        assert np.max(np.abs(o - full_o[tok[rank]])) < 1e-12
+        assert np.max(np.abs(l - full_l[:, tok[rank]])) < 1e-12

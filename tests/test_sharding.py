@@ -25,6 +25,18 @@ def test_rules_equal_oracle(cp, seed):
     if T2:
         for a, b in zip(LS.zigzag_tokens(T2, cp), OS.zigzag_tokens(T2, cp)):
             assert np.array_equal(a, b)
+    n = 4 * cp
+    padded = lengths + [n * 50 - T % (n * 50)]
+    assert LS.chunk_areas(padded, n).tolist() == OS.chunk_areas(padded, n)
+    for a, b in zip(LS.dispatch_tokens(padded, cp, n), OS.dispatch_tokens(padded, cp, n)):
+        assert np.array_equal(a, b)
+
+
+def test_dispatch_ties_equal_oracle():
+    # many equal areas: the heap's order must match the oracle's tie rules
+    for cp in (2, 3, 4):
+        areas = [4, 4, 4, 2, 2, 2, 4, 1, 1, 4, 2, 1]
+        assert LS.dispatch_chunks(areas, cp) == OS.dispatch_chunks(areas, cp)
 
 
 def test_zigzag_rejects_an_uneven_pack():
@@ -37,7 +49,7 @@ def oracle_work(pos, doc, qi, ki, bm):
     return sum(t["blocks"] for t in tl), len(tl)
 
 
-@pytest.mark.parametrize("rule", ["zigzag", "per_document", "striped"])
+@pytest.mark.parametrize("rule", ["zigzag", "per_document", "striped", "dispatch"])
 @pytest.mark.parametrize("bm", [32, 64])
 def test_predicted_work_equals_oracle_enumerator(rule, bm):
     """Key blocks and work items (tiles with any block) of every rank and ring step equal the
@@ -45,8 +57,8 @@ def test_predicted_work_equals_oracle_enumerator(rule, bm):
     r = np.random.default_rng(bm)
     cp = 4
     lengths = [int(x) for x in r.integers(1, 700, 9)]
-    if rule == "zigzag":
-        lengths.append(2 * cp * 600 - sum(lengths))
+    if rule in ("zigzag", "dispatch"):
+        lengths.append(4 * cp * 300 - sum(lengths))
     tok = LS.shard_tokens(rule, lengths, cp, width=37)
     pos, doc = A.pack_positions(lengths)
     for rank in range(cp):
@@ -81,3 +93,28 @@ def test_choose_sharding_prefers_per_document_for_few_long_documents():
     best, cost = LS.choose_sharding(lengths, 8, 64)
     assert best == "per_document"
     assert max(cost["per_document"]["us"]) < 0.9 * max(cost["zigzag"]["us"])
+
+
+def test_choose_sharding_with_the_dispatch_solver():
+    """"03 · 长文负载均衡", section 4.4: the mask-area dispatch over equal chunks evens the
+    area while every rank keeps the same token count and few runs.  On the 131072-token pack
+    of seed 0 at cp = 8 the measured busiest-rank times were dispatch/32 1.35 ms,
+    dispatch/64 1.48, zigzag 1.69, per-document 2.99; the fitted model ranks them the same
+    way and picks dispatch over 32 chunks."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    rules = ("zigzag", "per_document", "dispatch/32", "dispatch/64")
+    best, cost = LS.choose_sharding(lengths, 8, 64, rules=rules)
+    assert best == "dispatch/32"
+    busiest = {r: max(c["us"]) for r, c in cost.items()}
+    assert sorted(busiest, key=busiest.get) == ["dispatch/32", "dispatch/64", "zigzag", "per_document"]
+    for r, ms in {"dispatch/32": 1.35, "dispatch/64": 1.48, "zigzag": 1.69, "per_document": 2.99}.items():
+        assert abs(busiest[r] / 1e3 - ms) / ms < 0.08, r
+
+
+def test_spans_limit_filters_rules():
+    # stripes one token wide split every document into single-token runs: each query run
+    # meets many key runs of its document on every step, which the planner refuses
+    lengths = [4096, 4096]
+    assert LS.max_spans(lengths, LS.striped_tokens(8192, 4, 1)) > LS.MAX_SPANS
+    tok = LS.shard_tokens("dispatch", lengths, 4, n_chunks=16)
+    assert LS.max_spans(lengths, tok) <= LS.MAX_SPANS
