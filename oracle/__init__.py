@@ -15,11 +15,14 @@ Modules
                pairs hold visible pairs, their exact pair counts, the key
                blocks each sweeps, and the longest-first order.
 ``sharding``   which tokens each context-parallel rank holds (sequence zigzag,
-               per-document, striped) and one rank's sharded ring fold.
+               per-document, striped, mask-area dispatch) and one rank's sharded
+               ring fold.
+``backward``   the gradients dq, dk, dv of the varlen forward and of one ring
+               step (from the whole-row lse and D = <dout, out>).
 
 Pins (what each function is checked against, in ``tests/test_oracle_*.py``):
 every function here is pinned by closed forms, special cases, a library
 routine (torch ``scaled_dot_product_attention`` in float64) or brute force on
 tiny inputs; none is marked "parity unpinned".
 """
-from . import attention, plan, sharding  # noqa: F401
+from . import attention, backward, plan, sharding  # noqa: F401
