@@ -226,6 +226,73 @@ lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, 
 lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const float* lse_b,
                        int32_t n_rows, int32_t heads, int32_t d, hipStream_t stream);
 
+/*
+ * ---- Backward -------------------------------------------------------------------
+ * Gradients of the forwards above from their saved lse ("03 · 长文负载均衡", section 4.4:
+ * MagiAttention reduces each block's partial key/value gradients back to the rank that
+ * owns the keys; section 5: key/value gradients kept with their states).  With
+ * P = exp(scale <q_i, k_j> - lse_i) on visible pairs and D_i = <dout_i, out_i>:
+ *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (<dout_i, v_j> - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ * key/value gradients summed over the query heads of their kv group.  Rows whose lse
+ * is -inf get no gradient.  The same masks and head mapping as the forward.
+ */
+
+/* Bytes of workspace lb_varlen_attn_bwd needs for packs up to max_tokens tokens and
+   max_segments segments: two plans (query tiles for dq, key tiles for dk/dv) and the
+   row values D ([heads][tokens] fp32).  0 when the head counts are unsupported. */
+size_t lb_bwd_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads);
+
+/* Byte offset, inside a backward workspace, of its key-tile plan (the query-tile plan sits
+   at offset 0), for lb_read_plan and lb_read_device_error on either half.  block_path = 0:
+   lb_varlen_attn_bwd with total_tokens = n_q and n_seg segments; 1: lb_block_attn_bwd with
+   this workspace size.  0 when the arguments are invalid. */
+size_t lb_bwd_key_plan_offset(int32_t block_path, int32_t n_q, int32_t n_kv, int32_t n_seg, int32_t heads,
+                              int32_t kv_heads, size_t workspace_bytes);
+
+/*
+ * D[h][i] = sum_d out[i][h][d] * dout[i][h][d] (fp32), the row values of the backward.
+ *   out   bf16 [n_rows][heads][d] (out_f32 = 0) or fp32 (out_f32 = 1: a ring rank's merged
+ *         block output);  dout bf16 [n_rows][heads][d];  dvec fp32 [heads][n_rows] (written).
+ */
+lb_status lb_attn_bwd_rowdot(const void* out, int32_t out_f32, const void* dout, int32_t n_rows, int32_t heads,
+                             int32_t d, float* dvec, hipStream_t stream);
+
+/*
+ * Backward of lb_varlen_attn_fwd (same cu_seqlens, masks and shapes).
+ *   q, k, v   the forward's inputs;  out, lse  its outputs (bf16 [T][heads][d], fp32 [heads][T]);
+ *   dout      bf16 [T][heads][d];
+ *   dq        bf16 [T][heads][d] (written);  dk, dv  bf16 [T][kv_heads][d] (written).
+ * Launches one planning kernel (both plans), the D pass, the dq kernel and the dk/dv
+ * kernel on `stream`.  workspace: lb_bwd_workspace_bytes(total_tokens, n_seg, ...) bytes,
+ * 256-byte aligned, caller-owned; a plan error sets the device error word of its half
+ * (read with lb_read_device_error on the workspace: the query-tile plan sits at its start).
+ */
+lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                             int32_t heads, int32_t kv_heads, int32_t d, int32_t mask_kind, void* dq, void* dk,
+                             void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One ring step of the backward of lb_block_attn_fwd: the query shard's dq contribution
+ * and the key/value chunk's partial dk, dv (to be summed over the ranks that attended to
+ * the chunk, at the rank that owns it).
+ *   q_shard   bf16 [n_q][heads][d];  kv_chunk  bf16 [2][n_kv][kv_heads][d] (K then V);
+ *   dout      bf16 [n_q][heads][d];
+ *   lse, dvec fp32 [heads][n_q]: the whole row's lse after every step's merge, and
+ *             D = <dout, out> of the merged out (lb_attn_bwd_rowdot with out_f32 = 1);
+ *   q_pos, kv_pos, q_doc, kv_doc: as lb_block_attn_fwd;
+ *   dq        fp32 [n_q][heads][d]: this step's contribution is ADDED (zero it before the
+ *             first step; rows with no visible key in this step are left as they are);
+ *   dkv       fp32 [2][n_kv][kv_heads][d]: this step's dk then dv, WRITTEN (every key).
+ * workspace: split in two halves (query-tile and key-tile plans), each sized like an
+ * lb_plan_block workspace; LB_EWORKSPACE when a half holds less than one run.
+ */
+lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv, const void* dout,
+                            const float* lse, const float* dvec, const int32_t* q_pos, const int32_t* kv_pos,
+                            const int32_t* q_doc, const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
+                            float* dq, float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* lb_status_string(lb_status s);
 

@@ -6,7 +6,8 @@ kernels.  torch supplies device memory and the current stream.  There is no
 CPU fallback: if the library is missing, every call raises.
 
 Python names match the C entry points without their ``lb_`` prefix:
-``varlen_attn_fwd``, ``block_attn_fwd``, ``lse_merge``.
+``varlen_attn_fwd``, ``block_attn_fwd``, ``lse_merge``, and the backward
+``varlen_attn_bwd``, ``block_attn_bwd``, ``attn_bwd_rowdot``.
 """
 from __future__ import annotations
 
@@ -79,6 +80,16 @@ def lib() -> ctypes.CDLL:
     L.lb_attn_run.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.lb_lse_merge.restype = ctypes.c_int
+    L.lb_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    L.lb_bwd_workspace_bytes.restype = SZ
+    L.lb_bwd_key_plan_offset.argtypes = [I32, I32, I32, I32, I32, I32, SZ]
+    L.lb_bwd_key_plan_offset.restype = SZ
+    L.lb_attn_bwd_rowdot.argtypes = [P, I32, P, I32, I32, I32, P, P]
+    L.lb_attn_bwd_rowdot.restype = ctypes.c_int
+    L.lb_varlen_attn_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    L.lb_varlen_attn_bwd.restype = ctypes.c_int
+    L.lb_block_attn_bwd.argtypes = [P, I32, P, I32, P, P, P, P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_block_attn_bwd.restype = ctypes.c_int
     L.lb_status_string.argtypes = [ctypes.c_int]
     L.lb_status_string.restype = ctypes.c_char_p
     L.lb_read_device_error.argtypes = [P, SZ, ctypes.POINTER(I32), P]
@@ -276,3 +287,78 @@ def read_worker_timing(workspace, max_records: int = 4096, stream=None):
                                        ctypes.c_void_p(_stream(stream))), "lb_read_worker_timing")
     return [dict(hw_id=r.hw_id, xcc_id=r.xcc_id, t_start=r.t_start, t_end=r.t_end, pairs=r.pairs,
                  items=r.items) for r in buf[:min(n.value, max_records)]]
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def bwd_workspace_bytes(max_tokens: int, max_segments: int, heads: int, kv_heads: int) -> int:
+    n = int(lib().lb_bwd_workspace_bytes(max_tokens, max_segments, heads, kv_heads))
+    if n == 0:
+        raise LBError("lb_bwd_workspace_bytes: invalid or unsupported arguments")
+    return n
+
+
+def bwd_key_plan_offset(block_path: bool, n_q: int, n_kv: int, n_seg: int, heads: int, kv_heads: int,
+                        workspace_bytes: int) -> int:
+    """Where the key-tile plan of a backward workspace starts (the query-tile plan is at 0)."""
+    return int(lib().lb_bwd_key_plan_offset(int(block_path), n_q, n_kv, n_seg, heads, kv_heads, workspace_bytes))
+
+
+def attn_bwd_rowdot(out, dout, dvec=None, stream=None):
+    """D [H,R] fp32 = sum over d of out * dout; out bf16 or fp32 [R,H,d], dout bf16 [R,H,d]."""
+    R, H, d = dout.shape
+    if dvec is None:
+        dvec = torch.empty((H, R), dtype=torch.float32, device=dout.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or dout.dtype != torch.bfloat16:
+        raise LBError("out must be bfloat16 or float32 and dout bfloat16")
+    _check(lib().lb_attn_bwd_rowdot(_ptr(out), int(out.dtype == torch.float32), _ptr(dout), R, H, d, _ptr(dvec),
+                                    ctypes.c_void_p(_stream(stream))), "lb_attn_bwd_rowdot")
+    return dvec
+
+
+def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, dq=None, dk=None, dv=None,
+                    workspace=None, stream=None):
+    """dq [T,H,d], dk, dv [T,H_kv,d] (bf16) of varlen_attn_fwd from its out and lse."""
+    T, H, d = q.shape
+    Hkv = k.shape[1]
+    n_seg = cu_seqlens.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(T, max(1, n_seg), H, Hkv), dtype=torch.uint8, device=q.device)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+    if cu_seqlens.dtype != torch.int32 or lse.dtype != torch.float32:
+        raise LBError("cu_seqlens must be int32 and lse float32")
+    _check(lib().lb_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
+                                    n_seg, T, H, Hkv, d, int(mask_kind), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_varlen_attn_bwd")
+    return dq, dk, dv
+
+
+def block_attn_bwd(q_shard, kv_chunk, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, dq, dkv=None, workspace=None,
+                   stream=None):
+    """One ring step of the backward: adds this step's contribution to dq (fp32 [n_q,H,d]) and
+    returns dkv (fp32 [2,n_kv,H_kv,d]: this step's dk, dv) together with dq."""
+    n_q, H, d = q_shard.shape
+    _, n_kv, Hkv, _ = kv_chunk.shape
+    if dkv is None:
+        dkv = torch.empty((2, n_kv, Hkv, d), dtype=torch.float32, device=q_shard.device)
+    if workspace is None:
+        half = workspace_bytes(max(n_q, n_kv), max(n_q, n_kv, 1), H, Hkv)
+        workspace = torch.empty(2 * half + 512, dtype=torch.uint8, device=q_shard.device)
+    for t, name in ((q_shard, "q_shard"), (kv_chunk, "kv_chunk"), (dout, "dout")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+    for t, name in ((dq, "dq"), (dkv, "dkv"), (lse, "lse"), (dvec, "dvec")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous float32 tensor")
+    _check(lib().lb_block_attn_bwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(dout), _ptr(lse), _ptr(dvec),
+                                   _ptr(q_pos), _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, _ptr(dq),
+                                   _ptr(dkv), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_block_attn_bwd")
+    return dq, dkv

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblbattn.so")
-SOURCES = ["plan.hip", "attn_fwd.hip", "lse_merge.hip", "api.cpp"]
+SOURCES = ["plan.hip", "attn_fwd.hip", "lse_merge.hip", "bwd.hip", "api.cpp"]
 ARCH = os.environ.get("LB_OFFLOAD_ARCH", "gfx950")
 
 

@@ -173,6 +173,62 @@ lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t 
   return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
+// ---- backward: two plans (query tiles for dQ, key tiles for dK/dV) in one workspace ----
+struct BwdLayout {
+  WsLayout q, k;        // each relative to its own region
+  int64_t off_k;        // start of the key-tile plan's region
+  int64_t off_dvec;     // D = <dout, out>, [heads][tokens] fp32 (varlen only)
+  int64_t total;
+};
+
+BwdLayout bwd_layout_varlen(int64_t tokens, int64_t segments, int32_t heads, int32_t kv_heads) {
+  const int G = heads / kv_heads;
+  BwdLayout B{};
+  B.q = ws_layout(segments, std::min<int64_t>(kSortCap + 1, ceil_div(tokens, bwd_q_rows(G)) + segments));
+  B.k = ws_layout(segments, std::min<int64_t>(kSortCap + 1, ceil_div(tokens, bwd_k_rows(G)) + segments));
+  B.off_k = B.q.total;
+  B.off_dvec = B.off_k + B.k.total;
+  B.total = align256(B.off_dvec + (int64_t)heads * tokens * 4);
+  return B;
+}
+
+// Block path: the workspace is split in two halves, each holding as many runs as fit.
+lb_status bwd_layout_block(int32_t n_q, int32_t n_kv, int32_t heads, int32_t kv_heads, size_t bytes,
+                           BwdLayout* B) {
+  const int G = heads / kv_heads;
+  const int64_t half = ((int64_t)bytes / 2) & ~int64_t(255);
+  const int64_t max_runs = std::max<int64_t>(1, std::max(n_q, n_kv));
+  auto fit = [&](int64_t side_tokens, int bm, WsLayout* L) {
+    auto layout_for = [&](int64_t f) { return ws_layout(f, std::min<int64_t>(kSortCap, ceil_div(side_tokens, bm) + f)); };
+    if (layout_for(1).total > half) return false;
+    int64_t lo = 1, hi = max_runs;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (layout_for(mid).total <= half) lo = mid; else hi = mid - 1;
+    }
+    *L = layout_for(lo);
+    return true;
+  };
+  if (!fit(n_q, bwd_q_rows(G), &B->q) || !fit(n_kv, bwd_k_rows(G), &B->k)) return LB_EWORKSPACE;
+  B->off_k = half;
+  B->off_dvec = 2 * half;
+  B->total = 2 * half;
+  return LB_OK;
+}
+
+BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout, const float* lse, const float* dvec,
+                 void* dq, void* dk, void* dv, int32_t n_q, int32_t n_kv, int32_t heads, int32_t kv_heads,
+                 int32_t d) {
+  BwdArgs b{};
+  b.q = q; b.k = k; b.v = v; b.dout = dout; b.lse = lse; b.dvec = dvec;
+  b.dq = dq; b.dk = dk; b.dv = dv;
+  b.n_q = n_q; b.n_kv = n_kv;
+  b.heads = heads; b.kv_heads = kv_heads; b.group = heads / kv_heads;
+  b.scale = (float)(1.0 / std::sqrt((double)d));
+  b.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  return b;
+}
+
 bool read_header(const void* ws, size_t bytes, WsHeader* h, hipStream_t s) {
   if (!ws || bytes < sizeof(WsHeader)) return false;
   if (hipStreamSynchronize(s) != hipSuccess) return false;
@@ -295,6 +351,122 @@ lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const flo
   if (n_rows == 0) return LB_OK;
   MergeArgs m{out_a, lse_a, out_b, lse_b, n_rows, heads, d};
   return launch_lse_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+size_t lb_bwd_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads) {
+  if (max_tokens < 0 || max_segments < 1 || !group_supported(heads, kv_heads)) return 0;
+  return (size_t)bwd_layout_varlen(max_tokens, max_segments, heads, kv_heads).total;
+}
+
+size_t lb_bwd_key_plan_offset(int32_t block_path, int32_t n_q, int32_t n_kv, int32_t n_seg, int32_t heads,
+                              int32_t kv_heads, size_t workspace_bytes) {
+  if (!group_supported(heads, kv_heads) || n_q < 0 || n_kv < 0) return 0;
+  if (block_path) {
+    BwdLayout B;
+    return bwd_layout_block(n_q, n_kv, heads, kv_heads, workspace_bytes, &B) == LB_OK ? (size_t)B.off_k : 0;
+  }
+  if (n_seg < 1) return 0;
+  return (size_t)bwd_layout_varlen(n_q, n_seg, heads, kv_heads).off_k;
+}
+
+lb_status lb_attn_bwd_rowdot(const void* out, int32_t out_f32, const void* dout, int32_t n_rows, int32_t heads,
+                             int32_t d, float* dvec, hipStream_t stream) {
+  if (!out || !dout || !dvec || n_rows < 0 || heads <= 0) return LB_EINVAL;
+  if (d != 64 && d != 128) return LB_EUNSUPPORTED;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dvec, 4)) return LB_EINVAL;
+  if (n_rows == 0) return LB_OK;
+  return launch_bwd_rowdot(out, out_f32 != 0, dout, n_rows, heads, d, dvec, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                             int32_t heads, int32_t kv_heads, int32_t d, int32_t mask_kind, void* dq, void* dk,
+                             void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !cu_seqlens || !dq || !dk || !dv || !workspace) return LB_EINVAL;
+  if (n_seg < 1 || total_tokens < 0) return LB_EINVAL;
+  if (mask_kind != LB_MASK_CAUSAL_DOC && mask_kind != LB_MASK_SHARED_QUESTION) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(p, 16)) return LB_EINVAL;
+  if (!aligned(lse, 4) || !aligned(cu_seqlens, 4)) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const BwdLayout B = bwd_layout_varlen(total_tokens, n_seg, heads, kv_heads);
+  if (B.q.cap_tiles > kSortCap || B.k.cap_tiles > kSortCap) return LB_EUNSUPPORTED;
+  if ((int64_t)workspace_bytes < B.total) return LB_EWORKSPACE;
+  if (total_tokens == 0) return LB_OK;
+  char* ws = static_cast<char*>(workspace);
+  float* dvec = reinterpret_cast<float*>(ws + B.off_dvec);
+  PlanBatch pb{};
+  for (int side = 0; side < 2; ++side) {
+    PlanArgs& p = pb.step[side];
+    p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
+    p.transposed = side;
+    p.cu_seqlens = cu_seqlens;
+    p.n_seg = n_seg;
+    p.total_tokens = total_tokens;
+    p.tile_rows = side == 0 ? bwd_q_rows(heads / kv_heads) : bwd_k_rows(heads / kv_heads);
+    p.heads = heads;
+    p.kv_heads = kv_heads;
+    p.ws = ws + (side == 0 ? 0 : B.off_k);
+    p.L = side == 0 ? B.q : B.k;
+  }
+  if (launch_plan_steps(pb, 2, stream) != hipSuccess) return LB_EHIP;
+  if (launch_bwd_rowdot(out, false, dout, total_tokens, heads, d, dvec, stream) != hipSuccess) return LB_EHIP;
+  int workers = 0;
+  st = persistent_workers(&workers);
+  if (st != LB_OK) return st;
+  BwdArgs b = bwd_args(q, k, v, dout, lse, dvec, dq, dk, dv, total_tokens, total_tokens, heads, kv_heads, d);
+  b.ws = ws;
+  b.ws_bytes = B.q.total;
+  if (launch_bwd_dq(b, d, false, workers, stream) != hipSuccess) return LB_EHIP;
+  b.ws = ws + B.off_k;
+  b.ws_bytes = B.k.total;
+  return launch_bwd_dkv(b, d, false, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv, const void* dout,
+                            const float* lse, const float* dvec, const int32_t* q_pos, const int32_t* kv_pos,
+                            const int32_t* q_doc, const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
+                            float* dq, float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
+  if (!q_shard || !dout || !lse || !dvec || !q_pos || !q_doc || !dq || !workspace) return LB_EINVAL;
+  if (n_kv > 0 && (!kv_chunk || !kv_pos || !kv_doc || !dkv)) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(q_shard, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) || !aligned(dvec, 4))
+    return LB_EINVAL;
+  if (n_kv > 0 && (!aligned(kv_chunk, 16) || !aligned(dkv, 16))) return LB_EINVAL;
+  if (!aligned(q_pos, 4) || !aligned(q_doc, 4) || (n_kv > 0 && (!aligned(kv_pos, 4) || !aligned(kv_doc, 4))))
+    return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  BwdLayout B;
+  st = bwd_layout_block(n_q, n_kv, heads, kv_heads, workspace_bytes, &B);
+  if (st != LB_OK) return st;
+  if (n_q == 0 || n_kv == 0) return LB_OK;
+  char* ws = static_cast<char*>(workspace);
+  const __bf16* kbase = static_cast<const __bf16*>(kv_chunk);
+  const __bf16* vbase = kbase + (int64_t)n_kv * kv_heads * d;
+  PlanBatch pb{};
+  for (int side = 0; side < 2; ++side) {
+    pb.step[side] = block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads,
+                                    ws + (side == 0 ? 0 : B.off_k), side == 0 ? B.q : B.k);
+    pb.step[side].transposed = side;
+    pb.step[side].tile_rows = side == 0 ? bwd_q_rows(heads / kv_heads) : bwd_k_rows(heads / kv_heads);
+  }
+  if (launch_plan_steps(pb, 2, stream) != hipSuccess) return LB_EHIP;
+  int workers = 0;
+  st = persistent_workers(&workers);
+  if (st != LB_OK) return st;
+  float* dk = dkv;
+  float* dv = dkv + (int64_t)n_kv * kv_heads * d;
+  BwdArgs b = bwd_args(q_shard, kbase, vbase, dout, lse, dvec, dq, dk, dv, n_q, n_kv, heads, kv_heads, d);
+  b.ws = ws;
+  b.ws_bytes = B.off_k;
+  if (launch_bwd_dq(b, d, true, workers, stream) != hipSuccess) return LB_EHIP;
+  b.ws = ws + B.off_k;
+  b.ws_bytes = (int64_t)workspace_bytes - B.off_k;
+  return launch_bwd_dkv(b, d, true, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
 const char* lb_status_string(lb_status s) {

@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   // A missing plan, or one made for other shapes or another workspace size, could index
   // outside this launch's buffers: then run nothing and flag it.
   const int64_t n_tiles_hdr = hdr->n_tiles;
-  const bool mismatch = hdr->magic != kPlanMagic || hdr->plan_n_q != a.n_q || hdr->plan_n_kv != a.n_kv ||
+  const bool mismatch = hdr->magic != kPlanMagic || hdr->transposed != 0 || hdr->plan_n_q != a.n_q ||
+                        hdr->plan_n_kv != a.n_kv ||
                         hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
                         hdr->n_empty < 0 || hdr->n_empty > n_tiles_hdr ||
                         hdr->n_items != (n_tiles_hdr - hdr->n_empty) * a.kv_heads || n_tiles_hdr < 0 ||

@@ -1,0 +1,815 @@
+// Backward of the masked attention for gfx950 (MI355X): dQ, dK, dV from the
+// forward's saved log-sum-exp.
+//
+// The context-parallel systems of "03 · 长文负载均衡" train, so their attention
+// blocks carry gradients: section 4.4 (MagiAttention) reduces the partial key/value
+// gradients of every block back to the rank that owns the keys, and section 5 keeps
+// key/value gradients with their states.  The gradient itself is the plain one of
+// softmax attention, with P = exp(s - lse) rebuilt from the saved lse:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Two persistent kernels share the forward's queue machinery and plan format:
+//   * dQ, query-stationary, over query tiles (the forward's tiling): per 64-key
+//     block, S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and dO held in
+//     registers), then dQ^T += K^T dS^T with K^T from LDS.
+//   * dK/dV, key-stationary, over key tiles whose spans are the query rows that see
+//     them (the transposed plan): per block of 32 query rows and head,
+//     S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V held in
+//     registers), then dV^T += dO^T P and dK^T += Q^T dS.  The heads of a kv group
+//     add into the same accumulators, so no reduction over heads follows.
+// Each wave runs alone on its SIMD (4 waves per workgroup) and may hold 512
+// registers: both kernels keep two operand sets and two accumulators live.
+// Transposed operands (K^T, Q^T, dO^T) are written to LDS by the loader with the
+// index permutation that lets the other MFMA operand come straight from an
+// accumulator (the forward's V^T layout).
+#include "lbattn_internal.h"
+
+namespace lb {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = kBlockN;  // keys per block of the dQ kernel
+constexpr int kQB = 32;      // query rows per block of the dK/dV kernel
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ int vt_pos(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint32_t hw_id_reg() { return __builtin_amdgcn_s_getreg((31 << 11) | 4); }
+__device__ __forceinline__ uint32_t xcc_id_reg() { return __builtin_amdgcn_s_getreg((15 << 11) | 20); }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two bf16 values of one 16-byte chunk pair, interleaved for a transposed row: the
+// words for elements 2m and 2m + 1 of two consecutive source rows.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t x0, uint32_t x1) { return (x0 & 0xFFFFu) | (x1 << 16); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t x0, uint32_t x1) { return (x0 >> 16) | (x1 & 0xFFFF0000u); }
+
+// ------------------------------------------------------------------------------------
+// The plan and its queues (same format and protocol as the forward's)
+// ------------------------------------------------------------------------------------
+struct Queues {
+  WsHeader* hdr;
+  const lb_plan_tile* tiles;
+  const int32_t* order;
+  int n_items, n_queues, per_queue, heads_per_queue, queue;
+  int64_t n_tiles;
+  int n_empty;
+  bool dry;  // thread 0's view
+
+  __device__ void open(const BwdArgs& a, int transposed) {
+    hdr = reinterpret_cast<WsHeader*>(a.ws);
+    const int64_t nt = hdr->n_tiles;
+    const bool bad = hdr->magic != kPlanMagic || hdr->transposed != transposed || hdr->plan_n_q != a.n_q ||
+                     hdr->plan_n_kv != a.n_kv || hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
+                     hdr->n_empty < 0 || hdr->n_empty > nt || hdr->n_items != (nt - hdr->n_empty) * a.kv_heads ||
+                     nt < 0 || (hdr->n_queues != 1 && hdr->n_queues != kXcds) || a.kv_heads % hdr->n_queues != 0 ||
+                     (int64_t)hdr->per_queue * hdr->n_queues != hdr->n_items || hdr->off_tiles < kWorkersOffset ||
+                     hdr->off_order < kWorkersOffset ||
+                     hdr->off_tiles + nt * (int64_t)sizeof(lb_plan_tile) > a.ws_bytes ||
+                     hdr->off_order + nt * 4 > a.ws_bytes;
+    if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
+    n_items = bad ? 0 : hdr->n_items;
+    n_tiles = bad ? 0 : nt;
+    n_empty = bad ? 0 : hdr->n_empty;
+    tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + (bad ? 0 : hdr->off_tiles));
+    order = reinterpret_cast<const int32_t*>(a.ws + (bad ? 0 : hdr->off_order));
+    n_queues = bad ? 1 : hdr->n_queues;
+    per_queue = bad ? 0 : hdr->per_queue;
+    heads_per_queue = a.kv_heads / n_queues;
+    queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
+    dry = n_items == 0;
+  }
+
+  // Thread 0: the next item (global index), or -1 when every queue is empty.
+  __device__ int pop() {
+    while (!dry) {
+      const int k = atomicAdd(&hdr->queue_head[queue], 1);
+      if (k < per_queue) return queue * per_queue + k;
+      int next = -1;
+      for (int step = 1; step < n_queues; ++step) {
+        const int q = (queue + step) % n_queues;
+        if (__atomic_load_n(&hdr->queue_head[q], __ATOMIC_RELAXED) < per_queue) { next = q; break; }
+      }
+      if (next < 0) dry = true; else queue = next;
+    }
+    return -1;
+  }
+
+  // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
+  __device__ void decode(int item, const lb_plan_tile** T, int* g) const {
+    const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
+    *g = q_of + n_queues * (k_in % heads_per_queue);
+    *T = &tiles[order[k_in / heads_per_queue]];
+  }
+
+  // The last workgroup out rewinds the queues (every pop has happened before it counts itself).
+  __device__ void close(const BwdArgs& a, uint64_t t_start, int items, int64_t pairs) {
+    if (threadIdx.x != 0) return;
+    lb_worker_record rec;
+    rec.hw_id = hw_id_reg();
+    rec.xcc_id = xcc_id_reg();
+    rec.t_start = t_start;
+    rec.t_end = device_clock();
+    rec.pairs = pairs;
+    rec.items = items;
+    rec.reserved = 0;
+    reinterpret_cast<lb_worker_record*>(a.ws + kWorkersOffset)[blockIdx.x] = rec;
+    if (blockIdx.x == 0) hdr->n_workers = gridDim.x;
+    __threadfence();
+    if (atomicAdd(&hdr->done, 1) == (int)gridDim.x - 1) {
+      for (int q = 0; q < kXcds; ++q) atomicExch(&hdr->queue_head[q], 0);
+      atomicExch(&hdr->done, 0);
+    }
+  }
+};
+
+struct Span {
+  int start, len, pos0;
+};
+
+__device__ __forceinline__ Span span_of(const lb_plan_tile* T, int s) {
+  return Span{__builtin_amdgcn_readfirstlane(T->k_start[s]), __builtin_amdgcn_readfirstlane(T->k_len[s]),
+              __builtin_amdgcn_readfirstlane(T->k_pos0[s])};
+}
+
+// Writes one wave's 32 rows, staged row-major in LDS (`rows` rows valid, from lane-owned
+// rows), to a [row][heads][D] tensor: bf16, fp32, or fp32 added to what is there.
+template <int D, int MODE>  // MODE 0: bf16 store, 1: fp32 store, 2: fp32 accumulate
+__device__ __forceinline__ void store_rows(const char* stage, int stride, char* dst_row0, int64_t dst_row_step,
+                                           int rows, int lane) {
+  constexpr int kRowBytes = D * (MODE == 0 ? 2 : 4);
+  constexpr int kChunks = kRowBytes / 16;
+  constexpr int kRowsPerStep = 64 / kChunks;
+  const int r0 = lane / kChunks, ch = lane % kChunks;
+#pragma unroll
+  for (int j = 0; j < 32 / kRowsPerStep; ++j) {
+    const int r = r0 + j * kRowsPerStep;
+    if (r < rows) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * stride + ch * 16);
+      u32x4* dst = reinterpret_cast<u32x4*>(dst_row0 + r * dst_row_step + ch * 16);
+      if constexpr (MODE == 2) {
+        const f32x4 old = __builtin_bit_cast(f32x4, *dst);
+        *dst = __builtin_bit_cast(u32x4, old + __builtin_bit_cast(f32x4, x));
+      } else {
+        *dst = x;
+      }
+    }
+  }
+}
+
+// Stages a 32-column accumulator set (acc[db] holds X^T[d = db*32 + ...][col = lane % 32])
+// as 32 rows of D values, row-major: row = lane % 32, scaled by `mul`.
+template <int D, bool F32>
+__device__ __forceinline__ void stage_rows(char* stage, int stride, const f32x16* acc, float mul, int lane) {
+  const int l32 = lane & 31, hh = lane >> 5;
+  char* rowp = stage + l32 * stride;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d0 = db * 32 + r * 8 + hh * 4;
+      if constexpr (F32) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = acc[db][r * 4 + e] * mul;
+        *reinterpret_cast<f32x4*>(rowp + d0 * 4) = o;
+      } else {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[db][r * 4 + e] * mul);
+        *reinterpret_cast<bf16x4*>(rowp + d0 * 2) = o;
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// D = rowsum(dO * O)
+// ------------------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void rowdot_kernel(const void* out, const void* dout, int n_rows, int heads,
+                                                     float* dvec) {
+  constexpr int kLanes = D / 8;  // lanes per (row, head): 8 elements each
+  const int64_t rec = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kLanes;
+  const int part = threadIdx.x % kLanes;
+  const bool ok = rec < (int64_t)n_rows * heads;
+  float s = 0.f;
+  if (ok) {
+    const int64_t base = rec * D + part * 8;
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(dout) + base);
+    if constexpr (OUT_F32) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(out) + base);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(out) + base + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += o0[e] * (float)g[e] + o1[e] * (float)g[e + 4];
+    } else {
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(out) + base);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)o[e] * (float)g[e];
+    }
+  }
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (ok && part == 0) {
+    const int64_t row = rec / heads, h = rec % heads;
+    dvec[h * n_rows + row] = s;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// dQ: query-stationary
+// ------------------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  static constexpr int kStride = D * 2 + 16;  // K or V row
+  static constexpr int tStride = BN * 2 + 16; // K^T row (one d, the block's keys)
+  static constexpr int rowsBytes = BN * kStride;
+  static constexpr int tBytes = D * tStride;
+  static constexpr int stage = 2 * rowsBytes + tBytes;  // K rows, V rows, K^T
+  static constexpr int kUnits = (BN / 2) * (D / 8);     // (key pair, 16-byte chunk) units of K
+  static constexpr int kPerThread = kUnits / kBwdThreads;
+  static constexpr int vChunks = BN * (D / 8);
+  static constexpr int vPerThread = vChunks / kBwdThreads;
+  static constexpr int epiStride = D * 4 + 16;
+};
+
+template <int D>
+struct DqLoader {
+  using L = DqLds<D>;
+  u32x4 kr[L::kPerThread][2];
+  u32x4 vr[L::vPerThread];
+
+  __device__ __forceinline__ void load(const char* K, const char* V, int k0, int valid, int row_bytes, int g,
+                                       int tid) {
+    const int64_t base = (int64_t)k0 * row_bytes + (int64_t)g * D * 2;
+    const int nbytes = min(valid, BN) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, nbytes,
+                                                                        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, nbytes,
+                                                                        kBufferFlags);
+#pragma unroll
+    for (int e = 0; e < L::kPerThread; ++e) {
+      const int u = tid + e * kBwdThreads, p = u % (BN / 2), ch = u / (BN / 2);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        kr[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rk, (2 * p + x) * row_bytes + ch * 16, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < L::vPerThread; ++e) {
+      const int c = tid + e * kBwdThreads, row = c / (D / 8), ch = c % (D / 8);
+      vr[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * row_bytes + ch * 16, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store(char* stage, int tid) {
+    char* ks = stage;
+    char* vs = stage + L::rowsBytes;
+    char* kt = stage + 2 * L::rowsBytes;
+#pragma unroll
+    for (int e = 0; e < L::kPerThread; ++e) {
+      const int u = tid + e * kBwdThreads, p = u % (BN / 2), ch = u / (BN / 2);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(ks + (2 * p + x) * L::kStride + ch * 16) = kr[e][x];
+      const int col = vt_pos(2 * p) * 2;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        *reinterpret_cast<uint32_t*>(kt + (ch * 8 + 2 * m) * L::tStride + col) = pair_lo(kr[e][0][m], kr[e][1][m]);
+        *reinterpret_cast<uint32_t*>(kt + (ch * 8 + 2 * m + 1) * L::tStride + col) = pair_hi(kr[e][0][m], kr[e][1][m]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < L::vPerThread; ++e) {
+      const int c = tid + e * kBwdThreads, row = c / (D / 8), ch = c % (D / 8);
+      *reinterpret_cast<u32x4*>(vs + row * L::kStride + ch * 16) = vr[e];
+    }
+  }
+};
+
+template <int D, int HPW, bool OUT_F32>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  using L = DqLds<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
+  __shared__ int s_item;
+  static_assert(kBwdWaves * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int G = a.group;
+  const int HG = G / HPW, RG = kBwdWaves / HG;
+  const int rg = wave % RG, hgi = wave / RG;
+  const int wr0 = rg * 32;
+  const float c = a.scale_log2;
+  const int row_bytes = a.kv_heads * D * 2;
+  const char* Kb = reinterpret_cast<const char*>(a.k);
+  const char* Vb = reinterpret_cast<const char*>(a.v);
+  const __bf16* Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* dO = reinterpret_cast<const __bf16*>(a.dout);
+
+  Queues qs;
+  qs.open(a, 0);
+  uint64_t t_start = tid == 0 ? device_clock() : 0;
+  int my_items = 0;
+  int64_t my_pairs = 0;
+  DqLoader<D> ld;
+
+  if (tid == 0) s_item = qs.pop();
+  lds_barrier();
+  int item = __builtin_amdgcn_readfirstlane(s_item);
+  while (item >= 0) {
+    const lb_plan_tile* T;
+    int g;
+    qs.decode(item, &T, &g);
+    const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
+    const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
+    const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
+    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    int n_blocks = 0;
+    for (int s = 0; s < n_spans; ++s) n_blocks += (span_of(T, s).len + BN - 1) / BN;
+    if (tid == 0) {
+      ++my_items;
+      my_pairs += T->cost * G;
+    }
+    const int my_row = wr0 + l32;
+    const bool row_real = my_row < q_len;
+    const bool wave_rows = wr0 < q_len;
+    const int wave_last = min(wr0 + 32, q_len) - 1;
+    const int qpos = q_pos0 + my_row;
+    const int64_t grow = (int64_t)q_start + my_row;
+
+    bf16x8 qreg[HPW][D / 16], doreg[HPW][D / 16];
+    float lse2[HPW], dvv[HPW];
+    f32x16 acc[HPW][D / 32];
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) {
+      const int head = g * G + hgi * HPW + e;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 xq = u32x4{0, 0, 0, 0}, xd = u32x4{0, 0, 0, 0};
+        if (row_real) {
+          const int64_t off = (grow * a.heads + head) * D + kk * 16 + hh * 8;
+          xq = *reinterpret_cast<const u32x4*>(Q + off);
+          xd = *reinterpret_cast<const u32x4*>(dO + off);
+        }
+        qreg[e][kk] = __builtin_bit_cast(bf16x8, xq);
+        doreg[e][kk] = __builtin_bit_cast(bf16x8, xd);
+      }
+      const float l = row_real ? a.lse[(int64_t)head * a.n_q + grow] : -__builtin_inff();
+      // a row that sees nothing (or no row): every weight is 0
+      lse2[e] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+      dvv[e] = row_real ? a.dvec[(int64_t)head * a.n_q + grow] : 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[e][db] = f32x16{};
+    }
+
+    int cur_s = 0;
+    Span cur = span_of(T, 0);
+    int key0 = 0;
+    if (n_blocks > 0) {
+      ld.load(Kb, Vb, cur.start, cur.len, row_bytes, g, tid);
+      ld.store(smem, tid);
+    }
+    for (int it = 0; it < n_blocks; ++it) {
+      lds_barrier();
+      // the block after this one
+      Span nxt = cur;
+      int nkey0 = key0 + BN, nx_s = cur_s;
+      if (nkey0 >= cur.len) {
+        ++nx_s;
+        nkey0 = 0;
+        if (nx_s < n_spans) nxt = span_of(T, nx_s);
+      }
+      const bool has_next = it + 1 < n_blocks;
+      if (has_next) ld.load(Kb, Vb, nxt.start + nkey0, nxt.len - nkey0, row_bytes, g, tid);
+      const char* stage = smem + (it & 1) * L::stage;
+      const char* ks = stage;
+      const char* vs = stage + L::rowsBytes;
+      const char* kt = stage + 2 * L::rowsBytes;
+      const bool live = wave_rows && cur.pos0 + key0 <= q_pos0 + wave_last;
+      if (live) {
+        // visible iff the key's position <= the row's, and the key lies in its span
+        const bool full = key0 + BN <= cur.len && cur.pos0 + key0 + BN - 1 <= q_pos0 + wr0;
+        const int lim = min(cur.len, qpos - cur.pos0 + 1) - key0 - hh * 4;
+        // head by head: the operand fragments are read again for the second head rather
+        // than holding two heads' S^T and dP^T at once
+#pragma unroll
+        for (int e = 0; e < HPW; ++e) {
+          // keeps the compiler from merging the two heads' identical LDS reads into one
+          // set of 48 live fragments
+          if (e > 0) asm volatile("" ::: "memory");
+          f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const bf16x8 kf =
+                  *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * L::kStride + (kk * 16 + hh * 8) * 2);
+              const bf16x8 vf =
+                  *reinterpret_cast<const bf16x8*>(vs + (kb * 32 + l32) * L::kStride + (kk * 16 + hh * 8) * 2);
+              s[kb] = mfma(kf, qreg[e][kk], s[kb]);
+              dp[kb] = mfma(vf, doreg[e][kk], dp[kb]);
+            }
+          bf16x8 dsf[4];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int i = cc * 8 + j;
+                const bool vis = full || (kb * 32 + (i / 4) * 8 + (i % 4) < lim);
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -lse2[e])) : 0.f;
+                dsf[kb * 2 + cc][j] = (__bf16)(p * (dp[kb][i] - dvv[e]));
+              }
+#pragma unroll
+          for (int ks16 = 0; ks16 < 4; ++ks16)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const bf16x8 tf =
+                  *reinterpret_cast<const bf16x8*>(kt + (db * 32 + l32) * L::tStride + (ks16 * 16 + hh * 8) * 2);
+              acc[e][db] = mfma(tf, dsf[ks16], acc[e][db]);
+            }
+        }
+      }
+      if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
+      cur = nxt;
+      cur_s = nx_s;
+      key0 = nkey0;
+    }
+
+    // epilogue: dQ = scale * dQ^T, staged row-major per wave, head by head
+    lds_barrier();
+    char* ebuf = smem + wave * 32 * L::epiStride;
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) {
+      const int head = g * G + hgi * HPW + e;
+      if (e > 0) __builtin_amdgcn_wave_barrier();
+      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc[e], a.scale, lane);
+      __builtin_amdgcn_wave_barrier();
+      char* dst = reinterpret_cast<char*>(a.dq) + (((int64_t)q_start + wr0) * a.heads + head) * D * (OUT_F32 ? 4 : 2);
+      const int rows = max(0, min(32, q_len - wr0));
+      store_rows<D, OUT_F32 ? 2 : 0>(ebuf, L::epiStride, dst, (int64_t)a.heads * D * (OUT_F32 ? 4 : 2), rows, lane);
+    }
+    lds_barrier();
+    if (tid == 0) s_item = qs.pop();
+    lds_barrier();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  qs.close(a, t_start, my_items, my_pairs);
+}
+
+// ------------------------------------------------------------------------------------
+// dK, dV: key-stationary
+// ------------------------------------------------------------------------------------
+template <int D, int HG>
+struct KvLds {
+  static constexpr int rStride = D * 2 + 16;    // Q or dO row
+  static constexpr int tStride = kQB * 2 + 16;  // Q^T or dO^T row (one d, the block's rows)
+  static constexpr int rowsBytes = kQB * rStride;
+  static constexpr int tBytes = D * tStride;
+  static constexpr int head = 2 * rowsBytes + 2 * tBytes + 2 * kQB * 4;  // Q, dO rows; Q^T, dO^T; lse2, D
+  static constexpr int stage = HG * head;
+  static constexpr int units = HG * 2 * (kQB / 2) * (D / 8);  // (head, tensor, row pair, chunk)
+  static constexpr int perThread = units / kBwdThreads;
+  static constexpr int epiStride = D * 4 + 16;
+  static constexpr int accBytes = 2 * (D / 32) * 16 * 64 * 4;  // one wave's dK^T and dV^T accumulators
+};
+
+template <int D, int HG>
+struct QdoLoader {
+  using L = KvLds<D, HG>;
+  u32x4 r[L::perThread][2];
+  float lv, dv;
+
+  // rows r0 .. r0 + 32 of the span (valid rows: `valid`), heads head0 + hg * hstep
+  __device__ __forceinline__ void load(const BwdArgs& a, int r0, int valid, int head0, int hstep, int tid) {
+    const int64_t row_step = (int64_t)a.heads * D * 2;
+    const int nbytes = max(0, min(valid, kQB)) * (int)row_step;
+#pragma unroll
+    for (int e = 0; e < L::perThread; ++e) {
+      const int u = tid + e * kBwdThreads;
+      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = (u / (D / 8) / (kQB / 2)) % 2,
+                hg = u / (D / 8) / (kQB / 2) / 2;
+      const int head = head0 + hg * hstep;
+      const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
+                         (int64_t)head * D * 2;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferFlags);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        r[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rs, (2 * p + x) * (int)row_step + ch * 16, 0, 0);
+    }
+    lv = dv = 0.f;
+    if (tid < HG * kQB) {
+      const int hg = tid / kQB, i = tid % kQB;
+      const int head = head0 + hg * hstep;
+      const float l = i < valid ? a.lse[(int64_t)head * a.n_q + r0 + i] : -__builtin_inff();
+      lv = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+      dv = i < valid ? a.dvec[(int64_t)head * a.n_q + r0 + i] : 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void store(char* stage, int tid) {
+#pragma unroll
+    for (int e = 0; e < L::perThread; ++e) {
+      const int u = tid + e * kBwdThreads;
+      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = (u / (D / 8) / (kQB / 2)) % 2,
+                hg = u / (D / 8) / (kQB / 2) / 2;
+      char* h = stage + hg * L::head;
+      char* rows = h + t * L::rowsBytes;
+      char* tr = h + 2 * L::rowsBytes + t * L::tBytes;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(rows + (2 * p + x) * L::rStride + ch * 16) = r[e][x];
+      const int col = vt_pos(2 * p) * 2;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        *reinterpret_cast<uint32_t*>(tr + (ch * 8 + 2 * m) * L::tStride + col) = pair_lo(r[e][0][m], r[e][1][m]);
+        *reinterpret_cast<uint32_t*>(tr + (ch * 8 + 2 * m + 1) * L::tStride + col) = pair_hi(r[e][0][m], r[e][1][m]);
+      }
+    }
+    if (tid < HG * kQB) {
+      const int hg = tid / kQB, i = tid % kQB;
+      float* f = reinterpret_cast<float*>(stage + hg * L::head + 2 * L::rowsBytes + 2 * L::tBytes);
+      f[i] = lv;
+      f[kQB + i] = dv;
+    }
+  }
+};
+
+template <int D, int KG, bool OUT_F32>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int HG = kBwdWaves / KG;
+  using L = KvLds<D, HG>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
+  __shared__ int s_item;
+  static_assert((HG - 1) * KG * L::accBytes <= 2 * L::stage, "head-group reduction must fit in the ring");
+  static_assert(KG * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int G = a.group;
+  const int kg = wave % KG, hgi = wave / KG;
+  const int hsteps = G / HG;  // heads each head group runs through, one per stage
+  const float c = a.scale_log2;
+  const __bf16* K = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* V = reinterpret_cast<const __bf16*>(a.v);
+
+  Queues qs;
+  qs.open(a, 1);
+  uint64_t t_start = tid == 0 ? device_clock() : 0;
+  int my_items = 0;
+  int64_t my_pairs = 0;
+
+  // key tiles no query row sees: zero gradients, a grid-stride pass before the queues
+  for (int e = blockIdx.x; e < qs.n_empty; e += gridDim.x) {
+    const lb_plan_tile* T = &qs.tiles[qs.order[qs.n_tiles - qs.n_empty + e]];
+    const int k_start = T->q_start, k_len = T->q_len;
+    const int per_row = a.kv_heads * D;
+    for (int idx = tid; idx < k_len * per_row; idx += kBwdThreads) {
+      const int64_t o = (int64_t)k_start * per_row + idx;
+      if constexpr (OUT_F32) {
+        reinterpret_cast<float*>(a.dk)[o] = 0.f;
+        reinterpret_cast<float*>(a.dv)[o] = 0.f;
+      } else {
+        reinterpret_cast<__bf16*>(a.dk)[o] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(a.dv)[o] = (__bf16)0.f;
+      }
+    }
+  }
+
+  QdoLoader<D, HG> ld;
+  if (tid == 0) s_item = qs.pop();
+  lds_barrier();
+  int item = __builtin_amdgcn_readfirstlane(s_item);
+  while (item >= 0) {
+    const lb_plan_tile* T;
+    int g;
+    qs.decode(item, &T, &g);
+    const int k_start = __builtin_amdgcn_readfirstlane(T->q_start);  // the tile's keys
+    const int k_len = __builtin_amdgcn_readfirstlane(T->q_len);
+    const int k_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
+    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    if (tid == 0) {
+      ++my_items;
+      my_pairs += T->cost * G;
+    }
+    const int my_key = kg * 32 + l32;
+    const bool key_real = my_key < k_len;
+    const int kpos = k_pos0 + my_key;
+    const int wave_key_last = k_pos0 + min(kg * 32 + 32, k_len) - 1;  // position of the wave's last key
+    const bool wave_keys = kg * 32 < k_len;
+
+    // stationary operands: K and V rows of the wave's 32 keys, as B fragments
+    bf16x8 kfr[D / 16], vfr[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 xk = u32x4{0, 0, 0, 0}, xv = u32x4{0, 0, 0, 0};
+      if (key_real) {
+        const int64_t off = ((int64_t)(k_start + my_key) * a.kv_heads + g) * D + kk * 16 + hh * 8;
+        xk = *reinterpret_cast<const u32x4*>(K + off);
+        xv = *reinterpret_cast<const u32x4*>(V + off);
+      }
+      kfr[kk] = __builtin_bit_cast(bf16x8, xk);
+      vfr[kk] = __builtin_bit_cast(bf16x8, xv);
+    }
+    f32x16 acc_dk[D / 32], acc_dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      acc_dk[db] = f32x16{};
+      acc_dv[db] = f32x16{};
+    }
+
+    // stages: for each span, each block of 32 rows, each head step
+    int n_stages = 0;
+    for (int s = 0; s < n_spans; ++s) n_stages += (span_of(T, s).len + kQB - 1) / kQB * hsteps;
+    int cur_s = 0, off = 0, hs = 0;
+    Span cur = span_of(T, 0);
+    if (n_stages > 0) {
+      ld.load(a, cur.start + off, cur.len - off, g * G + hs, hsteps, tid);
+      ld.store(smem, tid);
+    }
+    for (int it = 0; it < n_stages; ++it) {
+      lds_barrier();
+      // the stage after this one: next head, else next 32 rows, else next span
+      int n_hs = hs + 1, n_off = off, n_s = cur_s;
+      Span nxt = cur;
+      if (n_hs == hsteps) {
+        n_hs = 0;
+        n_off += kQB;
+        if (n_off >= cur.len) {
+          n_off = 0;
+          ++n_s;
+          if (n_s < n_spans) nxt = span_of(T, n_s);
+        }
+      }
+      const bool has_next = it + 1 < n_stages;
+      if (has_next) ld.load(a, nxt.start + n_off, nxt.len - n_off, g * G + n_hs, hsteps, tid);
+
+      const char* h = smem + (it & 1) * L::stage + hgi * L::head;
+      const char* qrows = h;
+      const char* dorows = h + L::rowsBytes;
+      const char* qt = h + 2 * L::rowsBytes;
+      const char* dot = qt + L::tBytes;
+      const float* lsep = reinterpret_cast<const float*>(dot + L::tBytes);
+      const float* dvp = lsep + kQB;
+      const int rows_valid = min(kQB, cur.len - off);
+      const int row_pos0 = cur.pos0 + off;  // position of the block's first row
+      // any visible pair: the block's last row at or after the wave's first key
+      const bool live = wave_keys && row_pos0 + rows_valid - 1 >= k_pos0 + kg * 32;
+      if (live) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrows + l32 * L::rStride + (kk * 16 + hh * 8) * 2);
+          const bf16x8 df = *reinterpret_cast<const bf16x8*>(dorows + l32 * L::rStride + (kk * 16 + hh * 8) * 2);
+          s = mfma(qf, kfr[kk], s);
+          dp = mfma(df, vfr[kk], dp);
+        }
+        // rows of this lane's accumulator: 8i + 4hh + j; keys: column l32
+        const bool full = row_pos0 >= wave_key_last;
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + 8 * i4 + 4 * hh);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + 8 * i4 + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = i4 * 4 + j;
+            const int row = 8 * i4 + 4 * hh + j;
+            const bool vis = full || kpos <= row_pos0 + row;
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
+            pf[i / 8][i % 8] = (__bf16)p;
+            dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 dtf =
+                *reinterpret_cast<const bf16x8*>(dot + (db * 32 + l32) * L::tStride + (ks * 16 + hh * 8) * 2);
+            const bf16x8 qtf =
+                *reinterpret_cast<const bf16x8*>(qt + (db * 32 + l32) * L::tStride + (ks * 16 + hh * 8) * 2);
+            acc_dv[db] = mfma(dtf, pf[ks], acc_dv[db]);
+            acc_dk[db] = mfma(qtf, dsf[ks], acc_dk[db]);
+          }
+      }
+      if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
+      cur = nxt;
+      cur_s = n_s;
+      off = n_off;
+      hs = n_hs;
+    }
+
+    // epilogue: add the head groups' accumulators, then dK = scale * dK^T and dV = dV^T
+    lds_barrier();
+    if constexpr (HG > 1) {
+      if (hgi > 0) {
+        float* dst = reinterpret_cast<float*>(smem + ((hgi - 1) * KG + kg) * L::accBytes);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            dst[((0 * (D / 32) + db) * 16 + i) * 64 + lane] = acc_dk[db][i];
+            dst[((1 * (D / 32) + db) * 16 + i) * 64 + lane] = acc_dv[db][i];
+          }
+      }
+      lds_barrier();
+      if (hgi == 0) {
+#pragma unroll
+        for (int o = 1; o < HG; ++o) {
+          const float* src = reinterpret_cast<const float*>(smem + ((o - 1) * KG + kg) * L::accBytes);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              acc_dk[db][i] += src[((0 * (D / 32) + db) * 16 + i) * 64 + lane];
+              acc_dv[db][i] += src[((1 * (D / 32) + db) * 16 + i) * 64 + lane];
+            }
+        }
+      }
+      lds_barrier();
+    }
+    if (hgi == 0) {
+      char* ebuf = smem + kg * 32 * L::epiStride;
+      const int rows = max(0, min(32, k_len - kg * 32));
+      const int64_t elt = OUT_F32 ? 4 : 2;
+      const int64_t row_step = (int64_t)a.kv_heads * D * elt;
+      const int64_t first = (((int64_t)k_start + kg * 32) * a.kv_heads + g) * D * elt;
+      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc_dk, a.scale, lane);
+      __builtin_amdgcn_wave_barrier();
+      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(a.dk) + first, row_step, rows, lane);
+      __builtin_amdgcn_wave_barrier();
+      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc_dv, 1.0f, lane);
+      __builtin_amdgcn_wave_barrier();
+      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(a.dv) + first, row_step, rows, lane);
+    }
+    lds_barrier();
+    if (tid == 0) s_item = qs.pop();
+    lds_barrier();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  qs.close(a, t_start, my_items, my_pairs);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,
+                             float* dvec, hipStream_t s) {
+  const int64_t lanes = (int64_t)n_rows * heads * (d / 8);
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if (d == 128) {
+    if (out_f32) hipLaunchKernelGGL((rowdot_kernel<128, true>), grid, block, 0, s, out, dout, n_rows, heads, dvec);
+    else hipLaunchKernelGGL((rowdot_kernel<128, false>), grid, block, 0, s, out, dout, n_rows, heads, dvec);
+  } else {
+    if (out_f32) hipLaunchKernelGGL((rowdot_kernel<64, true>), grid, block, 0, s, out, dout, n_rows, heads, dvec);
+    else hipLaunchKernelGGL((rowdot_kernel<64, false>), grid, block, 0, s, out, dout, n_rows, heads, dvec);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+static void dq_launch(const BwdArgs& a, int workers, hipStream_t s) {
+  if (bwd_heads_per_wave(a.group) == 2)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 1, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
+  if (d == 128) {
+    if (out_f32) dq_launch<128, true>(a, n_workers, s); else dq_launch<128, false>(a, n_workers, s);
+  } else {
+    if (out_f32) dq_launch<64, true>(a, n_workers, s); else dq_launch<64, false>(a, n_workers, s);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+static void dkv_launch(const BwdArgs& a, int workers, hipStream_t s) {
+  if (bwd_k_head_groups(a.group) == 2)
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+}
+
+hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
+  if (d == 128) {
+    if (out_f32) dkv_launch<128, true>(a, n_workers, s); else dkv_launch<128, false>(a, n_workers, s);
+  } else {
+    if (out_f32) dkv_launch<64, true>(a, n_workers, s); else dkv_launch<64, false>(a, n_workers, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lb

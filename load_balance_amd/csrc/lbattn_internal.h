@@ -46,7 +46,8 @@ struct WsHeader {
   uint32_t magic;       // kPlanMagic once a plan has been written
   int32_t per_queue;    // items per queue
   int32_t n_empty;      // tiles with no key span: the last n_empty of the order, kept out of the queues
-  int32_t pad[2];
+  int32_t transposed;   // 1: tiles are key blocks and spans are query runs (the backward's dK/dV plan)
+  int32_t pad;
   int32_t queue_head[8];  // next item of each queue
 };
 
@@ -95,6 +96,7 @@ enum PlanMode { kPlanCausalDoc = 0, kPlanSharedQuestion = 1, kPlanBlock = 2 };
 
 struct PlanArgs {
   int32_t mode;
+  int32_t transposed;  // plan key tiles with the query spans that see them
   const int32_t* cu_seqlens;
   int32_t n_seg, total_tokens;
   const int32_t *q_pos, *q_doc, *kv_pos, *kv_doc;
@@ -131,10 +133,45 @@ struct MergeArgs {
   int32_t n_rows, heads, d;
 };
 
+// Backward kernels: 4 waves per workgroup, one wave per SIMD (each wave may hold 512
+// registers).  dQ: query tiles of bwd_q_rows(G) rows, a wave owning 32 rows of one
+// head (two heads when G = 8).  dK/dV: key tiles of bwd_k_rows(G) keys, a wave owning
+// 32 keys and looping over its share of the G heads; query rows stream in blocks of 32.
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * 64;
+inline __host__ __device__ int bwd_heads_per_wave(int group) { return group > kBwdWaves ? group / kBwdWaves : 1; }
+inline __host__ __device__ int bwd_q_rows(int group) {
+  return 32 * (kBwdWaves / (group / bwd_heads_per_wave(group)));
+}
+inline __host__ __device__ int bwd_k_head_groups(int group) { return group < 2 ? 1 : 2; }
+inline __host__ __device__ int bwd_k_rows(int group) { return 32 * (kBwdWaves / bwd_k_head_groups(group)); }
+
+struct BwdArgs {
+  const void* q;     // bf16 [n_q][heads][d]
+  const void* k;     // bf16 [n_kv][kv_heads][d]
+  const void* v;
+  const void* dout;  // bf16 [n_q][heads][d]
+  const float* lse;  // [heads][n_q], natural log, whole-row values
+  const float* dvec; // [heads][n_q], D = <dout, out>
+  void* dq;          // bf16 [n_q][heads][d], or fp32 accumulated (out_f32)
+  void* dk;          // bf16 [n_kv][kv_heads][d], or fp32 (out_f32)
+  void* dv;
+  int32_t n_q, n_kv;
+  int32_t heads, kv_heads, group;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  char* ws;          // the plan this kernel reads (query tiles for dQ, key tiles for dK/dV)
+  int64_t ws_bytes;
+};
+
 // Launchers, one per translation unit; each returns the launch's hipError_t.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,
+                             float* dvec, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
+hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
 
 }  // namespace lb

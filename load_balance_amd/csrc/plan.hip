@@ -255,6 +255,17 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
           f.q_pos0 = 0;
           f.n_spans = 1;
           f.k_start[0] = f.q_start; f.k_len[0] = f.q_len; f.k_pos0[0] = 0;
+        } else if (a.transposed && s == 0) {
+          // the question's keys, seen by the question's later rows and by every answer row:
+          // one span over the rest of the pack, positions = row index (an answer row's
+          // index is at least Q, past every question key)
+          f.q_pos0 = 0;
+          f.n_spans = 1;
+          f.k_start[0] = cu[0]; f.k_len[0] = a.total_tokens - cu[0]; f.k_pos0[0] = 0;
+        } else if (a.transposed) {  // an answer's keys, seen by its own rows only
+          f.q_pos0 = Q;
+          f.n_spans = 1;
+          f.k_start[0] = f.q_start; f.k_len[0] = f.q_len; f.k_pos0[0] = Q;
         } else if (s == 0) {  // the question: causal on itself
           f.q_pos0 = 0;
           f.n_spans = 1;
@@ -271,30 +282,38 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       }
     }
   } else {  // block path: runs of equal doc id and consecutive position
-    n_frags = find_runs(a.q_pos, a.q_doc, a.n_q, a.L.cap_frags, &frags[0].q_start, sizeof(Frag) / 4, sh);
-    n_kvruns = find_runs(a.kv_pos, a.kv_doc, a.n_kv, min(a.L.cap_frags, kLdsRuns), &kvr[0].start,
-                         sizeof(KvRun) / 4, sh);
+    // Transposed, the tile side is the keys and the spans are query runs: the same search
+    // with the two sides swapped and the visibility test turned around.
+    const int32_t* t_pos = a.transposed ? a.kv_pos : a.q_pos;
+    const int32_t* t_doc = a.transposed ? a.kv_doc : a.q_doc;
+    const int32_t* s_pos = a.transposed ? a.q_pos : a.kv_pos;
+    const int32_t* s_doc = a.transposed ? a.q_doc : a.kv_doc;
+    const int n_t = a.transposed ? a.n_kv : a.n_q, n_s = a.transposed ? a.n_q : a.n_kv;
+    n_frags = find_runs(t_pos, t_doc, n_t, a.L.cap_frags, &frags[0].q_start, sizeof(Frag) / 4, sh);
+    n_kvruns = find_runs(s_pos, s_doc, n_s, min(a.L.cap_frags, kLdsRuns), &kvr[0].start, sizeof(KvRun) / 4, sh);
     if (sh.err == 0) {
       // complete the key/value runs, in LDS for the span search below
       for (int r = tid; r < n_kvruns; r += NT) {
         const int s = kvr[r].start;
-        const int e = r + 1 < n_kvruns ? kvr[r + 1].start : a.n_kv;
-        lds_runs[r] = KvRun{s, e - s, a.kv_pos[s], a.kv_doc[s]};
+        const int e = r + 1 < n_kvruns ? kvr[r + 1].start : n_s;
+        lds_runs[r] = KvRun{s, e - s, s_pos[s], s_doc[s]};
       }
       __syncthreads();
       for (int r = tid; r < n_frags; r += NT) {
         const int s = frags[r].q_start;
-        const int e = r + 1 < n_frags ? frags[r + 1].q_start : a.n_q;
+        const int e = r + 1 < n_frags ? frags[r + 1].q_start : n_t;
         Frag f{};
         f.q_start = s;
         f.q_len = e - s;
-        f.q_pos0 = a.q_pos[s];
-        const int doc = a.q_doc[s];
+        f.q_pos0 = t_pos[s];
+        const int doc = t_doc[s];
         const int last_pos = f.q_pos0 + f.q_len - 1;
         int ns = 0;
         for (int j = 0; j < n_kvruns; ++j) {
           const KvRun kr = lds_runs[j];
-          if (kr.doc != doc || kr.pos0 > last_pos) continue;  // other document, or wholly in the future
+          // other document, or no pair: keys wholly after the query run (forward), or
+          // queries wholly before the key run (transposed)
+          if (kr.doc != doc || (a.transposed ? kr.pos0 + kr.len - 1 < f.q_pos0 : kr.pos0 > last_pos)) continue;
           if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
 #pragma unroll
           for (int o = 0; o < LB_MAX_SPANS; ++o)  // slot ns, selected so the fields stay in registers
@@ -357,12 +376,18 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
 #pragma unroll
       for (int sp = 0; sp < LB_MAX_SPANS; ++sp) {
         if (sp >= f.n_spans) break;
-        const int keep = min(f.k_len[sp], last - f.k_pos0[sp] + 1);
+        // forward: keys up to the tile's last row; transposed: query rows from the tile's
+        // first key on (c rows of the span see none of the tile's keys)
+        const int c = a.transposed ? max(0, T.q_pos0 - f.k_pos0[sp]) : 0;
+        const int keep = a.transposed ? f.k_len[sp] - c : min(f.k_len[sp], last - f.k_pos0[sp] + 1);
         if (keep <= 0) continue;
+        const int s_start = f.k_start[sp] + c, s_pos0 = f.k_pos0[sp] + c;
 #pragma unroll
         for (int o = 0; o <= sp; ++o)  // slot ns <= sp, selected so T stays in registers
-          if (o == ns) { T.k_start[o] = f.k_start[sp]; T.k_len[o] = keep; T.k_pos0[o] = f.k_pos0[sp]; }
-        cost += span_pairs(T.q_pos0, T.q_len, f.k_pos0[sp], keep);
+          if (o == ns) { T.k_start[o] = s_start; T.k_len[o] = keep; T.k_pos0[o] = s_pos0; }
+        // visible pairs: a key at position x and a query at position y with x <= y; the
+        // count is the same whichever side is the tile
+        cost += a.transposed ? span_pairs(s_pos0, keep, T.q_pos0, T.q_len) : span_pairs(T.q_pos0, T.q_len, s_pos0, keep);
         blocks += (keep + kBlockN - 1) / kBlockN;
         ++ns;
       }
@@ -420,6 +445,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     hdr->cap_frags = a.L.cap_frags;
     hdr->cap_tiles = a.L.cap_tiles;
     hdr->total_pairs = ok ? (int64_t)sh.pairs : 0;
+    hdr->transposed = a.transposed;
     hdr->plan_n_q = a.mode == kPlanBlock ? a.n_q : a.total_tokens;
     hdr->plan_n_kv = a.mode == kPlanBlock ? a.n_kv : a.total_tokens;
     hdr->plan_kv_heads = a.kv_heads;

@@ -35,6 +35,27 @@ Tiling rule written out here (the plan the library must reproduce exactly):
    ceil(keys kept / BLOCK_KEYS), the key blocks of BLOCK_KEYS keys it sweeps.
 5. *Order*: blocks descending, ties by natural order (fragment order, then
    tile order inside the fragment).
+
+Transposed tiling, for the key/value gradients of the backward (each key block
+gathers the query rows that see it):
+
+1. Key *fragments*.  Varlen causal: one per document, positions from 0.
+   Shared question: the question's keys (positions from 0) and each answer's
+   keys (positions from Q).  Block step: the runs of the key/value metadata.
+2. Query spans of a key fragment.  Varlen causal: the document's rows.  Shared
+   question: the question's keys are seen by the question's own later rows and
+   by every answer row, so their span is every row from the question's start
+   to the end of the pack, positions counted from the question's start (an
+   answer row's index is at least Q, past every question key); an answer's
+   keys are seen by that answer's rows only, positions from Q.  Block step:
+   every query run of the same document, in query order.  Query i of a span
+   sees key j of the fragment iff pos(j) <= pos(i).
+3. Tiles of BM keys anchored at the fragment start; a tile keeps each span
+   from its first row that sees the tile's first key (pos(row) >= pos of that
+   key); spans clipped to nothing are dropped.
+4. Cost = the tile's exact visible pairs, counted key by key; blocks = sum over
+   its spans of ceil(rows kept / BLOCK_KEYS).
+5. Order: as above.
 """
 from __future__ import annotations
 
@@ -115,6 +136,55 @@ def tiles(frags, bm):
                     cost += visible_in_span(p0 + r, kl, kp0)
             blocks = sum(-(-kl // BLOCK_KEYS) for (ks, kl, kp0) in kept)
             out.append(dict(q_start=qs + t0, q_len=n, q_pos0=p0, spans=kept, cost=cost, blocks=blocks))
+    return out
+
+
+def fragments_varlen_t(cu_seqlens, mask="causal_doc"):
+    """Key fragments of the transposed tiling: (k_start, k_len, k_pos0, [(q_start, q_len, q_pos0), ...])."""
+    cu = [int(x) for x in cu_seqlens]
+    frags = []
+    if mask == "causal_doc":
+        return fragments_varlen(cu, mask)  # a document's keys and its rows: the same ranges
+    if mask != "shared_question":
+        raise ValueError(mask)
+    Q = cu[1] - cu[0]
+    if Q > 0:
+        frags.append((cu[0], Q, 0, [(cu[0], cu[-1] - cu[0], 0)]))
+    for s in range(1, len(cu) - 1):
+        n = cu[s + 1] - cu[s]
+        if n > 0:
+            frags.append((cu[s], n, Q, [(cu[s], n, Q)]))
+    return frags
+
+
+def fragments_block_t(q_pos, q_doc, kv_pos, kv_doc):
+    q_runs = runs(q_pos, q_doc)
+    frags = []
+    for (ks, kl, kp0, kd) in runs(kv_pos, kv_doc):
+        spans = [(qs, ql, qp0) for (qs, ql, qp0, qd) in q_runs if qd == kd]
+        frags.append((ks, kl, kp0, spans))
+    return frags
+
+
+def tiles_t(frags, bm):
+    """Key tiles of the transposed tiling, in the same dict form as ``tiles`` (q_* fields
+    describe the tile's keys, spans are query rows)."""
+    out = []
+    for (ks, kl, kp0, spans) in frags:
+        for t0 in range(0, kl, bm):
+            n = min(bm, kl - t0)
+            p0 = kp0 + t0  # position of the tile's first key
+            kept = []
+            for (qs, ql, qp0) in spans:
+                c = max(0, p0 - qp0)  # rows before the first key's position see none of the tile
+                if ql - c > 0:
+                    kept.append((qs + c, ql - c, qp0 + c))
+            cost = 0
+            for j in range(n):  # key at position p0 + j: rows of each span at or after it
+                for (qs, ql, qp0) in kept:
+                    cost += sum(1 for r in range(ql) if qp0 + r >= p0 + j)
+            blocks = sum(-(-ql // BLOCK_KEYS) for (qs, ql, qp0) in kept)
+            out.append(dict(q_start=ks + t0, q_len=n, q_pos0=p0, spans=kept, cost=cost, blocks=blocks))
     return out
 
 

@@ -242,3 +242,60 @@ def test_zigzag_rank3_step_pairs_match_explicit_mask():
         assert span_count == explicit
         got.append(span_count)
     assert got == [20_319_978, 7_981_112, 0, 0, 0, 0, 0, 3_473_470]
+
+
+# --------------------------------------------------------------------------
+# transposed (key) tiling of the backward
+# --------------------------------------------------------------------------
+def brute_pairs_of_key_tile(t, visible):
+    keys = range(t["q_start"], t["q_start"] + t["q_len"])
+    rows = [r for (qs, ql, _) in t["spans"] for r in range(qs, qs + ql)]
+    return sum(1 for j in keys for i in rows if visible(i, j))
+
+
+@pytest.mark.parametrize("mask", ["causal_doc", "shared_question"])
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_transposed_tiles_cover_every_visible_pair_once_varlen(mask, bm):
+    r = np.random.default_rng(bm + (mask == "shared_question"))
+    lengths = [int(x) for x in r.integers(1, 90, 7)]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    seg = A.doc_of_tokens(cu)
+    T = int(cu[-1])
+    vis = A.visible_causal_doc if mask == "causal_doc" else A.visible_shared_question
+    V = vis(seg, np.arange(T), np.arange(T))
+    tl = P.tiles_t(P.fragments_varlen_t(cu, mask), bm)
+    seen = np.zeros((T, T), dtype=int)
+    for t in tl:
+        assert t["cost"] == brute_pairs_of_key_tile(t, lambda i, j: V[i, j])
+        for j in range(t["q_start"], t["q_start"] + t["q_len"]):
+            for (qs, ql, _) in t["spans"]:
+                seen[qs:qs + ql, j] += V[qs:qs + ql, j]
+    assert np.array_equal(seen, V.astype(int))  # every visible pair in exactly one (tile, span)
+    assert sum(t["cost"] for t in tl) == int(V.sum())
+    # the first row kept in every span sees the tile's first key
+    for t in tl:
+        for (qs, ql, _) in t["spans"]:
+            assert V[qs, t["q_start"]]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_transposed_tiles_cover_every_visible_pair_once_block(seed):
+    r = np.random.default_rng(40 + seed)
+    lengths = [int(x) for x in r.integers(1, 120, 6)]
+    pos, doc = A.pack_positions(lengths)
+    T = len(pos)
+    perm = r.permutation(T)
+    qi, ki = np.sort(perm[:T // 2]), np.sort(perm[T // 2:])
+    qi = np.sort(np.concatenate([qi, ki[:T // 5]]))  # some tokens on both sides
+    V = A.visible_block(pos[qi], doc[qi], pos[ki], doc[ki], np.arange(len(qi)), np.arange(len(ki)))
+    tl = P.tiles_t(P.fragments_block_t(pos[qi], doc[qi], pos[ki], doc[ki]), 16)
+    seen = np.zeros(V.shape, dtype=int)
+    for t in tl:
+        assert t["cost"] == brute_pairs_of_key_tile(t, lambda i, j: V[i, j])
+        for j in range(t["q_start"], t["q_start"] + t["q_len"]):
+            for (qs, ql, _) in t["spans"]:
+                seen[qs:qs + ql, j] += V[qs:qs + ql, j]
+    assert np.array_equal(seen, V.astype(int))
+    # and the pair total equals the forward tiling's
+    fwd = P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 16)
+    assert sum(t["cost"] for t in fwd) == sum(t["cost"] for t in tl) == int(V.sum())
