@@ -102,6 +102,52 @@ class VarlenStep:
         return self.lb.read_worker_timing(self.items[-1]["ws"])
 
 
+class VarlenBwdStep:
+    """The backward of one packed sequence: lb_varlen_attn_bwd (both plans, the D pass, the
+    dq kernel and the dk/dv kernel) from the forward's out and lse and a seeded dout, all
+    resident before the timed region.  Effective FLOPs: the five products of the gradient
+    (S recomputed, dP, dV, dQ, dK) at 2 * d per visible pair each, 10 * d * H * pairs,
+    2.5x the forward's count; the kernels compute S and dP in both passes (7 products)."""
+
+    def __init__(self, pack, mask_kind, name, torch, lb):
+        self.torch, self.lb = torch, lb
+        self.name = name
+        T, H, Hkv, d = pack["tokens"], pack["heads"], pack["kv_heads"], pack["d"]
+        self.q, self.k, self.v = to_dev(pack["q"], torch), to_dev(pack["k"], torch), to_dev(pack["v"], torch)
+        self.cu = torch.from_numpy(np.asarray(pack["cu_seqlens"], np.int32)).cuda()
+        self.mask_kind = mask_kind
+        self.out, self.lse = lb.varlen_attn_fwd(self.q, self.k, self.v, self.cu, mask_kind=mask_kind)
+        r = np.random.default_rng(2000)
+        import workloads
+        self.dout = to_dev(workloads.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32)), torch)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.ws = torch.empty(lb.bwd_workspace_bytes(T, len(pack["lengths"]), H, Hkv), dtype=torch.uint8,
+                              device="cuda")
+        self.key_plan = lb.bwd_key_plan_offset(False, T, T, len(pack["lengths"]), H, Hkv, self.ws.numel())
+        self.H, self.d = H, d
+        self.pairs = causal_pairs(pack["lengths"])
+        self.flops = 10 * d * H * self.pairs
+        self.kernel_name = "backward call (plans, D, bwd_dq_kernel<128,1>, bwd_dkv_kernel<128,2>)"
+
+    def n_launches(self):
+        return 1
+
+    def run(self, evs=None):
+        if evs is not None:
+            evs[0][0].record()
+            evs[0][1].record()
+        self.lb.varlen_attn_bwd(self.q, self.k, self.v, self.out, self.dout, self.lse, self.cu,
+                                mask_kind=self.mask_kind, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+        if evs is not None:
+            evs[0][2].record()
+
+    def plan_pairs(self):
+        return sum(t["cost"] for t in self.lb.read_plan(self.ws[self.key_plan:]))
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.ws[self.key_plan:])
+
+
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
@@ -267,6 +313,14 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "launch": (f"one HIP graph: plan, the 8 attention launches on {overlap} streams, merges in step "
                                "order" if overlap else "one HIP graph, one stream") if graph else "eager"}
         return w
+    if name == "longtail_bwd":
+        p = workloads.longtail_pack(seed)
+        w = VarlenBwdStep(p, lb.MASK_CAUSAL_DOC, name, torch, lb)
+        w.config = {"workload": f"backward (dq, dk, dv) of the 32K long-tail varlen pack, seed {seed}: "
+                                "lb_varlen_attn_bwd from the forward's out and lse and a seeded dout",
+                    "tokens": p["tokens"], "documents": len(p["lengths"]), "heads": 32, "kv_heads": 8,
+                    "head_dim": 128, "seed": seed, "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
+        return w
     if name == "cp_job":
         w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap)
         w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
@@ -347,7 +401,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
-                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job"])
+                    choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job",
+                             "longtail_bwd"])
     ap.add_argument("--rule", default="per_document", choices=list(CP_RULES),
                     help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)

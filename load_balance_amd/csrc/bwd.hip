@@ -9,16 +9,17 @@
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // Two persistent kernels share the forward's queue machinery and plan format:
-//   * dQ, query-stationary, over query tiles (the forward's tiling): per 64-key
-//     block, S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS, Q and dO held in
-//     registers), then dQ^T += K^T dS^T with K^T from LDS.
+//   * dQ, query-stationary, over the forward's query tiles and wave layout (8 waves,
+//     two per SIMD, each 32 rows of one head): per 64-key block, S^T = K Q^T and
+//     dP^T = V dO^T (K and V rows from LDS, Q and dO held in registers), then
+//     dQ^T += K^T dS^T with K^T from LDS.
 //   * dK/dV, key-stationary, over key tiles whose spans are the query rows that see
 //     them (the transposed plan): per block of 32 query rows and head,
 //     S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V held in
 //     registers), then dV^T += dO^T P and dK^T += Q^T dS.  The heads of a kv group
 //     add into the same accumulators, so no reduction over heads follows.
-// Each wave runs alone on its SIMD (4 waves per workgroup) and may hold 512
-// registers: both kernels keep two operand sets and two accumulators live.
+// The dK/dV kernel's waves run alone on their SIMDs (4 waves per workgroup) and may
+// hold 512 registers: two stationary operand sets and two accumulators stay live.
 // Transposed operands (K^T, Q^T, dO^T) are written to LDS by the loader with the
 // index permutation that lets the other MFMA operand come straight from an
 // accumulator (the forward's V^T layout).
@@ -35,7 +36,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = kBlockN;  // keys per block of the dQ kernel
-constexpr int kQB = 32;      // query rows per block of the dK/dV kernel
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = kDqWaves * 64;
+constexpr int kQB = 64;      // query rows per stage of the dK/dV kernel (two MFMA blocks of 32)
 constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ int vt_pos(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -112,9 +115,10 @@ struct Queues {
 
   // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
   __device__ void decode(int item, const lb_plan_tile** T, int* g) const {
+    // the header fields come through vector loads: state that the results are uniform
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
-    *g = q_of + n_queues * (k_in % heads_per_queue);
-    *T = &tiles[order[k_in / heads_per_queue]];
+    *g = __builtin_amdgcn_readfirstlane(q_of + n_queues * (k_in % heads_per_queue));
+    *T = &tiles[__builtin_amdgcn_readfirstlane(order[k_in / heads_per_queue])];
   }
 
   // The last workgroup out rewinds the queues (every pop has happened before it counts itself).
@@ -175,9 +179,11 @@ __device__ __forceinline__ void store_rows(const char* stage, int stride, char* 
 // Stages a 32-column accumulator set (acc[db] holds X^T[d = db*32 + ...][col = lane % 32])
 // as 32 rows of D values, row-major: row = lane % 32, scaled by `mul`.
 template <int D, bool F32>
-__device__ __forceinline__ void stage_rows(char* stage, int stride, const f32x16* acc, float mul, int lane) {
+__device__ __forceinline__ void stage_rows(char* stage, int stride, const f32x16* acc, float mul, int lane,
+                                           int r_lo = 0, int n_rows = 32) {
   const int l32 = lane & 31, hh = lane >> 5;
-  char* rowp = stage + l32 * stride;
+  if (l32 < r_lo || l32 >= r_lo + n_rows) return;
+  char* rowp = stage + (l32 - r_lo) * stride;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -241,9 +247,9 @@ struct DqLds {
   static constexpr int tBytes = D * tStride;
   static constexpr int stage = 2 * rowsBytes + tBytes;  // K rows, V rows, K^T
   static constexpr int kUnits = (BN / 2) * (D / 8);     // (key pair, 16-byte chunk) units of K
-  static constexpr int kPerThread = kUnits / kBwdThreads;
+  static constexpr int kPerThread = (kUnits + kDqThreads - 1) / kDqThreads;  // the last one partial at d = 64
   static constexpr int vChunks = BN * (D / 8);
-  static constexpr int vPerThread = vChunks / kBwdThreads;
+  static constexpr int vPerThread = vChunks / kDqThreads;
   static constexpr int epiStride = D * 4 + 16;
 };
 
@@ -263,14 +269,16 @@ struct DqLoader {
                                                                         kBufferFlags);
 #pragma unroll
     for (int e = 0; e < L::kPerThread; ++e) {
-      const int u = tid + e * kBwdThreads, p = u % (BN / 2), ch = u / (BN / 2);
+      const int u = tid + e * kDqThreads, p = u % (BN / 2), ch = u / (BN / 2);
+      if (L::kUnits % kDqThreads == 0 || u < L::kUnits) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-        kr[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rk, (2 * p + x) * row_bytes + ch * 16, 0, 0);
+        for (int x = 0; x < 2; ++x)
+          kr[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rk, (2 * p + x) * row_bytes + ch * 16, 0, 0);
+      }
     }
 #pragma unroll
     for (int e = 0; e < L::vPerThread; ++e) {
-      const int c = tid + e * kBwdThreads, row = c / (D / 8), ch = c % (D / 8);
+      const int c = tid + e * kDqThreads, row = c / (D / 8), ch = c % (D / 8);
       vr[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * row_bytes + ch * 16, 0, 0);
     }
   }
@@ -281,7 +289,8 @@ struct DqLoader {
     char* kt = stage + 2 * L::rowsBytes;
 #pragma unroll
     for (int e = 0; e < L::kPerThread; ++e) {
-      const int u = tid + e * kBwdThreads, p = u % (BN / 2), ch = u / (BN / 2);
+      const int u = tid + e * kDqThreads, p = u % (BN / 2), ch = u / (BN / 2);
+      if (!(L::kUnits % kDqThreads == 0 || u < L::kUnits)) continue;
 #pragma unroll
       for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(ks + (2 * p + x) * L::kStride + ch * 16) = kr[e][x];
       const int col = vt_pos(2 * p) * 2;
@@ -293,22 +302,22 @@ struct DqLoader {
     }
 #pragma unroll
     for (int e = 0; e < L::vPerThread; ++e) {
-      const int c = tid + e * kBwdThreads, row = c / (D / 8), ch = c % (D / 8);
+      const int c = tid + e * kDqThreads, row = c / (D / 8), ch = c % (D / 8);
       *reinterpret_cast<u32x4*>(vs + row * L::kStride + ch * 16) = vr[e];
     }
   }
 };
 
 template <int D, int HPW, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using L = DqLds<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
   __shared__ int s_item;
-  static_assert(kBwdWaves * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+  static_assert(kDqWaves * 32 * (D * 2 + 16) <= 2 * L::stage, "epilogue staging must fit in the ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
-  const int HG = G / HPW, RG = kBwdWaves / HG;
+  const int HG = G / HPW, RG = kDqWaves / HG;
   const int rg = wave % RG, hgi = wave / RG;
   const int wr0 = rg * 32;
   const float c = a.scale_log2;
@@ -449,18 +458,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       key0 = nkey0;
     }
 
-    // epilogue: dQ = scale * dQ^T, staged row-major per wave, head by head
+    // epilogue: dQ = scale * dQ^T, staged row-major per wave, head by head (fp32 rows in two
+    // passes of 16 where 32 rows of every wave do not fit in the ring)
     lds_barrier();
-    char* ebuf = smem + wave * 32 * L::epiStride;
+    constexpr int kEpiStride = OUT_F32 ? D * 4 + 16 : D * 2 + 16;
+    constexpr int kPassRows = kDqWaves * 32 * kEpiStride <= 2 * L::stage ? 32 : 16;
+    static_assert(kDqWaves * kPassRows * kEpiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+    char* ebuf = smem + wave * kPassRows * kEpiStride;
+    const int64_t row_step = (int64_t)a.heads * D * (OUT_F32 ? 4 : 2);
 #pragma unroll
     for (int e = 0; e < HPW; ++e) {
       const int head = g * G + hgi * HPW + e;
-      if (e > 0) __builtin_amdgcn_wave_barrier();
-      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc[e], a.scale, lane);
-      __builtin_amdgcn_wave_barrier();
-      char* dst = reinterpret_cast<char*>(a.dq) + (((int64_t)q_start + wr0) * a.heads + head) * D * (OUT_F32 ? 4 : 2);
-      const int rows = max(0, min(32, q_len - wr0));
-      store_rows<D, OUT_F32 ? 2 : 0>(ebuf, L::epiStride, dst, (int64_t)a.heads * D * (OUT_F32 ? 4 : 2), rows, lane);
+#pragma unroll
+      for (int r_lo = 0; r_lo < 32; r_lo += kPassRows) {
+        __builtin_amdgcn_wave_barrier();
+        stage_rows<D, OUT_F32>(ebuf, kEpiStride, acc[e], a.scale, lane, r_lo, kPassRows);
+        __builtin_amdgcn_wave_barrier();
+        char* dst = reinterpret_cast<char*>(a.dq) + (((int64_t)q_start + wr0 + r_lo) * a.heads + head) * D * (OUT_F32 ? 4 : 2);
+        const int rows = max(0, min(kPassRows, q_len - wr0 - r_lo));
+        store_rows<D, OUT_F32 ? 2 : 0>(ebuf, kEpiStride, dst, row_step, rows, lane);
+      }
     }
     lds_barrier();
     if (tid == 0) s_item = qs.pop();
@@ -495,14 +512,20 @@ struct QdoLoader {
 
   // rows r0 .. r0 + 32 of the span (valid rows: `valid`), heads head0 + hg * hstep
   __device__ __forceinline__ void load(const BwdArgs& a, int r0, int valid, int head0, int hstep, int tid) {
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    valid = __builtin_amdgcn_readfirstlane(valid);
     const int64_t row_step = (int64_t)a.heads * D * 2;
-    const int nbytes = max(0, min(valid, kQB)) * (int)row_step;
+    const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(valid, kQB)) * (int)row_step);
 #pragma unroll
     for (int e = 0; e < L::perThread; ++e) {
       const int u = tid + e * kBwdThreads;
-      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = (u / (D / 8) / (kQB / 2)) % 2,
-                hg = u / (D / 8) / (kQB / 2) / 2;
-      const int head = head0 + hg * hstep;
+      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2);
+      // (head, tensor) of the unit: one per (kQB / 2) * (D / 8) units, a multiple of 64, so
+      // the same in every lane of a wave -- made explicit, so that the buffer descriptor
+      // lives in scalar registers
+      const int combo = __builtin_amdgcn_readfirstlane(u / ((kQB / 2) * (D / 8)));
+      const int t = combo % 2, hg = combo / 2;
+      const int head = __builtin_amdgcn_readfirstlane(head0 + hg * hstep);
       const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
                          (int64_t)head * D * 2;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferFlags);
@@ -663,30 +686,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       const float* lsep = reinterpret_cast<const float*>(dot + L::tBytes);
       const float* dvp = lsep + kQB;
       const int rows_valid = min(kQB, cur.len - off);
-      const int row_pos0 = cur.pos0 + off;  // position of the block's first row
-      // any visible pair: the block's last row at or after the wave's first key
-      const bool live = wave_keys && row_pos0 + rows_valid - 1 >= k_pos0 + kg * 32;
-      if (live) {
+      const int row_pos0 = cur.pos0 + off;  // position of the stage's first row
+#pragma unroll
+      for (int sb = 0; sb < kQB / 32; ++sb) {
+        const int sb_rows = min(32, rows_valid - sb * 32);
+        const int sb_pos0 = row_pos0 + sb * 32;
+        // any visible pair: the sub-block's last row at or after the wave's first key
+        const bool live = wave_keys && sb_rows > 0 && sb_pos0 + sb_rows - 1 >= k_pos0 + kg * 32;
+        if (!live) continue;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrows + l32 * L::rStride + (kk * 16 + hh * 8) * 2);
-          const bf16x8 df = *reinterpret_cast<const bf16x8*>(dorows + l32 * L::rStride + (kk * 16 + hh * 8) * 2);
-          s = mfma(qf, kfr[kk], s);
-          dp = mfma(df, vfr[kk], dp);
+          const int o = (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2;
+          s = mfma(*reinterpret_cast<const bf16x8*>(qrows + o), kfr[kk], s);
+          dp = mfma(*reinterpret_cast<const bf16x8*>(dorows + o), vfr[kk], dp);
         }
-        // rows of this lane's accumulator: 8i + 4hh + j; keys: column l32
-        const bool full = row_pos0 >= wave_key_last;
+        // rows of this lane's accumulator: 8i + 4hh + j of the sub-block; keys: column l32
+        const bool full = sb_pos0 >= wave_key_last;
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + 8 * i4 + 4 * hh);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + 8 * i4 + 4 * hh);
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = i4 * 4 + j;
             const int row = 8 * i4 + 4 * hh + j;
-            const bool vis = full || kpos <= row_pos0 + row;
+            const bool vis = full || kpos <= sb_pos0 + row;
             const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
             pf[i / 8][i % 8] = (__bf16)p;
             dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
@@ -696,12 +722,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 dtf =
-                *reinterpret_cast<const bf16x8*>(dot + (db * 32 + l32) * L::tStride + (ks * 16 + hh * 8) * 2);
-            const bf16x8 qtf =
-                *reinterpret_cast<const bf16x8*>(qt + (db * 32 + l32) * L::tStride + (ks * 16 + hh * 8) * 2);
-            acc_dv[db] = mfma(dtf, pf[ks], acc_dv[db]);
-            acc_dk[db] = mfma(qtf, dsf[ks], acc_dk[db]);
+            const int o = (db * 32 + l32) * L::tStride + (sb * 32 + ks * 16 + hh * 8) * 2;
+            acc_dv[db] = mfma(*reinterpret_cast<const bf16x8*>(dot + o), pf[ks], acc_dv[db]);
+            acc_dk[db] = mfma(*reinterpret_cast<const bf16x8*>(qt + o), dsf[ks], acc_dk[db]);
           }
       }
       if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
@@ -780,10 +803,7 @@ hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, in
 
 template <int D, bool F32>
 static void dq_launch(const BwdArgs& a, int workers, hipStream_t s) {
-  if (bwd_heads_per_wave(a.group) == 2)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, 1, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, 1, F32>), dim3(workers), dim3(kDqThreads), 0, s, a);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
@@ -797,10 +817,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, h
 
 template <int D, bool F32>
 static void dkv_launch(const BwdArgs& a, int workers, hipStream_t s) {
-  if (bwd_k_head_groups(a.group) == 2)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 2, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+  static_assert(kBwdWaves / 4 == 1, "one head group: every wave runs all heads of the group");
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
 }
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {

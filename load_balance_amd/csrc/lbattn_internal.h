@@ -133,18 +133,14 @@ struct MergeArgs {
   int32_t n_rows, heads, d;
 };
 
-// Backward kernels: 4 waves per workgroup, one wave per SIMD (each wave may hold 512
-// registers).  dQ: query tiles of bwd_q_rows(G) rows, a wave owning 32 rows of one
-// head (two heads when G = 8).  dK/dV: key tiles of bwd_k_rows(G) keys, a wave owning
-// 32 keys and looping over its share of the G heads; query rows stream in blocks of 32.
+// Backward kernels.  dQ: the forward's query tiles and wave layout (8 waves, each 32
+// rows of one head).  dK/dV: 4 waves per workgroup, one per SIMD (each may hold 512
+// registers): key tiles of 128 keys, a wave owning 32 keys and looping over all G heads;
+// query rows stream in stages of 64, one head at a time.
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
-inline __host__ __device__ int bwd_heads_per_wave(int group) { return group > kBwdWaves ? group / kBwdWaves : 1; }
-inline __host__ __device__ int bwd_q_rows(int group) {
-  return 32 * (kBwdWaves / (group / bwd_heads_per_wave(group)));
-}
-inline __host__ __device__ int bwd_k_head_groups(int group) { return group < 2 ? 1 : 2; }
-inline __host__ __device__ int bwd_k_rows(int group) { return 32 * (kBwdWaves / bwd_k_head_groups(group)); }
+inline __host__ __device__ int bwd_q_rows(int group) { return tile_rows_for_group(group); }
+inline __host__ __device__ int bwd_k_rows(int) { return 32 * kBwdWaves; }
 
 struct BwdArgs {
   const void* q;     // bf16 [n_q][heads][d]

@@ -90,8 +90,8 @@ def test_key_tile_plan_equals_oracle(mask):
     H, Hkv, d = 8, 2, 128
     ws, off, cu = varlen_case(lengths, H, Hkv, d, seed=11, mask=mask)
     G = H // Hkv
-    q_rows = 32 * (4 // (G // (G // 4 if G > 4 else 1)))
-    k_rows = 32 * (4 // (1 if G < 2 else 2))
+    q_rows = 256 // G  # the forward's tile height
+    k_rows = 128
     ref_q = OP.plan(OP.fragments_varlen(cu, mask), q_rows)
     ref_k_tiles = OP.tiles_t(OP.fragments_varlen_t(cu, mask), k_rows)
     ref_k = [ref_k_tiles[i] for i in OP.lpt_order(ref_k_tiles)]
