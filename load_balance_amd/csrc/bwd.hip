@@ -488,44 +488,51 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: key-stationary
+// dK, dV: key-stationary, waves split by role
 // ------------------------------------------------------------------------------------
-template <int D, int HG>
+// A tile of 128 keys; 8 waves, two per SIMD.  Waves 0-3 (one per 32 keys) hold K and V and
+// accumulate dK^T = sum Q^T dS (S and dP recomputed); waves 4-7 hold K and accumulate
+// dV^T = sum dO^T P (S recomputed).  Each runs every head of the kv group, so no reduction
+// over heads or waves follows, and each fits in 256 registers.  Query rows stream in
+// stages of 64 (two MFMA blocks of 32), one head per stage, through a 2-stage LDS ring
+// that both roles read.
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKeyGroups = 4;  // 32 keys each: 128 keys per tile
+
+template <int D>
 struct KvLds {
   static constexpr int rStride = D * 2 + 16;    // Q or dO row
-  static constexpr int tStride = kQB * 2 + 16;  // Q^T or dO^T row (one d, the block's rows)
+  static constexpr int tStride = kQB * 2 + 16;  // Q^T or dO^T row (one d, the stage's rows)
   static constexpr int rowsBytes = kQB * rStride;
   static constexpr int tBytes = D * tStride;
-  static constexpr int head = 2 * rowsBytes + 2 * tBytes + 2 * kQB * 4;  // Q, dO rows; Q^T, dO^T; lse2, D
-  static constexpr int stage = HG * head;
-  static constexpr int units = HG * 2 * (kQB / 2) * (D / 8);  // (head, tensor, row pair, chunk)
-  static constexpr int perThread = units / kBwdThreads;
+  static constexpr int stage = 2 * rowsBytes + 2 * tBytes + 2 * kQB * 4;  // Q, dO rows; Q^T, dO^T; lse2, D
+  static constexpr int units = 2 * (kQB / 2) * (D / 8);  // (tensor, row pair, chunk)
+  static constexpr int perThread = units / kKvThreads;
   static constexpr int epiStride = D * 4 + 16;
-  static constexpr int accBytes = 2 * (D / 32) * 16 * 64 * 4;  // one wave's dK^T and dV^T accumulators
+  static_assert(units % kKvThreads == 0, "loader units must divide evenly");
 };
 
-template <int D, int HG>
+template <int D>
 struct QdoLoader {
-  using L = KvLds<D, HG>;
+  using L = KvLds<D>;
   u32x4 r[L::perThread][2];
   float lv, dv;
 
-  // rows r0 .. r0 + 32 of the span (valid rows: `valid`), heads head0 + hg * hstep
-  __device__ __forceinline__ void load(const BwdArgs& a, int r0, int valid, int head0, int hstep, int tid) {
+  // rows r0 .. r0 + kQB of the span (`valid` of them real) of one head
+  __device__ __forceinline__ void load(const BwdArgs& a, int r0, int valid, int head, int tid) {
     r0 = __builtin_amdgcn_readfirstlane(r0);
     valid = __builtin_amdgcn_readfirstlane(valid);
+    head = __builtin_amdgcn_readfirstlane(head);
     const int64_t row_step = (int64_t)a.heads * D * 2;
     const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(valid, kQB)) * (int)row_step);
 #pragma unroll
     for (int e = 0; e < L::perThread; ++e) {
-      const int u = tid + e * kBwdThreads;
+      const int u = tid + e * kKvThreads;
       const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2);
-      // (head, tensor) of the unit: one per (kQB / 2) * (D / 8) units, a multiple of 64, so
-      // the same in every lane of a wave -- made explicit, so that the buffer descriptor
-      // lives in scalar registers
-      const int combo = __builtin_amdgcn_readfirstlane(u / ((kQB / 2) * (D / 8)));
-      const int t = combo % 2, hg = combo / 2;
-      const int head = __builtin_amdgcn_readfirstlane(head0 + hg * hstep);
+      // the tensor of the unit is the same in every lane of a wave (a multiple of 64 units
+      // each): made explicit, so that the buffer descriptor lives in scalar registers
+      const int t = __builtin_amdgcn_readfirstlane(u / ((kQB / 2) * (D / 8)));
       const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
                          (int64_t)head * D * 2;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferFlags);
@@ -534,24 +541,20 @@ struct QdoLoader {
         r[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rs, (2 * p + x) * (int)row_step + ch * 16, 0, 0);
     }
     lv = dv = 0.f;
-    if (tid < HG * kQB) {
-      const int hg = tid / kQB, i = tid % kQB;
-      const int head = head0 + hg * hstep;
-      const float l = i < valid ? a.lse[(int64_t)head * a.n_q + r0 + i] : -__builtin_inff();
+    if (tid < kQB) {
+      const float l = tid < valid ? a.lse[(int64_t)head * a.n_q + r0 + tid] : -__builtin_inff();
       lv = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
-      dv = i < valid ? a.dvec[(int64_t)head * a.n_q + r0 + i] : 0.f;
+      dv = tid < valid ? a.dvec[(int64_t)head * a.n_q + r0 + tid] : 0.f;
     }
   }
 
   __device__ __forceinline__ void store(char* stage, int tid) {
 #pragma unroll
     for (int e = 0; e < L::perThread; ++e) {
-      const int u = tid + e * kBwdThreads;
-      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = (u / (D / 8) / (kQB / 2)) % 2,
-                hg = u / (D / 8) / (kQB / 2) / 2;
-      char* h = stage + hg * L::head;
-      char* rows = h + t * L::rowsBytes;
-      char* tr = h + 2 * L::rowsBytes + t * L::tBytes;
+      const int u = tid + e * kKvThreads;
+      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = u / ((kQB / 2) * (D / 8));
+      char* rows = stage + t * L::rowsBytes;
+      char* tr = stage + 2 * L::rowsBytes + t * L::tBytes;
 #pragma unroll
       for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(rows + (2 * p + x) * L::rStride + ch * 16) = r[e][x];
       const int col = vt_pos(2 * p) * 2;
@@ -561,28 +564,25 @@ struct QdoLoader {
         *reinterpret_cast<uint32_t*>(tr + (ch * 8 + 2 * m + 1) * L::tStride + col) = pair_hi(r[e][0][m], r[e][1][m]);
       }
     }
-    if (tid < HG * kQB) {
-      const int hg = tid / kQB, i = tid % kQB;
-      float* f = reinterpret_cast<float*>(stage + hg * L::head + 2 * L::rowsBytes + 2 * L::tBytes);
-      f[i] = lv;
-      f[kQB + i] = dv;
+    if (tid < kQB) {
+      float* f = reinterpret_cast<float*>(stage + 2 * L::rowsBytes + 2 * L::tBytes);
+      f[tid] = lv;
+      f[kQB + tid] = dv;
     }
   }
 };
 
-template <int D, int KG, bool OUT_F32>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int HG = kBwdWaves / KG;
-  using L = KvLds<D, HG>;
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
+  using L = KvLds<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
   __shared__ int s_item;
-  static_assert((HG - 1) * KG * L::accBytes <= 2 * L::stage, "head-group reduction must fit in the ring");
-  static_assert(KG * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+  static_assert(kKvWaves * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
-  const int kg = wave % KG, hgi = wave / KG;
-  const int hsteps = G / HG;  // heads each head group runs through, one per stage
+  const int kg = wave % kKeyGroups;
+  const bool dk_role = wave < kKeyGroups;  // else the dV role
   const float c = a.scale_log2;
   const __bf16* K = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* V = reinterpret_cast<const __bf16*>(a.v);
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     const lb_plan_tile* T = &qs.tiles[qs.order[qs.n_tiles - qs.n_empty + e]];
     const int k_start = T->q_start, k_len = T->q_len;
     const int per_row = a.kv_heads * D;
-    for (int idx = tid; idx < k_len * per_row; idx += kBwdThreads) {
+    for (int idx = tid; idx < k_len * per_row; idx += kKvThreads) {
       const int64_t o = (int64_t)k_start * per_row + idx;
       if constexpr (OUT_F32) {
         reinterpret_cast<float*>(a.dk)[o] = 0.f;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
   }
 
-  QdoLoader<D, HG> ld;
+  QdoLoader<D> ld;
   if (tid == 0) s_item = qs.pop();
   lds_barrier();
   int item = __builtin_amdgcn_readfirstlane(s_item);
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int wave_key_last = k_pos0 + min(kg * 32 + 32, k_len) - 1;  // position of the wave's last key
     const bool wave_keys = kg * 32 < k_len;
 
-    // stationary operands: K and V rows of the wave's 32 keys, as B fragments
+    // stationary operands: the wave's 32 keys as B fragments (K for both roles, V for dK)
     bf16x8 kfr[D / 16], vfr[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -640,33 +640,30 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       if (key_real) {
         const int64_t off = ((int64_t)(k_start + my_key) * a.kv_heads + g) * D + kk * 16 + hh * 8;
         xk = *reinterpret_cast<const u32x4*>(K + off);
-        xv = *reinterpret_cast<const u32x4*>(V + off);
+        if (dk_role) xv = *reinterpret_cast<const u32x4*>(V + off);
       }
       kfr[kk] = __builtin_bit_cast(bf16x8, xk);
       vfr[kk] = __builtin_bit_cast(bf16x8, xv);
     }
-    f32x16 acc_dk[D / 32], acc_dv[D / 32];
+    f32x16 acc[D / 32];  // dK^T or dV^T of the wave's keys
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      acc_dk[db] = f32x16{};
-      acc_dv[db] = f32x16{};
-    }
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-    // stages: for each span, each block of 32 rows, each head step
+    // stages: for each span, each 64 rows, each head of the group
     int n_stages = 0;
-    for (int s = 0; s < n_spans; ++s) n_stages += (span_of(T, s).len + kQB - 1) / kQB * hsteps;
+    for (int s = 0; s < n_spans; ++s) n_stages += (span_of(T, s).len + kQB - 1) / kQB * G;
     int cur_s = 0, off = 0, hs = 0;
     Span cur = span_of(T, 0);
     if (n_stages > 0) {
-      ld.load(a, cur.start + off, cur.len - off, g * G + hs, hsteps, tid);
+      ld.load(a, cur.start + off, cur.len - off, g * G + hs, tid);
       ld.store(smem, tid);
     }
     for (int it = 0; it < n_stages; ++it) {
       lds_barrier();
-      // the stage after this one: next head, else next 32 rows, else next span
+      // the stage after this one: next head, else next 64 rows, else next span
       int n_hs = hs + 1, n_off = off, n_s = cur_s;
       Span nxt = cur;
-      if (n_hs == hsteps) {
+      if (n_hs == G) {
         n_hs = 0;
         n_off += kQB;
         if (n_off >= cur.len) {
@@ -676,9 +673,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
         }
       }
       const bool has_next = it + 1 < n_stages;
-      if (has_next) ld.load(a, nxt.start + n_off, nxt.len - n_off, g * G + n_hs, hsteps, tid);
+      if (has_next) ld.load(a, nxt.start + n_off, nxt.len - n_off, g * G + n_hs, tid);
 
-      const char* h = smem + (it & 1) * L::stage + hgi * L::head;
+      const char* h = smem + (it & 1) * L::stage;
       const char* qrows = h;
       const char* dorows = h + L::rowsBytes;
       const char* qt = h + 2 * L::rowsBytes;
@@ -694,38 +691,59 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
         // any visible pair: the sub-block's last row at or after the wave's first key
         const bool live = wave_keys && sb_rows > 0 && sb_pos0 + sb_rows - 1 >= k_pos0 + kg * 32;
         if (!live) continue;
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int o = (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2;
-          s = mfma(*reinterpret_cast<const bf16x8*>(qrows + o), kfr[kk], s);
-          dp = mfma(*reinterpret_cast<const bf16x8*>(dorows + o), vfr[kk], dp);
-        }
         // rows of this lane's accumulator: 8i + 4hh + j of the sub-block; keys: column l32
         const bool full = sb_pos0 >= wave_key_last;
-        bf16x8 pf[2], dsf[2];
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
+        for (int kk = 0; kk < D / 16; ++kk)
+          s = mfma(*reinterpret_cast<const bf16x8*>(qrows + (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2),
+                   kfr[kk], s);
+        if (dk_role) {
+          f32x16 dp = f32x16{};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = i4 * 4 + j;
-            const int row = 8 * i4 + 4 * hh + j;
-            const bool vis = full || kpos <= sb_pos0 + row;
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
-            pf[i / 8][i % 8] = (__bf16)p;
-            dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
+          for (int kk = 0; kk < D / 16; ++kk)
+            dp = mfma(*reinterpret_cast<const bf16x8*>(dorows + (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2),
+                      vfr[kk], dp);
+          bf16x8 dsf[2];
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
+            const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = i4 * 4 + j;
+              const bool vis = full || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
+              const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
+              dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
+            }
           }
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+              acc[db] = mfma(*reinterpret_cast<const bf16x8*>(qt + (db * 32 + l32) * L::tStride +
+                                                               (sb * 32 + ks * 16 + hh * 8) * 2),
+                             dsf[ks], acc[db]);
+        } else {
+          bf16x8 pf[2];
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = i4 * 4 + j;
+              const bool vis = full || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
+              pf[i / 8][i % 8] = (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f);
+            }
+          }
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+              acc[db] = mfma(*reinterpret_cast<const bf16x8*>(dot + (db * 32 + l32) * L::tStride +
+                                                               (sb * 32 + ks * 16 + hh * 8) * 2),
+                             pf[ks], acc[db]);
         }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int o = (db * 32 + l32) * L::tStride + (sb * 32 + ks * 16 + hh * 8) * 2;
-            acc_dv[db] = mfma(*reinterpret_cast<const bf16x8*>(dot + o), pf[ks], acc_dv[db]);
-            acc_dk[db] = mfma(*reinterpret_cast<const bf16x8*>(qt + o), dsf[ks], acc_dk[db]);
-          }
       }
       if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
       cur = nxt;
@@ -734,48 +752,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       hs = n_hs;
     }
 
-    // epilogue: add the head groups' accumulators, then dK = scale * dK^T and dV = dV^T
+    // epilogue: dK = scale * dK^T, dV = dV^T, each role its own tensor
     lds_barrier();
-    if constexpr (HG > 1) {
-      if (hgi > 0) {
-        float* dst = reinterpret_cast<float*>(smem + ((hgi - 1) * KG + kg) * L::accBytes);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            dst[((0 * (D / 32) + db) * 16 + i) * 64 + lane] = acc_dk[db][i];
-            dst[((1 * (D / 32) + db) * 16 + i) * 64 + lane] = acc_dv[db][i];
-          }
-      }
-      lds_barrier();
-      if (hgi == 0) {
-#pragma unroll
-        for (int o = 1; o < HG; ++o) {
-          const float* src = reinterpret_cast<const float*>(smem + ((o - 1) * KG + kg) * L::accBytes);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              acc_dk[db][i] += src[((0 * (D / 32) + db) * 16 + i) * 64 + lane];
-              acc_dv[db][i] += src[((1 * (D / 32) + db) * 16 + i) * 64 + lane];
-            }
-        }
-      }
-      lds_barrier();
-    }
-    if (hgi == 0) {
-      char* ebuf = smem + kg * 32 * L::epiStride;
+    {
+      char* ebuf = smem + wave * 32 * L::epiStride;
       const int rows = max(0, min(32, k_len - kg * 32));
       const int64_t elt = OUT_F32 ? 4 : 2;
       const int64_t row_step = (int64_t)a.kv_heads * D * elt;
       const int64_t first = (((int64_t)k_start + kg * 32) * a.kv_heads + g) * D * elt;
-      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc_dk, a.scale, lane);
+      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc, dk_role ? a.scale : 1.0f, lane);
       __builtin_amdgcn_wave_barrier();
-      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(a.dk) + first, row_step, rows, lane);
-      __builtin_amdgcn_wave_barrier();
-      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc_dv, 1.0f, lane);
-      __builtin_amdgcn_wave_barrier();
-      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(a.dv) + first, row_step, rows, lane);
+      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(dk_role ? a.dk : a.dv) + first,
+                                     row_step, rows, lane);
     }
     lds_barrier();
     if (tid == 0) s_item = qs.pop();
@@ -817,8 +805,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, h
 
 template <int D, bool F32>
 static void dkv_launch(const BwdArgs& a, int workers, hipStream_t s) {
-  static_assert(kBwdWaves / 4 == 1, "one head group: every wave runs all heads of the group");
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, 4, F32>), dim3(workers), dim3(kBwdThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, F32>), dim3(workers), dim3(kKvThreads), 0, s, a);
 }
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
