@@ -84,7 +84,8 @@ enum {
   LB_DEVERR_CU_SEQLENS = 1,   /* cu_seqlens[0] != 0, decreasing, or cu_seqlens[n_seg] != total_tokens */
   LB_DEVERR_CAPACITY = 2,     /* more fragments or tiles than the workspace holds */
   LB_DEVERR_SPANS = 4,        /* a query run meets more than LB_MAX_SPANS key runs of its document */
-  LB_DEVERR_PLAN = 8          /* lb_attn_run's shapes differ from those the workspace's plan was made for */
+  LB_DEVERR_PLAN = 8,         /* lb_attn_run's shapes differ from those the workspace's plan was made for */
+  LB_DEVERR_SLICES = 16       /* a slice list out of range, unsorted, overlapping, or of an unknown kind */
 };
 
 #define LB_MAX_SPANS 4
@@ -292,6 +293,40 @@ lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chu
                             const float* lse, const float* dvec, const int32_t* q_pos, const int32_t* kv_pos,
                             const int32_t* q_doc, const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
                             float* dq, float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ---- Slice-list masks -------------------------------------------------------------
+ * "03 · 长文负载均衡", section 4.4 (MagiAttention): a mask written as rectangles of
+ * query rows x keys, each of one type; the mask is their union.  FULL: every pair of the
+ * rectangle.  CAUSAL (aligned at the bottom-right corner): row r of the rectangle
+ * (0-based) sees its keys 0 .. r + k_len - q_len.  Varlen causal, shared-question,
+ * block-causal (frames that see their document up to their own end) and prefix masks
+ * are all such lists.
+ * The list is sorted by q_start; slices with the same (q_start, q_len) form one query
+ * range and must cover disjoint key ranges (at most LB_MAX_SPANS of them); different
+ * query ranges must not overlap.  A violation sets LB_DEVERR_SLICES (more than
+ * LB_MAX_SPANS slices on one range: LB_DEVERR_SPANS) and nothing runs.
+ */
+typedef struct {
+  int32_t q_start, q_len;  /* query rows [q_start, q_start + q_len), q_len >= 1 */
+  int32_t k_start, k_len;  /* keys [k_start, k_start + k_len), k_len >= 1 */
+  int32_t kind;            /* LB_SLICE_FULL or LB_SLICE_CAUSAL */
+} lb_mask_slice;
+
+enum { LB_SLICE_FULL = 0, LB_SLICE_CAUSAL = 1 };
+
+/* The plan of a slice list: slices is a DEVICE array of n_slices entries; queries
+   [0, n_q), keys [0, n_kv).  Workspace: lb_workspace_bytes(n_q, n_slices, heads, kv_heads)
+   bytes.  Run it with lb_attn_run (k, v of n_kv rows; out bf16 or fp32). */
+lb_status lb_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
+                         int32_t kv_heads, int32_t d, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward under a slice-list mask: q bf16 [n_q][heads][d], k, v bf16 [n_kv][kv_heads][d];
+   out bf16 [n_q][heads][d], lse fp32 [heads][n_q].  lse is -inf on rows no slice covers
+   (their out is not written) and on rows that see no key. */
+lb_status lb_slices_attn_fwd(const void* q, const void* k, const void* v, const lb_mask_slice* slices,
+                             int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* lb_status_string(lb_status s);

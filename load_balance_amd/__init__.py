@@ -30,6 +30,9 @@ DEVERR_CU_SEQLENS = 1
 DEVERR_CAPACITY = 2
 DEVERR_SPANS = 4
 DEVERR_PLAN = 8
+DEVERR_SLICES = 16
+SLICE_FULL = 0
+SLICE_CAUSAL = 1
 
 
 class LBError(RuntimeError):
@@ -80,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.lb_attn_run.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.lb_lse_merge.restype = ctypes.c_int
+    L.lb_plan_slices.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_slices.restype = ctypes.c_int
+    L.lb_slices_attn_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_slices_attn_fwd.restype = ctypes.c_int
     L.lb_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32]
     L.lb_bwd_workspace_bytes.restype = SZ
     L.lb_bwd_key_plan_offset.argtypes = [I32, I32, I32, I32, I32, I32, SZ]
@@ -362,3 +369,46 @@ def block_attn_bwd(q_shard, kv_chunk, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_
                                    _ptr(dkv), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_block_attn_bwd")
     return dq, dkv
+
+
+# --------------------------------------------------------------------------
+# slice-list masks
+# --------------------------------------------------------------------------
+def _slice_tensor(slices, device):
+    """slices: an int32 tensor [n, 5] (q_start, q_len, k_start, k_len, kind) on the device, or a
+    list of such tuples (copied to the device)."""
+    if isinstance(slices, torch.Tensor):
+        if slices.dtype != torch.int32 or slices.dim() != 2 or slices.shape[1] != 5 or not slices.is_contiguous():
+            raise LBError("slices must be a contiguous int32 tensor of shape [n, 5]")
+        return slices
+    return torch.tensor([list(x) for x in slices], dtype=torch.int32, device=device).reshape(-1, 5)
+
+
+def plan_slices(slices, n_q, n_kv, heads, kv_heads, d, workspace=None, stream=None):
+    """The plan of a slice-list mask into ``workspace`` (run it with attn_run)."""
+    sl = _slice_tensor(slices, "cuda")
+    if workspace is None:
+        workspace = new_workspace(n_q, max(1, sl.shape[0]), heads, kv_heads, sl.device)
+    _check(lib().lb_plan_slices(_ptr(sl), sl.shape[0], n_q, n_kv, heads, kv_heads, d, _ptr(workspace),
+                                workspace.numel(), ctypes.c_void_p(_stream(stream))), "lb_plan_slices")
+    return workspace
+
+
+def slices_attn_fwd(q, k, v, slices, out=None, lse=None, workspace=None, stream=None):
+    """out [n_q,H,d] bf16 and lse [H,n_q] of q against k/v under a slice-list mask."""
+    n_q, H, d = q.shape
+    n_kv, Hkv = k.shape[0], k.shape[1]
+    sl = _slice_tensor(slices, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(n_q, max(1, sl.shape[0]), H, Hkv, q.device)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+    _check(lib().lb_slices_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), sl.shape[0], n_q, n_kv, H, Hkv, d, _ptr(out),
+                                    _ptr(lse), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_slices_attn_fwd")
+    return out, lse

@@ -229,6 +229,37 @@ BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout, 
   return b;
 }
 
+// Checks and layout of a slice-list plan; *L receives the layout when LB_OK.
+lb_status prepare_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
+                              int32_t kv_heads, int32_t d, void* workspace, size_t workspace_bytes, WsLayout* L) {
+  if (!slices || !workspace || n_slices < 1 || n_q < 0 || n_kv < 0) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(slices, 4)) return LB_EINVAL;
+  if (!aligned(workspace, 256)) return LB_EWORKSPACE;
+  const int64_t tiles = ceil_div(n_q, tile_rows_for_group(heads / kv_heads)) + n_slices;
+  if (tiles > kSortCap) return LB_EUNSUPPORTED;
+  *L = ws_layout(n_slices, tiles);
+  if ((int64_t)workspace_bytes < L->total) return LB_EWORKSPACE;
+  return LB_OK;
+}
+
+lb_status launch_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
+                             int32_t kv_heads, void* workspace, const WsLayout& L, hipStream_t stream) {
+  PlanArgs p{};
+  p.mode = kPlanSlices;
+  p.slices = slices;
+  p.n_slices = n_slices;
+  p.n_q = n_q;
+  p.n_kv = n_kv;
+  p.tile_rows = tile_rows_for_group(heads / kv_heads);
+  p.heads = heads;
+  p.kv_heads = kv_heads;
+  p.ws = static_cast<char*>(workspace);
+  p.L = L;
+  return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
 bool read_header(const void* ws, size_t bytes, WsHeader* h, hipStream_t s) {
   if (!ws || bytes < sizeof(WsHeader)) return false;
   if (hipStreamSynchronize(s) != hipSuccess) return false;
@@ -351,6 +382,31 @@ lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const flo
   if (n_rows == 0) return LB_OK;
   MergeArgs m{out_a, lse_a, out_b, lse_b, n_rows, heads, d};
   return launch_lse_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status lb_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
+                         int32_t kv_heads, int32_t d, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  WsLayout L;
+  lb_status st = prepare_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, d, workspace, workspace_bytes, &L);
+  if (st != LB_OK) return st;
+  return launch_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, workspace, L, stream);
+}
+
+lb_status lb_slices_attn_fwd(const void* q, const void* k, const void* v, const lb_mask_slice* slices,
+                             int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!k || !v) return LB_EINVAL;
+  lb_status st = check_run(q, k, v, n_q, n_kv, heads, kv_heads, d, out, lse, workspace, workspace_bytes);
+  if (st != LB_OK) return st;
+  WsLayout L;
+  st = prepare_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, d, workspace, workspace_bytes, &L);
+  if (st != LB_OK) return st;
+  if (n_q == 0) return LB_OK;
+  // rows no slice covers keep lse = -inf
+  if (launch_fill_f32(lse, (int64_t)heads * n_q, -INFINITY, stream) != hipSuccess) return LB_EHIP;
+  st = launch_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, workspace, L, stream);
+  if (st != LB_OK) return st;
+  return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, false, out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t lb_bwd_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads) {

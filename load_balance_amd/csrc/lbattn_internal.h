@@ -92,7 +92,11 @@ inline WsLayout ws_layout(int64_t cap_frags, int64_t cap_tiles) {
   return L;
 }
 
-enum PlanMode { kPlanCausalDoc = 0, kPlanSharedQuestion = 1, kPlanBlock = 2 };
+enum PlanMode { kPlanCausalDoc = 0, kPlanSharedQuestion = 1, kPlanBlock = 2, kPlanSlices = 3 };
+
+// Key position offset of a FULL slice's span: below every query position, so that every
+// key is visible (the planner's pair count stays in 64-bit range).
+constexpr int32_t kFullSpanPos = -(1 << 30);
 
 struct PlanArgs {
   int32_t mode;
@@ -100,6 +104,8 @@ struct PlanArgs {
   const int32_t* cu_seqlens;
   int32_t n_seg, total_tokens;
   const int32_t *q_pos, *q_doc, *kv_pos, *kv_doc;
+  const lb_mask_slice* slices;
+  int32_t n_slices;
   int32_t n_q, n_kv;
   int32_t tile_rows, heads, kv_heads;
   char* ws;
@@ -165,6 +171,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,
                              float* dvec, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);

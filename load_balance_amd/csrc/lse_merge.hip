@@ -95,4 +95,16 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int64_t n, float value) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = value;
+}
+}  // namespace
+
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s) {
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
 }  // namespace lb

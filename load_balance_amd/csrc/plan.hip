@@ -281,6 +281,50 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
         if (n_frags <= kLdsFrags) lds_frags[s] = f;
       }
     }
+  } else if (a.mode == kPlanSlices) {
+    // one fragment per query range: slice s opens one when its range differs from s - 1's
+    const lb_mask_slice* sl = a.slices;
+    int running = 0;
+    for (int base = 0; base < a.n_slices; base += NT) {
+      const int s = base + tid;
+      bool opens = false;
+      if (s < a.n_slices) {
+        const lb_mask_slice x = sl[s];
+        bool bad = x.q_len < 1 || x.k_len < 1 || x.q_start < 0 || x.k_start < 0 || x.q_start > a.n_q - x.q_len ||
+                   x.k_start > a.n_kv - x.k_len || (x.kind != LB_SLICE_FULL && x.kind != LB_SLICE_CAUSAL);
+        opens = s == 0 || sl[s - 1].q_start != x.q_start || sl[s - 1].q_len != x.q_len;
+        if (s > 0 && opens && sl[s - 1].q_start + sl[s - 1].q_len > x.q_start) bad = true;  // unsorted or overlapping
+        if (!opens && sl[s - 1].k_start + sl[s - 1].k_len > x.k_start) bad = true;  // key ranges must ascend, disjoint
+        if (bad) atomicOr(&sh.err, LB_DEVERR_SLICES);
+      }
+      int total;
+      const int off = block_excl_scan(opens ? 1 : 0, sh, &total);
+      if (opens && running + off < a.L.cap_frags) {
+        // the fragment's spans: this slice and the following ones on the same range
+        const lb_mask_slice x = sl[s];
+        Frag f{};
+        f.q_start = x.q_start;
+        f.q_len = x.q_len;
+        f.q_pos0 = 0;
+        int ns = 0;
+        for (int j = s; j < a.n_slices; ++j) {
+          const lb_mask_slice y = sl[j];
+          if (y.q_start != x.q_start || y.q_len != x.q_len) break;
+          if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
+          const int pos0 = y.kind == LB_SLICE_CAUSAL ? y.q_len - y.k_len : kFullSpanPos;
+#pragma unroll
+          for (int o = 0; o < LB_MAX_SPANS; ++o)
+            if (o == ns) { f.k_start[o] = y.k_start; f.k_len[o] = y.k_len; f.k_pos0[o] = pos0; }
+          ++ns;
+        }
+        f.n_spans = ns;
+        frags[running + off] = f;
+        if (running + off < kLdsFrags) lds_frags[running + off] = f;
+      }
+      running += total;
+    }
+    n_frags = running;
+    if (n_frags > a.L.cap_frags && tid == 0) sh.err |= LB_DEVERR_CAPACITY;
   } else {  // block path: runs of equal doc id and consecutive position
     // Transposed, the tile side is the keys and the spans are query runs: the same search
     // with the two sides swapped and the visibility test turned around.
@@ -446,8 +490,9 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     hdr->cap_tiles = a.L.cap_tiles;
     hdr->total_pairs = ok ? (int64_t)sh.pairs : 0;
     hdr->transposed = a.transposed;
-    hdr->plan_n_q = a.mode == kPlanBlock ? a.n_q : a.total_tokens;
-    hdr->plan_n_kv = a.mode == kPlanBlock ? a.n_kv : a.total_tokens;
+    const bool pair_sides = a.mode == kPlanBlock || a.mode == kPlanSlices;
+    hdr->plan_n_q = pair_sides ? a.n_q : a.total_tokens;
+    hdr->plan_n_kv = pair_sides ? a.n_kv : a.total_tokens;
     hdr->plan_kv_heads = a.kv_heads;
     hdr->plan_heads = a.heads;
     hdr->done = 0;

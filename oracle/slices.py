@@ -1,0 +1,114 @@
+"""Slice-list masks -- TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+"03 · 长文负载均衡", section 4.4 (MagiAttention): an irregular mask is written as a
+list of slices, each a query range, a key range and a mask type on that rectangle;
+the types are FULL, CAUSAL, INV-CAUSAL and BI-CAUSAL, and slices combine to express
+anything from varlen causal to varlen block-causal masks.  The mask of the list is
+the union of its slices' masks.  This module handles FULL and CAUSAL slices.
+
+Readings where the page is silent:
+* CAUSAL on a rectangle of Lq query rows and Lk keys is aligned at the bottom-right
+  corner: row r (0-based in the slice) sees keys 0 .. r + (Lk - Lq) of the slice, so
+  the last row sees every key (for Lq = Lk this is the usual causal triangle);
+* slices over the same query range must cover disjoint key ranges (the union is then
+  a plain sum of their pairs), and two different query ranges must not overlap;
+* a query row covered by no slice sees nothing: lse = -inf, out = 0 here.
+
+A slice is (q_start, q_len, k_start, k_len, kind) with kind 0 = FULL, 1 = CAUSAL.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import ROW_BLOCK, _as_f64, attend
+
+FULL, CAUSAL = 0, 1
+FAR = 1 << 30  # key position offset of a FULL span: below every query position
+
+
+def visible(slices, n_q, n_k):
+    """The explicit boolean mask [n_q, n_k] of a slice list."""
+    m = np.zeros((n_q, n_k), dtype=bool)
+    for (qs, ql, ks, kl, kind) in slices:
+        r = np.arange(ql)[:, None]
+        c = np.arange(kl)[None, :]
+        blk = np.ones((ql, kl), dtype=bool) if kind == FULL else (c <= r + (kl - ql))
+        m[qs:qs + ql, ks:ks + kl] |= blk
+    return m
+
+
+def slices_attention(q, k, v, slices, heads, kv_heads, scale=None):
+    """out [n_q,H,d] and lse [H,n_q] of q [n_q,H,d] against k/v [n_k,H_kv,d] under the mask."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    n_q, H, d = q.shape
+    n_k = k.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    vis = visible(slices, n_q, n_k)
+    G = heads // kv_heads
+    out = np.zeros((n_q, H, v.shape[2]))
+    lse = np.full((H, n_q), -np.inf)
+    for b in range(0, n_q, ROW_BLOCK):
+        rows = np.arange(b, min(n_q, b + ROW_BLOCK))
+        cols = np.nonzero(vis[rows].any(axis=0))[0]
+        for h in range(H):
+            o, l = attend(q[rows, h], k[cols, h // G], v[cols, h // G], vis[np.ix_(rows, cols)], scale)
+            out[rows, h] = o
+            lse[h, rows] = l
+    return out, lse
+
+
+def fragments(slices):
+    """Planner fragments of a slice list (query ranges in order, each with the key spans of
+    its slices): (q_start, q_len, q_pos0, [(k_start, k_len, k_pos0), ...]) with query
+    positions from 0 in the range, so that key j of a span is visible to row r iff
+    k_pos0 + j <= r: a CAUSAL span starts at position q_len - k_len, a FULL one far below."""
+    frags = []
+    for (qs, ql, ks, kl, kind) in slices:
+        span = (ks, kl, (ql - kl) if kind == CAUSAL else -FAR)
+        if frags and frags[-1][0] == qs and frags[-1][1] == ql:
+            frags[-1][3].append(span)
+        else:
+            frags.append((qs, ql, 0, [span]))
+    return frags
+
+
+def block_causal_slices(lengths, frame):
+    """Varlen block-causal (MAGI-1's mask in section 4.4): every document is cut into frames
+    of ``frame`` tokens; a frame's rows see every key of their document up to the frame's
+    end.  One FULL slice per frame."""
+    out = []
+    start = 0
+    for n in lengths:
+        for f0 in range(0, n, frame):
+            fl = min(frame, n - f0)
+            out.append((start + f0, fl, start, f0 + fl, FULL))
+        start += n
+    return out
+
+
+def varlen_causal_slices(lengths):
+    """The per-document causal mask as slices: one square CAUSAL slice per document."""
+    out, start = [], 0
+    for n in lengths:
+        if n:
+            out.append((start, n, start, n, CAUSAL))
+        start += n
+    return out
+
+
+def shared_question_slices(lengths):
+    """The shared-question mask as slices: the question causal on itself; every answer FULL
+    on the question and CAUSAL on itself."""
+    Q = lengths[0]
+    out = [(0, Q, 0, Q, CAUSAL)] if Q else []
+    start = Q
+    for n in lengths[1:]:
+        if n:
+            if Q:
+                out.append((start, n, 0, Q, FULL))
+            out.append((start, n, start, n, CAUSAL))
+        start += n
+    return out
