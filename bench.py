@@ -148,6 +148,50 @@ class VarlenBwdStep:
         return self.lb.read_worker_timing(self.ws[self.key_plan:])
 
 
+class SlicesStep:
+    """plan + attention of one pack under a slice-list mask (lb_plan_slices + lb_attn_run)."""
+
+    def __init__(self, pack, slices, name, torch, lb):
+        self.torch, self.lb = torch, lb
+        self.name = name
+        T, H, Hkv, d = pack["tokens"], pack["heads"], pack["kv_heads"], pack["d"]
+        self.T, self.H, self.Hkv, self.d = T, H, Hkv, d
+        self.q, self.k, self.v = to_dev(pack["q"], torch), to_dev(pack["k"], torch), to_dev(pack["v"], torch)
+        self.sl = torch.tensor([list(x) for x in slices], dtype=torch.int32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        self.ws = lb.new_workspace(T, len(slices), H, Hkv)
+        # visible pairs, rectangle by rectangle (FULL: all; CAUSAL aligned bottom-right)
+        pairs = 0
+        for (qs, ql, ks, kl, kind) in slices:
+            if kind == lb.SLICE_FULL:
+                pairs += ql * kl
+            else:
+                pairs += sum(min(kl, max(0, r + kl - ql + 1)) for r in range(ql))
+        self.pairs = pairs
+        self.flops = 4 * d * H * pairs
+
+    def n_launches(self):
+        return 1
+
+    def run(self, evs=None):
+        lb = self.lb
+        if evs is not None:
+            evs[0][0].record()
+        lb.plan_slices(self.sl, self.T, self.T, self.H, self.Hkv, self.d, workspace=self.ws)
+        if evs is not None:
+            evs[0][1].record()
+        lb.attn_run(self.q, self.k, self.v, self.out, self.lse, self.ws)
+        if evs is not None:
+            evs[0][2].record()
+
+    def plan_pairs(self):
+        return sum(t["cost"] for t in self.lb.read_plan(self.ws))
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.ws)
+
+
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
@@ -313,6 +357,22 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "launch": (f"one HIP graph: plan, the 8 attention launches on {overlap} streams, merges in step "
                                "order" if overlap else "one HIP graph, one stream") if graph else "eager"}
         return w
+    if name == "blockcausal":
+        p = workloads.longtail_pack(seed)
+        frame = 256
+        sl, start = [], 0
+        for n in p["lengths"]:  # every document cut into frames that see it up to their own end
+            for f0 in range(0, n, frame):
+                fl = min(frame, n - f0)
+                sl.append((start + f0, fl, start, f0 + fl, lb.SLICE_FULL))
+            start += n
+        w = SlicesStep(p, sl, name, torch, lb)
+        w.config = {"workload": f"varlen block-causal mask as a slice list: the 32K long-tail pack (seed {seed}), "
+                                f"every document in frames of {frame} tokens that see their document up to their "
+                                "own end (one FULL slice per frame)",
+                    "tokens": p["tokens"], "documents": len(p["lengths"]), "frame": frame, "slices": len(sl),
+                    "heads": 32, "kv_heads": 8, "head_dim": 128, "seed": seed}
+        return w
     if name == "longtail_bwd":
         p = workloads.longtail_pack(seed)
         w = VarlenBwdStep(p, lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -402,7 +462,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
                     choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job",
-                             "longtail_bwd"])
+                             "longtail_bwd", "blockcausal"])
     ap.add_argument("--rule", default="per_document", choices=list(CP_RULES),
                     help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)
