@@ -154,6 +154,8 @@ class SlicesStep:
     def __init__(self, pack, slices, name, torch, lb):
         self.torch, self.lb = torch, lb
         self.name = name
+        # lower-bounded slices (INV-CAUSAL, BI-CAUSAL) run on the bounded kernel
+        self.lower = any(x[4] in (lb.SLICE_INV_CAUSAL, lb.SLICE_BI_CAUSAL) for x in slices)
         T, H, Hkv, d = pack["tokens"], pack["heads"], pack["kv_heads"], pack["d"]
         self.T, self.H, self.Hkv, self.d = T, H, Hkv, d
         self.q, self.k, self.v = to_dev(pack["q"], torch), to_dev(pack["k"], torch), to_dev(pack["v"], torch)
@@ -161,13 +163,14 @@ class SlicesStep:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
         self.ws = lb.new_workspace(T, len(slices), H, Hkv)
-        # visible pairs, rectangle by rectangle (FULL: all; CAUSAL aligned bottom-right)
+        # visible pairs, rectangle by rectangle: row r sees keys lo .. hi of its slice (CAUSAL
+        # and BI-CAUSAL bound hi at r + kl - ql, INV-CAUSAL and BI-CAUSAL bound lo at r)
         pairs = 0
         for (qs, ql, ks, kl, kind) in slices:
-            if kind == lb.SLICE_FULL:
-                pairs += ql * kl
-            else:
-                pairs += sum(min(kl, max(0, r + kl - ql + 1)) for r in range(ql))
+            r = np.arange(ql)
+            hi = np.minimum(kl - 1, r + kl - ql) if kind in (lb.SLICE_CAUSAL, lb.SLICE_BI_CAUSAL) else np.full(ql, kl - 1)
+            lo = r if kind in (lb.SLICE_INV_CAUSAL, lb.SLICE_BI_CAUSAL) else np.zeros(ql, dtype=np.int64)
+            pairs += int(np.maximum(0, hi - lo + 1).sum())
         self.pairs = pairs
         self.flops = 4 * d * H * pairs
 
@@ -181,7 +184,7 @@ class SlicesStep:
         lb.plan_slices(self.sl, self.T, self.T, self.H, self.Hkv, self.d, workspace=self.ws)
         if evs is not None:
             evs[0][1].record()
-        lb.attn_run(self.q, self.k, self.v, self.out, self.lse, self.ws)
+        (lb.attn_run_lower if self.lower else lb.attn_run)(self.q, self.k, self.v, self.out, self.lse, self.ws)
         if evs is not None:
             evs[0][2].record()
 
@@ -373,6 +376,30 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "tokens": p["tokens"], "documents": len(p["lengths"]), "frame": frame, "slices": len(sl),
                     "heads": 32, "kv_heads": 8, "head_dim": 128, "seed": seed}
         return w
+    if name == "slidingwindow":
+        p = workloads.longtail_pack(seed)
+        window, rows = 1024, 64
+        sl, start = [], 0
+        for n in p["lengths"]:  # causal sliding window per document, as BI-CAUSAL bands of 64 rows
+            for q0 in range(0, n, rows):
+                ql = min(rows, n - q0)
+                k0 = q0 - window + 1
+                if k0 >= 0:
+                    sl.append((start + q0, ql, start + k0, ql + window - 1, lb.SLICE_BI_CAUSAL))
+                elif q0 + ql - window <= 0:
+                    sl.append((start + q0, ql, start, q0 + ql, lb.SLICE_CAUSAL))
+                else:
+                    for i in range(q0, q0 + ql):
+                        lo = max(0, i - window + 1)
+                        sl.append((start + i, 1, start + lo, i - lo + 1, lb.SLICE_FULL))
+            start += n
+        w = SlicesStep(p, sl, name, torch, lb)
+        w.config = {"workload": f"causal sliding window of {window} keys per document, as a slice list (BI-CAUSAL "
+                                f"bands of {rows} rows): the 32K long-tail pack (seed {seed})",
+                    "tokens": p["tokens"], "documents": len(p["lengths"]), "window": window, "slices": len(sl),
+                    "heads": 32, "kv_heads": 8, "head_dim": 128, "seed": seed}
+        w.kernel_name = "attn_kernel<128,false,lower bound> (persistent, LPT queue)"
+        return w
     if name == "longtail_bwd":
         p = workloads.longtail_pack(seed)
         w = VarlenBwdStep(p, lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -462,7 +489,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
                     choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job",
-                             "longtail_bwd", "blockcausal"])
+                             "longtail_bwd", "blockcausal", "slidingwindow"])
     ap.add_argument("--rule", default="per_document", choices=list(CP_RULES),
                     help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)

@@ -91,6 +91,7 @@ enum {
 #define LB_MAX_SPANS 4
 #define LB_MAX_PLAN_STEPS 16 /* block steps one lb_plan_block_steps call can plan */
 #define LB_BLOCK_KEYS 64 /* keys per block the attention kernel steps through */
+#define LB_NO_LOWER_BOUND (1 << 30) /* k_lo of a span whose keys have no lower bound */
 
 /*
  * One tile of the plan, as lb_read_plan returns it, in queue order: `blocks`
@@ -109,6 +110,8 @@ typedef struct {
   int32_t k_start[LB_MAX_SPANS]; /* first key row of each span */
   int32_t k_len[LB_MAX_SPANS];   /* keys kept: those the tile's last row can see */
   int32_t k_pos0[LB_MAX_SPANS];  /* mask position of the span's first key */
+  int32_t k_lo[LB_MAX_SPANS];    /* lower bound: key j of the span is visible to a row at position p
+                                    only if k_lo + j >= p (LB_NO_LOWER_BOUND: no such bound) */
   int32_t blocks;                /* sum over spans of ceil(k_len / LB_BLOCK_KEYS): the order key */
   int32_t reserved;
 } lb_plan_tile;
@@ -216,6 +219,13 @@ lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, 
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* lb_attn_run for plans whose spans bound their visible keys from below as well (slice
+   lists with INV-CAUSAL or BI-CAUSAL slices); it runs any plan, a little slower than
+   lb_attn_run on plans without such bounds. */
+lb_status lb_attn_run_lower(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                            int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 /*
  * In-place merge a <- merge(a, b) of two partials over disjoint key sets:
  *   M = max(lse_a, lse_b), w_x = exp(lse_x - M),
@@ -310,14 +320,19 @@ lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chu
 typedef struct {
   int32_t q_start, q_len;  /* query rows [q_start, q_start + q_len), q_len >= 1 */
   int32_t k_start, k_len;  /* keys [k_start, k_start + k_len), k_len >= 1 */
-  int32_t kind;            /* LB_SLICE_FULL or LB_SLICE_CAUSAL */
+  int32_t kind;            /* LB_SLICE_FULL, _CAUSAL, _INV_CAUSAL or _BI_CAUSAL */
 } lb_mask_slice;
 
-enum { LB_SLICE_FULL = 0, LB_SLICE_CAUSAL = 1 };
+/* INV-CAUSAL is aligned at the top-left corner: row r sees keys r .. k_len - 1.
+   BI-CAUSAL is CAUSAL and INV-CAUSAL at once (a band): keys r .. r + k_len - q_len; a causal
+   sliding window is a list of such bands. */
+enum { LB_SLICE_FULL = 0, LB_SLICE_CAUSAL = 1, LB_SLICE_INV_CAUSAL = 2, LB_SLICE_BI_CAUSAL = 3 };
 
 /* The plan of a slice list: slices is a DEVICE array of n_slices entries; queries
    [0, n_q), keys [0, n_kv).  Workspace: lb_workspace_bytes(n_q, n_slices, heads, kv_heads)
-   bytes.  Run it with lb_attn_run (k, v of n_kv rows; out bf16 or fp32). */
+   bytes.  Run it with lb_attn_run (k, v of n_kv rows; out bf16 or fp32) when every slice is
+   FULL or CAUSAL, with lb_attn_run_lower when some are INV-CAUSAL or BI-CAUSAL (lb_attn_run
+   refuses such a plan: LB_DEVERR_PLAN). */
 lb_status lb_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
                          int32_t kv_heads, int32_t d, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

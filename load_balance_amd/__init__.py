@@ -33,6 +33,9 @@ DEVERR_PLAN = 8
 DEVERR_SLICES = 16
 SLICE_FULL = 0
 SLICE_CAUSAL = 1
+SLICE_INV_CAUSAL = 2
+SLICE_BI_CAUSAL = 3
+NO_LOWER_BOUND = 1 << 30
 
 
 class LBError(RuntimeError):
@@ -43,7 +46,8 @@ class PlanTile(ctypes.Structure):
     _fields_ = [("q_start", ctypes.c_int32), ("q_len", ctypes.c_int32), ("q_pos0", ctypes.c_int32),
                 ("n_spans", ctypes.c_int32), ("cost", ctypes.c_int64),
                 ("k_start", ctypes.c_int32 * MAX_SPANS), ("k_len", ctypes.c_int32 * MAX_SPANS),
-                ("k_pos0", ctypes.c_int32 * MAX_SPANS), ("blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("k_pos0", ctypes.c_int32 * MAX_SPANS), ("k_lo", ctypes.c_int32 * MAX_SPANS),
+                ("blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class WorkerRecord(ctypes.Structure):
@@ -81,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.lb_plan_block_steps.restype = ctypes.c_int
     L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run.restype = ctypes.c_int
+    L.lb_attn_run_lower.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_attn_run_lower.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.lb_lse_merge.restype = ctypes.c_int
     L.lb_plan_slices.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
@@ -253,6 +259,16 @@ def attn_run(q, k, v, out, lse, workspace, stream=None):
     return out, lse
 
 
+def attn_run_lower(q, k, v, out, lse, workspace, stream=None):
+    """attn_run for plans with lower-bounded spans (INV-CAUSAL / BI-CAUSAL slices)."""
+    n_q, H, d = q.shape
+    n_kv, Hkv = k.shape[0], k.shape[1]
+    _check(lib().lb_attn_run_lower(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, H, Hkv, d, int(out.dtype == torch.float32),
+                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                   ctypes.c_void_p(_stream(stream))), "lb_attn_run_lower")
+    return out, lse
+
+
 def lse_merge(out_a, lse_a, out_b, lse_b, stream=None):
     """In place: (out_a, lse_a) <- merge((out_a, lse_a), (out_b, lse_b)).  fp32 [R,H,d] and [H,R]."""
     R, H, d = out_a.shape
@@ -281,7 +297,9 @@ def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
     out = []
     for i in range(min(n.value, max_tiles)):
         t = buf[i]
-        spans = [(t.k_start[s], t.k_len[s], t.k_pos0[s]) for s in range(t.n_spans)]
+        # (k_start, k_len, k_pos0), with k_lo appended when the span has a lower bound
+        spans = [(t.k_start[s], t.k_len[s], t.k_pos0[s]) + (() if t.k_lo[s] == NO_LOWER_BOUND else (t.k_lo[s],))
+                 for s in range(t.n_spans)]
         out.append(dict(q_start=t.q_start, q_len=t.q_len, q_pos0=t.q_pos0, spans=spans, cost=t.cost,
                         blocks=t.blocks))
     return out

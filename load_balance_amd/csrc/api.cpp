@@ -69,7 +69,7 @@ lb_status check_run(const void* q, const void* k, const void* v, int32_t n_q, in
 
 lb_status launch_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                      int32_t kv_heads, int32_t d, bool out_f32, void* out, float* lse, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+                     size_t workspace_bytes, hipStream_t stream, bool lower = false) {
   int workers = 0;
   lb_status st = persistent_workers(&workers);
   if (st != LB_OK) return st;
@@ -87,7 +87,7 @@ lb_status launch_run(const void* q, const void* k, const void* v, int32_t n_q, i
   at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   at.ws = static_cast<char*>(workspace);
   at.ws_bytes = (int64_t)workspace_bytes;
-  return launch_attention(at, d, out_f32, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+  return launch_attention(at, d, out_f32, lower, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
 // Checks and layout of a varlen plan; *L receives the layout when LB_OK.
@@ -332,6 +332,16 @@ lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, 
                     stream);
 }
 
+lb_status lb_attn_run_lower(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
+                            int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  lb_status st = check_run(q, k, v, n_q, n_kv, heads, kv_heads, d, out, lse, workspace, workspace_bytes);
+  if (st != LB_OK) return st;
+  if (n_q == 0) return LB_OK;
+  return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, out_f32 != 0, out, lse, workspace, workspace_bytes,
+                    stream, true);
+}
+
 lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                              int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
                              int32_t d, int32_t mask_kind, void* out, float* lse, void* workspace,
@@ -406,7 +416,8 @@ lb_status lb_slices_attn_fwd(const void* q, const void* k, const void* v, const 
   if (launch_fill_f32(lse, (int64_t)heads * n_q, -INFINITY, stream) != hipSuccess) return LB_EHIP;
   st = launch_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, workspace, L, stream);
   if (st != LB_OK) return st;
-  return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, false, out, lse, workspace, workspace_bytes, stream);
+  return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, false, out, lse, workspace, workspace_bytes, stream,
+                    true);
 }
 
 size_t lb_bwd_workspace_bytes(int32_t max_tokens, int32_t max_segments, int32_t heads, int32_t kv_heads) {

@@ -161,9 +161,13 @@ struct KvBlock {
   int len;    // keys of the span (already clipped to the tile's last row)
   int pos0;   // mask position of the span's first key
   int start;  // first key row of the span
+  int lo0;    // lower bound: key j of the span is visible to a row at position p only if lo0 + j >= p
 };
 
-template <int D, bool OUT_F32>
+// LOWER: spans may carry a lower bound on their visible keys (INV-CAUSAL and BI-CAUSAL
+// slices).  Without it the kernel refuses such plans: the bound costs scalar registers in
+// the key loop, so the common instance goes without.
+template <int D, bool OUT_F32, bool LOWER>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
   __shared__ int s_item;
@@ -182,7 +186,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   // A missing plan, or one made for other shapes or another workspace size, could index
   // outside this launch's buffers: then run nothing and flag it.
   const int64_t n_tiles_hdr = hdr->n_tiles;
-  const bool mismatch = hdr->magic != kPlanMagic || hdr->transposed != 0 || hdr->plan_n_q != a.n_q ||
+  const bool mismatch = hdr->magic != kPlanMagic || hdr->transposed != 0 || (!LOWER && hdr->has_lower != 0) ||
+                        hdr->plan_n_q != a.n_q ||
                         hdr->plan_n_kv != a.n_kv ||
                         hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
                         hdr->n_empty < 0 || hdr->n_empty > n_tiles_hdr ||
@@ -273,9 +278,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
     const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
-    // Span fields ride in the lanes of one register: lanes 0-3 k_start, 4-7 k_len, 8-11 k_pos0;
-    // a wave reads them back with v_readlane only when it steps into a new span.
-    const int span_v = lane < 3 * LB_MAX_SPANS ? (&T->k_start[0])[lane] : 0;
+    // Span fields ride in the lanes of one register: lanes 0-3 k_start, 4-7 k_len, 8-11 k_pos0,
+    // 12-15 k_lo; a wave reads them back with v_readlane only when it steps into a new span.
+    const int span_v = lane < (LOWER ? 4 : 3) * LB_MAX_SPANS ? (&T->k_start[0])[lane] : 0;
     int n_kv_tiles = 0;
 #pragma unroll
     for (int s = 0; s < LB_MAX_SPANS; ++s)
@@ -290,6 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       b.start = __builtin_amdgcn_readlane(span_v, s);
       b.len = __builtin_amdgcn_readlane(span_v, LB_MAX_SPANS + s);
       b.pos0 = __builtin_amdgcn_readlane(span_v, 2 * LB_MAX_SPANS + s);
+      b.lo0 = LOWER ? __builtin_amdgcn_readlane(span_v, 3 * LB_MAX_SPANS + s) : LB_NO_LOWER_BOUND;
       return b;
     };
 
@@ -318,7 +324,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     f32x16 acc_s[2];
 
     // does key block b have any visible pair for this wave's real rows?
-    auto live = [&](const KvBlock& b) { return wave_rows && b.pos0 + b.key0 <= q_pos0 + wave_last; };
+    // (and, under a lower bound, does the block's last key reach down to the wave's first row?)
+    auto live = [&](const KvBlock& b) {
+      return wave_rows && b.pos0 + b.key0 <= q_pos0 + wave_last && (!LOWER || b.lo0 + b.key0 + BN - 1 >= q_pos0 + wr0);
+    };
 
     auto qk = [&](const char* ks) {
 #pragma unroll
@@ -335,15 +344,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 
     // mask (diagonal / ragged blocks only), online softmax, O^T += V^T P^T
     auto softmax_pv = [&](const KvBlock& b, const char* vs) {
-      const bool full = b.key0 + BN <= b.len && b.pos0 + b.key0 + BN - 1 <= q_pos0 + wr0;
+      const bool full = b.key0 + BN <= b.len && b.pos0 + b.key0 + BN - 1 <= q_pos0 + wr0 &&
+                        (!LOWER || b.lo0 + b.key0 >= q_pos0 + wave_last);
       if (!full) {
         // key k of the block is visible iff k < lim (span end, and position <= this row's)
+        // and, under a lower bound, k >= lim_lo
         const int lim = min(b.len, qpos - b.pos0 + 1) - b.key0 - hh * 4;
+        if constexpr (LOWER) {
+          const int lim_lo = qpos - b.lo0 - b.key0 - hh * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (!(kb * 32 + (i / 4) * 8 + (i % 4) < lim)) acc_s[kb][i] = -__builtin_inff();
+            for (int i = 0; i < 16; ++i) {
+              const int k = kb * 32 + (i / 4) * 8 + (i % 4);
+              if (!(k < lim && k >= lim_lo)) acc_s[kb][i] = -__builtin_inff();
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (!(kb * 32 + (i / 4) * 8 + (i % 4) < lim)) acc_s[kb][i] = -__builtin_inff();
+        }
       }
       float mx = -__builtin_inff();
 #pragma unroll
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       ld.load(Kb, Vb, cur.start, cur.len, row_bytes, g, tid);
       ld.store(smem, tid);
     }
-    KvBlock prev{0, 0, 0, 0};
+    KvBlock prev{0, 0, 0, 0, LB_NO_LOWER_BOUND};
     bool prev_live = false;
 
     for (int it = 0; it < n_kv_tiles; ++it) {
@@ -523,14 +545,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
-  dim3 grid(n_workers), block(kThreads);
+template <int D, bool OUT_F32>
+static void launch_d(const AttnArgs& a, bool lower, int n_workers, hipStream_t s) {
+  if (lower) hipLaunchKernelGGL((attn_kernel<D, OUT_F32, true>), dim3(n_workers), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((attn_kernel<D, OUT_F32, false>), dim3(n_workers), dim3(kThreads), 0, s, a);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, int n_workers, hipStream_t s) {
   if (d == 128) {
-    if (out_f32) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, s, a);
+    if (out_f32) launch_d<128, true>(a, lower, n_workers, s); else launch_d<128, false>(a, lower, n_workers, s);
   } else {
-    if (out_f32) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, s, a);
+    if (out_f32) launch_d<64, true>(a, lower, n_workers, s); else launch_d<64, false>(a, lower, n_workers, s);
   }
   return hipGetLastError();
 }

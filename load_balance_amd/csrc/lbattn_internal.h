@@ -47,7 +47,7 @@ struct WsHeader {
   int32_t per_queue;    // items per queue
   int32_t n_empty;      // tiles with no key span: the last n_empty of the order, kept out of the queues
   int32_t transposed;   // 1: tiles are key blocks and spans are query runs (the backward's dK/dV plan)
-  int32_t pad;
+  int32_t has_lower;    // 1: some span has a lower bound (needs the bounded attention kernel)
   int32_t queue_head[8];  // next item of each queue
 };
 
@@ -58,16 +58,18 @@ static_assert(sizeof(WsHeader) <= 256, "header must fit its slot");
 // A query fragment with its key spans before per-tile clipping.
 struct Frag {
   int32_t q_start, q_len, q_pos0, n_spans;
-  int32_t k_start[LB_MAX_SPANS], k_len[LB_MAX_SPANS], k_pos0[LB_MAX_SPANS];
+  int32_t k_start[LB_MAX_SPANS], k_len[LB_MAX_SPANS], k_pos0[LB_MAX_SPANS], k_lo[LB_MAX_SPANS];
 };
-static_assert(sizeof(Frag) == 64, "");
+static_assert(sizeof(Frag) == 80, "");
 
 // A key/value run (block path): equal document id, consecutive positions.
 struct KvRun {
   int32_t start, len, pos0, doc;
 };
 
-static_assert(sizeof(lb_plan_tile) == 80, "lb_plan_tile layout");
+static_assert(sizeof(lb_plan_tile) == 96, "lb_plan_tile layout");
+static_assert(offsetof(lb_plan_tile, k_lo) == offsetof(lb_plan_tile, k_start) + 12 * LB_MAX_SPANS,
+              "span fields are contiguous: k_start, k_len, k_pos0, k_lo");
 static_assert(sizeof(lb_worker_record) == 40, "lb_worker_record layout");
 
 struct WsLayout {
@@ -169,7 +171,7 @@ struct BwdArgs {
 // Launchers, one per translation unit; each returns the launch's hipError_t.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,

@@ -39,6 +39,7 @@ struct PlanShared {
   int32_t run_sum[kRunRounds][kPlanWaves];
   int32_t err;
   int32_t n_empty;
+  int32_t has_lower;
   unsigned long long pairs;
 };
 
@@ -231,6 +232,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     sh.err = 0;
     sh.pairs = 0;
     sh.n_empty = 0;
+    sh.has_lower = 0;
   }
   __syncthreads();
 
@@ -249,6 +251,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       const int Q = cu[1] - cu[0];
       for (int s = tid; s < n_frags; s += NT) {
         Frag f{};
+#pragma unroll
+        for (int o = 0; o < LB_MAX_SPANS; ++o) f.k_lo[o] = LB_NO_LOWER_BOUND;
         f.q_start = cu[s];
         f.q_len = cu[s + 1] - cu[s];
         if (a.mode == kPlanCausalDoc) {
@@ -291,7 +295,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       if (s < a.n_slices) {
         const lb_mask_slice x = sl[s];
         bool bad = x.q_len < 1 || x.k_len < 1 || x.q_start < 0 || x.k_start < 0 || x.q_start > a.n_q - x.q_len ||
-                   x.k_start > a.n_kv - x.k_len || (x.kind != LB_SLICE_FULL && x.kind != LB_SLICE_CAUSAL);
+                   x.k_start > a.n_kv - x.k_len || x.kind < LB_SLICE_FULL || x.kind > LB_SLICE_BI_CAUSAL;
         opens = s == 0 || sl[s - 1].q_start != x.q_start || sl[s - 1].q_len != x.q_len;
         if (s > 0 && opens && sl[s - 1].q_start + sl[s - 1].q_len > x.q_start) bad = true;  // unsorted or overlapping
         if (!opens && sl[s - 1].k_start + sl[s - 1].k_len > x.k_start) bad = true;  // key ranges must ascend, disjoint
@@ -303,6 +307,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
         // the fragment's spans: this slice and the following ones on the same range
         const lb_mask_slice x = sl[s];
         Frag f{};
+#pragma unroll
+        for (int o = 0; o < LB_MAX_SPANS; ++o) f.k_lo[o] = LB_NO_LOWER_BOUND;
         f.q_start = x.q_start;
         f.q_len = x.q_len;
         f.q_pos0 = 0;
@@ -311,10 +317,16 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
           const lb_mask_slice y = sl[j];
           if (y.q_start != x.q_start || y.q_len != x.q_len) break;
           if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
-          const int pos0 = y.kind == LB_SLICE_CAUSAL ? y.q_len - y.k_len : kFullSpanPos;
+          // upper bound (bottom-right diagonal) for CAUSAL and BI-CAUSAL, lower bound (top-left
+          // diagonal: key j of the slice from row j on) for INV-CAUSAL and BI-CAUSAL
+          const bool upper = y.kind == LB_SLICE_CAUSAL || y.kind == LB_SLICE_BI_CAUSAL;
+          const bool lower = y.kind == LB_SLICE_INV_CAUSAL || y.kind == LB_SLICE_BI_CAUSAL;
+          const int pos0 = upper ? y.q_len - y.k_len : kFullSpanPos;
+          const int lo = lower ? 0 : LB_NO_LOWER_BOUND;
+          if (lower) sh.has_lower = 1;
 #pragma unroll
           for (int o = 0; o < LB_MAX_SPANS; ++o)
-            if (o == ns) { f.k_start[o] = y.k_start; f.k_len[o] = y.k_len; f.k_pos0[o] = pos0; }
+            if (o == ns) { f.k_start[o] = y.k_start; f.k_len[o] = y.k_len; f.k_pos0[o] = pos0; f.k_lo[o] = lo; }
           ++ns;
         }
         f.n_spans = ns;
@@ -347,6 +359,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
         const int s = frags[r].q_start;
         const int e = r + 1 < n_frags ? frags[r + 1].q_start : n_t;
         Frag f{};
+#pragma unroll
+        for (int o = 0; o < LB_MAX_SPANS; ++o) f.k_lo[o] = LB_NO_LOWER_BOUND;
         f.q_start = s;
         f.q_len = e - s;
         f.q_pos0 = t_pos[s];
@@ -411,6 +425,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       const Frag f = n_frags <= kLdsFrags ? lds_frags[lo] : frags[lo];
       const int kt = t - lds_ftile[lo];
       lb_plan_tile T{};
+#pragma unroll
+      for (int o = 0; o < LB_MAX_SPANS; ++o) T.k_lo[o] = LB_NO_LOWER_BOUND;
       T.q_start = f.q_start + kt * bm;
       T.q_len = min(bm, f.q_len - kt * bm);
       T.q_pos0 = f.q_pos0 + kt * bm;
@@ -420,18 +436,30 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
 #pragma unroll
       for (int sp = 0; sp < LB_MAX_SPANS; ++sp) {
         if (sp >= f.n_spans) break;
-        // forward: keys up to the tile's last row; transposed: query rows from the tile's
-        // first key on (c rows of the span see none of the tile's keys)
-        const int c = a.transposed ? max(0, T.q_pos0 - f.k_pos0[sp]) : 0;
-        const int keep = a.transposed ? f.k_len[sp] - c : min(f.k_len[sp], last - f.k_pos0[sp] + 1);
+        // forward: keys below the lower bound of the tile's first row dropped, then keys up
+        // to the tile's last row kept; transposed: query rows from the tile's first key on
+        // (c rows of the span see none of the tile's keys)
+        const int lo0 = f.k_lo[sp];
+        const int c = a.transposed ? max(0, T.q_pos0 - f.k_pos0[sp])
+                                   : (lo0 == LB_NO_LOWER_BOUND ? 0 : min(f.k_len[sp], max(0, T.q_pos0 - lo0)));
+        const int keep = a.transposed ? f.k_len[sp] - c : min(f.k_len[sp] - c, last - (f.k_pos0[sp] + c) + 1);
         if (keep <= 0) continue;
         const int s_start = f.k_start[sp] + c, s_pos0 = f.k_pos0[sp] + c;
+        const int s_lo = lo0 == LB_NO_LOWER_BOUND ? lo0 : lo0 + c;
 #pragma unroll
         for (int o = 0; o <= sp; ++o)  // slot ns <= sp, selected so T stays in registers
-          if (o == ns) { T.k_start[o] = s_start; T.k_len[o] = keep; T.k_pos0[o] = s_pos0; }
+          if (o == ns) { T.k_start[o] = s_start; T.k_len[o] = keep; T.k_pos0[o] = s_pos0; T.k_lo[o] = s_lo; }
         // visible pairs: a key at position x and a query at position y with x <= y; the
-        // count is the same whichever side is the tile
-        cost += a.transposed ? span_pairs(s_pos0, keep, T.q_pos0, T.q_len) : span_pairs(T.q_pos0, T.q_len, s_pos0, keep);
+        // count is the same whichever side is the tile.  A lower bound removes, for each row
+        // at position y, the keys j with s_lo + j < y: sum over rows of clamp(y - s_lo, 0, keep).
+        int64_t pairs = a.transposed ? span_pairs(s_pos0, keep, T.q_pos0, T.q_len)
+                                     : span_pairs(T.q_pos0, T.q_len, s_pos0, keep);
+        // (when s_pos0 > s_lo + 1 the band is empty for every row)
+        if (s_lo != LB_NO_LOWER_BOUND)
+          pairs = s_pos0 > s_lo + 1 ? 0
+                                    : pairs - (clamp_prefix((int64_t)T.q_pos0 - s_lo + T.q_len, keep) -
+                                               clamp_prefix((int64_t)T.q_pos0 - s_lo, keep));
+        cost += pairs;
         blocks += (keep + kBlockN - 1) / kBlockN;
         ++ns;
       }
@@ -490,6 +518,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     hdr->cap_tiles = a.L.cap_tiles;
     hdr->total_pairs = ok ? (int64_t)sh.pairs : 0;
     hdr->transposed = a.transposed;
+    hdr->has_lower = ok ? sh.has_lower : 0;
     const bool pair_sides = a.mode == kPlanBlock || a.mode == kPlanSlices;
     hdr->plan_n_q = pair_sides ? a.n_q : a.total_tokens;
     hdr->plan_n_kv = pair_sides ? a.n_kv : a.total_tokens;

@@ -117,8 +117,17 @@ def visible_in_span(row_pos, k_len, k_pos0):
     return max(0, min(k_len, row_pos - k_pos0 + 1))
 
 
+def visible_in_span_lo(row_pos, k_len, k_pos0, k_lo):
+    """Keys of a span visible to one query with both bounds: k_pos0 + j <= row_pos <= k_lo + j."""
+    return sum(1 for j in range(k_len) if k_pos0 + j <= row_pos <= k_lo + j)
+
+
 def tiles(frags, bm):
-    """Tiles in natural order: dicts with q_start, q_len, q_pos0, spans, cost."""
+    """Tiles in natural order: dicts with q_start, q_len, q_pos0, spans, cost.
+
+    A span with a lower bound, (k_start, k_len, k_pos0, k_lo), first loses the keys below
+    the bound of the tile's first row (k_lo + j < first position: no row of the tile sees
+    them), then is clipped like the others."""
     out = []
     for (qs, ql, qp0, spans) in frags:
         for t0 in range(0, ql, bm):
@@ -126,15 +135,20 @@ def tiles(frags, bm):
             p0 = qp0 + t0
             last = p0 + n - 1
             kept = []
-            for (ks, kl, kp0) in spans:
+            for sp in spans:
+                ks, kl, kp0 = sp[:3]
+                if len(sp) == 4:
+                    c = max(0, p0 - sp[3])
+                    ks, kl, kp0, klo = ks + c, kl - c, kp0 + c, sp[3] + c
                 keep = min(kl, last - kp0 + 1)
                 if keep > 0:
-                    kept.append((ks, keep, kp0))
+                    kept.append((ks, keep, kp0) if len(sp) == 3 else (ks, keep, kp0, klo))
             cost = 0
             for r in range(n):
-                for (ks, kl, kp0) in kept:
-                    cost += visible_in_span(p0 + r, kl, kp0)
-            blocks = sum(-(-kl // BLOCK_KEYS) for (ks, kl, kp0) in kept)
+                for sp in kept:
+                    cost += visible_in_span(p0 + r, sp[1], sp[2]) if len(sp) == 3 else \
+                        visible_in_span_lo(p0 + r, sp[1], sp[2], sp[3])
+            blocks = sum(-(-sp[1] // BLOCK_KEYS) for sp in kept)
             out.append(dict(q_start=qs + t0, q_len=n, q_pos0=p0, spans=kept, cost=cost, blocks=blocks))
     return out
 

@@ -4,17 +4,21 @@
 list of slices, each a query range, a key range and a mask type on that rectangle;
 the types are FULL, CAUSAL, INV-CAUSAL and BI-CAUSAL, and slices combine to express
 anything from varlen causal to varlen block-causal masks.  The mask of the list is
-the union of its slices' masks.  This module handles FULL and CAUSAL slices.
+the union of its slices' masks.
 
 Readings where the page is silent:
 * CAUSAL on a rectangle of Lq query rows and Lk keys is aligned at the bottom-right
   corner: row r (0-based in the slice) sees keys 0 .. r + (Lk - Lq) of the slice, so
   the last row sees every key (for Lq = Lk this is the usual causal triangle);
+* INV-CAUSAL is aligned at the top-left corner: row r sees keys r .. Lk - 1; BI-CAUSAL
+  is both at once, keys r .. r + (Lk - Lq) (a band; a sliding window of w keys over
+  rows q0.. is the BI-CAUSAL rectangle of those rows against keys q0 - w + 1 ..);
 * slices over the same query range must cover disjoint key ranges (the union is then
   a plain sum of their pairs), and two different query ranges must not overlap;
 * a query row covered by no slice sees nothing: lse = -inf, out = 0 here.
 
-A slice is (q_start, q_len, k_start, k_len, kind) with kind 0 = FULL, 1 = CAUSAL.
+A slice is (q_start, q_len, k_start, k_len, kind) with kind 0 = FULL, 1 = CAUSAL,
+2 = INV-CAUSAL, 3 = BI-CAUSAL.
 """
 from __future__ import annotations
 
@@ -24,8 +28,8 @@ import numpy as np
 
 from .attention import ROW_BLOCK, _as_f64, attend
 
-FULL, CAUSAL = 0, 1
-FAR = 1 << 30  # key position offset of a FULL span: below every query position
+FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL = 0, 1, 2, 3
+FAR = 1 << 30  # a bound offset that no position reaches: no bound on that side
 
 
 def visible(slices, n_q, n_k):
@@ -34,7 +38,11 @@ def visible(slices, n_q, n_k):
     for (qs, ql, ks, kl, kind) in slices:
         r = np.arange(ql)[:, None]
         c = np.arange(kl)[None, :]
-        blk = np.ones((ql, kl), dtype=bool) if kind == FULL else (c <= r + (kl - ql))
+        blk = np.ones((ql, kl), dtype=bool)
+        if kind in (CAUSAL, BI_CAUSAL):
+            blk &= c <= r + (kl - ql)
+        if kind in (INV_CAUSAL, BI_CAUSAL):
+            blk &= c >= r
         m[qs:qs + ql, ks:ks + kl] |= blk
     return m
 
@@ -62,12 +70,15 @@ def slices_attention(q, k, v, slices, heads, kv_heads, scale=None):
 
 def fragments(slices):
     """Planner fragments of a slice list (query ranges in order, each with the key spans of
-    its slices): (q_start, q_len, q_pos0, [(k_start, k_len, k_pos0), ...]) with query
-    positions from 0 in the range, so that key j of a span is visible to row r iff
-    k_pos0 + j <= r: a CAUSAL span starts at position q_len - k_len, a FULL one far below."""
+    its slices): (q_start, q_len, q_pos0, [span, ...]) with query positions from 0 in the
+    range.  A span (k_start, k_len, k_pos0) makes key j visible to row r iff
+    k_pos0 + j <= r: CAUSAL at k_pos0 = q_len - k_len, FULL far below.  Kinds with a lower
+    bound add k_lo, (k_start, k_len, k_pos0, k_lo), with key j visible only if k_lo + j >= r:
+    INV-CAUSAL (k_pos0 far below, k_lo = 0) and BI-CAUSAL (both)."""
     frags = []
     for (qs, ql, ks, kl, kind) in slices:
-        span = (ks, kl, (ql - kl) if kind == CAUSAL else -FAR)
+        hi = (ql - kl) if kind in (CAUSAL, BI_CAUSAL) else -FAR
+        span = (ks, kl, hi) if kind in (FULL, CAUSAL) else (ks, kl, hi, 0)
         if frags and frags[-1][0] == qs and frags[-1][1] == ql:
             frags[-1][3].append(span)
         else:
@@ -85,6 +96,30 @@ def block_causal_slices(lengths, frame):
         for f0 in range(0, n, frame):
             fl = min(frame, n - f0)
             out.append((start + f0, fl, start, f0 + fl, FULL))
+        start += n
+    return out
+
+
+def sliding_window_slices(lengths, window, rows=64):
+    """Per-document causal sliding window: row i of a document sees its keys i - window + 1
+    .. i.  Rows go in ranges of ``rows``; a range starting at q0 is the BI-CAUSAL band
+    against keys q0 - window + 1 .. q0 + rows - 1, cut at the document start (where it
+    becomes CAUSAL against keys 0 .. q0 + rows - 1 of the document, while q0 + rows - 1 <
+    window; the rows near the start see every earlier key)."""
+    out, start = [], 0
+    for n in lengths:
+        for q0 in range(0, n, rows):
+            ql = min(rows, n - q0)
+            k0 = q0 - window + 1
+            if k0 >= 0:
+                out.append((start + q0, ql, start + k0, ql + window - 1, BI_CAUSAL))
+            elif q0 + ql - 1 - window + 1 <= 0:  # no row of the range loses a key: plain causal
+                out.append((start + q0, ql, start, q0 + ql, CAUSAL))
+            else:  # mixed: row by row
+                for r in range(ql):
+                    i = q0 + r
+                    lo = max(0, i - window + 1)
+                    out.append((start + i, 1, start + lo, i - lo + 1, FULL))
         start += n
     return out
 

@@ -40,7 +40,9 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_struct_sizes_match_header(L):
-    assert ctypes.sizeof(lb.PlanTile) == 80
+    # the library asserts the same sizes (lbattn_internal.h): 96 and 40 bytes
+    assert ctypes.sizeof(lb.PlanTile) == 96
+    assert lb.PlanTile.k_lo.offset == lb.PlanTile.k_start.offset + 12 * lb.MAX_SPANS
     assert ctypes.sizeof(lb.WorkerRecord) == 40
 
 

@@ -88,7 +88,7 @@ def test_shared_question_as_slices():
 
 @pytest.mark.parametrize("seed", range(3))
 def test_random_slice_lists(seed):
-    """Rectangles of both kinds with unequal sides, several per query range, and query
+    """Rectangles of all four kinds with unequal sides, several per query range, and query
     ranges no slice covers (lse = -inf there)."""
     r = np.random.default_rng(50 + seed)
     n_q, n_k = 700, 520
@@ -102,7 +102,7 @@ def test_random_slice_lists(seed):
         bounds = [0] + cuts.tolist() + [n_k]
         picks = [(bounds[i], bounds[i + 1] - bounds[i]) for i in range(len(bounds) - 1) if r.random() < 0.6]
         for (ks, kl) in picks[:4]:
-            sl.append((q0, ql, ks, kl, int(r.integers(0, 2))))
+            sl.append((q0, ql, ks, kl, int(r.integers(0, 4))))
         q0 += ql
     H, Hkv, d = 4, 2, 64 if seed == 1 else 128
     (q, k, v), out, lse, ws = run(sl, n_q, n_k, H, Hkv, d, seed=seed)
@@ -124,3 +124,41 @@ def test_malformed_slice_lists_run_nothing(bad):
     torch.cuda.synchronize()
     assert lb.read_device_error(ws) & lb.DEVERR_SLICES
     assert torch.all(out == 3.0)
+
+
+@pytest.mark.parametrize("window", [1, 100, 4096])
+def test_sliding_window(window):
+    """The causal sliding window as slices (BI-CAUSAL bands) against the oracle; the plan,
+    spans with their lower bounds included, equals the oracle's bit for bit."""
+    lengths = [1500, 1, 700, 64]
+    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    sl = SL.sliding_window_slices(lengths, window)
+    (q, k, v), out, lse, ws = run(sl, T, T, H, Hkv, d, seed=window)
+    ref_o, ref_l = SL.slices_attention(q, k, v, sl, H, Hkv)
+    check(out, lse, ref_o, ref_l, f"sliding window {window}")
+    plan = lb.read_plan(ws)
+    t = OP.tiles(SL.fragments(sl), lb.tile_rows(H, Hkv, d))
+    ref = [t[i] for i in OP.lpt_order(t)]
+    assert [(a["q_start"], a["q_len"], a["q_pos0"], a["cost"], a["blocks"], [tuple(x) for x in a["spans"]]) for a in plan] \
+        == [(b["q_start"], b["q_len"], b["q_pos0"], b["cost"], b["blocks"], [tuple(x) for x in b["spans"]]) for b in ref]
+
+
+def test_plain_run_refuses_a_plan_with_lower_bounds():
+    """lb_attn_run keeps the key loop without a lower bound: given a plan with one it flags
+    LB_DEVERR_PLAN and writes nothing; lb_attn_run_lower runs it."""
+    H, Hkv, d, n = 4, 2, 128, 96
+    sl = [(0, 96, 0, 96, lb.SLICE_BI_CAUSAL)]
+    r = np.random.default_rng(3)
+    q, k, v = (dev_bf16(x) for x in workloads.values(r, n, H, Hkv, d))
+    ws = lb.plan_slices(sl, n, n, H, Hkv, d)
+    out = torch.full((n, H, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, n), 3.0, dtype=torch.float32, device="cuda")
+    lb.attn_run(q, k, v, out, lse, ws)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) & lb.DEVERR_PLAN
+    assert torch.all(out == 3.0) and torch.all(lse == 3.0)
+    ws = lb.plan_slices(sl, n, n, H, Hkv, d)
+    lb.attn_run_lower(q, k, v, out, lse, ws)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    assert torch.all(torch.isfinite(lse))  # the band keeps the diagonal: every row sees its own key

@@ -36,17 +36,21 @@ def test_shared_question_as_slices():
 
 
 @pytest.mark.parametrize("lq,lk,kind", [(9, 20, SL.CAUSAL), (20, 9, SL.CAUSAL), (13, 13, SL.CAUSAL),
-                                        (7, 30, SL.FULL)])
+                                        (7, 30, SL.FULL), (9, 20, SL.INV_CAUSAL), (20, 9, SL.INV_CAUSAL),
+                                        (9, 20, SL.BI_CAUSAL), (13, 13, SL.BI_CAUSAL)])
 def test_single_slice_against_sdpa(lq, lk, kind):
     """A CAUSAL rectangle is the lower triangle aligned at its bottom-right corner (row r sees
-    keys 0 .. r + lk - lq); FULL sees everything.  torch SDPA with that explicit mask."""
+    keys 0 .. r + lk - lq); INV-CAUSAL the upper one aligned at the top-left (keys r ..);
+    BI-CAUSAL both; FULL sees everything.  torch SDPA with that explicit mask."""
     r = np.random.default_rng(lq * 100 + lk)
     d = 16
     q, k, v = rand(r, lq, 1, d), rand(r, lk, 1, d), rand(r, lk, 1, d)
     o, lse = SL.slices_attention(q, k, v, [(0, lq, 0, lk, kind)], 1, 1)
     mask = torch.ones(lq, lk, dtype=torch.bool)
-    if kind == SL.CAUSAL:
+    if kind in (SL.CAUSAL, SL.BI_CAUSAL):
         mask = mask.tril(diagonal=lk - lq)
+    if kind in (SL.INV_CAUSAL, SL.BI_CAUSAL):
+        mask = mask.triu(diagonal=0)
     rows = mask.any(dim=1).numpy()
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.tensor(q[:, 0])[None], torch.tensor(k[:, 0])[None], torch.tensor(v[:, 0])[None], attn_mask=mask[None])
@@ -78,7 +82,7 @@ def random_slices(r, n_q, n_k):
         bounds = [0] + cuts.tolist() + [n_k]
         picks = [(bounds[i], bounds[i + 1] - bounds[i]) for i in range(len(bounds) - 1) if r.random() < 0.6]
         for (ks, kl) in picks[:4]:
-            out.append((q0, ql, ks, kl, int(r.integers(0, 2))))
+            out.append((q0, ql, ks, kl, int(r.integers(0, 4))))
         q0 += ql
     return out
 
@@ -95,10 +99,27 @@ def test_slice_tiles_count_every_pair_once(seed, bm):
     for t in tl:
         brute = 0
         for i in range(t["q_start"], t["q_start"] + t["q_len"]):
-            for (ks, kl, _) in t["spans"]:
+            for sp in t["spans"]:
+                ks, kl = sp[0], sp[1]
                 seen[i, ks:ks + kl] += V[i, ks:ks + kl]
                 brute += int(V[i, ks:ks + kl].sum())
         assert t["cost"] == brute
     # a span may keep keys its tile's first rows do not see, but no visible pair is missed
     # or counted twice
     assert np.array_equal(seen, V.astype(int))
+
+
+@pytest.mark.parametrize("window", [1, 5, 64, 100, 1000])
+def test_sliding_window_slices(window):
+    """The causal sliding window (row i sees keys i - window + 1 .. i of its document) as
+    slices equals the band written out directly, and its tiles count every pair once."""
+    lengths = [300, 1, 65, 129]
+    T = sum(lengths)
+    sl = SL.sliding_window_slices(lengths, window)
+    seg = np.repeat(np.arange(len(lengths)), lengths)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    band = (seg[:, None] == seg[None, :]) & (j <= i) & (j > i - window)
+    assert np.array_equal(SL.visible(sl, T, T), band)
+    tl = P.tiles(SL.fragments(sl), 64)
+    assert sum(t["cost"] for t in tl) == int(band.sum())
