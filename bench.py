@@ -270,6 +270,40 @@ class ZigzagStep:
         return self.lb.read_worker_timing(self.share.step_workspaces[0])
 
 
+class ZigzagBwdStep(ZigzagStep):
+    """The ring backward of the zigzag rank's share: D from the merged forward output, then
+    per step the block backward (dq added, the source chunk's partial dk, dv written).
+    Effective FLOPs 10 * d * H * pairs, 2.5x the forward's."""
+
+    def __init__(self, torch, lb, workloads, seed=0):
+        super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0)
+        sh = self.share
+        sh.run_planned()
+        r = np.random.default_rng(2001)
+        n_q = sh.q.shape[0]
+        self.dout = to_dev(workloads.f32_to_bf16_bits(r.standard_normal((n_q, self.H, self.d)).astype(np.float32)),
+                           torch)
+        sh.backward(self.dout)  # allocates the backward's buffers outside the timed region
+        torch.cuda.synchronize()
+        self.flops = 10 * self.d * self.H * self.pairs
+        self.kernel_name = "ring backward (D, then per step: plans, bwd_dq_kernel<128,1,true>, bwd_dkv_kernel<128,true>)"
+        self.graph = None
+
+    def n_launches(self):
+        return 1
+
+    def run(self, evs=None):
+        if evs is not None:
+            evs[0][0].record()
+            evs[0][1].record()
+        self.share.backward(self.dout)
+        if evs is not None:
+            evs[0][2].record()
+
+    def workers(self):
+        return self.lb.read_worker_timing(self.share.bwd_buffers["ws"][0])
+
+
 class CpJob:
     """Every rank's share of a context-parallel job at cp = 8 over the 131072-token pack,
     one after another on this GPU (each share replayed from its own HIP graph)."""
@@ -408,6 +442,14 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "tokens": p["tokens"], "documents": len(p["lengths"]), "heads": 32, "kv_heads": 8,
                     "head_dim": 128, "seed": seed, "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w
+    if name == "zigzag_bwd":
+        w = ZigzagBwdStep(torch, lb, workloads, seed=seed)
+        w.config = {"workload": "ring backward of one zigzag CP rank's share at cp=8: rank 3 of a 131072-token "
+                                f"lognormal pack (seed {seed}), 8 block-step backwards (dq accumulated, per-step "
+                                "partial dk, dv) after the forward's merged out and lse",
+                    "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
+                    "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
+        return w
     if name == "cp_job":
         w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap)
         w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
@@ -489,7 +531,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="longtail",
                     choices=["longtail", "pairA", "pairB", "zigzag", "shared_question", "tiny", "copy", "cp_job",
-                             "longtail_bwd", "blockcausal", "slidingwindow"])
+                             "longtail_bwd", "blockcausal", "slidingwindow", "zigzag_bwd"])
     ap.add_argument("--rule", default="per_document", choices=list(CP_RULES),
                     help="cp_job: how the pack is sharded over the ranks")
     ap.add_argument("--seed", type=int, default=0)

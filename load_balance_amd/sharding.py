@@ -389,6 +389,32 @@ class ShardedRank:
             lse_merge(self.out, self.lse, *self.overlap_buffers[t], stream=main)
         return self.out, self.lse
 
+    def backward(self, dout, stream=None):
+        """The rank's ring backward after a forward (run, run_planned, run_overlapped or a
+        replay) left out and lse: D = <dout, out> once, then per step the query shard's dq
+        contribution (added into one fp32 buffer, so the steps run in order) and the source
+        chunk's partial dk, dv, each in its own buffer -- what the rank would send back to
+        the chunk's owner ("03 · 长文负载均衡", section 4.4: partial key/value gradients are
+        reduced at the owning rank).  dout: bf16 [n_q, H, d] in the rank's token order.
+        Returns dq (fp32 [n_q, H, d]) and the list of per-step dkv (fp32 [2, n_kv, H_kv, d])."""
+        from . import attn_bwd_rowdot, block_attn_bwd
+        if getattr(self, "bwd_buffers", None) is None:
+            n_q, H, d = self.q.shape
+            ws_bytes = 2 * self.workspace.numel() + 512
+            self.bwd_buffers = dict(
+                dvec=torch.empty((H, n_q), dtype=torch.float32, device=self.q.device),
+                dq=torch.empty((n_q, H, d), dtype=torch.float32, device=self.q.device),
+                dkv=[torch.empty((2,) + tuple(st["kv"].shape[1:]), dtype=torch.float32, device=self.q.device)
+                     for st in self.steps],
+                ws=[torch.empty(ws_bytes, dtype=torch.uint8, device=self.q.device) for _ in self.steps])
+        b = self.bwd_buffers
+        attn_bwd_rowdot(self.out, dout, dvec=b["dvec"], stream=stream)
+        b["dq"].zero_()
+        for t, st in enumerate(self.steps):
+            block_attn_bwd(self.q, st["kv"], dout, self.lse, b["dvec"], self.q_pos, st["kv_pos"], self.q_doc,
+                           st["kv_doc"], b["dq"], dkv=b["dkv"][t], workspace=b["ws"][t], stream=stream)
+        return b["dq"], b["dkv"]
+
     def capture(self, stream=None, streams=None):
         """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
         merges -- or, given side streams, run_overlapped(), into a HIP graph, so that
