@@ -98,8 +98,8 @@ class VarlenStep:
     def plan_pairs(self):
         return sum(sum(t["cost"] for t in self.lb.read_plan(it["ws"])) for it in self.items)
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.items[-1]["ws"])
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.items[-1]["ws"]
 
 
 class VarlenBwdStep:
@@ -144,8 +144,8 @@ class VarlenBwdStep:
     def plan_pairs(self):
         return sum(t["cost"] for t in self.lb.read_plan(self.ws[self.key_plan:]))
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.ws[self.key_plan:])
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.ws[self.key_plan:]
 
 
 class SlicesStep:
@@ -191,8 +191,8 @@ class SlicesStep:
     def plan_pairs(self):
         return sum(t["cost"] for t in self.lb.read_plan(self.ws))
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.ws)
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.ws
 
 
 class ZigzagStep:
@@ -266,8 +266,8 @@ class ZigzagStep:
     def plan_pairs(self):
         return None
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.share.step_workspaces[0])
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.share.step_workspaces[0]
 
 
 class ZigzagBwdStep(ZigzagStep):
@@ -300,8 +300,8 @@ class ZigzagBwdStep(ZigzagStep):
         if evs is not None:
             evs[0][2].record()
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.share.bwd_buffers["ws"][0])
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.share.bwd_buffers["ws"][0]
 
 
 class CpJob:
@@ -347,8 +347,8 @@ class CpJob:
     def plan_pairs(self):
         return None
 
-    def workers(self):
-        return self.lb.read_worker_timing(self.shares[0].step_workspaces[0])
+    def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        return self.shares[0].step_workspaces[0]
 
 
 CP_RULES = ("zigzag", "per_document", "dispatch/16", "dispatch/32", "dispatch/64", "dispatch/128")
@@ -522,6 +522,14 @@ def cp_job_fields(w, per_launch):
 
 
 # ----------------------------------------------------------------------------------------
+def dump_worker_records(path, name, w, recs, lb):
+    """Per-workgroup busy ticks (100 MHz), pairs, key blocks and items of the last launch,
+    with the items of its plan in queue order (the input of ``load_balance_amd.fit_item_cost``)."""
+    plan = [dict(cost=int(t["cost"]), blocks=int(t["blocks"]), q_len=int(t["q_len"])) for t in lb.read_plan(w.worker_ws())]
+    with open(path, "w") as f:
+        json.dump({"workload": name, "config": w.config, "records": recs, "plan": plan}, f)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,6 +548,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
     ap.add_argument("--overlap", type=int, default=4,
                     help="zigzag, cp_job: streams the ring steps' attention launches are spread over (0: one)")
+    ap.add_argument("--worker-records", default=None, metavar="PATH",
+                    help="write the last launch's per-workgroup records and its plan (JSON) to PATH")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -601,7 +611,9 @@ def main():
                   for i in range(n_launch)]
     attn_ms_per_launch = attn_ms / n_launch
 
-    recs = w.workers()
+    recs = lb.read_worker_timing(w.worker_ws())
+    if args.worker_records:
+        dump_worker_records(args.worker_records, args.workload, w, recs, lb)
     busy = np.array([r["t_end"] - r["t_start"] for r in recs], dtype=np.float64)
     span_ticks = max(r["t_end"] for r in recs) - min(r["t_start"] for r in recs)
     cu_ratio = float(busy.max() / busy.mean()) if len(busy) and busy.mean() > 0 else None

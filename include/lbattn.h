@@ -124,7 +124,7 @@ typedef struct {
   uint64_t t_end;        /* ... and when it found the queue empty */
   int64_t pairs;         /* visible pairs x heads of the items it ran */
   int32_t items;         /* items it ran */
-  int32_t reserved;
+  int32_t blocks;        /* key blocks its items swept (query blocks, for the backward's key tiles) */
 } lb_worker_record;
 
 /* Query rows per tile for this head configuration (256 / (H / H_kv)); -1 if unsupported. */

@@ -53,7 +53,7 @@ class PlanTile(ctypes.Structure):
 class WorkerRecord(ctypes.Structure):
     _fields_ = [("hw_id", ctypes.c_uint32), ("xcc_id", ctypes.c_uint32), ("t_start", ctypes.c_uint64),
                 ("t_end", ctypes.c_uint64), ("pairs", ctypes.c_int64), ("items", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("blocks", ctypes.c_int32)]
 
 
 _lib = None
@@ -311,7 +311,7 @@ def read_worker_timing(workspace, max_records: int = 4096, stream=None):
     _check(lib().lb_read_worker_timing(_ptr(workspace), workspace.numel(), buf, max_records, ctypes.byref(n),
                                        ctypes.c_void_p(_stream(stream))), "lb_read_worker_timing")
     return [dict(hw_id=r.hw_id, xcc_id=r.xcc_id, t_start=r.t_start, t_end=r.t_end, pairs=r.pairs,
-                 items=r.items) for r in buf[:min(n.value, max_records)]]
+                 items=r.items, blocks=r.blocks) for r in buf[:min(n.value, max_records)]]
 
 
 # --------------------------------------------------------------------------

@@ -43,6 +43,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = kBlockN;
 constexpr int kStages = 3;  // LDS ring: the lagging waves still read block j-1 while block j+1 lands
+constexpr int kPairBits = 40;  // a workgroup's pairs stay below 2^40; its key blocks below 2^23
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -216,6 +217,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   uint64_t t_start = 0;
   if (tid == 0) t_start = device_clock();
   int my_items = 0;
+  // pairs in the low kPairBits, swept key blocks above them: one accumulator, so the
+  // per-item bookkeeping adds no live register across the key loop
   int64_t my_pairs = 0;
 
   KvLoader<D> ld;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       if (s < n_spans) n_kv_tiles += (__builtin_amdgcn_readlane(span_v, LB_MAX_SPANS + s) + BN - 1) / BN;
     if (tid == 0) {
       ++my_items;
-      my_pairs += T->cost * G;
+      my_pairs += T->cost * G + (static_cast<int64_t>(n_kv_tiles) << kPairBits);
     }
     auto span_of = [&](int s) {
       KvBlock b;
@@ -527,9 +530,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     rec.xcc_id = xcc_id_reg();
     rec.t_start = t_start;
     rec.t_end = device_clock();
-    rec.pairs = my_pairs;
+    rec.pairs = my_pairs & ((int64_t{1} << kPairBits) - 1);
     rec.items = my_items;
-    rec.reserved = 0;
+    rec.blocks = static_cast<int32_t>(my_pairs >> kPairBits);
     lb_worker_record* recs = reinterpret_cast<lb_worker_record*>(a.ws + kWorkersOffset);
     recs[blockIdx.x] = rec;
     if (blockIdx.x == 0) hdr->n_workers = gridDim.x;

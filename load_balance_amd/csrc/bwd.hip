@@ -122,7 +122,7 @@ struct Queues {
   }
 
   // The last workgroup out rewinds the queues (every pop has happened before it counts itself).
-  __device__ void close(const BwdArgs& a, uint64_t t_start, int items, int64_t pairs) {
+  __device__ void close(const BwdArgs& a, uint64_t t_start, int items, int64_t pairs, int blocks) {
     if (threadIdx.x != 0) return;
     lb_worker_record rec;
     rec.hw_id = hw_id_reg();
@@ -131,7 +131,7 @@ struct Queues {
     rec.t_end = device_clock();
     rec.pairs = pairs;
     rec.items = items;
-    rec.reserved = 0;
+    rec.blocks = blocks;
     reinterpret_cast<lb_worker_record*>(a.ws + kWorkersOffset)[blockIdx.x] = rec;
     if (blockIdx.x == 0) hdr->n_workers = gridDim.x;
     __threadfence();
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   Queues qs;
   qs.open(a, 0);
   uint64_t t_start = tid == 0 ? device_clock() : 0;
-  int my_items = 0;
+  int my_items = 0, my_blocks = 0;
   int64_t my_pairs = 0;
   DqLoader<D> ld;
 
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     int n_blocks = 0;
     for (int s = 0; s < n_spans; ++s) n_blocks += (span_of(T, s).len + BN - 1) / BN;
     if (tid == 0) {
+      my_blocks += n_blocks;
       ++my_items;
       my_pairs += T->cost * G;
     }
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     lds_barrier();
     item = __builtin_amdgcn_readfirstlane(s_item);
   }
-  qs.close(a, t_start, my_items, my_pairs);
+  qs.close(a, t_start, my_items, my_pairs, my_blocks);
 }
 
 // ------------------------------------------------------------------------------------
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   Queues qs;
   qs.open(a, 1);
   uint64_t t_start = tid == 0 ? device_clock() : 0;
-  int my_items = 0;
+  int my_items = 0, my_blocks = 0;
   int64_t my_pairs = 0;
 
   // key tiles no query row sees: zero gradients, a grid-stride pass before the queues
@@ -652,6 +653,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     // stages: for each span, each 64 rows, each head of the group
     int n_stages = 0;
     for (int s = 0; s < n_spans; ++s) n_stages += (span_of(T, s).len + kQB - 1) / kQB * G;
+    if (tid == 0) my_blocks += n_stages;
     int cur_s = 0, off = 0, hs = 0;
     Span cur = span_of(T, 0);
     if (n_stages > 0) {
@@ -770,7 +772,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     lds_barrier();
     item = __builtin_amdgcn_readfirstlane(s_item);
   }
-  qs.close(a, t_start, my_items, my_pairs);
+  qs.close(a, t_start, my_items, my_pairs, my_blocks);
 }
 
 }  // namespace

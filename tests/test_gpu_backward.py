@@ -101,6 +101,12 @@ def test_key_tile_plan_equals_oracle(mask):
             assert (a["q_start"], a["q_len"], a["q_pos0"], a["cost"], a["blocks"]) == \
                    (b["q_start"], b["q_len"], b["q_pos0"], b["cost"], b["blocks"]), (what, i)
             assert [tuple(s) for s in a["spans"]] == [tuple(s) for s in b["spans"]], (what, i)
+    # the workgroups' records account for every item: pairs per query head, and the blocks
+    # swept (dQ: 64-key blocks per kv head; dK/dV: 64-row query stages per query head)
+    for w, want, per in ((ws, ref_q, Hkv), (ws[off:], ref_k, H)):
+        recs = lb.read_worker_timing(w)
+        assert sum(x["pairs"] for x in recs) == H * sum(t["cost"] for t in want)
+        assert sum(x["blocks"] for x in recs) == per * sum(t["blocks"] for t in want)
 
 
 def test_single_token_documents():

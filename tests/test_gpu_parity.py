@@ -154,8 +154,10 @@ def test_longtail_pack(longtail):
     check(out[rows].float().cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "32K long-tail (sampled)")
     recs = lb.read_worker_timing(ws)
     assert len(recs) == torch.cuda.get_device_properties(0).multi_processor_count
-    assert sum(x["items"] for x in recs) == len(lb.read_plan(ws)) * 8
+    plan = lb.read_plan(ws)
+    assert sum(x["items"] for x in recs) == len(plan) * 8
     assert sum(x["pairs"] for x in recs) == 32 * 49_322_947
+    assert sum(x["blocks"] for x in recs) == 8 * sum(t["blocks"] for t in plan)
 
 
 def test_longtail_is_deterministic(longtail):
