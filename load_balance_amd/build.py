@@ -33,8 +33,11 @@ def hipcc() -> str:
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 # The attention kernel is scheduled with the iterative ILP strategy: the default one keeps
-# a single LDS read in flight ahead of the QK^T MFMAs in its key loop.
-EXTRA = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# a single LDS read in flight ahead of the QK^T MFMAs in its key loop.  Its atomics are all
+# issued by one lane, and the atomic optimizer's wave-wide rewrite would make that lane wait
+# for the result (and every load before it) at once instead of where it is used.
+EXTRA = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
+                          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 OBJ_DIR = os.path.join(PKG, "_build")
 
 

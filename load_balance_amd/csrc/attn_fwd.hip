@@ -59,17 +59,21 @@ struct Lds {
   static constexpr int vUnits = (BN / 2) * (D / 8);  // (key pair, 8-wide d chunk) units of a V block
 };
 
-// Output staging for the epilogue: each wave's rows, row-major, in 1/8 of the LDS ring;
-// two passes of 16 rows where 32 rows do not fit.
+// Output staging for the epilogue: each wave's rows, row-major, in 1/8 of the ring's stages
+// 1 .. kStages-1 (stage 0 receives the next item's first key block meanwhile), in as many
+// passes (32, 16 or 8 rows each) as that space requires.
 template <int D, bool OUT_F32>
 struct EpilogueLds {
   static constexpr int kRowBytes = D * (OUT_F32 ? 4 : 2);
   static constexpr int kStride = kRowBytes + 16;
   static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kWaveBytes = (kStages * Lds<D>::stage / kWaves) & ~15;
-  static constexpr int kPasses = 32 * kStride <= kWaveBytes ? 1 : 2;
-  static constexpr int kRows = 32 / kPasses;
-  static_assert(kRows * kStride <= kWaveBytes, "epilogue staging does not fit in the ring");
+  static constexpr int kBase = Lds<D>::stage;
+  static constexpr int kSpace = ((kStages - 1) * Lds<D>::stage / kWaves) & ~15;
+  static constexpr int kRows = 32 * kStride <= kSpace ? 32 : 16 * kStride <= kSpace ? 16 : 8;
+  static constexpr int kPasses = 32 / kRows;
+  static constexpr int kWaveBytes = kSpace;
+  static_assert(kRows * kStride <= kSpace, "epilogue staging does not fit in the ring");
+  static_assert(64 % kChunks == 0 && kRows % (64 / kChunks) == 0, "whole rows per store step");
 };
 
 // V^T keeps keys permuted inside each group of 16 so that the 8 keys one lane feeds to
@@ -95,6 +99,7 @@ __device__ __forceinline__ uint32_t xcc_id_reg() { return __builtin_amdgcn_s_get
 
 // Raw buffer resource word 3 for gfx9-family dword loads (no format conversion).
 constexpr int kBufferFlags = 0x00020000;
+
 
 template <int D>
 struct KvLoader {
@@ -172,6 +177,15 @@ template <int D, bool OUT_F32, bool LOWER>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
   __shared__ int s_item;
+  // Thread 0's bookkeeping (queue state, counts for the worker record) lives in LDS, so that
+  // it holds no register through the key loop.
+  __shared__ struct {
+    uint64_t t_start;
+    int64_t pairs;  // visible pairs in the low kPairBits, key blocks swept above them
+    int items;
+    int queue;      // the queue this workgroup pops from
+    int dry;        // every queue found empty
+  } s_pop;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -214,12 +228,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const float c = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  uint64_t t_start = 0;
-  if (tid == 0) t_start = device_clock();
-  int my_items = 0;
-  // pairs in the low kPairBits, swept key blocks above them: one accumulator, so the
-  // per-item bookkeeping adds no live register across the key loop
-  int64_t my_pairs = 0;
+  if (tid == 0) {
+    s_pop.t_start = device_clock();
+    s_pop.pairs = 0;
+    s_pop.items = 0;
+  }
 
   KvLoader<D> ld;
   ld.init(row_bytes, tid);
@@ -242,15 +255,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int n_queues = mismatch ? 1 : hdr->n_queues;
   const int per_queue = mismatch ? 0 : hdr->per_queue;
   const int heads_per_queue = a.kv_heads / n_queues;
-  int queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
-  bool queues_dry = n_items == 0;  // kept by thread 0 only
+  if (tid == 0) {
+    s_pop.queue = (int)(xcc_id_reg() % (uint32_t)n_queues);
+    s_pop.dry = n_items == 0;
+  }
 
   // Thread 0: completes a pop whose atomicAdd on the current queue returned k.  A dry queue
   // sends it on to the next queue in rotation that still holds items, judged from one read
   // of every queue head (another workgroup may still empty that queue first).
   auto finish_pop = [&](int k) -> int {
+    int queue = s_pop.queue, item = -1;
+    bool queues_dry = s_pop.dry != 0;
     while (!queues_dry) {
-      if (k < per_queue) return queue * per_queue + k;
+      if (k < per_queue) {
+        item = queue * per_queue + k;
+        break;
+      }
       int heads[kXcds];
 #pragma unroll
       for (int q = 0; q < kXcds; ++q)
@@ -264,11 +284,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       queue = next;
       k = atomicAdd(&hdr->queue_head[queue], 1);
     }
-    return -1;
+    s_pop.queue = queue;
+    s_pop.dry = queues_dry;
+    return item;
   };
-  if (tid == 0) s_item = queues_dry ? -1 : finish_pop(atomicAdd(&hdr->queue_head[queue], 1));
+  // thread 0: the first step of a pop, or -1 with the queues dry
+  auto start_pop = [&]() -> int { return s_pop.dry ? -1 : atomicAdd(&hdr->queue_head[s_pop.queue], 1); };
+  if (tid == 0) {
+    const int k = start_pop();
+    s_item = k < 0 ? -1 : finish_pop(k);
+  }
   lds_barrier();
   int qitem = __builtin_amdgcn_readfirstlane(s_item);
+  lds_barrier();  // every wave has read s_item before thread 0 writes it again
+
+  // The loads an item starts with, issued during the previous item's epilogue so that their
+  // latency hides behind it: this wave's Q fragment (B operand of S^T = K Q^T; lane holds
+  // Q[q = l32][d = kk*16 + hh*8 .. +8], zeros past the tile's end) and the first key block
+  // into the loader's registers.
+  bf16x8 qreg[D / 16];
+  auto issue_item_loads = [&](int item) {
+    const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
+    const int g = q_of + n_queues * (k_in % heads_per_queue);
+    const lb_plan_tile* T = &tiles[order[k_in / heads_per_queue]];
+    const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
+    const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
+    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    const int k_start0 = __builtin_amdgcn_readfirstlane(T->k_start[0]);
+    const int k_len0 = __builtin_amdgcn_readfirstlane(T->k_len[0]);
+    // one buffer over this wave's rows of the tile: no branches (a branch around a load
+    // makes the compiler wait for every load before it), zeros past the tile's end
+    const int head = __builtin_amdgcn_readfirstlane(g * G + head_in_group);
+    const int w0 = __builtin_amdgcn_readfirstlane(wr0);
+    const int q_row_bytes = a.heads * D * 2;
+    const int rows = n_spans > 0 ? min(max(q_len - w0, 0), kRowsPerWave) : 0;
+    const uint64_t q_off = ((uint64_t)(q_start + w0) * a.heads + head) * D * 2;
+    const uint64_t q_off_u = (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)q_off) |
+                             ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(q_off >> 32)) << 32);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(Q) + q_off_u), (short)0,
+                                          __builtin_amdgcn_readfirstlane(rows * q_row_bytes), kBufferFlags);
+    const int voff = l32 * q_row_bytes + hh * 16;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
+    if (n_spans > 0) ld.load(Kb, Vb, k_start0, k_len0, row_bytes, g, tid);
+  };
+  // Items are popped one ahead of the one whose loads go out: thread 0 issues the atomic in
+  // an item's epilogue and completes the pop at the next item's start, so the round trip
+  // sits on no wave's path.  s_item then holds the item after the one being run.
+  int k_after = -1;  // thread 0: that atomic's result, or -1 with the queues dry
+  if (qitem >= 0) {
+    issue_item_loads(qitem);
+    if (tid == 0) k_after = start_pop();
+  }
 
   while (qitem >= 0) {
 
@@ -289,8 +358,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     for (int s = 0; s < LB_MAX_SPANS; ++s)
       if (s < n_spans) n_kv_tiles += (__builtin_amdgcn_readlane(span_v, LB_MAX_SPANS + s) + BN - 1) / BN;
     if (tid == 0) {
-      ++my_items;
-      my_pairs += T->cost * G + (static_cast<int64_t>(n_kv_tiles) << kPairBits);
+      ++s_pop.items;
+      s_pop.pairs += T->cost * G + (static_cast<int64_t>(n_kv_tiles) << kPairBits);
+      s_item = k_after < 0 ? -1 : finish_pop(k_after);
     }
     auto span_of = [&](int s) {
       KvBlock b;
@@ -309,15 +379,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     const int64_t grow = (int64_t)q_start + my_row;
     const int qpos = q_pos0 + my_row;
 
-    // Q fragment: B operand of S^T = K Q^T; lane holds Q[q = l32][d = kk*16 + hh*8 .. +8].
-    bf16x8 qreg[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (n_kv_tiles > 0 && wave_rows && my_row < q_len)  // an item with no keys only writes lse
-        x = *reinterpret_cast<const u32x4*>(Q + (grow * a.heads + head) * D + kk * 16 + hh * 8);
-      qreg[kk] = __builtin_bit_cast(bf16x8, x);
-    }
 
     f32x16 acc_o[D / 32];
 #pragma unroll
@@ -389,38 +450,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
           for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
       }
       const float m_sub = m_used == -__builtin_inff() ? 0.0f : m_used;
+      // P^T in bf16, chunk ks16 = keys ks16*16 .. +16 of the block (S^T rows acc_s[ks16 / 2],
+      // elements (ks16 % 2) * 8 ..): pairs [p0, p1) of its four
       bf16x8 pf[4];
+      auto exp_pairs = [&](int ks16, int p0, int p1) {
+        const int kb = ks16 / 2, cc = ks16 % 2;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j], c, -m_sub));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j + 1], c, -m_sub));
-            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            // the row sum takes exactly the bf16 weights that enter the PV product
-            l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
-            pf[kb * 2 + cc][j] = pp[0];
-            pf[kb * 2 + cc][j + 1] = pp[1];
-          }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int ks16 = 0; ks16 < 4; ++ks16) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks16], acc_o[db], 0, 0, 0);
+        for (int p = p0; p < p1; ++p) {
+          const int j = 2 * p;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j], c, -m_sub));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j + 1], c, -m_sub));
+          const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
+          // the row sum takes exactly the bf16 weights that enter the PV product
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
+          pf[ks16][j] = pp[0];
+          pf[ks16][j + 1] = pp[1];
         }
+      };
+      constexpr int kDb = D / 32;             // 32-wide d blocks of O^T
+      constexpr int kPairsPerMfma = 4 / kDb;  // exponential pairs of the next chunk per MFMA
+      auto read_v = [&](int ks16, bf16x8* dst) {
+#pragma unroll
+        for (int db = 0; db < kDb; ++db)
+          dst[db] = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
+      };
+      // An explicit pipeline, fenced so that the scheduler keeps it whatever surrounds the
+      // loop: the MFMAs of chunk ks run with the exponentials of chunk ks + 1 between them,
+      // while the V^T fragments of chunk ks + 2 are read.
+      bf16x8 vf[2][kDb];
+      read_v(0, vf[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      exp_pairs(0, 0, 4);
+      read_v(1, vf[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int db = 0; db < kDb; ++db) {
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks & 1][db], pf[ks], acc_o[db], 0, 0, 0);
+          if (ks + 1 < 4) exp_pairs(ks + 1, db * kPairsPerMfma, (db + 1) * kPairsPerMfma);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ks + 2 < 4) read_v(ks + 2, vf[ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
 
-    // prologue: first key block into stage 0 (spans in the plan are never empty)
+    // prologue: first key block (loaded during the previous epilogue) into stage 0; spans in
+    // the plan are never empty.  The key loop's first barrier also ends every wave's Q
+    // staging read before the ring's stage 1 is written.
     int cur_s = 0;
     KvBlock cur = span_of(0);
-    if (n_kv_tiles > 0) {
-      ld.load(Kb, Vb, cur.start, cur.len, row_bytes, g, tid);
-      ld.store(smem, tid);
-    }
+    if (n_kv_tiles > 0) ld.store(smem, tid);
     KvBlock prev{0, 0, 0, 0, LB_NO_LOWER_BOUND};
     bool prev_live = false;
 
@@ -458,11 +539,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
 
     // ---- epilogue: out = O / l, lse = ln(sum exp) ----
-    // Every wave is done with the LDS ring after this barrier; thread 0 starts the next pop
-    // here and collects it after the LDS part of the epilogue, before any global store of it.
+    // Every wave is done with the LDS ring after this barrier, and the next item's number is
+    // in s_item: its loads go out first, then thread 0's atomic for the item after it.
     lds_barrier();
-    int k_next = 0;
-    if (tid == 0 && !queues_dry) k_next = atomicAdd(&hdr->queue_head[queue], 1);
+    const int next_item = __builtin_amdgcn_readfirstlane(s_item);
+    if (next_item >= 0) {
+      issue_item_loads(next_item);
+      if (tid == 0) k_after = start_pop();
+    }
     const float l_tot = l_part + __shfl_xor(l_part, 32);
     const bool row_real = wave_rows && my_row < q_len;
     const bool empty = !(l_tot > 0.0f);
@@ -478,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     int t_e = tid;
     asm volatile("" : "+v"(t_e));
     const int lane_e = t_e & 63, l32_e = t_e & 31;
-    char* ebuf = smem + (t_e >> 6) * Epi::kWaveBytes;
+    char* ebuf = smem + Epi::kBase + (t_e >> 6) * Epi::kWaveBytes;
 #pragma unroll
     for (int pass = 0; pass < Epi::kPasses; ++pass) {
       const int r_lo = pass * Epi::kRows;
@@ -503,7 +587,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
             }
           }
       }
-      if (pass == 0 && tid == 0) s_item = finish_pop(k_next);
       if (pass == 0 && row_real && hh == 0)
         a.lse[(int64_t)head * a.n_q + grow] = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
       // LDS instructions of one wave complete in order: the reads below see the writes above.
@@ -520,19 +603,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         if (wmask >> (r_lo + row0 + j * kRowsPerStep) & 1) *reinterpret_cast<u32x4*>(dst + j * dst_step) = x;
       }
     }
-    lds_barrier();  // s_item is written; the ring is free again for the next item's first block
-    qitem = __builtin_amdgcn_readfirstlane(s_item);
+    lds_barrier();  // every wave has read s_item before thread 0 writes it again
+    qitem = next_item;
   }
 
   if (tid == 0) {
     lb_worker_record rec;
     rec.hw_id = hw_id_reg();
     rec.xcc_id = xcc_id_reg();
-    rec.t_start = t_start;
+    rec.t_start = s_pop.t_start;
     rec.t_end = device_clock();
-    rec.pairs = my_pairs & ((int64_t{1} << kPairBits) - 1);
-    rec.items = my_items;
-    rec.blocks = static_cast<int32_t>(my_pairs >> kPairBits);
+    rec.pairs = s_pop.pairs & ((int64_t{1} << kPairBits) - 1);
+    rec.items = s_pop.items;
+    rec.blocks = static_cast<int32_t>(s_pop.pairs >> kPairBits);
     lb_worker_record* recs = reinterpret_cast<lb_worker_record*>(a.ws + kWorkersOffset);
     recs[blockIdx.x] = rec;
     if (blockIdx.x == 0) hdr->n_workers = gridDim.x;
