@@ -84,6 +84,17 @@ __device__ __forceinline__ int vt_pos(int key) {
 
 __device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
+// The two halves of a wave hold the same query rows (lanes r and r + 32): the value of the
+// lane 32 apart through v_permlane32_swap, a VALU exchange, rather than an LDS permute.  The
+// swap leaves the partner's value in its first result on the upper half and in its second on
+// the lower half.  (Combined directly, as op(first, second), the compiler folds the two
+// results of a swap of one value into one.)
+__device__ __forceinline__ float partner_lane(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+}
+
 // Workgroup barrier that orders LDS only.  The waves of a workgroup share nothing through
 // global memory here, and __syncthreads() would also wait for every outstanding global
 // store (the previous item's output) to complete.
@@ -431,12 +442,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
               if (!(kb * 32 + (i / 4) * 8 + (i % 4) < lim)) acc_s[kb][i] = -__builtin_inff();
         }
       }
-      float mx = -__builtin_inff();
+      // row max as a tree of 3-input maxima (depth 4, not a chain of 16)
+      float t[11];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = 0; i < 10; ++i) {
+        const int e = 3 * i;
+        t[i] = fmaxf(fmaxf(acc_s[e / 16][e % 16], acc_s[(e + 1) / 16][(e + 1) % 16]), acc_s[(e + 2) / 16][(e + 2) % 16]);
+      }
+      t[10] = fmaxf(acc_s[1][14], acc_s[1][15]);
+      const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+      const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+      const float m_own = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+      const float mx = fmaxf(m_own, partner_lane(m_own, lane));
       const float m_tile = mx * c;
       const bool need = m_tile > m_used + kRescaleThreshold;  // false when the row saw nothing
       if (__any(need)) {
@@ -453,6 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       // P^T in bf16, chunk ks16 = keys ks16*16 .. +16 of the block (S^T rows acc_s[ks16 / 2],
       // elements (ks16 % 2) * 8 ..): pairs [p0, p1) of its four
       bf16x8 pf[4];
+      float lsum[2] = {0.0f, 0.0f};  // this block's row sum, in two chains
       auto exp_pairs = [&](int ks16, int p0, int p1) {
         const int kb = ks16 / 2, cc = ks16 % 2;
 #pragma unroll
@@ -462,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][cc * 8 + j + 1], c, -m_sub));
           const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
           // the row sum takes exactly the bf16 weights that enter the PV product
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_part, false);
+          lsum[ks16 & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[ks16 & 1], false);
           pf[ks16][j] = pp[0];
           pf[ks16][j + 1] = pp[1];
         }
@@ -494,6 +512,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         if (ks + 2 < 4) read_v(ks + 2, vf[ks & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      l_part += lsum[0] + lsum[1];
     };
 
     // prologue: first key block (loaded during the previous epilogue) into stage 0; spans in
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       issue_item_loads(next_item);
       if (tid == 0) k_after = start_pop();
     }
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    const float l_tot = l_part + partner_lane(l_part, lane);
     const bool row_real = wave_rows && my_row < q_len;
     const bool empty = !(l_tot > 0.0f);
     // rows written: bit r for tile row wr0 + r (lanes r and r + 32 hold the same row)
