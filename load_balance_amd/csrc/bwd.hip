@@ -28,6 +28,14 @@
 namespace lb {
 namespace {
 
+// compile-time flag for code written once for the masked and the mask-free path: a block
+// fully visible to the wave takes the path without a compare per element
+template <bool B>
+struct Masked {
+  static constexpr bool value = B;
+};
+
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -432,17 +440,21 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
               dp[kb] = mfma(vf, doreg[e][kk], dp[kb]);
             }
           bf16x8 dsf[4];
+          auto make_ds = [&](auto masked) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+              for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const int i = cc * 8 + j;
-                const bool vis = full || (kb * 32 + (i / 4) * 8 + (i % 4) < lim);
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -lse2[e])) : 0.f;
-                dsf[kb * 2 + cc][j] = (__bf16)(p * (dp[kb][i] - dvv[e]));
-              }
+                for (int j = 0; j < 8; ++j) {
+                  const int i = cc * 8 + j;
+                  const bool vis = !decltype(masked)::value || (kb * 32 + (i / 4) * 8 + (i % 4) < lim);
+                  const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -lse2[e])) : 0.f;
+                  dsf[kb * 2 + cc][j] = (__bf16)(p * (dp[kb][i] - dvv[e]));
+                }
+          };
+          if (full) make_ds(Masked<false>{});
+          else make_ds(Masked<true>{});
 #pragma unroll
           for (int ks16 = 0; ks16 < 4; ++ks16)
 #pragma unroll
@@ -707,18 +719,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
             dp = mfma(*reinterpret_cast<const bf16x8*>(dorows + (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2),
                       vfr[kk], dp);
           bf16x8 dsf[2];
+          auto make_ds = [&](auto masked) {
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
-            const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
+              const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = i4 * 4 + j;
-              const bool vis = full || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
-              const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
-              dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
+              for (int j = 0; j < 4; ++j) {
+                const int i = i4 * 4 + j;
+                const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
+                dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
+              }
             }
-          }
+          };
+          if (full) make_ds(Masked<false>{});
+          else make_ds(Masked<true>{});
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -728,16 +744,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
                              dsf[ks], acc[db]);
         } else {
           bf16x8 pf[2];
+          auto make_p = [&](auto masked) {
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = i4 * 4 + j;
-              const bool vis = full || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
-              pf[i / 8][i % 8] = (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f);
+              for (int j = 0; j < 4; ++j) {
+                const int i = i4 * 4 + j;
+                const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
+                pf[i / 8][i % 8] = (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f);
+              }
             }
-          }
+          };
+          if (full) make_p(Masked<false>{});
+          else make_p(Masked<true>{});
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
