@@ -635,6 +635,7 @@ def main():
         "data": "synthetic",
         "config": dict(w.config, pairs_per_head=w.pairs, effective_flops=w.flops),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_bf16_peak_at_2400mhz": round(100 * value / PEAK_BF16_AT_2400MHZ, 2),
         "kernels_ms": {"plan": round(plan_ms, 4), "attention": round(attn_ms, 4)},
         "kernels_ms_per_launch": per_launch if n_launch > 1 else None,
         "eager_ms_per_step": None if eager_ms_per_step is None else round(eager_ms_per_step, 4),
