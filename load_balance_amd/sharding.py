@@ -279,6 +279,12 @@ def build_shards(lengths, tokens, get_rows, device="cuda"):
     return shards
 
 
+def live_steps(q_pos, q_doc, kv_sides):
+    """Indices of the (kv_pos, kv_doc) sides with at least one key some query row sees:
+    the planner's work items for them are not all empty."""
+    return [t for t, (kp, kd) in enumerate(kv_sides) if predicted_work(q_pos, q_doc, kp, kd, 64)[1] > 0]
+
+
 class ShardedRank:
     """One rank's cp ring steps over device-resident shards (see ``build_shards``).
 
@@ -286,6 +292,12 @@ class ShardedRank:
     in one launch first; run_overlapped() also lets the steps' attention launches overlap;
     capture()/replay() record either in a HIP graph.  Results are out (fp32 [n_q,H,d]) and
     lse ([H,n_q]) of the rank's tokens, in their order.
+
+    A step whose chunk holds no key any of the rank's rows sees (judged on the host from the
+    positions and document ids, which the sharding fixes before any data moves: the same
+    tile count as the planner's, ``predicted_work``) runs nothing: no plan, no attention
+    launch, no merge.  Merging it would change no bit (a partial whose lse is -inf leaves
+    the running result as it is), so ``live_steps`` lists the steps that run.
     """
 
     def __init__(self, shards, rank, device="cuda"):
@@ -312,15 +324,26 @@ class ShardedRank:
                    [len(_runs(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy())) for s in self.steps])
         self._ws_shape = (n_max, max(1, runs), H, Hkv, device)
         self.workspace = new_workspace(*self._ws_shape)
+        self.live_steps = live_steps(self.q_pos.cpu().numpy(), self.q_doc.cpu().numpy(),
+                                     [(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy()) for s in self.steps])
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None
 
+    def _no_live_step(self):
+        """The result when no step has a visible pair: every row sees nothing."""
+        self.out.zero_()
+        self.lse.fill_(-float("inf"))
+        return self.out, self.lse
+
     def run(self, stream=None, per_step=None):
-        """All cp steps, each a block_attn_fwd, plus cp - 1 merges."""
+        """Every live step, each a block_attn_fwd, and a merge for each after the first."""
         from . import block_attn_fwd, lse_merge
-        for t, st in enumerate(self.steps):
-            first = t == 0
+        if not self.live_steps:
+            return self._no_live_step()
+        for i, t in enumerate(self.live_steps):
+            st = self.steps[t]
+            first = i == 0
             out = self.out if first else self.step_out
             lse = self.lse if first else self.step_lse
             block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
@@ -332,23 +355,31 @@ class ShardedRank:
         return self.out, self.lse
 
     def plan_all(self, stream=None):
-        """Plans every ring step in one launch, one workspace per step: a step's key/value
-        positions and document ids follow from the sharding, before its data arrive."""
+        """Plans every live ring step in one launch, one workspace per step (None for the
+        others): a step's key/value positions and document ids follow from the sharding,
+        before its data arrive."""
         from . import new_workspace, plan_block_steps
         if self.step_workspaces is None:
-            self.step_workspaces = [new_workspace(*self._ws_shape) for _ in self.steps]
+            self.step_workspaces = [new_workspace(*self._ws_shape) if t in self.live_steps else None
+                                    for t in range(len(self.steps))]
+        if not self.live_steps:
+            return
         n_q, H, d = self.q.shape
-        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in self.steps],
-                         [st["kv_doc"] for st in self.steps], H, self.steps[0]["kv"].shape[2], d,
-                         self.step_workspaces, stream=stream)
+        live = [self.steps[t] for t in self.live_steps]
+        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in live], [st["kv_doc"] for st in live], H,
+                         self.steps[0]["kv"].shape[2], d, [self.step_workspaces[t] for t in self.live_steps],
+                         stream=stream)
 
     def run_planned(self, stream=None, per_step=None):
-        """run() with the plans of all steps made up front by plan_all(): one planning launch,
-        then per step the attention launch and (from step 1 on) the merge."""
+        """run() with the plans of all live steps made up front by plan_all(): one planning
+        launch, then per step the attention launch and (after the first) the merge."""
         from . import attn_run, lse_merge
+        if not self.live_steps:
+            return self._no_live_step()
         self.plan_all(stream)
-        for t, st in enumerate(self.steps):
-            first = t == 0
+        for i, t in enumerate(self.live_steps):
+            st = self.steps[t]
+            first = i == 0
             out = self.out if first else self.step_out
             lse = self.lse if first else self.step_lse
             attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=stream)
@@ -368,35 +399,40 @@ class ShardedRank:
         as run_planned(), so the same bits."""
         from . import attn_run, lse_merge
         main = torch.cuda.current_stream() if stream is None else stream
+        if not self.live_steps:
+            with torch.cuda.stream(main):
+                return self._no_live_step()
         if self.overlap_buffers is None:
             self.overlap_buffers = [(self.out, self.lse)] + [
-                (torch.empty_like(self.out), torch.empty_like(self.lse)) for _ in self.steps[1:]]
+                (torch.empty_like(self.out), torch.empty_like(self.lse)) for _ in self.live_steps[1:]]
         self.plan_all(main)
         planned = torch.cuda.Event()
         planned.record(main)
         done = []
-        for t, st in enumerate(self.steps):
-            s = streams[t % len(streams)]
+        for i, t in enumerate(self.live_steps):
+            st = self.steps[t]
+            s = streams[i % len(streams)]
             s.wait_event(planned)
-            out, lse = self.overlap_buffers[t]
+            out, lse = self.overlap_buffers[i]
             attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, self.step_workspaces[t], stream=s)
             ev = torch.cuda.Event()
             ev.record(s)
             done.append(ev)
         main.wait_event(done[0])
-        for t in range(1, len(self.steps)):
-            main.wait_event(done[t])
-            lse_merge(self.out, self.lse, *self.overlap_buffers[t], stream=main)
+        for i in range(1, len(self.live_steps)):
+            main.wait_event(done[i])
+            lse_merge(self.out, self.lse, *self.overlap_buffers[i], stream=main)
         return self.out, self.lse
 
     def backward(self, dout, stream=None):
         """The rank's ring backward after a forward (run, run_planned, run_overlapped or a
-        replay) left out and lse: D = <dout, out> once, then per step the query shard's dq
-        contribution (added into one fp32 buffer, so the steps run in order) and the source
+        replay) left out and lse: D = <dout, out> once, then per live step the query shard's
+        dq contribution (added into one fp32 buffer, so the steps run in order) and the source
         chunk's partial dk, dv, each in its own buffer -- what the rank would send back to
         the chunk's owner ("03 · 长文负载均衡", section 4.4: partial key/value gradients are
         reduced at the owning rank).  dout: bf16 [n_q, H, d] in the rank's token order.
-        Returns dq (fp32 [n_q, H, d]) and the list of per-step dkv (fp32 [2, n_kv, H_kv, d])."""
+        Returns dq (fp32 [n_q, H, d]) and the list of per-step dkv (fp32 [2, n_kv, H_kv, d]),
+        None for a step no row sees: it sends nothing back."""
         from . import attn_bwd_rowdot, block_attn_bwd
         if getattr(self, "bwd_buffers", None) is None:
             n_q, H, d = self.q.shape
@@ -410,14 +446,16 @@ class ShardedRank:
         b = self.bwd_buffers
         attn_bwd_rowdot(self.out, dout, dvec=b["dvec"], stream=stream)
         b["dq"].zero_()
-        for t, st in enumerate(self.steps):
+        for t in self.live_steps:
+            st = self.steps[t]
             block_attn_bwd(self.q, st["kv"], dout, self.lse, b["dvec"], self.q_pos, st["kv_pos"], self.q_doc,
                            st["kv_doc"], b["dq"], dkv=b["dkv"][t], workspace=b["ws"][t], stream=stream)
-        return b["dq"], b["dkv"]
+        return b["dq"], [b["dkv"][t] if t in self.live_steps else None for t in range(len(self.steps))]
 
     def capture(self, stream=None, streams=None):
-        """Captures run_planned() -- one planning launch, cp attention launches and cp - 1
-        merges -- or, given side streams, run_overlapped(), into a HIP graph, so that
+        """Captures run_planned() -- one planning launch, an attention launch per live step and
+        a merge for each after the first -- or, given side streams, run_overlapped(), into a
+        HIP graph, so that
         replay() launches the whole share at once.  Every kernel of the share is safe to
         replay: the planner resets the queue heads and the attention kernel rewinds them,
         and nothing in it clears memory with a memset node."""

@@ -9,7 +9,8 @@ Zigzag sharding ("03 · 长文负载均衡", section 4.2): the sequence is cut i
 
 Here one rank's share runs at its real shape on one GPU: the chunks a peer
 would have sent are already resident in HBM, and each step is one
-``block_attn_fwd`` call followed (from step 1 on) by ``lse_merge``.  No
+``block_attn_fwd`` call followed (after the first) by ``lse_merge``; a step whose
+chunks hold no key the rank's rows see runs nothing (``ShardedRank``).  No
 collectives are involved.
 """
 from __future__ import annotations
@@ -17,7 +18,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .sharding import ShardedRank
+from .sharding import ShardedRank, live_steps
 
 
 def chunks_of_rank(rank: int, cp: int):
@@ -85,6 +86,11 @@ class RankShare(ShardedRank):
         runs = int(min(max(n_q, n_kv), 2 * len(lengths) + 2))
         self.workspace = new_workspace(max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
         self._ws_shape = (max(n_q, n_kv), runs, H, self.steps[0]["kv"].shape[2], device)
+        qpos = np.concatenate([pos[span(c)] for c in qc])
+        qdoc = np.concatenate([doc[span(c)] for c in qc])
+        self.live_steps = live_steps(qpos, qdoc, [(np.concatenate([pos[span(c)] for c in st["chunks"]]),
+                                                   np.concatenate([doc[span(c)] for c in st["chunks"]]))
+                                                  for st in self.steps])
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None

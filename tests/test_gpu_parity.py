@@ -230,7 +230,7 @@ def test_shared_question_small_every_row():
 
 
 # --------------------------------------------------------------------------
-# config 4: one zigzag rank's share at cp=8, 8 ring steps + 7 merges
+# config 4: one zigzag rank's share at cp=8: 8 ring steps, a merge per live step after the first
 # --------------------------------------------------------------------------
 def test_zigzag_rank3_cp8():
     lengths = workloads.zigzag_pack_lengths(0)
@@ -244,10 +244,10 @@ def test_zigzag_rank3_cp8():
 
     say("  zigzag rank 3 of cp=8: building the share")
     share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
-    plans = []
+    plans = {}
 
     def per_step(t, o, l):
-        plans.append(lb.read_plan(share.workspace))
+        plans[t] = lb.read_plan(share.workspace)
 
     out, lse = share.run(per_step=per_step)
     torch.cuda.synchronize()
@@ -260,7 +260,10 @@ def test_zigzag_rank3_cp8():
         ki = np.concatenate([np.arange(c * C, (c + 1) * C)
                              for c in OA.zigzag_chunks_of_rank(OA.ring_source(rank, t, cp), cp)])
         ref = OP.plan(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 64)
-        assert_same_plan(plans[t], ref, f"zigzag step {t}")
+        if t in share.live_steps:
+            assert_same_plan(plans[t], ref, f"zigzag step {t}")
+        else:  # a step that runs nothing: the oracle gives it no tile with a key span
+            assert t not in plans and not any(x["spans"] for x in ref), t
         pairs.append(OP.total_pairs(ref))
     assert pairs == [20_319_978, 7_981_112, 0, 0, 0, 0, 0, 3_473_470]
     # output: oracle fold on sampled rows
@@ -283,14 +286,16 @@ def test_zigzag_plans_made_up_front_equal_per_step_plans():
         return cache[c]
 
     share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    # steps 2-6 of rank 3 hold no key its rows see (per-step pairs 20.3M, 8.0M, 0 x 5, 3.5M)
+    assert share.live_steps == [0, 1, 7]
     say("  per-step plans and runs")
-    ref_plans = []
-    out_ref, lse_ref = share.run(per_step=lambda t, o, l: ref_plans.append(lb.read_plan(share.workspace)))
+    ref_plans = {}
+    out_ref, lse_ref = share.run(per_step=lambda t, o, l: ref_plans.update({t: lb.read_plan(share.workspace)}))
     out_ref, lse_ref = out_ref.clone(), lse_ref.clone()
     say("  all plans in one launch, then the runs")
     out, lse = share.run_planned()
     torch.cuda.synchronize()
-    for t in range(cp):
+    for t in share.live_steps:
         assert lb.read_device_error(share.step_workspaces[t]) == 0
         assert_same_plan(lb.read_plan(share.step_workspaces[t]), ref_plans[t], f"step {t}")
     assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
@@ -326,7 +331,7 @@ def test_zigzag_graph_replays_equal_eager_runs():
         out, lse = share.run_planned()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager run after replay {i}"
-    for t in range(cp):
+    for t in share.live_steps:
         assert lb.read_device_error(share.step_workspaces[t]) == 0
 
 
@@ -364,7 +369,7 @@ def test_zigzag_overlapped_steps_equal_the_serial_share():
         out, lse = share.run_planned()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager run after replay {i}"
-    for t in range(cp):
+    for t in share.live_steps:
         assert lb.read_device_error(share.step_workspaces[t]) == 0
 
 
@@ -415,7 +420,7 @@ def test_sharded_ranks_reassemble_the_unsharded_result(rule):
         out, lse = share.run_planned()
         torch.cuda.synchronize()
         assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
-        for t in range(cp):
+        for t in share.live_steps:
             assert lb.read_device_error(share.step_workspaces[t]) == 0
         check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]], f"{rule} rank {rank}")
 

@@ -118,3 +118,32 @@ def test_spans_limit_filters_rules():
     assert LS.max_spans(lengths, LS.striped_tokens(8192, 4, 1)) > LS.MAX_SPANS
     tok = LS.shard_tokens("dispatch", lengths, 4, n_chunks=16)
     assert LS.max_spans(lengths, tok) <= LS.MAX_SPANS
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_live_steps_are_the_steps_with_planned_work(seed):
+    """A ring step runs only if the oracle's tile enumerator gives it a tile with a key span:
+    the host's test (the planner's tile count) keeps exactly those steps, for every rank of
+    a cp = 4 zigzag sharding of random packs with short and long documents."""
+    from load_balance_amd import zigzag as LZ
+    r = np.random.default_rng(seed)
+    cp, C = 4, 64
+    T = 2 * cp * C
+    lengths = workloads.lognormal_lengths(T, seed, T) if seed % 2 else [int(x) for x in r.integers(1, 40, 200)]
+    while sum(lengths) < T:
+        lengths.append(1)
+    tot = np.cumsum(lengths)
+    lengths = [int(x) for x in np.diff(np.r_[0, tot[tot < T], T])]
+    pos, doc = LZ.token_meta(lengths)
+    for rank in range(cp):
+        qc = LZ.chunks_of_rank(rank, cp)
+        qi = np.concatenate([np.arange(c * C, (c + 1) * C) for c in qc])
+        sides, want = [], []
+        for t in range(cp):
+            kc = LZ.chunks_of_rank(LZ.ring_source(rank, t, cp), cp)
+            ki = np.concatenate([np.arange(c * C, (c + 1) * C) for c in kc])
+            sides.append((pos[ki], doc[ki]))
+            tl = OP.tiles(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 64)
+            if any(len(x["spans"]) for x in tl):
+                want.append(t)
+        assert LS.live_steps(pos[qi], doc[qi], sides) == want, (seed, rank)
