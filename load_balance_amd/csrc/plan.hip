@@ -215,6 +215,8 @@ constexpr int kLdsRuns = kSortCap * 8 / 4 / (int)sizeof(KvRun);
 constexpr int kLdsFrags = kSortCap * 8 / 4 / (int)sizeof(Frag);
 constexpr int kLdsFtile = kSortCap * 8 / 2 / (int)sizeof(int32_t);
 constexpr int kMaxTilesPerThread = kSortCap / NT;
+constexpr int kRankSortMax = 2048;  // tiles ranked directly; larger plans take the bitonic sort
+static_assert(kRankSortMax % NT == 0 && kRankSortMax <= kSortCap, "");
 
 __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   const int tid = threadIdx.x;
@@ -475,8 +477,29 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   }
   __syncthreads();  // the staging areas are dead from here on; the sort buffer takes over
 
-  // ---- 3. longest-first order: bitonic sort of the unique keys in LDS --------------
-  if (sh.err == 0 && n_tiles > 0) {
+  // ---- 3. longest-first order of the unique keys ---------------------------------
+  // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys
+  // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS and
+  // one barrier, against the bitonic network's 55 barrier-separated passes at 1024 keys.
+  if (sh.err == 0 && n_tiles > 0 && n_tiles <= kRankSortMax) {
+#pragma unroll
+    for (int k = 0; k < kMaxTilesPerThread; ++k) {
+      const int i = tid + k * NT;
+      if (i < n_tiles) sh.keys[i] = my_keys[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRankSortMax / NT; ++k) {
+      const int t = tid + k * NT;
+      if (t >= n_tiles) break;
+      const uint64_t key = my_keys[k];
+      int rank = 0;
+#pragma unroll 8
+      for (int i = 0; i < n_tiles; ++i) rank += sh.keys[i] < key ? 1 : 0;
+      order[rank] = t;
+    }
+  } else if (sh.err == 0 && n_tiles > 0) {
+    // bitonic sort of the keys in LDS
     int n_pad = 1;
     while (n_pad < n_tiles) n_pad <<= 1;
 #pragma unroll
