@@ -162,17 +162,24 @@ lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
  *   kv_chunk   bf16 [2][n_kv][kv_heads][d]: all of K, then all of V
  *   q_pos, kv_pos  int32 global positions of each token
  *   q_doc, kv_doc  int32 document ids of each token
+ *   shared_doc LB_NO_SHARED_DOC, or the document id of a prefix every other document
+ *              shares (the shared-question mask of "03 · 长文负载均衡", section 1.2, on
+ *              the block path): each row of another document also sees every key of it
  *   out        fp32 [n_q][heads][d]; rows with no visible key are not written
  *   lse        fp32 [heads][n_q]; -inf for rows with no visible key
  *   workspace  >= lb_workspace_bytes(max(n_q, n_kv), max_runs, heads, kv_heads),
  *              max_runs bounding the runs of equal doc id and consecutive
  *              position on either side (exceeding it: LB_DEVERR_CAPACITY)
- * Key j is visible to query i iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i].
+ * Key j is visible to query i iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i], or
+ * kv_doc[j] == shared_doc != q_doc[i].  A query run meets at most LB_MAX_SPANS key runs
+ * (its own document's and the shared document's together; beyond: LB_DEVERR_SPANS).
+ * shared_doc < -1: LB_EINVAL.
  */
+#define LB_NO_SHARED_DOC (-1)
 lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,
                             const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
                             const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
-                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int32_t shared_doc, float* out, float* lse, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
 /*
@@ -194,7 +201,7 @@ lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total
 
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+                        int32_t shared_doc, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Plans n_steps block steps of one query shard in one launch, one workgroup per step:
@@ -212,7 +219,7 @@ lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
  */
 lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
                               const int32_t* const* kv_pos, const int32_t* const* kv_doc, const int32_t* n_kv,
-                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d,
+                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d, int32_t shared_doc,
                               void* const* workspaces, const size_t* workspace_bytes, hipStream_t stream);
 
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
@@ -292,7 +299,7 @@ lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
  *   dout      bf16 [n_q][heads][d];
  *   lse, dvec fp32 [heads][n_q]: the whole row's lse after every step's merge, and
  *             D = <dout, out> of the merged out (lb_attn_bwd_rowdot with out_f32 = 1);
- *   q_pos, kv_pos, q_doc, kv_doc: as lb_block_attn_fwd;
+ *   q_pos, kv_pos, q_doc, kv_doc, shared_doc: as lb_block_attn_fwd;
  *   dq        fp32 [n_q][heads][d]: this step's contribution is ADDED (zero it before the
  *             first step; rows with no visible key in this step are left as they are);
  *   dkv       fp32 [2][n_kv][kv_heads][d]: this step's dk then dv, WRITTEN (every key).
@@ -302,7 +309,8 @@ lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
 lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv, const void* dout,
                             const float* lse, const float* dvec, const int32_t* q_pos, const int32_t* kv_pos,
                             const int32_t* q_doc, const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
-                            float* dq, float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                            int32_t shared_doc, float* dq, float* dkv, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /*
  * ---- Slice-list masks -------------------------------------------------------------

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "liblbattn.so")
 
 MASK_CAUSAL_DOC = 0
 MASK_SHARED_QUESTION = 1
+NO_SHARED_DOC = -1  # block path: no document shared by the others
 MAX_SPANS = 4
 MAX_PLAN_STEPS = 16
 
@@ -75,13 +76,13 @@ def lib() -> ctypes.CDLL:
     L.lb_workspace_bytes.restype = SZ
     L.lb_varlen_attn_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_varlen_attn_fwd.restype = ctypes.c_int
-    L.lb_block_attn_fwd.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_block_attn_fwd.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_block_attn_fwd.restype = ctypes.c_int
     L.lb_plan_varlen.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_varlen.restype = ctypes.c_int
-    L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_block.restype = ctypes.c_int
-    L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, P, P, P]
+    L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P]
     L.lb_plan_block_steps.restype = ctypes.c_int
     L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run.restype = ctypes.c_int
@@ -101,7 +102,7 @@ def lib() -> ctypes.CDLL:
     L.lb_attn_bwd_rowdot.restype = ctypes.c_int
     L.lb_varlen_attn_bwd.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
     L.lb_varlen_attn_bwd.restype = ctypes.c_int
-    L.lb_block_attn_bwd.argtypes = [P, I32, P, I32, P, P, P, P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
+    L.lb_block_attn_bwd.argtypes = [P, I32, P, I32, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_block_attn_bwd.restype = ctypes.c_int
     L.lb_status_string.argtypes = [ctypes.c_int]
     L.lb_status_string.restype = ctypes.c_char_p
@@ -173,8 +174,10 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, out=None, ls
 
 
 def block_attn_fwd(q_shard, kv_chunk, q_pos, kv_pos, q_doc, kv_doc, out=None, lse=None, workspace=None,
-                   max_runs=None, stream=None):
+                   max_runs=None, stream=None, shared_doc=NO_SHARED_DOC):
     """One ring step: q_shard [n_q,H,d] bf16 against kv_chunk [2,n_kv,H_kv,d] bf16 (K then V).
+    shared_doc: a document whose keys every other document's rows see in full (the shared
+    question), or NO_SHARED_DOC.
 
     Returns out [n_q,H,d] fp32 (rows with no visible key left unwritten) and lse [H,n_q] fp32.
     """
@@ -194,7 +197,8 @@ def block_attn_fwd(q_shard, kv_chunk, q_pos, kv_pos, q_doc, kv_doc, out=None, ls
         if t.dtype != torch.int32:
             raise LBError(f"{name} must be int32")
     st = lib().lb_block_attn_fwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(q_pos), _ptr(kv_pos),
-                                 _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, _ptr(out), _ptr(lse), _ptr(workspace),
+                                 _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, int(shared_doc), _ptr(out), _ptr(lse),
+                                 _ptr(workspace),
                                  workspace.numel(), ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_block_attn_fwd")
     return out, lse
@@ -214,18 +218,19 @@ def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAU
     return workspace
 
 
-def plan_block(q_pos, q_doc, kv_pos, kv_doc, heads, kv_heads, d, workspace, stream=None):
+def plan_block(q_pos, q_doc, kv_pos, kv_doc, heads, kv_heads, d, workspace, stream=None, shared_doc=NO_SHARED_DOC):
     """First half of block_attn_fwd: writes the tile plan into ``workspace``."""
     for t, name in ((q_pos, "q_pos"), (kv_pos, "kv_pos"), (q_doc, "q_doc"), (kv_doc, "kv_doc")):
         if t.dtype != torch.int32:
             raise LBError(f"{name} must be int32")
     _check(lib().lb_plan_block(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), _ptr(kv_pos), _ptr(kv_doc), kv_pos.numel(),
-                               heads, kv_heads, d, _ptr(workspace), workspace.numel(),
+                               heads, kv_heads, d, int(shared_doc), _ptr(workspace), workspace.numel(),
                                ctypes.c_void_p(_stream(stream))), "lb_plan_block")
     return workspace
 
 
-def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d, workspaces, stream=None):
+def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d, workspaces, stream=None,
+                     shared_doc=NO_SHARED_DOC):
     """Plans of several block steps of one query shard, one launch: step s plans the shard
     against kv_pos_list[s], kv_doc_list[s] into workspaces[s] exactly as plan_block would."""
     n = len(workspaces)
@@ -239,7 +244,7 @@ def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d,
     n_kv = (ctypes.c_int32 * max(n, 1))(*[t.numel() for t in kv_pos_list])
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
     _check(lib().lb_plan_block_steps(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), ptrs(kv_pos_list), ptrs(kv_doc_list),
-                                     n_kv, n, heads, kv_heads, d, ptrs(workspaces), sizes,
+                                     n_kv, n, heads, kv_heads, d, int(shared_doc), ptrs(workspaces), sizes,
                                      ctypes.c_void_p(_stream(stream))), "lb_plan_block_steps")
     return workspaces
 
@@ -366,7 +371,7 @@ def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, mask_kind=MASK_CAUSAL_D
 
 
 def block_attn_bwd(q_shard, kv_chunk, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, dq, dkv=None, workspace=None,
-                   stream=None):
+                   stream=None, shared_doc=NO_SHARED_DOC):
     """One ring step of the backward: adds this step's contribution to dq (fp32 [n_q,H,d]) and
     returns dkv (fp32 [2,n_kv,H_kv,d]: this step's dk, dv) together with dq."""
     n_q, H, d = q_shard.shape
@@ -383,7 +388,8 @@ def block_attn_bwd(q_shard, kv_chunk, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise LBError(f"{name} must be a contiguous float32 tensor")
     _check(lib().lb_block_attn_bwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(dout), _ptr(lse), _ptr(dvec),
-                                   _ptr(q_pos), _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, _ptr(dq),
+                                   _ptr(q_pos), _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, int(shared_doc),
+                                   _ptr(dq),
                                    _ptr(dkv), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_block_attn_bwd")
     return dq, dkv

@@ -151,11 +151,12 @@ lb_status prepare_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t
 }
 
 PlanArgs block_plan_args(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
-                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
-                         const WsLayout& L) {
+                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t shared_doc,
+                         void* workspace, const WsLayout& L) {
   PlanArgs p{};
   p.mode = kPlanBlock;
   p.q_pos = q_pos; p.q_doc = q_doc; p.kv_pos = kv_pos; p.kv_doc = kv_doc;
+  p.shared_doc = shared_doc;
   p.n_q = n_q;
   p.n_kv = n_kv;
   p.tile_rows = tile_rows_for_group(heads / kv_heads);
@@ -167,9 +168,10 @@ PlanArgs block_plan_args(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q
 }
 
 lb_status launch_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
-                            const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, void* workspace,
-                            const WsLayout& L, hipStream_t stream) {
-  const PlanArgs p = block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L);
+                            const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t shared_doc,
+                            void* workspace, const WsLayout& L, hipStream_t stream) {
+  const PlanArgs p =
+      block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, shared_doc, workspace, L);
   return launch_plan(p, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
@@ -294,19 +296,21 @@ lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total
 
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        int32_t shared_doc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (shared_doc < -1) return LB_EINVAL;
   WsLayout L;
   lb_status st = prepare_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, d, workspace,
                                     workspace_bytes, &L);
   if (st != LB_OK) return st;
-  return launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L, stream);
+  return launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, shared_doc, workspace, L,
+                           stream);
 }
 
 lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q,
                               const int32_t* const* kv_pos, const int32_t* const* kv_doc, const int32_t* n_kv,
-                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d,
+                              int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d, int32_t shared_doc,
                               void* const* workspaces, const size_t* workspace_bytes, hipStream_t stream) {
-  if (n_steps < 1 || n_steps > kMaxPlanSteps) return LB_EINVAL;
+  if (n_steps < 1 || n_steps > kMaxPlanSteps || shared_doc < -1) return LB_EINVAL;
   if (!kv_pos || !kv_doc || !n_kv || !workspaces || !workspace_bytes) return LB_EINVAL;
   PlanBatch b{};
   for (int s = 0; s < n_steps; ++s) {
@@ -316,7 +320,7 @@ lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_
     lb_status st = prepare_plan_block(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads, d,
                                       workspaces[s], workspace_bytes[s], &L);
     if (st != LB_OK) return st;
-    b.step[s] = block_plan_args(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads,
+    b.step[s] = block_plan_args(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads, shared_doc,
                                 workspaces[s], L);
   }
   return launch_plan_steps(b, n_steps, stream) == hipSuccess ? LB_OK : LB_EHIP;
@@ -364,11 +368,11 @@ lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
 lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,
                             const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
                             const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
-                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            int32_t shared_doc, float* out, float* lse, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   const __bf16* kbase = static_cast<const __bf16*>(kv_chunk);
   const __bf16* vbase = kbase ? kbase + (int64_t)n_kv * kv_heads * d : nullptr;
-  if (n_kv < 0 || kv_heads <= 0 || d <= 0) return LB_EINVAL;
+  if (n_kv < 0 || kv_heads <= 0 || d <= 0 || shared_doc < -1) return LB_EINVAL;
   lb_status st = check_run(q_shard, kbase, vbase, n_q, n_kv, heads, kv_heads, d, out, lse, workspace,
                            workspace_bytes);
   if (st != LB_OK) return st;
@@ -377,7 +381,8 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
                           &L);
   if (st != LB_OK) return st;
   if (n_q == 0) return LB_OK;
-  st = launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, workspace, L, stream);
+  st = launch_plan_block(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, shared_doc, workspace, L,
+                         stream);
   if (st != LB_OK) return st;
   return launch_run(q_shard, kbase, vbase, n_q, n_kv, heads, kv_heads, d, true, out, lse, workspace,
                     workspace_bytes, stream);
@@ -495,8 +500,9 @@ lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
 lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv, const void* dout,
                             const float* lse, const float* dvec, const int32_t* q_pos, const int32_t* kv_pos,
                             const int32_t* q_doc, const int32_t* kv_doc, int32_t heads, int32_t kv_heads, int32_t d,
-                            float* dq, float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (n_q < 0 || n_kv < 0) return LB_EINVAL;
+                            int32_t shared_doc, float* dq, float* dkv, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (n_q < 0 || n_kv < 0 || shared_doc < -1) return LB_EINVAL;
   if (!q_shard || !dout || !lse || !dvec || !q_pos || !q_doc || !dq || !workspace) return LB_EINVAL;
   if (n_kv > 0 && (!kv_chunk || !kv_pos || !kv_doc || !dkv)) return LB_EINVAL;
   lb_status st = check_heads(heads, kv_heads, d);
@@ -516,7 +522,7 @@ lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chu
   const __bf16* vbase = kbase + (int64_t)n_kv * kv_heads * d;
   PlanBatch pb{};
   for (int side = 0; side < 2; ++side) {
-    pb.step[side] = block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads,
+    pb.step[side] = block_plan_args(q_pos, q_doc, n_q, kv_pos, kv_doc, n_kv, heads, kv_heads, shared_doc,
                                     ws + (side == 0 ? 0 : B.off_k), side == 0 ? B.q : B.k);
     pb.step[side].transposed = side;
     pb.step[side].tile_rows = side == 0 ? bwd_q_rows(heads / kv_heads) : bwd_k_rows(heads / kv_heads);

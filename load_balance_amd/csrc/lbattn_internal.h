@@ -99,6 +99,8 @@ enum PlanMode { kPlanCausalDoc = 0, kPlanSharedQuestion = 1, kPlanBlock = 2, kPl
 // Key position offset of a FULL slice's span: below every query position, so that every
 // key is visible (the planner's pair count stays in 64-bit range).
 constexpr int32_t kFullSpanPos = -(1 << 30);
+// The transposed counterpart: a query run at this position sees every key of the tile.
+constexpr int32_t kFullRowsPos = 1 << 30;
 
 struct PlanArgs {
   int32_t mode;
@@ -106,6 +108,7 @@ struct PlanArgs {
   const int32_t* cu_seqlens;
   int32_t n_seg, total_tokens;
   const int32_t *q_pos, *q_doc, *kv_pos, *kv_doc;
+  int32_t shared_doc;  // block path: the document every other document's rows see in full; -1: none
   const lb_mask_slice* slices;
   int32_t n_slices;
   int32_t n_q, n_kv;

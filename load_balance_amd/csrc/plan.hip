@@ -369,16 +369,36 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
         const int doc = t_doc[s];
         const int last_pos = f.q_pos0 + f.q_len - 1;
         int ns = 0;
+        int full_end = -1;  // end of the last span in the buffer when that span is FULL, else -1
         for (int j = 0; j < n_kvruns; ++j) {
           const KvRun kr = lds_runs[j];
+          // The shared document's keys are seen in full by every other document's rows
+          // (the shared-question mask): as a FULL span (keys far below every row) or,
+          // transposed, a query run far above every key.
+          const int key_doc = a.transposed ? doc : kr.doc, row_doc = a.transposed ? kr.doc : doc;
+          const bool shared = a.shared_doc >= 0 && key_doc == a.shared_doc && row_doc != a.shared_doc;
           // other document, or no pair: keys wholly after the query run (forward), or
           // queries wholly before the key run (transposed)
-          if (kr.doc != doc || (a.transposed ? kr.pos0 + kr.len - 1 < f.q_pos0 : kr.pos0 > last_pos)) continue;
+          if (!shared &&
+              (kr.doc != doc || (a.transposed ? kr.pos0 + kr.len - 1 < f.q_pos0 : kr.pos0 > last_pos)))
+            continue;
+          if (shared && full_end == kr.start) {
+            // a FULL run right after a FULL span in the buffer extends it: positions play no
+            // part in a FULL span, so one span covers both (a document cut into several
+            // chunks per rank stays one span)
+#pragma unroll
+            for (int o = 0; o < LB_MAX_SPANS; ++o)
+              if (o == ns - 1) f.k_len[o] += kr.len;
+            full_end += kr.len;
+            continue;
+          }
           if (ns == LB_MAX_SPANS) { atomicOr(&sh.err, LB_DEVERR_SPANS); break; }
+          const int pos0 = shared ? (a.transposed ? kFullRowsPos : kFullSpanPos) : kr.pos0;
 #pragma unroll
           for (int o = 0; o < LB_MAX_SPANS; ++o)  // slot ns, selected so the fields stay in registers
-            if (o == ns) { f.k_start[o] = kr.start; f.k_len[o] = kr.len; f.k_pos0[o] = kr.pos0; }
+            if (o == ns) { f.k_start[o] = kr.start; f.k_len[o] = kr.len; f.k_pos0[o] = pos0; }
           ++ns;
+          full_end = shared ? kr.start + kr.len : -1;
         }
         f.n_spans = ns;
         frags[r] = f;

@@ -156,18 +156,24 @@ def _runs(pos, doc):
     return np.stack([starts, lens, pos[starts], doc[starts]], axis=1).astype(np.int64)
 
 
-def predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int):
+def predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int, shared_doc: int = -1):
     """(key blocks, work items) of one kv head for a query shard against a key/value shard:
     each run of the query shard is cut into tiles of ``tile_rows``; a tile sweeps, of every
     key run of its document, the blocks holding keys its last row can see, and is a work
-    item when it sweeps any."""
+    item when it sweeps any.  With a shared document (shared_doc >= 0), a run of any other
+    document also sweeps every block of that document's key runs, runs next to each other in
+    the key buffer taken as one span (as the planner does)."""
     qr, kr = _runs(np.asarray(q_pos), np.asarray(q_doc)), _runs(np.asarray(kv_pos), np.asarray(kv_doc))
     blocks = items = 0
     by_doc = {}
+    far = -(1 << 30)  # a shared key run lies below every row
     for (_, ln, p0, d) in kr:
         by_doc.setdefault(int(d), []).append((int(ln), int(p0)))
+    shared = [(kl, far) for kl in _full_spans(kr, shared_doc)]
     for (_, ln, p0, d) in qr:
-        spans = by_doc.get(int(d))
+        spans = list(by_doc.get(int(d), []))
+        if shared_doc >= 0 and int(d) != shared_doc:
+            spans += shared
         if not spans:
             continue
         last = p0 + np.minimum(np.arange(tile_rows, int(ln) + tile_rows, tile_rows), ln) - 1  # last row of each tile
@@ -180,19 +186,46 @@ def predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int):
     return blocks, items
 
 
-MAX_SPANS = 4  # key runs of its document one query run may meet (LB_MAX_SPANS)
+def _full_spans(runs, doc):
+    """Lengths of the FULL spans that runs of ``doc`` make: runs next to each other in the
+    buffer join into one span (every pair of a FULL span is seen, so positions play no part)."""
+    out, end = [], -1
+    for (st, ln, _, d) in runs:
+        if doc < 0 or int(d) != doc:
+            continue
+        if out and end == st:
+            out[-1] += int(ln)
+        else:
+            out.append(int(ln))
+        end = int(st) + int(ln)
+    return out
 
 
-def max_spans(lengths, tokens) -> int:
-    """The most key runs of its own document, not wholly after it, that any query run of any
-    rank meets on any ring step: the planner refuses a step where this exceeds MAX_SPANS."""
+MAX_SPANS = 4  # spans one query run (or, in the backward, one key run) may meet (LB_MAX_SPANS)
+
+
+def max_spans(lengths, tokens, shared_doc: int = -1) -> int:
+    """The most spans any run of any rank meets on any ring step: the planner refuses a step
+    where this exceeds MAX_SPANS.  A query run's spans are the key runs of its own document
+    not wholly after it, plus, with a shared document, that document's FULL spans; in the
+    backward's key-tile plan a key run of the shared document also meets the other documents'
+    query runs as FULL spans."""
     pos, doc = token_meta(lengths)
     runs = [_runs(pos[t], doc[t]) for t in tokens]
     worst = 0
     for qr in runs:
         for kr in runs:
+            n_shared = len(_full_spans(kr, shared_doc))
             for (_, ln, p0, d) in qr:
-                worst = max(worst, int(np.count_nonzero((kr[:, 3] == d) & (kr[:, 2] <= p0 + ln - 1))))
+                n = int(np.count_nonzero((kr[:, 3] == d) & (kr[:, 2] <= p0 + ln - 1)))
+                worst = max(worst, n + (n_shared if shared_doc >= 0 and int(d) != shared_doc else 0))
+            if shared_doc >= 0:
+                other = [(st, ln, p0, 1) for (st, ln, p0, d) in qr if int(d) != shared_doc]
+                n_rows = len(_full_spans(other, 1))
+                for (_, ln, p0, d) in kr:
+                    if int(d) == shared_doc:
+                        n = int(np.count_nonzero((qr[:, 3] == d) & (qr[:, 2] + qr[:, 1] - 1 >= p0)))
+                        worst = max(worst, n + n_rows)
     return worst
 
 
@@ -279,10 +312,10 @@ def build_shards(lengths, tokens, get_rows, device="cuda"):
     return shards
 
 
-def live_steps(q_pos, q_doc, kv_sides):
+def live_steps(q_pos, q_doc, kv_sides, shared_doc: int = -1):
     """Indices of the (kv_pos, kv_doc) sides with at least one key some query row sees:
     the planner's work items for them are not all empty."""
-    return [t for t, (kp, kd) in enumerate(kv_sides) if predicted_work(q_pos, q_doc, kp, kd, 64)[1] > 0]
+    return [t for t, (kp, kd) in enumerate(kv_sides) if predicted_work(q_pos, q_doc, kp, kd, 64, shared_doc)[1] > 0]
 
 
 class ShardedRank:
@@ -300,10 +333,11 @@ class ShardedRank:
     the running result as it is), so ``live_steps`` lists the steps that run.
     """
 
-    def __init__(self, shards, rank, device="cuda"):
+    def __init__(self, shards, rank, device="cuda", shared_doc=-1):
         from . import new_workspace
         cp = len(shards)
         self.cp, self.rank = cp, rank
+        self.shared_doc = shared_doc  # a document every other document's rows see in full, or -1
         me = shards[rank]
         self.tokens = me["tokens"]
         self.q, self.q_pos, self.q_doc = me["q"], me["pos"], me["doc"]
@@ -325,7 +359,8 @@ class ShardedRank:
         self._ws_shape = (n_max, max(1, runs), H, Hkv, device)
         self.workspace = new_workspace(*self._ws_shape)
         self.live_steps = live_steps(self.q_pos.cpu().numpy(), self.q_doc.cpu().numpy(),
-                                     [(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy()) for s in self.steps])
+                                     [(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy()) for s in self.steps],
+                                     shared_doc)
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None
@@ -347,7 +382,7 @@ class ShardedRank:
             out = self.out if first else self.step_out
             lse = self.lse if first else self.step_lse
             block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
-                           workspace=self.workspace, stream=stream)
+                           workspace=self.workspace, stream=stream, shared_doc=self.shared_doc)
             if per_step is not None:
                 per_step(t, out, lse)
             if not first:
@@ -368,7 +403,7 @@ class ShardedRank:
         live = [self.steps[t] for t in self.live_steps]
         plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in live], [st["kv_doc"] for st in live], H,
                          self.steps[0]["kv"].shape[2], d, [self.step_workspaces[t] for t in self.live_steps],
-                         stream=stream)
+                         stream=stream, shared_doc=self.shared_doc)
 
     def run_planned(self, stream=None, per_step=None):
         """run() with the plans of all live steps made up front by plan_all(): one planning
@@ -449,7 +484,8 @@ class ShardedRank:
         for t in self.live_steps:
             st = self.steps[t]
             block_attn_bwd(self.q, st["kv"], dout, self.lse, b["dvec"], self.q_pos, st["kv_pos"], self.q_doc,
-                           st["kv_doc"], b["dq"], dkv=b["dkv"][t], workspace=b["ws"][t], stream=stream)
+                           st["kv_doc"], b["dq"], dkv=b["dkv"][t], workspace=b["ws"][t], stream=stream,
+                           shared_doc=self.shared_doc)
         return b["dq"], [b["dkv"][t] if t in self.live_steps else None for t in range(len(self.steps))]
 
     def capture(self, stream=None, streams=None):

@@ -49,6 +49,7 @@ class RankShare(ShardedRank):
 
     def __init__(self, lengths, chunk_tokens, rank, cp, get_chunk, device="cuda"):
         self.cp, self.rank, self.chunk = cp, rank, chunk_tokens
+        self.shared_doc = -1  # per-document causal mask
         pos, doc = token_meta(lengths)
         assert len(pos) == 2 * cp * chunk_tokens, "pack length must be 2*cp*chunk_tokens"
 

@@ -68,10 +68,17 @@ def visible_shared_question(seg, rows, cols) -> np.ndarray:
     return (cols <= rows) & (same | question_key)
 
 
-def visible_block(q_pos, q_doc, kv_pos, kv_doc, rows, cols) -> np.ndarray:
+def visible_block(q_pos, q_doc, kv_pos, kv_doc, rows, cols, shared_doc=None) -> np.ndarray:
+    """Same document and key position <= query position; with ``shared_doc``, also every key
+    of that document for the rows of every other document (the shared question of
+    "03 · 长文负载均衡", section 1.2: answers see the whole question, the question does not
+    see the answers)."""
     rows = np.asarray(rows)[:, None]
     cols = np.asarray(cols)[None, :]
-    return (q_doc[rows] == kv_doc[cols]) & (kv_pos[cols] <= q_pos[rows])
+    vis = (q_doc[rows] == kv_doc[cols]) & (kv_pos[cols] <= q_pos[rows])
+    if shared_doc is not None:
+        vis = vis | ((kv_doc[cols] == shared_doc) & (q_doc[rows] != shared_doc))
+    return vis
 
 
 # --------------------------------------------------------------------------
@@ -185,10 +192,12 @@ def varlen_attention(q, k, v, cu_seqlens, heads, kv_heads, mask="causal_doc", ro
 # --------------------------------------------------------------------------
 # block attention of one context-parallel step
 # --------------------------------------------------------------------------
-def block_attention(q, k, v, q_pos, kv_pos, q_doc, kv_doc, heads, kv_heads, rows=None, scale=None):
+def block_attention(q, k, v, q_pos, kv_pos, q_doc, kv_doc, heads, kv_heads, rows=None, scale=None,
+                    shared_doc=None):
     """Query shard [n_q,H,d] against one key/value chunk [n_kv,H_kv,d].
 
-    Visible iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i].
+    Visible iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i], or (with ``shared_doc``)
+    kv_doc[j] == shared_doc != q_doc[i].
     Returns out [R,H,d] (zeros on empty rows) and lse [H,R] (-inf on empty rows).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -203,8 +212,9 @@ def block_attention(q, k, v, q_pos, kv_pos, q_doc, kv_doc, heads, kv_heads, rows
     units = []
     for doc in np.unique(q_doc[rows]):
         r = rows[q_doc[rows] == doc]
-        cols = np.nonzero(kv_doc == doc)[0]
-        units.append((r, cols, lambda rr, cc: visible_block(q_pos, q_doc, kv_pos, kv_doc, rr, cc)))
+        sees = (kv_doc == doc) | ((kv_doc == shared_doc) if shared_doc is not None and doc != shared_doc else False)
+        cols = np.nonzero(sees)[0]
+        units.append((r, cols, lambda rr, cc: visible_block(q_pos, q_doc, kv_pos, kv_doc, rr, cc, shared_doc)))
     res = _run_units(q, k, v, heads, kv_heads, units, scale)
     return _collect(res, rows, heads, v.shape[2])
 

@@ -118,7 +118,8 @@ def varlen_attention_bwd(q, k, v, dout, cu_seqlens, heads, kv_heads, mask="causa
     return _bwd_units(q, k, v, dout, heads, kv_heads, units, scale)
 
 
-def block_attention_bwd(q, k, v, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, heads, kv_heads, scale=None):
+def block_attention_bwd(q, k, v, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, heads, kv_heads, scale=None,
+                        shared_doc=None):
     """One ring step: the query shard's dq contribution [n_q,H,d] and the key/value chunk's
     dk, dv [n_kv,H_kv,d], from the whole-row lse and D [H,n_q] of the merged forward."""
     q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
@@ -130,7 +131,8 @@ def block_attention_bwd(q, k, v, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, 
     units = []
     for doc in np.unique(q_doc):
         r = np.nonzero(q_doc == doc)[0]
-        cols = np.nonzero(kv_doc == doc)[0]
-        units.append((r, cols, lambda rr, cc: visible_block(q_pos, q_doc, kv_pos, kv_doc, rr, cc)))
+        sees = (kv_doc == doc) | ((kv_doc == shared_doc) if shared_doc is not None and doc != shared_doc else False)
+        cols = np.nonzero(sees)[0]
+        units.append((r, cols, lambda rr, cc: visible_block(q_pos, q_doc, kv_pos, kv_doc, rr, cc, shared_doc)))
     return _bwd_units(q, k, v, dout, heads, kv_heads, units, scale,
                       np.asarray(lse, dtype=np.float64), np.asarray(dvec, dtype=np.float64))

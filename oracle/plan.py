@@ -102,14 +102,37 @@ def runs(pos, doc):
     return [tuple(r) for r in out]
 
 
-def fragments_block(q_pos, q_doc, kv_pos, kv_doc):
+FAR = 1 << 30  # a position offset no real position reaches
+
+
+def fragments_block(q_pos, q_doc, kv_pos, kv_doc, shared_doc=None):
+    """Query runs with the key runs of their document.  With ``shared_doc``, a run of any
+    other document also gets that document's key runs, wholly visible: their positions are
+    taken as lying far below every row (a FULL span); FULL runs next to each other in the
+    key buffer make one span.  Spans keep the key runs' order."""
     q_runs = runs(q_pos, q_doc)
     kv_runs = runs(kv_pos, kv_doc)
     frags = []
     for (qs, ql, qp0, qd) in q_runs:
-        spans = [(ks, kl, kp0) for (ks, kl, kp0, kd) in kv_runs if kd == qd]
+        spans = []
+        for (ks, kl, kp0, kd) in kv_runs:
+            if kd == qd:
+                spans.append((ks, kl, kp0))
+            elif shared_doc is not None and kd == shared_doc and qd != shared_doc:
+                add_full_span(spans, ks, kl, -FAR)
         frags.append((qs, ql, qp0, spans))
     return frags
+
+
+def add_full_span(spans, start, length, pos0):
+    """Appends a FULL span, or lengthens the last span when that one is FULL too and ends
+    where this one starts in the buffer: a FULL span's positions are never looked at, so the
+    two cover the same pairs as one."""
+    if spans and spans[-1][2] == pos0 and spans[-1][0] + spans[-1][1] == start:
+        s, n, p = spans[-1]
+        spans[-1] = (s, n + length, p)
+    else:
+        spans.append((start, length, pos0))
 
 
 def visible_in_span(row_pos, k_len, k_pos0):
@@ -171,11 +194,19 @@ def fragments_varlen_t(cu_seqlens, mask="causal_doc"):
     return frags
 
 
-def fragments_block_t(q_pos, q_doc, kv_pos, kv_doc):
+def fragments_block_t(q_pos, q_doc, kv_pos, kv_doc, shared_doc=None):
+    """Key runs with the query runs of their document; a run of ``shared_doc`` also gets every
+    other document's query runs, which see all of it: their positions taken far above every
+    key, and runs next to each other in the query buffer (of any documents) make one span."""
     q_runs = runs(q_pos, q_doc)
     frags = []
     for (ks, kl, kp0, kd) in runs(kv_pos, kv_doc):
-        spans = [(qs, ql, qp0) for (qs, ql, qp0, qd) in q_runs if qd == kd]
+        spans = []
+        for (qs, ql, qp0, qd) in q_runs:
+            if qd == kd:
+                spans.append((qs, ql, qp0))
+            elif shared_doc is not None and kd == shared_doc and qd != shared_doc:
+                add_full_span(spans, qs, ql, FAR)
         frags.append((ks, kl, kp0, spans))
     return frags
 

@@ -101,11 +101,12 @@ def test_varlen_host_checks(L):
 def test_block_host_checks(L):
     def call(**kw):
         a = dict(q=FAKE, n_q=128, kv=FAKE, n_kv=128, qp=FAKE, kp=FAKE, qd=FAKE, kd=FAKE, H=32, Hkv=8, d=128,
-                 out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 20)
+                 shared=-1, out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 20)
         a.update(kw)
         return L.lb_block_attn_fwd(a["q"], a["n_q"], a["kv"], a["n_kv"], a["qp"], a["kp"], a["qd"], a["kd"], a["H"],
-                                   a["Hkv"], a["d"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+                                   a["Hkv"], a["d"], a["shared"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
     assert call(q=None) == LB_EINVAL
+    assert call(shared=-2) == LB_EINVAL
     assert call(kv=None) == LB_EINVAL
     assert call(n_q=-1) == LB_EINVAL
     assert call(d=80) == LB_EUNSUPPORTED
@@ -121,8 +122,9 @@ def test_split_host_checks(L):
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 5, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 0, FAKE, need - 1, None) == LB_EWORKSPACE
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 48, 0, FAKE, need, None) == LB_EUNSUPPORTED
-    assert L.lb_plan_block(None, FAKE, n, FAKE, FAKE, n, 2, 2, 64, FAKE, need, None) == LB_EINVAL
-    assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, FAKE, 64, None) == LB_EWORKSPACE
+    assert L.lb_plan_block(None, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, need, None) == LB_EINVAL
+    assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -2, FAKE, need, None) == LB_EINVAL
+    assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, 64, None) == LB_EWORKSPACE
     assert L.lb_attn_run(FAKE, FAKE, FAKE, n, n, 2, 2, 64, 0, None, FAKE, FAKE, need, None) == LB_EINVAL
     assert L.lb_attn_run(FAKE, None, FAKE, n, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, need, None) == LB_EINVAL
     assert L.lb_attn_run(FAKE, FAKE, FAKE, n, n, 2, 2, 64, 0, FAKE, FAKE, FAKE, 100, None) == LB_EWORKSPACE
@@ -137,7 +139,7 @@ def test_plan_steps_host_checks(L):
     two = [P(0x100000), P(0x200000)]
 
     def call(n_steps=2, ws=two, sizes=(need, need), kv=(FAKE, FAKE), n_kv=(n, n), d=64, q_pos=FAKE):
-        return L.lb_plan_block_steps(q_pos, FAKE, n, arr(P, kv), arr(P, kv), arr(I32, n_kv), n_steps, 2, 2, d,
+        return L.lb_plan_block_steps(q_pos, FAKE, n, arr(P, kv), arr(P, kv), arr(I32, n_kv), n_steps, 2, 2, d, -1,
                                      arr(P, ws), arr(SZ, sizes), None)
     assert call(n_steps=0) == LB_EINVAL
     assert call(n_steps=17) == LB_EINVAL           # more than LB_MAX_PLAN_STEPS
@@ -146,7 +148,7 @@ def test_plan_steps_host_checks(L):
     assert call(kv=(FAKE, None)) == LB_EINVAL
     assert call(q_pos=None) == LB_EINVAL
     assert call(d=48) == LB_EUNSUPPORTED
-    assert L.lb_plan_block_steps(FAKE, FAKE, n, None, None, None, 1, 2, 2, 64, None, None, None) == LB_EINVAL
+    assert L.lb_plan_block_steps(FAKE, FAKE, n, None, None, None, 1, 2, 2, 64, -1, None, None, None) == LB_EINVAL
 
 
 def test_merge_host_checks(L):

@@ -188,3 +188,76 @@ def test_block_backward_leaves_unseen_rows_and_zeroes_unseen_keys():
     lb.block_attn_bwd(dev_bf16(q[:n]), kv, dev_bf16(do), lse, dvec, q_pos, kv_pos, q_doc, kv_doc, dq, dkv)
     torch.cuda.synchronize()
     assert torch.all(dq == 3.0) and torch.all(dkv == 0.0)
+
+
+def test_block_backward_shared_question_whole_pack():
+    """One block step over a whole shared-question pack with document 0 shared: dq, dk, dv
+    against the varlen shared-question oracle gradient; the key-tile plan (the question's
+    keys with every answer's rows) against the oracle's transposed enumerator."""
+    lengths = [300, 120, 1, 64, 90]
+    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    r = np.random.default_rng(63)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    do = workloads.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32))
+    pos = np.arange(T, dtype=np.int32)
+    doc = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+    i32 = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).cuda()
+    say(f"  block bwd, shared question, T={T}")
+    tq, tdo = dev_bf16(q), dev_bf16(do)
+    kv = torch.stack([dev_bf16(k), dev_bf16(v)]).contiguous()
+    out, lse = lb.block_attn_fwd(tq, kv, i32(pos), i32(pos), i32(doc), i32(doc), shared_doc=0)
+    dvec = lb.attn_bwd_rowdot(out, tdo)
+    dq = torch.zeros((T, H, d), dtype=torch.float32, device="cuda")
+    half = lb.workspace_bytes(T, T, H, Hkv)
+    ws = torch.empty(2 * half + 512, dtype=torch.uint8, device="cuda")
+    _, dkv = lb.block_attn_bwd(tq, kv, tdo, lse, dvec, i32(pos), i32(pos), i32(doc), i32(doc), dq, workspace=ws,
+                               shared_doc=0)
+    torch.cuda.synchronize()
+    ref = OB.varlen_attention_bwd(q, k, v, do, workloads.cu_from_lengths(lengths), H, Hkv, mask="shared_question")
+    for name, got, want in zip(("dq", "dk", "dv"), (to64(dq), to64(dkv[0]), to64(dkv[1])), ref):
+        check_grad(got, want, f"{name} block path, shared question")
+    off = lb.bwd_key_plan_offset(True, T, T, T, H, Hkv, ws.numel())
+    ref_k_tiles = OP.tiles_t(OP.fragments_block_t(pos, doc, pos, doc, shared_doc=0), 128)
+    ref_k = [ref_k_tiles[i] for i in OP.lpt_order(ref_k_tiles)]
+    got = lb.read_plan(ws[off:])
+    assert len(got) == len(ref_k)
+    for i, (a, b) in enumerate(zip(got, ref_k)):
+        assert (a["q_start"], a["q_len"], a["q_pos0"], a["cost"], a["blocks"]) == \
+               (b["q_start"], b["q_len"], b["q_pos0"], b["cost"], b["blocks"]), i
+        assert [tuple(s) for s in a["spans"]] == [tuple(s) for s in b["spans"]], i
+
+
+def test_ring_backward_shared_question_reassembles():
+    """A shared-question pack sharded by sequence zigzag over cp = 4 ranks, document 0
+    shared: each rank's forward ring and ring backward (steps no row sees send nothing back),
+    summed per owner, equal the unsharded shared-question gradient."""
+    from load_balance_amd import sharding as LS
+    cp, H, Hkv, d = 4, 8, 2, 128
+    r = np.random.default_rng(64)
+    lengths = [500, 37, 1, 260, 9, 301]
+    lengths.append(2 * cp * 256 - sum(lengths))
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    do = workloads.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32))
+    tok = LS.shard_tokens("zigzag", lengths, cp)
+    shards = LS.build_shards(lengths, tok, lambda idx: (q[idx], k[idx], v[idx]))
+    ref = OB.varlen_attention_bwd(q, k, v, do, workloads.cu_from_lengths(lengths), H, Hkv, mask="shared_question")
+    dk_sum = [torch.zeros((2, len(t), Hkv, d), dtype=torch.float32, device="cuda") for t in tok]
+    dq_all = np.zeros((T, H, d))
+    for rank in range(cp):
+        share = LS.ShardedRank(shards, rank, shared_doc=0)
+        say(f"  zigzag rank {rank}, shared question: live steps {share.live_steps}")
+        share.run_planned()
+        dq, dkvs = share.backward(dev_bf16(do[tok[rank]]))
+        for st, dkv in zip(share.steps, dkvs):
+            if dkv is not None:
+                dk_sum[st["source"]] += dkv
+        torch.cuda.synchronize()
+        dq_all[tok[rank]] = to64(dq)
+    dk_all = np.zeros((T, Hkv, d))
+    dv_all = np.zeros((T, Hkv, d))
+    for s in range(cp):
+        dk_all[tok[s]] = to64(dk_sum[s][0])
+        dv_all[tok[s]] = to64(dk_sum[s][1])
+    for name, got, want in zip(("dq", "dk", "dv"), (dq_all, dk_all, dv_all), ref):
+        check_grad(got, want, f"zigzag ring {name}, shared question")

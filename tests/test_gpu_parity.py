@@ -625,3 +625,57 @@ def test_lse_merge_matches_oracle(d):
     keep = (lb_ == -np.inf).T
     assert np.array_equal(go[keep], np.float32(oa)[keep])
     assert np.all(np.isfinite(go[rows_fin]))
+
+
+# --------------------------------------------------------------------------
+# the shared-question mask on the block path (a shared document)
+# --------------------------------------------------------------------------
+def test_block_shared_question_whole_pack():
+    """Document 0 shared over a whole shared-question pack: every row against the varlen
+    shared-question oracle, and the plan (FULL spans for the question's keys) against the
+    oracle's enumerator bit for bit."""
+    lengths = [700, 300, 1, 128, 90, 64]
+    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    r = np.random.default_rng(61)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    pos, doc = OA.pack_positions(lengths)
+    i32 = lambda x: torch.from_numpy(np.asarray(x, dtype=np.int32)).cuda()
+    say(f"  block_attn_fwd, shared question, T={T}")
+    kv = torch.stack([dev_bf16(k), dev_bf16(v)]).contiguous()
+    ws = lb.new_workspace(T, T, H, Hkv)
+    out, lse = lb.block_attn_fwd(dev_bf16(q), kv, i32(pos), i32(pos), i32(doc), i32(doc), workspace=ws, shared_doc=0)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    ref_o, ref_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv, mask="shared_question")
+    check(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "block path, shared question")
+    ref_plan = OP.plan(OP.fragments_block(pos, doc, pos, doc, shared_doc=0), lb.tile_rows(H, Hkv, d))
+    assert_same_plan(lb.read_plan(ws), ref_plan, "shared question plan")
+
+
+@pytest.mark.parametrize("rule", ["zigzag", "per_document"])
+def test_sharded_shared_question_reassembles(rule):
+    """A shared-question pack sharded over cp = 4 ranks: each rank's ring with document 0
+    shared (steps without visible pairs run nothing) reassembles the unsharded oracle; the
+    plan-once path is bit-identical to the per-step calls."""
+    from load_balance_amd import sharding as LS
+    cp, H, Hkv, d, C = 4, 8, 2, 128, 256
+    r = np.random.default_rng(62)
+    lengths = [700, 300, 1, 128, 90, 333]
+    lengths.append(2 * cp * C - sum(lengths))
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    tok = LS.shard_tokens(rule, lengths, cp)
+    shards = LS.build_shards(lengths, tok, lambda idx: (q[idx], k[idx], v[idx]))
+    full_o, full_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv, mask="shared_question")
+    for rank in range(cp):
+        share = LS.ShardedRank(shards, rank, shared_doc=0)
+        say(f"  {rule} rank {rank}: live steps {share.live_steps}")
+        out, lse = share.run()
+        out_ref, lse_ref = out.clone(), lse.clone()
+        out, lse = share.run_planned()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref) and torch.equal(lse, lse_ref)
+        for t in share.live_steps:
+            assert lb.read_device_error(share.step_workspaces[t]) == 0
+        check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]],
+              f"{rule} rank {rank}, shared question")

@@ -220,3 +220,48 @@ def test_large_row_lse_statistics():
     _, lse = A.block_attention(q, k, v, [n], np.arange(n), [0], np.zeros(n), 1, 1)
     expect = math.log(n) + (q[0, 0] @ q[0, 0]) / d / 2
     assert abs(lse[0, 0] - expect) < 0.1
+
+
+@pytest.mark.parametrize("lengths", [[24, 9, 1, 17], [1, 5, 30], [40, 40]])
+def test_block_shared_doc_equals_varlen_shared_question(lengths):
+    """The block path with document 0 shared, over a whole pack, is the shared-question mask
+    of the varlen path: answers see the whole question and themselves causally."""
+    T = sum(lengths)
+    q, k, v = rand(T, 4, 8), rand(T, 2, 8), rand(T, 2, 8)
+    pos, doc = A.pack_positions(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    o1, l1 = A.varlen_attention(q, k, v, cu, 4, 2, mask="shared_question")
+    o2, l2 = A.block_attention(q, k, v, pos, pos, doc, doc, 4, 2, shared_doc=0)
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+@pytest.mark.parametrize("cp,chunk", [(2, 24), (4, 16)])
+def test_zigzag_reassembly_with_a_shared_question(cp, chunk):
+    """Every rank of a zigzag sharding of a shared-question pack, its steps merged, equals
+    the unsharded shared-question result: the question's keys reach the answers' rows on
+    whichever rank and step they meet."""
+    T = 2 * cp * chunk
+    r = np.random.default_rng(cp * 100 + chunk)
+    Q = int(r.integers(chunk, 3 * chunk))
+    rest = T - Q
+    answers = []
+    while rest > 0:
+        a = int(min(rest, r.integers(1, 2 * chunk)))
+        answers.append(a)
+        rest -= a
+    lengths = [Q] + answers
+    q, k, v = rand(T, 2, 8), rand(T, 1, 8), rand(T, 1, 8)
+    pos, doc = A.pack_positions(lengths)
+    full_o, full_l = A.varlen_attention(q, k, v, np.concatenate([[0], np.cumsum(lengths)]), 2, 1,
+                                        mask="shared_question")
+    for rank in range(cp):
+        qi = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+        acc = None
+        for step in range(cp):
+            src = A.ring_source(rank, step, cp)
+            ki = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(src, cp)])
+            o, l = A.block_attention(q[qi], k[ki], v[ki], pos[qi], pos[ki], doc[qi], doc[ki], 2, 1, shared_doc=0)
+            acc = (o, l) if acc is None else A.lse_merge(acc[0], acc[1], o, l)
+        np.testing.assert_allclose(acc[0], full_o[qi], atol=1e-12)
+        np.testing.assert_allclose(acc[1], full_l[:, qi], atol=1e-12)

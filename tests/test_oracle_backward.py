@@ -144,3 +144,22 @@ def test_ring_step_partials_reassemble_the_unsharded_gradient(rule):
             dv[ki] += gv
     for got, want in zip((dq, dk, dv), ref):
         assert np.max(np.abs(got - want)) < 1e-11
+
+
+def test_block_shared_doc_equals_varlen_shared_question():
+    """One block step over a whole shared-question pack (document 0 shared), from the block
+    forward's lse and D, gives the varlen shared-question gradient."""
+    from oracle import attention as A
+    r = np.random.default_rng(31)
+    lengths = [20, 7, 1, 13]
+    T, H, Hkv, d = sum(lengths), 4, 2, 8
+    q, k, v = (r.standard_normal((T, h, d)) for h in (H, Hkv, Hkv))
+    do = r.standard_normal((T, H, d))
+    pos, doc = A.pack_positions(lengths)
+    out, lse = A.block_attention(q, k, v, pos, pos, doc, doc, H, Hkv, shared_doc=0)
+    dvec = B.row_dot(out, do)
+    dq, dk, dv = B.block_attention_bwd(q, k, v, do, lse, dvec, pos, pos, doc, doc, H, Hkv, shared_doc=0)
+    rq, rk, rv = B.varlen_attention_bwd(q, k, v, do, np.concatenate([[0], np.cumsum(lengths)]), H, Hkv,
+                                        mask="shared_question")
+    for got, want in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, want, atol=1e-10)

@@ -299,3 +299,67 @@ def test_transposed_tiles_cover_every_visible_pair_once_block(seed):
     # and the pair total equals the forward tiling's
     fwd = P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 16)
     assert sum(t["cost"] for t in fwd) == sum(t["cost"] for t in tl) == int(V.sum())
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("bm", [16, 32])
+@pytest.mark.parametrize("rule", ["zigzag", "per_document"])
+def test_block_shared_doc_brute_force(seed, bm, rule):
+    """Shards of a shared-question pack (document 0 shared), by sequence zigzag or per
+    document (which cuts every document, the shared one too, into several runs per rank, so
+    its FULL runs join): every tile's cost equals the explicit mask count, its spans cover
+    each visible key once, and the transposed tiling covers every visible pair once."""
+    from oracle import sharding as S
+    r = np.random.default_rng(900 + seed)
+    cp = int(r.choice([2, 3, 4]))
+    chunk = int(r.integers(4, 40))
+    T = 2 * cp * chunk
+    lengths = random_lengths(r, T)
+    pos, doc = A.pack_positions(lengths)
+    rank, src = int(r.integers(0, cp)), int(r.integers(0, cp))
+    if rule == "zigzag":
+        qi = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+        ki = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(src, cp)])
+    else:
+        tok = S.per_document_tokens(lengths, cp)
+        qi, ki = tok[rank], tok[src]
+    vis = A.visible_block(pos[qi], doc[qi], pos[ki], doc[ki], np.arange(len(qi)), np.arange(len(ki)), 0)
+    tl = P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=0), bm)
+    brute_check(tl, vis, len(qi))
+    seen = np.zeros(vis.shape, dtype=int)
+    for t in P.tiles_t(P.fragments_block_t(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=0), bm):
+        assert t["cost"] == brute_pairs_of_key_tile(t, lambda i, j: vis[i, j])
+        for j in range(t["q_start"], t["q_start"] + t["q_len"]):
+            for (qs, ql, _) in t["spans"]:
+                seen[qs:qs + ql, j] += vis[qs:qs + ql, j]
+    assert np.array_equal(seen, vis.astype(int))
+
+
+def test_block_shared_doc_pairs_closed_form():
+    """Over a whole shared-question pack the tiles hold Q(Q+1)/2 + sum over answers of
+    A*Q + A(A+1)/2 pairs, forward and transposed."""
+    lengths = [300, 77, 1, 128, 64, 200]
+    Q = lengths[0]
+    want = Q * (Q + 1) // 2 + sum(a * Q + a * (a + 1) // 2 for a in lengths[1:])
+    pos, doc = A.pack_positions(lengths)
+    fwd = P.tiles(P.fragments_block(pos, doc, pos, doc, shared_doc=0), 64)
+    bwd = P.tiles_t(P.fragments_block_t(pos, doc, pos, doc, shared_doc=0), 128)
+    assert sum(t["cost"] for t in fwd) == want
+    assert sum(t["cost"] for t in bwd) == want
+
+
+def test_block_shared_doc_full_runs_join():
+    """FULL runs next to each other in the buffer make one span; a run of the row's own
+    document, or a gap in the buffer, starts a new one.  Spans written out by hand."""
+    far = P.FAR
+    # forward: a query run of document 1 against keys [doc 0 at 0..2 | doc 0 at 10..11 |
+    # doc 1 at 0..1 | doc 0 at 20]
+    q_pos, q_doc = np.arange(4), np.ones(4, dtype=int)
+    kv_pos, kv_doc = np.array([0, 1, 2, 10, 11, 0, 1, 20]), np.array([0, 0, 0, 0, 0, 1, 1, 0])
+    (f,) = P.fragments_block(q_pos, q_doc, kv_pos, kv_doc, shared_doc=0)
+    assert f[3] == [(0, 5, -far), (5, 2, 0), (7, 1, -far)]
+    # transposed: a key run of document 0 (positions 0..3) against query runs [doc 1 | doc 2 |
+    # doc 0 at position 0 | doc 3]: documents 1 and 2 join, document 3 follows the own run
+    q_pos, q_doc = np.array([0, 1, 0, 1, 2, 0, 0]), np.array([1, 1, 2, 2, 2, 0, 3])
+    (f,) = P.fragments_block_t(q_pos, q_doc, np.arange(4), np.zeros(4, dtype=int), shared_doc=0)
+    assert f[3] == [(0, 5, far), (5, 1, 0), (6, 1, far)]

@@ -44,9 +44,35 @@ def test_zigzag_rejects_an_uneven_pack():
         LS.zigzag_tokens(30, 4)
 
 
-def oracle_work(pos, doc, qi, ki, bm):
-    tl = [t for t in OP.tiles(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), bm) if t["blocks"] > 0]
+def oracle_work(pos, doc, qi, ki, bm, shared_doc=None):
+    tl = [t for t in OP.tiles(OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=shared_doc), bm)
+          if t["blocks"] > 0]
     return sum(t["blocks"] for t in tl), len(tl)
+
+
+@pytest.mark.parametrize("rule", ["zigzag", "per_document"])
+def test_predicted_work_with_a_shared_document(rule):
+    """With document 0 shared (a shared question), the key blocks and work items of every
+    rank and step equal the oracle enumerator's, and the steps kept are those with work."""
+    r = np.random.default_rng(77)
+    cp, bm = 4, 64
+    lengths = [900] + [int(x) for x in r.integers(1, 400, 8)]
+    lengths.append(4 * cp * 300 - sum(lengths))
+    tok = LS.shard_tokens(rule, lengths, cp, width=37)
+    pos, doc = A.pack_positions(lengths)
+    for rank in range(cp):
+        qi = tok[rank]
+        sides, want = [], []
+        for step in range(cp):
+            ki = tok[LS.ring_source(rank, step, cp)]
+            got = LS.predicted_work(pos[qi].astype(np.int32), doc[qi].astype(np.int32),
+                                    pos[ki].astype(np.int32), doc[ki].astype(np.int32), bm, 0)
+            ref = oracle_work(pos, doc, qi, ki, bm, shared_doc=0)
+            assert got == ref, (rank, step)
+            sides.append((pos[ki], doc[ki]))
+            if ref[1] > 0:
+                want.append(step)
+        assert LS.live_steps(pos[qi], doc[qi], sides, 0) == want
 
 
 @pytest.mark.parametrize("rule", ["zigzag", "per_document", "striped", "dispatch"])
@@ -147,3 +173,21 @@ def test_live_steps_are_the_steps_with_planned_work(seed):
             if any(len(x["spans"]) for x in tl):
                 want.append(t)
         assert LS.live_steps(pos[qi], doc[qi], sides) == want, (seed, rank)
+
+
+def test_max_spans_with_a_shared_document():
+    """Per-document sharding cuts the shared document into three runs per rank; they join
+    into one FULL span, so every step stays within the planner's limit, forward and in the
+    backward's key-tile plan, equal to the oracle enumerator's largest span count."""
+    cp = 4
+    lengths = [700, 300, 1, 128, 90, 333]
+    lengths.append(2 * cp * 256 - sum(lengths))
+    tok = LS.shard_tokens("per_document", lengths, cp)
+    pos, doc = A.pack_positions(lengths)
+    worst = 0
+    for qi in tok:
+        for ki in tok:
+            fw = OP.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=0)
+            bw = OP.fragments_block_t(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=0)
+            worst = max([worst] + [len(f[3]) for f in fw + bw])
+    assert LS.max_spans(lengths, tok, 0) == worst <= LS.MAX_SPANS
