@@ -198,8 +198,9 @@ class SlicesStep:
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
-    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True, overlap=4):
+    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True, overlap=4, ring=True):
         self.torch, self.lb = torch, lb
+        self.ring = ring
         lengths = workloads.zigzag_pack_lengths(seed)
         cache = {}
 
@@ -213,9 +214,13 @@ class ZigzagStep:
         # the share's 16 launches are replayed from one HIP graph, the attention launches
         # spread over `overlap` streams so that the steps overlap (none: one stream);
         # per-kernel events need eager launches one at a time (run_eager)
-        self.streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap else None
-        self.graph = self.share.capture(streams=self.streams) if graph else None
-        self.kernel_name = "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)"
+        self.streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap and not ring else None
+        if ring:
+            self.share.plan_ring()
+        self.graph = (self.share.capture(ring=True) if ring else self.share.capture(streams=self.streams)) \
+            if graph else None
+        self.kernel_name = ("attn_kernel<128,true,false,ring> (persistent, one LPT queue over the live steps; "
+                            "fp32 partials)" if ring else "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)")
         self.H, self.d = 32, 128
         # pairs: positions and document ids of the rank's rows against each step's chunks
         pos, doc = lb.zigzag.token_meta(lengths)
@@ -233,7 +238,7 @@ class ZigzagStep:
         self.name = f"zigzag cp={cp} rank {rank}"
 
     def n_launches(self):
-        return len(self.share.live_steps)
+        return 1 if self.ring else len(self.share.live_steps)
 
     def run(self, evs=None):
         if self.graph is not None and evs is None:
@@ -243,8 +248,20 @@ class ZigzagStep:
 
     def run_eager(self, evs=None):
         # one planning launch for all steps (their key/value metadata is known up front),
-        # then per step the attention launch and, from step 1 on, the merge
+        # then per step the attention launch and, from step 1 on, the merge; in ring mode
+        # the plans are merged and one attention launch runs every step
         lb, sh = self.lb, self.share
+        if self.ring:
+            if evs is not None:
+                evs[0][0].record()
+            sh.plan_ring()
+            if evs is not None:
+                evs[0][1].record()
+            sh.ring_attention()
+            if evs is not None:
+                evs[0][2].record()
+            sh.merge_partials()
+            return
         if evs is not None:
             evs[0][0].record()
         sh.plan_all()
@@ -268,6 +285,8 @@ class ZigzagStep:
         return None
 
     def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        if self.ring:
+            return self.share.ring_workspace
         return self.share.step_workspaces[self.share.live_steps[0]]
 
 
@@ -277,7 +296,7 @@ class ZigzagBwdStep(ZigzagStep):
     Effective FLOPs 10 * d * H * pairs, 2.5x the forward's."""
 
     def __init__(self, torch, lb, workloads, seed=0):
-        super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0)
+        super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0, ring=False)
         sh = self.share
         sh.run_planned()
         r = np.random.default_rng(2001)
@@ -309,7 +328,7 @@ class CpJob:
     """Every rank's share of a context-parallel job at cp = 8 over the 131072-token pack,
     one after another on this GPU (each share replayed from its own HIP graph)."""
 
-    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0, overlap=4):
+    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0, overlap=4, ring=True):
         from load_balance_amd import sharding as LS
         self.torch, self.lb = torch, lb
         lengths = workloads.zigzag_pack_lengths(seed)
@@ -319,9 +338,13 @@ class CpJob:
         self.tokens = LS.shard_tokens(base, lengths, cp, n_chunks=n_chunks)
         shards = LS.build_shards(lengths, self.tokens, lambda idx: (q[idx], k[idx], v[idx]))
         self.shares = [LS.ShardedRank(shards, r) for r in range(cp)]
-        streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap else None
+        streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap and not ring else None
+        self.ring = ring
         for s in self.shares:
-            s.capture(streams=streams)
+            if ring:
+                s.capture(ring=True)
+            else:
+                s.capture(streams=streams)
         self.H, self.d = 32, 128
         pos_in_doc = np.concatenate([np.arange(n) for n in lengths])
         self.rank_pairs = [int(np.sum(pos_in_doc[t] + 1)) for t in self.tokens]
@@ -349,13 +372,15 @@ class CpJob:
         return None
 
     def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        if self.ring:
+            return self.shares[0].ring_workspace
         return self.shares[0].step_workspaces[self.shares[0].live_steps[0]]
 
 
 CP_RULES = ("zigzag", "per_document", "dispatch/16", "dispatch/32", "dispatch/64", "dispatch/128")
 
 
-def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4):
+def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4, ring=True):
     if name == "longtail":
         p = workloads.longtail_pack(seed)
         w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -388,13 +413,15 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
         w.packs = [p]
         return w
     if name == "zigzag":
-        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph, overlap=overlap)
+        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph, overlap=overlap, ring=ring)
         w.config = {"workload": "one zigzag CP rank's share at cp=8: rank 3 of a 131072-token lognormal pack "
                                 f"(seed {seed}), 16 chunks of 8192, 8 ring steps and a merge per step after the "
                                 "first; steps whose chunks hold no key the rank's rows see (5 of 8 here, found on "
                                 "the host from positions and document ids) run nothing",
                     "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
-                    "launch": (f"one HIP graph: plan, the live steps' attention launches on {overlap} streams, merges "
+                    "launch": ("one HIP graph: the live steps' plans (one launch) merged into one longest-first "
+                               "queue, one attention launch over every live step, merges in step order" if ring else
+                               f"one HIP graph: plan, the live steps' attention launches on {overlap} streams, merges "
                                "in step order" if overlap else "one HIP graph, one stream") if graph else "eager"}
         return w
     if name == "blockcausal":
@@ -455,7 +482,7 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w
     if name == "cp_job":
-        w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap)
+        w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap, ring=ring)
         w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
                                 f"{rule} sharding: all 8 ranks' shares (8 ring steps + 7 merges each) in turn",
                     "tokens": 131072, "heads": 32, "kv_heads": 8, "head_dim": 128, "sharding": rule,
@@ -550,6 +577,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="zigzag, cp_job: one attention launch per live step instead of one over all of them")
     ap.add_argument("--overlap", type=int, default=4,
                     help="zigzag, cp_job: streams the ring steps' attention launches are spread over (0: one)")
     ap.add_argument("--worker-records", default=None, metavar="PATH",
@@ -577,7 +606,7 @@ def main():
     lb.lib()
     log(f"bench: building workload {args.workload}")
     w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule,
-                      overlap=args.overlap)
+                      overlap=args.overlap, ring=not args.no_ring)
     graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 

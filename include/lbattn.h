@@ -222,6 +222,48 @@ lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_
                               int32_t n_steps, int32_t heads, int32_t kv_heads, int32_t d, int32_t shared_doc,
                               void* const* workspaces, const size_t* workspace_bytes, hipStream_t stream);
 
+/*
+ * One rank's ring in one attention launch.  A rank's ring runs one block step per chunk
+ * it receives ("长序列训练与上下文并行", Ring Attention), and each step is a persistent
+ * launch whose end waits for its largest items: a light step leaves most compute units
+ * idle.  Merging the steps' plans gives one longest-first queue over the work of every
+ * step ("数据并行负载均衡", section 4.4: LPT over all items; "03 · 长文负载均衡", section
+ * 3.2: only blocks with visible pairs become work), and one launch runs it, each step's
+ * partial (out, lse) into its own buffers as lb_attn_run would write it, bit for bit.  The
+ * partials are then merged with lb_lse_merge in step order, as before.
+ *
+ * lb_ring_workspace_bytes: bytes of a ring workspace for n_steps steps, each within the
+ *   bounds given to lb_workspace_bytes (0 if out of range).
+ * lb_plan_ring: merges the plans in workspaces[0..n_steps) (made by lb_plan_block or
+ *   lb_plan_block_steps for the same query shard of n_q tokens, step s against n_kv[s]
+ *   key/value tokens; host arrays holding device pointers) into ring_workspace (256-byte
+ *   aligned, distinct from the step workspaces).  The tiles are copied in queue order:
+ *   key blocks descending, then step, then the step's own order; each tile's `reserved`
+ *   field holds its step; the steps' empty tiles follow.  A step plan that is not a
+ *   forward block plan for these shapes sets LB_DEVERR_PLAN in the ring's error word, a
+ *   step's own error bits pass on, more work tiles than 16384 (or than the workspace
+ *   holds) set LB_DEVERR_CAPACITY; the ring then runs nothing.  Plan the ring again
+ *   after any of its steps is planned again.  lb_read_plan, lb_read_device_error and
+ *   lb_read_worker_timing read a ring workspace too.
+ * lb_ring_attn_run: runs the ring's items.  q: bf16 [n_q][heads][d]; k[s], v[s]: bf16
+ *   [n_kv[s]][kv_heads][d]; out[s]: fp32 [n_q][heads][d]; lse[s]: fp32 [heads][n_q]; all
+ *   host arrays of n_steps device pointers, out and lse distinct per step.  Rows with no
+ *   visible key in step s get lse[s] = -inf and out[s] unwritten, as lb_attn_run.  A ring
+ *   made for other shapes or other n_kv sets LB_DEVERR_PLAN and runs nothing.  Argument
+ *   errors return LB_EINVAL / LB_EUNSUPPORTED / LB_EWORKSPACE before anything is enqueued.
+ */
+size_t lb_ring_workspace_bytes(int32_t n_steps, int32_t max_tokens, int32_t max_segments, int32_t heads,
+                               int32_t kv_heads);
+
+lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                       int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                       void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream);
+
+lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d, int32_t n_steps,
+                           const void* const* k, const void* const* v, const int32_t* n_kv, float* const* out,
+                           float* const* lse, void* ring_workspace, size_t ring_workspace_bytes,
+                           hipStream_t stream);
+
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);

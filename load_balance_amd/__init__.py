@@ -84,6 +84,12 @@ def lib() -> ctypes.CDLL:
     L.lb_plan_block.restype = ctypes.c_int
     L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P]
     L.lb_plan_block_steps.restype = ctypes.c_int
+    L.lb_ring_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    L.lb_ring_workspace_bytes.restype = SZ
+    L.lb_plan_ring.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_ring.restype = ctypes.c_int
+    L.lb_ring_attn_run.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    L.lb_ring_attn_run.restype = ctypes.c_int
     L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run.restype = ctypes.c_int
     L.lb_attn_run_lower.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
@@ -249,6 +255,53 @@ def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d,
     return workspaces
 
 
+def ring_workspace_bytes(n_steps: int, max_tokens: int, max_segments: int, heads: int, kv_heads: int) -> int:
+    n = int(lib().lb_ring_workspace_bytes(n_steps, max_tokens, max_segments, heads, kv_heads))
+    if n == 0:
+        raise LBError("lb_ring_workspace_bytes: invalid or unsupported arguments")
+    return n
+
+
+def new_ring_workspace(n_steps: int, max_tokens: int, max_segments: int, heads: int, kv_heads: int, device="cuda"):
+    """A uint8 device tensor for the merged plan of up to n_steps block steps."""
+    return torch.empty(ring_workspace_bytes(n_steps, max_tokens, max_segments, heads, kv_heads), dtype=torch.uint8,
+                       device=device)
+
+
+def plan_ring(workspaces, n_kv, n_q, heads, kv_heads, d, ring_workspace, stream=None):
+    """Merges the block-step plans in ``workspaces`` (step s made against n_kv[s] key/value
+    tokens, all for the same n_q query rows) into one longest-first queue in ring_workspace."""
+    n = len(workspaces)
+    if len(n_kv) != n:
+        raise LBError("n_kv must have one entry per workspace")
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[w.data_ptr() for w in workspaces])
+    sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
+    nkv = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in n_kv])
+    _check(lib().lb_plan_ring(ptrs, sizes, nkv, n, n_q, heads, kv_heads, d, _ptr(ring_workspace),
+                              ring_workspace.numel(), ctypes.c_void_p(_stream(stream))), "lb_plan_ring")
+    return ring_workspace
+
+
+def ring_attn_run(q, ks, vs, outs, lses, ring_workspace, stream=None):
+    """Runs a ring workspace's items in one launch: step s reads ks[s], vs[s] (bf16
+    [n_kv_s,H_kv,d]) and writes its partial into outs[s] (fp32 [n_q,H,d]) and lses[s]
+    (fp32 [H,n_q]), as attn_run would for that step's own plan."""
+    n_q, H, d = q.shape
+    n = len(ks)
+    if not (len(vs) == len(outs) == len(lses) == n):
+        raise LBError("ks, vs, outs and lses must have one entry per step")
+    for o, l in zip(outs, lses):
+        if o.dtype != torch.float32 or l.dtype != torch.float32:
+            raise LBError("ring partials are float32")
+    Hkv = ks[0].shape[1]
+    ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
+    nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[0] for k in ks])
+    _check(lib().lb_ring_attn_run(_ptr(q), n_q, H, Hkv, d, n, ptrs(ks), ptrs(vs), nkv, ptrs(outs), ptrs(lses),
+                                  _ptr(ring_workspace), ring_workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_ring_attn_run")
+    return outs, lses
+
+
 def attn_run(q, k, v, out, lse, workspace, stream=None):
     """Second half of either forward: runs the plan held in ``workspace``.
 
@@ -293,8 +346,9 @@ def read_device_error(workspace, stream=None) -> int:
     return err.value
 
 
-def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
-    """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost, blocks)."""
+def read_plan(workspace, max_tiles: int = 1 << 16, stream=None, with_step=False):
+    """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost, blocks);
+    with_step adds each tile's step (a ring workspace's `reserved` field)."""
     buf = (PlanTile * max_tiles)()
     n = ctypes.c_int32(0)
     _check(lib().lb_read_plan(_ptr(workspace), workspace.numel(), buf, max_tiles, ctypes.byref(n),
@@ -307,6 +361,8 @@ def read_plan(workspace, max_tiles: int = 1 << 16, stream=None):
                  for s in range(t.n_spans)]
         out.append(dict(q_start=t.q_start, q_len=t.q_len, q_pos0=t.q_pos0, spans=spans, cost=t.cost,
                         blocks=t.blocks))
+        if with_step:
+            out[-1]["step"] = t.reserved
     return out
 
 

@@ -326,6 +326,90 @@ lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_
   return launch_plan_steps(b, n_steps, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
+size_t lb_ring_workspace_bytes(int32_t n_steps, int32_t max_tokens, int32_t max_segments, int32_t heads,
+                               int32_t kv_heads) {
+  if (n_steps < 1 || n_steps > kMaxPlanSteps || max_tokens < 0 || max_segments < 1 ||
+      !group_supported(heads, kv_heads))
+    return 0;
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  const int64_t tiles = (int64_t)n_steps * std::min<int64_t>(kSortCap, ceil_div(max_tokens, bm) + max_segments);
+  return (size_t)align256(kRingTilesOffset + tiles * (int64_t)sizeof(lb_plan_tile));
+}
+
+lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                       int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                       void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream) {
+  if (n_steps < 1 || n_steps > kMaxPlanSteps || n_q < 0) return LB_EINVAL;
+  if (!workspaces || !workspace_bytes || !n_kv || !ring_workspace) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(ring_workspace, 256)) return LB_EWORKSPACE;
+  const int64_t cap = ((int64_t)ring_workspace_bytes - kRingTilesOffset) / (int64_t)sizeof(lb_plan_tile);
+  if (cap < 1) return LB_EWORKSPACE;
+  RingMergeArgs m{};
+  for (int s = 0; s < n_steps; ++s) {
+    if (!workspaces[s] || n_kv[s] < 0) return LB_EINVAL;
+    if (!aligned(workspaces[s], 256) || workspace_bytes[s] < sizeof(WsHeader)) return LB_EWORKSPACE;
+    if (workspaces[s] == ring_workspace) return LB_EINVAL;
+    m.step_ws[s] = static_cast<const char*>(workspaces[s]);
+    m.step_ws_bytes[s] = (int64_t)workspace_bytes[s];
+    m.n_kv[s] = n_kv[s];
+  }
+  m.n_steps = n_steps;
+  m.n_q = n_q;
+  m.heads = heads;
+  m.kv_heads = kv_heads;
+  m.ring = static_cast<char*>(ring_workspace);
+  m.ring_cap = (int32_t)std::min<int64_t>(cap, INT32_MAX);
+  return launch_ring_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d, int32_t n_steps,
+                           const void* const* k, const void* const* v, const int32_t* n_kv, float* const* out,
+                           float* const* lse, void* ring_workspace, size_t ring_workspace_bytes,
+                           hipStream_t stream) {
+  if (n_steps < 1 || n_steps > kMaxPlanSteps || n_q < 0) return LB_EINVAL;
+  if (!q || !k || !v || !n_kv || !out || !lse || !ring_workspace) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(q, 16)) return LB_EINVAL;
+  if (!aligned(ring_workspace, 256)) return LB_EWORKSPACE;
+  if ((int64_t)ring_workspace_bytes < kRingTilesOffset) return LB_EWORKSPACE;
+  RingSteps r{};
+  for (int s = 0; s < n_steps; ++s) {
+    if (n_kv[s] < 0 || !out[s] || !lse[s]) return LB_EINVAL;
+    if (!aligned(out[s], 16) || !aligned(lse[s], 4)) return LB_EINVAL;
+    for (int o = 0; o < s; ++o)
+      if (out[o] == out[s] || lse[o] == lse[s]) return LB_EINVAL;  // each step writes its own partial
+    if (n_kv[s] > 0 && (!k[s] || !v[s] || !aligned(k[s], 16) || !aligned(v[s], 16))) return LB_EINVAL;
+    r.k[s] = n_kv[s] > 0 ? k[s] : q;
+    r.v[s] = n_kv[s] > 0 ? v[s] : q;
+    r.out[s] = out[s];
+    r.lse[s] = lse[s];
+    r.n_kv[s] = n_kv[s];
+  }
+  r.n_steps = n_steps;
+  if (n_q == 0) return LB_OK;
+  int workers = 0;
+  st = persistent_workers(&workers);
+  if (st != LB_OK) return st;
+  AttnArgs at{};
+  at.q = q;
+  at.k = q;
+  at.v = q;
+  at.out = out[0];
+  at.lse = lse[0];
+  at.n_q = n_q;
+  at.n_kv = 0;
+  at.heads = heads;
+  at.kv_heads = kv_heads;
+  at.group = heads / kv_heads;
+  at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
+  at.ws = static_cast<char*>(ring_workspace);
+  at.ws_bytes = (int64_t)ring_workspace_bytes;
+  return launch_ring_attention(at, r, d, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
@@ -578,10 +662,14 @@ lb_status lb_read_plan(const void* workspace, size_t workspace_bytes, lb_plan_ti
   std::vector<int32_t> order(h.n_tiles);
   std::vector<lb_plan_tile> nat(h.n_tiles);
   const char* base = static_cast<const char*>(workspace);
-  if (hipMemcpy(order.data(), base + h.off_order, order.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(nat.data(), base + h.off_tiles, nat.size() * sizeof(lb_plan_tile), hipMemcpyDeviceToHost) !=
-          hipSuccess)
+  if (hipMemcpy(nat.data(), base + h.off_tiles, nat.size() * sizeof(lb_plan_tile), hipMemcpyDeviceToHost) !=
+      hipSuccess)
     return LB_EHIP;
+  if (h.magic == kRingMagic) {  // a ring workspace stores its tiles in queue order
+    for (int i = 0; i < h.n_tiles; ++i) order[i] = i;
+  } else if (hipMemcpy(order.data(), base + h.off_order, order.size() * 4, hipMemcpyDeviceToHost) != hipSuccess) {
+    return LB_EHIP;
+  }
   for (int i = 0; i < n; ++i) {
     const int32_t j = order[i];
     if (j < 0 || j >= h.n_tiles) return LB_EHIP;

@@ -184,8 +184,12 @@ struct KvBlock {
 // LOWER: spans may carry a lower bound on their visible keys (INV-CAUSAL and BI-CAUSAL
 // slices).  Without it the kernel refuses such plans: the bound costs scalar registers in
 // the key loop, so the common instance goes without.
-template <int D, bool OUT_F32, bool LOWER>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+// RING: the workspace is a ring workspace, several block steps' tiles in one longest-first
+// queue; a tile's step (its `reserved` field) selects the keys, values and outputs of that
+// step in r.  One launch then runs every step of a rank's ring, each step's partial into its
+// own buffers, with no tail per step.
+template <int D, bool OUT_F32, bool LOWER, bool RING>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps r) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
   __shared__ int s_item;
   // Thread 0's bookkeeping (queue state, counts for the worker record) lives in LDS, so that
@@ -212,7 +216,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   // A missing plan, or one made for other shapes or another workspace size, could index
   // outside this launch's buffers: then run nothing and flag it.
   const int64_t n_tiles_hdr = hdr->n_tiles;
-  const bool mismatch = hdr->magic != kPlanMagic || hdr->transposed != 0 || (!LOWER && hdr->has_lower != 0) ||
+  bool mismatch = hdr->magic != (RING ? kRingMagic : kPlanMagic) || hdr->transposed != 0 ||
+                  (!LOWER && hdr->has_lower != 0) ||
                         hdr->plan_n_q != a.n_q ||
                         hdr->plan_n_kv != a.n_kv ||
                         hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
@@ -223,10 +228,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
                         hdr->off_tiles < kWorkersOffset || hdr->off_order < kWorkersOffset ||
                         hdr->off_tiles + n_tiles_hdr * (int64_t)sizeof(lb_plan_tile) > a.ws_bytes ||
                         hdr->off_order + n_tiles_hdr * 4 > a.ws_bytes;
+  if constexpr (RING) {
+    // the ring was merged from plans made for these steps' key/value counts
+    mismatch = mismatch || r.n_steps < 1 || r.n_steps > kMaxPlanSteps || hdr->ring_steps != r.n_steps;
+#pragma unroll
+    for (int s = 0; s < kMaxPlanSteps; ++s)
+      if (s < r.n_steps && hdr->ring_n_kv[s] != r.n_kv[s]) mismatch = true;
+  }
   const int n_items = mismatch ? 0 : hdr->n_items;
   const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + (mismatch ? 0 : hdr->off_tiles));
   const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + (mismatch ? 0 : hdr->off_order));
   if (mismatch && blockIdx.x == 0 && tid == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
+  // the tile at queue position i: through the plan's order, or (ring) stored in queue order
+  auto tile_at = [&](int64_t i) -> const lb_plan_tile* {
+    if constexpr (RING) return &tiles[i];
+    else return &tiles[order[i]];
+  };
+  // a ring tile's step, kept inside the launch's step table
+  auto step_of = [&](const lb_plan_tile* T) -> int {
+    return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
+  };
 
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
   const char* Kb = reinterpret_cast<const char*>(a.k);
@@ -253,10 +274,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   {
     const int n_empty = mismatch ? 0 : hdr->n_empty;
     for (int e = blockIdx.x; e < n_empty; e += gridDim.x) {
-      const lb_plan_tile* T = &tiles[order[n_tiles_hdr - n_empty + e]];
+      const lb_plan_tile* T = tile_at(n_tiles_hdr - n_empty + e);
       const int q_start = T->q_start, q_len = T->q_len;
+      float* lse_e = a.lse;
+      if constexpr (RING) lse_e = r.lse[step_of(T)];
       for (int idx = tid; idx < q_len * a.heads; idx += kThreads)
-        a.lse[(int64_t)(idx / q_len) * a.n_q + q_start + idx % q_len] = -__builtin_inff();
+        lse_e[(int64_t)(idx / q_len) * a.n_q + q_start + idx % q_len] = -__builtin_inff();
     }
   }
 
@@ -317,10 +340,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   auto issue_item_loads = [&](int item) {
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
     const int g = q_of + n_queues * (k_in % heads_per_queue);
-    const lb_plan_tile* T = &tiles[order[k_in / heads_per_queue]];
+    const lb_plan_tile* T = tile_at(k_in / heads_per_queue);
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    const char* Kx = Kb;
+    const char* Vx = Vb;
+    if constexpr (RING) {
+      const int st = step_of(T);
+      Kx = reinterpret_cast<const char*>(r.k[st]);
+      Vx = reinterpret_cast<const char*>(r.v[st]);
+    }
     const int k_start0 = __builtin_amdgcn_readfirstlane(T->k_start[0]);
     const int k_len0 = __builtin_amdgcn_readfirstlane(T->k_len[0]);
     // one buffer over this wave's rows of the tile: no branches (a branch around a load
@@ -339,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
-    if (n_spans > 0) ld.load(Kb, Vb, k_start0, k_len0, row_bytes, g, tid);
+    if (n_spans > 0) ld.load(Kx, Vx, k_start0, k_len0, row_bytes, g, tid);
   };
   // Items are popped one ahead of the one whose loads go out: thread 0 issues the atomic in
   // an item's epilogue and completes the pop at the next item's start, so the round trip
@@ -355,7 +385,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
     const int q_of = qitem / max(per_queue, 1), k_in = qitem - q_of * per_queue;
     const int g = q_of + n_queues * (k_in % heads_per_queue);
-    const lb_plan_tile* T = &tiles[order[k_in / heads_per_queue]];
+    const lb_plan_tile* T = tile_at(k_in / heads_per_queue);
+    const char* Kit = Kb;
+    const char* Vit = Vb;
+    int step = 0;
+    if constexpr (RING) {
+      step = step_of(T);
+      Kit = reinterpret_cast<const char*>(r.k[step]);
+      Vit = reinterpret_cast<const char*>(r.v[step]);
+    }
     // tile fields, read once and kept wave-uniform
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
@@ -535,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         if (nx_s < n_spans) nxt = span_of(nx_s);
       }
       const bool has_next = it + 1 < n_kv_tiles;
-      if (has_next) ld.load(Kb, Vb, nxt.start + nxt.key0, nxt.len - nxt.key0, row_bytes, g, tid);
+      if (has_next) ld.load(Kit, Vit, nxt.start + nxt.key0, nxt.len - nxt.key0, row_bytes, g, tid);
       const char* stage = smem + (it % kStages) * Lds<D>::stage;
       const char* prev_stage = smem + ((it + kStages - 1) % kStages) * Lds<D>::stage;
       const bool cur_live = live(cur);
@@ -606,14 +644,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
             }
           }
       }
+      float* lse_out = a.lse;
+      if constexpr (RING) lse_out = r.lse[step];
       if (pass == 0 && row_real && hh == 0)
-        a.lse[(int64_t)head * a.n_q + grow] = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
+        lse_out[(int64_t)head * a.n_q + grow] = empty ? -__builtin_inff() : (m_used + __builtin_log2f(l_tot)) * kLn2;
       // LDS instructions of one wave complete in order: the reads below see the writes above.
       // One step of 64 lanes covers kRowsPerStep whole rows.
       constexpr int kRowsPerStep = 64 / Epi::kChunks;
       const int row0 = lane_e / Epi::kChunks, ch = lane_e % Epi::kChunks;
       const char* src = ebuf + row0 * Epi::kStride + ch * 16;
-      char* dst = reinterpret_cast<char*>(a.out) +
+      char* out_base = reinterpret_cast<char*>(a.out);
+      if constexpr (RING) out_base = reinterpret_cast<char*>(r.out[step]);
+      char* dst = out_base +
                   (((int64_t)q_start + wr0 + r_lo + row0) * a.heads + head) * Epi::kRowBytes + ch * 16;
       const int64_t dst_step = (int64_t)kRowsPerStep * a.heads * Epi::kRowBytes;
 #pragma unroll
@@ -652,8 +694,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 
 template <int D, bool OUT_F32>
 static void launch_d(const AttnArgs& a, bool lower, int n_workers, hipStream_t s) {
-  if (lower) hipLaunchKernelGGL((attn_kernel<D, OUT_F32, true>), dim3(n_workers), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((attn_kernel<D, OUT_F32, false>), dim3(n_workers), dim3(kThreads), 0, s, a);
+  const RingSteps none{};
+  if (lower) hipLaunchKernelGGL((attn_kernel<D, OUT_F32, true, false>), dim3(n_workers), dim3(kThreads), 0, s, a, none);
+  else hipLaunchKernelGGL((attn_kernel<D, OUT_F32, false, false>), dim3(n_workers), dim3(kThreads), 0, s, a, none);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, int n_workers, hipStream_t s) {
@@ -662,6 +705,12 @@ hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, 
   } else {
     if (out_f32) launch_d<64, true>(a, lower, n_workers, s); else launch_d<64, false>(a, lower, n_workers, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, hipStream_t s) {
+  if (d == 128) hipLaunchKernelGGL((attn_kernel<128, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+  else hipLaunchKernelGGL((attn_kernel<64, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
   return hipGetLastError();
 }
 

@@ -49,9 +49,16 @@ struct WsHeader {
   int32_t transposed;   // 1: tiles are key blocks and spans are query runs (the backward's dK/dV plan)
   int32_t has_lower;    // 1: some span has a lower bound (needs the bounded attention kernel)
   int32_t queue_head[8];  // next item of each queue
+  // ring workspaces only (magic kRingMagic): the steps merged, and each step's key/value count
+  int32_t ring_steps;
+  int32_t ring_n_kv[LB_MAX_PLAN_STEPS];
 };
 
 constexpr uint32_t kPlanMagic = 0x4C424154u;
+// A ring workspace: the work tiles of several block steps in one longest-first order, copied
+// from the steps' plans with the step index in each tile's `reserved` field, then the steps'
+// empty tiles; header and worker records laid out as in a plan workspace.
+constexpr uint32_t kRingMagic = 0x4C42524Eu;
 constexpr int64_t kWorkersOffset = 256;  // worker records sit right after the header
 static_assert(sizeof(WsHeader) <= 256, "header must fit its slot");
 
@@ -123,6 +130,31 @@ struct PlanBatch {
   PlanArgs step[kMaxPlanSteps];
 };
 
+// Ring workspace layout: header, worker records, then the merged tiles.
+constexpr int64_t kRingTilesOffset = (kWorkersOffset + kMaxWorkers * (int64_t)sizeof(lb_worker_record) + 255) &
+                                     ~int64_t(255);
+
+// Merge of several block steps' plans into one ring workspace (one workgroup).
+struct RingMergeArgs {
+  const char* step_ws[kMaxPlanSteps];
+  int64_t step_ws_bytes[kMaxPlanSteps];
+  int32_t n_kv[kMaxPlanSteps];
+  int32_t n_steps;
+  int32_t n_q, heads, kv_heads;
+  char* ring;
+  int32_t ring_cap;  // tiles the ring workspace holds
+};
+
+// Per-step operands of a ring attention launch (indexed by a tile's step).
+struct RingSteps {
+  const void* k[kMaxPlanSteps];
+  const void* v[kMaxPlanSteps];
+  float* out[kMaxPlanSteps];
+  float* lse[kMaxPlanSteps];
+  int32_t n_kv[kMaxPlanSteps];
+  int32_t n_steps;
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -175,6 +207,8 @@ struct BwdArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, int n_workers, hipStream_t s);
+hipError_t launch_ring_merge(const RingMergeArgs& m, hipStream_t s);
+hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,

@@ -586,7 +586,157 @@ __global__ __launch_bounds__(NT) void plan_steps_kernel(PlanBatch b) {
   plan_body(a, sh);
 }
 
+// ---- the ring: several steps' plans merged into one longest-first queue ----------------
+// The work tiles of all steps, ordered by key blocks (descending), then step, then their
+// place in the step's own order: the same longest-first rule over the union, so that one
+// persistent launch can run every step with no tail per step.  Each step's plan is already
+// sorted, so a tile's place in the union is its place in its own step plus, for every other
+// step, the number of that step's tiles that go before it (a binary search in LDS).  The
+// tiles are copied in that order, each with its step in `reserved`, and the steps' empty
+// tiles follow.
+__device__ __forceinline__ int count_before(const int32_t* blk, int n, int b, bool ties_before) {
+  // blk[0..n) is descending: entries > b (and == b when ties_before) come first
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int x = blk[mid];
+    if (x > b || (ties_before && x == b)) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void copy_tile(lb_plan_tile* dst, const lb_plan_tile* src, int step) {
+  static_assert(sizeof(lb_plan_tile) % 16 == 0, "");
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(lb_plan_tile) / 16); ++i) d4[i] = s4[i];
+  dst->reserved = step;
+}
+
+__global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
+  __shared__ int32_t blk[kSortCap];  // key blocks of the work tiles, step after step
+  __shared__ int32_t src[kSortCap];  // their index in the step's tile array
+  __shared__ int32_t base[kMaxPlanSteps + 1], ebase[kMaxPlanSteps + 1];
+  __shared__ const lb_plan_tile* tiles_of[kMaxPlanSteps];
+  __shared__ const int32_t* order_of[kMaxPlanSteps];
+  __shared__ int32_t ntiles_of[kMaxPlanSteps];
+  __shared__ int32_t err;       // written by thread 0 before the first barrier only
+  __shared__ int32_t err_tiles;  // bad order entries found by the copy loops
+  __shared__ int64_t pairs;
+  const int tid = threadIdx.x;
+  const int n_steps = m.n_steps;
+  WsHeader* rh = reinterpret_cast<WsHeader*>(m.ring);
+  lb_plan_tile* out = reinterpret_cast<lb_plan_tile*>(m.ring + kRingTilesOffset);
+
+  if (tid == 0) {
+    int e = 0;
+    int64_t p = 0;
+    base[0] = ebase[0] = 0;
+    for (int s = 0; s < n_steps; ++s) {
+      const WsHeader* h = reinterpret_cast<const WsHeader*>(m.step_ws[s]);
+      const int64_t nt = h->n_tiles, ne = h->n_empty;
+      // a step's plan must be a forward block plan made for these shapes, and lie inside
+      // its workspace; its own error bits pass on
+      const bool bad = h->magic != kPlanMagic || h->transposed != 0 || h->has_lower != 0 ||
+                       h->plan_n_q != m.n_q || h->plan_n_kv != m.n_kv[s] || h->plan_heads != m.heads ||
+                       h->plan_kv_heads != m.kv_heads || nt < 0 || ne < 0 || ne > nt ||
+                       h->off_tiles < kWorkersOffset || h->off_order < kWorkersOffset ||
+                       h->off_tiles + nt * (int64_t)sizeof(lb_plan_tile) > m.step_ws_bytes[s] ||
+                       h->off_order + nt * 4 > m.step_ws_bytes[s];
+      if (bad) e |= LB_DEVERR_PLAN;
+      if (!bad) e |= h->err;
+      const int work = bad ? 0 : (int)(nt - ne), empty = bad ? 0 : (int)ne;
+      base[s + 1] = base[s] + work;
+      ebase[s + 1] = ebase[s] + empty;
+      tiles_of[s] = reinterpret_cast<const lb_plan_tile*>(m.step_ws[s] + (bad ? 0 : h->off_tiles));
+      order_of[s] = reinterpret_cast<const int32_t*>(m.step_ws[s] + (bad ? 0 : h->off_order));
+      ntiles_of[s] = bad ? 0 : (int)nt;
+      p += bad ? 0 : h->total_pairs;
+    }
+    if (base[n_steps] > kSortCap || (int64_t)base[n_steps] + ebase[n_steps] > m.ring_cap) e |= LB_DEVERR_CAPACITY;
+    err = e;
+    err_tiles = 0;
+    pairs = p;
+  }
+  __syncthreads();
+  const int M = base[n_steps], E = ebase[n_steps];
+  const bool steps_ok = err == 0;  // the same for every thread: err is not written again
+  if (steps_ok) {
+    for (int j = tid; j < M; j += NT) {
+      int s = 0;
+      while (j >= base[s + 1]) ++s;
+      int t = order_of[s][j - base[s]];
+      if (t < 0 || t >= ntiles_of[s]) {  // an order entry outside the step's tiles: refuse the ring
+        atomicOr(&err_tiles, LB_DEVERR_PLAN);
+        t = 0;
+      }
+      src[j] = t;
+      blk[j] = tiles_of[s][t].blocks;
+    }
+  }
+  __syncthreads();
+  // (no barrier below depends on err_tiles: a thread that sees it set late only copies
+  // tiles of a ring that is refused anyway)
+  if (steps_ok && err_tiles == 0) {
+    for (int j = tid; j < M; j += NT) {
+      int s = 0;
+      while (j >= base[s + 1]) ++s;
+      const int b = blk[j];
+      int rank = j - base[s];
+      for (int o = 0; o < n_steps; ++o)
+        if (o != s) rank += count_before(blk + base[o], base[o + 1] - base[o], b, o < s);
+      copy_tile(&out[rank], &tiles_of[s][src[j]], s);
+    }
+    for (int j = tid; j < E; j += NT) {
+      int s = 0;
+      while (j >= ebase[s + 1]) ++s;
+      const int t = order_of[s][ntiles_of[s] - (ebase[s + 1] - ebase[s]) + (j - ebase[s])];
+      if (t >= 0 && t < ntiles_of[s]) copy_tile(&out[M + j], &tiles_of[s][t], s);
+      else atomicOr(&err_tiles, LB_DEVERR_PLAN);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    err |= err_tiles;
+    const bool ok = err == 0;
+    const int nq = m.kv_heads % kXcds == 0 ? kXcds : 1;
+    rh->err = err;
+    rh->n_frags = 0;
+    rh->n_kvruns = 0;
+    rh->n_tiles = ok ? M + E : 0;
+    rh->n_empty = ok ? E : 0;
+    rh->n_items = ok ? M * m.kv_heads : 0;
+    rh->n_queues = nq;
+    rh->per_queue = (ok ? M * m.kv_heads : 0) / nq;
+    for (int q = 0; q < kXcds; ++q) rh->queue_head[q] = 0;
+    rh->tile_rows = 0;
+    rh->n_workers = 0;
+    rh->off_frags = rh->off_kvruns = 0;
+    rh->off_tiles = rh->off_order = kRingTilesOffset;  // queue order is storage order
+    rh->off_workers = kWorkersOffset;
+    rh->cap_frags = 0;
+    rh->cap_tiles = m.ring_cap;
+    rh->total_pairs = ok ? pairs : 0;
+    rh->transposed = 0;
+    rh->has_lower = 0;
+    rh->plan_n_q = m.n_q;
+    rh->plan_n_kv = 0;
+    rh->plan_heads = m.heads;
+    rh->plan_kv_heads = m.kv_heads;
+    rh->ring_steps = n_steps;
+    for (int s = 0; s < kMaxPlanSteps; ++s) rh->ring_n_kv[s] = s < n_steps ? m.n_kv[s] : 0;
+    rh->done = 0;
+    rh->magic = kRingMagic;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ring_merge(const RingMergeArgs& m, hipStream_t s) {
+  hipLaunchKernelGGL(ring_merge_kernel, dim3(1), dim3(NT), 0, s, m);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, s, a);

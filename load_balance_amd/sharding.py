@@ -488,15 +488,63 @@ class ShardedRank:
                            shared_doc=self.shared_doc)
         return b["dq"], [b["dkv"][t] if t in self.live_steps else None for t in range(len(self.steps))]
 
-    def capture(self, stream=None, streams=None):
+    def plan_ring(self, stream=None):
+        """plan_all(), then the live steps' plans merged into one longest-first queue in the
+        ring workspace (allocated on first use, with the steps' partial buffers)."""
+        from . import new_ring_workspace, plan_ring
+        if self.overlap_buffers is None:
+            self.overlap_buffers = [(self.out, self.lse)] + [
+                (torch.empty_like(self.out), torch.empty_like(self.lse)) for _ in self.live_steps[1:]]
+        live = [self.steps[t] for t in self.live_steps]
+        if getattr(self, "ring_workspace", None) is None:
+            n_max, runs, H, Hkv, device = self._ws_shape
+            self.ring_workspace = new_ring_workspace(len(live), n_max, runs, H, Hkv, device=device)
+        n_q, H, d = self.q.shape
+        self.plan_all(stream)
+        plan_ring([self.step_workspaces[t] for t in self.live_steps], [st["kv"].shape[1] for st in live], n_q, H,
+                  live[0]["kv"].shape[2], d, self.ring_workspace, stream=stream)
+
+    def ring_attention(self, stream=None):
+        """The one attention launch over the ring workspace: live step i's partial into
+        overlap_buffers[i] (the first is out, lse themselves)."""
+        from . import ring_attn_run
+        live = [self.steps[t] for t in self.live_steps]
+        ring_attn_run(self.q, [st["kv"][0] for st in live], [st["kv"][1] for st in live],
+                      [b[0] for b in self.overlap_buffers], [b[1] for b in self.overlap_buffers],
+                      self.ring_workspace, stream=stream)
+
+    def merge_partials(self, stream=None):
+        """Merges the live steps' partials 1, 2, ... into out, lse in step order."""
+        from . import lse_merge
+        for i in range(1, len(self.live_steps)):
+            lse_merge(self.out, self.lse, *self.overlap_buffers[i], stream=stream)
+
+    def run_ring(self, stream=None):
+        """run_planned() with every live step's items in one attention launch: the steps'
+        plans (one planning launch) are merged into one longest-first queue, one persistent
+        launch runs it, each step's partial into its own buffers, and the merges follow in
+        step order.  A light step then adds its items to the common queue instead of a
+        launch whose end waits for its largest items.  Each item computes what it computes
+        in its own step's launch, so the result has the same bits as run_planned()."""
+        if not self.live_steps:
+            return self._no_live_step()
+        self.plan_ring(stream)
+        self.ring_attention(stream)
+        self.merge_partials(stream)
+        return self.out, self.lse
+
+    def capture(self, stream=None, streams=None, ring=False):
         """Captures run_planned() -- one planning launch, an attention launch per live step and
-        a merge for each after the first -- or, given side streams, run_overlapped(), into a
-        HIP graph, so that
+        a merge for each after the first -- or, given side streams, run_overlapped(), or with
+        ring=True run_ring(), into a HIP graph, so that
         replay() launches the whole share at once.  Every kernel of the share is safe to
         replay: the planner resets the queue heads and the attention kernel rewinds them,
         and nothing in it clears memory with a memset node."""
-        body = (lambda st=None: self.run_planned(stream=st)) if streams is None else \
-            (lambda st=None: self.run_overlapped(streams, stream=st))
+        if ring:
+            body = lambda st=None: self.run_ring(stream=st)
+        else:
+            body = (lambda st=None: self.run_planned(stream=st)) if streams is None else \
+                (lambda st=None: self.run_overlapped(streams, stream=st))
         body(stream)  # allocates the step workspaces and buffers, caches the CU count
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()

@@ -244,5 +244,18 @@ def plan(frags, bm):
     return [t[i] for i in lpt_order(t)]
 
 
+def merge_step_plans(plans):
+    """One longest-first queue over several block steps' plans (the LPT rule of
+    "数据并行负载均衡", section 4.4, applied to the union of the steps' items): the tiles that
+    have key spans, by key blocks descending, ties by step and then by place in the step's own
+    plan; after them every step's tiles without spans, step by step.  Each tile is tagged
+    with its step."""
+    work = [(-t["blocks"], s, i) for s, p in enumerate(plans) for i, t in enumerate(p) if t["spans"]]
+    work.sort()
+    out = [dict(plans[s][i], step=s) for (_, s, i) in work]
+    out += [dict(t, step=s) for s, p in enumerate(plans) for t in p if not t["spans"]]
+    return out
+
+
 def total_pairs(plan_tiles):
     return sum(t["cost"] for t in plan_tiles)

@@ -151,6 +151,46 @@ def test_plan_steps_host_checks(L):
     assert L.lb_plan_block_steps(FAKE, FAKE, n, None, None, None, 1, 2, 2, 64, -1, None, None, None) == LB_EINVAL
 
 
+def test_ring_host_checks(L):
+    """lb_ring_workspace_bytes, lb_plan_ring and lb_ring_attn_run reject bad arguments on the
+    host, before anything is enqueued."""
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    arr = lambda t, xs: (t * len(xs))(*xs)
+    one = L.lb_ring_workspace_bytes(1, 64, 3, 2, 2)
+    two = L.lb_ring_workspace_bytes(2, 64, 3, 2, 2)
+    assert one > 0 and two > one and one % 256 == 0
+    assert L.lb_ring_workspace_bytes(0, 64, 3, 2, 2) == 0
+    assert L.lb_ring_workspace_bytes(17, 64, 3, 2, 2) == 0
+    assert L.lb_ring_workspace_bytes(2, 64, 3, 3, 2) == 0
+    ring = P(0x300000)
+    wss = [P(0x100000), P(0x200000)]
+    need = L.lb_workspace_bytes(64, 3, 2, 2)
+
+    def plan(n_steps=2, ws=wss, sizes=(need, need), n_kv=(64, 64), d=64, ring=ring, ring_bytes=two):
+        return L.lb_plan_ring(arr(P, ws), arr(SZ, sizes), arr(I32, n_kv), n_steps, 64, 2, 2, d, ring, ring_bytes, None)
+    assert plan(n_steps=0) == LB_EINVAL
+    assert plan(n_steps=17) == LB_EINVAL
+    assert plan(ring=None) == LB_EINVAL
+    assert plan(ring=P(0x300010)) == LB_EWORKSPACE       # not 256-byte aligned
+    assert plan(ring_bytes=1024) == LB_EWORKSPACE        # no room for a tile
+    assert plan(ws=[P(0x100000), ring]) == LB_EINVAL     # a step's workspace is the ring's
+    assert plan(n_kv=(64, -1)) == LB_EINVAL
+    assert plan(d=48) == LB_EUNSUPPORTED
+    assert L.lb_plan_ring(None, None, None, 1, 64, 2, 2, 64, ring, two, None) == LB_EINVAL
+
+    def run(n_steps=2, k=(FAKE, FAKE), n_kv=(64, 64), out=(P(0x400000), P(0x500000)),
+            lse=(P(0x600000), P(0x700000)), n_q=0, d=64, ring=ring):
+        return L.lb_ring_attn_run(FAKE, n_q, 2, 2, d, n_steps, arr(P, k), arr(P, k), arr(I32, n_kv), arr(P, out),
+                                  arr(P, lse), ring, two, None)
+    assert run() == LB_OK                                  # no query rows: nothing to launch
+    assert run(n_steps=0) == LB_EINVAL
+    assert run(out=(P(0x400000), P(0x400000))) == LB_EINVAL  # two steps into one partial
+    assert run(k=(FAKE, None)) == LB_EINVAL
+    assert run(n_kv=(64, -2)) == LB_EINVAL
+    assert run(d=48) == LB_EUNSUPPORTED
+    assert run(ring=P(0x300010)) == LB_EWORKSPACE
+
+
 def test_merge_host_checks(L):
     assert L.lb_lse_merge(None, FAKE, FAKE, FAKE, 4, 2, 8, None) == LB_EINVAL
     assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, None) == LB_EUNSUPPORTED

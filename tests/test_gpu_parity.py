@@ -679,3 +679,126 @@ def test_sharded_shared_question_reassembles(rule):
             assert lb.read_device_error(share.step_workspaces[t]) == 0
         check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]],
               f"{rule} rank {rank}, shared question")
+
+
+# --------------------------------------------------------------------------
+# one attention launch over every live ring step (ring workspace)
+# --------------------------------------------------------------------------
+def ring_share(cp=4, C=256, rank=2, seed=9):
+    H, Hkv, d = 8, 2, 128
+    T = 2 * cp * C
+    lengths = workloads.lognormal_lengths(T, seed, T)
+    r = np.random.default_rng(14 + seed)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+
+    def get_chunk(c):
+        sl = slice(c * C, (c + 1) * C)
+        return q[sl], k[sl], v[sl]
+
+    return lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+
+
+def ring_oracle_plan(share):
+    """The oracle's merged queue over the share's live steps."""
+    n_q, H, d = share.q.shape
+    Hkv = share.steps[0]["kv"].shape[2]
+    bm = lb.tile_rows(H, Hkv, d)
+    qp, qd = share.q_pos.cpu().numpy(), share.q_doc.cpu().numpy()
+    shared = None if share.shared_doc < 0 else share.shared_doc
+    plans = [OP.plan(OP.fragments_block(qp, qd, share.steps[t]["kv_pos"].cpu().numpy(),
+                                        share.steps[t]["kv_doc"].cpu().numpy(), shared_doc=shared), bm)
+             for t in share.live_steps]
+    return OP.merge_step_plans(plans)
+
+
+def check_ring_against_steps(share, what):
+    out, lse = share.run_planned()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    out, lse = share.run_ring()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"{what}: ring launch != per-step launches"
+    assert lb.read_device_error(share.ring_workspace) == 0
+    want = ring_oracle_plan(share)
+    assert_same_plan(lb.read_plan(share.ring_workspace, with_step=True), want, f"{what}: ring plan")
+    # the workgroups' records cover every item once
+    n_q, H, d = share.q.shape
+    Hkv = share.steps[0]["kv"].shape[2]
+    recs = lb.read_worker_timing(share.ring_workspace)
+    work = [t for t in want if t["spans"]]
+    assert sum(x["items"] for x in recs) == len(work) * Hkv
+    assert sum(x["blocks"] for x in recs) == sum(t["blocks"] for t in work) * Hkv
+    assert sum(x["pairs"] for x in recs) == sum(t["cost"] for t in work) * H
+    return ref_out, ref_lse
+
+
+@pytest.mark.parametrize("rank", [0, 2, 3])
+def test_ring_launch_equals_the_step_launches(rank):
+    """A zigzag rank's live steps run from one merged queue in one launch: the same bits as
+    one launch per step, the merged queue equal to the oracle's (every step's tiles, key
+    blocks descending, ties by step), every item run once."""
+    share = ring_share(rank=rank)
+    say(f"  zigzag cp=4 rank {rank}: live steps {share.live_steps}")
+    check_ring_against_steps(share, f"rank {rank}")
+
+
+def test_ring_graph_replays_equal_eager_runs():
+    """The ring share captured in one HIP graph (plans, merged queue, one attention launch,
+    merges) and replayed three times with eager work in between gives the eager bits."""
+    share = ring_share(rank=1, seed=5)
+    ref_out, ref_lse = check_ring_against_steps(share, "graph share")
+    say("  capturing the ring share")
+    share.capture(ring=True)
+    for i in range(3):
+        share.out.fill_(7.0)
+        share.lse.fill_(7.0)
+        out, lse = share.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {i}")
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {i}"
+        out, lse = share.run_planned()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager run after replay {i}"
+
+
+@pytest.mark.parametrize("rule", ["per_document", "dispatch"])
+def test_ring_launch_on_sharded_ranks(rule):
+    """Every rank of a cp = 4 sharding with a shared question (document 0): the ring launch
+    gives the bits of the per-step launches and the ranks reassemble the unsharded oracle."""
+    from load_balance_amd import sharding as LS
+    cp, H, Hkv, d = 4, 8, 2, 128
+    r = np.random.default_rng(65)
+    lengths = [700, 300, 1, 128, 90, 333]
+    lengths.append(2 * cp * 256 - sum(lengths))
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    tok = LS.shard_tokens(rule, lengths, cp, n_chunks=4 * cp)
+    assert LS.max_spans(lengths, tok, 0) <= LS.MAX_SPANS
+    shards = LS.build_shards(lengths, tok, lambda idx: (q[idx], k[idx], v[idx]))
+    full_o, full_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv, mask="shared_question")
+    for rank in range(cp):
+        share = LS.ShardedRank(shards, rank, shared_doc=0)
+        say(f"  {rule} rank {rank}: live steps {share.live_steps}")
+        out, lse = check_ring_against_steps(share, f"{rule} rank {rank}")
+        check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]],
+              f"{rule} rank {rank}, ring")
+
+
+def test_ring_made_for_other_steps_runs_nothing():
+    """A ring merged for other key/value counts is refused on the device: LB_DEVERR_PLAN,
+    no partial written."""
+    share = ring_share(rank=2)
+    share.run_ring()
+    torch.cuda.synchronize()
+    live = [share.steps[t] for t in share.live_steps]
+    assert len(live) >= 2
+    ks = [st["kv"][0] for st in live]
+    vs = [st["kv"][1] for st in live]
+    ks[1], vs[1] = ks[1][:-1], vs[1][:-1]  # one token fewer than the ring was made for
+    outs = [torch.full_like(share.out, 7.0) for _ in live]
+    lses = [torch.full_like(share.lse, 7.0) for _ in live]
+    lb.ring_attn_run(share.q, ks, vs, outs, lses, share.ring_workspace)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(share.ring_workspace) & lb.DEVERR_PLAN
+    for o, l in zip(outs, lses):
+        assert torch.all(o == 7.0) and torch.all(l == 7.0)

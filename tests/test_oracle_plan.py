@@ -363,3 +363,42 @@ def test_block_shared_doc_full_runs_join():
     q_pos, q_doc = np.array([0, 1, 0, 1, 2, 0, 0]), np.array([1, 1, 2, 2, 2, 0, 3])
     (f,) = P.fragments_block_t(q_pos, q_doc, np.arange(4), np.zeros(4, dtype=int), shared_doc=0)
     assert f[3] == [(0, 5, far), (5, 1, 0), (6, 1, far)]
+
+
+def test_merge_step_plans_by_hand():
+    """Two steps' plans with key blocks [5, 3, 1] and [4, 3, (no span)]: the merged queue,
+    written out by hand, is 5, 4, 3 (step 0 first on the tie), 3, 1, then the spanless tile."""
+    def t(blocks, tag):
+        return dict(q_start=tag, q_len=1, q_pos0=0, spans=[(0, 1, 0)] if blocks else [], cost=blocks, blocks=blocks)
+    a = [t(5, 0), t(3, 1), t(1, 2)]
+    b = [t(4, 10), t(3, 11), t(0, 12)]
+    got = [(x["step"], x["q_start"]) for x in P.merge_step_plans([a, b])]
+    assert got == [(0, 0), (1, 10), (0, 1), (1, 11), (0, 2), (1, 12)]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_merge_step_plans_keeps_each_step_and_sorts(seed):
+    """The merged queue of the live steps of a zigzag rank: every step's tiles appear once and
+    in that step's own order, the key blocks never increase over the tiles with spans, and
+    spanless tiles come last."""
+    r = np.random.default_rng(seed)
+    cp, chunk = 4, 48
+    T = 2 * cp * chunk
+    lengths = random_lengths(r, T)
+    pos, doc = A.pack_positions(lengths)
+    rank = int(r.integers(0, cp))
+    qi = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+    plans = []
+    for src in range(cp):
+        ki = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(src, cp)])
+        plans.append(P.plan(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), 16))
+    merged = P.merge_step_plans(plans)
+    assert len(merged) == sum(len(p) for p in plans)
+    for s, p in enumerate(plans):
+        mine = [{k: v for k, v in x.items() if k != "step"} for x in merged if x["step"] == s]
+        assert [x for x in mine if x["spans"]] == [x for x in p if x["spans"]]
+        assert [x for x in mine if not x["spans"]] == [x for x in p if not x["spans"]]
+    n_work = sum(1 for x in merged if x["spans"])
+    assert all(x["spans"] for x in merged[:n_work]) and not any(x["spans"] for x in merged[n_work:])
+    blocks = [x["blocks"] for x in merged[:n_work]]
+    assert blocks == sorted(blocks, reverse=True)
