@@ -3,10 +3,13 @@
 // to one output ("03 · 长文负载均衡", section 3.2, DCP; "长序列训练与上下文并行",
 // Ring Attention: each ring step's local result is merged into the running one).
 //
-// HBM-bound elementwise work.  One wave takes 64 consecutive rows of one head: it
-// reads their 64 lse_b values in one coalesced load, and only the rows with a visible
-// key in the second partial (a ballot, compacted into a per-wave LDS table) move data.
-// A ring step that touches few rows of the shard costs little more than reading lse_b.
+// HBM-bound elementwise work.  One workgroup of 4 waves takes 64 consecutive rows of
+// one head: it reads their 64 lse_b values in one coalesced load, and only the rows with
+// a visible key in the second partial (a ballot) move data.  Wave 0 computes the rows'
+// weights into an LDS table (compacted by the ballot) and writes the merged lse; after
+// one barrier the four waves share the rows' 16-byte pieces, each loading its whole
+// share before storing any.  A ring step that touches few rows of the shard costs little
+// more than reading lse_b, and a row group's data moves in one round trip per wave.
 #include <algorithm>
 
 #include "lbattn_internal.h"
@@ -17,19 +20,18 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kBatch = 8;  // units per lane loaded before any is stored
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  // per wave: the taken rows of the current group, compacted, and their two weights
-  __shared__ int s_row[kMergeWaves][64];
-  __shared__ float s_wa[kMergeWaves][64], s_wb[kMergeWaves][64];
+  // the taken rows of the group, compacted, and their two weights
+  __shared__ int s_row[64];
+  __shared__ float s_wa[64], s_wb[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t groups = ((int64_t)a.n_rows + 63) / 64;  // row groups per head
   const int64_t n_tasks = groups * a.heads;
   const int chunks = a.d / 4;  // 16-byte pieces of one (row, head) vector
-  for (int64_t task = (int64_t)blockIdx.x * kMergeWaves + w; task < n_tasks; task += (int64_t)gridDim.x * kMergeWaves) {
-    // task-major over heads: neighbouring waves read neighbouring lse entries
+  for (int64_t task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+    // task-major over heads: neighbouring workgroups read neighbouring lse entries
     const int head = (int)(task / groups);
     const int64_t row0 = (task % groups) * 64;
     const int64_t row = row0 + lane;
@@ -37,9 +39,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     const int64_t li = (int64_t)head * a.n_rows + row;
     const float lb = in ? a.lse_b[li] : -__builtin_inff();
     const bool take = lb != -__builtin_inff();
-    const uint64_t mask = __ballot(take);
+    const uint64_t mask = __ballot(take);  // the same in every wave: the same 64 rows
     if (mask == 0) continue;
-    if (take) {
+    if (w == 0 && take) {
       // this lane's row: weights of the two partials (wa = 0: out_a is not read) and the merged lse
       const float la = a.lse_a[li];
       float wa = 0.0f, wb = 1.0f, lse = lb;
@@ -53,27 +55,27 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       }
       a.lse_a[li] = lse;
       const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      s_row[w][slot] = lane;
-      s_wa[w][slot] = wa;
-      s_wb[w][slot] = wb;
+      s_row[slot] = lane;
+      s_wa[slot] = wa;
+      s_wb[slot] = wb;
     }
-    // The table is this wave's alone and LDS instructions of one wave complete in order.
-    // Units (taken row, 16-byte piece) are spread over the lanes; each lane loads a batch
-    // of units before it stores any (a store to out_a could alias a later load, so the
-    // compiler would not hoist loads across it), keeping 2 x kBatch loads in flight.
+    __syncthreads();
+    // Units (taken row, 16-byte piece) are spread over the workgroup's lanes; each lane loads
+    // a batch of units before it stores any (a store to out_a could alias a later load, so
+    // the compiler would not hoist loads across it), keeping 2 x kBatch loads in flight.
     const int units = __popcll(mask) * chunks;
-    for (int u0 = 0; u0 < units; u0 += kBatch * 64) {
+    for (int u0 = w * 64; u0 < units; u0 += kBatch * kMergeThreads) {
       f32x4 x[kBatch], y[kBatch];
       float ca[kBatch], cb[kBatch];
       f32x4* dst[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int u = u0 + j * 64 + lane;
+        const int u = u0 + j * kMergeThreads + lane;
         const bool ok = u < units;
         const int k = ok ? u / chunks : 0, c = ok ? u - k * chunks : 0;
-        const int64_t rh = (row0 + s_row[w][k]) * a.heads + head;
-        ca[j] = ok ? s_wa[w][k] : -1.0f;  // -1: no unit
-        cb[j] = s_wb[w][k];
+        const int64_t rh = (row0 + s_row[k]) * a.heads + head;
+        ca[j] = ok ? s_wa[k] : -1.0f;  // -1: no unit
+        cb[j] = s_wb[k];
         dst[j] = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + c;
         y[j] = ok ? reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[c] : f32x4{};
         // out_a is not read where lse_a = -inf (ca = 0): the first partial never wrote that row
@@ -83,6 +85,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       for (int j = 0; j < kBatch; ++j)
         if (ca[j] >= 0.0f) *dst[j] = ca[j] == 0.0f ? y[j] : x[j] * ca[j] + y[j] * cb[j];
     }
+    __syncthreads();  // the table is read by every wave before the next group's wave 0 writes it
   }
 }
 
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t tasks = ((int64_t)a.n_rows + 63) / 64 * a.heads;
-  const int64_t blocks = std::min<int64_t>((tasks + kMergeWaves - 1) / kMergeWaves, 4096);
+  const int64_t blocks = std::min<int64_t>(tasks, 16384);
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
