@@ -682,7 +682,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_entry() if args.workload == "longtail" else None,
-            "kernel": getattr(w, "kernel_name", "attn_kernel<128,false,false> (persistent, LPT queue)"),
+            "kernel": getattr(w, "kernel_name", "attn_kernel<128,false,false,false> (persistent, LPT queue)"),
             "launch_ms": round(attn_ms_per_launch, 4),
         },
         "cpu_baseline": None,
