@@ -295,18 +295,22 @@ class ZigzagBwdStep(ZigzagStep):
     per step the block backward (dq added, the source chunk's partial dk, dv written).
     Effective FLOPs 10 * d * H * pairs, 2.5x the forward's."""
 
-    def __init__(self, torch, lb, workloads, seed=0):
+    def __init__(self, torch, lb, workloads, seed=0, ring=True):
         super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0, ring=False)
+        self.bwd_ring = ring
         sh = self.share
         sh.run_planned()
         r = np.random.default_rng(2001)
         n_q = sh.q.shape[0]
         self.dout = to_dev(workloads.f32_to_bf16_bits(r.standard_normal((n_q, self.H, self.d)).astype(np.float32)),
                            torch)
-        sh.backward(self.dout)  # allocates the backward's buffers outside the timed region
+        sh.backward(self.dout, ring=ring)  # allocates the backward's buffers outside the timed region
         torch.cuda.synchronize()
         self.flops = 10 * self.d * self.H * self.pairs
-        self.kernel_name = "ring backward (D, then per step: plans, bwd_dq_kernel<128,1,true>, bwd_dkv_kernel<128,true>)"
+        self.kernel_name = ("ring backward (D; all steps' plans in one launch, their key-tile plans merged; "
+                            "bwd_dq_kernel<128,1,true> per step; one bwd_dkv_kernel<128,true,ring> over every step)"
+                            if ring else "ring backward (D, then per step: plans, bwd_dq_kernel<128,1,true>, "
+                            "bwd_dkv_kernel<128,true,false>)")
         self.graph = None
 
     def n_launches(self):
@@ -316,11 +320,13 @@ class ZigzagBwdStep(ZigzagStep):
         if evs is not None:
             evs[0][0].record()
             evs[0][1].record()
-        self.share.backward(self.dout)
+        self.share.backward(self.dout, ring=self.bwd_ring)
         if evs is not None:
             evs[0][2].record()
 
     def worker_ws(self):  # the workspace whose worker records and plan the bench reports
+        if self.bwd_ring:
+            return self.share.bwd_ring_workspace
         return self.share.bwd_buffers["ws"][self.share.live_steps[0]]
 
 
@@ -473,11 +479,12 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "head_dim": 128, "seed": seed, "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w
     if name == "zigzag_bwd":
-        w = ZigzagBwdStep(torch, lb, workloads, seed=seed)
+        w = ZigzagBwdStep(torch, lb, workloads, seed=seed, ring=ring)
         w.config = {"workload": "ring backward of one zigzag CP rank's share at cp=8: rank 3 of a 131072-token "
                                 f"lognormal pack (seed {seed}), a block-step backward per step with visible pairs "
                                 "(3 of 8: dq accumulated, per-step partial dk, dv) after the forward's merged out and "
-                                "lse",
+                                "lse" + ("; the steps' dK/dV items in one launch from one longest-first queue" if ring
+                                         else "; one dK/dV launch per step"),
                     "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
                     "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w

@@ -264,6 +264,37 @@ lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv
                            float* const* lse, void* ring_workspace, size_t ring_workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * The backward of one rank's ring (the steps of lb_block_attn_bwd for n_steps key/value
+ * chunks of one query shard), with every step's dK/dV items in one launch.  A dK/dV
+ * launch ends with its longest key tiles (a tile near the start of a long document sweeps
+ * every later query row of it), so one launch per step pays that tail once per step; one
+ * longest-first queue over the key tiles of all steps ("数据并行负载均衡", section 4.4; the
+ * partial key/value gradients of each step go back to the chunk's owner, "03 · 长文负载均衡",
+ * section 4.4) runs the long tiles of all steps side by side.
+ *   Shared by all steps: q_shard, n_q, dout, lse, dvec, q_pos, q_doc, heads, kv_heads, d,
+ *   shared_doc and dq, as lb_block_attn_bwd takes them (dq fp32 [n_q][heads][d] is added to,
+ *   step after step in index order).
+ *   Per step s (host arrays of n_steps entries holding device pointers): kv_chunks[s] bf16
+ *   [2][n_kv[s]][kv_heads][d], kv_pos[s], kv_doc[s], dkv[s] fp32 [2][n_kv[s]][kv_heads][d]
+ *   (written: that chunk's partial dk, dv; zero where no row sees a key), workspaces[s] of
+ *   workspace_bytes[s] (as lb_block_attn_bwd sizes it).  1 <= n_steps <= LB_MAX_PLAN_STEPS / 2,
+ *   n_kv[s] >= 1; workspaces and dkv buffers distinct.
+ *   ring_workspace: 256-byte aligned, lb_ring_workspace_bytes(n_steps, ...) bytes or more
+ *   for the largest side; it receives the merged key-tile queue and the dK/dV launch's
+ *   worker records.
+ * Launches: one planning launch (both plans of every step), the merge of the key-tile
+ * plans, one dQ launch per step, one dK/dV launch.  Device errors as lb_block_attn_bwd,
+ * the dK/dV side's in ring_workspace.  Argument errors return before anything is enqueued.
+ */
+lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
+                                 const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
+                                 int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
+                                 const void* const* kv_chunks, const int32_t* n_kv, const int32_t* const* kv_pos,
+                                 const int32_t* const* kv_doc, float* dq, float* const* dkv,
+                                 void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
+                                 size_t ring_workspace_bytes, hipStream_t stream);
+
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);

@@ -110,6 +110,9 @@ def lib() -> ctypes.CDLL:
     L.lb_varlen_attn_bwd.restype = ctypes.c_int
     L.lb_block_attn_bwd.argtypes = [P, I32, P, I32, P, P, P, P, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_block_attn_bwd.restype = ctypes.c_int
+    L.lb_block_attn_bwd_ring.argtypes = [P, I32, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, SZ,
+                                         P]
+    L.lb_block_attn_bwd_ring.restype = ctypes.c_int
     L.lb_status_string.argtypes = [ctypes.c_int]
     L.lb_status_string.restype = ctypes.c_char_p
     L.lb_read_device_error.argtypes = [P, SZ, ctypes.POINTER(I32), P]
@@ -389,6 +392,34 @@ def bwd_key_plan_offset(block_path: bool, n_q: int, n_kv: int, n_seg: int, heads
                         workspace_bytes: int) -> int:
     """Where the key-tile plan of a backward workspace starts (the query-tile plan is at 0)."""
     return int(lib().lb_bwd_key_plan_offset(int(block_path), n_q, n_kv, n_seg, heads, kv_heads, workspace_bytes))
+
+
+def block_attn_bwd_ring(q, kvs, dout, lse, dvec, q_pos, q_doc, kv_pos_list, kv_doc_list, dq, dkvs, workspaces,
+                        ring_workspace, stream=None, shared_doc=NO_SHARED_DOC):
+    """The backward of a rank's ring steps: per step s the query shard against kvs[s] (bf16
+    [2,n_kv,H_kv,d]) with kv_pos_list[s], kv_doc_list[s]; dq (fp32 [n_q,H,d]) is added to,
+    step after step; dkvs[s] (fp32 [2,n_kv,H_kv,d]) receives step s's partial dk, dv.  One
+    dQ launch per step and one dK/dV launch over every step's key tiles."""
+    n_q, H, d = q.shape
+    n = len(kvs)
+    if not (len(kv_pos_list) == len(kv_doc_list) == len(dkvs) == len(workspaces) == n):
+        raise LBError("kvs, kv_pos_list, kv_doc_list, dkvs and workspaces need one entry per step")
+    for t in [q_pos, q_doc] + list(kv_pos_list) + list(kv_doc_list):
+        if t.dtype != torch.int32:
+            raise LBError("positions and document ids must be int32")
+    for x in list(dkvs) + [dq, lse, dvec]:
+        if x.dtype != torch.float32:
+            raise LBError("dq, dkv, lse and dvec are float32")
+    Hkv = kvs[0].shape[2]
+    ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
+    nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[1] for k in kvs])
+    sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
+    _check(lib().lb_block_attn_bwd_ring(_ptr(q), n_q, _ptr(dout), _ptr(lse), _ptr(dvec), _ptr(q_pos), _ptr(q_doc), H,
+                                        Hkv, d, int(shared_doc), n, ptrs(kvs), nkv, ptrs(kv_pos_list),
+                                        ptrs(kv_doc_list), _ptr(dq), ptrs(dkvs), ptrs(workspaces), sizes,
+                                        _ptr(ring_workspace), ring_workspace.numel(),
+                                        ctypes.c_void_p(_stream(stream))), "lb_block_attn_bwd_ring")
+    return dq, dkvs
 
 
 def attn_bwd_rowdot(out, dout, dvec=None, stream=None):

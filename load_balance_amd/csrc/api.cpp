@@ -361,6 +361,7 @@ lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, c
   m.kv_heads = kv_heads;
   m.ring = static_cast<char*>(ring_workspace);
   m.ring_cap = (int32_t)std::min<int64_t>(cap, INT32_MAX);
+  m.transposed = 0;
   return launch_ring_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
@@ -624,6 +625,92 @@ lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chu
   b.ws = ws + B.off_k;
   b.ws_bytes = (int64_t)workspace_bytes - B.off_k;
   return launch_bwd_dkv(b, d, true, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
+                                 const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
+                                 int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
+                                 const void* const* kv_chunks, const int32_t* n_kv, const int32_t* const* kv_pos,
+                                 const int32_t* const* kv_doc, float* dq, float* const* dkv,
+                                 void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
+                                 size_t ring_workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || shared_doc < -1 || n_steps < 1 || 2 * n_steps > kMaxPlanSteps) return LB_EINVAL;
+  if (!q_shard || !dout || !lse || !dvec || !q_pos || !q_doc || !dq || !ring_workspace) return LB_EINVAL;
+  if (!kv_chunks || !n_kv || !kv_pos || !kv_doc || !dkv || !workspaces || !workspace_bytes) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  if (!aligned(q_shard, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) || !aligned(dvec, 4) ||
+      !aligned(q_pos, 4) || !aligned(q_doc, 4))
+    return LB_EINVAL;
+  if (!aligned(ring_workspace, 256)) return LB_EWORKSPACE;
+  const int64_t cap = ((int64_t)ring_workspace_bytes - kRingTilesOffset) / (int64_t)sizeof(lb_plan_tile);
+  if (cap < 1) return LB_EWORKSPACE;
+  BwdLayout B[kMaxPlanSteps];
+  for (int s = 0; s < n_steps; ++s) {
+    if (n_kv[s] < 1 || !kv_chunks[s] || !kv_pos[s] || !kv_doc[s] || !dkv[s] || !workspaces[s]) return LB_EINVAL;
+    if (!aligned(kv_chunks[s], 16) || !aligned(dkv[s], 16) || !aligned(kv_pos[s], 4) || !aligned(kv_doc[s], 4))
+      return LB_EINVAL;
+    for (int o = 0; o < s; ++o)
+      if (workspaces[o] == workspaces[s] || dkv[o] == dkv[s]) return LB_EINVAL;
+    if (workspaces[s] == ring_workspace) return LB_EINVAL;
+    if (!aligned(workspaces[s], 256)) return LB_EWORKSPACE;
+    st = bwd_layout_block(n_q, n_kv[s], heads, kv_heads, workspace_bytes[s], &B[s]);
+    if (st != LB_OK) return st;
+  }
+  if (n_q == 0) return LB_OK;
+  // every step's two plans in one launch, then the key-tile plans merged into one queue
+  PlanBatch pb{};
+  for (int s = 0; s < n_steps; ++s) {
+    char* ws = static_cast<char*>(workspaces[s]);
+    for (int side = 0; side < 2; ++side) {
+      PlanArgs& p = pb.step[2 * s + side];
+      p = block_plan_args(q_pos, q_doc, n_q, kv_pos[s], kv_doc[s], n_kv[s], heads, kv_heads, shared_doc,
+                          ws + (side == 0 ? 0 : B[s].off_k), side == 0 ? B[s].q : B[s].k);
+      p.transposed = side;
+      p.tile_rows = side == 0 ? bwd_q_rows(heads / kv_heads) : bwd_k_rows(heads / kv_heads);
+    }
+  }
+  if (launch_plan_steps(pb, 2 * n_steps, stream) != hipSuccess) return LB_EHIP;
+  RingMergeArgs m{};
+  for (int s = 0; s < n_steps; ++s) {
+    m.step_ws[s] = static_cast<const char*>(workspaces[s]) + B[s].off_k;
+    m.step_ws_bytes[s] = (int64_t)workspace_bytes[s] - B[s].off_k;
+    m.n_kv[s] = n_kv[s];
+  }
+  m.n_steps = n_steps;
+  m.n_q = n_q;
+  m.heads = heads;
+  m.kv_heads = kv_heads;
+  m.ring = static_cast<char*>(ring_workspace);
+  m.ring_cap = (int32_t)std::min<int64_t>(cap, INT32_MAX);
+  m.transposed = 1;
+  if (launch_ring_merge(m, stream) != hipSuccess) return LB_EHIP;
+  int workers = 0;
+  st = persistent_workers(&workers);
+  if (st != LB_OK) return st;
+  // dq: the steps in order, each adding into the one fp32 buffer
+  RingBwdSteps r{};
+  for (int s = 0; s < n_steps; ++s) {
+    const __bf16* kbase = static_cast<const __bf16*>(kv_chunks[s]);
+    const __bf16* vbase = kbase + (int64_t)n_kv[s] * kv_heads * d;
+    float* dk = dkv[s];
+    float* dv = dkv[s] + (int64_t)n_kv[s] * kv_heads * d;
+    BwdArgs b = bwd_args(q_shard, kbase, vbase, dout, lse, dvec, dq, dk, dv, n_q, n_kv[s], heads, kv_heads, d);
+    b.ws = static_cast<char*>(workspaces[s]);
+    b.ws_bytes = B[s].off_k;
+    if (launch_bwd_dq(b, d, true, workers, stream) != hipSuccess) return LB_EHIP;
+    r.k[s] = kbase;
+    r.v[s] = vbase;
+    r.dk[s] = dk;
+    r.dv[s] = dv;
+    r.n_kv[s] = n_kv[s];
+  }
+  r.n_steps = n_steps;
+  // dk, dv: every step's key tiles in one launch, each step's gradients into its own buffer
+  BwdArgs b = bwd_args(q_shard, q_shard, q_shard, dout, lse, dvec, dq, r.dk[0], r.dv[0], n_q, 0, heads, kv_heads, d);
+  b.ws = static_cast<char*>(ring_workspace);
+  b.ws_bytes = (int64_t)ring_workspace_bytes;
+  return launch_bwd_dkv_ring(b, r, d, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
 const char* lb_status_string(lb_status s) {

@@ -73,7 +73,10 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t x0, uint32_t x1) { return (
 // ------------------------------------------------------------------------------------
 // The plan and its queues (same format and protocol as the forward's)
 // ------------------------------------------------------------------------------------
-struct Queues {
+// RING: the workspace is a ring workspace (several steps' tiles in one queue, stored in
+// queue order, each tile's step in its `reserved` word).
+template <bool RING>
+struct QueuesT {
   WsHeader* hdr;
   const lb_plan_tile* tiles;
   const int32_t* order;
@@ -82,10 +85,11 @@ struct Queues {
   int n_empty;
   bool dry;  // thread 0's view
 
-  __device__ void open(const BwdArgs& a, int transposed) {
+  __device__ void open(const BwdArgs& a, int transposed, const RingBwdSteps* r = nullptr) {
     hdr = reinterpret_cast<WsHeader*>(a.ws);
     const int64_t nt = hdr->n_tiles;
-    const bool bad = hdr->magic != kPlanMagic || hdr->transposed != transposed || hdr->plan_n_q != a.n_q ||
+    bool bad = hdr->magic != (RING ? kRingMagic : kPlanMagic) || hdr->transposed != transposed ||
+               hdr->plan_n_q != a.n_q ||
                      hdr->plan_n_kv != a.n_kv || hdr->plan_kv_heads != a.kv_heads || hdr->plan_heads != a.heads ||
                      hdr->n_empty < 0 || hdr->n_empty > nt || hdr->n_items != (nt - hdr->n_empty) * a.kv_heads ||
                      nt < 0 || (hdr->n_queues != 1 && hdr->n_queues != kXcds) || a.kv_heads % hdr->n_queues != 0 ||
@@ -93,6 +97,12 @@ struct Queues {
                      hdr->off_order < kWorkersOffset ||
                      hdr->off_tiles + nt * (int64_t)sizeof(lb_plan_tile) > a.ws_bytes ||
                      hdr->off_order + nt * 4 > a.ws_bytes;
+    if constexpr (RING) {
+      // the ring was merged from plans made for these steps' key/value counts
+      bad = bad || r->n_steps < 1 || r->n_steps > kMaxPlanSteps || hdr->ring_steps != r->n_steps;
+      for (int s = 0; s < kMaxPlanSteps; ++s)
+        if (s < r->n_steps && hdr->ring_n_kv[s] != r->n_kv[s]) bad = true;
+    }
     if (bad && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
     n_items = bad ? 0 : hdr->n_items;
     n_tiles = bad ? 0 : nt;
@@ -126,7 +136,13 @@ struct Queues {
     // the header fields come through vector loads: state that the results are uniform
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
     *g = __builtin_amdgcn_readfirstlane(q_of + n_queues * (k_in % heads_per_queue));
-    *T = &tiles[__builtin_amdgcn_readfirstlane(order[k_in / heads_per_queue])];
+    *T = tile_at(k_in / heads_per_queue);
+  }
+
+  // the tile at queue position i: through the plan's order, or (ring) stored in queue order
+  __device__ const lb_plan_tile* tile_at(int64_t i) const {
+    if constexpr (RING) return &tiles[i];
+    else return &tiles[__builtin_amdgcn_readfirstlane(order[i])];
   }
 
   // The last workgroup out rewinds the queues (every pop has happened before it counts itself).
@@ -149,6 +165,8 @@ struct Queues {
     }
   }
 };
+
+using Queues = QueuesT<false>;
 
 struct Span {
   int start, len, pos0;
@@ -585,8 +603,10 @@ struct QdoLoader {
   }
 };
 
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
+// RING: a ring workspace of several steps' key tiles; a tile's step selects the keys, values
+// and gradient outputs of that step in r (one launch for every step of a rank's ring).
+template <int D, bool OUT_F32, bool RING>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingBwdSteps r) {
   using L = KvLds<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
   __shared__ int s_item;
@@ -597,28 +617,39 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   const int kg = wave % kKeyGroups;
   const bool dk_role = wave < kKeyGroups;  // else the dV role
   const float c = a.scale_log2;
-  const __bf16* K = reinterpret_cast<const __bf16*>(a.k);
-  const __bf16* V = reinterpret_cast<const __bf16*>(a.v);
+  const __bf16* Kb = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* Vb = reinterpret_cast<const __bf16*>(a.v);
+  // a ring tile's step, kept inside the launch's step table
+  auto step_of = [&](const lb_plan_tile* T) -> int {
+    return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
+  };
 
-  Queues qs;
-  qs.open(a, 1);
+  QueuesT<RING> qs;
+  qs.open(a, 1, &r);
   uint64_t t_start = tid == 0 ? device_clock() : 0;
   int my_items = 0, my_blocks = 0;
   int64_t my_pairs = 0;
 
   // key tiles no query row sees: zero gradients, a grid-stride pass before the queues
   for (int e = blockIdx.x; e < qs.n_empty; e += gridDim.x) {
-    const lb_plan_tile* T = &qs.tiles[qs.order[qs.n_tiles - qs.n_empty + e]];
+    const lb_plan_tile* T = qs.tile_at(qs.n_tiles - qs.n_empty + e);
     const int k_start = T->q_start, k_len = T->q_len;
     const int per_row = a.kv_heads * D;
+    void* dk_e = a.dk;
+    void* dv_e = a.dv;
+    if constexpr (RING) {
+      const int st = step_of(T);
+      dk_e = r.dk[st];
+      dv_e = r.dv[st];
+    }
     for (int idx = tid; idx < k_len * per_row; idx += kKvThreads) {
       const int64_t o = (int64_t)k_start * per_row + idx;
       if constexpr (OUT_F32) {
-        reinterpret_cast<float*>(a.dk)[o] = 0.f;
-        reinterpret_cast<float*>(a.dv)[o] = 0.f;
+        reinterpret_cast<float*>(dk_e)[o] = 0.f;
+        reinterpret_cast<float*>(dv_e)[o] = 0.f;
       } else {
-        reinterpret_cast<__bf16*>(a.dk)[o] = (__bf16)0.f;
-        reinterpret_cast<__bf16*>(a.dv)[o] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(dk_e)[o] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(dv_e)[o] = (__bf16)0.f;
       }
     }
   }
@@ -638,6 +669,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
     if (tid == 0) {
       ++my_items;
       my_pairs += T->cost * G;
+    }
+    const __bf16* K = Kb;
+    const __bf16* V = Vb;
+    int step = 0;
+    if constexpr (RING) {
+      step = step_of(T);
+      K = reinterpret_cast<const __bf16*>(r.k[step]);
+      V = reinterpret_cast<const __bf16*>(r.v[step]);
     }
     const int my_key = kg * 32 + l32;
     const bool key_real = my_key < k_len;
@@ -784,7 +823,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       const int64_t first = (((int64_t)k_start + kg * 32) * a.kv_heads + g) * D * elt;
       stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc, dk_role ? a.scale : 1.0f, lane);
       __builtin_amdgcn_wave_barrier();
-      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(dk_role ? a.dk : a.dv) + first,
+      void* grad = dk_role ? a.dk : a.dv;
+      if constexpr (RING) grad = dk_role ? r.dk[step] : r.dv[step];
+      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(grad) + first,
                                      row_step, rows, lane);
     }
     lds_barrier();
@@ -827,7 +868,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, h
 
 template <int D, bool F32>
 static void dkv_launch(const BwdArgs& a, int workers, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, F32>), dim3(workers), dim3(kKvThreads), 0, s, a);
+  const RingBwdSteps none{};
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, F32, false>), dim3(workers), dim3(kKvThreads), 0, s, a, none);
 }
 
 hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {
@@ -836,6 +878,14 @@ hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, 
   } else {
     if (out_f32) dkv_launch<64, true>(a, n_workers, s); else dkv_launch<64, false>(a, n_workers, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv_ring(const BwdArgs& a, const RingBwdSteps& r, int d, int n_workers, hipStream_t s) {
+  if (d == 128)
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, true, true>), dim3(n_workers), dim3(kKvThreads), 0, s, a, r);
+  else
+    hipLaunchKernelGGL((bwd_dkv_kernel<64, true, true>), dim3(n_workers), dim3(kKvThreads), 0, s, a, r);
   return hipGetLastError();
 }
 

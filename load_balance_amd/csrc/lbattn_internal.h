@@ -142,7 +142,8 @@ struct RingMergeArgs {
   int32_t n_steps;
   int32_t n_q, heads, kv_heads;
   char* ring;
-  int32_t ring_cap;  // tiles the ring workspace holds
+  int32_t ring_cap;    // tiles the ring workspace holds
+  int32_t transposed;  // the steps' plans are key-tile plans (the backward's dK/dV side)
 };
 
 // Per-step operands of a ring attention launch (indexed by a tile's step).
@@ -215,5 +216,16 @@ hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, in
                              float* dvec, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s);
+
+// Per-step operands of a ring dK/dV launch (indexed by a key tile's step).
+struct RingBwdSteps {
+  const void* k[kMaxPlanSteps];
+  const void* v[kMaxPlanSteps];
+  float* dk[kMaxPlanSteps];
+  float* dv[kMaxPlanSteps];
+  int32_t n_kv[kMaxPlanSteps];
+  int32_t n_steps;
+};
+hipError_t launch_bwd_dkv_ring(const BwdArgs& a, const RingBwdSteps& r, int d, int n_workers, hipStream_t s);
 
 }  // namespace lb

@@ -636,9 +636,9 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
     for (int s = 0; s < n_steps; ++s) {
       const WsHeader* h = reinterpret_cast<const WsHeader*>(m.step_ws[s]);
       const int64_t nt = h->n_tiles, ne = h->n_empty;
-      // a step's plan must be a forward block plan made for these shapes, and lie inside
+      // a step's plan must be a block plan of the ring's kind made for these shapes, and lie inside
       // its workspace; its own error bits pass on
-      const bool bad = h->magic != kPlanMagic || h->transposed != 0 || h->has_lower != 0 ||
+      const bool bad = h->magic != kPlanMagic || h->transposed != m.transposed || h->has_lower != 0 ||
                        h->plan_n_q != m.n_q || h->plan_n_kv != m.n_kv[s] || h->plan_heads != m.heads ||
                        h->plan_kv_heads != m.kv_heads || nt < 0 || ne < 0 || ne > nt ||
                        h->off_tiles < kWorkersOffset || h->off_order < kWorkersOffset ||
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
     rh->cap_frags = 0;
     rh->cap_tiles = m.ring_cap;
     rh->total_pairs = ok ? pairs : 0;
-    rh->transposed = 0;
+    rh->transposed = m.transposed;
     rh->has_lower = 0;
     rh->plan_n_q = m.n_q;
     rh->plan_n_kv = 0;

@@ -459,7 +459,7 @@ class ShardedRank:
             lse_merge(self.out, self.lse, *self.overlap_buffers[i], stream=main)
         return self.out, self.lse
 
-    def backward(self, dout, stream=None):
+    def backward(self, dout, stream=None, ring=False):
         """The rank's ring backward after a forward (run, run_planned, run_overlapped or a
         replay) left out and lse: D = <dout, out> once, then per live step the query shard's
         dq contribution (added into one fp32 buffer, so the steps run in order) and the source
@@ -467,7 +467,9 @@ class ShardedRank:
         the chunk's owner ("03 · 长文负载均衡", section 4.4: partial key/value gradients are
         reduced at the owning rank).  dout: bf16 [n_q, H, d] in the rank's token order.
         Returns dq (fp32 [n_q, H, d]) and the list of per-step dkv (fp32 [2, n_kv, H_kv, d]),
-        None for a step no row sees: it sends nothing back."""
+        None for a step no row sees: it sends nothing back.  ring=True runs the live steps'
+        dK/dV items in one launch from one longest-first queue (lb_block_attn_bwd_ring); dq
+        is added step after step either way."""
         from . import attn_bwd_rowdot, block_attn_bwd
         if getattr(self, "bwd_buffers", None) is None:
             n_q, H, d = self.q.shape
@@ -481,6 +483,18 @@ class ShardedRank:
         b = self.bwd_buffers
         attn_bwd_rowdot(self.out, dout, dvec=b["dvec"], stream=stream)
         b["dq"].zero_()
+        if ring and self.live_steps:
+            from . import block_attn_bwd_ring, new_ring_workspace
+            if getattr(self, "bwd_ring_workspace", None) is None:
+                n_max, runs, H, Hkv, device = self._ws_shape
+                self.bwd_ring_workspace = new_ring_workspace(len(self.live_steps), n_max, runs, H, Hkv, device=device)
+            live = self.live_steps
+            block_attn_bwd_ring(self.q, [self.steps[t]["kv"] for t in live], dout, self.lse, b["dvec"], self.q_pos,
+                                self.q_doc, [self.steps[t]["kv_pos"] for t in live],
+                                [self.steps[t]["kv_doc"] for t in live], b["dq"], [b["dkv"][t] for t in live],
+                                [b["ws"][t] for t in live], self.bwd_ring_workspace, stream=stream,
+                                shared_doc=self.shared_doc)
+            return b["dq"], [b["dkv"][t] if t in live else None for t in range(len(self.steps))]
         for t in self.live_steps:
             st = self.steps[t]
             block_attn_bwd(self.q, st["kv"], dout, self.lse, b["dvec"], self.q_pos, st["kv_pos"], self.q_doc,

@@ -191,6 +191,35 @@ def test_ring_host_checks(L):
     assert run(ring=P(0x300010)) == LB_EWORKSPACE
 
 
+def test_ring_backward_host_checks(L):
+    """lb_block_attn_bwd_ring rejects bad arguments on the host, before anything is enqueued."""
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    arr = lambda t, xs: (t * len(xs))(*xs)
+    n = 64
+    ws_need = L.lb_bwd_workspace_bytes(n, 3, 2, 2) * 4
+    ring = P(0x900000)
+    ring_bytes = L.lb_ring_workspace_bytes(2, n, 3, 2, 2)
+
+    def call(n_steps=2, n_kv=(n, n), dkv=(P(0x400000), P(0x500000)), ws=(P(0x100000), P(0x200000)), n_q=0, d=64,
+             ring=ring):
+        k = max(n_steps, 1)
+        pad = lambda xs, fill: list(xs) + [fill] * (k - len(xs))
+        return L.lb_block_attn_bwd_ring(FAKE, n_q, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, d, -1, n_steps,
+                                        arr(P, pad([FAKE, FAKE], FAKE)), arr(I32, pad(n_kv, n)),
+                                        arr(P, pad([FAKE, FAKE], FAKE)), arr(P, pad([FAKE, FAKE], FAKE)), FAKE,
+                                        arr(P, pad(dkv, P(0x600000))), arr(P, pad(ws, P(0x700000))),
+                                        arr(SZ, pad([ws_need, ws_need], ws_need)), ring, ring_bytes, None)
+    assert call() == LB_OK                                   # no query rows: nothing to launch
+    assert call(n_steps=0) == LB_EINVAL
+    assert call(n_steps=9) == LB_EINVAL                      # two plans per step, at most LB_MAX_PLAN_STEPS
+    assert call(n_kv=(n, 0)) == LB_EINVAL                    # a ring step has keys
+    assert call(dkv=(P(0x400000), P(0x400000))) == LB_EINVAL  # two steps into one partial
+    assert call(ws=(P(0x100000), P(0x100000))) == LB_EINVAL
+    assert call(ws=(P(0x100000), ring)) == LB_EINVAL
+    assert call(ring=P(0x900010)) == LB_EWORKSPACE
+    assert call(d=48) == LB_EUNSUPPORTED
+
+
 def test_merge_host_checks(L):
     assert L.lb_lse_merge(None, FAKE, FAKE, FAKE, 4, 2, 8, None) == LB_EINVAL
     assert L.lb_lse_merge(FAKE, FAKE, FAKE, FAKE, 4, 2, 6, None) == LB_EUNSUPPORTED

@@ -227,10 +227,12 @@ def test_block_backward_shared_question_whole_pack():
         assert [tuple(s) for s in a["spans"]] == [tuple(s) for s in b["spans"]], i
 
 
-def test_ring_backward_shared_question_reassembles():
+@pytest.mark.parametrize("ring", [False, True])
+def test_ring_backward_shared_question_reassembles(ring):
     """A shared-question pack sharded by sequence zigzag over cp = 4 ranks, document 0
-    shared: each rank's forward ring and ring backward (steps no row sees send nothing back),
-    summed per owner, equal the unsharded shared-question gradient."""
+    shared: each rank's forward ring and ring backward (steps no row sees send nothing back;
+    with ring=True the steps' dK/dV items in one launch), summed per owner, equal the
+    unsharded shared-question gradient."""
     from load_balance_amd import sharding as LS
     cp, H, Hkv, d = 4, 8, 2, 128
     r = np.random.default_rng(64)
@@ -248,7 +250,7 @@ def test_ring_backward_shared_question_reassembles():
         share = LS.ShardedRank(shards, rank, shared_doc=0)
         say(f"  zigzag rank {rank}, shared question: live steps {share.live_steps}")
         share.run_planned()
-        dq, dkvs = share.backward(dev_bf16(do[tok[rank]]))
+        dq, dkvs = share.backward(dev_bf16(do[tok[rank]]), ring=ring)
         for st, dkv in zip(share.steps, dkvs):
             if dkv is not None:
                 dk_sum[st["source"]] += dkv
@@ -261,3 +263,57 @@ def test_ring_backward_shared_question_reassembles():
         dv_all[tok[s]] = to64(dk_sum[s][1])
     for name, got, want in zip(("dq", "dk", "dv"), (dq_all, dk_all, dv_all), ref):
         check_grad(got, want, f"zigzag ring {name}, shared question")
+
+
+@pytest.mark.parametrize("rank", [1, 3])
+def test_ring_dkv_launch_equals_the_step_backwards(rank):
+    """A zigzag rank's ring backward with every live step's dK/dV items in one launch: dq and
+    every step's partial dk, dv have the bits of the per-step backward; the merged key-tile
+    queue equals the oracle's (each step's transposed plan, merged longest first); the
+    workgroups' records cover every item once; summed per owner over all ranks the
+    gradients equal the oracle's."""
+    from load_balance_amd import zigzag as LZ
+    cp, C, H, Hkv, d = 4, 256, 8, 2, 128
+    T = 2 * cp * C
+    lengths = workloads.lognormal_lengths(T, 3, T)
+    r = np.random.default_rng(66 + rank)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    do_all = workloads.f32_to_bf16_bits(r.standard_normal((T, H, d)).astype(np.float32))
+
+    def get_chunk(c):
+        sl = slice(c * C, (c + 1) * C)
+        return q[sl], k[sl], v[sl]
+
+    share = LZ.RankShare(lengths, C, rank, cp, get_chunk)
+    say(f"  zigzag cp=4 rank {rank}: live steps {share.live_steps}")
+    share.run_planned()
+    rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in LZ.chunks_of_rank(rank, cp)])
+    dout = dev_bf16(do_all[rows])
+    dq, dkvs = share.backward(dout)
+    torch.cuda.synchronize()
+    ref_dq, ref_dkv = dq.clone(), {t: x.clone() for t, x in enumerate(dkvs) if x is not None}
+    dq, dkvs = share.backward(dout, ring=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref_dq), "dq"
+    for t, x in ref_dkv.items():
+        assert torch.equal(dkvs[t], x), f"dkv of step {t}"
+    assert lb.read_device_error(share.bwd_ring_workspace) == 0
+    # the merged key-tile queue against the oracle's
+    qp, qd = share.q_pos.cpu().numpy(), share.q_doc.cpu().numpy()
+    plans = []
+    for t in share.live_steps:
+        st = share.steps[t]
+        tl = OP.tiles_t(OP.fragments_block_t(qp, qd, st["kv_pos"].cpu().numpy(), st["kv_doc"].cpu().numpy()), 128)
+        plans.append([tl[i] for i in OP.lpt_order(tl)])
+    want = OP.merge_step_plans(plans)
+    got = lb.read_plan(share.bwd_ring_workspace, with_step=True)
+    assert len(got) == len(want)
+    for i, (a, b) in enumerate(zip(got, want)):
+        assert (a["q_start"], a["q_len"], a["q_pos0"], a["cost"], a["blocks"], a["step"]) == \
+               (b["q_start"], b["q_len"], b["q_pos0"], b["cost"], b["blocks"], b["step"]), i
+        assert [tuple(s) for s in a["spans"]] == [tuple(s) for s in b["spans"]], i
+    recs = lb.read_worker_timing(share.bwd_ring_workspace)
+    assert sum(x["items"] for x in recs) == sum(1 for t in want if t["spans"]) * Hkv
+    # the rank's dq against the oracle (every rank's dq rows are its own)
+    ref = OB.varlen_attention_bwd(q, k, v, do_all, workloads.cu_from_lengths(lengths), H, Hkv)
+    check_grad(to64(dq), ref[0][rows], f"rank {rank} ring dq")
