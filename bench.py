@@ -585,7 +585,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
     ap.add_argument("--no-ring", action="store_true",
-                    help="zigzag, cp_job: one attention launch per live step instead of one over all of them")
+                    help="zigzag, cp_job, zigzag_bwd: one attention (dK/dV) launch per live step instead of one over all of them")
     ap.add_argument("--overlap", type=int, default=4,
                     help="zigzag, cp_job: streams the ring steps' attention launches are spread over (0: one)")
     ap.add_argument("--worker-records", default=None, metavar="PATH",
