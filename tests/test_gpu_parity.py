@@ -802,3 +802,26 @@ def test_ring_made_for_other_steps_runs_nothing():
     assert lb.read_device_error(share.ring_workspace) & lb.DEVERR_PLAN
     for o, l in zip(outs, lses):
         assert torch.all(o == 7.0) and torch.all(l == 7.0)
+
+
+def test_ring_too_small_for_the_steps_runs_nothing():
+    """A ring workspace with room for two tiles: the merge flags LB_DEVERR_CAPACITY, the
+    ring holds no work, and a launch over it writes no partial."""
+    share = ring_share(rank=2)
+    share.run_ring()
+    torch.cuda.synchronize()
+    live = [share.steps[t] for t in share.live_steps]
+    n_q, H, d = share.q.shape
+    Hkv = live[0]["kv"].shape[2]
+    header_and_records = 256 + 2048 * 40  # the ring's tiles start after the worker records
+    small = torch.empty(header_and_records + 2 * 96, dtype=torch.uint8, device="cuda")
+    lb.plan_ring([share.step_workspaces[t] for t in share.live_steps], [st["kv"].shape[1] for st in live], n_q, H,
+                 Hkv, d, small)
+    outs = [torch.full_like(share.out, 7.0) for _ in live]
+    lses = [torch.full_like(share.lse, 7.0) for _ in live]
+    lb.ring_attn_run(share.q, [st["kv"][0] for st in live], [st["kv"][1] for st in live], outs, lses, small)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(small) & lb.DEVERR_CAPACITY
+    assert lb.read_plan(small) == []
+    for o, l in zip(outs, lses):
+        assert torch.all(o == 7.0) and torch.all(l == 7.0)
