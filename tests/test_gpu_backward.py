@@ -266,14 +266,15 @@ def test_ring_backward_shared_question_reassembles(ring):
 
 
 @pytest.mark.parametrize("rank", [1, 3])
-def test_ring_dkv_launch_equals_the_step_backwards(rank):
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64)])
+def test_ring_dkv_launch_equals_the_step_backwards(rank, H, Hkv, d):
     """A zigzag rank's ring backward with every live step's dK/dV items in one launch: dq and
     every step's partial dk, dv have the bits of the per-step backward; the merged key-tile
     queue equals the oracle's (each step's transposed plan, merged longest first); the
     workgroups' records cover every item once; summed per owner over all ranks the
     gradients equal the oracle's."""
     from load_balance_amd import zigzag as LZ
-    cp, C, H, Hkv, d = 4, 256, 8, 2, 128
+    cp, C = 4, 256
     T = 2 * cp * C
     lengths = workloads.lognormal_lengths(T, 3, T)
     r = np.random.default_rng(66 + rank)
@@ -285,7 +286,7 @@ def test_ring_dkv_launch_equals_the_step_backwards(rank):
         return q[sl], k[sl], v[sl]
 
     share = LZ.RankShare(lengths, C, rank, cp, get_chunk)
-    say(f"  zigzag cp=4 rank {rank}: live steps {share.live_steps}")
+    say(f"  zigzag cp=4 rank {rank} H={H} Hkv={Hkv} d={d}: live steps {share.live_steps}")
     share.run_planned()
     rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in LZ.chunks_of_rank(rank, cp)])
     dout = dev_bf16(do_all[rows])

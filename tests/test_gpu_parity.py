@@ -684,8 +684,7 @@ def test_sharded_shared_question_reassembles(rule):
 # --------------------------------------------------------------------------
 # one attention launch over every live ring step (ring workspace)
 # --------------------------------------------------------------------------
-def ring_share(cp=4, C=256, rank=2, seed=9):
-    H, Hkv, d = 8, 2, 128
+def ring_share(cp=4, C=256, rank=2, seed=9, H=8, Hkv=2, d=128):
     T = 2 * cp * C
     lengths = workloads.lognormal_lengths(T, seed, T)
     r = np.random.default_rng(14 + seed)
@@ -733,13 +732,15 @@ def check_ring_against_steps(share, what):
 
 
 @pytest.mark.parametrize("rank", [0, 2, 3])
-def test_ring_launch_equals_the_step_launches(rank):
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64), (16, 2, 128)])
+def test_ring_launch_equals_the_step_launches(rank, H, Hkv, d):
     """A zigzag rank's live steps run from one merged queue in one launch: the same bits as
     one launch per step, the merged queue equal to the oracle's (every step's tiles, key
-    blocks descending, ties by step), every item run once."""
-    share = ring_share(rank=rank)
-    say(f"  zigzag cp=4 rank {rank}: live steps {share.live_steps}")
-    check_ring_against_steps(share, f"rank {rank}")
+    blocks descending, ties by step), every item run once; every head grouping and head
+    size the ring kernel is built for."""
+    share = ring_share(rank=rank, H=H, Hkv=Hkv, d=d)
+    say(f"  zigzag cp=4 rank {rank} H={H} Hkv={Hkv} d={d}: live steps {share.live_steps}")
+    check_ring_against_steps(share, f"rank {rank} H={H} Hkv={Hkv} d={d}")
 
 
 def test_ring_graph_replays_equal_eager_runs():
