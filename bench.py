@@ -211,8 +211,9 @@ class ZigzagStep:
 
         self.share = lb.zigzag.RankShare(lengths, chunk, rank, cp, get_chunk)
         self.share.plan_all()  # allocates the per-step workspaces outside the timed region
-        # the share's 16 launches are replayed from one HIP graph, the attention launches
-        # spread over `overlap` streams so that the steps overlap (none: one stream);
+        # the share is replayed from one HIP graph: with ring, the live steps' plans, their
+        # merged queue, one attention launch and the merges; without, the per-step attention
+        # launches spread over `overlap` streams so that the steps overlap (none: one stream);
         # per-kernel events need eager launches one at a time (run_eager)
         self.streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap and not ring else None
         if ring:
@@ -587,7 +588,8 @@ def main():
     ap.add_argument("--no-ring", action="store_true",
                     help="zigzag, cp_job, zigzag_bwd: one attention (dK/dV) launch per live step instead of one over all of them")
     ap.add_argument("--overlap", type=int, default=4,
-                    help="zigzag, cp_job: streams the ring steps' attention launches are spread over (0: one)")
+                    help="zigzag, cp_job with --no-ring: streams the ring steps' attention launches are spread over "
+                         "(0: one)")
     ap.add_argument("--worker-records", default=None, metavar="PATH",
                     help="write the last launch's per-workgroup records and its plan (JSON) to PATH")
     args = ap.parse_args()
