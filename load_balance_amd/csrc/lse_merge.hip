@@ -77,7 +77,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
         ca[j] = ok ? s_wa[k] : -1.0f;  // -1: no unit
         cb[j] = s_wb[k];
         dst[j] = reinterpret_cast<f32x4*>(a.out_a + rh * a.d) + c;
-        y[j] = ok ? reinterpret_cast<const f32x4*>(a.out_b + rh * a.d)[c] : f32x4{};
+        // out_b is read once and never again: a non-temporal load keeps it from displacing
+        // out_a's lines, which are written back right after
+        y[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.out_b + rh * a.d) + c) : f32x4{};
         // out_a is not read where lse_a = -inf (ca = 0): the first partial never wrote that row
         x[j] = ca[j] > 0.0f ? *dst[j] : f32x4{};
       }
