@@ -629,30 +629,39 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
   WsHeader* rh = reinterpret_cast<WsHeader*>(m.ring);
   lb_plan_tile* out = reinterpret_cast<lb_plan_tile*>(m.ring + kRingTilesOffset);
 
+  // one thread per step reads that step's header, so the steps' header loads overlap
+  __shared__ int32_t work_of[kMaxPlanSteps], empty_of[kMaxPlanSteps], err_of[kMaxPlanSteps];
+  __shared__ int64_t pairs_of[kMaxPlanSteps];
+  if (tid < n_steps) {
+    const int s = tid;
+    const WsHeader* h = reinterpret_cast<const WsHeader*>(m.step_ws[s]);
+    const int64_t nt = h->n_tiles, ne = h->n_empty;
+    // a step's plan must be a block plan of the ring's kind made for these shapes, and lie inside
+    // its workspace; its own error bits pass on
+    const bool bad = h->magic != kPlanMagic || h->transposed != m.transposed || h->has_lower != 0 ||
+                     h->plan_n_q != m.n_q || h->plan_n_kv != m.n_kv[s] || h->plan_heads != m.heads ||
+                     h->plan_kv_heads != m.kv_heads || nt < 0 || ne < 0 || ne > nt ||
+                     h->off_tiles < kWorkersOffset || h->off_order < kWorkersOffset ||
+                     h->off_tiles + nt * (int64_t)sizeof(lb_plan_tile) > m.step_ws_bytes[s] ||
+                     h->off_order + nt * 4 > m.step_ws_bytes[s];
+    err_of[s] = bad ? LB_DEVERR_PLAN : h->err;
+    work_of[s] = bad ? 0 : (int)(nt - ne);
+    empty_of[s] = bad ? 0 : (int)ne;
+    tiles_of[s] = reinterpret_cast<const lb_plan_tile*>(m.step_ws[s] + (bad ? 0 : h->off_tiles));
+    order_of[s] = reinterpret_cast<const int32_t*>(m.step_ws[s] + (bad ? 0 : h->off_order));
+    ntiles_of[s] = bad ? 0 : (int)nt;
+    pairs_of[s] = bad ? 0 : h->total_pairs;
+  }
+  __syncthreads();
   if (tid == 0) {
     int e = 0;
     int64_t p = 0;
     base[0] = ebase[0] = 0;
     for (int s = 0; s < n_steps; ++s) {
-      const WsHeader* h = reinterpret_cast<const WsHeader*>(m.step_ws[s]);
-      const int64_t nt = h->n_tiles, ne = h->n_empty;
-      // a step's plan must be a block plan of the ring's kind made for these shapes, and lie inside
-      // its workspace; its own error bits pass on
-      const bool bad = h->magic != kPlanMagic || h->transposed != m.transposed || h->has_lower != 0 ||
-                       h->plan_n_q != m.n_q || h->plan_n_kv != m.n_kv[s] || h->plan_heads != m.heads ||
-                       h->plan_kv_heads != m.kv_heads || nt < 0 || ne < 0 || ne > nt ||
-                       h->off_tiles < kWorkersOffset || h->off_order < kWorkersOffset ||
-                       h->off_tiles + nt * (int64_t)sizeof(lb_plan_tile) > m.step_ws_bytes[s] ||
-                       h->off_order + nt * 4 > m.step_ws_bytes[s];
-      if (bad) e |= LB_DEVERR_PLAN;
-      if (!bad) e |= h->err;
-      const int work = bad ? 0 : (int)(nt - ne), empty = bad ? 0 : (int)ne;
-      base[s + 1] = base[s] + work;
-      ebase[s + 1] = ebase[s] + empty;
-      tiles_of[s] = reinterpret_cast<const lb_plan_tile*>(m.step_ws[s] + (bad ? 0 : h->off_tiles));
-      order_of[s] = reinterpret_cast<const int32_t*>(m.step_ws[s] + (bad ? 0 : h->off_order));
-      ntiles_of[s] = bad ? 0 : (int)nt;
-      p += bad ? 0 : h->total_pairs;
+      e |= err_of[s];
+      base[s + 1] = base[s] + work_of[s];
+      ebase[s + 1] = ebase[s] + empty_of[s];
+      p += pairs_of[s];
     }
     if (base[n_steps] > kSortCap || (int64_t)base[n_steps] + ebase[n_steps] > m.ring_cap) e |= LB_DEVERR_CAPACITY;
     err = e;
