@@ -132,6 +132,53 @@ def _check(status: int, what: str):
         raise LBError(f"{what}: {msg} (status {status})")
 
 
+def _dev(t, name, dtype, shape=None, device=None):
+    """Checks one operand before its pointer crosses the C ABI: a contiguous tensor of the
+    given dtype (or one of a tuple of dtypes), the exact shape when given, on `device` when
+    given.  A wrong dtype or a short buffer would otherwise reach a kernel.  Every wrapper
+    checks all its operands this way against its first one, then that one with _gpu, so a
+    host tensor never reaches the library either."""
+    if not isinstance(t, torch.Tensor):
+        raise LBError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if device is not None and t.device != device:
+        raise LBError(f"{name} is on {t.device}, the other operands on {device}")
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dtypes:
+        raise LBError(f"{name} must be {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise LBError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise LBError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    return t
+
+
+def _gpu(t, name):
+    """The operands share one device (checked by _dev); it must be a GPU."""
+    if t.device.type != "cuda":
+        raise LBError(f"{name} and the other operands must be GPU tensors, got {t.device}")
+
+
+def _ws(t, name="workspace", device=None):
+    """A workspace: a contiguous 1-D uint8 GPU tensor."""
+    _dev(t, name, torch.uint8, device=device)
+    if t.dim() != 1:
+        raise LBError(f"{name} must be 1-D")
+    return t
+
+
+def _raise_device_error(workspace, what, stream=None):
+    """For a call whose workspace the wrapper allocated (the caller cannot read it back):
+    errors only the device sees (malformed cu_seqlens, too many key runs, a capacity
+    overflow) leave out and lse unwritten, so they are read here and raised.  This waits
+    for the stream; callers that pass their own workspace read it with read_device_error."""
+    err = read_device_error(workspace, stream=stream)
+    if err:
+        names = [n for n, b in (("CU_SEQLENS", DEVERR_CU_SEQLENS), ("CAPACITY", DEVERR_CAPACITY),
+                                ("SPANS", DEVERR_SPANS), ("PLAN", DEVERR_PLAN), ("SLICES", DEVERR_SLICES)) if err & b]
+        raise LBError(f"{what}: the device rejected the call's metadata ({'|'.join(names) or err}); "
+                      "nothing was computed")
+
+
 def _stream(stream=None) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -161,24 +208,36 @@ def new_workspace(max_tokens: int, max_segments: int, heads: int, kv_heads: int,
 def varlen_attn_fwd(q, k, v, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, out=None, lse=None, workspace=None,
                     stream=None):
     """out [T,H,d] bf16, lse [H,T] fp32 for q [T,H,d], k/v [T,H_kv,d] bf16 and int32 cu_seqlens."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise LBError("q must be [T, H, d]")
     T, H, d = q.shape
+    dev = q.device
+    _dev(k, "k", torch.bfloat16, device=dev)
+    if k.dim() != 3:
+        raise LBError("k must be [T, H_kv, d]")
     Hkv = k.shape[1]
+    _dev(k, "k", torch.bfloat16, (T, Hkv, d), dev)
+    _dev(v, "v", torch.bfloat16, (T, Hkv, d), dev)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise LBError("cu_seqlens must be 1-D with at least two entries")
     n_seg = cu_seqlens.numel() - 1
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(T, max(1, n_seg), H, Hkv, q.device)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
-    if cu_seqlens.dtype != torch.int32 or lse.dtype != torch.float32:
-        raise LBError("cu_seqlens must be int32 and lse float32")
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.bfloat16, (T, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, T), dev)
+    owned = workspace is None
+    workspace = new_workspace(T, max(1, n_seg), H, Hkv, dev) if owned else _ws(workspace, device=dev)
+    _gpu(q, "q")
     st = lib().lb_varlen_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), n_seg, T, H, Hkv, d,
                                   int(mask_kind), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_varlen_attn_fwd")
+    if owned:
+        _raise_device_error(workspace, "lb_varlen_attn_fwd", stream)
     return out, lse
 
 
@@ -190,37 +249,57 @@ def block_attn_fwd(q_shard, kv_chunk, q_pos, kv_pos, q_doc, kv_doc, out=None, ls
 
     Returns out [n_q,H,d] fp32 (rows with no visible key left unwritten) and lse [H,n_q] fp32.
     """
+    _dev(q_shard, "q_shard", torch.bfloat16)
+    if q_shard.dim() != 3:
+        raise LBError("q_shard must be [n_q, H, d]")
     n_q, H, d = q_shard.shape
+    dev = q_shard.device
+    _dev(kv_chunk, "kv_chunk", torch.bfloat16, device=dev)
+    if kv_chunk.dim() != 4 or kv_chunk.shape[0] != 2 or kv_chunk.shape[3] != d:
+        raise LBError("kv_chunk must be [2, n_kv, H_kv, d] (K then V)")
     _, n_kv, Hkv, _ = kv_chunk.shape
+    _meta(q_pos, q_doc, n_q, "q", dev)
+    _meta(kv_pos, kv_doc, n_kv, "kv", dev)
     if out is None:
-        out = torch.empty((n_q, H, d), dtype=torch.float32, device=q_shard.device)
+        out = torch.empty((n_q, H, d), dtype=torch.float32, device=dev)
     if lse is None:
-        lse = torch.empty((H, n_q), dtype=torch.float32, device=q_shard.device)
-    if workspace is None:
+        lse = torch.empty((H, n_q), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.float32, (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    owned = workspace is None
+    if owned:
         runs = max_runs if max_runs is not None else max(n_q, n_kv, 1)
-        workspace = new_workspace(max(n_q, n_kv), runs, H, Hkv, q_shard.device)
-    for t, name in ((q_shard, "q_shard"), (kv_chunk, "kv_chunk")):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
-    for t, name in ((q_pos, "q_pos"), (kv_pos, "kv_pos"), (q_doc, "q_doc"), (kv_doc, "kv_doc")):
-        if t.dtype != torch.int32:
-            raise LBError(f"{name} must be int32")
+        workspace = new_workspace(max(n_q, n_kv), runs, H, Hkv, dev)
+    else:
+        _ws(workspace, device=dev)
+    _gpu(q_shard, "q_shard")
     st = lib().lb_block_attn_fwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(q_pos), _ptr(kv_pos),
                                  _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, int(shared_doc), _ptr(out), _ptr(lse),
                                  _ptr(workspace),
                                  workspace.numel(), ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_block_attn_fwd")
+    if owned:
+        _raise_device_error(workspace, "lb_block_attn_fwd", stream)
     return out, lse
+
+
+def _meta(pos, doc, n, side, device):
+    """Positions and document ids of one side of a block step: int32 [n] each."""
+    _dev(pos, f"{side}_pos", torch.int32, (n,), device)
+    _dev(doc, f"{side}_doc", torch.int32, (n,), device)
 
 
 def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAUSAL_DOC, workspace=None,
                 stream=None):
     """First half of varlen_attn_fwd: writes the tile plan into ``workspace`` (returned)."""
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise LBError("cu_seqlens must be 1-D with at least two entries")
     n_seg = cu_seqlens.numel() - 1
     if workspace is None:
         workspace = new_workspace(total_tokens, max(1, n_seg), heads, kv_heads, cu_seqlens.device)
-    if cu_seqlens.dtype != torch.int32:
-        raise LBError("cu_seqlens must be int32")
+    _ws(workspace, device=cu_seqlens.device)
+    _gpu(cu_seqlens, "cu_seqlens")
     _check(lib().lb_plan_varlen(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d, int(mask_kind),
                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_plan_varlen")
@@ -229,9 +308,10 @@ def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAU
 
 def plan_block(q_pos, q_doc, kv_pos, kv_doc, heads, kv_heads, d, workspace, stream=None, shared_doc=NO_SHARED_DOC):
     """First half of block_attn_fwd: writes the tile plan into ``workspace``."""
-    for t, name in ((q_pos, "q_pos"), (kv_pos, "kv_pos"), (q_doc, "q_doc"), (kv_doc, "kv_doc")):
-        if t.dtype != torch.int32:
-            raise LBError(f"{name} must be int32")
+    _ws(workspace)
+    _meta(q_pos, q_doc, q_pos.numel(), "q", workspace.device)
+    _meta(kv_pos, kv_doc, kv_pos.numel(), "kv", workspace.device)
+    _gpu(workspace, "workspace")
     _check(lib().lb_plan_block(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), _ptr(kv_pos), _ptr(kv_doc), kv_pos.numel(),
                                heads, kv_heads, d, int(shared_doc), _ptr(workspace), workspace.numel(),
                                ctypes.c_void_p(_stream(stream))), "lb_plan_block")
@@ -245,13 +325,17 @@ def plan_block_steps(q_pos, q_doc, kv_pos_list, kv_doc_list, heads, kv_heads, d,
     n = len(workspaces)
     if not (len(kv_pos_list) == len(kv_doc_list) == n):
         raise LBError("kv_pos_list, kv_doc_list and workspaces must have one entry per step")
-    for t, name in [(q_pos, "q_pos"), (q_doc, "q_doc")] + [(x, "kv_pos") for x in kv_pos_list] + \
-            [(x, "kv_doc") for x in kv_doc_list]:
-        if t.dtype != torch.int32:
-            raise LBError(f"{name} must be int32")
+    if n < 1:
+        raise LBError("plan_block_steps needs at least one step")
+    dev = workspaces[0].device
+    _meta(q_pos, q_doc, q_pos.numel(), "q", dev)
+    for s_, (kp, kd, w) in enumerate(zip(kv_pos_list, kv_doc_list, workspaces)):
+        _meta(kp, kd, kp.numel(), f"step {s_} kv", dev)
+        _ws(w, f"workspaces[{s_}]", dev)
     ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
     n_kv = (ctypes.c_int32 * max(n, 1))(*[t.numel() for t in kv_pos_list])
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
+    _gpu(q_pos, "q_pos")
     _check(lib().lb_plan_block_steps(_ptr(q_pos), _ptr(q_doc), q_pos.numel(), ptrs(kv_pos_list), ptrs(kv_doc_list),
                                      n_kv, n, heads, kv_heads, d, int(shared_doc), ptrs(workspaces), sizes,
                                      ctypes.c_void_p(_stream(stream))), "lb_plan_block_steps")
@@ -277,9 +361,13 @@ def plan_ring(workspaces, n_kv, n_q, heads, kv_heads, d, ring_workspace, stream=
     n = len(workspaces)
     if len(n_kv) != n:
         raise LBError("n_kv must have one entry per workspace")
+    _ws(ring_workspace, "ring_workspace")
+    for i, w in enumerate(workspaces):
+        _ws(w, f"workspaces[{i}]", ring_workspace.device)
     ptrs = (ctypes.c_void_p * max(n, 1))(*[w.data_ptr() for w in workspaces])
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
     nkv = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in n_kv])
+    _gpu(ring_workspace, "ring_workspace")
     _check(lib().lb_plan_ring(ptrs, sizes, nkv, n, n_q, heads, kv_heads, d, _ptr(ring_workspace),
                               ring_workspace.numel(), ctypes.c_void_p(_stream(stream))), "lb_plan_ring")
     return ring_workspace
@@ -289,20 +377,46 @@ def ring_attn_run(q, ks, vs, outs, lses, ring_workspace, stream=None):
     """Runs a ring workspace's items in one launch: step s reads ks[s], vs[s] (bf16
     [n_kv_s,H_kv,d]) and writes its partial into outs[s] (fp32 [n_q,H,d]) and lses[s]
     (fp32 [H,n_q]), as attn_run would for that step's own plan."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise LBError("q must be [n_q, H, d]")
     n_q, H, d = q.shape
+    dev = q.device
     n = len(ks)
-    if not (len(vs) == len(outs) == len(lses) == n):
-        raise LBError("ks, vs, outs and lses must have one entry per step")
-    for o, l in zip(outs, lses):
-        if o.dtype != torch.float32 or l.dtype != torch.float32:
-            raise LBError("ring partials are float32")
+    if n < 1 or not (len(vs) == len(outs) == len(lses) == n):
+        raise LBError("ks, vs, outs and lses must have one entry per step (at least one)")
+    _ws(ring_workspace, "ring_workspace", dev)
+    if ks[0].dim() != 3:
+        raise LBError("ks[s] must be [n_kv, H_kv, d]")
     Hkv = ks[0].shape[1]
+    for i in range(n):
+        _dev(ks[i], f"ks[{i}]", torch.bfloat16, (ks[i].shape[0], Hkv, d), dev)
+        _dev(vs[i], f"vs[{i}]", torch.bfloat16, tuple(ks[i].shape), dev)
+        _dev(outs[i], f"outs[{i}]", torch.float32, (n_q, H, d), dev)
+        _dev(lses[i], f"lses[{i}]", torch.float32, (H, n_q), dev)
     ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
     nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[0] for k in ks])
+    _gpu(q, "q")
     _check(lib().lb_ring_attn_run(_ptr(q), n_q, H, Hkv, d, n, ptrs(ks), ptrs(vs), nkv, ptrs(outs), ptrs(lses),
                                   _ptr(ring_workspace), ring_workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_ring_attn_run")
     return outs, lses
+
+
+def _run_operands(q, k, v, out, lse, workspace):
+    """Checks the operands of a plan's run; returns n_q, H, d, n_kv, H_kv."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise LBError("q must be [n_q, H, d] and k, v [n_kv, H_kv, d]")
+    n_q, H, d = q.shape
+    n_kv, Hkv = k.shape[0], k.shape[1]
+    dev = q.device
+    _dev(k, "k", torch.bfloat16, (n_kv, Hkv, d), dev)
+    _dev(v, "v", torch.bfloat16, (n_kv, Hkv, d), dev)
+    _dev(out, "out", (torch.bfloat16, torch.float32), (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    _ws(workspace, device=dev)
+    return n_q, H, d, n_kv, Hkv
 
 
 def attn_run(q, k, v, out, lse, workspace, stream=None):
@@ -310,10 +424,8 @@ def attn_run(q, k, v, out, lse, workspace, stream=None):
 
     q [n_q,H,d], k/v [n_kv,H_kv,d] bf16; out bf16 or fp32 [n_q,H,d]; lse fp32 [H,n_q].
     """
-    n_q, H, d = q.shape
-    n_kv, Hkv = k.shape[0], k.shape[1]
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise LBError("out must be bfloat16 or float32")
+    n_q, H, d, n_kv, Hkv = _run_operands(q, k, v, out, lse, workspace)
+    _gpu(q, "q")
     _check(lib().lb_attn_run(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, H, Hkv, d, int(out.dtype == torch.float32),
                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream(stream))), "lb_attn_run")
@@ -322,8 +434,8 @@ def attn_run(q, k, v, out, lse, workspace, stream=None):
 
 def attn_run_lower(q, k, v, out, lse, workspace, stream=None):
     """attn_run for plans with lower-bounded spans (INV-CAUSAL / BI-CAUSAL slices)."""
-    n_q, H, d = q.shape
-    n_kv, Hkv = k.shape[0], k.shape[1]
+    n_q, H, d, n_kv, Hkv = _run_operands(q, k, v, out, lse, workspace)
+    _gpu(q, "q")
     _check(lib().lb_attn_run_lower(_ptr(q), _ptr(k), _ptr(v), n_q, n_kv, H, Hkv, d, int(out.dtype == torch.float32),
                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                    ctypes.c_void_p(_stream(stream))), "lb_attn_run_lower")
@@ -332,10 +444,15 @@ def attn_run_lower(q, k, v, out, lse, workspace, stream=None):
 
 def lse_merge(out_a, lse_a, out_b, lse_b, stream=None):
     """In place: (out_a, lse_a) <- merge((out_a, lse_a), (out_b, lse_b)).  fp32 [R,H,d] and [H,R]."""
+    _dev(out_a, "out_a", torch.float32)
+    if out_a.dim() != 3:
+        raise LBError("out_a must be [R, H, d]")
     R, H, d = out_a.shape
-    for t in (out_a, lse_a, out_b, lse_b):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise LBError("lse_merge takes contiguous float32 tensors")
+    dev = out_a.device
+    _dev(lse_a, "lse_a", torch.float32, (H, R), dev)
+    _dev(out_b, "out_b", torch.float32, (R, H, d), dev)
+    _dev(lse_b, "lse_b", torch.float32, (H, R), dev)
+    _gpu(out_a, "out_a")
     st = lib().lb_lse_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), R, H, d,
                             ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_lse_merge")
@@ -343,7 +460,9 @@ def lse_merge(out_a, lse_a, out_b, lse_b, stream=None):
 
 
 def read_device_error(workspace, stream=None) -> int:
+    _ws(workspace)
     err = ctypes.c_int32(0)
+    _gpu(workspace, "workspace")
     _check(lib().lb_read_device_error(_ptr(workspace), workspace.numel(), ctypes.byref(err),
                                       ctypes.c_void_p(_stream(stream))), "lb_read_device_error")
     return err.value
@@ -352,8 +471,10 @@ def read_device_error(workspace, stream=None) -> int:
 def read_plan(workspace, max_tiles: int = 1 << 16, stream=None, with_step=False):
     """The last call's tiles in queue order, as dicts (q_start, q_len, q_pos0, spans, cost, blocks);
     with_step adds each tile's step (a ring workspace's `reserved` field)."""
+    _ws(workspace)
     buf = (PlanTile * max_tiles)()
     n = ctypes.c_int32(0)
+    _gpu(workspace, "workspace")
     _check(lib().lb_read_plan(_ptr(workspace), workspace.numel(), buf, max_tiles, ctypes.byref(n),
                               ctypes.c_void_p(_stream(stream))), "lb_read_plan")
     out = []
@@ -370,8 +491,10 @@ def read_plan(workspace, max_tiles: int = 1 << 16, stream=None, with_step=False)
 
 
 def read_worker_timing(workspace, max_records: int = 4096, stream=None):
+    _ws(workspace)
     buf = (WorkerRecord * max_records)()
     n = ctypes.c_int32(0)
+    _gpu(workspace, "workspace")
     _check(lib().lb_read_worker_timing(_ptr(workspace), workspace.numel(), buf, max_records, ctypes.byref(n),
                                        ctypes.c_void_p(_stream(stream))), "lb_read_worker_timing")
     return [dict(hw_id=r.hw_id, xcc_id=r.xcc_id, t_start=r.t_start, t_end=r.t_end, pairs=r.pairs,
@@ -400,20 +523,33 @@ def block_attn_bwd_ring(q, kvs, dout, lse, dvec, q_pos, q_doc, kv_pos_list, kv_d
     [2,n_kv,H_kv,d]) with kv_pos_list[s], kv_doc_list[s]; dq (fp32 [n_q,H,d]) is added to,
     step after step; dkvs[s] (fp32 [2,n_kv,H_kv,d]) receives step s's partial dk, dv.  One
     dQ launch per step and one dK/dV launch over every step's key tiles."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise LBError("q must be [n_q, H, d]")
     n_q, H, d = q.shape
+    dev = q.device
     n = len(kvs)
-    if not (len(kv_pos_list) == len(kv_doc_list) == len(dkvs) == len(workspaces) == n):
-        raise LBError("kvs, kv_pos_list, kv_doc_list, dkvs and workspaces need one entry per step")
-    for t in [q_pos, q_doc] + list(kv_pos_list) + list(kv_doc_list):
-        if t.dtype != torch.int32:
-            raise LBError("positions and document ids must be int32")
-    for x in list(dkvs) + [dq, lse, dvec]:
-        if x.dtype != torch.float32:
-            raise LBError("dq, dkv, lse and dvec are float32")
+    if n < 1 or not (len(kv_pos_list) == len(kv_doc_list) == len(dkvs) == len(workspaces) == n):
+        raise LBError("kvs, kv_pos_list, kv_doc_list, dkvs and workspaces need one entry per step (at least one)")
+    _dev(dout, "dout", torch.bfloat16, (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    _dev(dvec, "dvec", torch.float32, (H, n_q), dev)
+    _dev(dq, "dq", torch.float32, (n_q, H, d), dev)
+    _meta(q_pos, q_doc, n_q, "q", dev)
+    _ws(ring_workspace, "ring_workspace", dev)
+    if kvs[0].dim() != 4:
+        raise LBError("kvs[s] must be [2, n_kv, H_kv, d]")
     Hkv = kvs[0].shape[2]
+    for i in range(n):
+        n_kv = kvs[i].shape[1]
+        _dev(kvs[i], f"kvs[{i}]", torch.bfloat16, (2, n_kv, Hkv, d), dev)
+        _dev(dkvs[i], f"dkvs[{i}]", torch.float32, (2, n_kv, Hkv, d), dev)
+        _meta(kv_pos_list[i], kv_doc_list[i], n_kv, f"step {i} kv", dev)
+        _ws(workspaces[i], f"workspaces[{i}]", dev)
     ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
     nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[1] for k in kvs])
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
+    _gpu(q, "q")
     _check(lib().lb_block_attn_bwd_ring(_ptr(q), n_q, _ptr(dout), _ptr(lse), _ptr(dvec), _ptr(q_pos), _ptr(q_doc), H,
                                         Hkv, d, int(shared_doc), n, ptrs(kvs), nkv, ptrs(kv_pos_list),
                                         ptrs(kv_doc_list), _ptr(dq), ptrs(dkvs), ptrs(workspaces), sizes,
@@ -424,11 +560,15 @@ def block_attn_bwd_ring(q, kvs, dout, lse, dvec, q_pos, q_doc, kv_pos_list, kv_d
 
 def attn_bwd_rowdot(out, dout, dvec=None, stream=None):
     """D [H,R] fp32 = sum over d of out * dout; out bf16 or fp32 [R,H,d], dout bf16 [R,H,d]."""
+    _dev(dout, "dout", torch.bfloat16)
+    if dout.dim() != 3:
+        raise LBError("dout must be [R, H, d]")
     R, H, d = dout.shape
+    _dev(out, "out", (torch.bfloat16, torch.float32), (R, H, d), dout.device)
     if dvec is None:
         dvec = torch.empty((H, R), dtype=torch.float32, device=dout.device)
-    if out.dtype not in (torch.bfloat16, torch.float32) or dout.dtype != torch.bfloat16:
-        raise LBError("out must be bfloat16 or float32 and dout bfloat16")
+    _dev(dvec, "dvec", torch.float32, (H, R), dout.device)
+    _gpu(dout, "dout")
     _check(lib().lb_attn_bwd_rowdot(_ptr(out), int(out.dtype == torch.float32), _ptr(dout), R, H, d, _ptr(dvec),
                                     ctypes.c_void_p(_stream(stream))), "lb_attn_bwd_rowdot")
     return dvec
@@ -437,48 +577,82 @@ def attn_bwd_rowdot(out, dout, dvec=None, stream=None):
 def varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, dq=None, dk=None, dv=None,
                     workspace=None, stream=None):
     """dq [T,H,d], dk, dv [T,H_kv,d] (bf16) of varlen_attn_fwd from its out and lse."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise LBError("q must be [T, H, d] and k, v [T, H_kv, d]")
     T, H, d = q.shape
     Hkv = k.shape[1]
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v")):
+        _dev(t, name, torch.bfloat16, (T, Hkv, d), dev)
+    for t, name in ((out, "out"), (dout, "dout")):
+        _dev(t, name, torch.bfloat16, (T, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, T), dev)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise LBError("cu_seqlens must be 1-D with at least two entries")
     n_seg = cu_seqlens.numel() - 1
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(T, max(1, n_seg), H, Hkv), dtype=torch.uint8, device=q.device)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
-    if cu_seqlens.dtype != torch.int32 or lse.dtype != torch.float32:
-        raise LBError("cu_seqlens must be int32 and lse float32")
+    _dev(dq, "dq", torch.bfloat16, (T, H, d), dev)
+    _dev(dk, "dk", torch.bfloat16, (T, Hkv, d), dev)
+    _dev(dv, "dv", torch.bfloat16, (T, Hkv, d), dev)
+    owned = workspace is None
+    if owned:
+        workspace = torch.empty(bwd_workspace_bytes(T, max(1, n_seg), H, Hkv), dtype=torch.uint8, device=dev)
+    _ws(workspace, device=dev)
+    _gpu(q, "q")
     _check(lib().lb_varlen_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
                                     n_seg, T, H, Hkv, d, int(mask_kind), _ptr(dq), _ptr(dk), _ptr(dv),
                                     _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_varlen_attn_bwd")
+    if owned:
+        _raise_bwd_device_error(workspace, False, T, T, n_seg, H, Hkv, "lb_varlen_attn_bwd", stream)
     return dq, dk, dv
+
+
+def _raise_bwd_device_error(workspace, block_path, n_q, n_kv, n_seg, H, Hkv, what, stream):
+    """Both plans of a backward workspace the wrapper allocated: the query-tile plan at its
+    start, the key-tile plan at lb_bwd_key_plan_offset."""
+    _raise_device_error(workspace, what + " (query tiles)", stream)
+    off = bwd_key_plan_offset(block_path, n_q, n_kv, n_seg, H, Hkv, workspace.numel())
+    _raise_device_error(workspace[off:], what + " (key tiles)", stream)
 
 
 def block_attn_bwd(q_shard, kv_chunk, dout, lse, dvec, q_pos, kv_pos, q_doc, kv_doc, dq, dkv=None, workspace=None,
                    stream=None, shared_doc=NO_SHARED_DOC):
     """One ring step of the backward: adds this step's contribution to dq (fp32 [n_q,H,d]) and
     returns dkv (fp32 [2,n_kv,H_kv,d]: this step's dk, dv) together with dq."""
+    _dev(q_shard, "q_shard", torch.bfloat16)
+    if q_shard.dim() != 3 or kv_chunk.dim() != 4:
+        raise LBError("q_shard must be [n_q, H, d] and kv_chunk [2, n_kv, H_kv, d]")
     n_q, H, d = q_shard.shape
     _, n_kv, Hkv, _ = kv_chunk.shape
+    dev = q_shard.device
+    _dev(kv_chunk, "kv_chunk", torch.bfloat16, (2, n_kv, Hkv, d), dev)
+    _dev(dout, "dout", torch.bfloat16, (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    _dev(dvec, "dvec", torch.float32, (H, n_q), dev)
+    _dev(dq, "dq", torch.float32, (n_q, H, d), dev)
+    _meta(q_pos, q_doc, n_q, "q", dev)
+    _meta(kv_pos, kv_doc, n_kv, "kv", dev)
     if dkv is None:
-        dkv = torch.empty((2, n_kv, Hkv, d), dtype=torch.float32, device=q_shard.device)
-    if workspace is None:
+        dkv = torch.empty((2, n_kv, Hkv, d), dtype=torch.float32, device=dev)
+    _dev(dkv, "dkv", torch.float32, (2, n_kv, Hkv, d), dev)
+    owned = workspace is None
+    if owned:
         half = workspace_bytes(max(n_q, n_kv), max(n_q, n_kv, 1), H, Hkv)
-        workspace = torch.empty(2 * half + 512, dtype=torch.uint8, device=q_shard.device)
-    for t, name in ((q_shard, "q_shard"), (kv_chunk, "kv_chunk"), (dout, "dout")):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
-    for t, name in ((dq, "dq"), (dkv, "dkv"), (lse, "lse"), (dvec, "dvec")):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous float32 tensor")
+        workspace = torch.empty(2 * half + 512, dtype=torch.uint8, device=dev)
+    _ws(workspace, device=dev)
+    _gpu(q_shard, "q_shard")
     _check(lib().lb_block_attn_bwd(_ptr(q_shard), n_q, _ptr(kv_chunk), n_kv, _ptr(dout), _ptr(lse), _ptr(dvec),
                                    _ptr(q_pos), _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), H, Hkv, d, int(shared_doc),
                                    _ptr(dq),
                                    _ptr(dkv), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_block_attn_bwd")
+    if owned:
+        _raise_bwd_device_error(workspace, True, n_q, n_kv, max(n_q, n_kv, 1), H, Hkv, "lb_block_attn_bwd", stream)
     return dq, dkv
 
 
@@ -497,9 +671,12 @@ def _slice_tensor(slices, device):
 
 def plan_slices(slices, n_q, n_kv, heads, kv_heads, d, workspace=None, stream=None):
     """The plan of a slice-list mask into ``workspace`` (run it with attn_run)."""
-    sl = _slice_tensor(slices, "cuda")
+    sl = _slice_tensor(slices, "cuda" if workspace is None else workspace.device)
+    _dev(sl, "slices", torch.int32)
     if workspace is None:
         workspace = new_workspace(n_q, max(1, sl.shape[0]), heads, kv_heads, sl.device)
+    _ws(workspace, device=sl.device)
+    _gpu(sl, "sl")
     _check(lib().lb_plan_slices(_ptr(sl), sl.shape[0], n_q, n_kv, heads, kv_heads, d, _ptr(workspace),
                                 workspace.numel(), ctypes.c_void_p(_stream(stream))), "lb_plan_slices")
     return workspace
@@ -507,19 +684,30 @@ def plan_slices(slices, n_q, n_kv, heads, kv_heads, d, workspace=None, stream=No
 
 def slices_attn_fwd(q, k, v, slices, out=None, lse=None, workspace=None, stream=None):
     """out [n_q,H,d] bf16 and lse [H,n_q] of q against k/v under a slice-list mask."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise LBError("q must be [n_q, H, d] and k, v [n_kv, H_kv, d]")
     n_q, H, d = q.shape
     n_kv, Hkv = k.shape[0], k.shape[1]
-    sl = _slice_tensor(slices, q.device)
+    dev = q.device
+    _dev(k, "k", torch.bfloat16, (n_kv, Hkv, d), dev)
+    _dev(v, "v", torch.bfloat16, (n_kv, Hkv, d), dev)
+    sl = _slice_tensor(slices, dev)
+    _dev(sl, "slices", torch.int32, device=dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = new_workspace(n_q, max(1, sl.shape[0]), H, Hkv, q.device)
-    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise LBError(f"{name} must be a contiguous bfloat16 tensor")
+        lse = torch.empty((H, n_q), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.bfloat16, (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    owned = workspace is None
+    if owned:
+        workspace = new_workspace(n_q, max(1, sl.shape[0]), H, Hkv, dev)
+    _ws(workspace, device=dev)
+    _gpu(q, "q")
     _check(lib().lb_slices_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), sl.shape[0], n_q, n_kv, H, Hkv, d, _ptr(out),
                                     _ptr(lse), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_slices_attn_fwd")
+    if owned:
+        _raise_device_error(workspace, "lb_slices_attn_fwd", stream)
     return out, lse

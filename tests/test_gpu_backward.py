@@ -71,10 +71,19 @@ def varlen_case(lengths, H, Hkv, d, seed, mask="causal_doc"):
     return ws, off, cu
 
 
-@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (4, 2, 64), (8, 1, 64)])
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (4, 2, 64), (8, 1, 64), (32, 8, 128), (16, 8, 128),
+                                     (8, 8, 64)])
 def test_varlen_backward_every_element(H, Hkv, d):
     lengths = [1, 150, 37, 64, 1, 200, 3]
     varlen_case(lengths, H, Hkv, d, seed=H * 10 + Hkv + d)
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(32, 8, 128), (16, 8, 128)])
+def test_varlen_backward_eight_queues_many_items(H, Hkv, d):
+    """8 kv heads: the dQ and dK/dV kernels take one queue per XCD, and with documents of up
+    to 1000 tokens every queue holds several items of both kernels, stolen across queues."""
+    lengths = [1, 700, 3, 1, 257, 64, 129, 1000, 2]
+    varlen_case(lengths, H, Hkv, d, seed=H + Hkv + d)
 
 
 def test_varlen_backward_shared_question():
@@ -129,13 +138,13 @@ def test_single_token_documents():
     check_grad(to64(dv), want, "single-token dv")
 
 
-@pytest.mark.parametrize("rule", ["zigzag", "dispatch"])
-def test_ring_backward_reassembles_the_unsharded_gradient(rule):
+@pytest.mark.parametrize("rule,H,Hkv", [("zigzag", 8, 2), ("dispatch", 8, 2), ("zigzag", 32, 8)])
+def test_ring_backward_reassembles_the_unsharded_gradient(rule, H, Hkv):
     """Every rank of a cp = 4 sharding: the forward ring (block steps + merges) gives out and
     lse; D comes from the merged out; each step's backward adds its dq and returns the
     source chunk's partial dk, dv.  Summed per owner, they equal the unsharded gradient."""
     from load_balance_amd import sharding as LS
-    cp, H, Hkv, d = 4, 8, 2, 128
+    cp, d = 4, 128
     r = np.random.default_rng(21)
     lengths = [700, 37, 1, 260, 9, 301]
     lengths.append(2 * cp * 256 - sum(lengths))
@@ -227,14 +236,15 @@ def test_block_backward_shared_question_whole_pack():
         assert [tuple(s) for s in a["spans"]] == [tuple(s) for s in b["spans"]], i
 
 
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (32, 8)])
 @pytest.mark.parametrize("ring", [False, True])
-def test_ring_backward_shared_question_reassembles(ring):
+def test_ring_backward_shared_question_reassembles(ring, H, Hkv):
     """A shared-question pack sharded by sequence zigzag over cp = 4 ranks, document 0
     shared: each rank's forward ring and ring backward (steps no row sees send nothing back;
     with ring=True the steps' dK/dV items in one launch), summed per owner, equal the
     unsharded shared-question gradient."""
     from load_balance_amd import sharding as LS
-    cp, H, Hkv, d = 4, 8, 2, 128
+    cp, d = 4, 128
     r = np.random.default_rng(64)
     lengths = [500, 37, 1, 260, 9, 301]
     lengths.append(2 * cp * 256 - sum(lengths))
@@ -262,11 +272,11 @@ def test_ring_backward_shared_question_reassembles(ring):
         dk_all[tok[s]] = to64(dk_sum[s][0])
         dv_all[tok[s]] = to64(dk_sum[s][1])
     for name, got, want in zip(("dq", "dk", "dv"), (dq_all, dk_all, dv_all), ref):
-        check_grad(got, want, f"zigzag ring {name}, shared question")
+        check_grad(got, want, f"zigzag ring {name}, shared question, H={H}/{Hkv}")
 
 
 @pytest.mark.parametrize("rank", [1, 3])
-@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64)])
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64), (32, 8, 128), (16, 8, 128)])
 def test_ring_dkv_launch_equals_the_step_backwards(rank, H, Hkv, d):
     """A zigzag rank's ring backward with every live step's dK/dV items in one launch: dq and
     every step's partial dk, dv have the bits of the per-step backward; the merged key-tile

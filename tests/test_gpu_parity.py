@@ -160,6 +160,20 @@ def test_longtail_pack(longtail):
     assert sum(x["blocks"] for x in recs) == 8 * sum(t["blocks"] for t in plan)
 
 
+@pytest.mark.timeout(900)
+def test_longtail_pack_every_row(longtail, tmp_path):
+    """All 32768 rows x 32 heads of the 32K long-tail pack, as the benchmark runs it (one
+    launch over 256 persistent workgroups, 8 XCD queues, every item and every stolen tail),
+    against the float64 oracle: the oracle's rows are split over a pool of CPU processes."""
+    import oracle_pool
+    out, lse, ws = run_varlen(longtail)
+    st = oracle_pool.longtail_every_row(out.float().cpu().numpy(), lse.cpu().numpy(), 0, str(tmp_path), say)
+    say(f"  32K long-tail every row: out max {st['out_max']:.3e} mean {st['out_mean']:.3e}  "
+        f"lse max {st['lse_max']:.3e}")
+    assert st["finite"] and st["n"] == 32768 * 32 * 128
+    assert st["out_max"] <= OUT_MAX and st["out_mean"] <= OUT_MEAN and st["lse_max"] <= LSE_MAX
+
+
 def test_longtail_is_deterministic(longtail):
     a, la, _ = run_varlen(longtail)
     b, lb_, _ = run_varlen(longtail)
@@ -271,6 +285,48 @@ def test_zigzag_rank3_cp8():
     rows = np.unique(np.concatenate([[0, 1, 8191, 8192, 16383], r.integers(0, 2 * C, 60)]))
     ref_o, ref_l, _ = OA.zigzag_rank_attention(get_chunk, lengths, C, rank, cp, 32, 8, rows=rows)
     check(out[rows].cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "zigzag rank 3 (sampled)")
+
+
+def test_zigzag_rank3_cp8_ring_launch():
+    """Rank 3 of cp = 8 on the 131072-token pack, as the zigzag benchmark runs it: the live
+    steps' plans merged into one longest-first queue and run by one attention launch with
+    one queue per XCD, then the merges.  Same bits as the per-step launches, the merged
+    queue equal to the oracle's, every item run once, and the oracle's fold on sampled
+    rows."""
+    lengths = workloads.zigzag_pack_lengths(0)
+    C, cp, rank = 8192, 8, 3
+    cache = {}
+
+    def get_chunk(c):
+        if c not in cache:
+            cache[c] = workloads.zigzag_chunk_values(c)
+        return cache[c]
+
+    say("  zigzag rank 3 of cp=8: building the share")
+    share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    assert share.live_steps == [0, 1, 7]
+    out, lse = check_ring_against_steps(share, "zigzag rank 3 ring")
+    r = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 8191, 8192, 16383], r.integers(0, 2 * C, 60)]))
+    ref_o, ref_l, _ = OA.zigzag_rank_attention(get_chunk, lengths, C, rank, cp, 32, 8, rows=rows)
+    check(out[rows].cpu().numpy(), lse[:, rows].cpu().numpy(), ref_o, ref_l, "zigzag rank 3 ring (sampled)")
+
+
+@pytest.mark.timeout(900)
+def test_zigzag_rank3_cp8_ring_every_row(tmp_path):
+    """All 16384 rows x 32 heads of rank 3's share, through the ring launch the zigzag
+    benchmark times, against the oracle's fold of the 8 ring steps."""
+    import oracle_pool
+    lengths = workloads.zigzag_pack_lengths(0)
+    C, cp, rank = 8192, 8, 3
+    share = lb.zigzag.RankShare(lengths, C, rank, cp, workloads.zigzag_chunk_values)
+    out, lse = share.run_ring()
+    torch.cuda.synchronize()
+    st = oracle_pool.zigzag_every_row(out.cpu().numpy(), lse.cpu().numpy(), 0, rank, cp, C, str(tmp_path), say)
+    say(f"  zigzag rank 3 every row: out max {st['out_max']:.3e} mean {st['out_mean']:.3e}  "
+        f"lse max {st['lse_max']:.3e}")
+    assert st["finite"] and st["n"] == 2 * C * 32 * 128
+    assert st["out_max"] <= OUT_MAX and st["out_mean"] <= OUT_MEAN and st["lse_max"] <= LSE_MAX
 
 
 def test_zigzag_plans_made_up_front_equal_per_step_plans():
@@ -684,7 +740,7 @@ def test_sharded_shared_question_reassembles(rule):
 # --------------------------------------------------------------------------
 # one attention launch over every live ring step (ring workspace)
 # --------------------------------------------------------------------------
-def ring_share(cp=4, C=256, rank=2, seed=9, H=8, Hkv=2, d=128):
+def ring_share(cp=4, C=256, rank=2, seed=9, H=8, Hkv=2, d=128, with_inputs=False):
     T = 2 * cp * C
     lengths = workloads.lognormal_lengths(T, seed, T)
     r = np.random.default_rng(14 + seed)
@@ -694,7 +750,8 @@ def ring_share(cp=4, C=256, rank=2, seed=9, H=8, Hkv=2, d=128):
         sl = slice(c * C, (c + 1) * C)
         return q[sl], k[sl], v[sl]
 
-    return lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    share = lb.zigzag.RankShare(lengths, C, rank, cp, get_chunk)
+    return (share, (lengths, q, k, v)) if with_inputs else share
 
 
 def ring_oracle_plan(share):
@@ -732,15 +789,21 @@ def check_ring_against_steps(share, what):
 
 
 @pytest.mark.parametrize("rank", [0, 2, 3])
-@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64), (16, 2, 128)])
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (4, 4, 64), (8, 1, 64), (16, 2, 128), (32, 8, 128), (16, 8, 128),
+                                     (8, 8, 64)])
 def test_ring_launch_equals_the_step_launches(rank, H, Hkv, d):
     """A zigzag rank's live steps run from one merged queue in one launch: the same bits as
     one launch per step, the merged queue equal to the oracle's (every step's tiles, key
-    blocks descending, ties by step), every item run once; every head grouping and head
-    size the ring kernel is built for."""
-    share = ring_share(rank=rank, H=H, Hkv=Hkv, d=d)
+    blocks descending, ties by step), every item run once, and the merged result equal to
+    the unsharded oracle on every row of the rank; every head grouping and head size the
+    ring kernel is built for, with one queue (kv heads 1, 2, 4) and one per XCD (8)."""
+    cp, C = 4, 256
+    share, (lengths, q, k, v) = ring_share(cp=cp, C=C, rank=rank, H=H, Hkv=Hkv, d=d, with_inputs=True)
     say(f"  zigzag cp=4 rank {rank} H={H} Hkv={Hkv} d={d}: live steps {share.live_steps}")
-    check_ring_against_steps(share, f"rank {rank} H={H} Hkv={Hkv} d={d}")
+    out, lse = check_ring_against_steps(share, f"rank {rank} H={H} Hkv={Hkv} d={d}")
+    rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in lb.zigzag.chunks_of_rank(rank, cp)])
+    ref_o, ref_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv, rows=rows)
+    check(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"ring rank {rank} H={H}/{Hkv} d={d} vs oracle")
 
 
 def test_ring_graph_replays_equal_eager_runs():
@@ -762,12 +825,12 @@ def test_ring_graph_replays_equal_eager_runs():
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager run after replay {i}"
 
 
-@pytest.mark.parametrize("rule", ["per_document", "dispatch"])
-def test_ring_launch_on_sharded_ranks(rule):
+@pytest.mark.parametrize("rule,H,Hkv", [("per_document", 8, 2), ("dispatch", 8, 2), ("per_document", 32, 8)])
+def test_ring_launch_on_sharded_ranks(rule, H, Hkv):
     """Every rank of a cp = 4 sharding with a shared question (document 0): the ring launch
     gives the bits of the per-step launches and the ranks reassemble the unsharded oracle."""
     from load_balance_amd import sharding as LS
-    cp, H, Hkv, d = 4, 8, 2, 128
+    cp, d = 4, 128
     r = np.random.default_rng(65)
     lengths = [700, 300, 1, 128, 90, 333]
     lengths.append(2 * cp * 256 - sum(lengths))

@@ -63,13 +63,14 @@ def test_varlen_causal_as_slices_is_the_varlen_forward_bit_for_bit():
 
 
 @pytest.mark.parametrize("frame", [64, 200])
-def test_block_causal(frame):
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (32, 8)])
+def test_block_causal(frame, H, Hkv):
     lengths = [900, 1, 257, 333, 64]
-    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    T, d = sum(lengths), 128
     sl = SL.block_causal_slices(lengths, frame)
     (q, k, v), out, lse, ws = run(sl, T, T, H, Hkv, d, seed=frame)
     ref_o, ref_l = SL.slices_attention(q, k, v, sl, H, Hkv)
-    check(out, lse, ref_o, ref_l, f"block-causal frames of {frame}")
+    check(out, lse, ref_o, ref_l, f"block-causal frames of {frame} H={H}/{Hkv}")
     plan = lb.read_plan(ws)
     t = OP.tiles(SL.fragments(sl), lb.tile_rows(H, Hkv, d))
     ref = [t[i] for i in OP.lpt_order(t)]
@@ -126,16 +127,17 @@ def test_malformed_slice_lists_run_nothing(bad):
     assert torch.all(out == 3.0)
 
 
-@pytest.mark.parametrize("window", [1, 100, 4096])
-def test_sliding_window(window):
+@pytest.mark.parametrize("window,H,Hkv", [(1, 8, 2), (100, 8, 2), (4096, 8, 2), (100, 32, 8), (1024, 16, 8)])
+def test_sliding_window(window, H, Hkv):
     """The causal sliding window as slices (BI-CAUSAL bands) against the oracle; the plan,
-    spans with their lower bounds included, equals the oracle's bit for bit."""
+    spans with their lower bounds included, equals the oracle's bit for bit.  With 8 kv
+    heads the bounded kernel takes one queue per XCD."""
     lengths = [1500, 1, 700, 64]
-    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    T, d = sum(lengths), 128
     sl = SL.sliding_window_slices(lengths, window)
     (q, k, v), out, lse, ws = run(sl, T, T, H, Hkv, d, seed=window)
     ref_o, ref_l = SL.slices_attention(q, k, v, sl, H, Hkv)
-    check(out, lse, ref_o, ref_l, f"sliding window {window}")
+    check(out, lse, ref_o, ref_l, f"sliding window {window} H={H}/{Hkv}")
     plan = lb.read_plan(ws)
     t = OP.tiles(SL.fragments(sl), lb.tile_rows(H, Hkv, d))
     ref = [t[i] for i in OP.lpt_order(t)]
