@@ -157,6 +157,28 @@ lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * lb_varlen_attn_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same plan and the same
+ * kernels, with the plan kept in the library's own scratch array instead of a workspace.
+ *   q, k, v, cu_seqlens, n_seg, total_tokens, heads, kv_heads, d, mask_kind, out, lse:
+ *              as lb_varlen_attn_fwd (caller-owned device memory)
+ * The scratch array is LB_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the
+ * first call on that GPU until the process ends; the call allocates nothing (no hipMalloc,
+ * no hipFree).  A plan needing more than that (lb_workspace_bytes(total_tokens, n_seg,
+ * heads, kv_heads) > LB_NOALLOC_SCRATCH_BYTES) returns LB_EWORKSPACE before anything is
+ * enqueued; every other host-side error is that of lb_varlen_attn_fwd.  Every call on one
+ * GPU shares that GPU's array, so calls that overlap in time on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  The device error word
+ * (LB_DEVERR_*) lives in the array and cannot be read back: a malformed cu_seqlens makes
+ * the call compute nothing, as in lb_varlen_attn_fwd; callers that need the diagnosis use
+ * lb_varlen_attn_fwd with a workspace.
+ */
+#define LB_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+lb_status lb_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                     int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
+                                     int32_t d, int32_t mask_kind, void* out, float* lse, hipStream_t stream);
+
+/*
  * Block attention of one context-parallel step.
  *   q_shard    bf16 [n_q][heads][d]
  *   kv_chunk   bf16 [2][n_kv][kv_heads][d]: all of K, then all of V

@@ -26,6 +26,7 @@ MASK_SHARED_QUESTION = 1
 NO_SHARED_DOC = -1  # block path: no document shared by the others
 MAX_SPANS = 4
 MAX_PLAN_STEPS = 16
+NOALLOC_SCRATCH_BYTES = 8 << 20  # LB_NOALLOC_SCRATCH_BYTES
 
 DEVERR_CU_SEQLENS = 1
 DEVERR_CAPACITY = 2
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.lb_workspace_bytes.restype = SZ
     L.lb_varlen_attn_fwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_varlen_attn_fwd.restype = ctypes.c_int
+    L.lb_varlen_attn_fwd_noalloc.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, P]
+    L.lb_varlen_attn_fwd_noalloc.restype = ctypes.c_int
     L.lb_block_attn_fwd.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_block_attn_fwd.restype = ctypes.c_int
     L.lb_plan_varlen.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
@@ -238,6 +241,30 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, mask_kind=MASK_CAUSAL_DOC, out=None, ls
     _check(st, "lb_varlen_attn_fwd")
     if owned:
         _raise_device_error(workspace, "lb_varlen_attn_fwd", stream)
+    return out, lse
+
+
+def varlen_attn_fwd_noalloc(q, k, v, cu_seqlens, out, lse, mask_kind=MASK_CAUSAL_DOC, stream=None):
+    """varlen_attn_fwd with the plan in the library's per-GPU scratch array: no workspace, and
+    the library allocates nothing.  out [T,H,d] bf16 and lse [H,T] fp32 are the caller's.
+    Calls that overlap in time on one GPU race (they share the array)."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise LBError("q must be [T, H, d] and k, v [T, H_kv, d]")
+    T, H, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _dev(k, "k", torch.bfloat16, (T, Hkv, d), dev)
+    _dev(v, "v", torch.bfloat16, (T, Hkv, d), dev)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise LBError("cu_seqlens must be 1-D with at least two entries")
+    _dev(out, "out", torch.bfloat16, (T, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, T), dev)
+    _gpu(q, "q")
+    _check(lib().lb_varlen_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, H,
+                                            Hkv, d, int(mask_kind), _ptr(out), _ptr(lse),
+                                            ctypes.c_void_p(_stream(stream))), "lb_varlen_attn_fwd_noalloc")
     return out, lse
 
 

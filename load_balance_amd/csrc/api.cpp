@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "lbattn_internal.h"
@@ -448,6 +449,49 @@ lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
   if (st != LB_OK) return st;
   return launch_run(q, k, v, total_tokens, total_tokens, heads, kv_heads, d, false, out, lse, workspace,
                     workspace_bytes, stream);
+}
+
+// The plan workspace of lb_varlen_attn_fwd_noalloc.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address (one per GPU, each GPU holding its own
+// copy) is looked up once per device and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[LB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's scratch address; looked up on the first call made on that device.
+lb_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LB_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return LB_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LB_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LB_OK;
+}
+}  // namespace
+
+lb_status lb_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                     int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
+                                     int32_t d, int32_t mask_kind, void* out, float* lse, hipStream_t stream) {
+  if (n_seg < 1 || total_tokens < 0) return LB_EINVAL;
+  lb_status st = check_heads(heads, kv_heads, d);
+  if (st != LB_OK) return st;
+  // the plan this call needs, against the array's fixed size, before touching the device
+  const int bm = tile_rows_for_group(heads / kv_heads);
+  const int64_t tiles = ceil_div(total_tokens, bm) + n_seg;
+  if (tiles > kSortCap) return LB_EUNSUPPORTED;
+  if (ws_layout(n_seg, tiles).total > (int64_t)LB_NOALLOC_SCRATCH_BYTES) return LB_EWORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != LB_OK) return st;
+  return lb_varlen_attn_fwd(q, k, v, cu_seqlens, n_seg, total_tokens, heads, kv_heads, d, mask_kind, out, lse, ws,
+                            LB_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chunk, int32_t n_kv,

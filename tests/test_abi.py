@@ -98,6 +98,19 @@ def test_varlen_host_checks(L):
     assert varlen(L, T=0, ws_bytes=need) == LB_OK                        # nothing to do, nothing enqueued
 
 
+def test_noalloc_host_checks(L):
+    """The allocation-free forward's host checks: nothing reaches the device (there is none)."""
+    def call(n_seg=3, T=64, H=2, Hkv=2, d=64):
+        return L.lb_varlen_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, n_seg, T, H, Hkv, d, 0, FAKE, FAKE, None)
+    assert call(n_seg=0) == LB_EINVAL
+    assert call(T=-1) == LB_EINVAL
+    assert call(H=3, Hkv=2) == LB_EINVAL
+    assert call(d=96) == LB_EUNSUPPORTED
+    assert call(T=1 << 22, n_seg=1, H=32, Hkv=8, d=128) == LB_EUNSUPPORTED  # > sort capacity
+    # every plan within the sort capacity fits the scratch array
+    assert L.lb_workspace_bytes(16384 * 64, 16384, 32, 8) <= lb.NOALLOC_SCRATCH_BYTES
+
+
 def test_block_host_checks(L):
     def call(**kw):
         a = dict(q=FAKE, n_q=128, kv=FAKE, n_kv=128, qp=FAKE, kp=FAKE, qd=FAKE, kd=FAKE, H=32, Hkv=8, d=128,
