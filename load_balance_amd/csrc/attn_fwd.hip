@@ -191,7 +191,15 @@ struct KvBlock {
 template <int D, bool OUT_F32, bool LOWER, bool RING>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps r) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
-  __shared__ int s_item;
+  // s_item[p]: the item after the one whose descriptor is in s_tile[p] (written by thread 0
+  // when that item starts, read by every wave in its epilogue).  Two entries, so that thread
+  // 0 can write the next one while a slower wave still reads the last one, and the epilogue
+  // needs no closing barrier.
+  __shared__ int s_item[2];
+  // The descriptors of the item being run and of the next one, copied from the plan by wave 0
+  // with direct global-to-LDS loads while the previous item runs, so that no wave waits on a
+  // global round trip for a descriptor between items.
+  __shared__ __attribute__((aligned(16))) lb_plan_tile s_tile[2];
   // Thread 0's bookkeeping (queue state, counts for the worker record) lives in LDS, so that
   // it holds no register through the key loop.
   __shared__ struct {
@@ -236,14 +244,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       if (s < r.n_steps && hdr->ring_n_kv[s] != r.n_kv[s]) mismatch = true;
   }
   const int n_items = mismatch ? 0 : hdr->n_items;
+  // plans and rings both store their tiles in queue order: tile i of the queue is tiles[i]
   const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + (mismatch ? 0 : hdr->off_tiles));
-  const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + (mismatch ? 0 : hdr->off_order));
   if (mismatch && blockIdx.x == 0 && tid == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
-  // the tile at queue position i: through the plan's order, or (ring) stored in queue order
-  auto tile_at = [&](int64_t i) -> const lb_plan_tile* {
-    if constexpr (RING) return &tiles[i];
-    else return &tiles[order[i]];
-  };
+  auto tile_at = [&](int64_t i) -> const lb_plan_tile* { return &tiles[i]; };
   // a ring tile's step, kept inside the launch's step table
   auto step_of = [&](const lb_plan_tile* T) -> int {
     return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
@@ -326,21 +330,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
   auto start_pop = [&]() -> int { return s_pop.dry ? -1 : atomicAdd(&hdr->queue_head[s_pop.queue], 1); };
   if (tid == 0) {
     const int k = start_pop();
-    s_item = k < 0 ? -1 : finish_pop(k);
+    s_item[1] = k < 0 ? -1 : finish_pop(k);  // as if an item in slot 1 had run before
   }
   lds_barrier();
-  int qitem = __builtin_amdgcn_readfirstlane(s_item);
-  lds_barrier();  // every wave has read s_item before thread 0 writes it again
+  int qitem = __builtin_amdgcn_readfirstlane(s_item[1]);
 
   // The loads an item starts with, issued during the previous item's epilogue so that their
   // latency hides behind it: this wave's Q fragment (B operand of S^T = K Q^T; lane holds
   // Q[q = l32][d = kk*16 + hh*8 .. +8], zeros past the tile's end) and the first key block
   // into the loader's registers.
   bf16x8 qreg[D / 16];
-  auto issue_item_loads = [&](int item) {
+  auto issue_item_loads = [&](int item, const lb_plan_tile* T) {
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
     const int g = q_of + n_queues * (k_in % heads_per_queue);
-    const lb_plan_tile* T = tile_at(k_in / heads_per_queue);
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
@@ -371,12 +373,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
     if (n_spans > 0) ld.load(Kx, Vx, k_start0, k_len0, row_bytes, g, tid);
   };
+  // Wave 0 copies an item's 96-byte descriptor into an LDS slot (lanes 0-5, 16 bytes each);
+  // the copy lands asynchronously and is waited for before the barrier that precedes its use.
+  auto fetch_tile = [&](int item, lb_plan_tile* slot) {
+    // through a buffer over the queue's tiles: the tile's offset in a scalar register, each
+    // lane's 16-byte piece in a 32-bit vector offset (no 64-bit address per lane)
+    const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
+    const int t_off = __builtin_amdgcn_readfirstlane((k_in / heads_per_queue) * (int)sizeof(lb_plan_tile));
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)tiles, (short)0, (int)(n_tiles_hdr * (int64_t)sizeof(lb_plan_tile)), kBufferFlags);
+    if (wave == 0 && lane < (int)(sizeof(lb_plan_tile) / 16))
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)slot, 16, lane * 16,
+                                               t_off, 0, 0);
+  };
+  auto wait_tile = [&]() {
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the descriptor copy has landed
+  };
+  int slot = 0;  // s_tile[slot] holds the descriptor of the item being run
   // Items are popped one ahead of the one whose loads go out: thread 0 issues the atomic in
   // an item's epilogue and completes the pop at the next item's start, so the round trip
-  // sits on no wave's path.  s_item then holds the item after the one being run.
+  // sits on no wave's path.  s_item[slot] then holds the item after the one being run.
   int k_after = -1;  // thread 0: that atomic's result, or -1 with the queues dry
   if (qitem >= 0) {
-    issue_item_loads(qitem);
+    fetch_tile(qitem, &s_tile[0]);
+    wait_tile();
+    lds_barrier();
+    issue_item_loads(qitem, &s_tile[0]);
     if (tid == 0) k_after = start_pop();
   }
 
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     // item k of queue q: tile order[k / heads_per_queue], kv head q + n_queues * (k % heads_per_queue)
     const int q_of = qitem / max(per_queue, 1), k_in = qitem - q_of * per_queue;
     const int g = q_of + n_queues * (k_in % heads_per_queue);
-    const lb_plan_tile* T = tile_at(k_in / heads_per_queue);
+    const lb_plan_tile* T = &s_tile[slot];  // this item's descriptor, in LDS
     const char* Kit = Kb;
     const char* Vit = Vb;
     int step = 0;
@@ -409,7 +431,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     if (tid == 0) {
       ++s_pop.items;
       s_pop.pairs += T->cost * G + (static_cast<int64_t>(n_kv_tiles) << kPairBits);
-      s_item = k_after < 0 ? -1 : finish_pop(k_after);
+      s_item[slot] = k_after < 0 ? -1 : finish_pop(k_after);
+    }
+    // the next item's descriptor goes to the other slot while this item runs (thread 0 has
+    // just popped it; lane 0 of wave 0 is thread 0)
+    if (wave == 0) {
+      const int nxt_item = __builtin_amdgcn_readfirstlane(s_item[slot]);
+      if (nxt_item >= 0) fetch_tile(nxt_item, &s_tile[slot ^ 1]);
     }
     auto span_of = [&](int s) {
       KvBlock b;
@@ -596,12 +624,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
 
     // ---- epilogue: out = O / l, lse = ln(sum exp) ----
-    // Every wave is done with the LDS ring after this barrier, and the next item's number is
-    // in s_item: its loads go out first, then thread 0's atomic for the item after it.
+    // Every wave is done with the LDS ring after this barrier, the next item's number is in
+    // s_item and its descriptor in the other slot: its loads go out first, then thread 0's
+    // atomic for the item after it.
+    wait_tile();
     lds_barrier();
-    const int next_item = __builtin_amdgcn_readfirstlane(s_item);
+    const int next_item = __builtin_amdgcn_readfirstlane(s_item[slot]);
     if (next_item >= 0) {
-      issue_item_loads(next_item);
+      issue_item_loads(next_item, &s_tile[slot ^ 1]);
       if (tid == 0) k_after = start_pop();
     }
     const float l_tot = l_part + partner_lane(l_part, lane);
@@ -664,8 +694,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
         if (wmask >> (r_lo + row0 + j * kRowsPerStep) & 1) *reinterpret_cast<u32x4*>(dst + j * dst_step) = x;
       }
     }
-    lds_barrier();  // every wave has read s_item before thread 0 writes it again
+    // No barrier here: the next item's prologue writes only stage 0 of the ring (kept out of
+    // the staging), s_item[slot ^ 1] and s_tile[slot] (read by no wave after the epilogue's
+    // first barrier); the key loop's first barrier then orders the staging reads above
+    // before the loader writes stages 1 and 2.
     qitem = next_item;
+    slot ^= 1;
   }
 
   if (tid == 0) {

@@ -79,8 +79,12 @@ static_assert(offsetof(lb_plan_tile, k_lo) == offsetof(lb_plan_tile, k_start) + 
               "span fields are contiguous: k_start, k_len, k_pos0, k_lo");
 static_assert(sizeof(lb_worker_record) == 40, "lb_worker_record layout");
 
+// Plan workspace regions.  `tiles` holds the tiles in queue order (longest first), so the
+// kernels that run a plan read tile i of the queue without an indirection; `order` is the
+// identity, kept for readers written against a separate order; `ntiles` is the planner's
+// own natural-order copy, from which the queue order is gathered.
 struct WsLayout {
-  int64_t off_frags, off_ftile, off_kvruns, off_tiles, off_order, off_workers, total;
+  int64_t off_frags, off_ftile, off_kvruns, off_tiles, off_order, off_ntiles, off_workers, total;
   int32_t cap_frags, cap_tiles;
 };
 
@@ -95,6 +99,7 @@ inline WsLayout ws_layout(int64_t cap_frags, int64_t cap_tiles) {
   L.off_kvruns = o;  o = align256(o + cap_frags * (int64_t)sizeof(KvRun));
   L.off_tiles = o;   o = align256(o + cap_tiles * (int64_t)sizeof(lb_plan_tile));
   L.off_order = o;   o = align256(o + cap_tiles * (int64_t)sizeof(int32_t));
+  L.off_ntiles = o;  o = align256(o + cap_tiles * (int64_t)sizeof(lb_plan_tile));
   L.total = o;
   L.cap_frags = (int32_t)cap_frags;
   L.cap_tiles = (int32_t)cap_tiles;

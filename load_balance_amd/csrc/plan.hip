@@ -225,6 +225,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   Frag* frags = reinterpret_cast<Frag*>(ws + a.L.off_frags);
   KvRun* kvr = reinterpret_cast<KvRun*>(ws + a.L.off_kvruns);
   lb_plan_tile* tiles = reinterpret_cast<lb_plan_tile*>(ws + a.L.off_tiles);
+  lb_plan_tile* ntiles = reinterpret_cast<lb_plan_tile*>(ws + a.L.off_ntiles);
   int32_t* order = reinterpret_cast<int32_t*>(ws + a.L.off_order);
   KvRun* lds_runs = reinterpret_cast<KvRun*>(&sh.keys[0]);
   Frag* lds_frags = reinterpret_cast<Frag*>(&sh.keys[kSortCap / 4]);
@@ -488,7 +489,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       T.n_spans = ns;
       T.cost = cost;
       T.blocks = blocks;
-      tiles[t] = T;
+      ntiles[t] = T;
       if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
       my_keys[k] = ((kKeyMask - (uint64_t)blocks) << 24) | (uint64_t)t;
@@ -532,6 +533,14 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
     for (int k = 128; k <= n_pad; k <<= 1) bitonic_phase(sh, n_pad, k, k >> 1);
     for (int i = tid; i < n_tiles; i += NT) order[i] = (int32_t)(sh.keys[i] & 0xFFFFFF);
+  }
+  __syncthreads();
+  // ---- 4. the tiles in queue order; the order becomes the identity ----------------
+  if (sh.err == 0) {
+    for (int i = tid; i < n_tiles; i += NT) {
+      tiles[i] = ntiles[order[i]];
+      order[i] = i;
+    }
   }
   __syncthreads();
 
