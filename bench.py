@@ -33,6 +33,8 @@ METRIC = "effective masked-attn TFLOP/s (Σℓ² FLOPs) & % bf16 MFMA peak, 32K 
 PEAK_BF16_TFLOPS = 2500.0           # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 PEAK_BF16_AT_2400MHZ = 256 * 2.4e9 * 4096 / 1e12   # 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU = 2516.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longtail32k_traffic.json")
+TRAFFIC_SOURCE = ("profiles/attn_fwd_longtail32k_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes of this "
+                  "kernel source, copy-calibrated; read from that file, not measured in this run")
 KERNEL_SOURCE = os.path.join(ROOT, "load_balance_amd", "csrc", "attn_fwd.hip")
 
 
@@ -503,35 +505,75 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
 # ----------------------------------------------------------------------------------------
 # CPU baseline: the oracle, on a bounded sample of the same workload
 # ----------------------------------------------------------------------------------------
-def cpu_baseline(w, seconds, seed=0):
-    from oracle import attention as OA
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_info():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+        return ", ".join(f"{x.get('internal_api')} {x.get('version')}" for x in threadpool_info()
+                         if x.get("user_api") == "blas") or None
     except Exception:  # pragma: no cover
-        cores = 1
+        return None
+
+
+def cpu_baseline(w, seconds, seed=0):
+    """The float64 oracle on the host cores, on a bounded sample of the same pack: random
+    blocks of up to 32 rows of one document (all heads) handed to a pool of processes, one per
+    core with one BLAS thread each, until `seconds` have elapsed; blocks still running then
+    are not counted."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import tempfile
+    from oracle import timing as OT
     p = w.packs[0]
     lengths = np.asarray(p["lengths"])
     cu = np.concatenate([[0], np.cumsum(lengths)])
     seg = np.repeat(np.arange(len(lengths)), lengths)
     pos_in_doc = np.arange(p["tokens"]) - cu[seg]
-    blocks = np.random.default_rng(seed).permutation(p["tokens"] // 256)
-    done_rows = []
-    t0 = time.perf_counter()
-    for b in blocks:
-        rows = np.arange(b * 256, (b + 1) * 256)
-        OA.varlen_attention(p["q"], p["k"], p["v"], p["cu_seqlens"], p["heads"], p["kv_heads"], rows=rows)
-        done_rows.append(rows)
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    rows = np.concatenate(done_rows)
-    pairs = int(np.sum(pos_in_doc[rows] + 1))
+    cores = len(os.sched_getaffinity(0))
+    n_proc = max(1, min(cores, 16))  # a GPU box shares its host: at most 16 processes per GPU
+    rb = 32  # rows per task, inside one document
+    tasks = [(int(cu[d]), int(lengths[d]), r0, min(r0 + rb, int(lengths[d])))
+             for d in range(len(lengths)) for r0 in range(0, int(lengths[d]), rb)]
+    order = np.random.default_rng(seed).permutation(len(tasks))
+    done = []
+    with tempfile.TemporaryDirectory(dir="/tmp") as tmp:
+        paths = {}
+        for k in ("q", "k", "v"):
+            paths[k] = os.path.join(tmp, k + ".npy")
+            np.save(paths[k], p[k])
+        meta = dict(cu_seqlens=np.asarray(p["cu_seqlens"]), heads=p["heads"], kv_heads=p["kv_heads"])
+        # a worker that fails to start breaks the pool (an error here) rather than being respawned
+        with cf.ProcessPoolExecutor(n_proc, mp_context=mp.get_context("spawn"), initializer=OT.init_worker,
+                                    initargs=(paths, meta)) as ex:
+            list(ex.map(OT.ready, range(n_proc)))  # workers up before the clock starts
+            t0 = time.perf_counter()
+            futs = [ex.submit(OT.run_block, *tasks[i]) for i in order]
+            for f in cf.as_completed(futs):
+                if time.perf_counter() - t0 >= seconds:
+                    break
+                done.append(f.result())
+            el = time.perf_counter() - t0
+            for f in futs:
+                f.cancel()
+    rows = np.concatenate([np.arange(a, a + n) for a, n in done]) if done else np.zeros(0, int)
+    pairs = int(np.sum(pos_in_doc[rows] + 1)) if len(rows) else 0
     flops = 4 * p["d"] * p["heads"] * pairs
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(rows)} of {p['tokens']} query rows (random 256-row blocks, all {p['heads']} heads), "
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(n_proc), "kind": "oracle",
+            "host_cpus": cores, "cpu_model": _cpu_model(), "numpy": np.__version__, "blas": _blas_info(),
+            "sample": f"{len(rows)} of {p['tokens']} query rows (random blocks of up to {rb} rows of one document, "
+                      f"all {p['heads']} heads), "
                       f"{pairs} visible pairs per head = {pairs / causal_pairs(lengths):.1%} of the pack, "
-                      f"float64 numpy, {el:.1f} s"}
+                      f"float64 numpy, {n_proc} processes x 1 BLAS thread, {el:.1f} s"}
 
 
 def traffic_entry():
@@ -546,6 +588,25 @@ def traffic_entry():
         return t.get("hbm_bytes_per_launch")
     except Exception:
         return None
+
+
+def cu_balance(recs):
+    """Busy time per compute unit from the workgroups' records.  A workgroup's compute unit
+    is (XCC_ID, SE_ID, SH_ID, CU_ID) from its HW_ID and XCC_ID registers (gfx9 HW_ID fields:
+    CU_ID bits 8-11, SH_ID bit 12, SE_ID bits 13-15); workgroups that shared one compute
+    unit add up."""
+    per_cu = {}
+    for r in recs:
+        hw = int(r["hw_id"])
+        key = (int(r["xcc_id"]) & 0xF, (hw >> 13) & 0x7, (hw >> 12) & 0x1, (hw >> 8) & 0xF)
+        per_cu.setdefault(key, []).append(float(r["t_end"] - r["t_start"]))
+    if not per_cu:
+        return {"max_over_mean": None}
+    busy = np.array([sum(v) for v in per_cu.values()])
+    return {"max_over_mean": round(float(busy.max() / busy.mean()), 4) if busy.mean() > 0 else None,
+            "compute_units": len(per_cu), "workgroups": len(recs),
+            "max_workgroups_on_one_cu": max(len(v) for v in per_cu.values()),
+            "unit": "per compute unit, from s_memrealtime stamps"}
 
 
 def cp_job_fields(w, per_launch):
@@ -658,7 +719,7 @@ def main():
         dump_worker_records(args.worker_records, args.workload, w, recs, lb)
     busy = np.array([r["t_end"] - r["t_start"] for r in recs], dtype=np.float64)
     span_ticks = max(r["t_end"] for r in recs) - min(r["t_start"] for r in recs)
-    cu_ratio = float(busy.max() / busy.mean()) if len(busy) and busy.mean() > 0 else None
+    cu = cu_balance(recs)
 
     value = w.flops / (ms_per_step / 1e3) / 1e12
     achieved = w.flops / (attn_ms / 1e3) / 1e12
@@ -682,7 +743,8 @@ def main():
         "kernels_ms_per_launch": per_launch if n_launch > 1 else None,
         "eager_ms_per_step": None if eager_ms_per_step is None else round(eager_ms_per_step, 4),
         **cp_job_fields(w, per_launch),
-        "cu_busy_max_over_mean": None if cu_ratio is None else round(cu_ratio, 4),
+        "cu_busy_max_over_mean": cu["max_over_mean"],
+        "cu_busy": cu,
         "attention_span_device_clock_ms": round(span_ticks / 1e5, 4),
         "roofline": {
             "bound": "mfma",
@@ -691,6 +753,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_entry() if args.workload == "longtail" else None,
+            "traffic_source": (TRAFFIC_SOURCE if args.workload == "longtail" and traffic_entry() is not None
+                               else None),
             "kernel": getattr(w, "kernel_name", "attn_kernel<128,false,false,false> (persistent, LPT queue)"),
             "launch_ms": round(attn_ms_per_launch, 4),
         },

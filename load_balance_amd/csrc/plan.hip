@@ -498,7 +498,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   }
   __syncthreads();  // the staging areas are dead from here on; the sort buffer takes over
 
-  // ---- 3. longest-first order of the unique keys ---------------------------------
+  // ---- 3. longest-first order of the unique keys; tiles copied to their queue positions --
   // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys
   // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS and
   // one barrier, against the bitonic network's 55 barrier-separated passes at 1024 keys.
@@ -517,7 +517,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       int rank = 0;
 #pragma unroll 8
       for (int i = 0; i < n_tiles; ++i) rank += sh.keys[i] < key ? 1 : 0;
-      order[rank] = t;
+      tiles[rank] = ntiles[t];  // this thread's own tile, written by it in phase 2
+      order[rank] = rank;
     }
   } else if (sh.err == 0 && n_tiles > 0) {
     // bitonic sort of the keys in LDS
@@ -532,13 +533,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     // phases k = 2 .. min(n_pad, 64) pair lanes of one wave only: all in registers at once
     bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
     for (int k = 128; k <= n_pad; k <<= 1) bitonic_phase(sh, n_pad, k, k >> 1);
-    for (int i = tid; i < n_tiles; i += NT) order[i] = (int32_t)(sh.keys[i] & 0xFFFFFF);
-  }
-  __syncthreads();
-  // ---- 4. the tiles in queue order; the order becomes the identity ----------------
-  if (sh.err == 0) {
     for (int i = tid; i < n_tiles; i += NT) {
-      tiles[i] = ntiles[order[i]];
+      tiles[i] = ntiles[sh.keys[i] & 0xFFFFFF];
       order[i] = i;
     }
   }
