@@ -164,7 +164,7 @@ class SlicesStep:
         self.sl = torch.tensor([list(x) for x in slices], dtype=torch.int32, device="cuda")
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
-        self.ws = lb.new_workspace(T, len(slices), H, Hkv)
+        self.ws = lb.new_workspace(T, 2 * len(slices) + 1, H, Hkv)
         # visible pairs, rectangle by rectangle: row r sees keys lo .. hi of its slice (CAUSAL
         # and BI-CAUSAL bound hi at r + kl - ql, INV-CAUSAL and BI-CAUSAL bound lo at r)
         pairs = 0

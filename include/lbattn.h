@@ -432,8 +432,9 @@ typedef struct {
 enum { LB_SLICE_FULL = 0, LB_SLICE_CAUSAL = 1, LB_SLICE_INV_CAUSAL = 2, LB_SLICE_BI_CAUSAL = 3 };
 
 /* The plan of a slice list: slices is a DEVICE array of n_slices entries; queries
-   [0, n_q), keys [0, n_kv).  Workspace: lb_workspace_bytes(n_q, n_slices, heads, kv_heads)
-   bytes.  Run it with lb_attn_run (k, v of n_kv rows; out bf16 or fp32) when every slice is
+   [0, n_q), keys [0, n_kv).  Workspace: lb_workspace_bytes(n_q, 2 * n_slices + 1, heads,
+   kv_heads) bytes (a fragment per query range and one per run of rows no slice covers: those
+   rows get lse = -inf from the run and their out is not written).  Run it with lb_attn_run (k, v of n_kv rows; out bf16 or fp32) when every slice is
    FULL or CAUSAL, with lb_attn_run_lower when some are INV-CAUSAL or BI-CAUSAL (lb_attn_run
    refuses such a plan: LB_DEVERR_PLAN). */
 lb_status lb_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,

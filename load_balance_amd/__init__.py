@@ -701,7 +701,7 @@ def plan_slices(slices, n_q, n_kv, heads, kv_heads, d, workspace=None, stream=No
     sl = _slice_tensor(slices, "cuda" if workspace is None else workspace.device)
     _dev(sl, "slices", torch.int32)
     if workspace is None:
-        workspace = new_workspace(n_q, max(1, sl.shape[0]), heads, kv_heads, sl.device)
+        workspace = new_workspace(n_q, 2 * sl.shape[0] + 1, heads, kv_heads, sl.device)
     _ws(workspace, device=sl.device)
     _gpu(sl, "sl")
     _check(lib().lb_plan_slices(_ptr(sl), sl.shape[0], n_q, n_kv, heads, kv_heads, d, _ptr(workspace),
@@ -729,7 +729,7 @@ def slices_attn_fwd(q, k, v, slices, out=None, lse=None, workspace=None, stream=
     _dev(lse, "lse", torch.float32, (H, n_q), dev)
     owned = workspace is None
     if owned:
-        workspace = new_workspace(n_q, max(1, sl.shape[0]), H, Hkv, dev)
+        workspace = new_workspace(n_q, 2 * sl.shape[0] + 1, H, Hkv, dev)
     _ws(workspace, device=dev)
     _gpu(q, "q")
     _check(lib().lb_slices_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sl), sl.shape[0], n_q, n_kv, H, Hkv, d, _ptr(out),

@@ -240,9 +240,11 @@ lb_status prepare_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int
   if (st != LB_OK) return st;
   if (!aligned(slices, 4)) return LB_EINVAL;
   if (!aligned(workspace, 256)) return LB_EWORKSPACE;
-  const int64_t tiles = ceil_div(n_q, tile_rows_for_group(heads / kv_heads)) + n_slices;
+  // fragments: one per query range, and one per run of rows no slice covers
+  const int64_t frags = 2 * (int64_t)n_slices + 1;
+  const int64_t tiles = ceil_div(n_q, tile_rows_for_group(heads / kv_heads)) + frags;
   if (tiles > kSortCap) return LB_EUNSUPPORTED;
-  *L = ws_layout(n_slices, tiles);
+  *L = ws_layout(frags, tiles);
   if ((int64_t)workspace_bytes < L->total) return LB_EWORKSPACE;
   return LB_OK;
 }
@@ -546,8 +548,8 @@ lb_status lb_slices_attn_fwd(const void* q, const void* k, const void* v, const 
   st = prepare_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, d, workspace, workspace_bytes, &L);
   if (st != LB_OK) return st;
   if (n_q == 0) return LB_OK;
-  // rows no slice covers keep lse = -inf
-  if (launch_fill_f32(lse, (int64_t)heads * n_q, -INFINITY, stream) != hipSuccess) return LB_EHIP;
+  // rows no slice covers are the plan's tiles without a key span: the attention launch sets
+  // their lse to -inf
   st = launch_plan_slices(slices, n_slices, n_q, n_kv, heads, kv_heads, workspace, L, stream);
   if (st != LB_OK) return st;
   return launch_run(q, k, v, n_q, n_kv, heads, kv_heads, d, false, out, lse, workspace, workspace_bytes, stream,

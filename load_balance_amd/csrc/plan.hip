@@ -289,12 +289,15 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       }
     }
   } else if (a.mode == kPlanSlices) {
-    // one fragment per query range: slice s opens one when its range differs from s - 1's
+    // one fragment per query range: slice s opens one when its range differs from s - 1's.
+    // Rows no slice covers (before a range, between two, after the last) make a fragment
+    // with no key span, so that their lse is -inf like any row that sees no key.
     const lb_mask_slice* sl = a.slices;
     int running = 0;
     for (int base = 0; base < a.n_slices; base += NT) {
       const int s = base + tid;
-      bool opens = false;
+      bool opens = false, gap = false;
+      int gap_start = 0;
       if (s < a.n_slices) {
         const lb_mask_slice x = sl[s];
         bool bad = x.q_len < 1 || x.k_len < 1 || x.q_start < 0 || x.k_start < 0 || x.q_start > a.n_q - x.q_len ||
@@ -303,10 +306,21 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
         if (s > 0 && opens && sl[s - 1].q_start + sl[s - 1].q_len > x.q_start) bad = true;  // unsorted or overlapping
         if (!opens && sl[s - 1].k_start + sl[s - 1].k_len > x.k_start) bad = true;  // key ranges must ascend, disjoint
         if (bad) atomicOr(&sh.err, LB_DEVERR_SLICES);
+        gap_start = s == 0 ? 0 : sl[s - 1].q_start + sl[s - 1].q_len;
+        gap = opens && !bad && x.q_start > gap_start;
       }
       int total;
-      const int off = block_excl_scan(opens ? 1 : 0, sh, &total);
-      if (opens && running + off < a.L.cap_frags) {
+      const int off = block_excl_scan((opens ? 1 : 0) + (gap ? 1 : 0), sh, &total);
+      if (gap && running + off < a.L.cap_frags) {
+        Frag g{};
+#pragma unroll
+        for (int o = 0; o < LB_MAX_SPANS; ++o) g.k_lo[o] = LB_NO_LOWER_BOUND;
+        g.q_start = gap_start;
+        g.q_len = sl[s].q_start - gap_start;
+        frags[running + off] = g;
+        if (running + off < kLdsFrags) lds_frags[running + off] = g;
+      }
+      if (opens && running + off + (gap ? 1 : 0) < a.L.cap_frags) {
         // the fragment's spans: this slice and the following ones on the same range
         const lb_mask_slice x = sl[s];
         Frag f{};
@@ -333,10 +347,25 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
           ++ns;
         }
         f.n_spans = ns;
-        frags[running + off] = f;
-        if (running + off < kLdsFrags) lds_frags[running + off] = f;
+        const int at = running + off + (gap ? 1 : 0);
+        frags[at] = f;
+        if (at < kLdsFrags) lds_frags[at] = f;
       }
       running += total;
+    }
+    // the rows after the last range
+    const int end = a.n_slices > 0 ? sl[a.n_slices - 1].q_start + sl[a.n_slices - 1].q_len : 0;
+    if (end < a.n_q) {
+      if (tid == 0 && running < a.L.cap_frags) {
+        Frag g{};
+#pragma unroll
+        for (int o = 0; o < LB_MAX_SPANS; ++o) g.k_lo[o] = LB_NO_LOWER_BOUND;
+        g.q_start = end;
+        g.q_len = a.n_q - end;
+        frags[running] = g;
+        if (running < kLdsFrags) lds_frags[running] = g;
+      }
+      ++running;
     }
     n_frags = running;
     if (n_frags > a.L.cap_frags && tid == 0) sh.err |= LB_DEVERR_CAPACITY;

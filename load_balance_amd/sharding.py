@@ -229,6 +229,75 @@ def max_spans(lengths, tokens, shared_doc: int = -1) -> int:
     return worst
 
 
+def step_span_count(q_pos, q_doc, kv_pos, kv_doc, shared_doc: int = -1) -> int:
+    """The most key spans one query run of this step meets: the block planner's limit is
+    MAX_SPANS (the shared document's adjacent runs counted as one FULL span)."""
+    qr, kr = _runs(np.asarray(q_pos), np.asarray(q_doc)), _runs(np.asarray(kv_pos), np.asarray(kv_doc))
+    n_shared = len(_full_spans(kr, shared_doc))
+    worst = 0
+    for (_, ln, p0, d) in qr:
+        n = int(np.count_nonzero((kr[:, 3] == d) & (kr[:, 2] <= p0 + ln - 1)))
+        worst = max(worst, n + (n_shared if shared_doc >= 0 and int(d) != shared_doc else 0))
+    return worst
+
+
+def _segments(doc, what):
+    """(doc, start, length) of each maximal range of equal document id; a document must
+    occupy one range (its tokens contiguous, as every sharding rule here leaves them)."""
+    doc = np.asarray(doc)
+    if len(doc) == 0:
+        return []
+    starts = np.r_[0, np.flatnonzero(np.diff(doc) != 0) + 1]
+    ends = np.r_[starts[1:], len(doc)]
+    seg = [(int(doc[a]), int(a), int(b - a)) for a, b in zip(starts, ends)]
+    if len({d for d, _, _ in seg}) != len(seg):
+        raise ValueError(f"{what}: a document's tokens are not contiguous")
+    return seg
+
+
+def step_slices(q_pos, q_doc, kv_pos, kv_doc, shared_doc: int = -1):
+    """The block mask of one ring step as a slice list over local indices: key j visible to
+    query i iff q_doc[i] == kv_doc[j] and kv_pos[j] <= q_pos[i], or kv_doc[j] == shared_doc !=
+    q_doc[i].  Within each side a document's tokens are contiguous with ascending positions,
+    so a row sees a prefix of its document's keys, c_i of them; rows where c grows by one per
+    row are one CAUSAL rectangle (bottom-right aligned), rows of equal c one FULL rectangle,
+    and each also gets a FULL rectangle over the shared document's keys.  Rows that see no
+    key are left out (the plan gives them lse = -inf).  This is how a step whose query runs
+    meet more than MAX_SPANS key runs (striped sharding: stripes of w tokens make a run per
+    stripe) runs on the slice-list planner.  Returns (q_start, q_len, k_start, k_len, kind)."""
+    from . import SLICE_CAUSAL, SLICE_FULL
+    q_pos, kv_pos = np.asarray(q_pos, np.int64), np.asarray(kv_pos, np.int64)
+    qs, ks = _segments(q_doc, "query shard"), _segments(kv_doc, "key/value shard")
+    for side, pos in ((qs, q_pos), (ks, kv_pos)):
+        for _, a, n in side:
+            if n > 1 and np.any(np.diff(pos[a:a + n]) <= 0):
+                raise ValueError("positions must ascend within a document")
+    kv_of = {d: (a, n) for d, a, n in ks}
+    shared = kv_of.get(shared_doc) if shared_doc >= 0 else None
+    out = []
+    for d, a, n in qs:
+        own = kv_of.get(d)
+        c = np.searchsorted(kv_pos[own[0]:own[0] + own[1]], q_pos[a:a + n], side="right") if own else np.zeros(n, int)
+        sh = shared if shared is not None and d != shared_doc else None
+        i = 0
+        while i < n:
+            j = i + 1
+            step = int(c[j] - c[j - 1]) if j < n else None
+            if step in (0, 1):
+                while j < n and c[j] - c[j - 1] == step:
+                    j += 1
+            causal = step == 1 and j - i > 1
+            k_len = int(c[j - 1]) if causal else int(c[i])
+            rows = []
+            if own is not None and k_len >= 1:
+                rows.append((a + i, j - i, own[0], k_len, SLICE_CAUSAL if causal else SLICE_FULL))
+            if sh is not None:
+                rows.append((a + i, j - i, sh[0], sh[1], SLICE_FULL))
+            out.extend(sorted(rows, key=lambda x: x[2]))
+            i = j
+    return out
+
+
 def predicted_blocks(q_pos, q_doc, kv_pos, kv_doc, tile_rows: int) -> int:
     return predicted_work(q_pos, q_doc, kv_pos, kv_doc, tile_rows)[0]
 
@@ -358,9 +427,17 @@ class ShardedRank:
                    [len(_runs(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy())) for s in self.steps])
         self._ws_shape = (n_max, max(1, runs), H, Hkv, device)
         self.workspace = new_workspace(*self._ws_shape)
-        self.live_steps = live_steps(self.q_pos.cpu().numpy(), self.q_doc.cpu().numpy(),
-                                     [(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy()) for s in self.steps],
-                                     shared_doc)
+        qp, qd = self.q_pos.cpu().numpy(), self.q_doc.cpu().numpy()
+        self.live_steps = live_steps(qp, qd, [(s["kv_pos"].cpu().numpy(), s["kv_doc"].cpu().numpy())
+                                              for s in self.steps], shared_doc)
+        # a live step whose query runs meet more key runs than the block planner takes
+        # (striped shards) runs as a slice list: same mask, planned by the slice-list planner
+        for t in self.live_steps:
+            st = self.steps[t]
+            kp, kd = st["kv_pos"].cpu().numpy(), st["kv_doc"].cpu().numpy()
+            if step_span_count(qp, qd, kp, kd, shared_doc) > MAX_SPANS:
+                sl = step_slices(qp, qd, kp, kd, shared_doc)
+                st["slices"] = torch.tensor(sl, dtype=torch.int32, device=device).reshape(-1, 5)
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None
@@ -371,18 +448,36 @@ class ShardedRank:
         self.lse.fill_(-float("inf"))
         return self.out, self.lse
 
+    def _new_step_workspace(self, t):
+        from . import new_workspace
+        st = self.steps[t]
+        if "slices" in st:
+            n_q, H, _ = self.q.shape
+            return new_workspace(n_q, 2 * st["slices"].shape[0] + 1, H, st["kv"].shape[2], self.q.device)
+        return new_workspace(*self._ws_shape)
+
     def run(self, stream=None, per_step=None):
-        """Every live step, each a block_attn_fwd, and a merge for each after the first."""
-        from . import block_attn_fwd, lse_merge
+        """Every live step, each a block_attn_fwd (or, for a slice-list step, its plan and
+        run), and a merge for each after the first."""
+        from . import attn_run, block_attn_fwd, lse_merge, plan_slices
         if not self.live_steps:
             return self._no_live_step()
+        n_q, H, d = self.q.shape
         for i, t in enumerate(self.live_steps):
             st = self.steps[t]
             first = i == 0
             out = self.out if first else self.step_out
             lse = self.lse if first else self.step_lse
-            block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out, lse=lse,
-                           workspace=self.workspace, stream=stream, shared_doc=self.shared_doc)
+            if "slices" in st:
+                if self.step_workspaces is None:
+                    self.step_workspaces = [self._new_step_workspace(u) if u in self.live_steps else None
+                                            for u in range(len(self.steps))]
+                ws = plan_slices(st["slices"], n_q, st["kv"].shape[1], H, st["kv"].shape[2], d,
+                                 workspace=self.step_workspaces[t], stream=stream)
+                attn_run(self.q, st["kv"][0], st["kv"][1], out, lse, ws, stream=stream)
+            else:
+                block_attn_fwd(self.q, st["kv"], self.q_pos, st["kv_pos"], self.q_doc, st["kv_doc"], out=out,
+                               lse=lse, workspace=self.workspace, stream=stream, shared_doc=self.shared_doc)
             if per_step is not None:
                 per_step(t, out, lse)
             if not first:
@@ -393,17 +488,25 @@ class ShardedRank:
         """Plans every live ring step in one launch, one workspace per step (None for the
         others): a step's key/value positions and document ids follow from the sharding,
         before its data arrive."""
-        from . import new_workspace, plan_block_steps
+        from . import plan_block_steps, plan_slices
         if self.step_workspaces is None:
-            self.step_workspaces = [new_workspace(*self._ws_shape) if t in self.live_steps else None
+            self.step_workspaces = [self._new_step_workspace(t) if t in self.live_steps else None
                                     for t in range(len(self.steps))]
         if not self.live_steps:
             return
         n_q, H, d = self.q.shape
-        live = [self.steps[t] for t in self.live_steps]
-        plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in live], [st["kv_doc"] for st in live], H,
-                         self.steps[0]["kv"].shape[2], d, [self.step_workspaces[t] for t in self.live_steps],
-                         stream=stream, shared_doc=self.shared_doc)
+        Hkv = self.steps[0]["kv"].shape[2]
+        by_runs = [t for t in self.live_steps if "slices" not in self.steps[t]]
+        if by_runs:
+            live = [self.steps[t] for t in by_runs]
+            plan_block_steps(self.q_pos, self.q_doc, [st["kv_pos"] for st in live], [st["kv_doc"] for st in live], H,
+                             Hkv, d, [self.step_workspaces[t] for t in by_runs], stream=stream,
+                             shared_doc=self.shared_doc)
+        for t in self.live_steps:
+            st = self.steps[t]
+            if "slices" in st:
+                plan_slices(st["slices"], n_q, st["kv"].shape[1], H, Hkv, d, workspace=self.step_workspaces[t],
+                            stream=stream)
 
     def run_planned(self, stream=None, per_step=None):
         """run() with the plans of all live steps made up front by plan_all(): one planning
@@ -470,7 +573,10 @@ class ShardedRank:
         None for a step no row sees: it sends nothing back.  ring=True runs the live steps'
         dK/dV items in one launch from one longest-first queue (lb_block_attn_bwd_ring); dq
         is added step after step either way."""
-        from . import attn_bwd_rowdot, block_attn_bwd
+        from . import LBError, attn_bwd_rowdot, block_attn_bwd
+        if any("slices" in self.steps[t] for t in self.live_steps):
+            raise LBError("the backward of a ring step planned as a slice list (a step whose query runs meet more "
+                          f"than {MAX_SPANS} key runs, e.g. striped shards) is not built")
         if getattr(self, "bwd_buffers", None) is None:
             n_q, H, d = self.q.shape
             ws_bytes = 2 * self.workspace.numel() + 512
@@ -512,7 +618,8 @@ class ShardedRank:
         live = [self.steps[t] for t in self.live_steps]
         if getattr(self, "ring_workspace", None) is None:
             n_max, runs, H, Hkv, device = self._ws_shape
-            self.ring_workspace = new_ring_workspace(len(live), n_max, runs, H, Hkv, device=device)
+            frags = max([runs] + [2 * st["slices"].shape[0] + 1 for st in live if "slices" in st])
+            self.ring_workspace = new_ring_workspace(len(live), n_max, frags, H, Hkv, device=device)
         n_q, H, d = self.q.shape
         self.plan_all(stream)
         plan_ring([self.step_workspaces[t] for t in self.live_steps], [st["kv"].shape[1] for st in live], n_q, H,

@@ -68,21 +68,29 @@ def slices_attention(q, k, v, slices, heads, kv_heads, scale=None):
     return out, lse
 
 
-def fragments(slices):
+def fragments(slices, n_q=None):
     """Planner fragments of a slice list (query ranges in order, each with the key spans of
     its slices): (q_start, q_len, q_pos0, [span, ...]) with query positions from 0 in the
     range.  A span (k_start, k_len, k_pos0) makes key j visible to row r iff
     k_pos0 + j <= r: CAUSAL at k_pos0 = q_len - k_len, FULL far below.  Kinds with a lower
     bound add k_lo, (k_start, k_len, k_pos0, k_lo), with key j visible only if k_lo + j >= r:
-    INV-CAUSAL (k_pos0 far below, k_lo = 0) and BI-CAUSAL (both)."""
+    INV-CAUSAL (k_pos0 far below, k_lo = 0) and BI-CAUSAL (both).  Rows no slice covers
+    form fragments with no span (their lse is -inf): before and between the ranges, and,
+    given the query count n_q, after the last one."""
     frags = []
+    end = 0  # rows before `end` belong to a fragment already
     for (qs, ql, ks, kl, kind) in slices:
         hi = (ql - kl) if kind in (CAUSAL, BI_CAUSAL) else -FAR
         span = (ks, kl, hi) if kind in (FULL, CAUSAL) else (ks, kl, hi, 0)
         if frags and frags[-1][0] == qs and frags[-1][1] == ql:
             frags[-1][3].append(span)
         else:
+            if qs > end:  # rows no slice covers: a fragment without keys (lse = -inf)
+                frags.append((end, qs - end, 0, []))
             frags.append((qs, ql, 0, [span]))
+            end = qs + ql
+    if n_q is not None and end < n_q:
+        frags.append((end, n_q - end, 0, []))
     return frags
 
 

@@ -481,6 +481,41 @@ def test_sharded_ranks_reassemble_the_unsharded_result(rule):
         check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]], f"{rule} rank {rank}")
 
 
+@pytest.mark.parametrize("width,shared", [(1, False), (64, False), (3, True)])
+def test_striped_ranks_reassemble_the_unsharded_result(width, shared):
+    """Striped sharding ("03 · 长文负载均衡", section 4.2): stripes of `width` tokens dealt to
+    cp = 4 ranks in turn.  A query stripe then meets a key run per earlier stripe of its
+    document, more than the block planner's 4 spans, so those steps run as slice lists (the
+    same mask over local indices); per step (run, run_planned) and as one ring launch
+    (run_ring), every rank's rows equal the unsharded oracle (with a shared question:
+    document 0 shared)."""
+    from load_balance_amd import sharding as LS
+    cp, H, Hkv, d = 4, 8, 2, 128
+    r = np.random.default_rng(70 + width)
+    lengths = [2600, 37, 1, 650, 9, 301, 1350]  # 2600 tokens: 10 stripes of 64 per rank
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    tok = LS.shard_tokens("striped", lengths, cp, width=width)
+    assert LS.max_spans(lengths, tok, 0 if shared else -1) > LS.MAX_SPANS
+    shards = LS.build_shards(lengths, tok, lambda idx: (q[idx], k[idx], v[idx]))
+    full_o, full_l = OA.varlen_attention(q, k, v, workloads.cu_from_lengths(lengths), H, Hkv,
+                                         mask="shared_question" if shared else "causal_doc")
+    for rank in range(cp):
+        share = LS.ShardedRank(shards, rank, shared_doc=0 if shared else -1)
+        n_sl = sum(1 for t in share.live_steps if "slices" in share.steps[t])
+        say(f"  striped w={width} rank {rank}: {len(tok[rank])} tokens, live steps {share.live_steps}, "
+            f"{n_sl} as slice lists")
+        assert n_sl > 0
+        for name, fn in (("run", share.run), ("run_planned", share.run_planned), ("run_ring", share.run_ring)):
+            out, lse = fn()
+            torch.cuda.synchronize()
+            for t in share.live_steps:
+                if share.step_workspaces is not None and share.step_workspaces[t] is not None:
+                    assert lb.read_device_error(share.step_workspaces[t]) == 0
+            check(out.cpu().numpy(), lse.cpu().numpy(), full_o[tok[rank]], full_l[:, tok[rank]],
+                  f"striped w={width} rank {rank} {name}")
+
+
 # --------------------------------------------------------------------------
 # block path edge cases
 # --------------------------------------------------------------------------

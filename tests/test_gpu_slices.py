@@ -45,7 +45,7 @@ def run(slices, n_q, n_k, H, Hkv, d, seed):
     q, _, _ = workloads.values(r, n_q, H, Hkv, d)
     _, k, v = workloads.values(r, n_k, H, Hkv, d)
     say(f"  slices_attn_fwd n_q={n_q} n_kv={n_k} H={H}/{Hkv} d={d} slices={len(slices)}")
-    ws = lb.new_workspace(n_q, len(slices), H, Hkv)
+    ws = lb.new_workspace(n_q, 2 * len(slices) + 1, H, Hkv)
     out, lse = lb.slices_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), slices, workspace=ws)
     torch.cuda.synchronize()
     assert lb.read_device_error(ws) == 0
@@ -109,6 +109,12 @@ def test_random_slice_lists(seed):
     (q, k, v), out, lse, ws = run(sl, n_q, n_k, H, Hkv, d, seed=seed)
     ref_o, ref_l = SL.slices_attention(q, k, v, sl, H, Hkv)
     check(out, lse, ref_o, ref_l, f"random slices seed {seed}")
+    # the plan, the fragments of rows no slice covers included, equals the oracle's
+    t = OP.tiles(SL.fragments(sl, n_q), lb.tile_rows(H, Hkv, d))
+    ref = [t[i] for i in OP.lpt_order(t)]
+    plan = lb.read_plan(ws)
+    assert [(a["q_start"], a["q_len"], a["q_pos0"], a["cost"], a["blocks"], [tuple(x) for x in a["spans"]]) for a in plan] \
+        == [(b["q_start"], b["q_len"], b["q_pos0"], b["cost"], b["blocks"], [tuple(x) for x in b["spans"]]) for b in ref]
 
 
 @pytest.mark.parametrize("bad", ["overlap", "kind", "range"])
@@ -119,7 +125,7 @@ def test_malformed_slice_lists_run_nothing(bad):
           "range": [(0, 32, 0, 100, 0)]}[bad]
     r = np.random.default_rng(0)
     q, k, v = workloads.values(r, n, H, Hkv, d)
-    ws = lb.new_workspace(n, len(sl), H, Hkv)
+    ws = lb.new_workspace(n, 2 * len(sl) + 1, H, Hkv)
     out = torch.full((n, H, d), 3.0, dtype=torch.bfloat16, device="cuda")
     lb.slices_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), sl, out=out, workspace=ws)
     torch.cuda.synchronize()

@@ -94,7 +94,14 @@ def test_slice_tiles_count_every_pair_once(seed, bm):
     n_q, n_k = 300, 250
     sl = random_slices(r, n_q, n_k)
     V = SL.visible(sl, n_q, n_k)
-    tl = P.tiles(SL.fragments(sl), bm)
+    tl = P.tiles(SL.fragments(sl, n_q), bm)
+    # every row is in exactly one tile; rows no slice covers are in tiles without a span
+    rows = np.zeros(n_q, dtype=int)
+    for t in tl:
+        rows[t["q_start"]:t["q_start"] + t["q_len"]] += 1
+        if not t["spans"]:
+            assert not V[t["q_start"]:t["q_start"] + t["q_len"]].any()
+    assert np.all(rows == 1)
     seen = np.zeros(V.shape, dtype=int)
     for t in tl:
         brute = 0

@@ -191,3 +191,54 @@ def test_max_spans_with_a_shared_document():
             bw = OP.fragments_block_t(pos[qi], doc[qi], pos[ki], doc[ki], shared_doc=0)
             worst = max([worst] + [len(f[3]) for f in fw + bw])
     assert LS.max_spans(lengths, tok, 0) == worst <= LS.MAX_SPANS
+
+
+@pytest.mark.parametrize("rule", ["striped", "zigzag", "per_document", "dispatch"])
+def test_step_slices_are_the_block_mask(rule):
+    """The slice list of a ring step (how steps with more key runs than the block planner
+    takes run) marks exactly the pairs the block mask does, brute force over every pair of
+    ranks of random packs, with and without a shared document."""
+    from oracle import attention as OA
+    from oracle import slices as SL
+    r = np.random.default_rng(90)
+    for trial in range(40):
+        cp = int(r.integers(2, 6))
+        T = 2 * cp * int(r.integers(4, 40))
+        lengths = []
+        while sum(lengths) < T:
+            lengths.append(int(r.integers(1, T // 2 + 2)))
+        lengths[-1] -= sum(lengths) - T
+        lengths = [x for x in lengths if x > 0]
+        width = int(r.choice([1, 2, 3, 8, 64]))
+        tok = LS.shard_tokens(rule, lengths, cp, width=width, n_chunks=2 * cp)
+        pos, doc = OA.pack_positions(lengths)
+        shared = int(r.integers(-1, len(lengths))) if trial % 3 == 0 else -1
+        for a in range(cp):
+            for b in range(cp):
+                qp, qd, kp, kd = pos[tok[a]], doc[tok[a]], pos[tok[b]], doc[tok[b]]
+                sl = LS.step_slices(qp, qd, kp, kd, shared)
+                got = SL.visible(sl, len(qp), len(kp)) if sl else np.zeros((len(qp), len(kp)), bool)
+                want = OA.visible_block(qp, qd, kp, kd, np.arange(len(qp)), np.arange(len(kp)),
+                                        shared_doc=None if shared < 0 else shared)
+                assert np.array_equal(got, want), (rule, cp, width, a, b, shared)
+                # a valid slice list: query ranges ascending and disjoint, at most 4 slices on a
+                # range, their key ranges ascending and disjoint
+                for i in range(1, len(sl)):
+                    p, c = sl[i - 1], sl[i]
+                    if (p[0], p[1]) == (c[0], c[1]):
+                        assert p[2] + p[3] <= c[2]
+                    else:
+                        assert p[0] + p[1] <= c[0]
+
+
+def test_step_span_count_matches_max_spans():
+    """Over all steps of all ranks, the per-step span count's maximum is max_spans'."""
+    lengths = [700, 37, 1, 650, 9, 301, 350]
+    for rule, width in (("striped", 1), ("striped", 64), ("zigzag", 1), ("per_document", 1)):
+        tok = LS.shard_tokens(rule, lengths, 4, width=width) if rule != "zigzag" else \
+            LS.shard_tokens(rule, lengths + [4 * 2 * 256 - sum(lengths)], 4)
+        lens = lengths if rule != "zigzag" else lengths + [4 * 2 * 256 - sum(lengths)]
+        pos, doc = LS.token_meta(lens)
+        for shared in (-1, 0):
+            worst = max(LS.step_span_count(pos[a], doc[a], pos[b], doc[b], shared) for a in tok for b in tok)
+            assert worst <= LS.max_spans(lens, tok, shared)
