@@ -173,7 +173,7 @@ lb_status lb_varlen_attn_fwd(const void* q, const void* k, const void* v, const 
  * the call compute nothing, as in lb_varlen_attn_fwd; callers that need the diagnosis use
  * lb_varlen_attn_fwd with a workspace.
  */
-#define LB_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+#define LB_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 lb_status lb_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                                      int32_t n_seg, int32_t total_tokens, int32_t heads, int32_t kv_heads,
                                      int32_t d, int32_t mask_kind, void* out, float* lse, hipStream_t stream);

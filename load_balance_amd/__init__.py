@@ -26,7 +26,7 @@ MASK_SHARED_QUESTION = 1
 NO_SHARED_DOC = -1  # block path: no document shared by the others
 MAX_SPANS = 4
 MAX_PLAN_STEPS = 16
-NOALLOC_SCRATCH_BYTES = 8 << 20  # LB_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LB_NOALLOC_SCRATCH_BYTES
 
 DEVERR_CU_SEQLENS = 1
 DEVERR_CAPACITY = 2

@@ -21,7 +21,8 @@ constexpr int kBlockN = LB_BLOCK_KEYS;
 
 // Planning kernel: one workgroup sorts the tile keys in LDS.
 constexpr int kPlanThreads = 1024;
-constexpr int kSortCap = 16384;     // tiles per call
+constexpr int kSortCap = 32768;     // tiles per plan (32-bit sort keys, 128 KB of LDS)
+constexpr int kRingSortCap = 16384; // work tiles one ring merge takes (two int arrays in LDS)
 constexpr int kMaxWorkers = 2048;   // persistent workgroups per launch
 constexpr int kXcds = 8;            // accelerator complex dies (XCDs) of an MI355X, one L2 each
 

@@ -27,14 +27,20 @@ namespace lb {
 namespace {
 
 constexpr int NT = kPlanThreads;
-constexpr uint64_t kKeyMask = (uint64_t(1) << 40) - 1;  // block counts < 2^31 fit the key's 40 bits
+// Sort keys are 32 bits: (kBlocksMax - blocks) above kIndexBits bits of natural index, so
+// that ascending keys are blocks descending, ties in natural order.  A tile sweeping more
+// than kBlocksMax key blocks (a document of over two million tokens) sorts as kBlocksMax.
+constexpr int kIndexBits = 17;
+constexpr uint32_t kIndexMask = (1u << kIndexBits) - 1;
+constexpr uint32_t kBlocksMax = (1u << (32 - kIndexBits)) - 1;
+static_assert(kSortCap <= (int)kIndexMask + 1, "a tile index must fit the key");
 
 constexpr int kPlanWaves = NT / 64;
 
 constexpr int kRunRounds = 4;
 
 struct PlanShared {
-  uint64_t keys[kSortCap];
+  uint32_t keys[kSortCap];
   int32_t wave_sum[kPlanWaves];
   int32_t run_sum[kRunRounds][kPlanWaves];
   int32_t err;
@@ -180,7 +186,7 @@ __device__ __forceinline__ void bitonic_phase(PlanShared& sh, int n_pad, int k, 
     for (int i = tid; i < n_pad; i += NT) {
       const int p = i ^ j;
       if (p > i) {
-        const uint64_t x = sh.keys[i], y = sh.keys[p];
+        const uint32_t x = sh.keys[i], y = sh.keys[p];
         const bool ascending = (i & k) == 0;
         if ((x > y) == ascending) {
           sh.keys[i] = y;
@@ -194,10 +200,10 @@ __device__ __forceinline__ void bitonic_phase(PlanShared& sh, int n_pad, int k, 
   // every thread of the workgroup runs the shuffles (padding lanes carry the largest key)
   for (int base = 0; base < max(n_pad, NT); base += NT) {
     const int i = base + tid;
-    uint64_t x = i < n_pad ? sh.keys[i] : ~uint64_t(0);
+    uint32_t x = i < n_pad ? sh.keys[i] : ~uint32_t(0);
     for (int kk = (j_first >= 64 ? k : 2); kk <= k; kk <<= 1) {
       for (int jj = (kk == k ? j : kk >> 1); jj > 0; jj >>= 1) {
-        const uint64_t y = __shfl_xor(x, jj);
+        const uint32_t y = __shfl_xor(x, jj);
         const bool ascending = (i & kk) == 0;
         const bool lower = (i & jj) == 0;
         x = (lower == ascending) ? (x < y ? x : y) : (x < y ? y : x);
@@ -211,9 +217,10 @@ __device__ __forceinline__ void bitonic_phase(PlanShared& sh, int n_pad, int k, 
 // LDS staging inside the sort buffer, used before the sort needs it: key/value runs in the
 // first quarter, a copy of the fragments (when they fit) in the second, each fragment's
 // first tile index in the second half.
-constexpr int kLdsRuns = kSortCap * 8 / 4 / (int)sizeof(KvRun);
-constexpr int kLdsFrags = kSortCap * 8 / 4 / (int)sizeof(Frag);
-constexpr int kLdsFtile = kSortCap * 8 / 2 / (int)sizeof(int32_t);
+constexpr int kSortBytes = kSortCap * (int)sizeof(uint32_t);
+constexpr int kLdsRuns = kSortBytes / 4 / (int)sizeof(KvRun);
+constexpr int kLdsFrags = kSortBytes / 4 / (int)sizeof(Frag);
+constexpr int kLdsFtile = kSortBytes / 2 / (int)sizeof(int32_t);
 constexpr int kMaxTilesPerThread = kSortCap / NT;
 constexpr int kRankSortMax = 2048;  // tiles ranked directly; larger plans take the bitonic sort
 static_assert(kRankSortMax % NT == 0 && kRankSortMax <= kSortCap, "");
@@ -462,7 +469,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   __syncthreads();
   // sort keys of this thread's tiles, (2^40 - 1 - blocks) << 24 | natural index: ascending
   // order is blocks descending with ties in natural order, and every key is unique
-  uint64_t my_keys[kMaxTilesPerThread];
+  uint32_t my_keys[kMaxTilesPerThread];
   if (sh.err == 0) {
     unsigned long long my_pairs = 0;
 #pragma unroll
@@ -521,7 +528,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       ntiles[t] = T;
       if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
-      my_keys[k] = ((kKeyMask - (uint64_t)blocks) << 24) | (uint64_t)t;
+      my_keys[k] = ((kBlocksMax - min((uint32_t)blocks, kBlocksMax)) << kIndexBits) | (uint32_t)t;
     }
     atomicAdd(&sh.pairs, my_pairs);
   }
@@ -542,7 +549,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     for (int k = 0; k < kRankSortMax / NT; ++k) {
       const int t = tid + k * NT;
       if (t >= n_tiles) break;
-      const uint64_t key = my_keys[k];
+      const uint32_t key = my_keys[k];
       int rank = 0;
 #pragma unroll 8
       for (int i = 0; i < n_tiles; ++i) rank += sh.keys[i] < key ? 1 : 0;
@@ -556,14 +563,14 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
 #pragma unroll
     for (int k = 0; k < kMaxTilesPerThread; ++k) {
       const int i = tid + k * NT;
-      if (i < n_pad) sh.keys[i] = i < n_tiles ? my_keys[k] : ~uint64_t(0);
+      if (i < n_pad) sh.keys[i] = i < n_tiles ? my_keys[k] : ~0u;
     }
     __syncthreads();
     // phases k = 2 .. min(n_pad, 64) pair lanes of one wave only: all in registers at once
     bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
     for (int k = 128; k <= n_pad; k <<= 1) bitonic_phase(sh, n_pad, k, k >> 1);
     for (int i = tid; i < n_tiles; i += NT) {
-      tiles[i] = ntiles[sh.keys[i] & 0xFFFFFF];
+      tiles[i] = ntiles[sh.keys[i] & kIndexMask];
       order[i] = i;
     }
   }
@@ -649,8 +656,8 @@ __device__ __forceinline__ void copy_tile(lb_plan_tile* dst, const lb_plan_tile*
 }
 
 __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
-  __shared__ int32_t blk[kSortCap];  // key blocks of the work tiles, step after step
-  __shared__ int32_t src[kSortCap];  // their index in the step's tile array
+  __shared__ int32_t blk[kRingSortCap];  // key blocks of the work tiles, step after step
+  __shared__ int32_t src[kRingSortCap];  // their index in the step's tile array
   __shared__ int32_t base[kMaxPlanSteps + 1], ebase[kMaxPlanSteps + 1];
   __shared__ const lb_plan_tile* tiles_of[kMaxPlanSteps];
   __shared__ const int32_t* order_of[kMaxPlanSteps];
@@ -697,7 +704,7 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
       ebase[s + 1] = ebase[s] + empty_of[s];
       p += pairs_of[s];
     }
-    if (base[n_steps] > kSortCap || (int64_t)base[n_steps] + ebase[n_steps] > m.ring_cap) e |= LB_DEVERR_CAPACITY;
+    if (base[n_steps] > kRingSortCap || (int64_t)base[n_steps] + ebase[n_steps] > m.ring_cap) e |= LB_DEVERR_CAPACITY;
     err = e;
     err_tiles = 0;
     pairs = p;

@@ -233,9 +233,16 @@ def tiles_t(frags, bm):
     return out
 
 
+# Orders are taken on key blocks capped at ORDER_CAP: a tile sweeping more blocks (a
+# document of over two million tokens) is ordered as if it swept ORDER_CAP.  (Reading: the
+# order only needs to put the longest tiles first; the planner's 32-bit sort key holds 15
+# bits of block count.)
+ORDER_CAP = (1 << 15) - 1
+
+
 def lpt_order(tile_list, key="blocks"):
-    """Indices of tiles, `key` descending, ties in natural order."""
-    return sorted(range(len(tile_list)), key=lambda i: (-tile_list[i][key], i))
+    """Indices of tiles, `key` descending (capped at ORDER_CAP), ties in natural order."""
+    return sorted(range(len(tile_list)), key=lambda i: (-min(tile_list[i][key], ORDER_CAP), i))
 
 
 def plan(frags, bm):

@@ -108,7 +108,7 @@ def test_noalloc_host_checks(L):
     assert call(d=96) == LB_EUNSUPPORTED
     assert call(T=1 << 22, n_seg=1, H=32, Hkv=8, d=128) == LB_EUNSUPPORTED  # > sort capacity
     # every plan within the sort capacity fits the scratch array
-    assert L.lb_workspace_bytes(16384 * 64, 16384, 32, 8) <= lb.NOALLOC_SCRATCH_BYTES
+    assert L.lb_workspace_bytes(32768 * 64, 32768, 32, 8) <= lb.NOALLOC_SCRATCH_BYTES
 
 
 def test_block_host_checks(L):

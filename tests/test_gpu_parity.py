@@ -195,6 +195,33 @@ def test_longtail_other_seeds_plan(seed):
     assert np.array_equal(got, np.broadcast_to(n, got.shape))
 
 
+@pytest.mark.parametrize("tokens,H,Hkv", [(1 << 20, 32, 8), (1 << 19, 64, 8)])
+def test_plans_beyond_16k_tiles(tokens, H, Hkv):
+    """Plans of more than 16384 tiles (the pages' long-context packs: Libra trains on 1M-token
+    packed sequences, "03 · 长文负载均衡" section 1.3): a 1,048,576-token lognormal pack at 32 q
+    / 8 kv heads (tiles of 64 rows) and a 524,288-token one at 64 q / 8 kv (tiles of 32 rows),
+    planned on the device (bitonic order of 32-bit keys in LDS), equal the oracle's plan bit
+    for bit."""
+    lengths = workloads.lognormal_lengths(tokens, 11, tokens)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=tokens, heads=H,
+                kv_heads=Hkv, d=128)
+    cu = torch.from_numpy(np.asarray(pack["cu_seqlens"], dtype=np.int32)).cuda()
+    ws = lb.new_workspace(tokens, len(lengths), H, Hkv)
+    lb.plan_varlen(cu, tokens, H, Hkv, 128, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    lb.plan_varlen(cu, tokens, H, Hkv, 128, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    got = lb.read_plan(ws, max_tiles=1 << 16)
+    say(f"  {tokens} tokens, {len(lengths)} documents, H={H}/{Hkv}: {len(got)} tiles planned in "
+        f"{e0.elapsed_time(e1) * 1e3:.0f} us")
+    assert len(got) > 16384
+    assert_same_plan(got, plan_ref_varlen(pack), f"{tokens}-token plan")
+
+
 # --------------------------------------------------------------------------
 # config 3: equal-token pair
 # --------------------------------------------------------------------------
