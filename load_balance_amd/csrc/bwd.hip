@@ -525,103 +525,187 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 // accumulate dK^T = sum Q^T dS (S and dP recomputed); waves 4-7 hold K and accumulate
 // dV^T = sum dO^T P (S recomputed).  Each runs every head of the kv group, so no reduction
 // over heads or waves follows, and each fits in 256 registers.  Query rows stream in
-// stages of 64 (two MFMA blocks of 32), one head per stage, through a 2-stage LDS ring
-// that both roles read.
+// stages of 64 (two MFMA blocks of 32), one head per stage, through a ring of kKvStages
+// LDS stages that both roles read, kKvStages - 1 of them in flight.
+//
+// A stage holds the 64 Q rows and 64 dO rows row-major, copied from global memory straight
+// into LDS by the buffer loads' LDS mode (no registers, no stores), and the rows' raw lse
+// and D.  The row-major tiles serve both products: S = Q K^T and dP = dO V^T read row
+// fragments, and dK^T += Q^T dS and dV^T += dO^T P read the transposed fragments with
+// gfx950's LDS transpose load (ds_read_b64_tr_b16), which hands each lane one d column of
+// 4 rows.  Each row's 16-byte chunks are stored XOR-permuted by the row (swz) so that both
+// kinds of read hit 64 distinct banks per pass.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKeyGroups = 4;  // 32 keys each: 128 keys per tile
+constexpr int kKvStages = 4;   // LDS ring depth
 
 template <int D>
 struct KvLds {
-  static constexpr int rStride = D * 2 + 16;    // Q or dO row
-  static constexpr int tStride = kQB * 2 + 16;  // Q^T or dO^T row (one d, the stage's rows)
-  static constexpr int rowsBytes = kQB * rStride;
-  static constexpr int tBytes = D * tStride;
-  static constexpr int stage = 2 * rowsBytes + 2 * tBytes + 2 * kQB * 4;  // Q, dO rows; Q^T, dO^T; lse2, D
-  static constexpr int units = 2 * (kQB / 2) * (D / 8);  // (tensor, row pair, chunk)
-  static constexpr int perThread = units / kKvThreads;
+  static constexpr int rowBytes = D * 2;              // one Q or dO row, unpadded
+  static constexpr int chunks = D / 8;                 // 16-byte chunks per row
+  static constexpr int tileBytes = kQB * rowBytes;     // 64 rows of one tensor
+  static constexpr int stage = 2 * tileBytes + 2 * kQB * 4;  // Q, dO; raw lse, D
+  static constexpr int rowsPerDma = 1024 / rowBytes;   // rows one wave's 16-byte-per-lane copy covers
+  static constexpr int dmaPerTensor = kQB / rowsPerDma / kKvWaves;  // copies per wave per tensor
+  static constexpr int dmaPerStage = 2 * dmaPerTensor + 1;          // + one for lse or D
+  static constexpr int ring = kKvStages * stage;
   static constexpr int epiStride = D * 4 + 16;
-  static_assert(units % kKvThreads == 0, "loader units must divide evenly");
+  static constexpr int epiRows = kKvWaves * 32 * epiStride <= ring ? 32 : 16;  // rows per epilogue pass
+  static_assert(kQB % (rowsPerDma * kKvWaves) == 0, "the copies must divide evenly over the waves");
+  static_assert(kKvWaves * epiRows * epiStride <= ring, "epilogue staging must fit in the ring");
 };
 
+// The chunk permutation of row r (r mod 16 decides it).  Row reads: 16 lanes read one
+// logical chunk of 16 consecutive rows, which land on 16 distinct chunk slots (d = 128) or on
+// 8 slots in each bank half (d = 64: two rows per 256 bytes).  Transpose reads: 32 lanes read
+// four logical chunks (a 64-byte run) of 4 consecutive rows, which land on 4 disjoint runs.
 template <int D>
-struct QdoLoader {
-  using L = KvLds<D>;
-  u32x4 r[L::perThread][2];
-  float lv, dv;
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
-  // rows r0 .. r0 + kQB of the span (`valid` of them real) of one head
-  __device__ __forceinline__ void load(const BwdArgs& a, int r0, int valid, int head, int tid) {
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    valid = __builtin_amdgcn_readfirstlane(valid);
-    head = __builtin_amdgcn_readfirstlane(head);
-    const int64_t row_step = (int64_t)a.heads * D * 2;
-    const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(valid, kQB)) * (int)row_step);
-#pragma unroll
-    for (int e = 0; e < L::perThread; ++e) {
-      const int u = tid + e * kKvThreads;
-      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2);
-      // the tensor of the unit is the same in every lane of a wave (a multiple of 64 units
-      // each): made explicit, so that the buffer descriptor lives in scalar registers
-      const int t = __builtin_amdgcn_readfirstlane(u / ((kQB / 2) * (D / 8)));
-      const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
-                         (int64_t)head * D * 2;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, kBufferFlags);
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        r[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rs, (2 * p + x) * (int)row_step + ch * 16, 0, 0);
-    }
-    lv = dv = 0.f;
-    if (tid < kQB) {
-      const float l = tid < valid ? a.lse[(int64_t)head * a.n_q + r0 + tid] : -__builtin_inff();
-      lv = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
-      dv = tid < valid ? a.dvec[(int64_t)head * a.n_q + r0 + tid] : 0.f;
-    }
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }  // s_waitcnt vmcnt(n) only
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + nbytes): reads past the end return zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane(nbytes), kBufferFlags};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (int)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Copies global -> LDS without registers: lane i's 16 (or 4) bytes at voffset land at
+// lds + 16 i (or 4 i).  Written as inline assembly on purpose: the compiler, seeing the
+// builtin's LDS write, would wait for every copy in flight before each LDS read of the loop;
+// the kernel waits for its copies itself (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// The stages of one key tile: for each span, each 64 rows, each head of the group.  The
+// cursor carries the spans still ahead of it, read once per item into uniform registers and
+// shifted forward, never indexed: the loop that walks them then issues no memory read (a
+// vector or scratch read there would wait for every copy in flight).
+struct StageCursor {
+  int off, hs, left;  // left: spans after the current one
+  Span sp, n1, n2, n3;
+  __device__ __forceinline__ void start(const lb_plan_tile* T) {
+    static_assert(LB_MAX_SPANS == 4, "the cursor holds up to four spans");
+    off = hs = 0;
+    left = __builtin_amdgcn_readfirstlane(T->n_spans) - 1;
+    sp = span_of(T, 0);
+    n1 = span_of(T, 1);
+    n2 = span_of(T, 2);
+    n3 = span_of(T, 3);
   }
-
-  __device__ __forceinline__ void store(char* stage, int tid) {
-#pragma unroll
-    for (int e = 0; e < L::perThread; ++e) {
-      const int u = tid + e * kKvThreads;
-      const int ch = u % (D / 8), p = (u / (D / 8)) % (kQB / 2), t = u / ((kQB / 2) * (D / 8));
-      char* rows = stage + t * L::rowsBytes;
-      char* tr = stage + 2 * L::rowsBytes + t * L::tBytes;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(rows + (2 * p + x) * L::rStride + ch * 16) = r[e][x];
-      const int col = vt_pos(2 * p) * 2;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        *reinterpret_cast<uint32_t*>(tr + (ch * 8 + 2 * m) * L::tStride + col) = pair_lo(r[e][0][m], r[e][1][m]);
-        *reinterpret_cast<uint32_t*>(tr + (ch * 8 + 2 * m + 1) * L::tStride + col) = pair_hi(r[e][0][m], r[e][1][m]);
+  __device__ __forceinline__ void next(int G) {
+    if (++hs == G) {
+      hs = 0;
+      off += kQB;
+      if (off >= sp.len && left > 0) {
+        off = 0;
+        --left;
+        sp = n1;
+        n1 = n2;
+        n2 = n3;
       }
     }
-    if (tid < kQB) {
-      float* f = reinterpret_cast<float*>(stage + 2 * L::rowsBytes + 2 * L::tBytes);
-      f[tid] = lv;
-      f[kQB + tid] = dv;
-    }
   }
 };
+
+// Copies stage `c` (64 rows of one head from row sp.start + off) into `buf`: every wave issues
+// dmaPerStage copies (the same count in every wave, so that vmcnt waits are uniform).  Rows
+// past the span's end read as zeros (the buffer range ends there), and so do their lse and D.
+template <int D>
+__device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const StageCursor& c, int g, int wave,
+                                            int lane) {
+  using L = KvLds<D>;
+  const int head = __builtin_amdgcn_readfirstlane(g * a.group + c.hs);
+  const int r0 = __builtin_amdgcn_readfirstlane(c.sp.start + c.off);
+  const int valid = __builtin_amdgcn_readfirstlane(max(0, min(c.sp.len - c.off, kQB)));
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int row_step = a.heads * D * 2;
+  const uint32_t lds = lds_addr(buf);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
+                       (int64_t)head * D * 2;
+    const i32x4 rs = buffer_rsrc(base, valid * row_step);
+#pragma unroll
+    for (int j = 0; j < L::dmaPerTensor; ++j) {
+      const int blk = w * L::dmaPerTensor + j;  // the 1 KB piece of the tile
+      const int row = blk * L::rowsPerDma + lane / L::chunks;
+      const int chunk = (lane % L::chunks) ^ swz<D>(row);  // lane writes slot lane % chunks of its row
+      copy16_to_lds(rs, lds + t * L::tileBytes + blk * 1024, row * row_step + chunk * 16);
+    }
+  }
+  // lse (even waves) or D (odd waves), 16 rows per wave, 4 bytes per lane
+  const float* vec = (w & 1) ? a.dvec : a.lse;
+  const int q16 = w >> 1;
+  const i32x4 rv = buffer_rsrc(vec + (int64_t)head * a.n_q + r0, valid * 4);
+  if (lane < 16) copy4_to_lds(rv, lds + 2 * L::tileBytes + (w & 1) * kQB * 4 + q16 * 64, (q16 * 16 + lane) * 4);
+}
 
 // RING: a ring workspace of several steps' key tiles; a tile's step selects the keys, values
 // and gradient outputs of that step in r (one launch for every step of a rank's ring).
+// Requires a finite lse for every row of a span (a row that sees a key of the tile has one).
 template <int D, bool OUT_F32, bool RING>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingBwdSteps r) {
   using L = KvLds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
+  __shared__ __attribute__((aligned(1024))) char smem[L::ring];
   __shared__ int s_item;
-  static_assert(kKvWaves * 32 * L::epiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
   const int kg = wave % kKeyGroups;
   const bool dk_role = wave < kKeyGroups;  // else the dV role
   const float c = a.scale_log2;
+  constexpr float kNegLog2e = -1.4426950408889634f;
   const __bf16* Kb = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* Vb = reinterpret_cast<const __bf16*>(a.v);
   // a ring tile's step, kept inside the launch's step table
   auto step_of = [&](const lb_plan_tile* T) -> int {
     return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
+  };
+
+  // Per-lane LDS offsets inside a tile.  Row fragment kk (A operand of S or dP): row l32 of
+  // the 32-row block, logical chunk 2 kk + hh.  Transposed fragment (A operand of dK^T or
+  // dV^T), half q of column block db: the lane's 16-lane group supplies 4 rows x 16 columns,
+  // this lane's address being row 8 q + 4 hh + (lane % 16) / 4 of the 16-row block and
+  // columns 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3.
+  const int sw_r = swz<D>(l32);
+  const int lg = lane & 15, gq = (lane >> 4) & 1;
+  auto row_frag = [&](const char* tile, int sb, int kk) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(tile + (sb * 32 + l32) * L::rowBytes + (((2 * kk + hh) ^ sw_r) << 4));
+  };
+  auto tr_frag = [&](const char* tile, int sb, int ks, int db) -> bf16x8 {
+    bf16x4 h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = sb * 32 + ks * 16 + 8 * q + 4 * hh + (lg >> 2);
+      const int col = db * 32 + 16 * gq + 4 * (lg & 3);
+      const char* p = tile + row * L::rowBytes + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+      h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    }
+    return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   QueuesT<RING> qs;
@@ -654,7 +738,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     }
   }
 
-  QdoLoader<D> ld;
   if (tid == 0) s_item = qs.pop();
   lds_barrier();
   int item = __builtin_amdgcn_readfirstlane(s_item);
@@ -665,7 +748,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     const int k_start = __builtin_amdgcn_readfirstlane(T->q_start);  // the tile's keys
     const int k_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int k_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
-    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    StageCursor cur;  // the stage being computed
+    cur.start(T);
     if (tid == 0) {
       ++my_items;
       my_pairs += T->cost * G;
@@ -701,42 +785,40 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-    // stages: for each span, each 64 rows, each head of the group
-    int n_stages = 0;
-    for (int s = 0; s < n_spans; ++s) n_stages += (span_of(T, s).len + kQB - 1) / kQB * G;
+    const int n_stages =
+        ((cur.sp.len + kQB - 1) / kQB + (cur.left >= 1 ? (cur.n1.len + kQB - 1) / kQB : 0) +
+         (cur.left >= 2 ? (cur.n2.len + kQB - 1) / kQB : 0) + (cur.left >= 3 ? (cur.n3.len + kQB - 1) / kQB : 0)) *
+        G;
     if (tid == 0) my_blocks += n_stages;
-    int cur_s = 0, off = 0, hs = 0;
-    Span cur = span_of(T, 0);
-    if (n_stages > 0) {
-      ld.load(a, cur.start + off, cur.len - off, g * G + hs, tid);
-      ld.store(smem, tid);
-    }
-    for (int it = 0; it < n_stages; ++it) {
-      lds_barrier();
-      // the stage after this one: next head, else next 64 rows, else next span
-      int n_hs = hs + 1, n_off = off, n_s = cur_s;
-      Span nxt = cur;
-      if (n_hs == G) {
-        n_hs = 0;
-        n_off += kQB;
-        if (n_off >= cur.len) {
-          n_off = 0;
-          ++n_s;
-          if (n_s < n_spans) nxt = span_of(T, n_s);
-        }
+    StageCursor nxt = cur;  // the next stage to copy in
+#pragma unroll
+    for (int k = 0; k < kKvStages - 1; ++k)
+      if (k < n_stages) {
+        issue_stage<D>(a, smem + k * L::stage, nxt, g, wave, lane);
+        nxt.next(G);
       }
-      const bool has_next = it + 1 < n_stages;
-      if (has_next) ld.load(a, nxt.start + n_off, nxt.len - n_off, g * G + n_hs, tid);
+    for (int it = 0; it < n_stages; ++it) {
+      // this wave's copies of stage `it` have landed once at most the younger stages' are
+      // outstanding; the barrier then makes every wave's copies visible, and tells that every
+      // wave is done with the slot the next copy goes to
+      const int younger = min(kKvStages - 2, n_stages - 1 - it);
+      if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L::dmaPerStage));
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::dmaPerStage));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      static_assert(kKvStages == 4, "the waits above cover two younger stages");
+      lds_barrier();
+      if (it + kKvStages - 1 < n_stages) {
+        issue_stage<D>(a, smem + ((it + kKvStages - 1) % kKvStages) * L::stage, nxt, g, wave, lane);
+        nxt.next(G);
+      }
 
-      const char* h = smem + (it & 1) * L::stage;
-      const char* qrows = h;
-      const char* dorows = h + L::rowsBytes;
-      const char* qt = h + 2 * L::rowsBytes;
-      const char* dot = qt + L::tBytes;
-      const float* lsep = reinterpret_cast<const float*>(dot + L::tBytes);
+      const char* h = smem + (it % kKvStages) * L::stage;
+      const char* qtile = h;
+      const char* dotile = h + L::tileBytes;
+      const float* lsep = reinterpret_cast<const float*>(h + 2 * L::tileBytes);
       const float* dvp = lsep + kQB;
-      const int rows_valid = min(kQB, cur.len - off);
-      const int row_pos0 = cur.pos0 + off;  // position of the stage's first row
+      const int rows_valid = min(kQB, cur.sp.len - cur.off);
+      const int row_pos0 = cur.sp.pos0 + cur.off;  // position of the stage's first row
 #pragma unroll
       for (int sb = 0; sb < kQB / 32; ++sb) {
         const int sb_rows = min(32, rows_valid - sb * 32);
@@ -748,15 +830,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
         const bool full = sb_pos0 >= wave_key_last;
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s = mfma(*reinterpret_cast<const bf16x8*>(qrows + (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2),
-                   kfr[kk], s);
+        for (int kk = 0; kk < D / 16; ++kk) s = mfma(row_frag(qtile, sb, kk), kfr[kk], s);
         if (dk_role) {
           f32x16 dp = f32x16{};
 #pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk)
-            dp = mfma(*reinterpret_cast<const bf16x8*>(dorows + (sb * 32 + l32) * L::rStride + (kk * 16 + hh * 8) * 2),
-                      vfr[kk], dp);
+          for (int kk = 0; kk < D / 16; ++kk) dp = mfma(row_frag(dotile, sb, kk), vfr[kk], dp);
           bf16x8 dsf[2];
           auto make_ds = [&](auto masked) {
 #pragma unroll
@@ -767,7 +845,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
               for (int j = 0; j < 4; ++j) {
                 const int i = i4 * 4 + j;
                 const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f;
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, lv[j] * kNegLog2e)) : 0.f;
                 dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
               }
             }
@@ -777,10 +855,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-              acc[db] = mfma(*reinterpret_cast<const bf16x8*>(qt + (db * 32 + l32) * L::tStride +
-                                                               (sb * 32 + ks * 16 + hh * 8) * 2),
-                             dsf[ks], acc[db]);
+            for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_frag(qtile, sb, ks, db), dsf[ks], acc[db]);
         } else {
           bf16x8 pf[2];
           auto make_p = [&](auto masked) {
@@ -791,7 +866,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
               for (int j = 0; j < 4; ++j) {
                 const int i = i4 * 4 + j;
                 const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
-                pf[i / 8][i % 8] = (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lv[j])) : 0.f);
+                pf[i / 8][i % 8] =
+                    (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, lv[j] * kNegLog2e)) : 0.f);
               }
             }
           };
@@ -800,33 +876,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-              acc[db] = mfma(*reinterpret_cast<const bf16x8*>(dot + (db * 32 + l32) * L::tStride +
-                                                               (sb * 32 + ks * 16 + hh * 8) * 2),
-                             pf[ks], acc[db]);
+            for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_frag(dotile, sb, ks, db), pf[ks], acc[db]);
         }
       }
-      if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
-      cur = nxt;
-      cur_s = n_s;
-      off = n_off;
-      hs = n_hs;
+      cur.next(G);
     }
 
-    // epilogue: dK = scale * dK^T, dV = dV^T, each role its own tensor
+    // epilogue: dK = scale * dK^T, dV = dV^T, each role its own tensor, staged in the ring
     lds_barrier();
     {
-      char* ebuf = smem + wave * 32 * L::epiStride;
+      char* ebuf = smem + wave * L::epiRows * L::epiStride;
       const int rows = max(0, min(32, k_len - kg * 32));
       const int64_t elt = OUT_F32 ? 4 : 2;
       const int64_t row_step = (int64_t)a.kv_heads * D * elt;
       const int64_t first = (((int64_t)k_start + kg * 32) * a.kv_heads + g) * D * elt;
-      stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc, dk_role ? a.scale : 1.0f, lane);
-      __builtin_amdgcn_wave_barrier();
       void* grad = dk_role ? a.dk : a.dv;
       if constexpr (RING) grad = dk_role ? r.dk[step] : r.dv[step];
-      store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(grad) + first,
-                                     row_step, rows, lane);
+#pragma unroll
+      for (int r_lo = 0; r_lo < 32; r_lo += L::epiRows) {
+        __builtin_amdgcn_wave_barrier();
+        stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc, dk_role ? a.scale : 1.0f, lane, r_lo, L::epiRows);
+        __builtin_amdgcn_wave_barrier();
+        store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(grad) + first + r_lo * row_step,
+                                       row_step, max(0, min(L::epiRows, rows - r_lo)), lane);
+      }
     }
     lds_barrier();
     if (tid == 0) s_item = qs.pop();
