@@ -12,17 +12,15 @@
 //   * dQ, query-stationary, over the forward's query tiles and wave layout (8 waves,
 //     two per SIMD, each 32 rows of one head): per 64-key block, S^T = K Q^T and
 //     dP^T = V dO^T (K and V rows from LDS, Q and dO held in registers), then
-//     dQ^T += K^T dS^T with K^T from LDS.
+//     dQ^T += K^T dS^T with K^T read transposed from the same LDS rows.
 //   * dK/dV, key-stationary, over key tiles whose spans are the query rows that see
-//     them (the transposed plan): per block of 32 query rows and head,
-//     S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V held in
-//     registers), then dV^T += dO^T P and dK^T += Q^T dS.  The heads of a kv group
-//     add into the same accumulators, so no reduction over heads follows.
-// The dK/dV kernel's waves run alone on their SIMDs (4 waves per workgroup) and may
-// hold 512 registers: two stationary operand sets and two accumulators stay live.
-// Transposed operands (K^T, Q^T, dO^T) are written to LDS by the loader with the
-// index permutation that lets the other MFMA operand come straight from an
-// accumulator (the forward's V^T layout).
+//     them (the transposed plan), in producer/consumer wave pairs: per block of 32
+//     query rows and head, the producer computes S = Q K^T and dP = dO V^T (Q and dO
+//     rows from LDS, K and V held in registers) and from them P and dS; the consumer
+//     accumulates dV^T += dO^T P and dK^T += Q^T dS a block later.  The heads of a kv
+//     group add into the same accumulators, so no reduction over heads follows.
+// Both stream their row tiles through LDS rings filled by direct global->LDS copies;
+// the transposed operands come from gfx950's LDS transpose load.
 #include "lbattn_internal.h"
 
 namespace lb {
@@ -46,10 +44,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BN = kBlockN;  // keys per block of the dQ kernel
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
-constexpr int kQB = 64;      // query rows per stage of the dK/dV kernel (two MFMA blocks of 32)
+constexpr int kQB = 32;      // query rows per stage of the dK/dV kernel (one MFMA block)
 constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ int vt_pos(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -65,10 +61,6 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Two bf16 values of one 16-byte chunk pair, interleaved for a transposed row: the
-// words for elements 2m and 2m + 1 of two consecutive source rows.
-__device__ __forceinline__ uint32_t pair_lo(uint32_t x0, uint32_t x1) { return (x0 & 0xFFFFu) | (x1 << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t x0, uint32_t x1) { return (x0 >> 16) | (x1 & 0xFFFF0000u); }
 
 // ------------------------------------------------------------------------------------
 // The plan and its queues (same format and protocol as the forward's)
@@ -263,83 +255,177 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const void* out, const void
 }
 
 // ------------------------------------------------------------------------------------
-// dQ: query-stationary
+// Staging through LDS (both gradient kernels)
 // ------------------------------------------------------------------------------------
+// Row tiles (keys for dQ, query rows for dK/dV) are copied from global memory straight into
+// LDS by the buffer loads' LDS mode: no registers, no stores, several stages in flight in a
+// ring.  A tile is stored row-major and unpadded, each row's 16-byte chunks XOR-permuted by
+// the row (swz), and serves both MFMA operand shapes: row fragments (8 consecutive d of one
+// row) for the products that contract over d, and transposed fragments (one d column of 8
+// rows) for those that contract over the rows, read with gfx950's LDS transpose load
+// (ds_read_b64_tr_b16: each lane receives one column of 4 rows, the 16 lanes of a group
+// supplying the 4 x 16 block's row addresses).
+// The chunk permutation of row r (r mod 16 decides it).  Row reads: 16 lanes read one
+// logical chunk of 16 consecutive rows, which land on 16 distinct chunk slots (d = 128) or on
+// 8 slots in each bank half (d = 64: two rows per 256 bytes).  Transpose reads: 32 lanes read
+// four logical chunks (a 64-byte run) of 4 consecutive rows, which land on 4 disjoint runs.
 template <int D>
-struct DqLds {
-  static constexpr int kStride = D * 2 + 16;  // K or V row
-  static constexpr int tStride = BN * 2 + 16; // K^T row (one d, the block's keys)
-  static constexpr int rowsBytes = BN * kStride;
-  static constexpr int tBytes = D * tStride;
-  static constexpr int stage = 2 * rowsBytes + tBytes;  // K rows, V rows, K^T
-  static constexpr int kUnits = (BN / 2) * (D / 8);     // (key pair, 16-byte chunk) units of K
-  static constexpr int kPerThread = (kUnits + kDqThreads - 1) / kDqThreads;  // the last one partial at d = 64
-  static constexpr int vChunks = BN * (D / 8);
-  static constexpr int vPerThread = vChunks / kDqThreads;
-  static constexpr int epiStride = D * 4 + 16;
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }  // s_waitcnt vmcnt(n) only
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + nbytes): reads past the end return zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+               __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)), __builtin_amdgcn_readfirstlane(nbytes),
+               kBufferFlags};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (int)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Copies global -> LDS without registers: lane i's 16 (or 4) bytes at voffset land at
+// lds + 16 i (or 4 i).  Written as inline assembly on purpose: the compiler, seeing the
+// builtin's LDS write, would wait for every copy in flight before each LDS read of the loop;
+// the kernel waits for its copies itself (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Row fragment: 8 consecutive d (logical chunk `chunk`) of row `row` of a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * (D * 2) + ((chunk ^ swz<D>(row)) << 4));
+}
+
+// Transposed fragment (the A operand of an MFMA contracting over rows): for the lane's
+// column d = 32 db + lane % 32, rows r0 + 8 t' + 4 hh + j (t' = 0, 1; j = 0..3) as elements
+// 4 t' + j, hh = lane / 32.  Each half is one transpose load: in a group of 16 lanes, lane i
+// supplies row r0 + 8 t' + 4 hh + i / 4 at columns 32 db + 16 (group % 2) + 4 (i % 4).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int db, int lane) {
+  const int lg = lane & 15, gq = (lane >> 4) & 1, hh = lane >> 5;
+  const int col = db * 32 + 16 * gq + 4 * (lg & 3);
+  bf16x4 h[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = r0 + 8 * q + 4 * hh + (lg >> 2);
+    const char* p = tile + row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+    h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  }
+  return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Issues the copy of rows [r0, r0 + 64) (the first `valid` of them real, the rest read as
+// zeros) of one head of a [row][heads][D] tensor into a 64-row tile, spread over 8 waves:
+// every wave issues the same count, copies64_per_wave<D>().
+template <int D>
+constexpr int copies64_per_wave() { return 64 * D * 2 / 1024 / 8; }
+template <int D>
+__device__ __forceinline__ void issue_tile64(const void* src, int64_t row_step, int r0, int valid, int head,
+                                             uint32_t lds, int wave, int lane) {
+  constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2);
+  const char* base = reinterpret_cast<const char*>(src) + (int64_t)r0 * row_step + (int64_t)head * D * 2;
+  const i32x4 rs = buffer_rsrc(base, valid * (int)row_step);
+#pragma unroll
+  for (int j = 0; j < copies64_per_wave<D>(); ++j) {
+    const int blk = wave * copies64_per_wave<D>() + j;  // the 1 KB piece of the tile
+    const int row = blk * kRowsPerCopy + lane / kChunks;
+    const int chunk = (lane % kChunks) ^ swz<D>(row);   // lane writes slot lane % kChunks of its row
+    copy16_to_lds(rs, lds + blk * 1024, row * (int)row_step + chunk * 16);
+  }
+}
+
+// s_waitcnt vmcnt(k * per) for k = min(2, younger) stages still allowed in flight
+__device__ __forceinline__ void wait_stage(int younger, int per) {
+  if (younger >= 2) {
+    if (per == 5) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+    else if (per == 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    else if (per == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+  } else if (younger == 1) {
+    if (per == 5) __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
+    else if (per == 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+    else if (per == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
+// Walks a tile's spans in blocks of `step` rows, `reps` passes per block (heads).  The
+// cursor carries the spans still ahead of it, read once per item into uniform registers and
+// shifted forward, never indexed: the loop that walks them then issues no memory read (a
+// vector or scratch read there would wait for every copy in flight).
+struct SpanCursor {
+  int off, rep, left;  // left: spans after the current one
+  Span sp, n1, n2, n3;
+  __device__ __forceinline__ void start(const lb_plan_tile* T) {
+    static_assert(LB_MAX_SPANS == 4, "the cursor holds up to four spans");
+    off = rep = 0;
+    left = __builtin_amdgcn_readfirstlane(T->n_spans) - 1;
+    sp = span_of(T, 0);
+    n1 = span_of(T, 1);
+    n2 = span_of(T, 2);
+    n3 = span_of(T, 3);
+  }
+  // blocks of `step` rows over all spans (the span count is at least 1)
+  __device__ __forceinline__ int blocks(int step) const {
+    return (sp.len + step - 1) / step + (left >= 1 ? (n1.len + step - 1) / step : 0) +
+           (left >= 2 ? (n2.len + step - 1) / step : 0) + (left >= 3 ? (n3.len + step - 1) / step : 0);
+  }
+  __device__ __forceinline__ void next(int step, int reps) {
+    if (++rep == reps) {
+      rep = 0;
+      off += step;
+      if (off >= sp.len && left > 0) {
+        off = 0;
+        --left;
+        sp = n1;
+        n1 = n2;
+        n2 = n3;
+      }
+    }
+  }
 };
 
+// ------------------------------------------------------------------------------------
+// dQ: query-stationary
+// ------------------------------------------------------------------------------------
+constexpr int kDqStages = 4;  // LDS ring depth of the dQ kernel
+
 template <int D>
-struct DqLoader {
-  using L = DqLds<D>;
-  u32x4 kr[L::kPerThread][2];
-  u32x4 vr[L::vPerThread];
-
-  __device__ __forceinline__ void load(const char* K, const char* V, int k0, int valid, int row_bytes, int g,
-                                       int tid) {
-    const int64_t base = (int64_t)k0 * row_bytes + (int64_t)g * D * 2;
-    const int nbytes = min(valid, BN) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, nbytes,
-                                                                        kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, nbytes,
-                                                                        kBufferFlags);
-#pragma unroll
-    for (int e = 0; e < L::kPerThread; ++e) {
-      const int u = tid + e * kDqThreads, p = u % (BN / 2), ch = u / (BN / 2);
-      if (L::kUnits % kDqThreads == 0 || u < L::kUnits) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-          kr[e][x] = __builtin_amdgcn_raw_buffer_load_b128(rk, (2 * p + x) * row_bytes + ch * 16, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < L::vPerThread; ++e) {
-      const int c = tid + e * kDqThreads, row = c / (D / 8), ch = c % (D / 8);
-      vr[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * row_bytes + ch * 16, 0, 0);
-    }
-  }
-
-  __device__ __forceinline__ void store(char* stage, int tid) {
-    char* ks = stage;
-    char* vs = stage + L::rowsBytes;
-    char* kt = stage + 2 * L::rowsBytes;
-#pragma unroll
-    for (int e = 0; e < L::kPerThread; ++e) {
-      const int u = tid + e * kDqThreads, p = u % (BN / 2), ch = u / (BN / 2);
-      if (!(L::kUnits % kDqThreads == 0 || u < L::kUnits)) continue;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(ks + (2 * p + x) * L::kStride + ch * 16) = kr[e][x];
-      const int col = vt_pos(2 * p) * 2;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        *reinterpret_cast<uint32_t*>(kt + (ch * 8 + 2 * m) * L::tStride + col) = pair_lo(kr[e][0][m], kr[e][1][m]);
-        *reinterpret_cast<uint32_t*>(kt + (ch * 8 + 2 * m + 1) * L::tStride + col) = pair_hi(kr[e][0][m], kr[e][1][m]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < L::vPerThread; ++e) {
-      const int c = tid + e * kDqThreads, row = c / (D / 8), ch = c % (D / 8);
-      *reinterpret_cast<u32x4*>(vs + row * L::kStride + ch * 16) = vr[e];
-    }
-  }
+struct DqLds {
+  static constexpr int tileBytes = BN * D * 2;  // 64 keys of K or V
+  static constexpr int stage = 2 * tileBytes;   // K, V
+  static constexpr int copiesPerStage = 2 * copies64_per_wave<D>();
+  static constexpr int ring = kDqStages * stage;
+  static_assert(BN == 64, "a stage is one 64-row tile per tensor");
 };
 
 template <int D, int HPW, bool OUT_F32>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using L = DqLds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
+  __shared__ __attribute__((aligned(1024))) char smem[L::ring];
   __shared__ int s_item;
-  static_assert(kDqWaves * 32 * (D * 2 + 16) <= 2 * L::stage, "epilogue staging must fit in the ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
@@ -347,9 +433,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int rg = wave % RG, hgi = wave / RG;
   const int wr0 = rg * 32;
   const float c = a.scale_log2;
-  const int row_bytes = a.kv_heads * D * 2;
-  const char* Kb = reinterpret_cast<const char*>(a.k);
-  const char* Vb = reinterpret_cast<const char*>(a.v);
+  const int64_t row_bytes = (int64_t)a.kv_heads * D * 2;
   const __bf16* Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* dO = reinterpret_cast<const __bf16*>(a.dout);
 
@@ -358,7 +442,6 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   uint64_t t_start = tid == 0 ? device_clock() : 0;
   int my_items = 0, my_blocks = 0;
   int64_t my_pairs = 0;
-  DqLoader<D> ld;
 
   if (tid == 0) s_item = qs.pop();
   lds_barrier();
@@ -370,9 +453,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
-    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
-    int n_blocks = 0;
-    for (int s = 0; s < n_spans; ++s) n_blocks += (span_of(T, s).len + BN - 1) / BN;
+    SpanCursor cur;  // the key block being computed
+    cur.start(T);
+    const int n_blocks = cur.blocks(BN);
     if (tid == 0) {
       my_blocks += n_blocks;
       ++my_items;
@@ -410,34 +493,38 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int db = 0; db < D / 32; ++db) acc[e][db] = f32x16{};
     }
 
-    int cur_s = 0;
-    Span cur = span_of(T, 0);
-    int key0 = 0;
-    if (n_blocks > 0) {
-      ld.load(Kb, Vb, cur.start, cur.len, row_bytes, g, tid);
-      ld.store(smem, tid);
-    }
+    // the rows' operands are in registers before any copy goes out: a wait for them inside the
+    // loop would also wait for every copy in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    SpanCursor nxt = cur;  // the next key block to copy in
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int slot) {
+      const int k0 = __builtin_amdgcn_readfirstlane(nxt.sp.start + nxt.off);
+      const int valid = __builtin_amdgcn_readfirstlane(max(0, min(nxt.sp.len - nxt.off, BN)));
+      const uint32_t lds = lds_addr(smem + slot * L::stage);
+      issue_tile64<D>(a.k, row_bytes, k0, valid, g, lds, w, lane);
+      issue_tile64<D>(a.v, row_bytes, k0, valid, g, lds + L::tileBytes, w, lane);
+      nxt.next(BN, 1);
+    };
+#pragma unroll
+    for (int k = 0; k < kDqStages - 1; ++k)
+      if (k < n_blocks) issue(k);
     for (int it = 0; it < n_blocks; ++it) {
+      // as in the dK/dV kernel: this wave's copies of block `it` have landed, the barrier
+      // publishes every wave's and frees the slot the next copy goes to
+      static_assert(kDqStages == 4, "wait_stage covers two younger stages");
+      wait_stage(min(kDqStages - 2, n_blocks - 1 - it), L::copiesPerStage);
       lds_barrier();
-      // the block after this one
-      Span nxt = cur;
-      int nkey0 = key0 + BN, nx_s = cur_s;
-      if (nkey0 >= cur.len) {
-        ++nx_s;
-        nkey0 = 0;
-        if (nx_s < n_spans) nxt = span_of(T, nx_s);
-      }
-      const bool has_next = it + 1 < n_blocks;
-      if (has_next) ld.load(Kb, Vb, nxt.start + nkey0, nxt.len - nkey0, row_bytes, g, tid);
-      const char* stage = smem + (it & 1) * L::stage;
-      const char* ks = stage;
-      const char* vs = stage + L::rowsBytes;
-      const char* kt = stage + 2 * L::rowsBytes;
-      const bool live = wave_rows && cur.pos0 + key0 <= q_pos0 + wave_last;
+      if (it + kDqStages - 1 < n_blocks) issue((it + kDqStages - 1) % kDqStages);
+      const char* ks = smem + (it % kDqStages) * L::stage;
+      const char* vs = ks + L::tileBytes;
+      const Span cs = cur.sp;
+      const int key0 = cur.off;
+      const bool live = wave_rows && cs.pos0 + key0 <= q_pos0 + wave_last;
       if (live) {
         // visible iff the key's position <= the row's, and the key lies in its span
-        const bool full = key0 + BN <= cur.len && cur.pos0 + key0 + BN - 1 <= q_pos0 + wr0;
-        const int lim = min(cur.len, qpos - cur.pos0 + 1) - key0 - hh * 4;
+        const bool full = key0 + BN <= cs.len && cs.pos0 + key0 + BN - 1 <= q_pos0 + wr0;
+        const int lim = min(cs.len, qpos - cs.pos0 + 1) - key0 - hh * 4;
         // head by head: the operand fragments are read again for the second head rather
         // than holding two heads' S^T and dP^T at once
 #pragma unroll
@@ -450,10 +537,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-              const bf16x8 kf =
-                  *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * L::kStride + (kk * 16 + hh * 8) * 2);
-              const bf16x8 vf =
-                  *reinterpret_cast<const bf16x8*>(vs + (kb * 32 + l32) * L::kStride + (kk * 16 + hh * 8) * 2);
+              const bf16x8 kf = row_frag<D>(ks, kb * 32 + l32, 2 * kk + hh);
+              const bf16x8 vf = row_frag<D>(vs, kb * 32 + l32, 2 * kk + hh);
               s[kb] = mfma(kf, qreg[e][kk], s[kb]);
               dp[kb] = mfma(vf, doreg[e][kk], dp[kb]);
             }
@@ -476,25 +561,19 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int ks16 = 0; ks16 < 4; ++ks16)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const bf16x8 tf =
-                  *reinterpret_cast<const bf16x8*>(kt + (db * 32 + l32) * L::tStride + (ks16 * 16 + hh * 8) * 2);
-              acc[e][db] = mfma(tf, dsf[ks16], acc[e][db]);
-            }
+            for (int db = 0; db < D / 32; ++db)
+              acc[e][db] = mfma(tr_frag<D>(ks, ks16 * 16, db, lane), dsf[ks16], acc[e][db]);
         }
       }
-      if (has_next) ld.store(smem + ((it + 1) & 1) * L::stage, tid);
-      cur = nxt;
-      cur_s = nx_s;
-      key0 = nkey0;
+      cur.next(BN, 1);
     }
 
     // epilogue: dQ = scale * dQ^T, staged row-major per wave, head by head (fp32 rows in two
     // passes of 16 where 32 rows of every wave do not fit in the ring)
     lds_barrier();
     constexpr int kEpiStride = OUT_F32 ? D * 4 + 16 : D * 2 + 16;
-    constexpr int kPassRows = kDqWaves * 32 * kEpiStride <= 2 * L::stage ? 32 : 16;
-    static_assert(kDqWaves * kPassRows * kEpiStride <= 2 * L::stage, "epilogue staging must fit in the ring");
+    constexpr int kPassRows = kDqWaves * 32 * kEpiStride <= L::ring ? 32 : 16;
+    static_assert(kDqWaves * kPassRows * kEpiStride <= L::ring, "epilogue staging must fit in the ring");
     char* ebuf = smem + wave * kPassRows * kEpiStride;
     const int64_t row_step = (int64_t)a.heads * D * (OUT_F32 ? 4 : 2);
 #pragma unroll
@@ -505,7 +584,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_wave_barrier();
         stage_rows<D, OUT_F32>(ebuf, kEpiStride, acc[e], a.scale, lane, r_lo, kPassRows);
         __builtin_amdgcn_wave_barrier();
-        char* dst = reinterpret_cast<char*>(a.dq) + (((int64_t)q_start + wr0 + r_lo) * a.heads + head) * D * (OUT_F32 ? 4 : 2);
+        char* dst = reinterpret_cast<char*>(a.dq) +
+                    (((int64_t)q_start + wr0 + r_lo) * a.heads + head) * D * (OUT_F32 ? 4 : 2);
         const int rows = max(0, min(kPassRows, q_len - wr0 - r_lo));
         store_rows<D, OUT_F32 ? 2 : 0>(ebuf, kEpiStride, dst, row_step, rows, lane);
       }
@@ -519,149 +599,71 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: key-stationary, waves split by role
+// dK, dV: key-stationary, producer and consumer waves
 // ------------------------------------------------------------------------------------
-// A tile of 128 keys; 8 waves, two per SIMD.  Waves 0-3 (one per 32 keys) hold K and V and
-// accumulate dK^T = sum Q^T dS (S and dP recomputed); waves 4-7 hold K and accumulate
-// dV^T = sum dO^T P (S recomputed).  Each runs every head of the kv group, so no reduction
-// over heads or waves follows, and each fits in 256 registers.  Query rows stream in
-// stages of 64 (two MFMA blocks of 32), one head per stage, through a ring of kKvStages
-// LDS stages that both roles read, kKvStages - 1 of them in flight.
+// A tile of 128 keys; 8 waves, two per SIMD, in pairs that own 32 keys each.  The producer of
+// a pair (waves 0-3) holds its keys' K and V and, per block of 32 query rows of one head,
+// computes S = Q K^T and dP = dO V^T, then P = exp(S - lse) and dS = P (dP - D), which it
+// leaves in LDS as bf16 in the layout of an MFMA B operand.  The consumer (waves 4-7) takes
+// them one block later and accumulates both dV^T = sum dO^T P and dK^T = sum Q^T dS.  Each
+// block costs both waves of a SIMD the same 16 MFMAs.  The heads of the kv group add into the
+// same accumulators, so no reduction over heads or waves follows.
 //
-// A stage holds the 64 Q rows and 64 dO rows row-major, copied from global memory straight
-// into LDS by the buffer loads' LDS mode (no registers, no stores), and the rows' raw lse
-// and D.  The row-major tiles serve both products: S = Q K^T and dP = dO V^T read row
-// fragments, and dK^T += Q^T dS and dV^T += dO^T P read the transposed fragments with
-// gfx950's LDS transpose load (ds_read_b64_tr_b16), which hands each lane one d column of
-// 4 rows.  Each row's 16-byte chunks are stored XOR-permuted by the row (swz) so that both
-// kinds of read hit 64 distinct banks per pass.
+// Query rows stream in stages of 32 rows of one head through a ring of kKvStages LDS slots:
+// at stage i the producers read slot i, the consumers slot i - 1, and the copy of stage i + 2
+// goes into slot i + 2 (the consumers left it at stage i - 1).  A stage holds the 32 Q rows and
+// 32 dO rows (swizzled row tiles) and the rows' raw lse and D; P and dS go through two slots
+// of their own.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kKeyGroups = 4;  // 32 keys each: 128 keys per tile
+constexpr int kKeyGroups = kBwdKeyGroups;  // 32 keys each: 128 keys per tile
 constexpr int kKvStages = 4;   // LDS ring depth
 
 template <int D>
 struct KvLds {
-  static constexpr int rowBytes = D * 2;              // one Q or dO row, unpadded
-  static constexpr int chunks = D / 8;                 // 16-byte chunks per row
-  static constexpr int tileBytes = kQB * rowBytes;     // 64 rows of one tensor
+  static constexpr int tileBytes = kQB * D * 2;              // 32 rows of one tensor
   static constexpr int stage = 2 * tileBytes + 2 * kQB * 4;  // Q, dO; raw lse, D
-  static constexpr int rowsPerDma = 1024 / rowBytes;   // rows one wave's 16-byte-per-lane copy covers
-  static constexpr int dmaPerTensor = kQB / rowsPerDma / kKvWaves;  // copies per wave per tensor
-  static constexpr int dmaPerStage = 2 * dmaPerTensor + 1;          // + one for lse or D
+  static constexpr int copies = 2 * tileBytes / 1024 / kKvWaves;  // row copies per wave per stage
+  static constexpr int copiesPerStage = copies + 1;                // + lse or D
   static constexpr int ring = kKvStages * stage;
+  static constexpr int xBytes = 2048;                    // one B operand block: 64 lanes x 2 x 16 bytes
+  static constexpr int xSlot = kKeyGroups * 2 * xBytes;  // P and dS of every key group
+  static constexpr int total = ring + 2 * xSlot;
   static constexpr int epiStride = D * 4 + 16;
-  static constexpr int epiRows = kKvWaves * 32 * epiStride <= ring ? 32 : 16;  // rows per epilogue pass
-  static_assert(kQB % (rowsPerDma * kKvWaves) == 0, "the copies must divide evenly over the waves");
-  static_assert(kKvWaves * epiRows * epiStride <= ring, "epilogue staging must fit in the ring");
+  static_assert(2 * tileBytes % (1024 * kKvWaves) == 0, "the row copies must divide evenly over the waves");
+  static_assert(kKeyGroups * 32 * epiStride <= total, "epilogue staging must fit in the kernel's LDS");
 };
 
-// The chunk permutation of row r (r mod 16 decides it).  Row reads: 16 lanes read one
-// logical chunk of 16 consecutive rows, which land on 16 distinct chunk slots (d = 128) or on
-// 8 slots in each bank half (d = 64: two rows per 256 bytes).  Transpose reads: 32 lanes read
-// four logical chunks (a 64-byte run) of 4 consecutive rows, which land on 4 disjoint runs.
+// Copies the stage at cursor `c` (32 rows of one head from row sp.start + off) into `buf`:
+// every wave issues copiesPerStage copies (the same count in every wave, so that the vmcnt
+// waits are uniform).  Rows past the span's end read as zeros, and so do their lse and D.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }  // s_waitcnt vmcnt(n) only
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + nbytes): reads past the end return zeros.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int nbytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
-               __builtin_amdgcn_readfirstlane(nbytes), kBufferFlags};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (int)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// Copies global -> LDS without registers: lane i's 16 (or 4) bytes at voffset land at
-// lds + 16 i (or 4 i).  Written as inline assembly on purpose: the compiler, seeing the
-// builtin's LDS write, would wait for every copy in flight before each LDS read of the loop;
-// the kernel waits for its copies itself (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-
-// The stages of one key tile: for each span, each 64 rows, each head of the group.  The
-// cursor carries the spans still ahead of it, read once per item into uniform registers and
-// shifted forward, never indexed: the loop that walks them then issues no memory read (a
-// vector or scratch read there would wait for every copy in flight).
-struct StageCursor {
-  int off, hs, left;  // left: spans after the current one
-  Span sp, n1, n2, n3;
-  __device__ __forceinline__ void start(const lb_plan_tile* T) {
-    static_assert(LB_MAX_SPANS == 4, "the cursor holds up to four spans");
-    off = hs = 0;
-    left = __builtin_amdgcn_readfirstlane(T->n_spans) - 1;
-    sp = span_of(T, 0);
-    n1 = span_of(T, 1);
-    n2 = span_of(T, 2);
-    n3 = span_of(T, 3);
-  }
-  __device__ __forceinline__ void next(int G) {
-    if (++hs == G) {
-      hs = 0;
-      off += kQB;
-      if (off >= sp.len && left > 0) {
-        off = 0;
-        --left;
-        sp = n1;
-        n1 = n2;
-        n2 = n3;
-      }
-    }
-  }
-};
-
-// Copies stage `c` (64 rows of one head from row sp.start + off) into `buf`: every wave issues
-// dmaPerStage copies (the same count in every wave, so that vmcnt waits are uniform).  Rows
-// past the span's end read as zeros (the buffer range ends there), and so do their lse and D.
-template <int D>
-__device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const StageCursor& c, int g, int wave,
+__device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const SpanCursor& c, int g, int wave,
                                             int lane) {
   using L = KvLds<D>;
-  const int head = __builtin_amdgcn_readfirstlane(g * a.group + c.hs);
+  constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2), kBlocksPerTile = L::tileBytes / 1024;
+  const int head = __builtin_amdgcn_readfirstlane(g * a.group + c.rep);
   const int r0 = __builtin_amdgcn_readfirstlane(c.sp.start + c.off);
   const int valid = __builtin_amdgcn_readfirstlane(max(0, min(c.sp.len - c.off, kQB)));
   const int w = __builtin_amdgcn_readfirstlane(wave);
-  const int row_step = a.heads * D * 2;
+  const int64_t row_step = (int64_t)a.heads * D * 2;
   const uint32_t lds = lds_addr(buf);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int j = 0; j < L::copies; ++j) {
+    const int blk = w * L::copies + j;  // the 1 KB piece of the Q and dO tiles
+    const int t = blk / kBlocksPerTile, tb = blk % kBlocksPerTile;
     const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
                        (int64_t)head * D * 2;
-    const i32x4 rs = buffer_rsrc(base, valid * row_step);
-#pragma unroll
-    for (int j = 0; j < L::dmaPerTensor; ++j) {
-      const int blk = w * L::dmaPerTensor + j;  // the 1 KB piece of the tile
-      const int row = blk * L::rowsPerDma + lane / L::chunks;
-      const int chunk = (lane % L::chunks) ^ swz<D>(row);  // lane writes slot lane % chunks of its row
-      copy16_to_lds(rs, lds + t * L::tileBytes + blk * 1024, row * row_step + chunk * 16);
-    }
+    const i32x4 rs = buffer_rsrc(base, valid * (int)row_step);
+    const int row = tb * kRowsPerCopy + lane / kChunks;
+    const int chunk = (lane % kChunks) ^ swz<D>(row);  // lane writes slot lane % kChunks of its row
+    copy16_to_lds(rs, lds + blk * 1024, row * (int)row_step + chunk * 16);
   }
-  // lse (even waves) or D (odd waves), 16 rows per wave, 4 bytes per lane
+  // lse (even waves) or D (odd waves), 8 rows per wave, 4 bytes per lane
   const float* vec = (w & 1) ? a.dvec : a.lse;
-  const int q16 = w >> 1;
+  const int q8 = w >> 1;
   const i32x4 rv = buffer_rsrc(vec + (int64_t)head * a.n_q + r0, valid * 4);
-  if (lane < 16) copy4_to_lds(rv, lds + 2 * L::tileBytes + (w & 1) * kQB * 4 + q16 * 64, (q16 * 16 + lane) * 4);
+  if (lane < 8) copy4_to_lds(rv, lds + 2 * L::tileBytes + (w & 1) * kQB * 4 + q8 * 32, (q8 * 8 + lane) * 4);
 }
 
 // RING: a ring workspace of several steps' key tiles; a tile's step selects the keys, values
@@ -670,13 +672,14 @@ __device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const S
 template <int D, bool OUT_F32, bool RING>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingBwdSteps r) {
   using L = KvLds<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[L::ring];
+  __shared__ __attribute__((aligned(1024))) char smem[L::total];
   __shared__ int s_item;
+  char* xbuf = smem + L::ring;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
   const int kg = wave % kKeyGroups;
-  const bool dk_role = wave < kKeyGroups;  // else the dV role
+  const bool producer = wave < kKeyGroups;
   const float c = a.scale_log2;
   constexpr float kNegLog2e = -1.4426950408889634f;
   const __bf16* Kb = reinterpret_cast<const __bf16*>(a.k);
@@ -684,28 +687,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
   // a ring tile's step, kept inside the launch's step table
   auto step_of = [&](const lb_plan_tile* T) -> int {
     return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
-  };
-
-  // Per-lane LDS offsets inside a tile.  Row fragment kk (A operand of S or dP): row l32 of
-  // the 32-row block, logical chunk 2 kk + hh.  Transposed fragment (A operand of dK^T or
-  // dV^T), half q of column block db: the lane's 16-lane group supplies 4 rows x 16 columns,
-  // this lane's address being row 8 q + 4 hh + (lane % 16) / 4 of the 16-row block and
-  // columns 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3.
-  const int sw_r = swz<D>(l32);
-  const int lg = lane & 15, gq = (lane >> 4) & 1;
-  auto row_frag = [&](const char* tile, int sb, int kk) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(tile + (sb * 32 + l32) * L::rowBytes + (((2 * kk + hh) ^ sw_r) << 4));
-  };
-  auto tr_frag = [&](const char* tile, int sb, int ks, int db) -> bf16x8 {
-    bf16x4 h[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = sb * 32 + ks * 16 + 8 * q + 4 * hh + (lg >> 2);
-      const int col = db * 32 + 16 * gq + 4 * (lg & 3);
-      const char* p = tile + row * L::rowBytes + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
-      h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    }
-    return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   QueuesT<RING> qs;
@@ -748,7 +729,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     const int k_start = __builtin_amdgcn_readfirstlane(T->q_start);  // the tile's keys
     const int k_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int k_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
-    StageCursor cur;  // the stage being computed
+    SpanCursor cur;  // the block the producers compute
     cur.start(T);
     if (tid == 0) {
       ++my_items;
@@ -765,140 +746,150 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     const int my_key = kg * 32 + l32;
     const bool key_real = my_key < k_len;
     const int kpos = k_pos0 + my_key;
-    const int wave_key_last = k_pos0 + min(kg * 32 + 32, k_len) - 1;  // position of the wave's last key
-    const bool wave_keys = kg * 32 < k_len;
+    const int pair_key_first = k_pos0 + kg * 32;                       // position of the pair's first key
+    const int pair_key_last = k_pos0 + min(kg * 32 + 32, k_len) - 1;  // and of its last
+    const bool pair_keys = kg * 32 < k_len;
+    // A block of `rows` rows from position pos0 has a visible pair with the pair's keys iff its
+    // last row is at or after their first key.
+    auto live_block = [&](int rows, int pos0) { return pair_keys && rows > 0 && pos0 + rows - 1 >= pair_key_first; };
 
-    // stationary operands: the wave's 32 keys as B fragments (K for both roles, V for dK)
-    bf16x8 kfr[D / 16], vfr[D / 16];
+    const int n_stages = cur.blocks(kQB) * G;
+    if (tid == 0) my_blocks += cur.blocks(64) * G;  // recorded in the plan's 64-row query blocks
+    SpanCursor nxt = cur;  // the next stage to copy in
+    // Both roles run the same barrier sequence: one per stage, then two in the epilogue.  The
+    // roles are separate code paths, so that the producer's K and V and the consumer's
+    // accumulators can share registers.
+    // Copies go out only once the wave's own loads are in registers: a wait for those inside
+    // the loop would also wait for every copy in flight.
+    auto start_copies = [&]() {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 xk = u32x4{0, 0, 0, 0}, xv = u32x4{0, 0, 0, 0};
-      if (key_real) {
-        const int64_t off = ((int64_t)(k_start + my_key) * a.kv_heads + g) * D + kk * 16 + hh * 8;
-        xk = *reinterpret_cast<const u32x4*>(K + off);
-        if (dk_role) xv = *reinterpret_cast<const u32x4*>(V + off);
-      }
-      kfr[kk] = __builtin_bit_cast(bf16x8, xk);
-      vfr[kk] = __builtin_bit_cast(bf16x8, xv);
-    }
-    f32x16 acc[D / 32];  // dK^T or dV^T of the wave's keys
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-
-    const int n_stages =
-        ((cur.sp.len + kQB - 1) / kQB + (cur.left >= 1 ? (cur.n1.len + kQB - 1) / kQB : 0) +
-         (cur.left >= 2 ? (cur.n2.len + kQB - 1) / kQB : 0) + (cur.left >= 3 ? (cur.n3.len + kQB - 1) / kQB : 0)) *
-        G;
-    if (tid == 0) my_blocks += n_stages;
-    StageCursor nxt = cur;  // the next stage to copy in
-#pragma unroll
-    for (int k = 0; k < kKvStages - 1; ++k)
-      if (k < n_stages) {
-        issue_stage<D>(a, smem + k * L::stage, nxt, g, wave, lane);
-        nxt.next(G);
-      }
-    for (int it = 0; it < n_stages; ++it) {
-      // this wave's copies of stage `it` have landed once at most the younger stages' are
-      // outstanding; the barrier then makes every wave's copies visible, and tells that every
-      // wave is done with the slot the next copy goes to
-      const int younger = min(kKvStages - 2, n_stages - 1 - it);
-      if (younger >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L::dmaPerStage));
-      else if (younger == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::dmaPerStage));
+      for (int k = 0; k < 2; ++k)
+        if (k < n_stages) {
+          issue_stage<D>(a, smem + k * L::stage, nxt, g, wave, lane);
+          nxt.next(kQB, G);
+        }
+    };
+    // Stage `it`: this wave's copies of it have landed once at most those of stage it + 1 are
+    // in flight; the barrier publishes every wave's copies and the P, dS of block it - 1, and
+    // frees slot it + 2 (stage it - 2) and the P, dS slot of block it - 2.
+    auto stage_sync = [&](int it) {
+      if (it + 1 < n_stages) wait_stage(1, L::copiesPerStage);
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      static_assert(kKvStages == 4, "the waits above cover two younger stages");
       lds_barrier();
-      if (it + kKvStages - 1 < n_stages) {
-        issue_stage<D>(a, smem + ((it + kKvStages - 1) % kKvStages) * L::stage, nxt, g, wave, lane);
-        nxt.next(G);
+      if (it + 2 < n_stages) {
+        issue_stage<D>(a, smem + ((it + 2) % kKvStages) * L::stage, nxt, g, wave, lane);
+        nxt.next(kQB, G);
       }
+    };
 
-      const char* h = smem + (it % kKvStages) * L::stage;
-      const char* qtile = h;
-      const char* dotile = h + L::tileBytes;
-      const float* lsep = reinterpret_cast<const float*>(h + 2 * L::tileBytes);
-      const float* dvp = lsep + kQB;
-      const int rows_valid = min(kQB, cur.sp.len - cur.off);
-      const int row_pos0 = cur.sp.pos0 + cur.off;  // position of the stage's first row
+    if (producer) {
+      // stationary operands: the pair's keys' K and V as B fragments
+      bf16x8 kfr[D / 16], vfr[D / 16];
 #pragma unroll
-      for (int sb = 0; sb < kQB / 32; ++sb) {
-        const int sb_rows = min(32, rows_valid - sb * 32);
-        const int sb_pos0 = row_pos0 + sb * 32;
-        // any visible pair: the sub-block's last row at or after the wave's first key
-        const bool live = wave_keys && sb_rows > 0 && sb_pos0 + sb_rows - 1 >= k_pos0 + kg * 32;
-        if (!live) continue;
-        // rows of this lane's accumulator: 8i + 4hh + j of the sub-block; keys: column l32
-        const bool full = sb_pos0 >= wave_key_last;
-        f32x16 s = f32x16{};
+      for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4 xk = u32x4{0, 0, 0, 0}, xv = u32x4{0, 0, 0, 0};
+        if (key_real) {
+          const int64_t off = ((int64_t)(k_start + my_key) * a.kv_heads + g) * D + kk * 16 + hh * 8;
+          xk = *reinterpret_cast<const u32x4*>(K + off);
+          xv = *reinterpret_cast<const u32x4*>(V + off);
+        }
+        kfr[kk] = __builtin_bit_cast(bf16x8, xk);
+        vfr[kk] = __builtin_bit_cast(bf16x8, xv);
+      }
+      start_copies();
+      for (int it = 0; it <= n_stages; ++it) {
+        stage_sync(it);
+        const int rows = min(kQB, cur.sp.len - cur.off);
+        const int row_pos0 = cur.sp.pos0 + cur.off;  // position of the block's first row
+        if (it < n_stages && live_block(rows, row_pos0)) {
+          const char* h = smem + (it % kKvStages) * L::stage;
+          const char* qtile = h;
+          const char* dotile = h + L::tileBytes;
+          const float* lsep = reinterpret_cast<const float*>(h + 2 * L::tileBytes);
+          const float* dvp = lsep + kQB;
+          char* xw = xbuf + (it & 1) * L::xSlot + kg * 2 * L::xBytes;
+          // rows of this lane's accumulators: 8 i4 + 4 hh + j of the block; keys: column l32
+          f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) s = mfma(row_frag(qtile, sb, kk), kfr[kk], s);
-        if (dk_role) {
-          f32x16 dp = f32x16{};
+          for (int kk = 0; kk < D / 16; ++kk) s = mfma(row_frag<D>(qtile, l32, 2 * kk + hh), kfr[kk], s);
 #pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) dp = mfma(row_frag(dotile, sb, kk), vfr[kk], dp);
-          bf16x8 dsf[2];
-          auto make_ds = [&](auto masked) {
+          for (int kk = 0; kk < D / 16; ++kk) dp = mfma(row_frag<D>(dotile, l32, 2 * kk + hh), vfr[kk], dp);
+          bf16x8 pf[2], dsf[2];
+          // the lane's key sees row 8 i4 + 4 hh + j iff that row's position is at least the
+          // key's: compared as kdist <= 8 i4 + j, against constants
+          const int kdist = kpos - row_pos0 - 4 * hh;
+          auto make = [&](auto masked) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
-              const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + sb * 32 + 8 * i4 + 4 * hh);
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + 8 * i4 + 4 * hh);
+              const f32x4 dv = *reinterpret_cast<const f32x4*>(dvp + 8 * i4 + 4 * hh);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int i = i4 * 4 + j;
-                const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
+                const bool vis = !decltype(masked)::value || kdist <= 8 * i4 + j;
                 const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, lv[j] * kNegLog2e)) : 0.f;
+                pf[i / 8][i % 8] = (__bf16)p;
                 dsf[i / 8][i % 8] = (__bf16)(p * (dp[i] - dv[j]));
               }
             }
           };
-          if (full) make_ds(Masked<false>{});
-          else make_ds(Masked<true>{});
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_frag(qtile, sb, ks, db), dsf[ks], acc[db]);
-        } else {
-          bf16x8 pf[2];
-          auto make_p = [&](auto masked) {
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + sb * 32 + 8 * i4 + 4 * hh);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int i = i4 * 4 + j;
-                const bool vis = !decltype(masked)::value || kpos <= sb_pos0 + 8 * i4 + 4 * hh + j;
-                pf[i / 8][i % 8] =
-                    (__bf16)(vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, lv[j] * kNegLog2e)) : 0.f);
-              }
-            }
-          };
-          if (full) make_p(Masked<false>{});
-          else make_p(Masked<true>{});
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_frag(dotile, sb, ks, db), pf[ks], acc[db]);
+          if (row_pos0 >= pair_key_last) make(Masked<false>{});
+          else make(Masked<true>{});
+          *reinterpret_cast<bf16x8*>(xw + lane * 16) = pf[0];
+          *reinterpret_cast<bf16x8*>(xw + 1024 + lane * 16) = pf[1];
+          *reinterpret_cast<bf16x8*>(xw + L::xBytes + lane * 16) = dsf[0];
+          *reinterpret_cast<bf16x8*>(xw + L::xBytes + 1024 + lane * 16) = dsf[1];
         }
+        if (it < n_stages) cur.next(kQB, G);
       }
-      cur.next(G);
-    }
-
-    // epilogue: dK = scale * dK^T, dV = dV^T, each role its own tensor, staged in the ring
-    lds_barrier();
-    {
-      char* ebuf = smem + wave * L::epiRows * L::epiStride;
+      lds_barrier();  // the consumers stage dK
+      lds_barrier();  // the consumers stage dV
+    } else {
+      f32x16 acck[D / 32], accv[D / 32];  // dK^T and dV^T of the pair's keys
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acck[db] = accv[db] = f32x16{};
+      start_copies();
+      for (int it = 0; it <= n_stages; ++it) {
+        stage_sync(it);
+        if (it == 0) continue;
+        // block it - 1, at cur
+        const int rows = min(kQB, cur.sp.len - cur.off);
+        const int row_pos0 = cur.sp.pos0 + cur.off;
+        if (live_block(rows, row_pos0)) {
+          const char* h = smem + ((it - 1) % kKvStages) * L::stage;
+          const char* qtile = h;
+          const char* dotile = h + L::tileBytes;
+          const char* xr = xbuf + ((it - 1) & 1) * L::xSlot + kg * 2 * L::xBytes;
+          const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(xr + lane * 16);
+          const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(xr + 1024 + lane * 16);
+          const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(xr + L::xBytes + lane * 16);
+          const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(xr + L::xBytes + 1024 + lane * 16);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            accv[db] = mfma(tr_frag<D>(dotile, 0, db, lane), p0, accv[db]);
+            accv[db] = mfma(tr_frag<D>(dotile, 16, db, lane), p1, accv[db]);
+            acck[db] = mfma(tr_frag<D>(qtile, 0, db, lane), d0, acck[db]);
+            acck[db] = mfma(tr_frag<D>(qtile, 16, db, lane), d1, acck[db]);
+          }
+        }
+        cur.next(kQB, G);
+      }
+      // epilogue: dK = scale * dK^T, then dV = dV^T, staged in LDS
       const int rows = max(0, min(32, k_len - kg * 32));
       const int64_t elt = OUT_F32 ? 4 : 2;
       const int64_t row_step = (int64_t)a.kv_heads * D * elt;
       const int64_t first = (((int64_t)k_start + kg * 32) * a.kv_heads + g) * D * elt;
-      void* grad = dk_role ? a.dk : a.dv;
-      if constexpr (RING) grad = dk_role ? r.dk[step] : r.dv[step];
+      char* ebuf = smem + kg * 32 * L::epiStride;
 #pragma unroll
-      for (int r_lo = 0; r_lo < 32; r_lo += L::epiRows) {
+      for (int t = 0; t < 2; ++t) {
+        lds_barrier();
+        void* grad = t == 0 ? a.dk : a.dv;
+        if constexpr (RING) grad = t == 0 ? r.dk[step] : r.dv[step];
+        stage_rows<D, OUT_F32>(ebuf, L::epiStride, t == 0 ? acck : accv, t == 0 ? a.scale : 1.0f, lane);
         __builtin_amdgcn_wave_barrier();
-        stage_rows<D, OUT_F32>(ebuf, L::epiStride, acc, dk_role ? a.scale : 1.0f, lane, r_lo, L::epiRows);
-        __builtin_amdgcn_wave_barrier();
-        store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(grad) + first + r_lo * row_step,
-                                       row_step, max(0, min(L::epiRows, rows - r_lo)), lane);
+        store_rows<D, OUT_F32 ? 1 : 0>(ebuf, L::epiStride, reinterpret_cast<char*>(grad) + first, row_step, rows,
+                                       lane);
       }
     }
     lds_barrier();

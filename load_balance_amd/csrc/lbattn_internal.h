@@ -184,13 +184,12 @@ struct MergeArgs {
 };
 
 // Backward kernels.  dQ: the forward's query tiles and wave layout (8 waves, each 32
-// rows of one head).  dK/dV: 4 waves per workgroup, one per SIMD (each may hold 512
-// registers): key tiles of 128 keys, a wave owning 32 keys and looping over all G heads;
-// query rows stream in stages of 64, one head at a time.
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = kBwdWaves * 64;
+// rows of one head).  dK/dV: key tiles of 128 keys, 4 groups of 32 keys, each owned by a
+// pair of waves that loops over all G heads; query rows stream in stages of 32, one head
+// at a time.
+constexpr int kBwdKeyGroups = 4;
 inline __host__ __device__ int bwd_q_rows(int group) { return tile_rows_for_group(group); }
-inline __host__ __device__ int bwd_k_rows(int) { return 32 * kBwdWaves; }
+inline __host__ __device__ int bwd_k_rows(int) { return 32 * kBwdKeyGroups; }
 
 struct BwdArgs {
   const void* q;     // bf16 [n_q][heads][d]
