@@ -17,7 +17,9 @@
 // with fp32 accumulation, in transposed form so that no register transpose is
 // needed:
 //   S^T[key][q] = K . Q^T    A = K rows from LDS, B = Q held in registers
-//   O^T[d][q]  += V^T . P^T  A = V^T rows from LDS, B = P^T straight from S^T
+//   O^T[d][q]  += V^T . P^T  A = V read transposed from LDS, B = P^T straight from S^T
+// K and V blocks reach LDS by direct global -> LDS copies, two blocks ahead, into a
+// 4-slot ring of swizzled row tiles; V^T fragments come from gfx950's LDS transpose load.
 // A lane of the 32x32 accumulator owns one query column (q = lane % 32), so
 // row max / row sum are per-lane loops plus one exchange with lane ^ 32, and
 // the rescale of O is a per-lane scalar.  Exponentials use exp2 with the
@@ -30,6 +32,7 @@
 // diagonal and ragged blocks evaluate "key position <= query position" per
 // element.
 #include "lbattn_internal.h"
+#include "lds_staging.h"
 
 namespace lb {
 namespace {
@@ -42,21 +45,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = kBlockN;
-constexpr int kStages = 3;  // LDS ring: the lagging waves still read block j-1 while block j+1 lands
+constexpr int kStages = 4;  // LDS ring: the lagging waves read block j-1, block j+1 has landed, j+2 lands
 constexpr int kPairBits = 40;  // a workgroup's pairs stay below 2^40; its key blocks below 2^23
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
 struct Lds {
-  static constexpr int kStride = D * 2 + 16;   // bytes per key row of K (16 B pad: conflict-free b128 reads)
-  static constexpr int vStride = BN * 2 + 16;  // bytes per d row of V^T
-  static constexpr int kBytes = BN * kStride;
-  static constexpr int vBytes = D * vStride;
-  static constexpr int stage = kBytes + vBytes;
-  static constexpr int kChunks = BN * D / 8;          // 16-byte pieces of a K block
-  static constexpr int kPerThread = kChunks / kThreads;
-  static constexpr int vUnits = (BN / 2) * (D / 8);  // (key pair, 8-wide d chunk) units of a V block
+  static constexpr int kBytes = BN * D * 2;  // a K block (64 swizzled rows); the V block follows
+  static constexpr int stage = 2 * kBytes;
+  static constexpr int copiesPerStage = 2 * copies64_per_wave<D>();
 };
 
 // Output staging for the epilogue: each wave's rows, row-major, in 1/8 of the ring's stages
@@ -75,12 +73,6 @@ struct EpilogueLds {
   static_assert(kRows * kStride <= kSpace, "epilogue staging does not fit in the ring");
   static_assert(64 % kChunks == 0 && kRows % (64 / kChunks) == 0, "whole rows per store step");
 };
-
-// V^T keeps keys permuted inside each group of 16 so that the 8 keys one lane feeds to
-// the PV product are contiguous: swap bits 2 and 3 of the key index.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 __device__ __forceinline__ uint64_t device_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -109,68 +101,7 @@ __device__ __forceinline__ uint32_t hw_id_reg() { return __builtin_amdgcn_s_getr
 __device__ __forceinline__ uint32_t xcc_id_reg() { return __builtin_amdgcn_s_getreg((15 << 11) | 20); }
 
 // Raw buffer resource word 3 for gfx9-family dword loads (no format conversion).
-constexpr int kBufferFlags = 0x00020000;
 
-
-template <int D>
-struct KvLoader {
-  u32x4 kreg[Lds<D>::kPerThread];
-  u32x4 vreg[2];
-  int k_off[Lds<D>::kPerThread];  // byte offset of this thread's 16-byte piece inside a block
-  int v_off[2];
-
-  __device__ __forceinline__ void init(int row_bytes, int tid) {
-#pragma unroll
-    for (int e = 0; e < Lds<D>::kPerThread; ++e) {
-      const int c = tid + e * kThreads;
-      k_off[e] = (c / (D / 8)) * row_bytes + (c % (D / 8)) * 16;
-    }
-    const int p = tid % (BN / 2), ch = tid / (BN / 2);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) v_off[e] = (2 * p + e) * row_bytes + ch * 16;
-  }
-
-  // Loads key rows [k0, k0 + BN) of kv head g into registers.  The buffer range ends after
-  // `valid` rows, and the hardware returns zeros beyond it: no bounds code, no zero fill.
-  __device__ __forceinline__ void load(const char* K, const char* V, int k0, int valid, int row_bytes, int g,
-                                       int tid) {
-    const int64_t base = (int64_t)k0 * row_bytes + (int64_t)g * D * 2;
-    const int nbytes = min(valid, BN) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + base), (short)0, nbytes,
-                                                                        kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + base), (short)0, nbytes,
-                                                                        kBufferFlags);
-#pragma unroll
-    for (int e = 0; e < Lds<D>::kPerThread; ++e) kreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[e], 0, 0);
-    if (tid < Lds<D>::vUnits) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) vreg[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[e], 0, 0);
-    }
-  }
-
-  __device__ __forceinline__ void store(char* stage, int tid) {
-    char* ks = stage;
-    char* vs = stage + Lds<D>::kBytes;
-#pragma unroll
-    for (int e = 0; e < Lds<D>::kPerThread; ++e) {
-      const int c = tid + e * kThreads;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * Lds<D>::kStride + ch * 16) = kreg[e];
-    }
-    if (tid < Lds<D>::vUnits) {
-      const int p = tid % (BN / 2), ch = tid / (BN / 2);
-      const int col = vt_pos(2 * p) * 2;  // byte offset of the key pair inside a V^T row
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t x0 = vreg[0][m], x1 = vreg[1][m];
-        const uint32_t lo = (x0 & 0xFFFFu) | (x1 << 16);          // d = ch*8 + 2m
-        const uint32_t hi = (x0 >> 16) | (x1 & 0xFFFF0000u);      // d = ch*8 + 2m + 1
-        *reinterpret_cast<uint32_t*>(vs + (ch * 8 + 2 * m) * Lds<D>::vStride + col) = lo;
-        *reinterpret_cast<uint32_t*>(vs + (ch * 8 + 2 * m + 1) * Lds<D>::vStride + col) = hi;
-      }
-    }
-  }
-};
 
 // Uniform description of one key block: which span, which block of it.
 struct KvBlock {
@@ -270,8 +201,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     s_pop.items = 0;
   }
 
-  KvLoader<D> ld;
-  ld.init(row_bytes, tid);
 
   // Tiles with no key span only set lse = -inf on their rows: a grid-stride pass before the
   // queues, without barriers or LDS.
@@ -371,7 +300,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
-    if (n_spans > 0) ld.load(Kx, Vx, k_start0, k_len0, row_bytes, g, tid);
+    if (n_spans > 0) {
+      const uint32_t lds = lds_addr(smem);  // block 0 goes to slot 0 (kept out of the epilogue staging)
+      const int valid = __builtin_amdgcn_readfirstlane(min(k_len0, BN));
+      issue_tile64<D>(Kx, row_bytes, k_start0, valid, g, lds, wave, lane);
+      issue_tile64<D>(Vx, row_bytes, k_start0, valid, g, lds + Lds<D>::kBytes, wave, lane);
+    }
   };
   // Wave 0 copies an item's 96-byte descriptor into an LDS slot (lanes 0-5, 16 bytes each);
   // the copy lands asynchronously and is waited for before the barrier that precedes its use.
@@ -380,11 +314,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     // lane's 16-byte piece in a 32-bit vector offset (no 64-bit address per lane)
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
     const int t_off = __builtin_amdgcn_readfirstlane((k_in / heads_per_queue) * (int)sizeof(lb_plan_tile));
-    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)tiles, (short)0, (int)(n_tiles_hdr * (int64_t)sizeof(lb_plan_tile)), kBufferFlags);
-    if (wave == 0 && lane < (int)(sizeof(lb_plan_tile) / 16))
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)slot, 16, lane * 16,
-                                               t_off, 0, 0);
+    const i32x4 rt = buffer_rsrc(reinterpret_cast<const char*>(tiles) + t_off,
+                                 (int)sizeof(lb_plan_tile));
+    if (wave == 0 && lane < (int)(sizeof(lb_plan_tile) / 16)) copy16_to_lds(rt, lds_addr(slot), lane * 16);
   };
   auto wait_tile = [&]() {
     if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the descriptor copy has landed
@@ -476,8 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
         acc_s[kb] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * Lds<D>::kStride + (kk * 16 + hh * 8) * 2);
+          const bf16x8 kf = row_frag<D>(ks, kb * 32 + l32, 2 * kk + hh);
           acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], acc_s[kb], 0, 0, 0);
         }
       }
@@ -556,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       auto read_v = [&](int ks16, bf16x8* dst) {
 #pragma unroll
         for (int db = 0; db < kDb; ++db)
-          dst[db] = *reinterpret_cast<const bf16x8*>(vs + (db * 32 + l32) * Lds<D>::vStride + (ks16 * 16 + hh * 8) * 2);
+          dst[db] = tr_frag<D>(vs, ks16 * 16, db, lane);
       };
       // An explicit pipeline, fenced so that the scheduler keeps it whatever surrounds the
       // loop: the MFMAs of chunk ks run with the exponentials of chunk ks + 1 between them,
@@ -581,27 +512,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       l_part += lsum[0] + lsum[1];
     };
 
-    // prologue: first key block (loaded during the previous epilogue) into stage 0; spans in
-    // the plan are never empty.  The key loop's first barrier also ends every wave's Q
-    // staging read before the ring's stage 1 is written.
+    // Block 0 was copied into slot 0 during the previous epilogue, with this wave's Q
+    // fragment: both are waited for here, before any copy of this item goes out (a wait for
+    // the fragment inside the loop would also wait for every copy in flight).  Block b goes
+    // to slot b % kStages; at block `it` the copy of block it + 2 goes out (blocks 1 and 2 at
+    // block 0, once the key loop's first barrier has ended every wave's epilogue staging).
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     int cur_s = 0;
     KvBlock cur = span_of(0);
-    if (n_kv_tiles > 0) ld.store(smem, tid);
+    int iss_s = 0;  // the next block to copy in
+    KvBlock iss = cur;
+    auto advance = [&](KvBlock& b, int& s) {
+      b.key0 += BN;
+      if (b.key0 >= b.len) {
+        ++s;
+        if (s < n_spans) b = span_of(s);
+      }
+    };
+    advance(iss, iss_s);
+    auto issue_block = [&](int slot_i) {
+      const uint32_t lds = lds_addr(smem + slot_i * Lds<D>::stage);
+      const int k0 = __builtin_amdgcn_readfirstlane(iss.start + iss.key0);
+      const int valid = __builtin_amdgcn_readfirstlane(min(iss.len - iss.key0, BN));
+      issue_tile64<D>(Kit, row_bytes, k0, valid, g, lds, wave, lane);
+      issue_tile64<D>(Vit, row_bytes, k0, valid, g, lds + Lds<D>::kBytes, wave, lane);
+      advance(iss, iss_s);
+    };
     KvBlock prev{0, 0, 0, 0, LB_NO_LOWER_BOUND};
     bool prev_live = false;
 
     for (int it = 0; it < n_kv_tiles; ++it) {
+      // this wave's copies of block `it` have landed once at most those of block it + 1 are in
+      // flight; the barrier publishes every wave's, and frees slot it + 2 (block it - 2)
+      if (it > 0 && it + 1 < n_kv_tiles) wait_stage(1, Lds<D>::copiesPerStage);
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
-      // the block after this one: next 64 keys of this span, or the first of the next span
-      KvBlock nxt = cur;
-      nxt.key0 += BN;
-      int nx_s = cur_s;
-      if (nxt.key0 >= cur.len) {
-        ++nx_s;
-        if (nx_s < n_spans) nxt = span_of(nx_s);
+      if (it == 0) {
+        if (1 < n_kv_tiles) issue_block(1);
+        if (2 < n_kv_tiles) issue_block(2);
+      } else if (it + 2 < n_kv_tiles) {
+        issue_block((it + 2) % kStages);
       }
-      const bool has_next = it + 1 < n_kv_tiles;
-      if (has_next) ld.load(Kit, Vit, nxt.start + nxt.key0, nxt.len - nxt.key0, row_bytes, g, tid);
       const char* stage = smem + (it % kStages) * Lds<D>::stage;
       const char* prev_stage = smem + ((it + kStages - 1) % kStages) * Lds<D>::stage;
       const bool cur_live = live(cur);
@@ -614,11 +565,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
         if (prev_live) softmax_pv(prev, prev_stage + Lds<D>::kBytes);
         if (cur_live) qk(stage);
       }
-      if (has_next) ld.store(smem + ((it + 1) % kStages) * Lds<D>::stage, tid);
       prev = cur;
       prev_live = cur_live;
-      cur = nxt;
-      cur_s = nx_s;
+      advance(cur, cur_s);
     }
     if (lagging && prev_live)
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
