@@ -35,7 +35,8 @@ PEAK_BF16_AT_2400MHZ = 256 * 2.4e9 * 4096 / 1e12   # 256 CUs x 2.4 GHz x 4096 FL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longtail32k_traffic.json")
 TRAFFIC_SOURCE = ("profiles/attn_fwd_longtail32k_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes of this "
                   "kernel source, copy-calibrated; read from that file, not measured in this run")
-KERNEL_SOURCE = os.path.join(ROOT, "load_balance_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's source files: the traffic file applies while their joint hash matches
+KERNEL_SOURCES = [os.path.join(ROOT, "load_balance_amd", "csrc", f) for f in ("attn_fwd.hip", "lds_staging.h")]
 
 
 def log(*a):
@@ -129,7 +130,7 @@ class VarlenBwdStep:
         self.H, self.d = H, d
         self.pairs = causal_pairs(pack["lengths"])
         self.flops = 10 * d * H * self.pairs
-        self.kernel_name = "backward call (plans, D, bwd_dq_kernel<128,1>, bwd_dkv_kernel<128,2>)"
+        self.kernel_name = "backward call (plans, D, bwd_dq_kernel<128,1,false>, bwd_dkv_kernel<128,false,false>)"
 
     def n_launches(self):
         return 1
@@ -581,9 +582,11 @@ def traffic_entry():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if t.get("source_sha256") != sha:
+        h = hashlib.sha256()
+        for path in KERNEL_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        if t.get("source_sha256") != h.hexdigest():
             return None
         return t.get("hbm_bytes_per_launch")
     except Exception:
