@@ -141,6 +141,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     int dry;        // every queue found empty
   } s_pop;
 
+  // LDS addresses of the ring and of the descriptor slots, for the direct copies
+  const uint32_t ring_lds = lds_addr(smem), tile_lds = lds_addr(s_tile);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     for (int kk = 0; kk < D / 16; ++kk)
       qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
     if (n_spans > 0) {
-      const uint32_t lds = lds_addr(smem);  // block 0 goes to slot 0 (kept out of the epilogue staging)
+      const uint32_t lds = ring_lds;  // block 0 goes to slot 0 (kept out of the epilogue staging)
       const int valid = __builtin_amdgcn_readfirstlane(min(k_len0, BN));
       issue_tile64<D>(Kx, row_bytes, k_start0, valid, g, lds, wave, lane);
       issue_tile64<D>(Vx, row_bytes, k_start0, valid, g, lds + Lds<D>::kBytes, wave, lane);
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     const int t_off = __builtin_amdgcn_readfirstlane((k_in / heads_per_queue) * (int)sizeof(lb_plan_tile));
     const i32x4 rt = buffer_rsrc(reinterpret_cast<const char*>(tiles) + t_off,
                                  (int)sizeof(lb_plan_tile));
-    if (wave == 0 && lane < (int)(sizeof(lb_plan_tile) / 16)) copy16_to_lds(rt, lds_addr(slot), lane * 16);
+    if (wave == 0 && lane < (int)(sizeof(lb_plan_tile) / 16))
+      copy16_to_lds(rt, tile_lds + (uint32_t)((char*)slot - (char*)s_tile), lane * 16);
   };
   auto wait_tile = [&]() {
     if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the descriptor copy has landed
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     };
     advance(iss, iss_s);
     auto issue_block = [&](int slot_i) {
-      const uint32_t lds = lds_addr(smem + slot_i * Lds<D>::stage);
+      const uint32_t lds = ring_lds + slot_i * Lds<D>::stage;
       const int k0 = __builtin_amdgcn_readfirstlane(iss.start + iss.key0);
       const int valid = __builtin_amdgcn_readfirstlane(min(iss.len - iss.key0, BN));
       issue_tile64<D>(Kit, row_bytes, k0, valid, g, lds, wave, lane);

@@ -261,14 +261,18 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const void* out, const void
 struct SpanCursor {
   int off, rep, left;  // left: spans after the current one
   Span sp, n1, n2, n3;
-  __device__ __forceinline__ void start(const lb_plan_tile* T) {
+  bool down;           // each span's blocks from its last to its first
+  __device__ __forceinline__ static int last_block(int len, int step) { return (len - 1) / step * step; }
+  __device__ __forceinline__ void start(const lb_plan_tile* T, int step, bool descending = false) {
     static_assert(LB_MAX_SPANS == 4, "the cursor holds up to four spans");
-    off = rep = 0;
+    rep = 0;
+    down = descending;
     left = __builtin_amdgcn_readfirstlane(T->n_spans) - 1;
     sp = span_of(T, 0);
     n1 = span_of(T, 1);
     n2 = span_of(T, 2);
     n3 = span_of(T, 3);
+    off = down ? last_block(sp.len, step) : 0;
   }
   // blocks of `step` rows over all spans (the span count is at least 1)
   __device__ __forceinline__ int blocks(int step) const {
@@ -278,13 +282,13 @@ struct SpanCursor {
   __device__ __forceinline__ void next(int step, int reps) {
     if (++rep == reps) {
       rep = 0;
-      off += step;
-      if (off >= sp.len && left > 0) {
-        off = 0;
+      off += down ? -step : step;
+      if ((down ? off < 0 : off >= sp.len) && left > 0) {
         --left;
         sp = n1;
         n1 = n2;
         n2 = n3;
+        off = down ? last_block(sp.len, step) : 0;
       }
     }
   }
@@ -309,6 +313,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using L = DqLds<D>;
   __shared__ __attribute__((aligned(1024))) char smem[L::ring];
   __shared__ int s_item;
+  const uint32_t ring_lds = lds_addr(smem);  // the ring's LDS address, for the copies
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
     SpanCursor cur;  // the key block being computed
-    cur.start(T);
+    cur.start(T, BN);
     const int n_blocks = cur.blocks(BN);
     if (tid == 0) {
       my_blocks += n_blocks;
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     auto issue = [&](int slot) {
       const int k0 = __builtin_amdgcn_readfirstlane(nxt.sp.start + nxt.off);
       const int valid = __builtin_amdgcn_readfirstlane(max(0, min(nxt.sp.len - nxt.off, BN)));
-      const uint32_t lds = lds_addr(smem + slot * L::stage);
+      const uint32_t lds = ring_lds + slot * L::stage;
       issue_tile64<D>(a.k, row_bytes, k0, valid, g, lds, w, lane);
       issue_tile64<D>(a.v, row_bytes, k0, valid, g, lds + L::tileBytes, w, lane);
       nxt.next(BN, 1);
@@ -517,11 +522,11 @@ struct KvLds {
   static_assert(kKeyGroups * 32 * epiStride <= total, "epilogue staging must fit in the kernel's LDS");
 };
 
-// Copies the stage at cursor `c` (32 rows of one head from row sp.start + off) into `buf`:
+// Copies the stage at cursor `c` (32 rows of one head from row sp.start + off) to LDS address `lds`:
 // every wave issues copiesPerStage copies (the same count in every wave, so that the vmcnt
 // waits are uniform).  Rows past the span's end read as zeros, and so do their lse and D.
 template <int D>
-__device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const SpanCursor& c, int g, int wave,
+__device__ __forceinline__ void issue_stage(const BwdArgs& a, uint32_t lds, const SpanCursor& c, int g, int wave,
                                             int lane) {
   using L = KvLds<D>;
   constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2), kBlocksPerTile = L::tileBytes / 1024;
@@ -530,7 +535,6 @@ __device__ __forceinline__ void issue_stage(const BwdArgs& a, char* buf, const S
   const int valid = __builtin_amdgcn_readfirstlane(max(0, min(c.sp.len - c.off, kQB)));
   const int w = __builtin_amdgcn_readfirstlane(wave);
   const int64_t row_step = (int64_t)a.heads * D * 2;
-  const uint32_t lds = lds_addr(buf);
 #pragma unroll
   for (int j = 0; j < L::copies; ++j) {
     const int blk = w * L::copies + j;  // the 1 KB piece of the Q and dO tiles
@@ -558,6 +562,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
   __shared__ __attribute__((aligned(1024))) char smem[L::total];
   __shared__ int s_item;
   char* xbuf = smem + L::ring;
+  const uint32_t ring_lds = lds_addr(smem);  // the ring's LDS address, for the copies
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
@@ -612,8 +617,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     const int k_start = __builtin_amdgcn_readfirstlane(T->q_start);  // the tile's keys
     const int k_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int k_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
+    // Each span's query rows stream from its last block to its first: the key tiles of one
+    // document all end at the document's last row, so tiles that run at the same time read
+    // the same rows at about the same time and share them in L2.
     SpanCursor cur;  // the block the producers compute
-    cur.start(T);
+    cur.start(T, kQB, true);
     if (tid == 0) {
       ++my_items;
       my_pairs += T->cost * G;
@@ -649,7 +657,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         if (k < n_stages) {
-          issue_stage<D>(a, smem + k * L::stage, nxt, g, wave, lane);
+          issue_stage<D>(a, ring_lds + k * L::stage, nxt, g, wave, lane);
           nxt.next(kQB, G);
         }
     };
@@ -661,7 +669,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
       if (it + 2 < n_stages) {
-        issue_stage<D>(a, smem + ((it + 2) % kKvStages) * L::stage, nxt, g, wave, lane);
+        issue_stage<D>(a, ring_lds + ((it + 2) % kKvStages) * L::stage, nxt, g, wave, lane);
         nxt.next(kQB, G);
       }
     };
