@@ -54,7 +54,7 @@ template <int D>
 struct Lds {
   static constexpr int kBytes = BN * D * 2;  // a K block (64 swizzled rows); the V block follows
   static constexpr int stage = 2 * kBytes;
-  static constexpr int copiesPerStage = 2 * copies64_per_wave<D>();
+  static constexpr int copiesPerStage = 2 * TileCopier<D, BN>::kCopies;
 };
 
 // Output staging for the epilogue: each wave's rows, row-major, in 1/8 of the ring's stages
@@ -191,6 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
   const char* Kb = reinterpret_cast<const char*>(a.k);
   const char* Vb = reinterpret_cast<const char*>(a.v);
   const int row_bytes = a.kv_heads * D * 2;  // one token's K (or V) across all kv heads
+  TileCopier<D, BN> copier;  // this wave's share of a K or V block's copy
+  copier.init(row_bytes, wave, lane);
 
   const int G = a.group;
   const int head_in_group = wave % G;
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     if (n_spans > 0) {
       const uint32_t lds = ring_lds;  // block 0 goes to slot 0 (kept out of the epilogue staging)
       const int valid = __builtin_amdgcn_readfirstlane(min(k_len0, BN));
-      issue_tile64<D>(Kx, row_bytes, k_start0, valid, g, lds, wave, lane);
-      issue_tile64<D>(Vx, row_bytes, k_start0, valid, g, lds + Lds<D>::kBytes, wave, lane);
+      copier.issue(Kx, row_bytes, k_start0, valid, g, lds);
+      copier.issue(Vx, row_bytes, k_start0, valid, g, lds + Lds<D>::kBytes);
     }
   };
   // Wave 0 copies an item's 96-byte descriptor into an LDS slot (lanes 0-5, 16 bytes each);
@@ -538,8 +540,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       const uint32_t lds = ring_lds + slot_i * Lds<D>::stage;
       const int k0 = __builtin_amdgcn_readfirstlane(iss.start + iss.key0);
       const int valid = __builtin_amdgcn_readfirstlane(min(iss.len - iss.key0, BN));
-      issue_tile64<D>(Kit, row_bytes, k0, valid, g, lds, wave, lane);
-      issue_tile64<D>(Vit, row_bytes, k0, valid, g, lds + Lds<D>::kBytes, wave, lane);
+      copier.issue(Kit, row_bytes, k0, valid, g, lds);
+      copier.issue(Vit, row_bytes, k0, valid, g, lds + Lds<D>::kBytes);
       advance(iss, iss_s);
     };
     KvBlock prev{0, 0, 0, 0, LB_NO_LOWER_BOUND};

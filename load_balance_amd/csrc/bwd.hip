@@ -303,7 +303,7 @@ template <int D>
 struct DqLds {
   static constexpr int tileBytes = BN * D * 2;  // 64 keys of K or V
   static constexpr int stage = 2 * tileBytes;   // K, V
-  static constexpr int copiesPerStage = 2 * copies64_per_wave<D>();
+  static constexpr int copiesPerStage = 2 * TileCopier<D, BN>::kCopies;
   static constexpr int ring = kDqStages * stage;
   static_assert(BN == 64, "a stage is one 64-row tile per tensor");
 };
@@ -385,13 +385,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     // loop would also wait for every copy in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     SpanCursor nxt = cur;  // the next key block to copy in
-    const int w = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int slot) {
       const int k0 = __builtin_amdgcn_readfirstlane(nxt.sp.start + nxt.off);
       const int valid = __builtin_amdgcn_readfirstlane(max(0, min(nxt.sp.len - nxt.off, BN)));
       const uint32_t lds = ring_lds + slot * L::stage;
-      issue_tile64<D>(a.k, row_bytes, k0, valid, g, lds, w, lane);
-      issue_tile64<D>(a.v, row_bytes, k0, valid, g, lds + L::tileBytes, w, lane);
+      TileCopier<D, BN>::issue_now(a.k, row_bytes, k0, valid, g, lds, wave, lane);
+      TileCopier<D, BN>::issue_now(a.v, row_bytes, k0, valid, g, lds + L::tileBytes, wave, lane);
       nxt.next(BN, 1);
     };
 #pragma unroll
@@ -511,47 +510,59 @@ template <int D>
 struct KvLds {
   static constexpr int tileBytes = kQB * D * 2;              // 32 rows of one tensor
   static constexpr int stage = 2 * tileBytes + 2 * kQB * 4;  // Q, dO; raw lse, D
-  static constexpr int copies = 2 * tileBytes / 1024 / kKvWaves;  // row copies per wave per stage
-  static constexpr int copiesPerStage = copies + 1;                // + lse or D
   static constexpr int ring = kKvStages * stage;
   static constexpr int xBytes = 2048;                    // one B operand block: 64 lanes x 2 x 16 bytes
   static constexpr int xSlot = kKeyGroups * 2 * xBytes;  // P and dS of every key group
   static constexpr int total = ring + 2 * xSlot;
   static constexpr int epiStride = D * 4 + 16;
-  static_assert(2 * tileBytes % (1024 * kKvWaves) == 0, "the row copies must divide evenly over the waves");
   static_assert(kKeyGroups * 32 * epiStride <= total, "epilogue staging must fit in the kernel's LDS");
 };
 
-// Copies the stage at cursor `c` (32 rows of one head from row sp.start + off) to LDS address `lds`:
-// every wave issues copiesPerStage copies (the same count in every wave, so that the vmcnt
-// waits are uniform).  Rows past the span's end read as zeros, and so do their lse and D.
+// A wave's share of a stage's copies: waves 0-3 copy the Q tile, waves 4-7 the dO tile (a
+// 32-row tile is 8 or 4 pieces of 1 KB, one or two per wave of the half), and every wave 8 rows
+// of lse (even waves) or D (odd waves).  Every wave issues the same count, kPerStage, so that
+// the vmcnt waits are uniform.  Rows past the span's end read as zeros, and so do their lse and
+// D.  The lane offsets are computed once.
 template <int D>
-__device__ __forceinline__ void issue_stage(const BwdArgs& a, uint32_t lds, const SpanCursor& c, int g, int wave,
-                                            int lane) {
+struct StageCopier {
   using L = KvLds<D>;
-  constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2), kBlocksPerTile = L::tileBytes / 1024;
-  const int head = __builtin_amdgcn_readfirstlane(g * a.group + c.rep);
-  const int r0 = __builtin_amdgcn_readfirstlane(c.sp.start + c.off);
-  const int valid = __builtin_amdgcn_readfirstlane(max(0, min(c.sp.len - c.off, kQB)));
-  const int w = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t row_step = (int64_t)a.heads * D * 2;
+  static constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2), kCopies = D / 64;
+  static constexpr int kPerStage = kCopies + 1;
+  static_assert(kCopies * 4 * 1024 == L::tileBytes, "four waves per tile");
+  int voff[kCopies], voff_v;  // lane byte offsets from the tile's (the vector's) first row
+  uint32_t loff, loff_v;      // the wave's pieces within a stage (wave-uniform)
+  int t, w;                   // the wave's tensor (0: Q, 1: dO); its index
+
+  __device__ __forceinline__ void init(int64_t row_step, int wave, int lane) {
+    w = __builtin_amdgcn_readfirstlane(wave);
+    t = w >> 2;
 #pragma unroll
-  for (int j = 0; j < L::copies; ++j) {
-    const int blk = w * L::copies + j;  // the 1 KB piece of the Q and dO tiles
-    const int t = blk / kBlocksPerTile, tb = blk % kBlocksPerTile;
+    for (int j = 0; j < kCopies; ++j) {
+      const int row = ((w & 3) * kCopies + j) * kRowsPerCopy + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ swz<D>(row);  // lane writes slot lane % kChunks of its row
+      voff[j] = row * (int)row_step + chunk * 16;
+    }
+    loff = __builtin_amdgcn_readfirstlane(t * L::tileBytes + (w & 3) * kCopies * 1024);
+    voff_v = ((w >> 1) * 8 + lane) * 4;
+    loff_v = __builtin_amdgcn_readfirstlane(2 * L::tileBytes + (w & 1) * kQB * 4 + (w >> 1) * 32);
+  }
+  // the stage at cursor `c` (32 rows of head g * G + c.rep from row sp.start + off) to LDS
+  // address `lds`
+  __device__ __forceinline__ void issue(const BwdArgs& a, uint32_t lds, const SpanCursor& c, int g, int lane) const {
+    const int head = __builtin_amdgcn_readfirstlane(g * a.group + c.rep);
+    const int r0 = __builtin_amdgcn_readfirstlane(c.sp.start + c.off);
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(c.sp.len - c.off, kQB)));
+    const int64_t row_step = (int64_t)a.heads * D * 2;
     const char* base = reinterpret_cast<const char*>(t == 0 ? a.q : a.dout) + (int64_t)r0 * row_step +
                        (int64_t)head * D * 2;
     const i32x4 rs = buffer_rsrc(base, valid * (int)row_step);
-    const int row = tb * kRowsPerCopy + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ swz<D>(row);  // lane writes slot lane % kChunks of its row
-    copy16_to_lds(rs, lds + blk * 1024, row * (int)row_step + chunk * 16);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy16_to_lds(rs, lds + loff + j * 1024, voff[j]);
+    const float* vec = (w & 1) ? a.dvec : a.lse;
+    const i32x4 rv = buffer_rsrc(vec + (int64_t)head * a.n_q + r0, valid * 4);
+    if (lane < 8) copy4_to_lds(rv, lds + loff_v, voff_v);
   }
-  // lse (even waves) or D (odd waves), 8 rows per wave, 4 bytes per lane
-  const float* vec = (w & 1) ? a.dvec : a.lse;
-  const int q8 = w >> 1;
-  const i32x4 rv = buffer_rsrc(vec + (int64_t)head * a.n_q + r0, valid * 4);
-  if (lane < 8) copy4_to_lds(rv, lds + 2 * L::tileBytes + (w & 1) * kQB * 4 + q8 * 32, (q8 * 8 + lane) * 4);
-}
+};
 
 // RING: a ring workspace of several steps' key tiles; a tile's step selects the keys, values
 // and gradient outputs of that step in r (one launch for every step of a rank's ring).
@@ -563,6 +574,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
   __shared__ int s_item;
   char* xbuf = smem + L::ring;
   const uint32_t ring_lds = lds_addr(smem);  // the ring's LDS address, for the copies
+  StageCopier<D> copier;
+  copier.init((int64_t)a.heads * D * 2, threadIdx.x >> 6, threadIdx.x & 63);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int G = a.group;
@@ -657,7 +670,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         if (k < n_stages) {
-          issue_stage<D>(a, ring_lds + k * L::stage, nxt, g, wave, lane);
+          copier.issue(a, ring_lds + k * L::stage, nxt, g, lane);
           nxt.next(kQB, G);
         }
     };
@@ -665,11 +678,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
     // in flight; the barrier publishes every wave's copies and the P, dS of block it - 1, and
     // frees slot it + 2 (stage it - 2) and the P, dS slot of block it - 2.
     auto stage_sync = [&](int it) {
-      if (it + 1 < n_stages) wait_stage(1, L::copiesPerStage);
+      if (it + 1 < n_stages) wait_stage(1, StageCopier<D>::kPerStage);
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
       if (it + 2 < n_stages) {
-        issue_stage<D>(a, ring_lds + ((it + 2) % kKvStages) * L::stage, nxt, g, wave, lane);
+        copier.issue(a, ring_lds + ((it + 2) % kKvStages) * L::stage, nxt, g, lane);
         nxt.next(kQB, G);
       }
     };
@@ -701,11 +714,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
           const float* dvp = lsep + kQB;
           char* xw = xbuf + (it & 1) * L::xSlot + kg * 2 * L::xBytes;
           // rows of this lane's accumulators: 8 i4 + 4 hh + j of the block; keys: column l32
+          // all operand reads first (their latency overlaps), then the S and dP chains interleaved
+          bf16x8 fq[D / 16], fd[D / 16];
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            fq[kk] = row_frag<D>(qtile, l32, 2 * kk + hh);
+            fd[kk] = row_frag<D>(dotile, l32, 2 * kk + hh);
+          }
+          __builtin_amdgcn_sched_barrier(0);
           f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) s = mfma(row_frag<D>(qtile, l32, 2 * kk + hh), kfr[kk], s);
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) dp = mfma(row_frag<D>(dotile, l32, 2 * kk + hh), vfr[kk], dp);
+          for (int kk = 0; kk < D / 16; ++kk) {
+            s = mfma(fq[kk], kfr[kk], s);
+            dp = mfma(fd[kk], vfr[kk], dp);
+          }
           bf16x8 pf[2], dsf[2];
           // the lane's key sees row 8 i4 + 4 hh + j iff that row's position is at least the
           // key's: compared as kdist <= 8 i4 + j, against constants
@@ -756,12 +778,29 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a, RingB
           const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(xr + 1024 + lane * 16);
           const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(xr + L::xBytes + lane * 16);
           const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(xr + L::xBytes + 1024 + lane * 16);
+          // every operand read goes out before the first product: the reads' latency then
+          // overlaps, and each product waits only for its own operands
+          bf16x8 fv[2][D / 32], fk[2][D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            accv[db] = mfma(tr_frag<D>(dotile, 0, db, lane), p0, accv[db]);
-            accv[db] = mfma(tr_frag<D>(dotile, 16, db, lane), p1, accv[db]);
-            acck[db] = mfma(tr_frag<D>(qtile, 0, db, lane), d0, acck[db]);
-            acck[db] = mfma(tr_frag<D>(qtile, 16, db, lane), d1, acck[db]);
+            fv[0][db] = tr_frag<D>(dotile, 0, db, lane);
+            fv[1][db] = tr_frag<D>(dotile, 16, db, lane);
+          }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            fk[0][db] = tr_frag<D>(qtile, 0, db, lane);
+            fk[1][db] = tr_frag<D>(qtile, 16, db, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            accv[db] = mfma(fv[0][db], p0, accv[db]);
+            accv[db] = mfma(fv[1][db], p1, accv[db]);
+          }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            acck[db] = mfma(fk[0][db], d0, acck[db]);
+            acck[db] = mfma(fk[1][db], d1, acck[db]);
           }
         }
         cur.next(kQB, G);

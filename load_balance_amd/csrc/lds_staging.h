@@ -98,26 +98,46 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int db, int 
   return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Issues the copy of rows [r0, r0 + 64) (the first `valid` of them real, the rest read as
-// zeros) of one head of a [row][heads][D] tensor into a 64-row tile, spread over 8 waves:
-// every wave issues the same count, copies64_per_wave<D>().
-template <int D>
-constexpr int copies64_per_wave() { return 64 * D * 2 / 1024 / 8; }
-template <int D>
-__device__ __forceinline__ void issue_tile64(const void* src, int64_t row_step, int r0, int valid, int head,
-                                             uint32_t lds, int wave, int lane) {
-  constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2);
-  const char* base = reinterpret_cast<const char*>(src) + (int64_t)r0 * row_step + (int64_t)head * D * 2;
-  const i32x4 rs = buffer_rsrc(base, valid * (int)row_step);
-  wave = __builtin_amdgcn_readfirstlane(wave);
+// One wave's share of copying a tile of ROWS rows of one head of a [row][heads][D] bf16 tensor
+// (row_step bytes per row) into LDS: the tile's 1 KB pieces are spread evenly over 8 waves,
+// and every wave issues the same count, kCopies.  The lane offsets are computed once; a copy
+// then costs the tile's base address, one buffer resource and the copy instructions.  Rows
+// from `valid` on read as zeros (the buffer range ends there).
+template <int D, int ROWS>
+struct TileCopier {
+  static constexpr int kChunks = D / 8, kRowsPerCopy = 1024 / (D * 2);
+  static constexpr int kCopies = ROWS * D * 2 / 1024 / 8;
+  static_assert(ROWS * D * 2 % (1024 * 8) == 0, "the pieces must divide evenly over 8 waves");
+  int voff[kCopies];  // the lane's byte offset in the source, from the tile's first row of its head
+  uint32_t loff;      // the wave's first piece in the tile (wave-uniform)
+
+  __device__ __forceinline__ void init(int64_t row_step, int wave, int lane) {
+    wave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-  for (int j = 0; j < copies64_per_wave<D>(); ++j) {
-    const int blk = wave * copies64_per_wave<D>() + j;  // the 1 KB piece of the tile
-    const int row = blk * kRowsPerCopy + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ swz<D>(row);   // lane writes slot lane % kChunks of its row
-    copy16_to_lds(rs, lds + blk * 1024, row * (int)row_step + chunk * 16);
+    for (int j = 0; j < kCopies; ++j) {
+      const int row = (wave * kCopies + j) * kRowsPerCopy + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ swz<D>(row);  // lane writes slot lane % kChunks of its row
+      voff[j] = row * (int)row_step + chunk * 16;
+    }
+    loff = __builtin_amdgcn_readfirstlane(wave * kCopies * 1024);
   }
-}
+  // rows [r0, r0 + ROWS) of head `head` into the tile at LDS address `lds`
+  __device__ __forceinline__ void issue(const void* src, int64_t row_step, int r0, int valid, int head,
+                                        uint32_t lds) const {
+    const char* base = reinterpret_cast<const char*>(src) + (int64_t)r0 * row_step + (int64_t)head * D * 2;
+    const i32x4 rs = buffer_rsrc(base, valid * (int)row_step);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy16_to_lds(rs, lds + loff + j * 1024, voff[j]);
+  }
+  // the same copy with the lane offsets computed on the spot, for kernels that cannot spare
+  // the registers that keep them
+  __device__ __forceinline__ static void issue_now(const void* src, int64_t row_step, int r0, int valid, int head,
+                                                   uint32_t lds, int wave, int lane) {
+    TileCopier c;
+    c.init(row_step, wave, lane);
+    c.issue(src, row_step, r0, valid, head, lds);
+  }
+};
 
 // s_waitcnt vmcnt(k * per) for k = min(2, younger) stages still allowed in flight
 __device__ __forceinline__ void wait_stage(int younger, int per) {
