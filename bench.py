@@ -61,6 +61,7 @@ class VarlenStep:
         self.torch, self.lb = torch, lb
         self.name = name
         self.mask_kind = mask_kind
+        self.lpt_weights = None  # (block, pair) weights of the queue order; None: lb_plan_varlen's fitted ones
         self.items = []
         for p in packs:
             T, H, Hkv, d = p["tokens"], p["heads"], p["kv_heads"], p["d"]
@@ -91,7 +92,11 @@ class VarlenStep:
             ev = None if evs is None else evs[i]
             if ev is not None:
                 ev[0].record()
-            lb.plan_varlen(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], self.mask_kind, workspace=it["ws"])
+            if self.lpt_weights is None:
+                lb.plan_varlen(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], self.mask_kind, workspace=it["ws"])
+            else:
+                lb.plan_varlen_weighted(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], *self.lpt_weights,
+                                        mask_kind=self.mask_kind, workspace=it["ws"])
             if ev is not None:
                 ev[1].record()
             lb.attn_run(it["q"], it["k"], it["v"], it["out"], it["lse"], it["ws"])
@@ -654,6 +659,10 @@ def main():
     ap.add_argument("--overlap", type=int, default=4,
                     help="zigzag, cp_job with --no-ring: streams the ring steps' attention launches are spread over "
                          "(0: one)")
+    ap.add_argument("--lpt-weights", default=None, metavar="blocks|BLOCK,PAIR",
+                    help="longtail, pairA, pairB, shared_question: queue the tiles by BLOCK * key blocks + "
+                         "PAIR * G * pairs (lb_plan_varlen_weighted; 'blocks' is 1,0) instead of lb_plan_varlen's "
+                         "fitted weights")
     ap.add_argument("--worker-records", default=None, metavar="PATH",
                     help="write the last launch's per-workgroup records and its plan (JSON) to PATH")
     args = ap.parse_args()
@@ -680,6 +689,13 @@ def main():
     log(f"bench: building workload {args.workload}")
     w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule,
                       overlap=args.overlap, ring=not args.no_ring)
+    if args.lpt_weights is not None:
+        if not isinstance(w, VarlenStep):
+            sys.exit("--lpt-weights applies to the varlen forward workloads")
+        bw, pw = (1, 0) if args.lpt_weights == "blocks" else map(int, args.lpt_weights.split(","))
+        w.lpt_weights = (bw, pw)
+    if isinstance(w, VarlenStep):
+        w.config = dict(w.config, lpt_weights=list(w.lpt_weights or (lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT)))
     graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 

@@ -24,7 +24,8 @@
  * keeps only the key spans that hold visible pairs (DCP's computation blocks,
  * section 3.2; MagiAttention's full/causal slices, section 4.4), bills each
  * tile its exact visible-pair count (Libra TAP, section 3.2), and orders tiles
- * longest first (VRSP, section 2.1; "数据并行负载均衡", section 4.4).  A
+ * longest first by an estimate of their time (VRSP, section 2.1; "数据并行负载均衡",
+ * sections 4.2 and 4.4: LPT on a fitted load model).  A
  * persistent attention kernel then pulls (tile, key/value head) items from
  * that queue, so the next free compute unit always takes the largest
  * remaining item.
@@ -94,12 +95,18 @@ enum {
 #define LB_NO_LOWER_BOUND (1 << 30) /* k_lo of a span whose keys have no lower bound */
 
 /*
- * One tile of the plan, as lb_read_plan returns it, in queue order: `blocks`
- * descending, ties in natural order (fragment order, then tile order).  A tile's
- * time is set by the key blocks it sweeps, a short tile costing as much as a full
- * one ("03 · 长文负载均衡", section 3.3: a query block shorter than one tile is
- * billed as a whole tile), and items go out longest first ("数据并行负载均衡",
- * section 4.4, LPT on estimated cost).
+ * One tile of the plan, as lb_read_plan returns it, in queue order: ordering cost
+ * descending, ties in natural order (fragment order, then tile order).  The cost of
+ * the varlen forward's plans (lb_plan_varlen, lb_varlen_attn_fwd) is the fitted time
+ * estimate of lb_plan_varlen_weighted; that of every other plan is `blocks`.  A tile's
+ * time is set mostly by the key blocks it sweeps, a short tile costing
+ * as much as a full one ("03 · 长文负载均衡", section 3.3: a query block shorter than
+ * one tile is billed as a whole tile), and items go out longest first ("数据并行负载
+ * 均衡", section 4.4, LPT on estimated cost).  Costs are sorted on 15 bits: each is
+ * divided by the least power of two that brings the plan's largest cost to 32767 or
+ * below, rounding up, so the order is exact while no cost exceeds 32767 (a block count
+ * does only for a document of over two million tokens) and a tile with work always
+ * precedes every tile without.
  */
 typedef struct {
   int32_t q_start;               /* first query row (index into the call's query rows) */
@@ -112,7 +119,8 @@ typedef struct {
   int32_t k_pos0[LB_MAX_SPANS];  /* mask position of the span's first key */
   int32_t k_lo[LB_MAX_SPANS];    /* lower bound: key j of the span is visible to a row at position p
                                     only if k_lo + j >= p (LB_NO_LOWER_BOUND: no such bound) */
-  int32_t blocks;                /* sum over spans of ceil(k_len / LB_BLOCK_KEYS): the order key */
+  int32_t blocks;                /* sum over spans of ceil(k_len / LB_BLOCK_KEYS): the order key,
+                                    or its main term in the varlen forward's fitted estimate */
   int32_t reserved;
 } lb_plan_tile;
 
@@ -205,7 +213,8 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
                             hipStream_t stream);
 
 /*
- * The two halves of the forward calls.  lb_varlen_attn_fwd is lb_plan_varlen followed by
+ * The two halves of the forward calls.  lb_plan_varlen queues the tiles by the fitted time
+ * estimate that lb_plan_varlen_weighted below describes.  lb_varlen_attn_fwd is lb_plan_varlen followed by
  * lb_attn_run (bf16 out); lb_block_attn_fwd is lb_plan_block followed by lb_attn_run (fp32
  * out).  Split, a plan can serve several attention launches -- every layer of a model sees
  * the same cu_seqlens -- and each half can be timed on its own.  The plan stays valid in
@@ -220,6 +229,33 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
 lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
                          int32_t kv_heads, int32_t d, int32_t mask_kind, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lb_plan_varlen with the caller's weights for the time estimate that orders the queue
+ * ("数据并行负载均衡", section 4.2: a load model fitted to measured step times; section
+ * 4.4: LPT on that estimate).  A tile's ordering cost is
+ *     block_weight * blocks + pair_weight * (heads / kv_heads) * cost
+ * with `blocks` and `cost` (visible pairs of one head) as in lb_plan_tile; the per-item
+ * constant of a fitted model is left out, since it shifts every item alike.  Tiles,
+ * spans and the workspace layout are those of lb_plan_varlen; only the queue order can
+ * differ, and lb_attn_run runs the plan as any other.  lb_plan_varlen is this call with
+ * LB_LPT_FIT_BLOCK_WEIGHT and LB_LPT_FIT_PAIR_WEIGHT; block_weight = 1, pair_weight = 0
+ * orders by key blocks alone.
+ *   block_weight  1 .. LB_LPT_BLOCK_WEIGHT_MAX (a tile with work never costs 0)
+ *   pair_weight   0 .. LB_LPT_PAIR_WEIGHT_MAX
+ * Weights out of range: LB_EINVAL; every other argument and error as lb_plan_varlen.
+ * LB_LPT_FIT_BLOCK_WEIGHT : LB_LPT_FIT_PAIR_WEIGHT is the ratio fitted to this library's
+ * attention kernel on MI355X by least squares over its workgroups' busy times on six
+ * workloads: 1.37 us per key block, 3.3e-5 us per query-head pair.
+ */
+#define LB_LPT_BLOCK_WEIGHT_MAX ((1u << 24) - 1)
+#define LB_LPT_PAIR_WEIGHT_MAX ((1u << 16) - 1)
+#define LB_LPT_FIT_BLOCK_WEIGHT 41515u
+#define LB_LPT_FIT_PAIR_WEIGHT 1u
+lb_status lb_plan_varlen_weighted(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                                  int32_t heads, int32_t kv_heads, int32_t d, int32_t mask_kind,
+                                  uint32_t block_weight, uint32_t pair_weight, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,

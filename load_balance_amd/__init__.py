@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.lb_block_attn_fwd.restype = ctypes.c_int
     L.lb_plan_varlen.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_varlen.restype = ctypes.c_int
+    U32 = ctypes.c_uint32
+    L.lb_plan_varlen_weighted.argtypes = [P, I32, I32, I32, I32, I32, I32, U32, U32, P, SZ, P]
+    L.lb_plan_varlen_weighted.restype = ctypes.c_int
     L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_block.restype = ctypes.c_int
     L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P]
@@ -316,9 +319,7 @@ def _meta(pos, doc, n, side, device):
     _dev(doc, f"{side}_doc", torch.int32, (n,), device)
 
 
-def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAUSAL_DOC, workspace=None,
-                stream=None):
-    """First half of varlen_attn_fwd: writes the tile plan into ``workspace`` (returned)."""
+def _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace):
     _dev(cu_seqlens, "cu_seqlens", torch.int32)
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise LBError("cu_seqlens must be 1-D with at least two entries")
@@ -327,9 +328,36 @@ def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAU
         workspace = new_workspace(total_tokens, max(1, n_seg), heads, kv_heads, cu_seqlens.device)
     _ws(workspace, device=cu_seqlens.device)
     _gpu(cu_seqlens, "cu_seqlens")
+    return n_seg, workspace
+
+
+def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAUSAL_DOC, workspace=None,
+                stream=None):
+    """First half of varlen_attn_fwd: writes the tile plan into ``workspace`` (returned), its
+    queue ordered by the fitted estimate (LPT_FIT_BLOCK_WEIGHT, LPT_FIT_PAIR_WEIGHT)."""
+    n_seg, workspace = _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace)
     _check(lib().lb_plan_varlen(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d, int(mask_kind),
                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_plan_varlen")
+    return workspace
+
+
+# The per-item cost fitted to the attention kernel on MI355X, as LPT weights: 1.37 us per
+# key block against 3.3e-5 us per query-head pair.
+LPT_FIT_BLOCK_WEIGHT = 41515
+LPT_FIT_PAIR_WEIGHT = 1
+
+
+def plan_varlen_weighted(cu_seqlens, total_tokens, heads, kv_heads, d, block_weight, pair_weight,
+                         mask_kind=MASK_CAUSAL_DOC, workspace=None, stream=None):
+    """plan_varlen with the queue ordered by block_weight * blocks + pair_weight * G * pairs
+    ("数据并行负载均衡", sections 4.2 and 4.4: LPT on a fitted load estimate); (1, 0) orders by
+    key blocks alone."""
+    n_seg, workspace = _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace)
+    _check(lib().lb_plan_varlen_weighted(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d,
+                                         int(mask_kind), int(block_weight), int(pair_weight), _ptr(workspace),
+                                         workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_plan_varlen_weighted")
     return workspace
 
 

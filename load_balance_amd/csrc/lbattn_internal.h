@@ -126,6 +126,9 @@ struct PlanArgs {
   int32_t n_slices;
   int32_t n_q, n_kv;
   int32_t tile_rows, heads, kv_heads;
+  // LPT ordering cost of a tile: block_weight * key blocks + pair_weight * G * visible pairs
+  uint32_t block_weight = 1;  // 1 .. LB_LPT_BLOCK_WEIGHT_MAX
+  uint32_t pair_weight = 0;   // 0 .. LB_LPT_PAIR_WEIGHT_MAX
   char* ws;
   WsLayout L;
 };

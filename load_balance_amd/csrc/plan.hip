@@ -8,10 +8,13 @@
 // carries its exact number of visible (query, key) pairs (section 3.2, Libra
 // TAP), and tiles are handed out largest first (section 2.1, VRSP's LPT
 // placement; "数据并行负载均衡", section 4.4, LPT on estimated cost).  The
-// estimate that orders them is the number of 64-key blocks a tile sweeps: the
-// attention kernel spends the same time on a block whatever share of it is
-// visible, and a tile of few rows as long as a full one (section 3.3: a query
-// block shorter than one tile is billed as a whole tile).
+// estimate that orders them is a linear cost wb * blocks + wp * G * pairs: blocks
+// is the number of 64-key blocks a tile sweeps (the attention kernel spends the
+// same time on a block whatever share of it is visible, and a tile of few rows as
+// long as a full one; section 3.3: a query block shorter than one tile is billed
+// as a whole tile), pairs its visible (query, key) pairs, G the query heads one
+// item serves.  The caller picks the weights (section 4.2 of the same page: a
+// load model fitted to measured times); wb = 1, wp = 0 orders by blocks alone.
 //
 // One workgroup of 1024 threads does everything: the metadata is a few
 // thousand integers, far below what a multi-workgroup launch would pay off.
@@ -19,7 +22,7 @@
 //      consecutive position (block path); spans = keys the fragment may see.
 //   2. tiles: each fragment cut into `tile_rows` rows from its start; spans
 //      clipped to what the tile's last row sees; pairs in closed form, blocks.
-//   3. order: bitonic sort of (blocks descending, natural index) keys in LDS.
+//   3. order: sort of (cost descending, natural index) keys in LDS.
 // The plan lands in the caller's workspace; the attention kernel reads it.
 #include "lbattn_internal.h"
 
@@ -27,12 +30,14 @@ namespace lb {
 namespace {
 
 constexpr int NT = kPlanThreads;
-// Sort keys are 32 bits: (kBlocksMax - blocks) above kIndexBits bits of natural index, so
-// that ascending keys are blocks descending, ties in natural order.  A tile sweeping more
-// than kBlocksMax key blocks (a document of over two million tokens) sorts as kBlocksMax.
+// Sort keys are 32 bits: (kCostMax - q) above kIndexBits bits of natural index, so that
+// ascending keys are costs descending, ties in natural order.  q is the tile's cost divided
+// by 2^shift and rounded up, shift the least that brings the plan's largest cost to
+// kCostMax or below: with costs up to kCostMax the order is exact, and a tile with work
+// never ties with an empty one (cost 0).
 constexpr int kIndexBits = 17;
 constexpr uint32_t kIndexMask = (1u << kIndexBits) - 1;
-constexpr uint32_t kBlocksMax = (1u << (32 - kIndexBits)) - 1;
+constexpr uint32_t kCostMax = (1u << (32 - kIndexBits)) - 1;
 static_assert(kSortCap <= (int)kIndexMask + 1, "a tile index must fit the key");
 
 constexpr int kPlanWaves = NT / 64;
@@ -47,6 +52,7 @@ struct PlanShared {
   int32_t n_empty;
   int32_t has_lower;
   unsigned long long pairs;
+  unsigned long long max_cost;
 };
 
 // Exclusive prefix sum of one value per thread across the workgroup (thread order),
@@ -241,6 +247,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   if (tid == 0) {
     sh.err = 0;
     sh.pairs = 0;
+    sh.max_cost = 0;
     sh.n_empty = 0;
     sh.has_lower = 0;
   }
@@ -467,11 +474,13 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     }
   }
   __syncthreads();
-  // sort keys of this thread's tiles, (2^40 - 1 - blocks) << 24 | natural index: ascending
-  // order is blocks descending with ties in natural order, and every key is unique
-  uint32_t my_keys[kMaxTilesPerThread];
+  // ordering cost of this thread's tiles; the weights are below 2^24 and 2^16, so with
+  // blocks below 2^25, G <= 8 and pairs below 2^39 (256 rows by 2^31 keys) a cost stays
+  // below 2^59
+  unsigned long long my_cost[kMaxTilesPerThread];
   if (sh.err == 0) {
-    unsigned long long my_pairs = 0;
+    unsigned long long my_pairs = 0, my_max = 0;
+    const unsigned long long wp = (unsigned long long)a.pair_weight * (unsigned)(a.heads / a.kv_heads);
 #pragma unroll
     for (int k = 0; k < kMaxTilesPerThread; ++k) {
       const int t = tid + k * NT;
@@ -528,11 +537,29 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       ntiles[t] = T;
       if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
-      my_keys[k] = ((kBlocksMax - min((uint32_t)blocks, kBlocksMax)) << kIndexBits) | (uint32_t)t;
+      my_cost[k] = (unsigned long long)a.block_weight * (unsigned)blocks + wp * (unsigned long long)cost;
+      my_max = max(my_max, my_cost[k]);
     }
     atomicAdd(&sh.pairs, my_pairs);
+    atomicMax(&sh.max_cost, my_max);
   }
   __syncthreads();  // the staging areas are dead from here on; the sort buffer takes over
+
+  // sort keys: (kCostMax - q) << kIndexBits | natural index, q the rounded-up scaled cost;
+  // ascending keys are costs descending with ties in natural order, and every key is unique
+  uint32_t my_keys[kMaxTilesPerThread];
+  {
+    int shift = 0;
+    while (((sh.max_cost + (1ull << shift) - 1) >> shift) > kCostMax) ++shift;
+    const unsigned long long round = (1ull << shift) - 1;
+#pragma unroll
+    for (int k = 0; k < kMaxTilesPerThread; ++k) {
+      const int t = tid + k * NT;
+      if (t >= n_tiles) break;
+      const uint32_t q = (uint32_t)((my_cost[k] + round) >> shift);
+      my_keys[k] = ((kCostMax - q) << kIndexBits) | (uint32_t)t;
+    }
+  }
 
   // ---- 3. longest-first order of the unique keys; tiles copied to their queue positions --
   // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys

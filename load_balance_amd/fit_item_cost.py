@@ -6,19 +6,21 @@ Each file is what ``bench.py --workload <name> --worker-records <file>`` writes:
 persistent workgroup of the last launch its busy ticks (the 100 MHz device clock), the
 query-head pairs, key blocks and items it ran, and the plan's items in queue order.
 
-The queue orders items longest first by their key-block count: the kernel does a whole key
-block for any block the mask touches ("03 · 长文负载均衡", section 3.3, a short block billed
-as a whole tile).  The pages sort by a time estimate from a fitted cost model ("数据并行负载
-均衡", sections 4.3 and 4.4); this fits one to the kernel.  The fit is least squares of a
+The kernel does a whole key block for any block the mask touches ("03 · 长文负载均衡",
+section 3.3, a short block billed as a whole tile), so the key-block count carries most of
+an item's time.  The pages sort by a time estimate from a fitted cost model ("数据并行负载
+均衡", sections 4.2 to 4.4); this fits one to the kernel.  The fit is least squares of a
 workgroup's busy microseconds on (pairs, blocks, items, 1): the per-pair term is the part
 of the cost that the partial blocks on a causal diagonal save or not, the per-item term
 the prologue and epilogue of an item, the constant the workgroup's start and drain.
 
 Since every workgroup pops from a shared queue, a per-item constant shifts every item's
-key alike and cannot change a longest-first order; only the pairs term can.  The report
-gives, per workload, the makespan over mean busy time predicted by list scheduling under
-the fitted costs for the plan's order (blocks) and for the order by fitted cost, next to
-the measured max/mean of the workgroups' busy time.
+key alike and cannot change a longest-first order; only the ratio of the block and pair
+terms can.  That ratio, as integer weights, is what lb_plan_varlen_weighted takes (the
+library's default, LB_LPT_FIT_BLOCK_WEIGHT : LB_LPT_FIT_PAIR_WEIGHT = 41515 : 1, came from
+this fit).  The report gives, per workload, the makespan over mean busy time predicted by
+list scheduling under the fitted costs for the recorded plan's order and for the order by
+the new fit, next to the measured max/mean of the workgroups' busy time.
 """
 from __future__ import annotations
 
@@ -73,7 +75,7 @@ def compare_orders(d, m):
     cost = [m["per_pair_us"] * t["cost"] * group + m["per_block_us"] * t["blocks"]
             + m["per_item_us"] for t in d["plan"]]
     out = {}
-    for name, order in (("blocks", list(range(len(cost)))),
+    for name, order in (("plan", list(range(len(cost)))),
                         ("fitted", sorted(range(len(cost)), key=lambda i: -cost[i]))):
         times = [cost[i] for i in order for _ in range(reps)]
         mk, mean = list_schedule(times, per_xcd_wg)
@@ -90,7 +92,9 @@ if __name__ == "__main__":
     model, quality = fit(files)
     print(json.dumps({k: round(float(v), 5) for k, v in model.items()}),
           f"R^2 {quality['r2']:.4f}, max relative error {quality['max_rel_err']:.3f}")
+    if model["per_pair_us"] > 0:
+        print(f"LPT weights (block, pair): ({round(model['per_block_us'] / model['per_pair_us'])}, 1)")
     for f, d in zip(sys.argv[1:], files):
         c = compare_orders(d, model)
-        print(f"{d['workload']:>16}: max/mean busy measured {c['measured']:.4f}, predicted blocks order "
-              f"{c['blocks']:.4f}, fitted order {c['fitted']:.4f} ({c['reordered_items']} items move)")
+        print(f"{d['workload']:>16}: max/mean busy measured {c['measured']:.4f}, predicted plan order "
+              f"{c['plan']:.4f}, order by this fit {c['fitted']:.4f} ({c['reordered_items']} items move)")

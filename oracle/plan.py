@@ -33,8 +33,10 @@ Tiling rule written out here (the plan the library must reproduce exactly):
 4. *Cost* of a tile = its exact number of visible (query, key) pairs for one
    head, counted row by row.  *Blocks* of a tile = sum over its spans of
    ceil(keys kept / BLOCK_KEYS), the key blocks of BLOCK_KEYS keys it sweeps.
-5. *Order*: blocks descending, ties by natural order (fragment order, then
-   tile order inside the fragment).
+5. *Order*: estimated time descending, ties by natural order (fragment order,
+   then tile order inside the fragment).  The estimate is the block count, or a
+   weighted sum of blocks and pairs (``lpt_order_weighted``); either is scaled
+   to 15 bits as ``quantised`` states before ordering.
 
 Transposed tiling, for the key/value gradients of the backward (each key block
 gathers the query rows that see it):
@@ -233,22 +235,57 @@ def tiles_t(frags, bm):
     return out
 
 
-# Orders are taken on key blocks capped at ORDER_CAP: a tile sweeping more blocks (a
-# document of over two million tokens) is ordered as if it swept ORDER_CAP.  (Reading: the
-# order only needs to put the longest tiles first; the planner's 32-bit sort key holds 15
-# bits of block count.)
-ORDER_CAP = (1 << 15) - 1
+# Orders are taken on costs of at most COST_MAX: every cost is divided by the least power of
+# two 2^s that brings the largest cost to COST_MAX or below, rounding up.  (Reading: the
+# pages fix no resolution for the estimate; the order only needs to put the longest tiles
+# first, and the planner's 32-bit sort key holds 15 bits of cost.  Rounding up keeps every
+# tile with work ahead of every tile without.)
+COST_MAX = (1 << 15) - 1
+
+
+def quantised(costs):
+    """Non-negative integer costs scaled to at most COST_MAX: ceil(c / 2^s), least such s."""
+    m = max(costs, default=0)
+    s = 0
+    while -(-m // (1 << s)) > COST_MAX:
+        s += 1
+    return [-(-c // (1 << s)) for c in costs]
+
+
+def order_by_cost(costs):
+    """Indices by quantised cost descending, ties in natural order."""
+    q = quantised(costs)
+    return sorted(range(len(q)), key=lambda i: (-q[i], i))
 
 
 def lpt_order(tile_list, key="blocks"):
-    """Indices of tiles, `key` descending (capped at ORDER_CAP), ties in natural order."""
-    return sorted(range(len(tile_list)), key=lambda i: (-min(tile_list[i][key], ORDER_CAP), i))
+    """Indices of tiles, `key` descending (after quantisation), ties in natural order."""
+    return order_by_cost([t[key] for t in tile_list])
+
+
+def weighted_cost(t, block_weight, pair_weight, group):
+    """A tile's time estimate: a linear load model in its key blocks and in the visible
+    (query, key) pairs of the `group` query heads one item serves ("数据并行负载均衡",
+    section 4.2: the load is fitted as a linear model of the work terms; the per-item
+    constant of such a fit is dropped, as it moves every item alike)."""
+    return block_weight * t["blocks"] + pair_weight * group * t["cost"]
+
+
+def lpt_order_weighted(tile_list, block_weight, pair_weight, group):
+    """LPT order on the weighted estimate ("数据并行负载均衡", section 4.4)."""
+    return order_by_cost([weighted_cost(t, block_weight, pair_weight, group) for t in tile_list])
 
 
 def plan(frags, bm):
     """The full reference plan: tiles in longest-first order."""
     t = tiles(frags, bm)
     return [t[i] for i in lpt_order(t)]
+
+
+def plan_weighted(frags, bm, block_weight, pair_weight, group):
+    """The plan with tiles in the order of the weighted estimate."""
+    t = tiles(frags, bm)
+    return [t[i] for i in lpt_order_weighted(t, block_weight, pair_weight, group)]
 
 
 def merge_step_plans(plans):

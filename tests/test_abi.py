@@ -135,6 +135,13 @@ def test_split_host_checks(L):
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 5, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 64, 0, FAKE, need - 1, None) == LB_EWORKSPACE
     assert L.lb_plan_varlen(FAKE, 3, n, 2, 2, 48, 0, FAKE, need, None) == LB_EUNSUPPORTED
+    W = L.lb_plan_varlen_weighted
+    assert W(FAKE, 3, n, 2, 2, 64, 0, 0, 0, FAKE, need, None) == LB_EINVAL  # block weight 0
+    assert W(FAKE, 3, n, 2, 2, 64, 0, 1 << 24, 0, FAKE, need, None) == LB_EINVAL
+    assert W(FAKE, 3, n, 2, 2, 64, 0, 1, 1 << 16, FAKE, need, None) == LB_EINVAL
+    assert W(None, 3, n, 2, 2, 64, 0, 1, 0, FAKE, need, None) == LB_EINVAL
+    assert W(FAKE, 3, n, 2, 2, 64, 0, 41515, 1, FAKE, need - 1, None) == LB_EWORKSPACE
+    assert W(FAKE, 3, n, 2, 2, 48, 0, 41515, 1, FAKE, need, None) == LB_EUNSUPPORTED
     assert L.lb_plan_block(None, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -2, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, 64, None) == LB_EWORKSPACE

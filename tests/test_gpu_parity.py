@@ -2,7 +2,9 @@
 
 Tolerances (bf16 inputs, fp32 accumulation): out max |d| <= 2e-2 and mean
 |d| <= 2e-3, lse max |d| <= 5e-3.  Plans (tiles, spans, exact pair costs and
-longest-first order) must equal the oracle's enumerator bit for bit.
+longest-first order) must equal the oracle's enumerator bit for bit; the varlen
+forward's queue follows the fitted estimate (41515 per key block, 1 per
+query-head pair).
 Large configurations are compared on sampled rows that the oracle computes
 one by one; small ones on every row.
 """
@@ -81,8 +83,13 @@ def sample_rows(lengths, bm, n_random, seed, cap=None):
 
 
 def plan_ref_varlen(pack, mask="causal_doc"):
+    return plan_ref_weighted(pack, lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT, mask)
+
+
+def plan_ref_weighted(pack, block_weight, pair_weight, mask="causal_doc"):
     bm = lb.tile_rows(pack["heads"], pack["kv_heads"], pack["d"])
-    return OP.plan(OP.fragments_varlen(pack["cu_seqlens"], mask), bm)
+    return OP.plan_weighted(OP.fragments_varlen(pack["cu_seqlens"], mask), bm, block_weight, pair_weight,
+                            pack["heads"] // pack["kv_heads"])
 
 
 def assert_same_plan(gpu, ref, what):
@@ -220,6 +227,78 @@ def test_plans_beyond_16k_tiles(tokens, H, Hkv):
         f"{e0.elapsed_time(e1) * 1e3:.0f} us")
     assert len(got) > 16384
     assert_same_plan(got, plan_ref_varlen(pack), f"{tokens}-token plan")
+
+
+# --------------------------------------------------------------------------
+# queue order on a fitted time estimate (lb_plan_varlen_weighted)
+# --------------------------------------------------------------------------
+def run_weighted(pack, block_weight, pair_weight, mask_kind=lb.MASK_CAUSAL_DOC):
+    T, H, Hkv, d = pack["tokens"], pack["heads"], pack["kv_heads"], pack["d"]
+    say(f"  plan_varlen_weighted T={T} H={H} Hkv={Hkv} d={d} weights=({block_weight}, {pair_weight}) "
+        f"mask={mask_kind}")
+    q, k, v = dev_bf16(pack["q"]), dev_bf16(pack["k"]), dev_bf16(pack["v"])
+    cu = torch.from_numpy(np.asarray(pack["cu_seqlens"], dtype=np.int32)).cuda()
+    ws = lb.new_workspace(T, len(pack["lengths"]), H, Hkv)
+    lb.plan_varlen_weighted(cu, T, H, Hkv, d, block_weight, pair_weight, mask_kind=mask_kind, workspace=ws)
+    out = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    lb.attn_run(q, k, v, out, lse, ws)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    return out, lse, ws
+
+
+def test_weighted_plan_longtail(longtail):
+    """The 32K long-tail pack queued by key blocks alone (weights 1, 0) and by the fitted
+    estimate through the explicit call: both orders equal the oracle's bit for bit, they
+    differ (the pair term orders tiles of equal block count), the fitted one is
+    lb_plan_varlen's, and every order writes the same bits, since each item computes its own
+    rows whatever its place in the queue."""
+    p = longtail
+    out_b, lse_b, ws_b = run_weighted(p, 1, 0)
+    blocks_order = lb.read_plan(ws_b)
+    assert_same_plan(blocks_order, plan_ref_weighted(p, 1, 0), "32K long-tail block-count plan")
+    assert [t["blocks"] for t in blocks_order] == sorted((t["blocks"] for t in blocks_order), reverse=True)
+    out_w, lse_w, ws_w = run_weighted(p, 41515, 1)
+    fitted = lb.read_plan(ws_w)
+    assert_same_plan(fitted, plan_ref_weighted(p, 41515, 1), "32K long-tail fitted plan")
+    moved = sum(1 for a, b in zip(fitted, blocks_order) if a != b)
+    say(f"  {moved} of {len(fitted)} queue positions differ between the two orders")
+    assert moved > 0
+    recs = lb.read_worker_timing(ws_b)
+    assert sum(x["items"] for x in recs) == len(blocks_order) * 8
+    assert sum(x["blocks"] for x in recs) == 8 * sum(t["blocks"] for t in blocks_order)
+    out_d, lse_d, ws_d = run_varlen(p)
+    assert lb.read_plan(ws_d) == fitted
+    for o, l in ((out_w, lse_w), (out_d, lse_d)):
+        assert torch.equal(o, out_b) and torch.equal(l, lse_b)
+
+
+@pytest.mark.parametrize("H,Hkv,d,weights,mask", [
+    (8, 2, 128, (41515, 1), "causal_doc"),
+    (2, 2, 64, (1, (1 << 16) - 1), "causal_doc"),
+    (32, 8, 128, ((1 << 24) - 1, (1 << 16) - 1), "causal_doc"),
+    (16, 2, 128, (1, 0), "shared_question"),
+    (8, 8, 64, (41515, 1), "shared_question"),
+])
+def test_weighted_plan_every_row(H, Hkv, d, weights, mask):
+    """Small packs with ragged tails and 1-token documents under weights from blocks alone to
+    pairs dominating, and the largest weights the call accepts (largest costs, widest
+    scaling): the plan equals the oracle's, every row equals the float64 oracle, and the
+    outputs equal the block-count plan's bit for bit."""
+    r = np.random.default_rng(H * 100 + Hkv * 10 + d + weights[1])
+    lengths = [1, 700, 3, 1, 257, 64, 129, 1000, 2] if mask == "causal_doc" else [300, 41, 180, 7, 1]
+    T = sum(lengths)
+    q, k, v = workloads.values(r, T, H, Hkv, d)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=H, kv_heads=Hkv,
+                d=d, q=q, k=k, v=v)
+    kind = lb.MASK_CAUSAL_DOC if mask == "causal_doc" else lb.MASK_SHARED_QUESTION
+    out, lse, ws = run_weighted(pack, *weights, mask_kind=kind)
+    assert_same_plan(lb.read_plan(ws), plan_ref_weighted(pack, *weights, mask), f"weighted plan {weights}")
+    ref_o, ref_l = OA.varlen_attention(q, k, v, pack["cu_seqlens"], H, Hkv, mask=mask)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"weighted {weights} H={H} Hkv={Hkv} d={d}")
+    out_b, lse_b, _ = run_varlen(pack, kind)
+    assert torch.equal(out, out_b) and torch.equal(lse, lse_b)
 
 
 # --------------------------------------------------------------------------

@@ -126,6 +126,58 @@ def test_lpt_order():
     assert by_cost == sorted(by_cost, reverse=True)
 
 
+def test_quantised_costs_closed_form():
+    """Costs up to 32767 order exactly; above, each is divided by the least power of two
+    that brings the largest to 32767 or below, rounding up."""
+    assert P.quantised([5, 32767, 0]) == [5, 32767, 0]
+    assert P.quantised([32768]) == [16384]
+    # 70000 / 2 = 35000 is still above 32767; / 4 rounds 69999 and 70000 up to 17500
+    assert P.quantised([70000, 69999, 1, 0]) == [17500, 17500, 1, 0]
+    assert P.order_by_cost([69999, 70000, 1, 0]) == [0, 1, 2, 3]  # equal after scaling: natural order
+    # a tile with work never ties with one without, however large the plan's largest cost
+    assert P.quantised([1 << 58, 1, 0]) == [1 << 14, 1, 0]
+    assert P.order_by_cost([0, 1, 1 << 58]) == [2, 1, 0]
+    assert P.quantised([]) == []
+
+
+def test_weighted_order_default_is_blocks():
+    """Weights (1, 0) give the block-count order, for any head grouping."""
+    cu = workloads.cu_from_lengths([700, 3, 1, 257, 64, 129, 1000, 2])
+    for mask in ("causal_doc", "shared_question"):
+        tl = P.tiles(P.fragments_varlen(cu, mask), 64)
+        for g in (1, 2, 4, 8):
+            assert P.lpt_order_weighted(tl, 1, 0, g) == P.lpt_order(tl)
+
+
+def test_weighted_order_pairs_break_block_ties():
+    """A 256-token causal document in 32-row tiles: tile k holds rows 32k .. 32k + 31, sweeps
+    ceil((32k + 32) / 64) blocks (1, 1, 2, 2, 3, 3, 4, 4) and holds sum of (r + 1) over its
+    rows = 1024k + 528 pairs.  By blocks, the two tiles of each block count keep their natural
+    order; with the fitted weights (41515 per block, 1 per pair) the later tile of each pair
+    has 1024 more pairs and goes first.  Largest cost 4 * 41515 + 7696 = 173756 is scaled by
+    2^3 (by 2^2 it would be 43439): tiles 7 and 6 become 21720 and 21592, still distinct."""
+    tl = P.tiles(P.fragments_varlen([0, 256]), 32)
+    assert [t["blocks"] for t in tl] == [1, 1, 2, 2, 3, 3, 4, 4]
+    assert [t["cost"] for t in tl] == [1024 * k + 528 for k in range(8)]
+    assert P.lpt_order(tl) == [6, 7, 4, 5, 2, 3, 0, 1]
+    assert P.lpt_order_weighted(tl, 41515, 1, 1) == [7, 6, 5, 4, 3, 2, 1, 0]
+    costs = [P.weighted_cost(t, 41515, 1, 1) for t in tl]
+    assert costs[7] == 173756 and P.quantised(costs)[6:] == [21592, 21720]
+
+
+def test_weighted_order_group_multiplies_pairs():
+    """The pair term counts the query heads an item serves: tile A (2 blocks, 100 pairs) and
+    tile B (1 block, 150 pairs) under weights (100, 1) cost 300 and 250 at G = 1 (A first),
+    400 and 400 at G = 2 (a tie: natural order), 600 and 700 at G = 4 (B first)."""
+    a = dict(blocks=2, cost=100)
+    b = dict(blocks=1, cost=150)
+    assert P.lpt_order_weighted([a, b], 100, 1, 1) == [0, 1]
+    assert P.lpt_order_weighted([b, a], 100, 1, 2) == [0, 1]
+    assert P.lpt_order_weighted([a, b], 100, 1, 2) == [0, 1]
+    assert P.lpt_order_weighted([a, b], 100, 1, 4) == [1, 0]
+    assert P.weighted_cost(b, 100, 1, 4) == 700
+
+
 def test_short_tile_is_billed_as_a_whole_tile():
     """"03 · 长文负载均衡", section 3.3: a query block shorter than one tile costs a whole
     tile.  A 4-row ragged tail of a 4100-token document sweeps 65 key blocks, more than
