@@ -193,6 +193,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
   const int row_bytes = a.kv_heads * D * 2;  // one token's K (or V) across all kv heads
   TileCopier<D, BN> copier;  // this wave's share of a K or V block's copy
   copier.init(row_bytes, wave, lane);
+  TrOffsets<D> vt_off;  // lane offsets of the V^T fragments in a value block
+  vt_off.init(lane);
 
   const int G = a.group;
   const int head_in_group = wave % G;
@@ -445,18 +447,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
               if (!(kb * 32 + (i / 4) * 8 + (i % 4) < lim)) acc_s[kb][i] = -__builtin_inff();
         }
       }
-      // row max as a tree of 3-input maxima (depth 4, not a chain of 16)
+      // row max as a tree of 3-input maxima (depth 4, not a chain of 16).  The NaN-propagating
+      // maximum maps to gfx950's v_maximum3_f32 as it is; fmaxf would first quiet its inputs.
+      auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
       float t[11];
 #pragma unroll
       for (int i = 0; i < 10; ++i) {
         const int e = 3 * i;
-        t[i] = fmaxf(fmaxf(acc_s[e / 16][e % 16], acc_s[(e + 1) / 16][(e + 1) % 16]), acc_s[(e + 2) / 16][(e + 2) % 16]);
+        t[i] = mx2(mx2(acc_s[e / 16][e % 16], acc_s[(e + 1) / 16][(e + 1) % 16]), acc_s[(e + 2) / 16][(e + 2) % 16]);
       }
-      t[10] = fmaxf(acc_s[1][14], acc_s[1][15]);
-      const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
-      const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
-      const float m_own = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
-      const float mx = fmaxf(m_own, partner_lane(m_own, lane));
+      t[10] = mx2(acc_s[1][14], acc_s[1][15]);
+      const float u0 = mx2(mx2(t[0], t[1]), t[2]), u1 = mx2(mx2(t[3], t[4]), t[5]);
+      const float u2 = mx2(mx2(t[6], t[7]), t[8]), u3 = mx2(t[9], t[10]);
+      const float m_own = mx2(mx2(u0, u1), mx2(u2, u3));
+      const float mx = mx2(m_own, partner_lane(m_own, lane));
       const float m_tile = mx * c;
       const bool need = m_tile > m_used + kRescaleThreshold;  // false when the row saw nothing
       if (__any(need)) {
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       auto read_v = [&](int ks16, bf16x8* dst) {
 #pragma unroll
         for (int db = 0; db < kDb; ++db)
-          dst[db] = tr_frag<D>(vs, ks16 * 16, db, lane);
+          dst[db] = tr_frag_at<D>(vs, vt_off, ks16 * 16, db);
       };
       // An explicit pipeline, fenced so that the scheduler keeps it whatever surrounds the
       // loop: the MFMAs of chunk ks run with the exponentials of chunk ks + 1 between them,

@@ -56,13 +56,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // builtin's LDS write, would wait for every copy in flight before each LDS read of the loop;
 // the kernel waits for its copies itself (vmcnt) before the barrier that publishes a stage.
 // The copy takes its LDS address from m0, which the statement restores.  `lds` must be
-// wave-uniform.
+// wave-uniform (it is read from the first active lane, so that the compiler can keep it in
+// a scalar register wherever it cannot prove it uniform).
 __device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
       : "memory");
 }
 __device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
@@ -70,7 +71,7 @@ __device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, uint32_t lds, int voffs
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
       : "memory");
 }
 
@@ -95,6 +96,35 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int db, int 
     const char* p = tile + row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
     h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
   }
+  return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The same fragments with the lane's address arithmetic done once: for a fragment whose first
+// row r0 is a multiple of 16, rows r0 + i land on the chunk permutation of row i (swz reads
+// r mod 16 only), so each fragment is a lane offset fixed for the tile, per 32-wide d block
+// and half, plus r0 * 2D bytes, which the LDS read takes as its immediate offset.
+template <int D>
+struct TrOffsets {
+  int off[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int lg = lane & 15, gq = (lane >> 4) & 1, hh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int col = db * 32 + 16 * gq + 4 * (lg & 3);
+        const int row = 8 * q + 4 * hh + (lg >> 2);
+        off[db][q] = row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+      }
+  }
+};
+// tr_frag(tile, r0, db, lane) for r0 a multiple of 16
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag_at(const char* tile, const TrOffsets<D>& o, int r0, int db) {
+  bf16x4 h[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + o.off[db][q] + r0 * (D * 2)));
   return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
