@@ -231,6 +231,22 @@ constexpr int kMaxTilesPerThread = kSortCap / NT;
 constexpr int kRankSortMax = 2048;  // tiles ranked directly; larger plans take the bitonic sort
 static_assert(kRankSortMax % NT == 0 && kRankSortMax <= kSortCap, "");
 
+// Sum and maximum of a 64-bit value over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_u64(v, m);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = max(v, shfl_xor_u64(v, m));
+  return v;
+}
+
 __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   const int tid = threadIdx.x;
   char* ws = a.ws;
@@ -474,13 +490,18 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     }
   }
   __syncthreads();
-  // ordering cost of this thread's tiles; the weights are below 2^24 and 2^16, so with
-  // blocks below 2^25, G <= 8 and pairs below 2^39 (256 rows by 2^31 keys) a cost stays
-  // below 2^59
-  unsigned long long my_cost[kMaxTilesPerThread];
+  // ordering cost of a tile; the weights are below 2^24 and 2^16, so with blocks below 2^25,
+  // G <= 8 and pairs below 2^39 (256 rows by 2^31 keys) a cost stays below 2^59
+  const unsigned long long wp = (unsigned long long)a.pair_weight * (unsigned)(a.heads / a.kv_heads);
+  auto cost_of = [&](int blocks, int64_t pairs) -> unsigned long long {
+    return (unsigned long long)a.block_weight * (unsigned)blocks + wp * (unsigned long long)pairs;
+  };
+  // the order terms of this thread's first tiles, kept for the rank sort's keys
+  constexpr int kMine = kRankSortMax / NT;
+  int mine_blocks[kMine] = {};
+  int64_t mine_pairs[kMine] = {};
   if (sh.err == 0) {
     unsigned long long my_pairs = 0, my_max = 0;
-    const unsigned long long wp = (unsigned long long)a.pair_weight * (unsigned)(a.heads / a.kv_heads);
 #pragma unroll
     for (int k = 0; k < kMaxTilesPerThread; ++k) {
       const int t = tid + k * NT;
@@ -537,61 +558,79 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       ntiles[t] = T;
       if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
-      my_cost[k] = (unsigned long long)a.block_weight * (unsigned)blocks + wp * (unsigned long long)cost;
-      my_max = max(my_max, my_cost[k]);
+      my_max = max(my_max, cost_of(blocks, cost));
+      if (k < kMine) {
+        mine_blocks[k] = blocks;
+        mine_pairs[k] = cost;
+      }
     }
-    atomicAdd(&sh.pairs, my_pairs);
-    atomicMax(&sh.max_cost, my_max);
+    // one LDS atomic per wave: 1024 lanes updating one LDS word one after another would
+    // take longer than everything else in this phase
+    my_pairs = wave_sum_u64(my_pairs);
+    my_max = wave_max_u64(my_max);
+    if ((tid & 63) == 0) {
+      atomicAdd(&sh.pairs, my_pairs);
+      atomicMax(&sh.max_cost, my_max);
+    }
   }
   __syncthreads();  // the staging areas are dead from here on; the sort buffer takes over
 
   // sort keys: (kCostMax - q) << kIndexBits | natural index, q the rounded-up scaled cost;
-  // ascending keys are costs descending with ties in natural order, and every key is unique
-  uint32_t my_keys[kMaxTilesPerThread];
-  {
-    int shift = 0;
-    while (((sh.max_cost + (1ull << shift) - 1) >> shift) > kCostMax) ++shift;
-    const unsigned long long round = (1ull << shift) - 1;
-#pragma unroll
-    for (int k = 0; k < kMaxTilesPerThread; ++k) {
-      const int t = tid + k * NT;
-      if (t >= n_tiles) break;
-      const uint32_t q = (uint32_t)((my_cost[k] + round) >> shift);
-      my_keys[k] = ((kCostMax - q) << kIndexBits) | (uint32_t)t;
-    }
-  }
+  // ascending keys are costs descending with ties in natural order, and every key is unique.
+  // A tile's cost is recomputed from its blocks and pairs: kept in registers for the rank
+  // sort's (at most two per thread), read back from the tile's record for the bitonic sort
+  // (a cost for each of up to 32 tiles per thread would not stay in registers).
+  int shift = 0;
+  while (((sh.max_cost + (1ull << shift) - 1) >> shift) > kCostMax) ++shift;
+  const unsigned long long round = (1ull << shift) - 1;
+  auto key_of = [&](int t, int blocks, int64_t pairs) -> uint32_t {
+    const uint32_t q = (uint32_t)((cost_of(blocks, pairs) + round) >> shift);
+    return ((kCostMax - q) << kIndexBits) | (uint32_t)t;
+  };
 
   // ---- 3. longest-first order of the unique keys; tiles copied to their queue positions --
   // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys
-  // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS and
-  // one barrier, against the bitonic network's 55 barrier-separated passes at 1024 keys.
+  // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS,
+  // four keys per read, and one barrier, against the bitonic network's 55 barrier-separated
+  // passes at 1024 keys.
   if (sh.err == 0 && n_tiles > 0 && n_tiles <= kRankSortMax) {
+    uint32_t my_key[kMine];
 #pragma unroll
-    for (int k = 0; k < kMaxTilesPerThread; ++k) {
-      const int i = tid + k * NT;
-      if (i < n_tiles) sh.keys[i] = my_keys[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kRankSortMax / NT; ++k) {
+    for (int k = 0; k < kMine; ++k) {
       const int t = tid + k * NT;
-      if (t >= n_tiles) break;
-      const uint32_t key = my_keys[k];
-      int rank = 0;
-#pragma unroll 8
-      for (int i = 0; i < n_tiles; ++i) rank += sh.keys[i] < key ? 1 : 0;
-      tiles[rank] = ntiles[t];  // this thread's own tile, written by it in phase 2
-      order[rank] = rank;
+      my_key[k] = ~0u;
+      if (t < n_tiles) {
+        my_key[k] = key_of(t, mine_blocks[k], mine_pairs[k]);
+        sh.keys[t] = my_key[k];
+      }
+    }
+    const int n4 = (n_tiles + 3) & ~3;
+    if (tid < n4 - n_tiles) sh.keys[n_tiles + tid] = ~0u;  // above every key: never counted
+    __syncthreads();
+    int rank[kMine] = {};
+    const uint4* keys4 = reinterpret_cast<const uint4*>(sh.keys);
+#pragma unroll
+    for (int k = 0; k < kMine; ++k) {
+      if (k * NT >= n_tiles) break;  // no thread holds a k-th tile
+#pragma unroll 4
+      for (int i = 0; i < n4 / 4; ++i) {
+        const uint4 v = keys4[i];
+        rank[k] += (v.x < my_key[k] ? 1 : 0) + (v.y < my_key[k] ? 1 : 0) + (v.z < my_key[k] ? 1 : 0) +
+                   (v.w < my_key[k] ? 1 : 0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMine; ++k) {
+      if (tid + k * NT >= n_tiles) break;
+      tiles[rank[k]] = ntiles[tid + k * NT];  // this thread's own tile, written by it in phase 2
+      order[rank[k]] = rank[k];
     }
   } else if (sh.err == 0 && n_tiles > 0) {
     // bitonic sort of the keys in LDS
     int n_pad = 1;
     while (n_pad < n_tiles) n_pad <<= 1;
-#pragma unroll
-    for (int k = 0; k < kMaxTilesPerThread; ++k) {
-      const int i = tid + k * NT;
-      if (i < n_pad) sh.keys[i] = i < n_tiles ? my_keys[k] : ~0u;
-    }
+    for (int i = tid; i < n_pad; i += NT)
+      sh.keys[i] = i < n_tiles ? key_of(i, ntiles[i].blocks, ntiles[i].cost) : ~0u;
     __syncthreads();
     // phases k = 2 .. min(n_pad, 64) pair lanes of one wave only: all in registers at once
     bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
