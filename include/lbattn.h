@@ -288,7 +288,7 @@ lb_status lb_plan_block_steps(const int32_t* q_pos, const int32_t* q_doc, int32_
  * step ("数据并行负载均衡", section 4.4: LPT over all items; "03 · 长文负载均衡", section
  * 3.2: only blocks with visible pairs become work), and one launch runs it, each step's
  * partial (out, lse) into its own buffers as lb_attn_run would write it, bit for bit.  The
- * partials are then merged with lb_lse_merge in step order, as before.
+ * partials are then merged in step order (lb_lse_merge_parts, or lb_lse_merge step after step).
  *
  * lb_ring_workspace_bytes: bytes of a ring workspace for n_steps steps, each within the
  *   bounds given to lb_workspace_bytes (0 if out of range).
@@ -374,6 +374,21 @@ lb_status lb_attn_run_lower(const void* q, const void* k, const void* v, int32_t
  */
 lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const float* lse_b,
                        int32_t n_rows, int32_t heads, int32_t d, hipStream_t stream);
+
+/*
+ * The merges of a ring's partials in one pass: parts 1 .. n_parts - 1 merged into part 0 in
+ * index order, each as lb_lse_merge would merge it, with the same bits as n_parts - 1 calls
+ * of lb_lse_merge in sequence ("长序列训练与上下文并行", Ring Attention: the step results are
+ * folded into the running one in step order).  A row is read from a partial only where
+ * that partial has a visible key (lse != -inf) and written once; part 0's row is not read
+ * where the first merge that touches the row keeps no share of it.
+ *   out, lse  host arrays of n_parts device pointers, each as lb_lse_merge's out_a, lse_a
+ *             (fp32 [n_rows][heads][d], [heads][n_rows]); distinct; out[0], lse[0] written
+ *   2 <= n_parts <= LB_MAX_PLAN_STEPS; d a multiple of 4, at most 1024 (else LB_EUNSUPPORTED)
+ * Argument errors return LB_EINVAL before anything is enqueued.
+ */
+lb_status lb_lse_merge_parts(float* const* out, float* const* lse, int32_t n_parts, int32_t n_rows, int32_t heads,
+                             int32_t d, hipStream_t stream);
 
 /*
  * ---- Backward -------------------------------------------------------------------

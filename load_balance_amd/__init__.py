@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.lb_attn_run_lower.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run_lower.restype = ctypes.c_int
     L.lb_lse_merge.argtypes = [P, P, P, P, I32, I32, I32, P]
+    L.lb_lse_merge_parts.argtypes = [P, P, I32, I32, I32, I32, P]
+    L.lb_lse_merge_parts.restype = ctypes.c_int
     L.lb_lse_merge.restype = ctypes.c_int
     L.lb_plan_slices.argtypes = [P, I32, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_slices.restype = ctypes.c_int
@@ -512,6 +514,27 @@ def lse_merge(out_a, lse_a, out_b, lse_b, stream=None):
                             ctypes.c_void_p(_stream(stream)))
     _check(st, "lb_lse_merge")
     return out_a, lse_a
+
+
+def lse_merge_parts(outs, lses, stream=None):
+    """In place: (outs[0], lses[0]) <- the merge of every partial, 1, 2, ... in order, in one
+    pass; the same bits as lse_merge step after step.  fp32 [R,H,d] and [H,R] each."""
+    if len(outs) != len(lses) or not 2 <= len(outs) <= MAX_PLAN_STEPS:
+        raise LBError(f"lse_merge_parts takes 2 to {MAX_PLAN_STEPS} partials, as many lse as out")
+    _dev(outs[0], "outs[0]", torch.float32)
+    if outs[0].dim() != 3:
+        raise LBError("outs[0] must be [R, H, d]")
+    R, H, d = outs[0].shape
+    dev = outs[0].device
+    for i, (o, l) in enumerate(zip(outs, lses)):
+        _dev(o, f"outs[{i}]", torch.float32, (R, H, d), dev)
+        _dev(l, f"lses[{i}]", torch.float32, (H, R), dev)
+    _gpu(outs[0], "outs[0]")
+    P = ctypes.c_void_p
+    st = lib().lb_lse_merge_parts((P * len(outs))(*[_ptr(o) for o in outs]), (P * len(lses))(*[_ptr(l) for l in lses]),
+                                  len(outs), R, H, d, ctypes.c_void_p(_stream(stream)))
+    _check(st, "lb_lse_merge_parts")
+    return outs[0], lses[0]
 
 
 def read_device_error(workspace, stream=None) -> int:

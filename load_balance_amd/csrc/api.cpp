@@ -547,6 +547,27 @@ lb_status lb_lse_merge(float* out_a, float* lse_a, const float* out_b, const flo
   return launch_lse_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
+lb_status lb_lse_merge_parts(float* const* out, float* const* lse, int32_t n_parts, int32_t n_rows, int32_t heads,
+                             int32_t d, hipStream_t stream) {
+  if (!out || !lse || n_parts < 2 || n_parts > kMaxPlanSteps) return LB_EINVAL;
+  if (n_rows < 0 || heads <= 0 || d <= 0) return LB_EINVAL;
+  if (d % 4 != 0 || d > 1024) return LB_EUNSUPPORTED;
+  MergePartsArgs m{};
+  for (int i = 0; i < n_parts; ++i) {
+    if (!out[i] || !lse[i] || !aligned(out[i], 16) || !aligned(lse[i], 4)) return LB_EINVAL;
+    for (int o = 0; o < i; ++o)
+      if (out[o] == out[i] || lse[o] == lse[i]) return LB_EINVAL;
+    m.out[i] = out[i];
+    m.lse[i] = lse[i];
+  }
+  m.n_parts = n_parts;
+  m.n_rows = n_rows;
+  m.heads = heads;
+  m.d = d;
+  if (n_rows == 0) return LB_OK;
+  return launch_lse_merge_parts(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
 lb_status lb_plan_slices(const lb_mask_slice* slices, int32_t n_slices, int32_t n_q, int32_t n_kv, int32_t heads,
                          int32_t kv_heads, int32_t d, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   WsLayout L;

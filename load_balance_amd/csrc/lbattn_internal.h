@@ -186,6 +186,13 @@ struct MergeArgs {
   int32_t n_rows, heads, d;
 };
 
+// Partials 1 .. n_parts - 1 merged into partial 0 (written), in one pass.
+struct MergePartsArgs {
+  float* out[kMaxPlanSteps];
+  float* lse[kMaxPlanSteps];
+  int32_t n_parts, n_rows, heads, d;
+};
+
 // Backward kernels.  dQ: the forward's query tiles and wave layout (8 waves, each 32
 // rows of one head).  dK/dV: key tiles of 128 keys, 4 groups of 32 keys, each owned by a
 // pair of waves that loops over all G heads; query rows stream in stages of 32, one head
@@ -219,6 +226,7 @@ hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, 
 hipError_t launch_ring_merge(const RingMergeArgs& m, hipStream_t s);
 hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_lse_merge_parts(const MergePartsArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, int n_rows, int heads, int d,
                              float* dvec, hipStream_t s);

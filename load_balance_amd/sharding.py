@@ -635,10 +635,12 @@ class ShardedRank:
                       self.ring_workspace, stream=stream)
 
     def merge_partials(self, stream=None):
-        """Merges the live steps' partials 1, 2, ... into out, lse in step order."""
-        from . import lse_merge
-        for i in range(1, len(self.live_steps)):
-            lse_merge(self.out, self.lse, *self.overlap_buffers[i], stream=stream)
+        """Merges the live steps' partials 1, 2, ... into out, lse in step order, in one pass
+        (the same bits as a merge per step)."""
+        from . import lse_merge_parts
+        if len(self.live_steps) > 1:
+            lse_merge_parts([b[0] for b in self.overlap_buffers], [b[1] for b in self.overlap_buffers],
+                            stream=stream)
 
     def run_ring(self, stream=None):
         """run_planned() with every live step's items in one attention launch: the steps'

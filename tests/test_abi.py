@@ -128,6 +128,24 @@ def test_block_host_checks(L):
     assert call(n_q=0, kv=None, n_kv=0) == LB_OK
 
 
+def test_lse_merge_parts_host_checks(L):
+    """Argument errors of lb_lse_merge_parts, all caught on the host before any launch."""
+    P = ctypes.c_void_p
+    arr = lambda *xs: (P * len(xs))(*xs)
+    A, B = 0x100000, 0x200000  # aligned, never dereferenced by the host checks
+    outs, lses = arr(A, B), arr(A + 0x1000, B + 0x1000)
+    M = L.lb_lse_merge_parts
+    assert M(outs, lses, 1, 100, 4, 128, None) == LB_EINVAL
+    assert M(outs, lses, 17, 100, 4, 128, None) == LB_EINVAL
+    assert M(None, lses, 2, 100, 4, 128, None) == LB_EINVAL
+    assert M(arr(A, A), lses, 2, 100, 4, 128, None) == LB_EINVAL  # one buffer twice
+    assert M(arr(A, None), lses, 2, 100, 4, 128, None) == LB_EINVAL
+    assert M(outs, lses, 2, 100, 4, 6, None) == LB_EUNSUPPORTED
+    assert M(arr(A, B + 4), lses, 2, 100, 4, 128, None) == LB_EINVAL  # misaligned
+    assert M(outs, lses, 2, -1, 4, 128, None) == LB_EINVAL
+    assert M(outs, lses, 2, 0, 4, 128, None) == LB_OK  # nothing to merge, nothing launched
+
+
 def test_split_host_checks(L):
     n = 64
     need = L.lb_workspace_bytes(n, 3, 2, 2)

@@ -56,6 +56,15 @@ def block_args(n_q=64, n_kv=128, **kw):
     return a
 
 
+def test_lse_merge_parts_checks():
+    o, l = z((10, H, D), f32), z((H, 10), f32)
+    raises("2 to 16 partials", lb.lse_merge_parts, [o], [l])
+    raises("2 to 16 partials", lb.lse_merge_parts, [o, o], [l])
+    raises("outs\\[1\\] has shape", lb.lse_merge_parts, [o, z((11, H, D), f32)], [l, l])
+    raises("lses\\[1\\] must be torch.float32", lb.lse_merge_parts, [o, o], [l, z((H, 10), bf16)])
+    raises("GPU tensors", lb.lse_merge_parts, [o, z((10, H, D), f32)], [l, z((H, 10), f32)])
+
+
 def test_block_forward_checks():
     raises("GPU tensors", lb.block_attn_fwd, **block_args())
     raises("q_pos has shape", lb.block_attn_fwd, **block_args(q_pos=z(63, i32)))

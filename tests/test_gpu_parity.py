@@ -824,6 +824,46 @@ def test_lse_merge_matches_oracle(d):
     assert np.all(np.isfinite(go[rows_fin]))
 
 
+@pytest.mark.parametrize("n_parts,d", [(2, 128), (3, 128), (5, 64), (16, 128)])
+def test_lse_merge_parts_equals_pairwise_merges(n_parts, d):
+    """lb_lse_merge_parts against n_parts - 1 lb_lse_merge calls in sequence: the same bits,
+    on partials with -inf rows in every part (rows no part touches, rows only part 0 holds,
+    rows whose first writer is a later part), NaN in every row a partial never wrote (so a
+    read of one shows), and rows touched by several parts; the result also against the
+    float64 oracle's merges in step order."""
+    r = np.random.default_rng(100 + n_parts)
+    R, H = 1000, 4
+    outs = [r.standard_normal((R, H, d)) for _ in range(n_parts)]
+    lses = [r.standard_normal((H, R)) * 3 for _ in range(n_parts)]
+    for i in range(n_parts):
+        lses[i][r.random((H, R)) < (0.3 if i == 0 else 0.7)] = -np.inf
+    lses[0][:, :64] = -np.inf  # a whole row group first written by a later part
+    for i in range(n_parts):
+        lses[i][:, 64:100] = -np.inf  # rows no part touches
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    def poisoned():
+        go = [t(o) for o in outs]
+        for o, l in zip(go, lses):
+            o[torch.from_numpy((l == -np.inf).T.copy())] = float("nan")
+        return go, [t(l) for l in lses]
+    seq_o, seq_l = poisoned()
+    for i in range(1, n_parts):
+        lb.lse_merge(seq_o[0], seq_l[0], seq_o[i], seq_l[i])
+    one_o, one_l = poisoned()
+    lb.lse_merge_parts(one_o, one_l)
+    torch.cuda.synchronize()
+    assert torch.equal(one_l[0], seq_l[0])
+    a, b = one_o[0].cpu().numpy(), seq_o[0].cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))  # NaN rows (never written) included
+    ref_o, ref_l = outs[0], lses[0]
+    for i in range(1, n_parts):
+        ref_o, ref_l = OA.lse_merge(ref_o, ref_l, outs[i], lses[i])
+    fin = ref_l != -np.inf
+    assert np.array_equal(one_l[0].cpu().numpy() == -np.inf, ~fin)
+    assert np.abs(one_l[0].cpu().numpy()[fin] - ref_l[fin]).max() <= 1e-5
+    assert np.abs(a[fin.T] - ref_o[fin.T]).max() <= 1e-5
+
+
 # --------------------------------------------------------------------------
 # the shared-question mask on the block path (a shared document)
 # --------------------------------------------------------------------------
