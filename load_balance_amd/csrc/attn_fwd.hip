@@ -271,26 +271,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
   lds_barrier();
   int qitem = __builtin_amdgcn_readfirstlane(s_item[1]);
 
-  // The loads an item starts with, issued during the previous item's epilogue so that their
-  // latency hides behind it: this wave's Q fragment (B operand of S^T = K Q^T; lane holds
-  // Q[q = l32][d = kk*16 + hh*8 .. +8], zeros past the tile's end) and the first key block
-  // into the loader's registers.
+  // The loads an item starts with, issued before it starts so that their latency hides
+  // behind the previous item's end: this wave's Q fragment (B operand of S^T = K Q^T; lane
+  // holds Q[q = l32][d = kk*16 + hh*8 .. +8], zeros past the tile's end) and the first key
+  // block, copied into ring slot 0.
   bf16x8 qreg[D / 16];
-  auto issue_item_loads = [&](int item, const lb_plan_tile* T) {
+  auto issue_q = [&](int item, const lb_plan_tile* T) {
     const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
     const int g = q_of + n_queues * (k_in % heads_per_queue);
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
-    const char* Kx = Kb;
-    const char* Vx = Vb;
-    if constexpr (RING) {
-      const int st = step_of(T);
-      Kx = reinterpret_cast<const char*>(r.k[st]);
-      Vx = reinterpret_cast<const char*>(r.v[st]);
-    }
-    const int k_start0 = __builtin_amdgcn_readfirstlane(T->k_start[0]);
-    const int k_len0 = __builtin_amdgcn_readfirstlane(T->k_len[0]);
     // one buffer over this wave's rows of the tile: no branches (a branch around a load
     // makes the compiler wait for every load before it), zeros past the tile's end
     const int head = __builtin_amdgcn_readfirstlane(g * G + head_in_group);
@@ -307,6 +298,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + kk * 32, 0, 0));
+  };
+  auto issue_block0 = [&](int item, const lb_plan_tile* T) {
+    const int q_of = item / max(per_queue, 1), k_in = item - q_of * per_queue;
+    const int g = q_of + n_queues * (k_in % heads_per_queue);
+    const int n_spans = __builtin_amdgcn_readfirstlane(T->n_spans);
+    const char* Kx = Kb;
+    const char* Vx = Vb;
+    if constexpr (RING) {
+      const int st = step_of(T);
+      Kx = reinterpret_cast<const char*>(r.k[st]);
+      Vx = reinterpret_cast<const char*>(r.v[st]);
+    }
+    const int k_start0 = __builtin_amdgcn_readfirstlane(T->k_start[0]);
+    const int k_len0 = __builtin_amdgcn_readfirstlane(T->k_len[0]);
     if (n_spans > 0) {
       const uint32_t lds = ring_lds;  // block 0 goes to slot 0 (kept out of the epilogue staging)
       const int valid = __builtin_amdgcn_readfirstlane(min(k_len0, BN));
@@ -338,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     fetch_tile(qitem, &s_tile[0]);
     wait_tile();
     lds_barrier();
-    issue_item_loads(qitem, &s_tile[0]);
+    issue_q(qitem, &s_tile[0]);
+    issue_block0(qitem, &s_tile[0]);
     if (tid == 0) k_after = start_pop();
   }
 
@@ -581,16 +587,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     }
     if (lagging && prev_live)
       softmax_pv(prev, smem + ((n_kv_tiles + kStages - 1) % kStages) * Lds<D>::stage + Lds<D>::kBytes);
+    // This wave's Q fragment for the next item goes out before the epilogue barrier (the
+    // leading waves, done with their last block, otherwise wait there for the lagging ones):
+    // the next item's number (s_item) and descriptor are published by the key loop's
+    // barriers once it has two or more blocks (the descriptor copy is older than block 1's,
+    // which the second barrier waits for), by a barrier of their own otherwise.
+    if (n_kv_tiles < 2) {
+      wait_tile();
+      lds_barrier();
+    }
+    {
+      const int nxt = __builtin_amdgcn_readfirstlane(s_item[slot]);
+      if (nxt >= 0) issue_q(nxt, &s_tile[slot ^ 1]);
+    }
 
     // ---- epilogue: out = O / l, lse = ln(sum exp) ----
-    // Every wave is done with the LDS ring after this barrier, the next item's number is in
-    // s_item and its descriptor in the other slot: its loads go out first, then thread 0's
-    // atomic for the item after it.
-    wait_tile();
+    // Every wave is done with the LDS ring after this barrier (the next item's descriptor has
+    // been published above): the next item's first block goes out first, then thread 0's
+    // atomic for the item after it.  (No wait for wave 0's copies here: it would also wait for
+    // its Q fragment, just issued.)
     lds_barrier();
     const int next_item = __builtin_amdgcn_readfirstlane(s_item[slot]);
     if (next_item >= 0) {
-      issue_item_loads(next_item, &s_tile[slot ^ 1]);
+      issue_block0(next_item, &s_tile[slot ^ 1]);
       if (tid == 0) k_after = start_pop();
     }
     const float l_tot = l_part + partner_lane(l_part, lane);
