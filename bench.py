@@ -34,9 +34,12 @@ PEAK_BF16_TFLOPS = 2500.0           # MI355X published dense bf16 MFMA peak (2.5
 PEAK_BF16_AT_2400MHZ = 256 * 2.4e9 * 4096 / 1e12   # 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU = 2516.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longtail32k_traffic.json")
 TRAFFIC_SOURCE = ("profiles/attn_fwd_longtail32k_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE passes of this "
-                  "kernel source, copy-calibrated; read from that file, not measured in this run")
-# the attention kernel's source files: the traffic file applies while their joint hash matches
-KERNEL_SOURCES = [os.path.join(ROOT, "load_balance_amd", "csrc", f) for f in ("attn_fwd.hip", "lds_staging.h")]
+                  "kernel and planner source and queue order, copy-calibrated; read from that file, not measured "
+                  "in this run")
+# the attention kernel's and the planner's source files (the queue order decides which reads hit
+# in L2): the traffic file applies while their joint hash and the run's queue order match it
+KERNEL_SOURCES = [os.path.join(ROOT, "load_balance_amd", "csrc", f) for f in ("attn_fwd.hip", "lds_staging.h",
+                                                                              "plan.hip")]
 
 
 def log(*a):
@@ -62,6 +65,7 @@ class VarlenStep:
         self.name = name
         self.mask_kind = mask_kind
         self.lpt_weights = None  # (block, pair) weights of the queue order; None: lb_plan_varlen's fitted ones
+        self.queue_order = None  # lb.ORDER_LPT or lb.ORDER_DOCUMENTS; None: lb_plan_varlen's (documents)
         self.items = []
         for p in packs:
             T, H, Hkv, d = p["tokens"], p["heads"], p["kv_heads"], p["d"]
@@ -92,11 +96,13 @@ class VarlenStep:
             ev = None if evs is None else evs[i]
             if ev is not None:
                 ev[0].record()
-            if self.lpt_weights is None:
+            if self.lpt_weights is None and self.queue_order is None:
                 lb.plan_varlen(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], self.mask_kind, workspace=it["ws"])
             else:
-                lb.plan_varlen_weighted(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], *self.lpt_weights,
-                                        mask_kind=self.mask_kind, workspace=it["ws"])
+                weights = self.lpt_weights or (lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT)
+                order = lb.ORDER_LPT if self.queue_order is None else self.queue_order
+                lb.plan_varlen_ordered(it["cu"], it["T"], it["H"], it["Hkv"], it["d"], *weights, order,
+                                       mask_kind=self.mask_kind, workspace=it["ws"])
             if ev is not None:
                 ev[1].record()
             lb.attn_run(it["q"], it["k"], it["v"], it["out"], it["lse"], it["ws"])
@@ -582,8 +588,9 @@ def cpu_baseline(w, seconds, seed=0):
                       f"float64 numpy, {n_proc} processes x 1 BLAS thread, {el:.1f} s"}
 
 
-def traffic_entry():
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel."""
+def traffic_entry(config):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel,
+    planner and queue order."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -592,6 +599,8 @@ def traffic_entry():
             with open(path, "rb") as f:
                 h.update(f.read())
         if t.get("source_sha256") != h.hexdigest():
+            return None
+        if t.get("queue_order") != config.get("queue_order") or t.get("lpt_weights") != config.get("lpt_weights"):
             return None
         return t.get("hbm_bytes_per_launch")
     except Exception:
@@ -663,6 +672,10 @@ def main():
                     help="longtail, pairA, pairB, shared_question: queue the tiles by BLOCK * key blocks + "
                          "PAIR * G * pairs (lb_plan_varlen_weighted; 'blocks' is 1,0) instead of lb_plan_varlen's "
                          "fitted weights")
+    ap.add_argument("--order", default=None, choices=["lpt", "documents"],
+                    help="longtail, pairA, pairB, shared_question: queue order (lb_plan_varlen_ordered): the tiles "
+                         "by their estimate (lpt) or the documents by their largest tile's, each document's tiles "
+                         "together (documents, lb_plan_varlen's); with --lpt-weights the default is lpt")
     ap.add_argument("--worker-records", default=None, metavar="PATH",
                     help="write the last launch's per-workgroup records and its plan (JSON) to PATH")
     args = ap.parse_args()
@@ -694,8 +707,14 @@ def main():
             sys.exit("--lpt-weights applies to the varlen forward workloads")
         bw, pw = (1, 0) if args.lpt_weights == "blocks" else map(int, args.lpt_weights.split(","))
         w.lpt_weights = (bw, pw)
+    if args.order is not None:
+        if not isinstance(w, VarlenStep):
+            sys.exit("--order applies to the varlen forward workloads")
+        w.queue_order = lb.ORDER_LPT if args.order == "lpt" else lb.ORDER_DOCUMENTS
     if isinstance(w, VarlenStep):
-        w.config = dict(w.config, lpt_weights=list(w.lpt_weights or (lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT)))
+        order = w.queue_order if w.queue_order is not None else (lb.ORDER_LPT if w.lpt_weights else lb.ORDER_DOCUMENTS)
+        w.config = dict(w.config, lpt_weights=list(w.lpt_weights or (lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT)),
+                        queue_order="documents" if order == lb.ORDER_DOCUMENTS else "lpt")
     graphed = getattr(w, "graph", None) is not None
     torch.cuda.synchronize()
 
@@ -771,10 +790,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_entry() if args.workload == "longtail" else None,
-            "traffic_source": (TRAFFIC_SOURCE if args.workload == "longtail" and traffic_entry() is not None
+            "traffic": traffic_entry(w.config) if args.workload == "longtail" else None,
+            "traffic_source": (TRAFFIC_SOURCE if args.workload == "longtail" and traffic_entry(w.config) is not None
                                else None),
-            "kernel": getattr(w, "kernel_name", "attn_kernel<128,false,false,false> (persistent, LPT queue)"),
+            "kernel": getattr(w, "kernel_name", "attn_kernel<128,false,false,false> (persistent, longest-first queue)"),
             "launch_ms": round(attn_ms_per_launch, 4),
         },
         "cpu_baseline": None,

@@ -96,9 +96,11 @@ enum {
 
 /*
  * One tile of the plan, as lb_read_plan returns it, in queue order: ordering cost
- * descending, ties in natural order (fragment order, then tile order).  The cost of
- * the varlen forward's plans (lb_plan_varlen, lb_varlen_attn_fwd) is the fitted time
- * estimate of lb_plan_varlen_weighted; that of every other plan is `blocks`.  A tile's
+ * descending, ties in natural order (fragment order, then tile order), except in the
+ * LB_ORDER_DOCUMENTS order of lb_plan_varlen_ordered, the default of the varlen forward
+ * (lb_plan_varlen, lb_varlen_attn_fwd), described there.  The cost of the varlen forward's
+ * plans is the fitted time estimate of lb_plan_varlen_weighted; that of every other plan is
+ * `blocks`.  A tile's
  * time is set mostly by the key blocks it sweeps, a short tile costing
  * as much as a full one ("03 · 长文负载均衡", section 3.3: a query block shorter than
  * one tile is billed as a whole tile), and items go out longest first ("数据并行负载
@@ -213,8 +215,9 @@ lb_status lb_block_attn_fwd(const void* q_shard, int32_t n_q, const void* kv_chu
                             hipStream_t stream);
 
 /*
- * The two halves of the forward calls.  lb_plan_varlen queues the tiles by the fitted time
- * estimate that lb_plan_varlen_weighted below describes.  lb_varlen_attn_fwd is lb_plan_varlen followed by
+ * The two halves of the forward calls.  lb_plan_varlen queues the tiles in the
+ * LB_ORDER_DOCUMENTS order of lb_plan_varlen_ordered below, on the fitted time estimate that
+ * lb_plan_varlen_weighted describes.  lb_varlen_attn_fwd is lb_plan_varlen followed by
  * lb_attn_run (bf16 out); lb_block_attn_fwd is lb_plan_block followed by lb_attn_run (fp32
  * out).  Split, a plan can serve several attention launches -- every layer of a model sees
  * the same cu_seqlens -- and each half can be timed on its own.  The plan stays valid in
@@ -238,9 +241,10 @@ lb_status lb_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total
  * with `blocks` and `cost` (visible pairs of one head) as in lb_plan_tile; the per-item
  * constant of a fitted model is left out, since it shifts every item alike.  Tiles,
  * spans and the workspace layout are those of lb_plan_varlen; only the queue order can
- * differ, and lb_attn_run runs the plan as any other.  lb_plan_varlen is this call with
- * LB_LPT_FIT_BLOCK_WEIGHT and LB_LPT_FIT_PAIR_WEIGHT; block_weight = 1, pair_weight = 0
- * orders by key blocks alone.
+ * differ, and lb_attn_run runs the plan as any other.  The order is LPT on the estimate
+ * (LB_ORDER_LPT of lb_plan_varlen_ordered); lb_plan_varlen uses the same estimate with
+ * LB_LPT_FIT_BLOCK_WEIGHT and LB_LPT_FIT_PAIR_WEIGHT, grouped by document
+ * (LB_ORDER_DOCUMENTS).  block_weight = 1, pair_weight = 0 orders by key blocks alone.
  *   block_weight  1 .. LB_LPT_BLOCK_WEIGHT_MAX (a tile with work never costs 0)
  *   pair_weight   0 .. LB_LPT_PAIR_WEIGHT_MAX
  * Weights out of range: LB_EINVAL; every other argument and error as lb_plan_varlen.
@@ -256,6 +260,35 @@ lb_status lb_plan_varlen_weighted(const int32_t* cu_seqlens, int32_t n_seg, int3
                                   int32_t heads, int32_t kv_heads, int32_t d, int32_t mask_kind,
                                   uint32_t block_weight, uint32_t pair_weight, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lb_plan_varlen_weighted with a choice of queue order.
+ *   LB_ORDER_LPT        the tiles by their estimate, largest first, ties in natural order
+ *                       (lb_plan_varlen_weighted).
+ *   LB_ORDER_DOCUMENTS  the fragments (one per segment of cu_seqlens) by the largest estimate
+ *                       among their tiles, largest first, ties later fragment first; each
+ *                       fragment's tiles together, from its last tile back to its first; the
+ *                       tiles without key spans last, in descending natural order.  The
+ *                       estimates are the 15-bit scaled ones of the LPT order.  This is LPT
+ *                       applied to documents: the long documents' items go out first and
+ *                       the short ones' at the end, as in LB_ORDER_LPT, but the items in
+ *                       flight together mostly belong to one document and share its keys and
+ *                       values in L2 (on the 32K long-tail pack of 30 documents, 0.48 GB
+ *                       read past L2 per launch instead of 0.94, against 0.40 GB that every
+ *                       order must read).  Plans of more than 4096 fragments or more than
+ *                       16384 tiles are ordered as LB_ORDER_LPT.  Within a causal
+ *                       document a later tile never sees fewer keys, so its tiles also go out
+ *                       largest first, up to a shorter last tile.
+ * order not one of these: LB_EINVAL; weights and every other argument as
+ * lb_plan_varlen_weighted.  lb_plan_varlen is this call with LB_LPT_FIT_BLOCK_WEIGHT,
+ * LB_LPT_FIT_PAIR_WEIGHT and LB_ORDER_DOCUMENTS.  Every order writes the same bits.
+ */
+#define LB_ORDER_LPT 0
+#define LB_ORDER_DOCUMENTS 1
+lb_status lb_plan_varlen_ordered(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens,
+                                 int32_t heads, int32_t kv_heads, int32_t d, int32_t mask_kind,
+                                 uint32_t block_weight, uint32_t pair_weight, int32_t order, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,
                         const int32_t* kv_doc, int32_t n_kv, int32_t heads, int32_t kv_heads, int32_t d,

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     U32 = ctypes.c_uint32
     L.lb_plan_varlen_weighted.argtypes = [P, I32, I32, I32, I32, I32, I32, U32, U32, P, SZ, P]
     L.lb_plan_varlen_weighted.restype = ctypes.c_int
+    L.lb_plan_varlen_ordered.argtypes = [P, I32, I32, I32, I32, I32, I32, U32, U32, I32, P, SZ, P]
+    L.lb_plan_varlen_ordered.restype = ctypes.c_int
     L.lb_plan_block.argtypes = [P, P, I32, P, P, I32, I32, I32, I32, I32, P, SZ, P]
     L.lb_plan_block.restype = ctypes.c_int
     L.lb_plan_block_steps.argtypes = [P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P]
@@ -336,7 +338,8 @@ def _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace):
 def plan_varlen(cu_seqlens, total_tokens, heads, kv_heads, d, mask_kind=MASK_CAUSAL_DOC, workspace=None,
                 stream=None):
     """First half of varlen_attn_fwd: writes the tile plan into ``workspace`` (returned), its
-    queue ordered by the fitted estimate (LPT_FIT_BLOCK_WEIGHT, LPT_FIT_PAIR_WEIGHT)."""
+    queue in the documents order (ORDER_DOCUMENTS) of the fitted estimate (LPT_FIT_BLOCK_WEIGHT,
+    LPT_FIT_PAIR_WEIGHT)."""
     n_seg, workspace = _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace)
     _check(lib().lb_plan_varlen(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d, int(mask_kind),
                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
@@ -360,6 +363,24 @@ def plan_varlen_weighted(cu_seqlens, total_tokens, heads, kv_heads, d, block_wei
                                          int(mask_kind), int(block_weight), int(pair_weight), _ptr(workspace),
                                          workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_plan_varlen_weighted")
+    return workspace
+
+
+# queue orders of plan_varlen_ordered (LB_ORDER_*)
+ORDER_LPT = 0
+ORDER_DOCUMENTS = 1
+
+
+def plan_varlen_ordered(cu_seqlens, total_tokens, heads, kv_heads, d, block_weight, pair_weight, order,
+                        mask_kind=MASK_CAUSAL_DOC, workspace=None, stream=None):
+    """plan_varlen_weighted with a choice of queue order: ORDER_LPT (tiles by the estimate,
+    largest first) or ORDER_DOCUMENTS (documents by their largest tile's estimate, largest
+    first, each document's tiles together from its last back to its first)."""
+    n_seg, workspace = _plan_varlen_args(cu_seqlens, total_tokens, heads, kv_heads, workspace)
+    _check(lib().lb_plan_varlen_ordered(_ptr(cu_seqlens), n_seg, total_tokens, heads, kv_heads, d,
+                                        int(mask_kind), int(block_weight), int(pair_weight), int(order),
+                                        _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(stream))),
+           "lb_plan_varlen_ordered")
     return workspace
 
 

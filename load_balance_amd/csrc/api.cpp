@@ -113,10 +113,11 @@ lb_status prepare_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t 
 lb_status launch_plan_varlen(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
                              int32_t kv_heads, int32_t mask_kind, void* workspace, const WsLayout& L,
                              hipStream_t stream, uint32_t block_weight = LB_LPT_FIT_BLOCK_WEIGHT,
-                             uint32_t pair_weight = LB_LPT_FIT_PAIR_WEIGHT) {
+                             uint32_t pair_weight = LB_LPT_FIT_PAIR_WEIGHT, int32_t order = LB_ORDER_DOCUMENTS) {
   PlanArgs p{};
   p.block_weight = block_weight;
   p.pair_weight = pair_weight;
+  p.order = order;
   p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
   p.cu_seqlens = cu_seqlens;
   p.n_seg = n_seg;
@@ -311,7 +312,22 @@ lb_status lb_plan_varlen_weighted(const int32_t* cu_seqlens, int32_t n_seg, int3
                                      workspace_bytes, &L);
   if (st != LB_OK) return st;
   return launch_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, mask_kind, workspace, L, stream,
-                            block_weight, pair_weight);
+                            block_weight, pair_weight, LB_ORDER_LPT);
+}
+
+lb_status lb_plan_varlen_ordered(const int32_t* cu_seqlens, int32_t n_seg, int32_t total_tokens, int32_t heads,
+                                 int32_t kv_heads, int32_t d, int32_t mask_kind, uint32_t block_weight,
+                                 uint32_t pair_weight, int32_t order, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (block_weight < 1 || block_weight > LB_LPT_BLOCK_WEIGHT_MAX || pair_weight > LB_LPT_PAIR_WEIGHT_MAX)
+    return LB_EINVAL;
+  if (order != LB_ORDER_LPT && order != LB_ORDER_DOCUMENTS) return LB_EINVAL;
+  WsLayout L;
+  lb_status st = prepare_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, d, mask_kind, workspace,
+                                     workspace_bytes, &L);
+  if (st != LB_OK) return st;
+  return launch_plan_varlen(cu_seqlens, n_seg, total_tokens, heads, kv_heads, mask_kind, workspace, L, stream,
+                            block_weight, pair_weight, order);
 }
 
 lb_status lb_plan_block(const int32_t* q_pos, const int32_t* q_doc, int32_t n_q, const int32_t* kv_pos,

@@ -129,6 +129,7 @@ struct PlanArgs {
   // LPT ordering cost of a tile: block_weight * key blocks + pair_weight * G * visible pairs
   uint32_t block_weight = 1;  // 1 .. LB_LPT_BLOCK_WEIGHT_MAX
   uint32_t pair_weight = 0;   // 0 .. LB_LPT_PAIR_WEIGHT_MAX
+  int32_t order = LB_ORDER_LPT;  // LB_ORDER_DOCUMENTS: fragments longest first, each one's tiles last first
   char* ws;
   WsLayout L;
 };

@@ -22,7 +22,11 @@
 //      consecutive position (block path); spans = keys the fragment may see.
 //   2. tiles: each fragment cut into `tile_rows` rows from its start; spans
 //      clipped to what the tile's last row sees; pairs in closed form, blocks.
-//   3. order: sort of (cost descending, natural index) keys in LDS.
+//   3. order: sort of (cost descending, natural index) keys in LDS; or, with
+//      LB_ORDER_DOCUMENTS, of (the fragment's largest cost descending, natural index
+//      descending) keys: the fragments longest first, each one's tiles from its last row
+//      back, so that the items in flight at one time share their fragment's keys and values
+//      in L2 (the order the tiles of one fragment run in decides only which reads hit).
 // The plan lands in the caller's workspace; the attention kernel reads it.
 #include "lbattn_internal.h"
 
@@ -43,9 +47,14 @@ static_assert(kSortCap <= (int)kIndexMask + 1, "a tile index must fit the key");
 constexpr int kPlanWaves = NT / 64;
 
 constexpr int kRunRounds = 4;
+// LB_ORDER_DOCUMENTS applies to plans of at most kGroupCap fragments and kSortCap / 2 tiles
+// (the fragment maxima sit in their own LDS array; the bitonic sort's keys then stay clear of
+// the tile table it reads fragments from); larger plans are ordered as LB_ORDER_LPT.
+constexpr int kGroupCap = 4096;
 
 struct PlanShared {
   uint32_t keys[kSortCap];
+  uint32_t group_q[kGroupCap];  // LB_ORDER_DOCUMENTS: each fragment's largest scaled cost
   int32_t wave_sum[kPlanWaves];
   int32_t run_sum[kRunRounds][kPlanWaves];
   int32_t err;
@@ -583,9 +592,56 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   int shift = 0;
   while (((sh.max_cost + (1ull << shift) - 1) >> shift) > kCostMax) ++shift;
   const unsigned long long round = (1ull << shift) - 1;
+  auto scaled = [&](int blocks, int64_t pairs) -> uint32_t {
+    return (uint32_t)((cost_of(blocks, pairs) + round) >> shift);
+  };
+  // the fragment of tile t (tiles are numbered fragment after fragment)
+  auto frag_of = [&](int t) -> int {
+    int lo = 0, hi = n_frags - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (lds_ftile[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  const bool by_doc = a.order == LB_ORDER_DOCUMENTS && n_frags <= kGroupCap && n_tiles <= kSortCap / 2;
+  if (by_doc && sh.err == 0) {
+    // each fragment's largest scaled cost: over each wave's 64 consecutive tiles, the maximum
+    // of every run of one fragment (a segmented scan towards the run's first lane), then one
+    // LDS atomic per run.  Tiles without spans count 0.
+    for (int i = tid; i < n_frags; i += NT) sh.group_q[i] = 0;
+    __syncthreads();
+    const int lane = tid & 63;
+    for (int base = 0; base < n_tiles; base += NT) {
+      const int t = base + tid;
+      int f = -1;
+      uint32_t q = 0;
+      if (t < n_tiles) {
+        f = frag_of(t);
+        const int blocks = ntiles[t].blocks;  // this thread's own tile, written by it in phase 2
+        q = blocks > 0 ? scaled(blocks, ntiles[t].cost) : 0u;
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t q2 = __shfl_down(q, off);
+        const int f2 = __shfl_down(f, off);
+        if (lane + off < 64 && f2 == f) q = max(q, q2);
+      }
+      const int f_prev = __shfl_up(f, 1);
+      if (t < n_tiles && (lane == 0 || f_prev != f)) atomicMax(&sh.group_q[f], q);
+    }
+  }
+  __syncthreads();
+  // LB_ORDER_LPT: (kCostMax - q) << kIndexBits | t, q the tile's scaled cost: costs descending,
+  // ties in natural order.  LB_ORDER_DOCUMENTS: q the largest of the tile's fragment (0 for a
+  // tile without spans, so that those still come last) and the index reversed: fragments
+  // longest first, ties and the tiles within a fragment in descending natural order.
   auto key_of = [&](int t, int blocks, int64_t pairs) -> uint32_t {
-    const uint32_t q = (uint32_t)((cost_of(blocks, pairs) + round) >> shift);
-    return ((kCostMax - q) << kIndexBits) | (uint32_t)t;
+    if (by_doc) {
+      const uint32_t q = blocks > 0 ? sh.group_q[frag_of(t)] : 0u;
+      return ((kCostMax - q) << kIndexBits) | (kIndexMask - (uint32_t)t);
+    }
+    return ((kCostMax - scaled(blocks, pairs)) << kIndexBits) | (uint32_t)t;
   };
 
   // ---- 3. longest-first order of the unique keys; tiles copied to their queue positions --
@@ -636,7 +692,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     bitonic_phase(sh, n_pad, min(n_pad, 64), min(n_pad, 64) >> 1);
     for (int k = 128; k <= n_pad; k <<= 1) bitonic_phase(sh, n_pad, k, k >> 1);
     for (int i = tid; i < n_tiles; i += NT) {
-      tiles[i] = ntiles[sh.keys[i] & kIndexMask];
+      const uint32_t idx = sh.keys[i] & kIndexMask;
+      tiles[i] = ntiles[by_doc ? kIndexMask - idx : idx];
       order[i] = i;
     }
   }

@@ -36,7 +36,10 @@ Tiling rule written out here (the plan the library must reproduce exactly):
 5. *Order*: estimated time descending, ties by natural order (fragment order,
    then tile order inside the fragment).  The estimate is the block count, or a
    weighted sum of blocks and pairs (``lpt_order_weighted``); either is scaled
-   to 15 bits as ``quantised`` states before ordering.
+   to 15 bits as ``quantised`` states before ordering.  The documents order
+   (``documents_order``) applies the same longest-first rule to fragments: a
+   fragment's estimate is the largest of its tiles', fragments go out largest
+   first, and each one's tiles together, from its last tile back to its first.
 
 Transposed tiling, for the key/value gradients of the backward (each key block
 gathers the query rows that see it):
@@ -274,6 +277,45 @@ def weighted_cost(t, block_weight, pair_weight, group):
 def lpt_order_weighted(tile_list, block_weight, pair_weight, group):
     """LPT order on the weighted estimate ("数据并行负载均衡", section 4.4)."""
     return order_by_cost([weighted_cost(t, block_weight, pair_weight, group) for t in tile_list])
+
+
+# The documents order groups a fragment's tiles so that the items running at one time share
+# that fragment's keys and values (a cache effect: every order computes the same results).
+# Reading: the pages order work longest first and say nothing of the order of items of
+# equal standing; taking the longest-first rule at the level of documents, with a document's
+# estimate its largest tile's, keeps the long items first and the short ones last.  Beyond
+# GROUP_CAP segments or GROUP_TILE_CAP tiles the plan keeps the tile-level order (a capacity
+# rule of the planner's shared memory, stated so that the two agree).
+GROUP_CAP = 4096
+GROUP_TILE_CAP = 16384
+
+
+def documents_order(tile_list, frags, bm, costs, n_segments):
+    """Indices of tiles: fragments by their largest quantised cost descending, ties later
+    fragment first; inside a fragment, tiles in descending natural order; tiles without
+    blocks (no key span) after all others, in descending natural order.  Falls back to
+    ``order_by_cost`` beyond the capacities above."""
+    n = len(tile_list)
+    if n_segments > GROUP_CAP or n > GROUP_TILE_CAP:
+        return order_by_cost(costs)
+    q = quantised(costs)
+    frag_of = []
+    for f, (_, q_len, _, _) in enumerate(frags):
+        frag_of += [f] * (-(-q_len // bm))
+    assert len(frag_of) == n
+    top = {}
+    for i in range(n):
+        if tile_list[i]["blocks"] > 0:
+            top[frag_of[i]] = max(top.get(frag_of[i], 0), q[i])
+    group = [top[frag_of[i]] if tile_list[i]["blocks"] > 0 else 0 for i in range(n)]
+    return sorted(range(n), key=lambda i: (-group[i], -i))
+
+
+def plan_documents(frags, bm, block_weight, pair_weight, group, n_segments):
+    """The plan with tiles in the documents order of the weighted estimate."""
+    t = tiles(frags, bm)
+    costs = [weighted_cost(x, block_weight, pair_weight, group) for x in t]
+    return [t[i] for i in documents_order(t, frags, bm, costs, n_segments)]
 
 
 def plan(frags, bm):

@@ -160,6 +160,14 @@ def test_split_host_checks(L):
     assert W(None, 3, n, 2, 2, 64, 0, 1, 0, FAKE, need, None) == LB_EINVAL
     assert W(FAKE, 3, n, 2, 2, 64, 0, 41515, 1, FAKE, need - 1, None) == LB_EWORKSPACE
     assert W(FAKE, 3, n, 2, 2, 48, 0, 41515, 1, FAKE, need, None) == LB_EUNSUPPORTED
+    O = L.lb_plan_varlen_ordered
+    for order in (-1, 2):
+        assert O(FAKE, 3, n, 2, 2, 64, 0, 41515, 1, order, FAKE, need, None) == LB_EINVAL
+    assert O(FAKE, 3, n, 2, 2, 64, 0, 0, 1, 1, FAKE, need, None) == LB_EINVAL  # block weight 0
+    assert O(FAKE, 3, n, 2, 2, 64, 0, 1, 1 << 16, 0, FAKE, need, None) == LB_EINVAL
+    assert O(None, 3, n, 2, 2, 64, 0, 1, 0, 1, FAKE, need, None) == LB_EINVAL
+    assert O(FAKE, 3, n, 2, 2, 64, 0, 41515, 1, 1, FAKE, need - 1, None) == LB_EWORKSPACE
+    assert O(FAKE, 3, n, 2, 2, 48, 0, 41515, 1, 0, FAKE, need, None) == LB_EUNSUPPORTED
     assert L.lb_plan_block(None, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -2, FAKE, need, None) == LB_EINVAL
     assert L.lb_plan_block(FAKE, FAKE, n, FAKE, FAKE, n, 2, 2, 64, -1, FAKE, 64, None) == LB_EWORKSPACE

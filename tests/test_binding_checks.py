@@ -48,6 +48,15 @@ def test_varlen_forward_checks():
     raises("must be a torch tensor", lb.varlen_attn_fwd, **varlen_args(lse=[0.0] * T))
 
 
+def test_plan_varlen_checks():
+    cu = torch.tensor([0, 10, T], dtype=i32)
+    for fn, extra in ((lb.plan_varlen, ()), (lb.plan_varlen_weighted, (41515, 1)),
+                      (lb.plan_varlen_ordered, (41515, 1, lb.ORDER_DOCUMENTS))):
+        raises("GPU tensors", fn, cu, T, H, HKV, D, *extra, workspace=WS)
+        raises("cu_seqlens must be torch.int32", fn, torch.tensor([0, T], dtype=torch.int64), T, H, HKV, D, *extra,
+               workspace=WS)
+
+
 def block_args(n_q=64, n_kv=128, **kw):
     a = dict(q_shard=z((n_q, H, D), bf16), kv_chunk=z((2, n_kv, HKV, D), bf16), q_pos=z(n_q, i32),
              kv_pos=z(n_kv, i32), q_doc=z(n_q, i32), kv_doc=z(n_kv, i32), out=z((n_q, H, D), f32),

@@ -83,7 +83,15 @@ def sample_rows(lengths, bm, n_random, seed, cap=None):
 
 
 def plan_ref_varlen(pack, mask="causal_doc"):
-    return plan_ref_weighted(pack, lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT, mask)
+    return plan_ref_ordered(pack, lb.LPT_FIT_BLOCK_WEIGHT, lb.LPT_FIT_PAIR_WEIGHT, lb.ORDER_DOCUMENTS, mask)
+
+
+def plan_ref_ordered(pack, block_weight, pair_weight, order, mask="causal_doc"):
+    if order == lb.ORDER_LPT:
+        return plan_ref_weighted(pack, block_weight, pair_weight, mask)
+    bm = lb.tile_rows(pack["heads"], pack["kv_heads"], pack["d"])
+    return OP.plan_documents(OP.fragments_varlen(pack["cu_seqlens"], mask), bm, block_weight, pair_weight,
+                             pack["heads"] // pack["kv_heads"], len(pack["cu_seqlens"]) - 1)
 
 
 def plan_ref_weighted(pack, block_weight, pair_weight, mask="causal_doc"):
@@ -251,9 +259,9 @@ def run_weighted(pack, block_weight, pair_weight, mask_kind=lb.MASK_CAUSAL_DOC):
 def test_weighted_plan_longtail(longtail):
     """The 32K long-tail pack queued by key blocks alone (weights 1, 0) and by the fitted
     estimate through the explicit call: both orders equal the oracle's bit for bit, they
-    differ (the pair term orders tiles of equal block count), the fitted one is
-    lb_plan_varlen's, and every order writes the same bits, since each item computes its own
-    rows whatever its place in the queue."""
+    differ (the pair term orders tiles of equal block count), lb_plan_varlen's documents order
+    of the fitted estimate equals the oracle's too, and every order writes the same bits,
+    since each item computes its own rows whatever its place in the queue."""
     p = longtail
     out_b, lse_b, ws_b = run_weighted(p, 1, 0)
     blocks_order = lb.read_plan(ws_b)
@@ -269,9 +277,88 @@ def test_weighted_plan_longtail(longtail):
     assert sum(x["items"] for x in recs) == len(blocks_order) * 8
     assert sum(x["blocks"] for x in recs) == 8 * sum(t["blocks"] for t in blocks_order)
     out_d, lse_d, ws_d = run_varlen(p)
-    assert lb.read_plan(ws_d) == fitted
+    assert_same_plan(lb.read_plan(ws_d), plan_ref_varlen(p), "32K long-tail documents plan")
+    assert sorted(map(str, lb.read_plan(ws_d))) == sorted(map(str, fitted))  # the same tiles
     for o, l in ((out_w, lse_w), (out_d, lse_d)):
         assert torch.equal(o, out_b) and torch.equal(l, lse_b)
+
+
+# --------------------------------------------------------------------------
+# queue orders (lb_plan_varlen_ordered): LPT on tiles, or LPT on documents
+# --------------------------------------------------------------------------
+def plan_ordered(pack, order, weights=(41515, 1), mask_kind=lb.MASK_CAUSAL_DOC):
+    T, H, Hkv, d = pack["tokens"], pack["heads"], pack["kv_heads"], pack["d"]
+    say(f"  plan_varlen_ordered T={T} documents={len(pack['lengths'])} H={H} Hkv={Hkv} order={order} "
+        f"weights={weights} mask={mask_kind}")
+    cu = torch.from_numpy(np.asarray(pack["cu_seqlens"], dtype=np.int32)).cuda()
+    ws = lb.new_workspace(T, len(pack["lengths"]), H, Hkv)
+    lb.plan_varlen_ordered(cu, T, H, Hkv, d, weights[0], weights[1], order, mask_kind=mask_kind, workspace=ws)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(ws) == 0
+    return ws
+
+
+def test_documents_order_longtail(longtail):
+    """The 32K long-tail pack in both orders of the fitted estimate: each equals the oracle's
+    bit for bit, the documents order keeps every document's tiles together (its last tile
+    first) with documents by their largest estimate, lb_plan_varlen's plan is the documents
+    order, and the attention outputs of both orders are the same bits."""
+    p = longtail
+    T, H, Hkv, d = p["tokens"], p["heads"], p["kv_heads"], p["d"]
+    q, k, v = dev_bf16(p["q"]), dev_bf16(p["k"]), dev_bf16(p["v"])
+    outs = []
+    for order in (lb.ORDER_LPT, lb.ORDER_DOCUMENTS):
+        ws = plan_ordered(p, order)
+        got = lb.read_plan(ws)
+        assert_same_plan(got, plan_ref_ordered(p, 41515, 1, order), f"32K long-tail order {order}")
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        lb.attn_run(q, k, v, out, lse, ws)
+        torch.cuda.synchronize()
+        assert lb.read_device_error(ws) == 0
+        outs.append((out, lse))
+        if order == lb.ORDER_DOCUMENTS:
+            cu = np.asarray(p["cu_seqlens"])
+            doc = [int(np.searchsorted(cu, t["q_start"], side="right") - 1) for t in got]
+            runs = [doc[0]] + [b for a, b in zip(doc, doc[1:]) if b != a]
+            assert len(runs) == len(set(runs)), "a document's tiles are not together"
+            assert all(got[i]["q_start"] < got[i - 1]["q_start"] for i in range(1, len(got)) if doc[i] == doc[i - 1])
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    _, _, ws_d = run_varlen(p)
+    assert lb.read_plan(ws_d) == lb.read_plan(plan_ordered(p, lb.ORDER_DOCUMENTS))
+
+
+@pytest.mark.parametrize("case", ["bitonic", "4096_documents", "4097_documents", "shared_question"])
+def test_documents_order_capacities(case):
+    """The documents order at the planner's limits, against the oracle bit for bit: a
+    262,144-token pack (more than 2048 tiles: the bitonic sort with reversed tile indices),
+    exactly 4096 documents (grouped), 4097 documents (the tile-level order), and a shared
+    question pack."""
+    r = np.random.default_rng(7)
+    H, Hkv, d, mask = 32, 8, 128, "causal_doc"
+    if case == "bitonic":
+        lengths = workloads.lognormal_lengths(262144, 5, 262144)
+    elif case == "4096_documents":
+        lengths = [int(x) for x in r.integers(1, 40, size=4096)]
+    elif case == "4097_documents":
+        lengths = [int(x) for x in r.integers(1, 40, size=4097)]
+    else:
+        H, Hkv, mask = 16, 2, "shared_question"
+        lengths = [900, 130, 7, 500, 64, 1, 260]
+    T = sum(lengths)
+    pack = dict(lengths=lengths, cu_seqlens=workloads.cu_from_lengths(lengths), tokens=T, heads=H,
+                kv_heads=Hkv, d=d)
+    kind = lb.MASK_CAUSAL_DOC if mask == "causal_doc" else lb.MASK_SHARED_QUESTION
+    got = lb.read_plan(plan_ordered(pack, lb.ORDER_DOCUMENTS, mask_kind=kind), max_tiles=1 << 16)
+    ref = plan_ref_ordered(pack, 41515, 1, lb.ORDER_DOCUMENTS, mask)
+    assert_same_plan(got, ref, f"documents order, {case}")
+    lpt = plan_ref_ordered(pack, 41515, 1, lb.ORDER_LPT, mask)
+    if case == "4097_documents":
+        assert ref == lpt
+    else:
+        assert ref != lpt
+    if case == "bitonic":
+        assert len(got) > 2048
 
 
 @pytest.mark.parametrize("H,Hkv,d,weights,mask", [

@@ -178,6 +178,86 @@ def test_weighted_order_group_multiplies_pairs():
     assert P.weighted_cost(b, 100, 1, 4) == 700
 
 
+def test_documents_order_hand_worked():
+    """Segments of 300, 100, 200, 0 and 10 tokens in 64-row tiles: 5 + 2 + 4 + 0 + 1 tiles,
+    natural indices 0-4, 5-6, 7-10, 11.  A tile of rows a .. b sweeps ceil((b + 1) / 64)
+    blocks of its document, so the documents' largest tiles sweep 5, 2, 4 and 1 blocks; at
+    41515 per block the pair term (at most 4 * 64 * 300 = 76800 here, under two blocks) does
+    not reorder them.  Documents longest first, each from its last tile back."""
+    cu = [0, 300, 400, 600, 600, 610]
+    frags = P.fragments_varlen(cu)
+    tl = P.tiles(frags, 64)
+    assert [t["blocks"] for t in tl] == [1, 2, 3, 4, 5, 1, 2, 1, 2, 3, 4, 1]
+    costs = [P.weighted_cost(t, 41515, 1, 4) for t in tl]
+    assert P.documents_order(tl, frags, 64, costs, len(cu) - 1) == [4, 3, 2, 1, 0, 10, 9, 8, 7, 6, 5, 11]
+    assert [t["q_start"] for t in P.plan_documents(frags, 64, 41515, 1, 4, len(cu) - 1)] == \
+        [256, 192, 128, 64, 0, 592, 528, 464, 400, 364, 300, 600]
+    # the LPT order of the same estimates interleaves the documents
+    assert P.order_by_cost(costs)[:4] == [4, 3, 10, 2]
+
+
+def test_documents_order_ties_and_empty_tiles():
+    """Fragments of equal largest cost: the later one first.  A tile without key blocks
+    counts 0 for its fragment and goes after every tile with blocks, all such tiles in
+    descending natural order."""
+    frags = [(0, 128, 0, []), (128, 64, 0, []), (192, 128, 0, [])]
+    tl = [dict(blocks=3), dict(blocks=0), dict(blocks=3), dict(blocks=1), dict(blocks=0)]
+    costs = [3, 0, 3, 1, 0]
+    assert P.documents_order(tl, frags, 64, costs, 3) == [2, 0, 3, 4, 1]
+
+
+@pytest.mark.parametrize("mask", ["causal_doc", "shared_question"])
+def test_documents_order_invariants(mask):
+    """On random packs: a permutation; each document's tiles together, in descending natural
+    order; documents by their largest quantised estimate, non-increasing; equal documents
+    later first; a single document is its tiles from last to first."""
+    rng = np.random.default_rng(3)
+    for trial in range(6):
+        lengths = [int(x) for x in rng.integers(1, 900, size=int(rng.integers(2, 12)))]
+        cu = workloads.cu_from_lengths(lengths)
+        frags = P.fragments_varlen(cu, mask)
+        for bm, g in ((64, 4), (32, 8), (256, 1)):
+            tl = P.tiles(frags, bm)
+            costs = [P.weighted_cost(t, 41515, 1, g) for t in tl]
+            order = P.documents_order(tl, frags, bm, costs, len(cu) - 1)
+            assert sorted(order) == list(range(len(tl)))
+            frag_of = [f for f, fr in enumerate(frags) for _ in range(-(-fr[1] // bm))]
+            q = P.quantised(costs)
+            top = {}
+            for i, t in enumerate(tl):
+                top[frag_of[i]] = max(top.get(frag_of[i], 0), q[i])
+            seen, last_top, last_frag = set(), None, None
+            for a, b in zip(order, order[1:]):
+                if frag_of[a] == frag_of[b]:
+                    assert a > b
+            for i in order:
+                f = frag_of[i]
+                if f != last_frag:
+                    assert f not in seen, "a document's tiles are split"
+                    if last_top is not None:
+                        assert top[f] < last_top or (top[f] == last_top and f < last_frag)
+                    seen.add(f)
+                    last_top, last_frag = top[f], f
+    one = P.fragments_varlen([0, 1000], mask="causal_doc")
+    tl = P.tiles(one, 64)
+    costs = [P.weighted_cost(t, 41515, 1, 4) for t in tl]
+    assert P.documents_order(tl, one, 64, costs, 1) == list(range(len(tl)))[::-1]
+
+
+def test_documents_order_capacities():
+    """Beyond 4096 segments or 16384 tiles the tile-level order applies."""
+    frags = [(64 * i, 64, 0, []) for i in range(4097)]
+    tl = [dict(blocks=1 + i % 5) for i in range(4097)]
+    costs = [t["blocks"] for t in tl]
+    assert P.documents_order(tl, frags, 64, costs, 4097) == P.order_by_cost(costs)
+    assert P.documents_order(tl[:4096], frags[:4096], 64, costs[:4096], 4096) != P.order_by_cost(costs[:4096])
+    frags = [(320 * i, 320, 0, []) for i in range(3300)]  # 16500 tiles of 64 rows
+    tl = [dict(blocks=1 + i % 5) for i in range(16500)]
+    costs = [t["blocks"] for t in tl]
+    assert P.documents_order(tl, frags, 64, costs, 3300) == P.order_by_cost(costs)
+    assert P.documents_order(tl[:16380], frags[:3276], 64, costs[:16380], 3276) != P.order_by_cost(costs[:16380])
+
+
 def test_short_tile_is_billed_as_a_whole_tile():
     """"03 · 长文负载均衡", section 3.3: a query block shorter than one tile costs a whole
     tile.  A 4-row ragged tail of a 4100-token document sweeps 65 key blocks, more than
