@@ -498,6 +498,13 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       if (tid == 0) sh.err |= LB_DEVERR_CAPACITY;
     }
   }
+  // LB_ORDER_DOCUMENTS: each fragment's largest ordering cost, kept while the tiles are cut in
+  // the LDS that held phase 1's key/value runs (the first quarter of the sort buffer)
+  const bool by_doc = a.order == LB_ORDER_DOCUMENTS && n_frags <= kGroupCap && n_tiles <= kSortCap / 2;
+  unsigned long long* frag_cost = reinterpret_cast<unsigned long long*>(&sh.keys[0]);
+  static_assert(kGroupCap * sizeof(unsigned long long) <= kSortCap / 4 * sizeof(uint32_t), "");
+  if (by_doc)
+    for (int i = tid; i < n_frags; i += NT) frag_cost[i] = 0;
   __syncthreads();
   // ordering cost of a tile; the weights are below 2^24 and 2^16, so with blocks below 2^25,
   // G <= 8 and pairs below 2^39 (256 rows by 2^31 keys) a cost stays below 2^59
@@ -568,6 +575,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
       if (ns == 0) atomicAdd(&sh.n_empty, 1);  // no blocks: sorts to the end of the order
       my_pairs += (unsigned long long)cost;
       my_max = max(my_max, cost_of(blocks, cost));
+      if (by_doc && blocks > 0) atomicMax(&frag_cost[lo], cost_of(blocks, cost));
       if (k < kMine) {
         mine_blocks[k] = blocks;
         mine_pairs[k] = cost;
@@ -604,33 +612,13 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     }
     return lo;
   };
-  const bool by_doc = a.order == LB_ORDER_DOCUMENTS && n_frags <= kGroupCap && n_tiles <= kSortCap / 2;
-  if (by_doc && sh.err == 0) {
-    // each fragment's largest scaled cost: over each wave's 64 consecutive tiles, the maximum
-    // of every run of one fragment (a segmented scan towards the run's first lane), then one
-    // LDS atomic per run.  Tiles without spans count 0.
-    for (int i = tid; i < n_frags; i += NT) sh.group_q[i] = 0;
-    __syncthreads();
-    const int lane = tid & 63;
-    for (int base = 0; base < n_tiles; base += NT) {
-      const int t = base + tid;
-      int f = -1;
-      uint32_t q = 0;
-      if (t < n_tiles) {
-        f = frag_of(t);
-        const int blocks = ntiles[t].blocks;  // this thread's own tile, written by it in phase 2
-        q = blocks > 0 ? scaled(blocks, ntiles[t].cost) : 0u;
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t q2 = __shfl_down(q, off);
-        const int f2 = __shfl_down(f, off);
-        if (lane + off < 64 && f2 == f) q = max(q, q2);
-      }
-      const int f_prev = __shfl_up(f, 1);
-      if (t < n_tiles && (lane == 0 || f_prev != f)) atomicMax(&sh.group_q[f], q);
+  // the fragments' largest costs scaled as the tiles' are (scaling is monotone: the scaled
+  // maximum is the maximum of the scaled costs); 0 for a fragment without a tile with blocks
+  if (by_doc && sh.err == 0)
+    for (int i = tid; i < n_frags; i += NT) {
+      const unsigned long long c = frag_cost[i];
+      sh.group_q[i] = c > 0 ? (uint32_t)((c + round) >> shift) : 0u;
     }
-  }
   __syncthreads();
   // LB_ORDER_LPT: (kCostMax - q) << kIndexBits | t, q the tile's scaled cost: costs descending,
   // ties in natural order.  LB_ORDER_DOCUMENTS: q the largest of the tile's fragment (0 for a
