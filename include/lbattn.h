@@ -461,7 +461,10 @@ lb_status lb_attn_bwd_rowdot(const void* out, int32_t out_f32, const void* dout,
  *   dout      bf16 [T][heads][d];
  *   dq        bf16 [T][heads][d] (written);  dk, dv  bf16 [T][kv_heads][d] (written).
  * Launches one planning kernel (both plans), the D pass, the dq kernel and the dk/dv
- * kernel on `stream`.  workspace: lb_bwd_workspace_bytes(total_tokens, n_seg, ...) bytes,
+ * kernel on `stream`.  Both plans queue their tiles in the LB_ORDER_DOCUMENTS order (see
+ * lb_plan_varlen_ordered) of key blocks alone: the items of one document run side by side
+ * and share its keys (dq) or its query rows (dk/dv) in L2.
+ * workspace: lb_bwd_workspace_bytes(total_tokens, n_seg, ...) bytes,
  * 256-byte aligned, caller-owned; a plan error sets the device error word of its half
  * (read with lb_read_device_error on the workspace: the query-tile plan sits at its start).
  */

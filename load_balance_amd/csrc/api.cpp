@@ -659,6 +659,7 @@ lb_status lb_varlen_attn_bwd(const void* q, const void* k, const void* v, const 
     PlanArgs& p = pb.step[side];
     p.mode = mask_kind == LB_MASK_CAUSAL_DOC ? kPlanCausalDoc : kPlanSharedQuestion;
     p.transposed = side;
+    p.order = LB_ORDER_DOCUMENTS;  // a document's items share its rows (dK/dV) or keys (dQ) in L2
     p.cu_seqlens = cu_seqlens;
     p.n_seg = n_seg;
     p.total_tokens = total_tokens;

@@ -94,16 +94,19 @@ def test_varlen_backward_shared_question():
 def test_key_tile_plan_equals_oracle(mask):
     """The key-tile (transposed) plan of the backward, in queue order, equals the oracle's
     transposed enumerator bit for bit; the query-tile plan equals the forward enumerator at
-    the backward's tile height."""
+    the backward's tile height.  Both are in the documents order of key blocks."""
     lengths = [300, 1, 64, 65, 129, 2, 90]
     H, Hkv, d = 8, 2, 128
     ws, off, cu = varlen_case(lengths, H, Hkv, d, seed=11, mask=mask)
     G = H // Hkv
     q_rows = 256 // G  # the forward's tile height
     k_rows = 128
-    ref_q = OP.plan(OP.fragments_varlen(cu, mask), q_rows)
-    ref_k_tiles = OP.tiles_t(OP.fragments_varlen_t(cu, mask), k_rows)
-    ref_k = [ref_k_tiles[i] for i in OP.lpt_order(ref_k_tiles)]
+    n_seg = len(cu) - 1
+    ref_q = OP.plan_documents(OP.fragments_varlen(cu, mask), q_rows, 1, 0, G, n_seg)
+    frags_t = OP.fragments_varlen_t(cu, mask)
+    ref_k_tiles = OP.tiles_t(frags_t, k_rows)
+    ref_k = [ref_k_tiles[i] for i in OP.documents_order(ref_k_tiles, frags_t, k_rows,
+                                                        [t["blocks"] for t in ref_k_tiles], n_seg)]
     for got, want, what in ((lb.read_plan(ws), ref_q, "query tiles"), (lb.read_plan(ws[off:]), ref_k, "key tiles")):
         assert len(got) == len(want), what
         for i, (a, b) in enumerate(zip(got, want)):
