@@ -633,11 +633,66 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
   };
 
   // ---- 3. longest-first order of the unique keys; tiles copied to their queue positions --
-  // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys
-  // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS,
-  // four keys per read, and one barrier, against the bitonic network's 55 barrier-separated
-  // passes at 1024 keys.
-  if (sh.err == 0 && n_tiles > 0 && n_tiles <= kRankSortMax) {
+  // The documents order of a plan whose tiles all have spans needs no sort of the tiles: the
+  // fragments are ranked by their keys ((kCostMax - group q) << kIndexBits | reversed
+  // fragment index, the order the tiles' keys give them), a prefix sum over the fragments in
+  // that order gives each one's first queue position, and a tile's place is its fragment's
+  // first position plus the tiles of the fragment after it.  The fragment keys, ranks and
+  // positions use the first quarter of the sort buffer (free since the fragment maxima were
+  // scaled); the fragments' first tiles stay in lds_ftile.
+  const bool direct = by_doc && sh.n_empty == 0 && n_frags <= kRankSortMax;
+  if (sh.err == 0 && n_tiles > 0 && direct) {
+    uint32_t* fkey = &sh.keys[0];                // fragment keys, then first queue positions
+    int32_t* fpos = reinterpret_cast<int32_t*>(&sh.keys[kRankSortMax]);  // tiles per rank, scanned
+    constexpr int kFrag = kRankSortMax / NT;
+    const int nf4 = (n_frags + 3) & ~3;
+    for (int f = tid; f < nf4; f += NT)
+      fkey[f] = f < n_frags ? ((kCostMax - sh.group_q[f]) << kIndexBits) | (kIndexMask - (uint32_t)f) : ~0u;
+    __syncthreads();
+    int frank[kFrag];
+    const uint4* fkey4 = reinterpret_cast<const uint4*>(fkey);
+#pragma unroll
+    for (int k = 0; k < kFrag; ++k) {
+      const int f = tid + k * NT;
+      frank[k] = 0;
+      if (f < n_frags) {
+        const uint32_t mine = fkey[f];
+        for (int i = 0; i < nf4 / 4; ++i) {
+          const uint4 v = fkey4[i];
+          frank[k] += (v.x < mine ? 1 : 0) + (v.y < mine ? 1 : 0) + (v.z < mine ? 1 : 0) + (v.w < mine ? 1 : 0);
+        }
+        fpos[frank[k]] = lds_ftile[f + 1] - lds_ftile[f];
+      }
+    }
+    __syncthreads();
+    // exclusive prefix sum of the tile counts in fragment order
+    int running = 0;
+    for (int base = 0; base < n_frags; base += NT) {
+      const int r = base + tid;
+      const int cnt = r < n_frags ? fpos[r] : 0;
+      int total;
+      const int off = block_excl_scan(cnt, sh, &total);
+      if (r < n_frags) fpos[r] = running + off;
+      running += total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kFrag; ++k) {
+      const int f = tid + k * NT;
+      if (f < n_frags) fkey[f] = (uint32_t)fpos[frank[k]];
+    }
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += NT) {
+      const int f = frag_of(t);
+      const int q = (int)fkey[f] + (lds_ftile[f + 1] - 1 - t);
+      tiles[q] = ntiles[t];
+      order[q] = q;
+    }
+  } else if (sh.err == 0 && n_tiles > 0 && n_tiles <= kRankSortMax) {
+    // Up to kRankSortMax tiles, every thread ranks its own keys against all of them (the keys
+    // are unique, so the ranks are a permutation): n^2 / threads broadcast reads from LDS,
+    // four keys per read, and one barrier, against the bitonic network's 55 barrier-separated
+    // passes at 1024 keys.
     uint32_t my_key[kMine];
 #pragma unroll
     for (int k = 0; k < kMine; ++k) {
