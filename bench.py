@@ -538,11 +538,12 @@ def _blas_info():
 
 
 def cpu_baseline(w, seconds, seed=0):
-    """The float64 oracle on the host cores, on a bounded sample of the same pack: random
-    blocks of up to 32 rows of one document (all heads) handed to a pool of processes, one per
-    core with one BLAS thread each, until `seconds` have elapsed; blocks still running then
-    are not counted."""
+    """The float64 oracle on the host cores, on a bounded sample of the same pack: blocks of up
+    to 32 rows of one document (all heads), in a random order that starts over once every
+    block has been handed out, fed to a pool of processes, one per core with one BLAS thread
+    each, until `seconds` have elapsed; blocks still running then are not counted."""
     import concurrent.futures as cf
+    import itertools
     import multiprocessing as mp
     import tempfile
     from oracle import timing as OT
@@ -556,7 +557,7 @@ def cpu_baseline(w, seconds, seed=0):
     rb = 32  # rows per task, inside one document
     tasks = [(int(cu[d]), int(lengths[d]), r0, min(r0 + rb, int(lengths[d])))
              for d in range(len(lengths)) for r0 in range(0, int(lengths[d]), rb)]
-    order = np.random.default_rng(seed).permutation(len(tasks))
+    order = itertools.cycle(np.random.default_rng(seed).permutation(len(tasks)).tolist())
     done = []
     with tempfile.TemporaryDirectory(dir="/tmp") as tmp:
         paths = {}
@@ -569,22 +570,25 @@ def cpu_baseline(w, seconds, seed=0):
                                     initargs=(paths, meta)) as ex:
             list(ex.map(OT.ready, range(n_proc)))  # workers up before the clock starts
             t0 = time.perf_counter()
-            futs = [ex.submit(OT.run_block, *tasks[i]) for i in order]
-            for f in cf.as_completed(futs):
+            inflight = {ex.submit(OT.run_block, *tasks[next(order)]) for _ in range(4 * n_proc)}
+            while True:
+                finished, inflight = cf.wait(inflight, return_when=cf.FIRST_COMPLETED)
                 if time.perf_counter() - t0 >= seconds:
                     break
-                done.append(f.result())
+                for f in finished:
+                    done.append(f.result())
+                    inflight.add(ex.submit(OT.run_block, *tasks[next(order)]))
             el = time.perf_counter() - t0
-            for f in futs:
+            for f in inflight:
                 f.cancel()
-    rows = np.concatenate([np.arange(a, a + n) for a, n in done]) if done else np.zeros(0, int)
-    pairs = int(np.sum(pos_in_doc[rows] + 1)) if len(rows) else 0
+    pairs = int(sum(np.sum(pos_in_doc[a:a + n] + 1) for a, n in done))
+    rows = int(sum(n for _, n in done))
     flops = 4 * p["d"] * p["heads"] * pairs
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(n_proc), "kind": "oracle",
             "host_cpus": cores, "cpu_model": _cpu_model(), "numpy": np.__version__, "blas": _blas_info(),
-            "sample": f"{len(rows)} of {p['tokens']} query rows (random blocks of up to {rb} rows of one document, "
-                      f"all {p['heads']} heads), "
-                      f"{pairs} visible pairs per head = {pairs / causal_pairs(lengths):.1%} of the pack, "
+            "sample": f"{len(done)} blocks of up to {rb} query rows of one document (all {p['heads']} heads) of the "
+                      f"{p['tokens']}-token pack, in a random order repeated once exhausted: {rows} rows, "
+                      f"{pairs} visible pairs per head = {pairs / causal_pairs(lengths):.2f} x the pack's, "
                       f"float64 numpy, {n_proc} processes x 1 BLAS thread, {el:.1f} s"}
 
 
