@@ -345,3 +345,44 @@ def merge_step_plans(plans):
 
 def total_pairs(plan_tiles):
     return sum(t["cost"] for t in plan_tiles)
+
+
+FUSED_SPAN_CAP = 4  # key spans one query tile of a fused ring holds
+FUSED_TILE_CAP = 4096  # query tiles one fused ring takes
+
+
+def fuse_step_plans(natural_plans):
+    """A ring's block steps fused per query tile: the steps cut the query shard into the same
+    tiles (the tiling depends on the query side only), so query tile x gathers the key spans
+    of tile x of every step, in step order, each span tagged with its step; its pairs and key
+    blocks are the sums over the steps.  Its attention is then one online softmax over all
+    the keys its rows see in any step: the rescale-and-sum of the steps' partials ("03 ·
+    长文负载均衡", section 3.2, DCP) taken inside one tile instead of after the steps.  Tiles
+    with key blocks go first, by key blocks descending (above COST_MAX as COST_MAX), ties in
+    natural order; then the tiles without spans, in natural order (the LPT rule of
+    "数据并行负载均衡", section 4.4, over whole query tiles).  ``natural_plans``: each step's
+    tiles in natural order (``tiles``).  None when a tile would hold more than FUSED_SPAN_CAP
+    spans, or there are more than FUSED_TILE_CAP tiles."""
+    n = len(natural_plans[0])
+    if any(len(p) != n for p in natural_plans):
+        raise ValueError("the steps' plans cut the query shard differently")
+    if n > FUSED_TILE_CAP:
+        return None
+    fused = []
+    for x in range(n):
+        first = natural_plans[0][x]
+        spans, steps, cost, blocks = [], [], 0, 0
+        for s, p in enumerate(natural_plans):
+            t = p[x]
+            if (t["q_start"], t["q_len"], t["q_pos0"]) != (first["q_start"], first["q_len"], first["q_pos0"]):
+                raise ValueError("the steps' plans cut the query shard differently")
+            spans += list(t["spans"])
+            steps += [s] * len(t["spans"])
+            cost += t["cost"]
+            blocks += t["blocks"]
+        if len(spans) > FUSED_SPAN_CAP:
+            return None
+        fused.append(dict(q_start=first["q_start"], q_len=first["q_len"], q_pos0=first["q_pos0"], spans=spans,
+                          span_steps=steps, cost=cost, blocks=blocks))
+    order = sorted(range(n), key=lambda x: (-min(fused[x]["blocks"], COST_MAX), x))
+    return [fused[x] for x in order]

@@ -534,3 +534,75 @@ def test_merge_step_plans_keeps_each_step_and_sorts(seed):
     assert all(x["spans"] for x in merged[:n_work]) and not any(x["spans"] for x in merged[n_work:])
     blocks = [x["blocks"] for x in merged[:n_work]]
     assert blocks == sorted(blocks, reverse=True)
+
+
+def test_fuse_step_plans_by_hand():
+    """Three query tiles over two steps, written out by hand.  Step 0: tile 0 one span of 10
+    keys (1 block), tile 1 none, tile 2 one span of 70 keys (2 blocks).  Step 1: tile 0 none,
+    tile 1 one span of 5 keys (1 block), tile 2 two spans of 64 and 1 keys (2 blocks).  Fused:
+    tile 2 (4 blocks, spans steps 0, 1, 1), then tiles 0 and 1 (1 block each, natural order)."""
+    def t(x, spans, cost):
+        return dict(q_start=16 * x, q_len=16, q_pos0=100 + 16 * x, spans=spans, cost=cost,
+                    blocks=sum(-(-n // P.BLOCK_KEYS) for _, n, _ in spans))
+    s0 = [t(0, [(0, 10, 0)], 7), t(1, [], 0), t(2, [(20, 70, 30)], 50)]
+    s1 = [t(0, [], 0), t(1, [(3, 5, 9)], 4), t(2, [(0, 64, 0), (64, 1, 64)], 9)]
+    got = P.fuse_step_plans([s0, s1])
+    assert [g["q_start"] for g in got] == [32, 0, 16]
+    assert got[0]["spans"] == [(20, 70, 30), (0, 64, 0), (64, 1, 64)] and got[0]["span_steps"] == [0, 1, 1]
+    assert [(g["cost"], g["blocks"]) for g in got] == [(59, 4), (7, 1), (4, 1)]
+    assert got[2]["span_steps"] == [1] and got[1]["span_steps"] == [0]
+
+
+def test_fuse_step_plans_refuses_past_the_span_capacity():
+    def t(n_spans):
+        return dict(q_start=0, q_len=8, q_pos0=0, spans=[(64 * i, 8, 0) for i in range(n_spans)], cost=8 * n_spans,
+                    blocks=n_spans)
+    assert P.fuse_step_plans([[t(2)], [t(2)]]) is not None
+    assert P.fuse_step_plans([[t(3)], [t(2)]]) is None
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fuse_step_plans_against_explicit_masks(seed):
+    """A zigzag rank's steps fused: each fused tile's spans of step s cover exactly the keys of
+    step s that some row of the tile sees (brute force over the explicit block mask: same
+    document, key position <= row position), its pairs are the visible pairs counted the same
+    way, and the order is key blocks descending, spanless tiles last."""
+    r = np.random.default_rng(100 + seed)
+    cp, chunk, bm = 4, 48, 16
+    T = 2 * cp * chunk
+    lengths = random_lengths(r, T)
+    pos, doc = A.pack_positions(lengths)
+    rank = int(r.integers(0, cp))
+    qi = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(rank, cp)])
+    kis, plans = [], []
+    for t in range(cp):
+        src = (rank - t) % cp
+        ki = np.concatenate([np.arange(c * chunk, (c + 1) * chunk) for c in A.zigzag_chunks_of_rank(src, cp)])
+        kis.append(ki)
+        plans.append(P.tiles(P.fragments_block(pos[qi], doc[qi], pos[ki], doc[ki]), bm))
+    fused = P.fuse_step_plans(plans)
+    if fused is None:  # more than FUSED_SPAN_CAP spans in some tile: nothing to check here
+        pytest.skip("a tile past the span capacity")
+    assert len(fused) == len(plans[0])
+    rows_seen = set()
+    for f in fused:
+        rows = qi[f["q_start"]:f["q_start"] + f["q_len"]]
+        rows_seen.update(range(f["q_start"], f["q_start"] + f["q_len"]))
+        pairs = 0
+        for s, ki in enumerate(kis):
+            vis = (doc[rows][:, None] == doc[ki][None, :]) & (pos[ki][None, :] <= pos[rows][:, None])
+            pairs += int(vis.sum())
+            want = set(np.nonzero(vis.any(axis=0))[0].tolist())
+            have = set()
+            for (ks, kl, _), st in zip(f["spans"], f["span_steps"]):
+                if st == s:
+                    have.update(range(ks, ks + kl))
+            assert have == want
+        assert f["cost"] == pairs
+    assert rows_seen == set(range(len(qi)))
+    n_work = sum(1 for f in fused if f["blocks"] > 0)
+    assert all(f["spans"] for f in fused[:n_work]) and not any(f["spans"] for f in fused[n_work:])
+    blocks = [f["blocks"] for f in fused[:n_work]]
+    assert blocks == sorted(blocks, reverse=True)
+    empty_starts = [f["q_start"] for f in fused[n_work:]]
+    assert empty_starts == sorted(empty_starts)
