@@ -212,7 +212,8 @@ class SlicesStep:
 class ZigzagStep:
     """one zigzag rank's share: cp block steps (plan + attention each) and cp-1 merges."""
 
-    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True, overlap=4, ring=True):
+    def __init__(self, torch, lb, workloads, rank=3, cp=8, chunk=8192, seed=0, graph=True, overlap=4, ring=True,
+                 fused=True):
         self.torch, self.lb = torch, lb
         self.ring = ring
         lengths = workloads.zigzag_pack_lengths(seed)
@@ -225,17 +226,30 @@ class ZigzagStep:
 
         self.share = lb.zigzag.RankShare(lengths, chunk, rank, cp, get_chunk)
         self.share.plan_all()  # allocates the per-step workspaces outside the timed region
+        # fused: the live steps as one item per query tile and kv head, no partials, no merges
+        self.fused = ring and fused and self.share.fusable
         # the share is replayed from one HIP graph: with ring, the live steps' plans, their
         # merged queue, one attention launch and the merges; without, the per-step attention
         # launches spread over `overlap` streams so that the steps overlap (none: one stream);
         # per-kernel events need eager launches one at a time (run_eager)
         self.streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap and not ring else None
-        if ring:
+        if self.fused:
+            self.share.plan_ring_fused()
+        elif ring:
             self.share.plan_ring()
-        self.graph = (self.share.capture(ring=True) if ring else self.share.capture(streams=self.streams)) \
-            if graph else None
-        self.kernel_name = ("attn_kernel<128,true,false,ring> (persistent, one LPT queue over the live steps; "
-                            "fp32 partials)" if ring else "attn_kernel<128,true> (persistent, LPT queue; fp32 partials)")
+        if not graph:
+            self.graph = None
+        elif self.fused:
+            self.graph = self.share.capture(fused=True)
+        else:
+            self.graph = self.share.capture(ring=True) if ring else self.share.capture(streams=self.streams)
+        if self.fused:
+            self.kernel_name = ("attn_kernel<128,true,false,true,true> (persistent, one LPT queue of query tiles, "
+                                "each against the keys of every live step; the merged result, no partials)")
+        else:
+            self.kernel_name = ("attn_kernel<128,true,false,true,false> (persistent, one LPT queue over the live "
+                                "steps; fp32 partials)" if ring else
+                                "attn_kernel<128,true,false,false,false> (persistent, LPT queue; fp32 partials)")
         self.H, self.d = 32, 128
         # pairs: positions and document ids of the rank's rows against each step's chunks
         pos, doc = lb.zigzag.token_meta(lengths)
@@ -266,6 +280,18 @@ class ZigzagStep:
         # then per step the attention launch and, from step 1 on, the merge; in ring mode
         # the plans are merged and one attention launch runs every step
         lb, sh = self.lb, self.share
+        if self.fused:
+            if evs is not None:
+                evs[0][0].record()
+            sh.plan_ring_fused()
+            if evs is not None:
+                evs[0][1].record()
+            live = [sh.steps[t] for t in sh.live_steps]
+            lb.ring_attn_run_fused(sh.q, [st["kv"][0] for st in live], [st["kv"][1] for st in live], sh.out, sh.lse,
+                                   sh.ring_workspace)
+            if evs is not None:
+                evs[0][2].record()
+            return
         if self.ring:
             if evs is not None:
                 evs[0][0].record()
@@ -311,7 +337,7 @@ class ZigzagBwdStep(ZigzagStep):
     Effective FLOPs 10 * d * H * pairs, 2.5x the forward's."""
 
     def __init__(self, torch, lb, workloads, seed=0, ring=True):
-        super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0, ring=False)
+        super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0, ring=False, fused=False)
         self.bwd_ring = ring
         sh = self.share
         sh.run_planned()
@@ -401,7 +427,8 @@ class CpJob:
 CP_RULES = ("zigzag", "per_document", "dispatch/16", "dispatch/32", "dispatch/64", "dispatch/128")
 
 
-def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4, ring=True):
+def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_document", overlap=4, ring=True,
+                  fused=True):
     if name == "longtail":
         p = workloads.longtail_pack(seed)
         w = VarlenStep([p], lb.MASK_CAUSAL_DOC, name, torch, lb)
@@ -434,13 +461,18 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
         w.packs = [p]
         return w
     if name == "zigzag":
-        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph, overlap=overlap, ring=ring)
+        w = ZigzagStep(torch, lb, workloads, seed=seed, graph=graph, overlap=overlap, ring=ring, fused=fused)
         w.config = {"workload": "one zigzag CP rank's share at cp=8: rank 3 of a 131072-token lognormal pack "
-                                f"(seed {seed}), 16 chunks of 8192, 8 ring steps and a merge per step after the "
-                                "first; steps whose chunks hold no key the rank's rows see (5 of 8 here, found on "
+                                f"(seed {seed}), 16 chunks of 8192, 8 ring steps"
+                                + (", fused per query tile (each tile against the keys of every live step in one "
+                                   "online softmax, the merged result written once)" if w.fused else
+                                   " and a merge per step after the first")
+                                + "; steps whose chunks hold no key the rank's rows see (5 of 8 here, found on "
                                 "the host from positions and document ids) run nothing",
                     "tokens": 16384, "heads": 32, "kv_heads": 8, "head_dim": 128,
-                    "launch": ("one HIP graph: the live steps' plans (one launch) merged into one longest-first "
+                    "launch": ("one HIP graph: the live steps' plans (one launch) fused per query tile into one "
+                               "longest-first queue, one attention launch" if w.fused else
+                               "one HIP graph: the live steps' plans (one launch) merged into one longest-first "
                                "queue, one attention launch over every live step, merges in step order" if ring else
                                f"one HIP graph: plan, the live steps' attention launches on {overlap} streams, merges "
                                "in step order" if overlap else "one HIP graph, one stream") if graph else "eager"}
@@ -669,6 +701,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="zigzag: launch the kernels one by one, no HIP graph")
     ap.add_argument("--no-ring", action="store_true",
                     help="zigzag, cp_job, zigzag_bwd: one attention (dK/dV) launch per live step instead of one over all of them")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="zigzag: the ring with a partial per live step and the merges, instead of the ring fused per "
+                         "query tile")
     ap.add_argument("--overlap", type=int, default=4,
                     help="zigzag, cp_job with --no-ring: streams the ring steps' attention launches are spread over "
                          "(0: one)")
@@ -705,7 +740,7 @@ def main():
     lb.lib()
     log(f"bench: building workload {args.workload}")
     w = make_workload(args.workload, args.seed, torch, lb, workloads, graph=not args.eager, rule=args.rule,
-                      overlap=args.overlap, ring=not args.no_ring)
+                      overlap=args.overlap, ring=not args.no_ring, fused=not args.no_fuse)
     if args.lpt_weights is not None:
         if not isinstance(w, VarlenStep):
             sys.exit("--lpt-weights applies to the varlen forward workloads")

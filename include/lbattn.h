@@ -356,6 +356,39 @@ lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv
                            hipStream_t stream);
 
 /*
+ * One rank's ring fused per query tile.  The steps' plans of one query shard cut it into the
+ * same tiles (the tiling depends on the query side only), so tile x of every step can run as
+ * one item: its rows against the key spans of every step, in one online softmax, which is the
+ * rescale-and-sum of the steps' partials ("03 · 长文负载均衡", section 3.2, DCP) taken inside the
+ * tile rather than by merges after the launch.  The ring then writes no partials and needs no
+ * merge; the queue holds one item per query tile and kv head, longest first ("数据并行负载均衡",
+ * section 4.4).  The result equals the merged partials to the rounding of the bf16 softmax weights
+ * (each path rounds them against its own running maximum), not bit for bit.
+ *
+ * lb_plan_ring_fused: as lb_plan_ring (same arguments and workspace), but tile x of the ring
+ *   gathers tile x of every step: spans in step order (at most LB_MAX_SPANS in all; span s's
+ *   step in bits 4s..4s+3 of `reserved`), pairs and key blocks summed.  Queue order: key
+ *   blocks descending (above 32767 as 32767), ties in query order, tiles without spans last
+ *   in query order.  Sets LB_DEVERR_SPANS when a tile would hold more spans (use lb_plan_ring
+ *   then), LB_DEVERR_PLAN when a step plan is not a forward block plan for these shapes or the
+ *   steps tile the queries differently, LB_DEVERR_CAPACITY above 4096 tiles or the workspace's
+ *   capacity; the ring then runs nothing.
+ * lb_ring_attn_run_fused: runs a fused ring.  q, k, v, n_kv as lb_ring_attn_run; out: fp32
+ *   [n_q][heads][d], lse: fp32 [heads][n_q], device pointers: the merged result over every
+ *   step.  Rows with no visible key in any step get lse = -inf and out unwritten.  A ring that
+ *   is not a fused ring for these shapes sets LB_DEVERR_PLAN and runs nothing.  Argument
+ *   errors return LB_EINVAL / LB_EUNSUPPORTED / LB_EWORKSPACE before anything is enqueued.
+ */
+lb_status lb_plan_ring_fused(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                             int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                             void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream);
+
+lb_status lb_ring_attn_run_fused(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                                 int32_t n_steps, const void* const* k, const void* const* v, const int32_t* n_kv,
+                                 float* out, float* lse, void* ring_workspace, size_t ring_workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * The backward of one rank's ring (the steps of lb_block_attn_bwd for n_steps key/value
  * chunks of one query shard), with every step's dK/dV items in one launch.  A dK/dV
  * launch ends with its longest key tiles (a tile near the start of a long document sweeps

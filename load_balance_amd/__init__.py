@@ -98,6 +98,10 @@ def lib() -> ctypes.CDLL:
     L.lb_plan_ring.restype = ctypes.c_int
     L.lb_ring_attn_run.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
     L.lb_ring_attn_run.restype = ctypes.c_int
+    L.lb_plan_ring_fused.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, SZ, P]
+    L.lb_plan_ring_fused.restype = ctypes.c_int
+    L.lb_ring_attn_run_fused.argtypes = [P, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    L.lb_ring_attn_run_fused.restype = ctypes.c_int
     L.lb_attn_run.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
     L.lb_attn_run.restype = ctypes.c_int
     L.lb_attn_run_lower.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, SZ, P]
@@ -433,9 +437,11 @@ def new_ring_workspace(n_steps: int, max_tokens: int, max_segments: int, heads: 
                        device=device)
 
 
-def plan_ring(workspaces, n_kv, n_q, heads, kv_heads, d, ring_workspace, stream=None):
+def plan_ring(workspaces, n_kv, n_q, heads, kv_heads, d, ring_workspace, stream=None, fused=False):
     """Merges the block-step plans in ``workspaces`` (step s made against n_kv[s] key/value
-    tokens, all for the same n_q query rows) into one longest-first queue in ring_workspace."""
+    tokens, all for the same n_q query rows) into one longest-first queue in ring_workspace.
+    fused=True (lb_plan_ring_fused): one tile per query tile with the spans of every step,
+    run by ring_attn_run_fused."""
     n = len(workspaces)
     if len(n_kv) != n:
         raise LBError("n_kv must have one entry per workspace")
@@ -446,8 +452,9 @@ def plan_ring(workspaces, n_kv, n_q, heads, kv_heads, d, ring_workspace, stream=
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
     nkv = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in n_kv])
     _gpu(ring_workspace, "ring_workspace")
-    _check(lib().lb_plan_ring(ptrs, sizes, nkv, n, n_q, heads, kv_heads, d, _ptr(ring_workspace),
-                              ring_workspace.numel(), ctypes.c_void_p(_stream(stream))), "lb_plan_ring")
+    fn, name = (lib().lb_plan_ring_fused, "lb_plan_ring_fused") if fused else (lib().lb_plan_ring, "lb_plan_ring")
+    _check(fn(ptrs, sizes, nkv, n, n_q, heads, kv_heads, d, _ptr(ring_workspace), ring_workspace.numel(),
+              ctypes.c_void_p(_stream(stream))), name)
     return ring_workspace
 
 
@@ -479,6 +486,36 @@ def ring_attn_run(q, ks, vs, outs, lses, ring_workspace, stream=None):
                                   _ptr(ring_workspace), ring_workspace.numel(), ctypes.c_void_p(_stream(stream))),
            "lb_ring_attn_run")
     return outs, lses
+
+
+def ring_attn_run_fused(q, ks, vs, out, lse, ring_workspace, stream=None):
+    """Runs a fused ring (plan_ring(..., fused=True)) in one launch: every step's keys and
+    values (ks[s], vs[s], bf16 [n_kv_s,H_kv,d]) for each query tile, the merged result into
+    out (fp32 [n_q,H,d]) and lse (fp32 [H,n_q])."""
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise LBError("q must be [n_q, H, d]")
+    n_q, H, d = q.shape
+    dev = q.device
+    n = len(ks)
+    if n < 1 or len(vs) != n:
+        raise LBError("ks and vs must have one entry per step (at least one)")
+    _ws(ring_workspace, "ring_workspace", dev)
+    if ks[0].dim() != 3:
+        raise LBError("ks[s] must be [n_kv, H_kv, d]")
+    Hkv = ks[0].shape[1]
+    for i in range(n):
+        _dev(ks[i], f"ks[{i}]", torch.bfloat16, (ks[i].shape[0], Hkv, d), dev)
+        _dev(vs[i], f"vs[{i}]", torch.bfloat16, tuple(ks[i].shape), dev)
+    _dev(out, "out", torch.float32, (n_q, H, d), dev)
+    _dev(lse, "lse", torch.float32, (H, n_q), dev)
+    ptrs = lambda ts: (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in ts])
+    nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[0] for k in ks])
+    _gpu(q, "q")
+    _check(lib().lb_ring_attn_run_fused(_ptr(q), n_q, H, Hkv, d, n, ptrs(ks), ptrs(vs), nkv, _ptr(out), _ptr(lse),
+                                        _ptr(ring_workspace), ring_workspace.numel(),
+                                        ctypes.c_void_p(_stream(stream))), "lb_ring_attn_run_fused")
+    return out, lse
 
 
 def _run_operands(q, k, v, out, lse, workspace):

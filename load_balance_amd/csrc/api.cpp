@@ -372,9 +372,10 @@ size_t lb_ring_workspace_bytes(int32_t n_steps, int32_t max_tokens, int32_t max_
   return (size_t)align256(kRingTilesOffset + tiles * (int64_t)sizeof(lb_plan_tile));
 }
 
-lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
-                       int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
-                       void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream) {
+namespace {
+lb_status ring_merge_args(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                          int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                          void* ring_workspace, size_t ring_workspace_bytes, RingMergeArgs* out) {
   if (n_steps < 1 || n_steps > kMaxPlanSteps || n_q < 0) return LB_EINVAL;
   if (!workspaces || !workspace_bytes || !n_kv || !ring_workspace) return LB_EINVAL;
   lb_status st = check_heads(heads, kv_heads, d);
@@ -398,13 +399,37 @@ lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, c
   m.ring = static_cast<char*>(ring_workspace);
   m.ring_cap = (int32_t)std::min<int64_t>(cap, INT32_MAX);
   m.transposed = 0;
+  *out = m;
+  return LB_OK;
+}
+}  // namespace
+
+lb_status lb_plan_ring(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                       int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                       void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream) {
+  RingMergeArgs m{};
+  const lb_status st = ring_merge_args(workspaces, workspace_bytes, n_kv, n_steps, n_q, heads, kv_heads, d,
+                                       ring_workspace, ring_workspace_bytes, &m);
+  if (st != LB_OK) return st;
   return launch_ring_merge(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
-lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d, int32_t n_steps,
-                           const void* const* k, const void* const* v, const int32_t* n_kv, float* const* out,
-                           float* const* lse, void* ring_workspace, size_t ring_workspace_bytes,
-                           hipStream_t stream) {
+lb_status lb_plan_ring_fused(void* const* workspaces, const size_t* workspace_bytes, const int32_t* n_kv,
+                             int32_t n_steps, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                             void* ring_workspace, size_t ring_workspace_bytes, hipStream_t stream) {
+  RingMergeArgs m{};
+  const lb_status st = ring_merge_args(workspaces, workspace_bytes, n_kv, n_steps, n_q, heads, kv_heads, d,
+                                       ring_workspace, ring_workspace_bytes, &m);
+  if (st != LB_OK) return st;
+  return launch_ring_fuse(m, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+
+namespace {
+// fused: one result (out[0], lse[0]) for every step instead of a partial per step
+lb_status ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d, int32_t n_steps,
+                        const void* const* k, const void* const* v, const int32_t* n_kv, float* const* out,
+                        float* const* lse, void* ring_workspace, size_t ring_workspace_bytes, bool fused,
+                        hipStream_t stream) {
   if (n_steps < 1 || n_steps > kMaxPlanSteps || n_q < 0) return LB_EINVAL;
   if (!q || !k || !v || !n_kv || !out || !lse || !ring_workspace) return LB_EINVAL;
   lb_status st = check_heads(heads, kv_heads, d);
@@ -413,16 +438,20 @@ lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv
   if (!aligned(ring_workspace, 256)) return LB_EWORKSPACE;
   if ((int64_t)ring_workspace_bytes < kRingTilesOffset) return LB_EWORKSPACE;
   RingSteps r{};
-  for (int s = 0; s < n_steps; ++s) {
-    if (n_kv[s] < 0 || !out[s] || !lse[s]) return LB_EINVAL;
+  const int n_out = fused ? 1 : n_steps;
+  for (int s = 0; s < n_out; ++s) {
+    if (!out[s] || !lse[s]) return LB_EINVAL;
     if (!aligned(out[s], 16) || !aligned(lse[s], 4)) return LB_EINVAL;
     for (int o = 0; o < s; ++o)
       if (out[o] == out[s] || lse[o] == lse[s]) return LB_EINVAL;  // each step writes its own partial
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    if (n_kv[s] < 0) return LB_EINVAL;
     if (n_kv[s] > 0 && (!k[s] || !v[s] || !aligned(k[s], 16) || !aligned(v[s], 16))) return LB_EINVAL;
     r.k[s] = n_kv[s] > 0 ? k[s] : q;
     r.v[s] = n_kv[s] > 0 ? v[s] : q;
-    r.out[s] = out[s];
-    r.lse[s] = lse[s];
+    r.out[s] = out[fused ? 0 : s];
+    r.lse[s] = lse[fused ? 0 : s];
     r.n_kv[s] = n_kv[s];
   }
   r.n_steps = n_steps;
@@ -444,7 +473,26 @@ lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv
   at.scale_log2 = (float)(1.0 / std::sqrt((double)d) * 1.4426950408889634);
   at.ws = static_cast<char*>(ring_workspace);
   at.ws_bytes = (int64_t)ring_workspace_bytes;
-  return launch_ring_attention(at, r, d, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+  return launch_ring_attention(at, r, d, workers, fused, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+}  // namespace
+
+lb_status lb_ring_attn_run(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d, int32_t n_steps,
+                           const void* const* k, const void* const* v, const int32_t* n_kv, float* const* out,
+                           float* const* lse, void* ring_workspace, size_t ring_workspace_bytes,
+                           hipStream_t stream) {
+  return ring_attn_run(q, n_q, heads, kv_heads, d, n_steps, k, v, n_kv, out, lse, ring_workspace,
+                       ring_workspace_bytes, false, stream);
+}
+
+lb_status lb_ring_attn_run_fused(const void* q, int32_t n_q, int32_t heads, int32_t kv_heads, int32_t d,
+                                 int32_t n_steps, const void* const* k, const void* const* v, const int32_t* n_kv,
+                                 float* out, float* lse, void* ring_workspace, size_t ring_workspace_bytes,
+                                 hipStream_t stream) {
+  float* const outs[1] = {out};
+  float* const lses[1] = {lse};
+  return ring_attn_run(q, n_q, heads, kv_heads, d, n_steps, k, v, n_kv, outs, lses, ring_workspace,
+                       ring_workspace_bytes, true, stream);
 }
 
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,

@@ -119,7 +119,10 @@ struct KvBlock {
 // queue; a tile's step (its `reserved` field) selects the keys, values and outputs of that
 // step in r.  One launch then runs every step of a rank's ring, each step's partial into its
 // own buffers, with no tail per step.
-template <int D, bool OUT_F32, bool LOWER, bool RING>
+// FUSED (with RING): a fused ring, one tile per query tile with the key spans of every step (span
+// s's step in bits 4s..4s+3 of the tile's `reserved`); an item runs its rows against the keys of
+// every step in one online softmax and writes the merged result to the first step's buffers.
+template <int D, bool OUT_F32, bool LOWER, bool RING, bool FUSED = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps r) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * Lds<D>::stage];
   // s_item[p]: the item after the one whose descriptor is in s_tile[p] (written by thread 0
@@ -172,7 +175,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
                         hdr->off_order + n_tiles_hdr * 4 > a.ws_bytes;
   if constexpr (RING) {
     // the ring was merged from plans made for these steps' key/value counts
-    mismatch = mismatch || r.n_steps < 1 || r.n_steps > kMaxPlanSteps || hdr->ring_steps != r.n_steps;
+    mismatch = mismatch || r.n_steps < 1 || r.n_steps > kMaxPlanSteps || hdr->ring_steps != r.n_steps ||
+               hdr->ring_fused != (FUSED ? 1 : 0);
 #pragma unroll
     for (int s = 0; s < kMaxPlanSteps; ++s)
       if (s < r.n_steps && hdr->ring_n_kv[s] != r.n_kv[s]) mismatch = true;
@@ -182,9 +186,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
   const lb_plan_tile* tiles = reinterpret_cast<const lb_plan_tile*>(a.ws + (mismatch ? 0 : hdr->off_tiles));
   if (mismatch && blockIdx.x == 0 && tid == 0) atomicOr(&hdr->err, LB_DEVERR_PLAN);
   auto tile_at = [&](int64_t i) -> const lb_plan_tile* { return &tiles[i]; };
-  // a ring tile's step, kept inside the launch's step table
+  // a ring tile's step (a fused ring tile: its first span's), kept inside the launch's step table
   auto step_of = [&](const lb_plan_tile* T) -> int {
-    return min(max(__builtin_amdgcn_readfirstlane(T->reserved), 0), r.n_steps - 1);
+    const int v = __builtin_amdgcn_readfirstlane(T->reserved);
+    return min(max(FUSED ? (v & 15) : v, 0), r.n_steps - 1);
   };
 
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       const lb_plan_tile* T = tile_at(n_tiles_hdr - n_empty + e);
       const int q_start = T->q_start, q_len = T->q_len;
       float* lse_e = a.lse;
-      if constexpr (RING) lse_e = r.lse[step_of(T)];
+      if constexpr (RING) lse_e = r.lse[FUSED ? 0 : step_of(T)];
       for (int idx = tid; idx < q_len * a.heads; idx += kThreads)
         lse_e[(int64_t)(idx / q_len) * a.n_q + q_start + idx % q_len] = -__builtin_inff();
     }
@@ -356,11 +361,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
     const lb_plan_tile* T = &s_tile[slot];  // this item's descriptor, in LDS
     const char* Kit = Kb;
     const char* Vit = Vb;
-    int step = 0;
+    int step = 0;              // the step whose buffers the item writes
+    uint32_t span_steps = 0;   // FUSED: span s's step in bits 4s..4s+3
     if constexpr (RING) {
-      step = step_of(T);
-      Kit = reinterpret_cast<const char*>(r.k[step]);
-      Vit = reinterpret_cast<const char*>(r.v[step]);
+      const int st0 = step_of(T);
+      Kit = reinterpret_cast<const char*>(r.k[st0]);
+      Vit = reinterpret_cast<const char*>(r.v[st0]);
+      if constexpr (FUSED) span_steps = __builtin_amdgcn_readfirstlane((uint32_t)T->reserved);
+      else step = st0;
     }
     // tile fields, read once and kept wave-uniform
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
@@ -550,8 +558,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a, RingSteps
       const uint32_t lds = ring_lds + slot_i * Lds<D>::stage;
       const int k0 = __builtin_amdgcn_readfirstlane(iss.start + iss.key0);
       const int valid = __builtin_amdgcn_readfirstlane(min(iss.len - iss.key0, BN));
-      copier.issue(Kit, row_bytes, k0, valid, g, lds);
-      copier.issue(Vit, row_bytes, k0, valid, g, lds + Lds<D>::kBytes);
+      const char* Kx = Kit;
+      const char* Vx = Vit;
+      if constexpr (FUSED) {  // the keys and values of the step the span belongs to
+        const int st = min((int)(span_steps >> (4 * iss_s)) & 15, r.n_steps - 1);
+        Kx = reinterpret_cast<const char*>(r.k[st]);
+        Vx = reinterpret_cast<const char*>(r.v[st]);
+      }
+      copier.issue(Kx, row_bytes, k0, valid, g, lds);
+      copier.issue(Vx, row_bytes, k0, valid, g, lds + Lds<D>::kBytes);
       advance(iss, iss_s);
     };
     KvBlock prev{0, 0, 0, 0, LB_NO_LOWER_BOUND};
@@ -720,9 +735,15 @@ hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, 
   return hipGetLastError();
 }
 
-hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, hipStream_t s) {
-  if (d == 128) hipLaunchKernelGGL((attn_kernel<128, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
-  else hipLaunchKernelGGL((attn_kernel<64, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, bool fused,
+                                 hipStream_t s) {
+  if (d == 128) {
+    if (fused) hipLaunchKernelGGL((attn_kernel<128, true, false, true, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+    else hipLaunchKernelGGL((attn_kernel<128, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+  } else {
+    if (fused) hipLaunchKernelGGL((attn_kernel<64, true, false, true, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+    else hipLaunchKernelGGL((attn_kernel<64, true, false, true>), dim3(n_workers), dim3(kThreads), 0, s, a, r);
+  }
   return hipGetLastError();
 }
 

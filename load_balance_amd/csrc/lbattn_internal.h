@@ -23,6 +23,7 @@ constexpr int kBlockN = LB_BLOCK_KEYS;
 constexpr int kPlanThreads = 1024;
 constexpr int kSortCap = 32768;     // tiles per plan (32-bit sort keys, 128 KB of LDS)
 constexpr int kRingSortCap = 16384; // work tiles one ring merge takes (two int arrays in LDS)
+constexpr int kFusedTileCap = 4096;  // query tiles one fused ring takes (its sort keys in LDS)
 constexpr int kMaxWorkers = 2048;   // persistent workgroups per launch
 constexpr int kXcds = 8;            // accelerator complex dies (XCDs) of an MI355X, one L2 each
 
@@ -53,6 +54,10 @@ struct WsHeader {
   // ring workspaces only (magic kRingMagic): the steps merged, and each step's key/value count
   int32_t ring_steps;
   int32_t ring_n_kv[LB_MAX_PLAN_STEPS];
+  // 1: a fused ring, one tile per query tile with the spans of every step (each span's step in
+  // 4 bits of the tile's `reserved`, span s at bits 4s..4s+3); the steps' results are one
+  int32_t ring_fused;
+  int64_t off_ntiles;  // plan workspaces: the tiles in natural (query) order
 };
 
 constexpr uint32_t kPlanMagic = 0x4C424154u;
@@ -225,7 +230,9 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_steps(const PlanBatch& b, int n_steps, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int d, bool out_f32, bool lower, int n_workers, hipStream_t s);
 hipError_t launch_ring_merge(const RingMergeArgs& m, hipStream_t s);
-hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, hipStream_t s);
+hipError_t launch_ring_fuse(const RingMergeArgs& m, hipStream_t s);
+hipError_t launch_ring_attention(const AttnArgs& a, const RingSteps& r, int d, int n_workers, bool fused,
+                                 hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_lse_merge_parts(const MergePartsArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);

@@ -763,6 +763,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     hdr->off_kvruns = a.L.off_kvruns;
     hdr->off_tiles = a.L.off_tiles;
     hdr->off_order = a.L.off_order;
+    hdr->off_ntiles = a.L.off_ntiles;
     hdr->off_workers = a.L.off_workers;
     hdr->cap_frags = a.L.cap_frags;
     hdr->cap_tiles = a.L.cap_tiles;
@@ -774,6 +775,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& a, PlanShared& sh) {
     hdr->plan_n_kv = pair_sides ? a.n_kv : a.total_tokens;
     hdr->plan_kv_heads = a.kv_heads;
     hdr->plan_heads = a.heads;
+    hdr->ring_fused = 0;
     hdr->done = 0;
     hdr->magic = kPlanMagic;
   }
@@ -942,6 +944,177 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
     rh->plan_kv_heads = m.kv_heads;
     rh->ring_steps = n_steps;
     for (int s = 0; s < kMaxPlanSteps; ++s) rh->ring_n_kv[s] = s < n_steps ? m.n_kv[s] : 0;
+    rh->ring_fused = 0;
+    rh->off_ntiles = 0;
+    rh->done = 0;
+    rh->magic = kRingMagic;
+  }
+}
+
+// ---- a fused ring: one tile per query tile, with the key spans of every step ---------------
+// The steps' plans cut the query shard into the same tiles (the tiling depends on the query
+// side only), so query tile x of the fused ring gathers tile x of every step, read from the
+// natural-order copy each plan keeps: its spans in step order, each span's step in 4 bits of
+// `reserved` (span s at bits 4s..4s+3), its pairs and key blocks summed.  One attention item
+// then runs the rows against the keys of every step with one online softmax and writes what
+// the steps' partials would have merged to (the rescale-and-sum of the partials, taken inside
+// the tile).  Queue order: key blocks descending (above 32767 as 32767), ties in natural order,
+// the tiles without spans last in natural order -- the unique 32-bit keys (32767 - blocks) << 17
+// | x, ranked against each other in LDS.  A tile with more than LB_MAX_SPANS spans refuses the
+// ring (LB_DEVERR_SPANS), as do more than kFusedTileCap tiles (LB_DEVERR_CAPACITY).
+__device__ __forceinline__ void fused_tile(const lb_plan_tile* const* nt_of, int n_steps, int x, lb_plan_tile* F,
+                                           bool* same_rows, int* n_spans) {
+  const lb_plan_tile* t0 = &nt_of[0][x];
+  F->q_start = t0->q_start;
+  F->q_len = t0->q_len;
+  F->q_pos0 = t0->q_pos0;
+#pragma unroll
+  for (int o = 0; o < LB_MAX_SPANS; ++o) {
+    F->k_start[o] = 0;
+    F->k_len[o] = 0;
+    F->k_pos0[o] = 0;
+    F->k_lo[o] = LB_NO_LOWER_BOUND;
+  }
+  int ns = 0, blocks = 0;
+  int64_t cost = 0;
+  uint32_t steps = 0;
+  bool same = true;
+  for (int s = 0; s < n_steps; ++s) {
+    const lb_plan_tile* t = &nt_of[s][x];
+    same = same && t->q_start == F->q_start && t->q_len == F->q_len && t->q_pos0 == F->q_pos0;
+    const int tn = min(max(t->n_spans, 0), LB_MAX_SPANS);
+    // span slots chosen by comparison, not by a computed index: the tile stays in registers
+#pragma unroll
+    for (int sp = 0; sp < LB_MAX_SPANS; ++sp) {
+      if (sp >= tn) break;
+#pragma unroll
+      for (int o = 0; o < LB_MAX_SPANS; ++o)
+        if (o == ns) {
+          F->k_start[o] = t->k_start[sp];
+          F->k_len[o] = t->k_len[sp];
+          F->k_pos0[o] = t->k_pos0[sp];
+        }
+      if (ns < LB_MAX_SPANS) steps |= (uint32_t)s << (4 * ns);
+      ++ns;
+    }
+    cost += t->cost;
+    blocks += t->blocks;
+  }
+  F->n_spans = min(ns, LB_MAX_SPANS);
+  F->cost = cost;
+  F->blocks = blocks;
+  F->reserved = (int32_t)steps;
+  *same_rows = same;
+  *n_spans = ns;
+}
+
+__global__ __launch_bounds__(NT) void ring_fuse_kernel(RingMergeArgs m) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kFusedTileCap];
+  __shared__ const lb_plan_tile* nt_of[kMaxPlanSteps];
+  __shared__ int32_t n_of[kMaxPlanSteps], err_of[kMaxPlanSteps];
+  __shared__ int64_t pairs_of[kMaxPlanSteps];
+  __shared__ int32_t err;        // written by thread 0 before the second barrier only
+  __shared__ int32_t err_tiles;  // found while the tiles are gathered
+  __shared__ int32_t n_empty;
+  const int tid = threadIdx.x;
+  const int n_steps = m.n_steps;
+  WsHeader* rh = reinterpret_cast<WsHeader*>(m.ring);
+  lb_plan_tile* out = reinterpret_cast<lb_plan_tile*>(m.ring + kRingTilesOffset);
+  if (tid < n_steps) {
+    const int s = tid;
+    const WsHeader* h = reinterpret_cast<const WsHeader*>(m.step_ws[s]);
+    const int64_t nt = h->n_tiles;
+    // a step's plan must be a forward block plan made for these shapes, with its natural-order
+    // tiles inside its workspace; its own error bits pass on
+    const bool bad = h->magic != kPlanMagic || h->transposed != 0 || h->has_lower != 0 ||
+                     h->plan_n_q != m.n_q || h->plan_n_kv != m.n_kv[s] || h->plan_heads != m.heads ||
+                     h->plan_kv_heads != m.kv_heads || nt < 0 || h->off_ntiles < kWorkersOffset ||
+                     h->off_ntiles + nt * (int64_t)sizeof(lb_plan_tile) > m.step_ws_bytes[s];
+    err_of[s] = bad ? LB_DEVERR_PLAN : h->err;
+    n_of[s] = bad ? 0 : (int)nt;
+    nt_of[s] = reinterpret_cast<const lb_plan_tile*>(m.step_ws[s] + (bad ? 0 : h->off_ntiles));
+    pairs_of[s] = bad ? 0 : h->total_pairs;
+  }
+  if (tid == 0) {
+    err_tiles = 0;
+    n_empty = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int e = 0;
+    for (int s = 0; s < n_steps; ++s) e |= err_of[s] | (n_of[s] != n_of[0] ? LB_DEVERR_PLAN : 0);
+    if (n_of[0] > kFusedTileCap || n_of[0] > m.ring_cap) e |= LB_DEVERR_CAPACITY;
+    err = e;
+  }
+  __syncthreads();
+  const int N = err == 0 ? n_of[0] : 0;
+  // pass 1: every tile's key (and its checks)
+  for (int x = tid; x < N; x += NT) {
+    lb_plan_tile F;
+    bool same;
+    int ns;
+    fused_tile(nt_of, n_steps, x, &F, &same, &ns);
+    if (!same) atomicOr(&err_tiles, LB_DEVERR_PLAN);
+    if (ns > LB_MAX_SPANS) atomicOr(&err_tiles, LB_DEVERR_SPANS);
+    if (F.blocks <= 0) atomicAdd(&n_empty, 1);
+    keys[x] = (uint32_t)(32767 - min(max(F.blocks, 0), 32767)) << 17 | (uint32_t)x;
+  }
+  const int n4 = (N + 3) & ~3;
+  if (tid < n4 - N) keys[N + tid] = ~0u;  // above every key: never counted
+  __syncthreads();
+  // pass 2: each tile's rank among the keys (unique, so the ranks are a permutation), and the
+  // tile written at it
+  if (err_tiles == 0) {
+    const uint4* keys4 = reinterpret_cast<const uint4*>(keys);
+    for (int x = tid; x < N; x += NT) {
+      const uint32_t k = keys[x];
+      int rank = 0;
+      for (int i = 0; i < n4 / 4; ++i) {
+        const uint4 v = keys4[i];
+        rank += (v.x < k ? 1 : 0) + (v.y < k ? 1 : 0) + (v.z < k ? 1 : 0) + (v.w < k ? 1 : 0);
+      }
+      lb_plan_tile F;
+      bool same;
+      int ns;
+      fused_tile(nt_of, n_steps, x, &F, &same, &ns);
+      out[rank] = F;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int e = err | err_tiles;
+    const bool ok = e == 0;
+    int64_t p = 0;
+    for (int s = 0; s < n_steps; ++s) p += pairs_of[s];
+    const int nq = m.kv_heads % kXcds == 0 ? kXcds : 1;
+    const int n_work = ok ? N - n_empty : 0;
+    rh->err = e;
+    rh->n_frags = 0;
+    rh->n_kvruns = 0;
+    rh->n_tiles = ok ? N : 0;
+    rh->n_empty = ok ? n_empty : 0;
+    rh->n_items = n_work * m.kv_heads;
+    rh->n_queues = nq;
+    rh->per_queue = n_work * m.kv_heads / nq;
+    for (int q = 0; q < kXcds; ++q) rh->queue_head[q] = 0;
+    rh->tile_rows = 0;
+    rh->n_workers = 0;
+    rh->off_frags = rh->off_kvruns = 0;
+    rh->off_tiles = rh->off_order = kRingTilesOffset;  // queue order is storage order
+    rh->off_workers = kWorkersOffset;
+    rh->off_ntiles = 0;
+    rh->cap_frags = 0;
+    rh->cap_tiles = m.ring_cap;
+    rh->total_pairs = ok ? p : 0;
+    rh->transposed = 0;
+    rh->has_lower = 0;
+    rh->plan_n_q = m.n_q;
+    rh->plan_n_kv = 0;
+    rh->plan_heads = m.heads;
+    rh->plan_kv_heads = m.kv_heads;
+    rh->ring_steps = n_steps;
+    for (int s = 0; s < kMaxPlanSteps; ++s) rh->ring_n_kv[s] = s < n_steps ? m.n_kv[s] : 0;
+    rh->ring_fused = 1;
     rh->done = 0;
     rh->magic = kRingMagic;
   }
@@ -951,6 +1124,11 @@ __global__ __launch_bounds__(NT) void ring_merge_kernel(RingMergeArgs m) {
 
 hipError_t launch_ring_merge(const RingMergeArgs& m, hipStream_t s) {
   hipLaunchKernelGGL(ring_merge_kernel, dim3(1), dim3(NT), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fuse(const RingMergeArgs& m, hipStream_t s) {
+  hipLaunchKernelGGL(ring_fuse_kernel, dim3(1), dim3(NT), 0, s, m);
   return hipGetLastError();
 }
 

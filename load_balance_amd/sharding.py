@@ -241,6 +241,21 @@ def step_span_count(q_pos, q_doc, kv_pos, kv_doc, shared_doc: int = -1) -> int:
     return worst
 
 
+def fused_span_count(q_pos, q_doc, kv_sides, shared_doc: int = -1) -> int:
+    """The most key spans one query run meets over all the given steps together (the sum of
+    its per-step counts, ``step_span_count``'s rule): a tile of a fused ring holds at most
+    MAX_SPANS, so a ring fuses when this is within it."""
+    qr = _runs(np.asarray(q_pos), np.asarray(q_doc))
+    total = np.zeros(len(qr), dtype=np.int64)
+    for kv_pos, kv_doc in kv_sides:
+        kr = _runs(np.asarray(kv_pos), np.asarray(kv_doc))
+        n_shared = len(_full_spans(kr, shared_doc))
+        for i, (_, ln, p0, d) in enumerate(qr):
+            total[i] += int(np.count_nonzero((kr[:, 3] == d) & (kr[:, 2] <= p0 + ln - 1)))
+            total[i] += n_shared if shared_doc >= 0 and int(d) != shared_doc else 0
+    return int(total.max()) if len(total) else 0
+
+
 def _segments(doc, what):
     """(doc, start, length) of each maximal range of equal document id; a document must
     occupy one range (its tokens contiguous, as every sharding rule here leaves them)."""
@@ -441,6 +456,15 @@ class ShardedRank:
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None
+        self._set_fusable(qp, qd)
+
+    def _set_fusable(self, q_pos, q_doc):
+        """The live steps can run as a fused ring (run_fused) when they are all block steps and
+        no query run meets more than MAX_SPANS key runs over all of them together."""
+        live_sides = [(self.steps[t]["kv_pos"].cpu().numpy(), self.steps[t]["kv_doc"].cpu().numpy())
+                      for t in self.live_steps]
+        self.fusable = bool(self.live_steps) and not any("slices" in self.steps[t] for t in self.live_steps) and \
+            fused_span_count(q_pos, q_doc, live_sides, self.shared_doc) <= MAX_SPANS
 
     def _no_live_step(self):
         """The result when no step has a visible pair: every row sees nothing."""
@@ -656,14 +680,45 @@ class ShardedRank:
         self.merge_partials(stream)
         return self.out, self.lse
 
-    def capture(self, stream=None, streams=None, ring=False):
+    def plan_ring_fused(self, stream=None):
+        """plan_all(), then the live steps' plans fused per query tile in the ring workspace."""
+        from . import new_ring_workspace, plan_ring
+        if not self.fusable:
+            raise ValueError("this share's live steps do not fuse (a slice-list step, or a query run meeting "
+                             f"more than {MAX_SPANS} key runs over all of them)")
+        live = [self.steps[t] for t in self.live_steps]
+        if getattr(self, "ring_workspace", None) is None:
+            n_max, runs, H, Hkv, device = self._ws_shape
+            self.ring_workspace = new_ring_workspace(len(live), n_max, runs, H, Hkv, device=device)
+        n_q, H, d = self.q.shape
+        self.plan_all(stream)
+        plan_ring([self.step_workspaces[t] for t in self.live_steps], [st["kv"].shape[1] for st in live], n_q, H,
+                  live[0]["kv"].shape[2], d, self.ring_workspace, stream=stream, fused=True)
+
+    def run_fused(self, stream=None):
+        """The share as a fused ring: one item per query tile and kv head runs the tile's rows
+        against the keys of every live step in one online softmax and writes out, lse
+        directly.  No partials, no merges; equal to run_ring() to the rounding of the bf16 softmax
+        weights (each path rounds them against its own running maximum)."""
+        from . import ring_attn_run_fused
+        if not self.live_steps:
+            return self._no_live_step()
+        self.plan_ring_fused(stream)
+        live = [self.steps[t] for t in self.live_steps]
+        ring_attn_run_fused(self.q, [st["kv"][0] for st in live], [st["kv"][1] for st in live], self.out, self.lse,
+                            self.ring_workspace, stream=stream)
+        return self.out, self.lse
+
+    def capture(self, stream=None, streams=None, ring=False, fused=False):
         """Captures run_planned() -- one planning launch, an attention launch per live step and
         a merge for each after the first -- or, given side streams, run_overlapped(), or with
         ring=True run_ring(), into a HIP graph, so that
         replay() launches the whole share at once.  Every kernel of the share is safe to
         replay: the planner resets the queue heads and the attention kernel rewinds them,
         and nothing in it clears memory with a memset node."""
-        if ring:
+        if fused:
+            body = lambda st=None: self.run_fused(stream=st)
+        elif ring:
             body = lambda st=None: self.run_ring(stream=st)
         else:
             body = (lambda st=None: self.run_planned(stream=st)) if streams is None else \

@@ -95,3 +95,4 @@ class RankShare(ShardedRank):
         self.step_workspaces = None
         self.graph = None
         self.overlap_buffers = None
+        self._set_fusable(qpos, qdoc)

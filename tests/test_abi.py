@@ -237,6 +237,41 @@ def test_ring_host_checks(L):
     assert run(ring=P(0x300010)) == LB_EWORKSPACE
 
 
+
+def test_fused_ring_host_checks(L):
+    """lb_plan_ring_fused and lb_ring_attn_run_fused reject bad arguments on the host, before
+    anything is enqueued, as their unfused counterparts do."""
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    arr = lambda t, xs: (t * len(xs))(*xs)
+    two = L.lb_ring_workspace_bytes(2, 64, 3, 2, 2)
+    ring = P(0x300000)
+    wss = [P(0x100000), P(0x200000)]
+    need = L.lb_workspace_bytes(64, 3, 2, 2)
+
+    def plan(n_steps=2, ws=wss, n_kv=(64, 64), d=64, ring=ring, ring_bytes=two):
+        return L.lb_plan_ring_fused(arr(P, ws), arr(SZ, (need, need)), arr(I32, n_kv), n_steps, 64, 2, 2, d, ring,
+                                    ring_bytes, None)
+    assert plan(n_steps=0) == LB_EINVAL
+    assert plan(n_steps=17) == LB_EINVAL
+    assert plan(ring=None) == LB_EINVAL
+    assert plan(ring=P(0x300010)) == LB_EWORKSPACE
+    assert plan(ring_bytes=1024) == LB_EWORKSPACE
+    assert plan(ws=[P(0x100000), ring]) == LB_EINVAL
+    assert plan(n_kv=(64, -1)) == LB_EINVAL
+    assert plan(d=48) == LB_EUNSUPPORTED
+
+    def run(n_steps=2, k=(FAKE, FAKE), n_kv=(64, 64), out=P(0x400000), lse=P(0x600000), n_q=0, d=64, ring=ring):
+        return L.lb_ring_attn_run_fused(FAKE, n_q, 2, 2, d, n_steps, arr(P, k), arr(P, k), arr(I32, n_kv), out, lse,
+                                        ring, two, None)
+    assert run() == LB_OK                                  # no query rows: nothing to launch
+    assert run(n_steps=0) == LB_EINVAL
+    assert run(out=None) == LB_EINVAL
+    assert run(lse=P(0x600002)) == LB_EINVAL               # lse not 4-byte aligned
+    assert run(k=(FAKE, None)) == LB_EINVAL
+    assert run(n_kv=(64, -2)) == LB_EINVAL
+    assert run(d=48) == LB_EUNSUPPORTED
+    assert run(ring=P(0x300010)) == LB_EWORKSPACE
+
 def test_ring_backward_host_checks(L):
     """lb_block_attn_bwd_ring rejects bad arguments on the host, before anything is enqueued."""
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
