@@ -777,13 +777,21 @@ def main():
     ms_per_step = el / args.steps * 1e3
     eager_ms_per_step = None
     if graphed:
-        # per-kernel times come from one more pass of eager launches, outside the timed region
-        log(f"bench: {args.steps} eager steps for the per-kernel events")
+        # per-kernel times come from more passes of eager launches, outside the timed region: one
+        # plain pass for the eager step time, then one with events, each step's launches queued
+        # behind a short spin kernel so that the host's launch latency falls before the step's
+        # first event rather than between its events (a share whose kernels finish faster than
+        # the host enqueues them would otherwise show the host's time as the plan's)
+        log(f"bench: {args.steps} eager steps, then {args.steps} with per-kernel events")
         t1 = time.perf_counter()
         for s in range(args.steps):
-            w.run_eager(evs[s])
+            w.run_eager(None)
         torch.cuda.synchronize()
         eager_ms_per_step = (time.perf_counter() - t1) / args.steps * 1e3
+        for s in range(args.steps):
+            torch.cuda._sleep(1_000_000)
+            w.run_eager(evs[s])
+        torch.cuda.synchronize()
     plan_ms = float(np.mean([sum(e[0].elapsed_time(e[1]) for e in step) for step in evs]))
     attn_ms = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in step) for step in evs]))
     per_launch = [[round(float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)])), 4),
