@@ -375,7 +375,7 @@ class CpJob:
     """Every rank's share of a context-parallel job at cp = 8 over the 131072-token pack,
     one after another on this GPU (each share replayed from its own HIP graph)."""
 
-    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0, overlap=4, ring=True):
+    def __init__(self, torch, lb, workloads, rule, cp=8, chunk=8192, seed=0, overlap=4, ring=True, fused=True):
         from load_balance_amd import sharding as LS
         self.torch, self.lb = torch, lb
         lengths = workloads.zigzag_pack_lengths(seed)
@@ -387,9 +387,11 @@ class CpJob:
         self.shares = [LS.ShardedRank(shards, r) for r in range(cp)]
         streams = [torch.cuda.Stream() for _ in range(overlap)] if overlap and not ring else None
         self.ring = ring
-        for s in self.shares:
+        # with ring, a rank whose live steps fuse (ShardedRank.fusable) runs the fused ring
+        self.fused_ranks = [r for r, s in enumerate(self.shares) if ring and fused and s.fusable]
+        for r, s in enumerate(self.shares):
             if ring:
-                s.capture(ring=True)
+                s.capture(ring=True, fused=r in self.fused_ranks)
             else:
                 s.capture(streams=streams)
         self.H, self.d = 32, 128
@@ -536,11 +538,11 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w
     if name == "cp_job":
-        w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap, ring=ring)
+        w = CpJob(torch, lb, workloads, rule, seed=seed, overlap=overlap, ring=ring, fused=fused)
         w.config = {"workload": f"context-parallel job at cp=8 over a 131072-token lognormal pack (seed {seed}), "
                                 f"{rule} sharding: all 8 ranks' shares (8 ring steps + 7 merges each) in turn",
                     "tokens": 131072, "heads": 32, "kv_heads": 8, "head_dim": 128, "sharding": rule,
-                    "rank_pairs_per_head": w.rank_pairs,
+                    "rank_pairs_per_head": w.rank_pairs, "fused_ring_ranks": w.fused_ranks,
                     "time_model_prediction": w.predicted}
         return w
     raise SystemExit(f"unknown workload {name}")
