@@ -91,7 +91,8 @@ struct QueuesT {
                      hdr->off_order + nt * 4 > a.ws_bytes;
     if constexpr (RING) {
       // the ring was merged from plans made for these steps' key/value counts
-      bad = bad || r->n_steps < 1 || r->n_steps > kMaxPlanSteps || hdr->ring_steps != r->n_steps;
+      bad = bad || r->n_steps < 1 || r->n_steps > kMaxPlanSteps || hdr->ring_steps != r->n_steps ||
+            hdr->ring_fused != 0;  // a fused ring's tiles hold several steps' spans: not a key-tile ring
       for (int s = 0; s < kMaxPlanSteps; ++s)
         if (s < r->n_steps && hdr->ring_n_kv[s] != r->n_kv[s]) bad = true;
     }
