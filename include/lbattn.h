@@ -123,7 +123,8 @@ typedef struct {
                                     only if k_lo + j >= p (LB_NO_LOWER_BOUND: no such bound) */
   int32_t blocks;                /* sum over spans of ceil(k_len / LB_BLOCK_KEYS): the order key,
                                     or its main term in the varlen forward's fitted estimate */
-  int32_t reserved;
+  int32_t reserved;              /* 0 in a plan; in a ring workspace the tile's step (lb_plan_ring), or
+                                    in a fused ring span s's step in bits 4s..4s+3 (lb_plan_ring_fused) */
 } lb_plan_tile;
 
 /* One persistent workgroup's record (lb_read_worker_timing). */
