@@ -336,19 +336,24 @@ class ZigzagBwdStep(ZigzagStep):
     per step the block backward (dq added, the source chunk's partial dk, dv written).
     Effective FLOPs 10 * d * H * pairs, 2.5x the forward's."""
 
-    def __init__(self, torch, lb, workloads, seed=0, ring=True):
+    def __init__(self, torch, lb, workloads, seed=0, ring=True, fused=True):
         super().__init__(torch, lb, workloads, seed=seed, graph=False, overlap=0, ring=False, fused=False)
         self.bwd_ring = ring
+        # the dQ side fused per query tile (one launch over every live step) when the share fuses
+        self.bwd_fused = ring and fused and self.share.fusable
         sh = self.share
         sh.run_planned()
         r = np.random.default_rng(2001)
         n_q = sh.q.shape[0]
         self.dout = to_dev(workloads.f32_to_bf16_bits(r.standard_normal((n_q, self.H, self.d)).astype(np.float32)),
                            torch)
-        sh.backward(self.dout, ring=ring)  # allocates the backward's buffers outside the timed region
+        sh.backward(self.dout, ring=ring, fused=self.bwd_fused)  # allocates its buffers outside the timed region
         torch.cuda.synchronize()
         self.flops = 10 * self.d * self.H * self.pairs
-        self.kernel_name = ("ring backward (D; all steps' plans in one launch, their key-tile plans merged; "
+        self.kernel_name = ("ring backward (D; all steps' plans in one launch, their key-tile plans merged and their "
+                            "query-tile plans fused; one bwd_dq_kernel<128,1,true,fused> over every step; one "
+                            "bwd_dkv_kernel<128,true,ring> over every step)" if self.bwd_fused else
+                            "ring backward (D; all steps' plans in one launch, their key-tile plans merged; "
                             "bwd_dq_kernel<128,1,true> per step; one bwd_dkv_kernel<128,true,ring> over every step)"
                             if ring else "ring backward (D, then per step: plans, bwd_dq_kernel<128,1,true>, "
                             "bwd_dkv_kernel<128,true,false>)")
@@ -361,7 +366,7 @@ class ZigzagBwdStep(ZigzagStep):
         if evs is not None:
             evs[0][0].record()
             evs[0][1].record()
-        self.share.backward(self.dout, ring=self.bwd_ring)
+        self.share.backward(self.dout, ring=self.bwd_ring, fused=self.bwd_fused)
         if evs is not None:
             evs[0][2].record()
 
@@ -528,7 +533,7 @@ def make_workload(name, seed, torch, lb, workloads, graph=True, rule="per_docume
                     "head_dim": 128, "seed": seed, "flop_convention": "10*d*H*pairs (2.5x the forward's)"}
         return w
     if name == "zigzag_bwd":
-        w = ZigzagBwdStep(torch, lb, workloads, seed=seed, ring=ring)
+        w = ZigzagBwdStep(torch, lb, workloads, seed=seed, ring=ring, fused=fused)
         w.config = {"workload": "ring backward of one zigzag CP rank's share at cp=8: rank 3 of a 131072-token "
                                 f"lognormal pack (seed {seed}), a block-step backward per step with visible pairs "
                                 "(3 of 8: dq accumulated, per-step partial dk, dv) after the forward's merged out and "

@@ -420,6 +420,27 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
                                  void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
                                  size_t ring_workspace_bytes, hipStream_t stream);
 
+/*
+ * lb_block_attn_bwd_ring with the dQ side fused as the forward's fused ring is
+ * (lb_plan_ring_fused): the steps' query-tile plans are fused into q_ring_workspace (256-byte
+ * aligned, distinct from the other workspaces; sized by lb_ring_workspace_bytes), and one dQ
+ * launch runs each query tile against the keys and values of every step, adding the tile
+ * rows' whole dq into dq once.  dq, dkv and the other arguments as lb_block_attn_bwd_ring;
+ * dk, dv have its bits, dq agrees with it to fp32 rounding (one sum over every step's key
+ * blocks instead of a sum per step added into dq).  A query tile meeting more than
+ * LB_MAX_SPANS key runs over all steps sets LB_DEVERR_SPANS in q_ring_workspace's error
+ * word and the dQ launch then adds nothing (use lb_block_attn_bwd_ring then).  Argument
+ * errors return before anything is enqueued.
+ */
+lb_status lb_block_attn_bwd_ring_fused(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
+                                       const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
+                                       int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
+                                       const void* const* kv_chunks, const int32_t* n_kv,
+                                       const int32_t* const* kv_pos, const int32_t* const* kv_doc, float* dq,
+                                       float* const* dkv, void* const* workspaces, const size_t* workspace_bytes,
+                                       void* ring_workspace, size_t ring_workspace_bytes, void* q_ring_workspace,
+                                       size_t q_ring_workspace_bytes, hipStream_t stream);
+
 lb_status lb_attn_run(const void* q, const void* k, const void* v, int32_t n_q, int32_t n_kv, int32_t heads,
                       int32_t kv_heads, int32_t d, int32_t out_f32, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);

@@ -126,6 +126,9 @@ def lib() -> ctypes.CDLL:
     L.lb_block_attn_bwd.restype = ctypes.c_int
     L.lb_block_attn_bwd_ring.argtypes = [P, I32, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, SZ,
                                          P]
+    L.lb_block_attn_bwd_ring_fused.argtypes = [P, I32, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P,
+                                               P, SZ, P, SZ, P]
+    L.lb_block_attn_bwd_ring_fused.restype = ctypes.c_int
     L.lb_block_attn_bwd_ring.restype = ctypes.c_int
     L.lb_status_string.argtypes = [ctypes.c_int]
     L.lb_status_string.restype = ctypes.c_char_p
@@ -654,7 +657,7 @@ def bwd_key_plan_offset(block_path: bool, n_q: int, n_kv: int, n_seg: int, heads
 
 
 def block_attn_bwd_ring(q, kvs, dout, lse, dvec, q_pos, q_doc, kv_pos_list, kv_doc_list, dq, dkvs, workspaces,
-                        ring_workspace, stream=None, shared_doc=NO_SHARED_DOC):
+                        ring_workspace, stream=None, shared_doc=NO_SHARED_DOC, q_ring_workspace=None):
     """The backward of a rank's ring steps: per step s the query shard against kvs[s] (bf16
     [2,n_kv,H_kv,d]) with kv_pos_list[s], kv_doc_list[s]; dq (fp32 [n_q,H,d]) is added to,
     step after step; dkvs[s] (fp32 [2,n_kv,H_kv,d]) receives step s's partial dk, dv.  One
@@ -686,6 +689,14 @@ def block_attn_bwd_ring(q, kvs, dout, lse, dvec, q_pos, q_doc, kv_pos_list, kv_d
     nkv = (ctypes.c_int32 * max(n, 1))(*[k.shape[1] for k in kvs])
     sizes = (ctypes.c_size_t * max(n, 1))(*[w.numel() for w in workspaces])
     _gpu(q, "q")
+    if q_ring_workspace is not None:  # lb_block_attn_bwd_ring_fused: the dQ side fused per query tile
+        _ws(q_ring_workspace, "q_ring_workspace", dev)
+        _check(lib().lb_block_attn_bwd_ring_fused(
+            _ptr(q), n_q, _ptr(dout), _ptr(lse), _ptr(dvec), _ptr(q_pos), _ptr(q_doc), H, Hkv, d, int(shared_doc), n,
+            ptrs(kvs), nkv, ptrs(kv_pos_list), ptrs(kv_doc_list), _ptr(dq), ptrs(dkvs), ptrs(workspaces), sizes,
+            _ptr(ring_workspace), ring_workspace.numel(), _ptr(q_ring_workspace), q_ring_workspace.numel(),
+            ctypes.c_void_p(_stream(stream))), "lb_block_attn_bwd_ring_fused")
+        return dq, dkvs
     _check(lib().lb_block_attn_bwd_ring(_ptr(q), n_q, _ptr(dout), _ptr(lse), _ptr(dvec), _ptr(q_pos), _ptr(q_doc), H,
                                         Hkv, d, int(shared_doc), n, ptrs(kvs), nkv, ptrs(kv_pos_list),
                                         ptrs(kv_doc_list), _ptr(dq), ptrs(dkvs), ptrs(workspaces), sizes,

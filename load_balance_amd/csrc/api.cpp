@@ -776,13 +776,15 @@ lb_status lb_block_attn_bwd(const void* q_shard, int32_t n_q, const void* kv_chu
   return launch_bwd_dkv(b, d, true, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
 }
 
-lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
-                                 const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
-                                 int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
-                                 const void* const* kv_chunks, const int32_t* n_kv, const int32_t* const* kv_pos,
-                                 const int32_t* const* kv_doc, float* dq, float* const* dkv,
-                                 void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
-                                 size_t ring_workspace_bytes, hipStream_t stream) {
+namespace {
+// q_ring: null for one dQ launch per step, else the workspace the steps' query-tile plans are
+// fused into for one dQ launch over every step
+lb_status bwd_ring(const void* q_shard, int32_t n_q, const void* dout, const float* lse, const float* dvec,
+                   const int32_t* q_pos, const int32_t* q_doc, int32_t heads, int32_t kv_heads, int32_t d,
+                   int32_t shared_doc, int32_t n_steps, const void* const* kv_chunks, const int32_t* n_kv,
+                   const int32_t* const* kv_pos, const int32_t* const* kv_doc, float* dq, float* const* dkv,
+                   void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
+                   size_t ring_workspace_bytes, void* q_ring, size_t q_ring_bytes, hipStream_t stream) {
   if (n_q < 0 || shared_doc < -1 || n_steps < 1 || 2 * n_steps > kMaxPlanSteps) return LB_EINVAL;
   if (!q_shard || !dout || !lse || !dvec || !q_pos || !q_doc || !dq || !ring_workspace) return LB_EINVAL;
   if (!kv_chunks || !n_kv || !kv_pos || !kv_doc || !dkv || !workspaces || !workspace_bytes) return LB_EINVAL;
@@ -794,6 +796,9 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
   if (!aligned(ring_workspace, 256)) return LB_EWORKSPACE;
   const int64_t cap = ((int64_t)ring_workspace_bytes - kRingTilesOffset) / (int64_t)sizeof(lb_plan_tile);
   if (cap < 1) return LB_EWORKSPACE;
+  const int64_t q_cap = q_ring ? ((int64_t)q_ring_bytes - kRingTilesOffset) / (int64_t)sizeof(lb_plan_tile) : 0;
+  if (q_ring && (!aligned(q_ring, 256) || q_cap < 1)) return LB_EWORKSPACE;
+  if (q_ring && q_ring == ring_workspace) return LB_EINVAL;
   BwdLayout B[kMaxPlanSteps];
   for (int s = 0; s < n_steps; ++s) {
     if (n_kv[s] < 1 || !kv_chunks[s] || !kv_pos[s] || !kv_doc[s] || !dkv[s] || !workspaces[s]) return LB_EINVAL;
@@ -801,7 +806,7 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
       return LB_EINVAL;
     for (int o = 0; o < s; ++o)
       if (workspaces[o] == workspaces[s] || dkv[o] == dkv[s]) return LB_EINVAL;
-    if (workspaces[s] == ring_workspace) return LB_EINVAL;
+    if (workspaces[s] == ring_workspace || (q_ring && workspaces[s] == q_ring)) return LB_EINVAL;
     if (!aligned(workspaces[s], 256)) return LB_EWORKSPACE;
     st = bwd_layout_block(n_q, n_kv[s], heads, kv_heads, workspace_bytes[s], &B[s]);
     if (st != LB_OK) return st;
@@ -834,6 +839,17 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
   m.ring_cap = (int32_t)std::min<int64_t>(cap, INT32_MAX);
   m.transposed = 1;
   if (launch_ring_merge(m, stream) != hipSuccess) return LB_EHIP;
+  if (q_ring) {  // the query-tile plans fused: one tile per query tile with every step's spans
+    RingMergeArgs mq = m;
+    for (int s = 0; s < n_steps; ++s) {
+      mq.step_ws[s] = static_cast<const char*>(workspaces[s]);
+      mq.step_ws_bytes[s] = B[s].off_k;
+    }
+    mq.ring = static_cast<char*>(q_ring);
+    mq.ring_cap = (int32_t)std::min<int64_t>(q_cap, INT32_MAX);
+    mq.transposed = 0;
+    if (launch_ring_fuse(mq, stream) != hipSuccess) return LB_EHIP;
+  }
   int workers = 0;
   st = persistent_workers(&workers);
   if (st != LB_OK) return st;
@@ -847,7 +863,7 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
     BwdArgs b = bwd_args(q_shard, kbase, vbase, dout, lse, dvec, dq, dk, dv, n_q, n_kv[s], heads, kv_heads, d);
     b.ws = static_cast<char*>(workspaces[s]);
     b.ws_bytes = B[s].off_k;
-    if (launch_bwd_dq(b, d, true, workers, stream) != hipSuccess) return LB_EHIP;
+    if (!q_ring && launch_bwd_dq(b, d, true, workers, stream) != hipSuccess) return LB_EHIP;
     r.k[s] = kbase;
     r.v[s] = vbase;
     r.dk[s] = dk;
@@ -855,11 +871,44 @@ lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* d
     r.n_kv[s] = n_kv[s];
   }
   r.n_steps = n_steps;
+  if (q_ring) {  // dq: one launch, each query tile against every step's keys and values
+    BwdArgs bq = bwd_args(q_shard, q_shard, q_shard, dout, lse, dvec, dq, r.dk[0], r.dv[0], n_q, 0, heads, kv_heads, d);
+    bq.ws = static_cast<char*>(q_ring);
+    bq.ws_bytes = (int64_t)q_ring_bytes;
+    if (launch_bwd_dq_fused(bq, r, d, workers, stream) != hipSuccess) return LB_EHIP;
+  }
   // dk, dv: every step's key tiles in one launch, each step's gradients into its own buffer
   BwdArgs b = bwd_args(q_shard, q_shard, q_shard, dout, lse, dvec, dq, r.dk[0], r.dv[0], n_q, 0, heads, kv_heads, d);
   b.ws = static_cast<char*>(ring_workspace);
   b.ws_bytes = (int64_t)ring_workspace_bytes;
   return launch_bwd_dkv_ring(b, r, d, workers, stream) == hipSuccess ? LB_OK : LB_EHIP;
+}
+}  // namespace
+
+lb_status lb_block_attn_bwd_ring(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
+                                 const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
+                                 int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
+                                 const void* const* kv_chunks, const int32_t* n_kv, const int32_t* const* kv_pos,
+                                 const int32_t* const* kv_doc, float* dq, float* const* dkv,
+                                 void* const* workspaces, const size_t* workspace_bytes, void* ring_workspace,
+                                 size_t ring_workspace_bytes, hipStream_t stream) {
+  return bwd_ring(q_shard, n_q, dout, lse, dvec, q_pos, q_doc, heads, kv_heads, d, shared_doc, n_steps, kv_chunks,
+                  n_kv, kv_pos, kv_doc, dq, dkv, workspaces, workspace_bytes, ring_workspace, ring_workspace_bytes,
+                  nullptr, 0, stream);
+}
+
+lb_status lb_block_attn_bwd_ring_fused(const void* q_shard, int32_t n_q, const void* dout, const float* lse,
+                                       const float* dvec, const int32_t* q_pos, const int32_t* q_doc, int32_t heads,
+                                       int32_t kv_heads, int32_t d, int32_t shared_doc, int32_t n_steps,
+                                       const void* const* kv_chunks, const int32_t* n_kv,
+                                       const int32_t* const* kv_pos, const int32_t* const* kv_doc, float* dq,
+                                       float* const* dkv, void* const* workspaces, const size_t* workspace_bytes,
+                                       void* ring_workspace, size_t ring_workspace_bytes, void* q_ring_workspace,
+                                       size_t q_ring_workspace_bytes, hipStream_t stream) {
+  if (!q_ring_workspace) return LB_EINVAL;
+  return bwd_ring(q_shard, n_q, dout, lse, dvec, q_pos, q_doc, heads, kv_heads, d, shared_doc, n_steps, kv_chunks,
+                  n_kv, kv_pos, kv_doc, dq, dkv, workspaces, workspace_bytes, ring_workspace, ring_workspace_bytes,
+                  q_ring_workspace, q_ring_workspace_bytes, stream);
 }
 
 const char* lb_status_string(lb_status s) {

@@ -77,7 +77,8 @@ struct QueuesT {
   int n_empty;
   bool dry;  // thread 0's view
 
-  __device__ void open(const BwdArgs& a, int transposed, const RingBwdSteps* r = nullptr) {
+  // fused: the ring must be a fused ring (lb_plan_ring_fused), else an unfused one
+  __device__ void open(const BwdArgs& a, int transposed, const RingBwdSteps* r = nullptr, bool fused = false) {
     hdr = reinterpret_cast<WsHeader*>(a.ws);
     const int64_t nt = hdr->n_tiles;
     bool bad = hdr->magic != (RING ? kRingMagic : kPlanMagic) || hdr->transposed != transposed ||
@@ -92,7 +93,7 @@ struct QueuesT {
     if constexpr (RING) {
       // the ring was merged from plans made for these steps' key/value counts
       bad = bad || r->n_steps < 1 || r->n_steps > kMaxPlanSteps || hdr->ring_steps != r->n_steps ||
-            hdr->ring_fused != 0;  // a fused ring's tiles hold several steps' spans: not a key-tile ring
+            hdr->ring_fused != (fused ? 1 : 0);
       for (int s = 0; s < kMaxPlanSteps; ++s)
         if (s < r->n_steps && hdr->ring_n_kv[s] != r->n_kv[s]) bad = true;
     }
@@ -309,8 +310,11 @@ struct DqLds {
   static_assert(BN == 64, "a stage is one 64-row tile per tensor");
 };
 
-template <int D, int HPW, bool OUT_F32>
-__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+// FUSED: the workspace is a fused ring (lb_plan_ring_fused over the steps' query-tile plans):
+// each tile holds the key spans of every step, span s's step in bits 4s..4s+3 of `reserved`,
+// whose keys and values r gives; one item adds the tile rows' whole dq over every step.
+template <int D, int HPW, bool OUT_F32, bool FUSED = false>
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a, RingBwdSteps r) {
   using L = DqLds<D>;
   __shared__ __attribute__((aligned(1024))) char smem[L::ring];
   __shared__ int s_item;
@@ -326,8 +330,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* dO = reinterpret_cast<const __bf16*>(a.dout);
 
-  Queues qs;
-  qs.open(a, 0);
+  QueuesT<FUSED> qs;
+  qs.open(a, 0, &r, FUSED);
   uint64_t t_start = tid == 0 ? device_clock() : 0;
   int my_items = 0, my_blocks = 0;
   int64_t my_pairs = 0;
@@ -342,6 +346,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int q_start = __builtin_amdgcn_readfirstlane(T->q_start);
     const int q_len = __builtin_amdgcn_readfirstlane(T->q_len);
     const int q_pos0 = __builtin_amdgcn_readfirstlane(T->q_pos0);
+    // FUSED: the step of every span, and the tile's span count (the copy cursor's span index
+    // is n_spans - 1 - left)
+    const uint32_t span_steps = FUSED ? __builtin_amdgcn_readfirstlane((uint32_t)T->reserved) : 0u;
+    const int n_spans_t = __builtin_amdgcn_readfirstlane(T->n_spans);
     SpanCursor cur;  // the key block being computed
     cur.start(T, BN);
     const int n_blocks = cur.blocks(BN);
@@ -390,8 +398,16 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       const int k0 = __builtin_amdgcn_readfirstlane(nxt.sp.start + nxt.off);
       const int valid = __builtin_amdgcn_readfirstlane(max(0, min(nxt.sp.len - nxt.off, BN)));
       const uint32_t lds = ring_lds + slot * L::stage;
-      TileCopier<D, BN>::issue_now(a.k, row_bytes, k0, valid, g, lds, wave, lane);
-      TileCopier<D, BN>::issue_now(a.v, row_bytes, k0, valid, g, lds + L::tileBytes, wave, lane);
+      const void* kx = a.k;
+      const void* vx = a.v;
+      if constexpr (FUSED) {  // the keys and values of the step the span belongs to
+        const int idx = min(max(n_spans_t - 1 - nxt.left, 0), LB_MAX_SPANS - 1);
+        const int st = min((int)(span_steps >> (4 * idx)) & 15, r.n_steps - 1);
+        kx = r.k[st];
+        vx = r.v[st];
+      }
+      TileCopier<D, BN>::issue_now(kx, row_bytes, k0, valid, g, lds, wave, lane);
+      TileCopier<D, BN>::issue_now(vx, row_bytes, k0, valid, g, lds + L::tileBytes, wave, lane);
       nxt.next(BN, 1);
     };
 #pragma unroll
@@ -849,7 +865,14 @@ hipError_t launch_bwd_rowdot(const void* out, bool out_f32, const void* dout, in
 
 template <int D, bool F32>
 static void dq_launch(const BwdArgs& a, int workers, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dq_kernel<D, 1, F32>), dim3(workers), dim3(kDqThreads), 0, s, a);
+  const RingBwdSteps none{};
+  hipLaunchKernelGGL((bwd_dq_kernel<D, 1, F32>), dim3(workers), dim3(kDqThreads), 0, s, a, none);
+}
+
+hipError_t launch_bwd_dq_fused(const BwdArgs& a, const RingBwdSteps& r, int d, int n_workers, hipStream_t s) {
+  if (d == 128) hipLaunchKernelGGL((bwd_dq_kernel<128, 1, true, true>), dim3(n_workers), dim3(kDqThreads), 0, s, a, r);
+  else hipLaunchKernelGGL((bwd_dq_kernel<64, 1, true, true>), dim3(n_workers), dim3(kDqThreads), 0, s, a, r);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, bool out_f32, int n_workers, hipStream_t s) {

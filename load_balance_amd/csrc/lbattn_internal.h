@@ -251,5 +251,6 @@ struct RingBwdSteps {
   int32_t n_steps;
 };
 hipError_t launch_bwd_dkv_ring(const BwdArgs& a, const RingBwdSteps& r, int d, int n_workers, hipStream_t s);
+hipError_t launch_bwd_dq_fused(const BwdArgs& a, const RingBwdSteps& r, int d, int n_workers, hipStream_t s);
 
 }  // namespace lb

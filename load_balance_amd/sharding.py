@@ -586,7 +586,7 @@ class ShardedRank:
             lse_merge(self.out, self.lse, *self.overlap_buffers[i], stream=main)
         return self.out, self.lse
 
-    def backward(self, dout, stream=None, ring=False):
+    def backward(self, dout, stream=None, ring=False, fused=False):
         """The rank's ring backward after a forward (run, run_planned, run_overlapped or a
         replay) left out and lse: D = <dout, out> once, then per live step the query shard's
         dq contribution (added into one fp32 buffer, so the steps run in order) and the source
@@ -619,11 +619,20 @@ class ShardedRank:
                 n_max, runs, H, Hkv, device = self._ws_shape
                 self.bwd_ring_workspace = new_ring_workspace(len(self.live_steps), n_max, runs, H, Hkv, device=device)
             live = self.live_steps
+            q_ring = None
+            if fused:  # the dQ side as a fused ring: one launch, each query tile against every step
+                if not self.fusable:
+                    raise ValueError("this share's live steps do not fuse")
+                if getattr(self, "bwd_q_ring_workspace", None) is None:
+                    n_max, runs, H, Hkv, device = self._ws_shape
+                    self.bwd_q_ring_workspace = new_ring_workspace(len(self.live_steps), n_max, runs, H, Hkv,
+                                                                   device=device)
+                q_ring = self.bwd_q_ring_workspace
             block_attn_bwd_ring(self.q, [self.steps[t]["kv"] for t in live], dout, self.lse, b["dvec"], self.q_pos,
                                 self.q_doc, [self.steps[t]["kv_pos"] for t in live],
                                 [self.steps[t]["kv_doc"] for t in live], b["dq"], [b["dkv"][t] for t in live],
                                 [b["ws"][t] for t in live], self.bwd_ring_workspace, stream=stream,
-                                shared_doc=self.shared_doc)
+                                shared_doc=self.shared_doc, q_ring_workspace=q_ring)
             return b["dq"], [b["dkv"][t] if t in live else None for t in range(len(self.steps))]
         for t in self.live_steps:
             st = self.steps[t]

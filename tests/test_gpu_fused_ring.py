@@ -212,3 +212,39 @@ def test_fused_ring_zigzag_rank3_cp8_every_row(tmp_path):
         f"lse max {st['lse_max']:.3e}")
     assert st["finite"] and st["n"] == 2 * C * 32 * 128
     assert st["out_max"] <= OUT_MAX and st["out_mean"] <= OUT_MEAN and st["lse_max"] <= LSE_MAX
+
+
+def check_fused_bwd(share, what):
+    """The ring backward with the dQ side fused (lb_block_attn_bwd_ring_fused) against the
+    unfused ring backward: dk, dv bit for bit (the same dK/dV launch), dq to fp32 rounding
+    (one sum over every step's key blocks instead of a sum per step added into dq)."""
+    n_q, H, d = share.q.shape
+    r = np.random.default_rng(31)
+    dout = torch.from_numpy(workloads.f32_to_bf16_bits(r.standard_normal((n_q, H, d)).astype(np.float32))
+                            .view(np.int16)).view(torch.bfloat16).cuda()
+    share.run_fused()
+    dq, dkv = share.backward(dout, ring=True)
+    torch.cuda.synchronize()
+    dq_ref, dkv_ref = dq.clone(), [None if x is None else x.clone() for x in dkv]
+    dq, dkv = share.backward(dout, ring=True, fused=True)
+    torch.cuda.synchronize()
+    assert lb.read_device_error(share.bwd_q_ring_workspace) == 0, what
+    for a, b in zip(dkv, dkv_ref):
+        assert (a is None) == (b is None)
+        if a is not None:
+            assert torch.equal(a, b), f"{what}: dk/dv differ"
+    scale = dq_ref.abs().max().item()
+    diff = (dq - dq_ref).abs().max().item()
+    say(f"  {what}: fused dQ vs per-step dQ: max |diff| {diff:.2e} (max |dq| {scale:.2e})")
+    assert diff <= 1e-4 * scale, what
+
+
+@pytest.mark.parametrize("rank,H,Hkv,d", [(0, 8, 2, 128), (3, 32, 8, 128), (2, 8, 1, 64)])
+def test_fused_dq_ring_backward(rank, H, Hkv, d):
+    share = ring_share(cp=4, C=256, rank=rank, H=H, Hkv=Hkv, d=d)
+    check_fused_bwd(share, f"bwd rank {rank} H={H}/{Hkv} d={d}")
+
+
+def test_fused_dq_ring_backward_zigzag_rank3_cp8():
+    share, _, _ = zigzag_rank3()
+    check_fused_bwd(share, "zigzag rank 3 backward")
