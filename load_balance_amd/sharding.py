@@ -46,6 +46,7 @@ import numpy as np
 import torch
 
 BLOCK_KEYS = 64  # keys per block of the attention kernel (LB_BLOCK_KEYS)
+FUSED_TILE_CAP = 4096  # query tiles one fused ring takes (lb_plan_ring_fused)
 
 
 # --------------------------------------------------------------------------
@@ -463,8 +464,11 @@ class ShardedRank:
         no query run meets more than MAX_SPANS key runs over all of them together."""
         live_sides = [(self.steps[t]["kv_pos"].cpu().numpy(), self.steps[t]["kv_doc"].cpu().numpy())
                       for t in self.live_steps]
+        # the fused planner takes at most FUSED_TILE_CAP query tiles; bounded here with the
+        # shortest tile either the forward or the backward's dQ side cuts (32 rows)
+        q_tiles = int(np.sum(-(-_runs(np.asarray(q_pos), np.asarray(q_doc))[:, 1] // 32)))
         self.fusable = bool(self.live_steps) and not any("slices" in self.steps[t] for t in self.live_steps) and \
-            fused_span_count(q_pos, q_doc, live_sides, self.shared_doc) <= MAX_SPANS
+            fused_span_count(q_pos, q_doc, live_sides, self.shared_doc) <= MAX_SPANS and q_tiles <= FUSED_TILE_CAP
 
     def _no_live_step(self):
         """The result when no step has a visible pair: every row sees nothing."""
